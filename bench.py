@@ -1,0 +1,184 @@
+"""Benchmark of the LaplacianFormer attention forward pass on one MI355X.
+
+A step is one lf_attn_fwd call over one batch of synthetic input that is already resident in HBM. The call is
+landmark pooling -> fused L1-distance+exp kernels -> Newton-Schulz pseudo-inverse -> C_K^T V -> landmark mix ->
+output GEMM with the depthwise-conv epilogue. The default workload is the PVT stage-1 shape: B=8, one head,
+56x56 tokens, d=64, r=8 (m=49), lambda=4, eps=1e-3, 12 Newton-Schulz steps, fp32.
+
+It prints one JSON line with the whole-job throughput (tokens/s = B*heads*N per step). It also prints the roofline
+of the dominant kernel (laplace_l1_exp: VALU-bound, timed with HIP events on its own stream) and the fp64 CPU
+oracle timed on a bounded sample of the same workload on the host cores.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Laplacian-Nyström attention fwd tokens/s (B·heads·N) + % VALU/MFMA roofline"
+
+# MI355X: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz issue 39.3e12 fp32 lane-operations per second. The published
+# 157.3 TFLOP/s fp32 vector peak counts an FMA as two flops and packed-fp32 as two lanes; the distance kernel's
+# v_sub_f32 and v_add_f32 |.| are neither, so its peak is 157.3 / 4.
+VALU_PEAK_TFLOPS = 256 * 64 * 2.4e9 / 1e12
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="pvt_s1_56x56_m49")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall time budget of the oracle sample")
+    ap.add_argument("--kernel-reps", type=int, default=100)
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, inp, budget_s):
+    """The fp64 oracle as it stands, on one thread, over whole slices of the same workload until the budget."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    op = O.Params(B=wl.B, heads=wl.heads, H=wl.H, W=wl.W, d=wl.d, r=wl.r, lam=wl.lam, eps=wl.eps,
+                  ns_iters=wl.ns_iters, whiten=wl.whiten, whiten_eps=wl.whiten_eps)
+    slices = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            b, h = divmod(slices % wl.G, wl.heads)
+            O.forward_slice(inp["Q"][b, h], inp["K"][b, h], inp["V"][b, h], inp["w64"][h * wl.d:(h + 1) * wl.d], op)
+            slices += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": slices * wl.N / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{slices} (batch, head) slices of {wl.name} ({wl.N} tokens each), fp64 numpy, one thread, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the B*heads slices are "
+              "independent, so a multi-GPU run would shard them with no communication.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from laplacian_nystr_vit_amd import lf
+    from laplacian_nystr_vit_amd import workloads as WL
+
+    wl = WL.ALL[args.workload]
+    torch.cuda.set_device(0)
+    inp = WL.make_inputs(wl, seed=0)
+    dt = torch.bfloat16 if wl.dtype == WL.BF16 else torch.float32
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    Q, K, V, w = dev(inp["Q_raw"]), dev(inp["K_raw"]), dev(inp["V_raw"]), dev(inp["w"])
+    p = lf.make_params(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.r, wl.lam, wl.eps, wl.ns_iters, wl.whiten, wl.whiten_eps,
+                       dt)
+    fwd_b, _, _ = lf.lf_attn_query(p)
+    ws = torch.empty(fwd_b, dtype=torch.uint8, device="cuda")
+    Y = torch.empty_like(Q)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        lf.lf_attn_fwd(p, Q, K, V, w, Y, None, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = wl.tokens * args.steps / elapsed
+
+    # Dominant kernel: laplace_l1_exp, through its own entry point on the same stream, bracketed by HIP events.
+    G, N, m, d = p.G, p.N, p.m, p.d
+    L = torch.empty(G * m * d, device="cuda")
+    CQ = torch.empty(G * N * m, device="cuda")
+    CK = torch.empty_like(CQ)
+    We = torch.empty(G * m * m, device="cuda")
+    lf.lf_landmark_pool(p, Q, L, stream)
+    for _ in range(5):
+        lf.lf_laplace_l1_exp(p, Q, K, L, CQ, CK, We, stream)
+    durs = []
+    for _ in range(args.kernel_reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lf.lf_laplace_l1_exp(p, Q, K, L, CQ, CK, We, stream)
+        e1.record(stream)
+        durs.append((e0, e1))
+    torch.cuda.synchronize()
+    lap_us = float(np.mean([a.elapsed_time(b) for a, b in durs])) * 1e3
+    # Algorithmic work: per (row, landmark, channel) one subtract and one |.|-add, over 2N + m rows per slice.
+    ops = 2.0 * G * (2 * N + m) * m * d
+    achieved = ops / (lap_us * 1e-6) / 1e12
+
+    # Per-stage event times (each stage entry point alone, same stream), for context.
+    stages = {}
+
+    def time_stage(name, fn, reps=50):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stages[name] = round(e0.elapsed_time(e1) / reps * 1e3, 2)
+
+    X = torch.empty(G * m * m, device="cuda")
+    S = torch.empty(G * m * d, device="cuda")
+    P = torch.empty(G * m * d, device="cuda")
+    time_stage("landmark_pool", lambda: lf.lf_landmark_pool(p, Q, L, stream))
+    time_stage("laplace_l1_exp", lambda: lf.lf_laplace_l1_exp(p, Q, K, L, CQ, CK, We, stream))
+    time_stage("ns_pinv", lambda: lf.lf_ns_pinv(p, We, X, None, None, None, ws, stream))
+    time_stage("ckv_reduce", lambda: lf.lf_ckv_reduce(p, CK, V, S, ws, stream))
+    time_stage("landmark_mix", lambda: lf.lf_landmark_mix(p, X, S, None, P, stream))
+    time_stage("out_gemm_dwc", lambda: lf.lf_out_gemm_dwc(p, CQ, P, None, V, w, Y, stream))
+
+    rec = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == WL.F32 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} forward", "B": wl.B, "heads": wl.heads, "H": wl.H, "W": wl.W, "d": wl.d,
+                   "r": wl.r, "m": wl.m, "lambda": wl.lam, "eps": wl.eps, "ns_iters": wl.ns_iters,
+                   "tokens_per_step": wl.tokens},
+        "roofline": {"kernel": "laplace_l1_exp", "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / VALU_PEAK_TFLOPS, "traffic": None,
+                     "avg_us": lap_us, "ops_per_launch": ops},
+        "stages_us": stages,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

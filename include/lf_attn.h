@@ -1,0 +1,141 @@
+/*
+ * lf_attn.h — C ABI of liblf_attn.so, the LaplacianFormer attention block on AMD Instinct MI355X (gfx950).
+ *
+ * Sources. The operation is defined by the papernotes.org ICLR 2026 reading note
+ * "LaplacianFormer：用拉普拉斯核重新思考线性注意力" (cited below as [note]). Its sections used here are:
+ *   - motivation, "core idea" paragraph: the Laplacian kernel k(x,y) = exp(-||x-y||_1/lambda) and its gradient;
+ *   - framework: the flowchart Q,K,V -> kernel -> whitening -> landmarks -> Nystrom -> Newton-Schulz -> ZV + DWC(V);
+ *   - Design 1: injective normalisation by diagonal whitening, output = ZV + DWC(V);
+ *   - Design 2: Nystrom approximation C W^+ C^T with landmarks from r x r average pooling of the query map;
+ *   - Design 3: W + eps I, Newton-Schulz X_0 = alpha W^T, X_{k+1} = X_k (2I - W X_k), fused kernels.
+ * The arXiv 2604.20368 abstract ([abs]) adds that the kernel and the solver have forward and backward passes.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Shapes:   G = B*heads independent slices; N = H*W tokens, row-major (token n = y*W + x);
+ *            m = (H/r)*(W/r) landmarks, landmark index l = Y*(W/r) + X for the r x r block at (Y, X).
+ *  Tensors:  Q, K, V, Y, dY, dQ, dK, dV are [B][heads][N][d], contiguous, in params->dtype (float32 or the bf16
+ *            bit pattern). Intermediates are float32: L [G][m][d], C_Q and C_K [G][N][m], W_eps and X [G][m][m],
+ *            S and P [G][m][d], mu and rstd [G][m]. The DWC weight is float32 [heads*d][3][3].
+ *  Pointers: every pointer is a device pointer owned by the caller, 16-byte aligned. The library never allocates,
+ *            frees or synchronises. Work is enqueued on `stream` (a hipStream_t; NULL means the null stream)
+ *            and the call returns as soon as it is enqueued.
+ *  Errors:   every entry point returns LF_OK (0) or a negative code. Parameters, pointers and workspace sizes are
+ *            checked on the host before anything is launched; on an error nothing is launched. LF_EHIP reports a
+ *            failed launch (hipGetLastError). Nothing throws across this ABI. Calls are reentrant; calls that
+ *            share output or workspace buffers must be ordered by the caller.
+ *  Readings: where the pages are silent the library takes these readings: landmarks come from Q and serve C_Q,
+ *            C_K and W; the cross form Y = A_hat X (C_K^T V); alpha = 1/(||W_eps||_1 ||W_eps||_inf); sign(0) = 0;
+ *            alpha is held constant in the backward pass; whitening centres and scales the landmark columns of
+ *            C_Q over the slice's N tokens (biased variance); DWC is a 3x3 zero-padded cross-correlation, no bias.
+ */
+#ifndef LF_ATTN_H
+#define LF_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* lf_stream_t; /* same type as hipStream_t */
+
+enum lf_status {
+  LF_OK = 0,
+  LF_EINVAL = -1,       /* bad shape, parameter, null or misaligned pointer */
+  LF_EWORKSPACE = -2,   /* workspace smaller than lf_attn_query reports */
+  LF_EUNSUPPORTED = -3, /* valid but not implemented: d not in {16,32,64,128}, m > LF_M_MAX, backward with m or d > 64 */
+  LF_EHIP = -4          /* a kernel launch failed */
+};
+
+enum lf_dtype { LF_F32 = 0, LF_BF16 = 1 };
+
+#define LF_M_MAX 256
+#define LF_NS_ITERS_MAX 64
+
+typedef struct lf_attn_params {
+  int32_t B, heads, H, W, d; /* N = H*W */
+  int32_t r;                 /* pooling window and stride; H % r == 0 and W % r == 0 */
+  float lambda;              /* kernel scale, > 0 ([note] ablation default 4) */
+  float eps;                 /* >= 0, added to the diagonal of W ([note] Design 3) */
+  int32_t ns_iters;          /* 0..LF_NS_ITERS_MAX Newton-Schulz steps, no early exit (0 gives X = alpha W_eps^T) */
+  int32_t whiten;            /* 0 or 1: diagonal whitening of C_Q's landmark columns ([note] Design 1) */
+  float whiten_eps;          /* > 0, added to the column variance when whiten = 1 */
+  int32_t dtype;             /* LF_F32 or LF_BF16: type of Q, K, V, Y, dY, dQ, dK, dV */
+} lf_attn_params;
+
+/* Byte offsets of the intermediates inside the `saved` buffer written by lf_attn_fwd (each 256-byte aligned).
+ * xs holds X_0 .. X_{ns_iters} ([G][ns_iters+1][m][m]); alpha is float32 [G]. mu and rstd are written only
+ * when whiten = 1. The layout is fixed for given params; lf_attn_bwd reads it. */
+typedef struct lf_saved_layout {
+  size_t L, CQ, CK, We, xs, mu, rstd, S, P, alpha, total;
+} lf_saved_layout;
+
+/* Sizes, in bytes, of the forward workspace, the saved buffer and the backward workspace for `p`.
+ * Any pointer may be NULL. Host-only; launches nothing. Returns LF_EINVAL / LF_EUNSUPPORTED for bad params. */
+int lf_attn_query(const lf_attn_params* p, size_t* fwd_ws_bytes, size_t* saved_bytes, size_t* bwd_ws_bytes);
+
+/* Layout of the saved buffer (host-only). */
+int lf_attn_saved_layout(const lf_attn_params* p, lf_saved_layout* out);
+
+/* Forward pass ([note] framework flowchart; Designs 1-3):
+ *   L = pool_r(Q); C_Q = k(Q, L); C_K = k(K, L); W_eps = k(L, L) + eps I; X = NS^{ns_iters}(W_eps);
+ *   A_hat = C_Q, or its whitened form when whiten = 1; Y = A_hat X (C_K^T V) + DWC(V).
+ * dwc_w: [heads*d][3][3] float32, or NULL for the attention branch alone (Y = A_hat X C_K^T V).
+ * saved: NULL, or a buffer of lf_attn_query's saved_bytes that receives the intermediates for lf_attn_bwd.
+ * ws/ws_bytes: device workspace of at least fwd_ws_bytes. Y must not alias Q, K or V. */
+int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w, void* Y,
+                void* saved, void* ws, size_t ws_bytes, lf_stream_t stream);
+
+/* Backward pass of <dY, Y> with respect to Q, K and V ([abs]: forward and backward; [note] motivation "core idea"
+ * for the kernel gradient, with the sign read as d/dx exp(-||x-y||_1/lambda) = -(1/lambda) sign(x-y) k).
+ * saved: the buffer filled by lf_attn_fwd with the same params and inputs. ws: at least bwd_ws_bytes.
+ * dQ, dK, dV are overwritten. Supports m <= 64 and d <= 64 (LF_EUNSUPPORTED otherwise). */
+int lf_attn_bwd(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
+                const void* saved, const void* dY, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
+                lf_stream_t stream);
+
+/* Static description of a status code. */
+const char* lf_strerror(int code);
+
+/* ---- Stage entry points: each step of the forward pass on its own, same conventions as above. ---- */
+
+/* L[g][l][c] = (1/r^2) sum_{a,b<r} Q[g][(Y r + a) W + X r + b][c]   ([note] Design 2: r x r average pooling). */
+int lf_landmark_pool(const lf_attn_params* p, const void* Q, float* L, lf_stream_t stream);
+
+/* C_Q[g][i][l] = exp(-sum_c |Q[g][i][c] - L[g][l][c]| / lambda); C_K likewise with K;
+ * W_eps[g][l][l'] = exp(-||L_l - L_l'||_1 / lambda) + eps [l == l']   ([note] motivation; Designs 2 and 3). */
+int lf_laplace_l1_exp(const lf_attn_params* p, const void* Q, const void* K, const float* L, float* CQ, float* CK,
+                      float* We, lf_stream_t stream);
+
+/* Newton-Schulz pseudo-inverse ([note] Design 3): alpha = 1/(||W_eps||_1 ||W_eps||_inf), X_0 = alpha W_eps^T,
+ * X_{k+1} = X_k (2I - W_eps X_k) for p->ns_iters steps. X: [G][m][m] receives X_{ns_iters}.
+ * xs: NULL or [G][ns_iters+1][m][m] receiving X_0..X_{ns_iters}; alpha_out: NULL or [G];
+ * resid: NULL or [G] receiving ||W_eps X - I||_F. ws: at least fwd_ws_bytes. */
+int lf_ns_pinv(const lf_attn_params* p, const float* We, float* X, float* xs, float* alpha_out, float* resid,
+               void* ws, size_t ws_bytes, lf_stream_t stream);
+
+/* S[g][l][c] = sum_i C_K[g][i][l] V[g][i][c]: the "K^T V first" association of linear attention, as a
+ * deterministic split-N reduction ([note] motivation; Design 2). ws: at least fwd_ws_bytes. */
+int lf_ckv_reduce(const lf_attn_params* p, const float* CK, const void* V, float* S, void* ws, size_t ws_bytes,
+                  lf_stream_t stream);
+
+/* Diagonal whitening statistics of C_Q ([note] Design 1): mu[g][l] = mean_i C_Q[g][i][l],
+ * rstd[g][l] = 1/sqrt(mean_i (C_Q[g][i][l] - mu)^2 + whiten_eps). */
+int lf_whiten_stats(const lf_attn_params* p, const float* CQ, float* mu, float* rstd, lf_stream_t stream);
+
+/* P[g][l][c] = rstd[g][l] * sum_k X[g][l][k] S[g][k][c]; rstd may be NULL (then 1). */
+int lf_landmark_mix(const lf_attn_params* p, const float* X, const float* S, const float* rstd, float* P,
+                    lf_stream_t stream);
+
+/* Y[g][i][c] = sum_l C_Q[g][i][l] P[g][l][c] - sum_l mu[g][l] P[g][l][c] + DWC(V)[g][i][c]
+ * ([note] Design 1 and flowchart nodes G, H, I). mu may be NULL (no whitening bias); dwc_w may be NULL. */
+int lf_out_gemm_dwc(const lf_attn_params* p, const float* CQ, const float* P, const float* mu, const void* V,
+                    const float* dwc_w, void* Y, lf_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LF_ATTN_H */

@@ -1,0 +1,318 @@
+// C ABI of liblf_attn: parameter validation, workspace planning and the launch sequence of the forward and
+// backward passes. Host code only; the kernels live in lf_fwd.hip, lf_ns.hip and lf_bwd.hip.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/lf_attn.h"
+#include "lf_internal.h"
+#include "lf_bwd_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Checks everything that can be checked without touching the device.
+int validate(const lf_attn_params* p) {
+  if (!p) return LF_EINVAL;
+  if (p->B < 1 || p->heads < 1 || p->H < 1 || p->W < 1 || p->d < 1 || p->r < 1) return LF_EINVAL;
+  if (p->H % p->r != 0 || p->W % p->r != 0) return LF_EINVAL;
+  if (!(p->lambda > 0.f) || !std::isfinite(p->lambda)) return LF_EINVAL;
+  if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return LF_EINVAL;
+  if (p->ns_iters < 0 || p->ns_iters > LF_NS_ITERS_MAX) return LF_EINVAL;
+  if (p->whiten != 0 && p->whiten != 1) return LF_EINVAL;
+  if (p->whiten == 1 && (!(p->whiten_eps > 0.f) || !std::isfinite(p->whiten_eps))) return LF_EINVAL;
+  if (p->dtype != LF_F32 && p->dtype != LF_BF16) return LF_EINVAL;
+  // Sizes: keep every element index inside int range for the per-slice arithmetic, and totals in size_t.
+  const int64_t N = static_cast<int64_t>(p->H) * p->W;
+  if (N > (1 << 24)) return LF_EUNSUPPORTED;
+  const int64_t G = static_cast<int64_t>(p->B) * p->heads;
+  if (G > (1 << 20)) return LF_EUNSUPPORTED;
+  if (p->d != 16 && p->d != 32 && p->d != 64 && p->d != 128) return LF_EUNSUPPORTED;
+  const int64_t m = static_cast<int64_t>(p->H / p->r) * (p->W / p->r);
+  if (m > LF_M_MAX) return LF_EUNSUPPORTED;
+  return LF_OK;
+}
+
+lf::Shape make_shape(const lf_attn_params* p) {
+  lf::Shape s;
+  s.G = p->B * p->heads;
+  s.heads = p->heads;
+  s.H = p->H;
+  s.W = p->W;
+  s.d = p->d;
+  s.r = p->r;
+  s.m = (p->H / p->r) * (p->W / p->r);
+  s.N = p->H * p->W;
+  s.dtype = p->dtype;
+  s.lambda = p->lambda;
+  s.eps = p->eps;
+  s.ns_iters = p->ns_iters;
+  s.whiten_eps = p->whiten_eps;
+  return s;
+}
+
+inline bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+lf_saved_layout saved_layout(const lf::Shape& s) {
+  const size_t G = s.G, N = s.N, m = s.m, d = s.d, K = s.ns_iters;
+  Carver c;
+  lf_saved_layout L;
+  L.L = c.take(4 * G * m * d);
+  L.CQ = c.take(4 * G * N * m);
+  L.CK = c.take(4 * G * N * m);
+  L.We = c.take(4 * G * m * m);
+  L.xs = c.take(4 * G * (K + 1) * m * m);
+  L.mu = c.take(4 * G * m);
+  L.rstd = c.take(4 * G * m);
+  L.S = c.take(4 * G * m * d);
+  L.P = c.take(4 * G * m * d);
+  L.alpha = c.take(4 * G);
+  L.total = c.off;
+  return L;
+}
+
+// Forward workspace. Without a saved buffer every intermediate lives here; with one, only X, the scaled P,
+// the C_K^T V partials and the Newton-Schulz scratch do.
+struct FwdWs {
+  size_t L, CQ, CK, We, X, S, P, Pw, mu, rstd, alpha, part, nstmp, total;
+};
+
+FwdWs fwd_ws(const lf::Shape& s) {
+  const size_t G = s.G, N = s.N, m = s.m, d = s.d;
+  int nsplit, rps;
+  lf::ckv_split(s, &nsplit, &rps);
+  Carver c;
+  FwdWs w;
+  w.L = c.take(4 * G * m * d);
+  w.CQ = c.take(4 * G * N * m);
+  w.CK = c.take(4 * G * N * m);
+  w.We = c.take(4 * G * m * m);
+  w.X = c.take(4 * G * m * m);
+  w.S = c.take(4 * G * m * d);
+  w.P = c.take(4 * G * m * d);
+  w.Pw = c.take(4 * G * m * d);
+  w.mu = c.take(4 * G * m);
+  w.rstd = c.take(4 * G * m);
+  w.alpha = c.take(4 * G);
+  w.part = c.take(nsplit > 1 ? 4 * G * static_cast<size_t>(nsplit) * m * d : 0);
+  w.nstmp = c.take(4 * lf::ns_tmp_floats(s));
+  w.total = c.off;
+  return w;
+}
+
+template <typename T>
+inline T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? LF_OK : LF_EHIP; }
+
+#define LF_TRY(expr)                        \
+  do {                                      \
+    const int _rc = hip_status(expr);       \
+    if (_rc != LF_OK) return _rc;           \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* lf_strerror(int code) {
+  switch (code) {
+    case LF_OK: return "ok";
+    case LF_EINVAL: return "invalid argument (shape, parameter, null or misaligned pointer)";
+    case LF_EWORKSPACE: return "workspace too small";
+    case LF_EUNSUPPORTED: return "unsupported configuration";
+    case LF_EHIP: return "HIP kernel launch failed";
+    default: return "unknown lf_attn status";
+  }
+}
+
+int lf_attn_query(const lf_attn_params* p, size_t* fwd_ws_bytes, size_t* saved_bytes, size_t* bwd_ws_bytes) {
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  const lf::Shape s = make_shape(p);
+  if (fwd_ws_bytes) *fwd_ws_bytes = fwd_ws(s).total;
+  if (saved_bytes) *saved_bytes = saved_layout(s).total;
+  if (bwd_ws_bytes) *bwd_ws_bytes = lf::bwd_ws_bytes(s);
+  return LF_OK;
+}
+
+int lf_attn_saved_layout(const lf_attn_params* p, lf_saved_layout* out) {
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  if (!out) return LF_EINVAL;
+  *out = saved_layout(make_shape(p));
+  return LF_OK;
+}
+
+int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w, void* Y,
+                void* saved, void* ws, size_t ws_bytes, lf_stream_t stream) {
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  if (!Q || !K || !V || !Y || !ws) return LF_EINVAL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(Y) || !aligned16(ws)) return LF_EINVAL;
+  if ((dwc_w && !aligned16(dwc_w)) || (saved && !aligned16(saved))) return LF_EINVAL;
+  if (Y == Q || Y == K || Y == V) return LF_EINVAL;
+  const lf::Shape s = make_shape(p);
+  const FwdWs w = fwd_ws(s);
+  if (ws_bytes < w.total) return LF_EWORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool wh = p->whiten == 1;
+
+  float *L, *CQ, *CK, *We, *xs, *mu, *rstd, *S, *Praw, *alpha;
+  if (saved) {
+    const lf_saved_layout sl = saved_layout(s);
+    L = at<float>(saved, sl.L);
+    CQ = at<float>(saved, sl.CQ);
+    CK = at<float>(saved, sl.CK);
+    We = at<float>(saved, sl.We);
+    xs = at<float>(saved, sl.xs);
+    mu = at<float>(saved, sl.mu);
+    rstd = at<float>(saved, sl.rstd);
+    S = at<float>(saved, sl.S);
+    Praw = at<float>(saved, sl.P);
+    alpha = at<float>(saved, sl.alpha);
+  } else {
+    L = at<float>(ws, w.L);
+    CQ = at<float>(ws, w.CQ);
+    CK = at<float>(ws, w.CK);
+    We = at<float>(ws, w.We);
+    xs = nullptr;
+    mu = at<float>(ws, w.mu);
+    rstd = at<float>(ws, w.rstd);
+    S = at<float>(ws, w.S);
+    Praw = nullptr;
+    alpha = at<float>(ws, w.alpha);
+  }
+  float* X = at<float>(ws, w.X);
+  float* P = at<float>(ws, w.Pw);
+  float* part = at<float>(ws, w.part);
+  float* nstmp = at<float>(ws, w.nstmp);
+
+  LF_TRY(lf::launch_landmark_pool(s, Q, L, st));
+  LF_TRY(lf::launch_laplace(s, Q, K, L, CQ, CK, We, st));
+  if (wh) LF_TRY(lf::launch_whiten_stats(s, CQ, mu, rstd, st));
+  LF_TRY(lf::launch_ns(s, We, X, xs, alpha, nullptr, nstmp, st));
+  LF_TRY(lf::launch_ckv(s, CK, V, part, S, st));
+  LF_TRY(lf::launch_mix(s, X, S, wh ? rstd : nullptr, P, Praw, st));
+  LF_TRY(lf::launch_out(s, CQ, P, wh ? mu : nullptr, V, dwc_w, Y, st));
+  return LF_OK;
+}
+
+int lf_attn_bwd(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
+                const void* saved, const void* dY, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
+                lf_stream_t stream) {
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  const lf::Shape s = make_shape(p);
+  if (s.m > 64 || s.d > 64) return LF_EUNSUPPORTED;
+  if (!Q || !K || !V || !saved || !dY || !dQ || !dK || !dV || !ws) return LF_EINVAL;
+  const void* ptrs[] = {Q, K, V, saved, dY, dQ, dK, dV, ws};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return LF_EINVAL;
+  if (dwc_w && !aligned16(dwc_w)) return LF_EINVAL;
+  if (ws_bytes < lf::bwd_ws_bytes(s)) return LF_EWORKSPACE;
+  const lf_saved_layout sl = saved_layout(s);
+  lf::SavedPtrs sp;
+  const char* sb = static_cast<const char*>(saved);
+  sp.L = reinterpret_cast<const float*>(sb + sl.L);
+  sp.CQ = reinterpret_cast<const float*>(sb + sl.CQ);
+  sp.CK = reinterpret_cast<const float*>(sb + sl.CK);
+  sp.We = reinterpret_cast<const float*>(sb + sl.We);
+  sp.xs = reinterpret_cast<const float*>(sb + sl.xs);
+  sp.mu = reinterpret_cast<const float*>(sb + sl.mu);
+  sp.rstd = reinterpret_cast<const float*>(sb + sl.rstd);
+  sp.S = reinterpret_cast<const float*>(sb + sl.S);
+  sp.P = reinterpret_cast<const float*>(sb + sl.P);
+  sp.alpha = reinterpret_cast<const float*>(sb + sl.alpha);
+  return hip_status(lf::launch_backward(s, p->whiten == 1, Q, K, V, dwc_w, sp, dY, dQ, dK, dV, ws,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+// ---- stage entry points ----
+
+int lf_landmark_pool(const lf_attn_params* p, const void* Q, float* L, lf_stream_t stream) {
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  if (!Q || !L || !aligned16(Q) || !aligned16(L)) return LF_EINVAL;
+  return hip_status(lf::launch_landmark_pool(make_shape(p), Q, L, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int lf_laplace_l1_exp(const lf_attn_params* p, const void* Q, const void* K, const float* L, float* CQ, float* CK,
+                      float* We, lf_stream_t stream) {
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  const void* ptrs[] = {Q, K, L, CQ, CK, We};
+  for (const void* ptr : ptrs)
+    if (!ptr || !aligned16(ptr)) return LF_EINVAL;
+  return hip_status(lf::launch_laplace(make_shape(p), Q, K, L, CQ, CK, We, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int lf_ns_pinv(const lf_attn_params* p, const float* We, float* X, float* xs, float* alpha_out, float* resid,
+               void* ws, size_t ws_bytes, lf_stream_t stream) {
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  if (!We || !X || !aligned16(We) || !aligned16(X)) return LF_EINVAL;
+  if ((xs && !aligned16(xs)) || (alpha_out && !aligned16(alpha_out)) || (resid && !aligned16(resid)))
+    return LF_EINVAL;
+  const lf::Shape s = make_shape(p);
+  const FwdWs w = fwd_ws(s);
+  if (lf::ns_tmp_floats(s) > 0 && (!ws || ws_bytes < w.total)) return LF_EWORKSPACE;
+  float* tmp = ws ? at<float>(ws, w.nstmp) : nullptr;
+  return hip_status(lf::launch_ns(s, We, X, xs, alpha_out, resid, tmp, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int lf_ckv_reduce(const lf_attn_params* p, const float* CK, const void* V, float* S, void* ws, size_t ws_bytes,
+                  lf_stream_t stream) {
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  if (!CK || !V || !S || !aligned16(CK) || !aligned16(V) || !aligned16(S)) return LF_EINVAL;
+  const lf::Shape s = make_shape(p);
+  const FwdWs w = fwd_ws(s);
+  if (!ws || ws_bytes < w.total) return LF_EWORKSPACE;
+  return hip_status(lf::launch_ckv(s, CK, V, at<float>(ws, w.part), S, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int lf_whiten_stats(const lf_attn_params* p, const float* CQ, float* mu, float* rstd, lf_stream_t stream) {
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  if (!CQ || !mu || !rstd || !aligned16(CQ) || !aligned16(mu) || !aligned16(rstd)) return LF_EINVAL;
+  if (!(p->whiten_eps > 0.f)) return LF_EINVAL;
+  return hip_status(lf::launch_whiten_stats(make_shape(p), CQ, mu, rstd, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int lf_landmark_mix(const lf_attn_params* p, const float* X, const float* S, const float* rstd, float* P,
+                    lf_stream_t stream) {
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  if (!X || !S || !P || !aligned16(X) || !aligned16(S) || !aligned16(P)) return LF_EINVAL;
+  if (rstd && !aligned16(rstd)) return LF_EINVAL;
+  return hip_status(lf::launch_mix(make_shape(p), X, S, rstd, P, nullptr, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int lf_out_gemm_dwc(const lf_attn_params* p, const float* CQ, const float* P, const float* mu, const void* V,
+                    const float* dwc_w, void* Y, lf_stream_t stream) {
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  if (!CQ || !P || !V || !Y || !aligned16(CQ) || !aligned16(P) || !aligned16(V) || !aligned16(Y)) return LF_EINVAL;
+  if ((mu && !aligned16(mu)) || (dwc_w && !aligned16(dwc_w))) return LF_EINVAL;
+  return hip_status(
+      lf::launch_out(make_shape(p), CQ, P, mu, V, dwc_w, Y, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,501 @@
+// Backward pass of the LaplacianFormer attention block for gfx950 (m <= 64, d <= 64).
+//
+// [note] = papernotes.org ICLR 2026 reading note "LaplacianFormer：用拉普拉斯核重新思考线性注意力";
+// [abs]  = the arXiv 2604.20368 abstract, which states that the kernel and the solver have forward and backward
+//          implementations.
+// The gradient of k(x, l) = exp(-||x - l||_1 / lambda) is -(1/lambda) sign(x - l) k in x and +(1/lambda)
+// sign(x - l) k in l ([note] motivation, "core idea", with the minus sign the page drops restored; sign(0) = 0).
+// alpha of the Newton-Schulz start is held constant.
+//
+// Per slice, with A_hat = C_Q (or its whitened form), S = C_K^T V, P = X_K S, Y = A_hat P + DWC(V):
+//   dP = A_hat^T dY          dA_hat = dY P^T        dX_K = dP S^T      dS = X_K^T dP
+//   dV = C_K dS + DWC^T(dY)  dC_K = V dS^T
+//   whitening: dC_Q = rstd (dA_hat - mean_i dA_hat - A_hat mean_i(dA_hat A_hat))
+//   Newton-Schulz reverse (X_{k+1} = 2 X_k - X_k W X_k):  dW -= X_k^T G X_k^T ; G <- 2G - G (W X_k)^T - (X_k W)^T G
+//   and finally dW += alpha G^T (X_0 = alpha W^T).
+//   Gq = dC_Q C_Q / lambda, Gk = dC_K C_K / lambda, Gw = dW W / lambda (off the diagonal)
+//   dQ = -sum_l Gq sign(Q - L) ; dK = -sum_l Gk sign(K - L)
+//   dL = sum_i Gq sign(Q - L) + sum_j Gk sign(K - L) - sum_l' (Gw + Gw^T) sign(L - L')
+//   dQ_i += dL_{owner(i)} / r^2 (landmarks are r x r block means of Q).
+// Both column means of the whitening backward come from m x d products: mean_i dA_hat[:, l] = (1/N) P_l . (1^T dY)
+// and mean_i (dA_hat A_hat)[:, l] = (1/N) P_l . dP_l, so no extra pass over the N x m matrices is needed.
+#include "lf_bwd_internal.h"
+#include "lf_device.h"
+
+namespace lf {
+
+static inline int cdiv(long a, long b) { return static_cast<int>((a + b - 1) / b); }
+
+__device__ __forceinline__ float sgnf(float x) { return x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f); }
+
+namespace {
+
+struct BwdWs {
+  size_t T1, part, dX, dS, stats, dWe, dLW, Gq, Gk, dLpart, dL, total;
+  int nsplitL, rpsL, nlb;
+};
+
+constexpr size_t kAlign = 256;
+inline size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+BwdWs plan(const Shape& s) {
+  const size_t G = s.G, N = s.N, m = s.m, d = s.d;
+  int nsplit, rps;
+  ckv_split(s, &nsplit, &rps);
+  BwdWs w;
+  const int lpb = 256 / s.d;
+  w.nlb = cdiv(s.m, lpb);
+  int want = cdiv(512, static_cast<long>(s.G) * w.nlb);
+  const int maxs = cdiv(s.N, 64);
+  if (want > maxs) want = maxs;
+  if (want < 1) want = 1;
+  w.rpsL = cdiv(s.N, want);
+  w.nsplitL = cdiv(s.N, w.rpsL);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = al(off + bytes);
+    return o;
+  };
+  w.T1 = take(4 * G * (m + 1) * d);
+  w.part = take(nsplit > 1 ? 4 * G * nsplit * (m + 1) * d : 0);
+  w.dX = take(4 * G * m * m);
+  w.dS = take(4 * G * m * d);
+  w.stats = take(4 * G * 2 * m);
+  w.dWe = take(4 * G * m * m);
+  w.dLW = take(4 * G * m * d);
+  w.Gq = take(4 * G * N * m);
+  w.Gk = take(4 * G * N * m);
+  w.dLpart = take(4 * G * static_cast<size_t>(w.nsplitL) * m * d);
+  w.dL = take(4 * G * m * d);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------------------
+// Small per-slice products: dP from T1 = [C_Q | 1]^T dY, then dX = dP S^T, dS = X_K^T dP and the two whitening
+// column means. m x m x d work per slice, on the VALU.
+// ---------------------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_small1(const float* __restrict__ T1, const float* __restrict__ S,
+                                                    const float* __restrict__ P, const float* __restrict__ xs,
+                                                    const float* __restrict__ mu, const float* __restrict__ rstd,
+                                                    float* __restrict__ dX, float* __restrict__ dS,
+                                                    float* __restrict__ stats, int m, int K, int N, int whiten) {
+  __shared__ float sT1[65 * D];
+  __shared__ float sS[64 * D];
+  __shared__ float sP[64 * D];
+  __shared__ float sdP[64 * D];
+  __shared__ float sX[64 * 64];
+  const int g = blockIdx.x, tid = threadIdx.x;
+  const size_t md = static_cast<size_t>(m) * D, mm = static_cast<size_t>(m) * m;
+  const float* t1 = T1 + static_cast<size_t>(g) * (m + 1) * D;
+  for (int idx = tid; idx < (m + 1) * D; idx += 256) sT1[idx] = t1[idx];
+  for (int idx = tid; idx < m * D; idx += 256) {
+    sS[idx] = S[g * md + idx];
+    sP[idx] = P[g * md + idx];
+  }
+  const float* xk = xs + (static_cast<size_t>(g) * (K + 1) + K) * mm;
+  for (int idx = tid; idx < m * m; idx += 256) sX[idx] = xk[idx];
+  __syncthreads();
+  for (int idx = tid; idx < m * D; idx += 256) {
+    const int l = idx / D, c = idx % D;
+    float v = sT1[idx];
+    if (whiten) v = rstd[g * m + l] * (v - mu[g * m + l] * sT1[m * D + c]);
+    sdP[idx] = v;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < m * m; idx += 256) {
+    const int l = idx / m, k = idx % m;
+    float acc = 0.f;
+    for (int c = 0; c < D; ++c) acc += sdP[l * D + c] * sS[k * D + c];
+    dX[g * mm + idx] = acc;
+  }
+  for (int idx = tid; idx < m * D; idx += 256) {
+    const int l = idx / D, c = idx % D;
+    float acc = 0.f;
+    for (int k = 0; k < m; ++k) acc += sX[k * m + l] * sdP[k * D + c];
+    dS[g * md + idx] = acc;
+  }
+  if (whiten) {
+    for (int l = tid; l < m; l += 256) {
+      float a = 0.f, b = 0.f;
+      for (int c = 0; c < D; ++c) {
+        a += sT1[m * D + c] * sP[l * D + c];
+        b += sP[l * D + c] * sdP[l * D + c];
+      }
+      stats[static_cast<size_t>(g) * 2 * m + l] = a / static_cast<float>(N);
+      stats[static_cast<size_t>(g) * 2 * m + m + l] = b / static_cast<float>(N);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Newton-Schulz reverse chain on fp32 MFMA, one block per slice, everything in LDS (64 x 64 padded).
+// ---------------------------------------------------------------------------------------------------------
+constexpr int BL = 66;
+
+template <bool TA, bool TB>
+__device__ __forceinline__ void mm64(const float* __restrict__ sA, const float* __restrict__ sB, int ksteps, int wv,
+                                     int ln, int ntile, f32x4 acc[4]) {
+  const int i = wv * 16 + (ln & 15);
+  for (int ks = 0; ks < ksteps; ++ks) {
+    const int k = ks * 4 + (ln >> 4);
+    const float a = TA ? sA[k * BL + i] : sA[i * BL + k];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < ntile) {
+        const int j = t * 16 + (ln & 15);
+        const float b = TB ? sB[j * BL + k] : sB[k * BL + j];
+        acc[t] = mfma16x16x4(a, b, acc[t]);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void zero4(f32x4 acc[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+__device__ __forceinline__ void store4(float* __restrict__ sC, const f32x4 acc[4], int wv, int ln, int ntile) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (t < ntile) {
+      const int j = t * 16 + (ln & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sC[(wv * 16 + 4 * (ln >> 4) + r) * BL + j] = acc[t][r];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_bwd_ns(const float* __restrict__ We, const float* __restrict__ xs,
+                                                const float* __restrict__ alpha, const float* __restrict__ dX,
+                                                float* __restrict__ dWe, int m, int K) {
+  __shared__ float sW[64 * BL];
+  __shared__ float sXk[64 * BL];
+  __shared__ float sG[2][64 * BL];
+  __shared__ float sA1[64 * BL];
+  __shared__ float sA2[64 * BL];
+  __shared__ float sZ[64 * BL];
+  const int g = blockIdx.x, tid = threadIdx.x, wv = wave_id(), ln = lane_id();
+  const size_t mm = static_cast<size_t>(m) * m;
+  for (int idx = tid; idx < 64 * 64; idx += 256) {
+    const int i = idx >> 6, j = idx & 63;
+    const bool in = i < m && j < m;
+    sW[i * BL + j] = in ? We[g * mm + i * m + j] : 0.f;
+    sG[0][i * BL + j] = in ? dX[g * mm + i * m + j] : 0.f;
+  }
+  const int ksteps = (m + 3) / 4, ntile = (m + 15) / 16;
+  const bool active = wv < ntile;
+  f32x4 dacc[4], acc[4];
+  zero4(dacc);
+  int cur = 0;
+  for (int k = K - 1; k >= 0; --k) {
+    const float* xk = xs + (static_cast<size_t>(g) * (K + 1) + k) * mm;
+    __syncthreads();
+    for (int idx = tid; idx < 64 * 64; idx += 256) {
+      const int i = idx >> 6, j = idx & 63;
+      sXk[i * BL + j] = (i < m && j < m) ? xk[i * m + j] : 0.f;
+    }
+    __syncthreads();
+    if (active) {
+      zero4(acc);
+      mm64<false, false>(sW, sXk, ksteps, wv, ln, ntile, acc);  // A1 = W X_k
+      store4(sA1, acc, wv, ln, ntile);
+      zero4(acc);
+      mm64<false, false>(sXk, sW, ksteps, wv, ln, ntile, acc);  // A2 = X_k W
+      store4(sA2, acc, wv, ln, ntile);
+      zero4(acc);
+      mm64<true, false>(sXk, sG[cur], ksteps, wv, ln, ntile, acc);  // Z = X_k^T G
+      store4(sZ, acc, wv, ln, ntile);
+    }
+    __syncthreads();
+    const int nxt = cur ^ 1;
+    if (active) {
+      zero4(acc);
+      mm64<false, true>(sZ, sXk, ksteps, wv, ln, ntile, acc);  // Z X_k^T
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dacc[t] -= acc[t];
+      zero4(acc);
+      mm64<false, true>(sG[cur], sA1, ksteps, wv, ln, ntile, acc);  // G A1^T
+      mm64<true, false>(sA2, sG[cur], ksteps, wv, ln, ntile, acc);  // + A2^T G
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < ntile) {
+          const int j = t * 16 + (ln & 15);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = wv * 16 + 4 * (ln >> 4) + r;
+            sG[nxt][i * BL + j] = 2.f * sG[cur][i * BL + j] - acc[t][r];
+          }
+        }
+      }
+    }
+    cur = nxt;
+  }
+  __syncthreads();
+  if (active) {
+    const float a = alpha[g];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < ntile) {
+        const int j = t * 16 + (ln & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = wv * 16 + 4 * (ln >> 4) + r;
+          if (i < m && j < m) dWe[g * mm + i * m + j] = dacc[t][r] + a * sG[cur][j * BL + i];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Landmark-kernel part of dL: dLW[l][c] = -sum_{l' != l} (Gw[l][l'] + Gw[l'][l]) sign(L[l][c] - L[l'][c]).
+// ---------------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bwd_wpart(const float* __restrict__ L, const float* __restrict__ We,
+                                                   const float* __restrict__ dWe, float* __restrict__ dLW, int m,
+                                                   int D, float inv_lam) {
+  const int g = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= m * D) return;
+  const int l = t / D, c = t % D;
+  const size_t mm = static_cast<size_t>(m) * m;
+  const float* Lg = L + static_cast<size_t>(g) * m * D;
+  const float* wg = We + g * mm;
+  const float* dw = dWe + g * mm;
+  const float ll = Lg[t];
+  float acc = 0.f;
+  for (int l2 = 0; l2 < m; ++l2) {
+    if (l2 == l) continue;
+    const float gw = (dw[l * m + l2] * wg[l * m + l2] + dw[l2 * m + l] * wg[l2 * m + l]) * inv_lam;
+    acc -= gw * sgnf(ll - Lg[l2 * D + c]);
+  }
+  dLW[static_cast<size_t>(g) * m * D + t] = acc;
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Row gradients of the kernel matrices on fp32 MFMA: dA_hat = dY P^T (side 0) and dC_K = V dS^T (side 1),
+// 64 tokens x m landmarks per block, K = d. The epilogue applies the whitening backward and the kernel
+// derivative factor: Gq = dC_Q C_Q / lambda, Gk = dC_K C_K / lambda.
+// ---------------------------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, const T* __restrict__ V,
+                                                     const float* __restrict__ P, const float* __restrict__ dS,
+                                                     const float* __restrict__ CQ, const float* __restrict__ CK,
+                                                     const float* __restrict__ mu, const float* __restrict__ rstd,
+                                                     const float* __restrict__ stats, float* __restrict__ Gq,
+                                                     float* __restrict__ Gk, int N, int m, float inv_lam,
+                                                     int whiten) {
+  constexpr int LDA = D + 2;  // 2 mod 4 with LDA/2 odd: conflict-free A-style reads
+  constexpr int LDB = 80;     // 16 mod 32
+  __shared__ float sA[64 * LDA];
+  __shared__ float sB[D * LDB];
+  const int side = blockIdx.z, g = blockIdx.y, i0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
+  const T* A = (side == 0 ? dY : V) + static_cast<size_t>(g) * N * D;
+  const float* Bm = (side == 0 ? P : dS) + static_cast<size_t>(g) * m * D;
+  for (int idx = tid; idx < 64 * D; idx += 256) {
+    const int rr = idx / D, c = idx % D;
+    sA[rr * LDA + c] = (i0 + rr < N) ? to_f32(A[static_cast<size_t>(i0 + rr) * D + c]) : 0.f;
+  }
+  for (int idx = tid; idx < D * 64; idx += 256) {
+    const int l = idx / D, c = idx % D;
+    sB[c * LDB + l] = (l < m) ? Bm[static_cast<size_t>(l) * D + c] : 0.f;
+  }
+  __syncthreads();
+  const int ntile = (m + 15) / 16;
+  f32x4 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ks = 0; ks < D / 4; ++ks) {
+    const int k = ks * 4 + (ln >> 4);
+    const float a = sA[(wv * 16 + (ln & 15)) * LDA + k];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < ntile) acc[t] = mfma16x16x4(a, sB[k * LDB + t * 16 + (ln & 15)], acc[t]);
+    }
+  }
+  const float* cm = (side == 0 ? CQ : CK) + static_cast<size_t>(g) * N * m;
+  float* out = (side == 0 ? Gq : Gk) + static_cast<size_t>(g) * N * m;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (t >= ntile) continue;
+    const int l = t * 16 + (ln & 15);
+    if (l >= m) continue;
+    float mu_l = 0.f, rs_l = 1.f, mA = 0.f, mAA = 0.f;
+    if (side == 0 && whiten) {
+      mu_l = mu[static_cast<size_t>(g) * m + l];
+      rs_l = rstd[static_cast<size_t>(g) * m + l];
+      mA = stats[static_cast<size_t>(g) * 2 * m + l];
+      mAA = stats[static_cast<size_t>(g) * 2 * m + m + l];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + wv * 16 + 4 * (ln >> 4) + r;
+      if (i >= N) continue;
+      const float c = cm[static_cast<size_t>(i) * m + l];
+      float v = acc[t][r];
+      if (side == 0 && whiten) {
+        const float ahat = (c - mu_l) * rs_l;
+        v = rs_l * (v - mA - ahat * mAA);
+      }
+      out[static_cast<size_t>(i) * m + l] = v * c * inv_lam;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// dL partials: sum over a range of token rows of Gq sign(Q - L) + Gk sign(K - L). Thread = (landmark, channel);
+// with d = 64 every wave owns one landmark, so the Gq/Gk values it reads are wave-uniform.
+// ---------------------------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_bwd_dl_partial(const T* __restrict__ Q, const T* __restrict__ K,
+                                                        const float* __restrict__ L, const float* __restrict__ Gq,
+                                                        const float* __restrict__ Gk, float* __restrict__ part, int N,
+                                                        int m, int nsplit, int rps, int nlb) {
+  constexpr int LPB = 256 / D;
+  int b = blockIdx.x;
+  const int lb = b % nlb;
+  b /= nlb;
+  const int s = b % nsplit, g = b / nsplit;
+  const int ll = threadIdx.x / D, c = threadIdx.x % D;
+  const int l = lb * LPB + ll;
+  if (l >= m) return;
+  const float lv = L[(static_cast<size_t>(g) * m + l) * D + c];
+  const int r0 = s * rps, r1 = min(N, r0 + rps);
+  const size_t base = static_cast<size_t>(g) * N;
+  float acc = 0.f;
+  for (int i = r0; i < r1; ++i) {
+    const float gq = Gq[(base + i) * m + l];
+    const float gk = Gk[(base + i) * m + l];
+    acc += gq * sgnf(to_f32(Q[(base + i) * D + c]) - lv);
+    acc += gk * sgnf(to_f32(K[(base + i) * D + c]) - lv);
+  }
+  part[((static_cast<size_t>(g) * nsplit + s) * m + l) * D + c] = acc;
+}
+
+__global__ __launch_bounds__(256) void k_bwd_dl_finalize(const float* __restrict__ part, const float* __restrict__ dLW,
+                                                         float* __restrict__ dL, int G, int nsplit, int md) {
+  const size_t t = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= static_cast<size_t>(G) * md) return;
+  const size_t g = t / md, e = t % md;
+  float acc = 0.f;
+  for (int s = 0; s < nsplit; ++s) acc += part[(g * nsplit + s) * md + e];
+  dL[t] = acc + dLW[t];
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Token rows: dQ_i = -sum_l Gq[i][l] sign(Q_i - L_l) + dL_owner(i) / r^2 ; dK_j = -sum_l Gk[j][l] sign(K_j - L_l).
+// One thread per row, row and accumulator in VGPRs; the landmark row is wave-uniform (scalar loads).
+// ---------------------------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_bwd_rows(const T* __restrict__ Q, const T* __restrict__ K,
+                                                 const float* __restrict__ L, const float* __restrict__ Gq,
+                                                 const float* __restrict__ Gk, const float* __restrict__ dL,
+                                                 T* __restrict__ dQ, T* __restrict__ dK, int N, int m, int W, int r) {
+  const int side = blockIdx.z, g = blockIdx.y;
+  const int row = blockIdx.x * 64 + static_cast<int>(threadIdx.x);
+  if (row >= N) return;
+  const T* X = (side == 0 ? Q : K) + (static_cast<size_t>(g) * N + row) * D;
+  const float* gx = (side == 0 ? Gq : Gk) + (static_cast<size_t>(g) * N + row) * m;
+  const float* __restrict__ Lg = L + static_cast<size_t>(g) * m * D;
+  float x[D], acc[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    x[c] = to_f32(X[c]);
+    acc[c] = 0.f;
+  }
+  for (int l = 0; l < m; ++l) {
+    const float gl = gx[l];
+    const float* __restrict__ lp = Lg + static_cast<size_t>(l) * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) acc[c] = fmaf(-gl, sgnf(x[c] - lp[c]), acc[c]);
+  }
+  if (side == 0) {
+    const int yy = row / W, xx = row % W;
+    const int owner = (yy / r) * (W / r) + xx / r;
+    const float inv = 1.f / static_cast<float>(r * r);
+    const float* dl = dL + (static_cast<size_t>(g) * m + owner) * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) acc[c] += dl[c] * inv;
+  }
+  T* out = (side == 0 ? dQ : dK) + (static_cast<size_t>(g) * N + row) * D;
+#pragma unroll
+  for (int c = 0; c < D; ++c) out[c] = from_f32<T>(acc[c]);
+}
+
+// ---------------------------------------------------------------------------------------------------------
+size_t bwd_ws_bytes(const Shape& s) {
+  if (s.m > 64 || s.d > 64) return 0;
+  return plan(s).total;
+}
+
+template <typename T, int D>
+static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void* Kv, const void* Vv, const float* w,
+                        const SavedPtrs& sp, const void* dYv, void* dQv, void* dKv, void* dVv, void* ws,
+                        hipStream_t st) {
+  const BwdWs p = plan(s);
+  char* b = static_cast<char*>(ws);
+  float* T1 = reinterpret_cast<float*>(b + p.T1);
+  float* part = reinterpret_cast<float*>(b + p.part);
+  float* dX = reinterpret_cast<float*>(b + p.dX);
+  float* dS = reinterpret_cast<float*>(b + p.dS);
+  float* stats = reinterpret_cast<float*>(b + p.stats);
+  float* dWe = reinterpret_cast<float*>(b + p.dWe);
+  float* dLW = reinterpret_cast<float*>(b + p.dLW);
+  float* Gq = reinterpret_cast<float*>(b + p.Gq);
+  float* Gk = reinterpret_cast<float*>(b + p.Gk);
+  float* dLpart = reinterpret_cast<float*>(b + p.dLpart);
+  float* dL = reinterpret_cast<float*>(b + p.dL);
+  const T* Q = static_cast<const T*>(Qv);
+  const T* K = static_cast<const T*>(Kv);
+  const T* V = static_cast<const T*>(Vv);
+  const T* dY = static_cast<const T*>(dYv);
+  T* dQ = static_cast<T*>(dQv);
+  T* dK = static_cast<T*>(dKv);
+  const float inv_lam = static_cast<float>(1.0 / static_cast<double>(s.lambda));
+  const int wh = whiten ? 1 : 0;
+
+  hipError_t e = launch_ckv_general(s, sp.CQ, 1, dY, part, T1, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_bwd_small1<D>, dim3(s.G), dim3(256), 0, st, T1, sp.S, sp.P, sp.xs, sp.mu, sp.rstd, dX, dS,
+                     stats, s.m, s.ns_iters, s.N, wh);
+  hipLaunchKernelGGL(k_bwd_ns, dim3(s.G), dim3(256), 0, st, sp.We, sp.xs, sp.alpha, dX, dWe, s.m, s.ns_iters);
+  hipLaunchKernelGGL(k_bwd_wpart, dim3(cdiv(static_cast<long>(s.m) * D, 256), s.G), dim3(256), 0, st, sp.L, sp.We,
+                     dWe, dLW, s.m, D, inv_lam);
+  hipLaunchKernelGGL((k_bwd_rowgrad<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(256), 0, st, dY, V, sp.P, dS, sp.CQ,
+                     sp.CK, sp.mu, sp.rstd, stats, Gq, Gk, s.N, s.m, inv_lam, wh);
+  e = launch_out_adjoint(s, sp.CK, dS, dY, w, dVv, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_bwd_dl_partial<T, D>), dim3(s.G * p.nsplitL * p.nlb), dim3(256), 0, st, Q, K, sp.L, Gq, Gk,
+                     dLpart, s.N, s.m, p.nsplitL, p.rpsL, p.nlb);
+  const int md = s.m * D;
+  hipLaunchKernelGGL(k_bwd_dl_finalize, dim3(cdiv(static_cast<long>(s.G) * md, 256)), dim3(256), 0, st, dLpart, dLW,
+                     dL, s.G, p.nsplitL, md);
+  hipLaunchKernelGGL((k_bwd_rows<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(64), 0, st, Q, K, sp.L, Gq, Gk, dL, dQ, dK,
+                     s.N, s.m, s.W, s.r);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t bwd_d(const Shape& s, bool whiten, const void* Q, const void* K, const void* V, const float* w,
+                        const SavedPtrs& sp, const void* dY, void* dQ, void* dK, void* dV, void* ws, hipStream_t st) {
+  switch (s.d) {
+    case 16: return bwd_t<T, 16>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st);
+    case 32: return bwd_t<T, 32>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st);
+    default: return bwd_t<T, 64>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st);
+  }
+}
+
+hipError_t launch_backward(const Shape& s, bool whiten, const void* Q, const void* K, const void* V, const float* w,
+                           const SavedPtrs& sp, const void* dY, void* dQ, void* dK, void* dV, void* ws,
+                           hipStream_t st) {
+  if (s.dtype == 1) return bwd_d<bf16_t>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st);
+  return bwd_d<float>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st);
+}
+
+}  // namespace lf

@@ -1,0 +1,44 @@
+// Host-side launch interface between the C ABI layer (lf_api.cpp) and the kernel translation units.
+// Every launcher enqueues on `stream` and returns hipGetLastError()'s status; shapes were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lf {
+
+struct Shape {
+  int G, heads, H, W, d, r, m, N;
+  int dtype;  // 0 = float32, 1 = bf16
+  float lambda, eps;
+  int ns_iters;
+  float whiten_eps;
+};
+
+// Number of row splits of the C_K^T V reduction, and the rows each split covers (a multiple of 64).
+void ckv_split(const Shape& s, int* nsplit, int* rows_per_split);
+
+hipError_t launch_landmark_pool(const Shape& s, const void* Q, float* L, hipStream_t st);
+hipError_t launch_laplace(const Shape& s, const void* Q, const void* K, const float* L, float* CQ, float* CK,
+                          float* We, hipStream_t st);
+hipError_t launch_whiten_stats(const Shape& s, const float* CQ, float* mu, float* rstd, hipStream_t st);
+hipError_t launch_ckv(const Shape& s, const float* CK, const void* V, float* partial, float* S, hipStream_t st);
+// Same reduction with an optional appended column of ones in C (ones = 1): S gets m + ones rows.
+// `partial` must hold G * nsplit * (m + ones) * d floats.
+hipError_t launch_ckv_general(const Shape& s, const float* C, int ones, const void* V, float* partial, float* S,
+                              hipStream_t st);
+hipError_t launch_mix(const Shape& s, const float* X, const float* S, const float* rstd, float* P, float* Praw,
+                      hipStream_t st);
+hipError_t launch_out(const Shape& s, const float* CQ, const float* P, const float* mu, const void* V,
+                      const float* w, void* Y, hipStream_t st);
+// out = C P + DWC^T(U): the output kernel with the 3x3 filter rotated by 180 degrees (adjoint stencil).
+hipError_t launch_out_adjoint(const Shape& s, const float* C, const float* P, const void* U, const float* w, void* out,
+                              hipStream_t st);
+
+// Newton-Schulz. `tmp` is a [G][m][m] float32 scratch (used when m > 64); xs may be null.
+size_t ns_tmp_floats(const Shape& s);
+hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float* alpha, float* resid, float* tmp,
+                     hipStream_t st);
+
+}  // namespace lf

@@ -1,0 +1,203 @@
+"""GPU parity of the forward pass: every stage and the whole block against the fp64 oracle, through the C ABI.
+
+Bars: relative Frobenius error <= 1e-4 for float32 inputs and <= 2e-2 for bf16 inputs (fp32 accumulation), on the
+attention branch alone (no DWC) and on the full output separately. Stage inputs are the oracle's own values rounded
+to float32, so that each kernel is checked in isolation.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import (dev, gpu_forward, host, inputs, note, oparams, oracle_forward, params, relF, tol,
+                      upload)
+from laplacian_nystr_vit_amd import lf
+from laplacian_nystr_vit_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+# The five workload shapes plus edge cases: m = 1; N < 64 with several heads (channel h*d + c); a ragged grid with
+# m = 99 > 64 (multi-launch Newton-Schulz with ragged tiles) and d = 128; no NS steps; bf16 at the stage-1 shape;
+# whitening on a small grid; N = 196 tokens that end in a ragged 64-row tile.
+MAIN = [WL.TINY, WL.TINY_R1, WL.PVT_S1, WL.PVT_S3, WL.HIRES_BF16, WL.TRAIN_S1]
+EDGE = [
+    WL.TINY.replace(name="m1_8x8_r8", r=8),
+    WL.TINY.replace(name="ragged_10x6_d32_h3", B=2, heads=3, H=10, W=6, d=32, r=2),
+    WL.TINY.replace(name="ragged_18x22_d128_m99", H=18, W=22, d=128, r=2, qk_dist="student_t"),
+    WL.TINY.replace(name="ns_iters0", ns_iters=0),
+    WL.PVT_S1.replace(name="s1_bf16_B2", B=2, dtype=WL.BF16),
+    WL.TINY.replace(name="whiten_12x12_d16_B2", B=2, H=12, W=12, r=3, whiten=True),
+    WL.PVT_S3.replace(name="s3_B2_h5", B=2),
+    WL.TINY.replace(name="d64_20x20_m100_bf16", H=20, W=20, d=64, r=2, dtype=WL.BF16, qk_dist="student_t"),
+]
+ALL = MAIN + EDGE
+
+
+@pytest.mark.parametrize("wl", ALL, ids=lambda w: w.name)
+def test_forward_end_to_end(wl):
+    note(f"[gpu] forward {wl.name}")
+    ref = oracle_forward(wl)
+    Y, sv, p = gpu_forward(wl, dwc=True, save=True)
+    Ya, _, _ = gpu_forward(wl, dwc=False, save=False)
+    e_full = relF(host(Y), ref["Y"])
+    e_attn = relF(host(Ya), ref["Yattn"])
+    G = wl.G
+    worst = max(relF(host(Ya).reshape(G, -1)[g], ref["Yattn"].reshape(G, -1)[g]) for g in range(G))
+    note(f"    relF full={e_full:.3e} attn={e_attn:.3e} worst-slice attn={worst:.3e}")
+    assert e_full <= tol(wl)
+    assert e_attn <= tol(wl)
+    # intermediates the forward kept in the saved buffer
+    rs = lambda a: np.asarray(a).reshape((G,) + np.asarray(a).shape[2:])
+    assert relF(host(sv["L"]), rs(ref["L"])) <= 1e-6
+    assert relF(host(sv["CQ"]), rs(ref["CQ"])) <= 1e-5
+    assert relF(host(sv["CK"]), rs(ref["CK"])) <= 1e-5
+    assert relF(host(sv["We"]), rs(ref["We"])) <= 1e-5
+    Xk = host(sv["xs"])[:, wl.ns_iters]
+    assert relF(Xk, rs(ref["X"])) <= tol(wl)
+    assert relF(host(sv["S"]), rs(ref["S"])) <= tol(wl)
+    assert relF(host(sv["P"]), rs(ref["P"])) <= tol(wl)
+    if wl.whiten:
+        assert relF(host(sv["mu"]), rs(ref["mu"])) <= 1e-5
+        assert relF(host(sv["rstd"]), rs(ref["rstd"])) <= 1e-5
+
+
+@pytest.mark.parametrize("wl", [WL.TINY, WL.PVT_S1, WL.PVT_S3, WL.HIRES_BF16], ids=lambda w: w.name)
+def test_forward_is_deterministic(wl):
+    note(f"[gpu] determinism {wl.name}")
+    Y1, _, _ = gpu_forward(wl, save=False)
+    Y2, _, _ = gpu_forward(wl, save=False)
+    assert torch.equal(Y1, Y2)
+
+
+# ------------------------------------------------------------------------------------------------ stages alone
+def _f32(x):
+    return dev(np.ascontiguousarray(np.asarray(x, dtype=np.float32)))
+
+
+def _r32(x):
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("wl", [WL.TINY, WL.PVT_S1, WL.HIRES_BF16, EDGE[1]], ids=lambda w: w.name)
+def test_stage_pool_and_laplace(wl):
+    note(f"[gpu] stages pool+laplace {wl.name}")
+    p = params(wl)
+    inp = inputs(wl)
+    t = upload(wl)
+    G, N, m, d = p.G, p.N, p.m, p.d
+    L = torch.empty(G * m * d, device="cuda")
+    lf.lf_landmark_pool(p, t["Q"], L)
+    Lref = np.stack([O.landmark_pool(q, wl.H, wl.W, wl.r) for q in inp["Q"].reshape(G, N, d)])
+    assert relF(host(L).reshape(G, m, d), Lref) <= 1e-6
+    # laplace on the oracle's landmarks rounded to float32
+    L32 = _f32(Lref)
+    CQ = torch.empty(G * N * m, device="cuda")
+    CK = torch.empty_like(CQ)
+    We = torch.empty(G * m * m, device="cuda")
+    lf.lf_laplace_l1_exp(p, t["Q"], t["K"], L32, CQ, CK, We)
+    torch.cuda.synchronize()
+    Lr = _r32(Lref)
+    for g in range(G):
+        q, k = inp["Q"].reshape(G, N, d)[g], inp["K"].reshape(G, N, d)[g]
+        assert relF(host(CQ).reshape(G, N, m)[g], O.laplacian_kernel(q, Lr[g], wl.lam)) <= 1e-5
+        assert relF(host(CK).reshape(G, N, m)[g], O.laplacian_kernel(k, Lr[g], wl.lam)) <= 1e-5
+        Wref = O.laplacian_kernel(Lr[g], Lr[g], wl.lam) + wl.eps * np.eye(m)
+        assert relF(host(We).reshape(G, m, m)[g], Wref) <= 1e-5
+
+
+@pytest.mark.parametrize("wl", [WL.TINY, WL.TINY_R1, WL.PVT_S1, WL.PVT_S3, WL.HIRES_BF16, EDGE[2]],
+                         ids=lambda w: w.name)
+def test_stage_newton_schulz(wl):
+    note(f"[gpu] stage ns_pinv {wl.name}")
+    p = params(wl)
+    ref = oracle_forward(wl)
+    G, m, K = p.G, p.m, p.ns_iters
+    We64 = _r32(np.asarray(ref["We"]).reshape(G, m, m))
+    fwd_b, _, _ = lf.lf_attn_query(p)
+    ws = torch.empty(fwd_b, dtype=torch.uint8, device="cuda")
+    X = torch.empty(G * m * m, device="cuda")
+    xs = torch.empty(G * (K + 1) * m * m, device="cuda")
+    alpha = torch.empty(G, device="cuda")
+    resid = torch.empty(G, device="cuda")
+    lf.lf_ns_pinv(p, _f32(We64), X, xs, alpha, resid, ws)
+    torch.cuda.synchronize()
+    Xh = host(X).reshape(G, m, m)
+    for g in range(G):
+        Xref, xs_ref, aref = O.newton_schulz(We64[g], K)
+        assert abs(host(alpha)[g] - aref) <= 1e-6 * aref
+        assert relF(Xh[g], Xref) <= tol(wl)
+        assert relF(host(xs).reshape(G, K + 1, m, m)[g, 0], xs_ref[0]) <= 1e-6
+        assert np.array_equal(host(xs).reshape(G, K + 1, m, m)[g, K], Xh[g])
+        r_ref = np.linalg.norm(We64[g] @ Xref - np.eye(m))
+        r_gpu = float(host(resid)[g])
+        # fp32 NS cannot go below ~1e-6 * sqrt(m); above that it must track the oracle's residual
+        assert r_gpu <= max(2 * r_ref, 1e-4)
+
+
+def test_stage_newton_schulz_kappa50():
+    """The pages' claim: NS copes with condition number 50. Synthetic SPD W, m = 32, enough steps to converge."""
+    note("[gpu] stage ns_pinv kappa=50")
+    rng = np.random.default_rng(8)
+    Qm, _ = np.linalg.qr(rng.standard_normal((32, 32)))
+    A = (Qm * np.geomspace(1.0, 50.0, 32)) @ Qm.T
+    A = 0.5 * (A + A.T)
+    wl = WL.TINY.replace(H=8, W=16, r=2, ns_iters=30)  # m = 32
+    p = params(wl)
+    X = torch.empty(32 * 32, device="cuda")
+    resid = torch.empty(1, device="cuda")
+    lf.lf_ns_pinv(p, _f32(A), X, None, None, resid, None)
+    torch.cuda.synchronize()
+    A32 = _r32(A)
+    inv = np.linalg.inv(A32)
+    assert relF(host(X).reshape(32, 32), inv) <= 1e-4
+    assert float(host(resid)[0]) <= 1e-4
+
+
+@pytest.mark.parametrize("wl", [WL.TINY, WL.PVT_S1, WL.PVT_S3, WL.HIRES_BF16, EDGE[2]], ids=lambda w: w.name)
+def test_stage_ckv_mix_out(wl):
+    note(f"[gpu] stages ckv+mix+out {wl.name}")
+    p = params(wl)
+    inp = inputs(wl)
+    ref = oracle_forward(wl)
+    t = upload(wl)
+    G, N, m, d = p.G, p.N, p.m, p.d
+    CK = _r32(np.asarray(ref["CK"]).reshape(G, N, m))
+    CQ = _r32(np.asarray(ref["CQ"]).reshape(G, N, m))
+    X = _r32(np.asarray(ref["X"]).reshape(G, m, m))
+    V = inp["V"].reshape(G, N, d)
+    fwd_b, _, _ = lf.lf_attn_query(p)
+    ws = torch.empty(fwd_b, dtype=torch.uint8, device="cuda")
+    S = torch.empty(G * m * d, device="cuda")
+    lf.lf_ckv_reduce(p, _f32(CK), t["V"], S, ws)
+    Sref = np.einsum("gil,gic->glc", CK, V)
+    P = torch.empty(G * m * d, device="cuda")
+    lf.lf_landmark_mix(p, _f32(X), _f32(Sref), None, P)
+    Pref = np.einsum("glk,gkc->glc", X, _r32(Sref))
+    Y = torch.empty_like(t["Q"])
+    lf.lf_out_gemm_dwc(p, _f32(CQ), _f32(Pref), None, t["V"], t["w"], Y)
+    torch.cuda.synchronize()
+    assert relF(host(S).reshape(G, m, d), Sref) <= 1e-5
+    assert relF(host(P).reshape(G, m, d), Pref) <= 1e-5
+    P32 = _r32(Pref)
+    w = inp["w64"]
+    Yref = np.stack([CQ[g] @ P32[g] + O.dwc(V[g], w[(g % wl.heads) * d:(g % wl.heads + 1) * d], wl.H, wl.W)
+                     for g in range(G)])
+    bar = 1e-5 if wl.dtype == WL.F32 else tol(wl)
+    assert relF(host(Y).reshape(G, N, d), Yref) <= bar
+
+
+def test_stage_whiten_stats_and_folded_output():
+    wl = WL.TRAIN_S1
+    note(f"[gpu] stages whiten {wl.name}")
+    p = params(wl)
+    ref = oracle_forward(wl)
+    G, N, m, d = p.G, p.N, p.m, p.d
+    CQ = _r32(np.asarray(ref["CQ"]).reshape(G, N, m))
+    mu = torch.empty(G * m, device="cuda")
+    rstd = torch.empty(G * m, device="cuda")
+    lf.lf_whiten_stats(p, _f32(CQ), mu, rstd)
+    torch.cuda.synchronize()
+    A, muref, rsref = zip(*[O.whiten_columns(CQ[g], wl.whiten_eps) for g in range(G)])
+    assert relF(host(mu).reshape(G, m), np.stack(muref)) <= 1e-6
+    assert relF(host(rstd).reshape(G, m), np.stack(rsref)) <= 1e-6
