@@ -46,6 +46,23 @@ __device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
+// Four consecutive elements as float4 (16-byte aligned for float, 8-byte aligned for bf16).
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const bf16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ void store4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ void store4(bf16_t* p, float4 v) {
+  const bf16_t a = from_f32<bf16_t>(v.x), b = from_f32<bf16_t>(v.y), c = from_f32<bf16_t>(v.z),
+               d = from_f32<bf16_t>(v.w);
+  uint2 u;
+  u.x = static_cast<uint32_t>(a.bits) | (static_cast<uint32_t>(b.bits) << 16);
+  u.y = static_cast<uint32_t>(c.bits) | (static_cast<uint32_t>(d.bits) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 

@@ -9,27 +9,55 @@ namespace lf {
 
 // =====================================================================================================
 // landmark_pool: L[g][l][c] = (1/r^2) sum_{a,b<r} Q[g][(Y r + a) W + X r + b][c]      ([note] Design 2)
-// One thread per output element, channel fastest, so each wave reads whole token rows (coalesced).
+// Thread = (landmark, window row slot, 4 channels): it sums its window rows with independent 16-byte (fp32) or
+// 8-byte (bf16) loads that are all in flight at once, and the window-row partials are added through LDS in a
+// fixed order. `tpl` threads serve one landmark (d/4 channel quads x `slots` row slots), `lpb` landmarks a block.
 // =====================================================================================================
 template <typename T>
 __global__ __launch_bounds__(256) void k_landmark_pool(const T* __restrict__ Q, float* __restrict__ L, int G, int H,
-                                                       int W, int d, int r, int m) {
-  const size_t t = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  const size_t total = static_cast<size_t>(G) * m * d;
-  if (t >= total) return;
-  const int c = static_cast<int>(t % d);
-  const size_t gl = t / d;
-  const int l = static_cast<int>(gl % m);
-  const size_t g = gl / m;
-  const int wr = W / r;
-  const int Yb = l / wr, Xb = l % wr;
-  const T* q = Q + g * static_cast<size_t>(H) * W * d + c;
-  float acc = 0.f;
-  for (int a = 0; a < r; ++a) {
-    const T* row = q + (static_cast<size_t>(Yb * r + a) * W + static_cast<size_t>(Xb) * r) * d;
-    for (int b = 0; b < r; ++b) acc += to_f32(row[static_cast<size_t>(b) * d]);
+                                                       int W, int d, int r, int m, int tpl, int lpb) {
+  __shared__ float4 part[256];
+  const int c4n = d >> 2;
+  const int slots = tpl / c4n;
+  const int t = threadIdx.x;
+  const int ll = t / tpl, rem = t % tpl;
+  const int slot = rem / c4n, c4 = rem % c4n;
+  const size_t lin = static_cast<size_t>(blockIdx.x) * lpb + ll;
+  const bool valid = ll < lpb && lin < static_cast<size_t>(G) * m;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  size_t g = 0;
+  if (valid) {
+    g = lin / m;
+    const int l = static_cast<int>(lin % m);
+    const int wr = W / r;
+    const int Yb = l / wr, Xb = l % wr;
+    const T* base = Q + g * static_cast<size_t>(H) * W * d + 4 * c4;
+    for (int a = slot; a < r; a += slots) {
+      const T* row = base + (static_cast<size_t>(Yb * r + a) * W + static_cast<size_t>(Xb) * r) * d;
+#pragma unroll 8
+      for (int b = 0; b < r; ++b) {
+        const float4 v = load4(row + static_cast<size_t>(b) * d);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+    }
   }
-  L[t] = acc / static_cast<float>(r * r);
+  part[t] = acc;
+  __syncthreads();
+  if (valid && slot == 0) {
+    float4 s = part[t];
+    for (int k = 1; k < slots; ++k) {
+      const float4 v = part[t + k * c4n];
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    const float inv = static_cast<float>(r * r);
+    store4(L + lin * d + 4 * c4, make_float4(s.x / inv, s.y / inv, s.z / inv, s.w / inv));
+  }
 }
 
 // =====================================================================================================
@@ -150,68 +178,102 @@ __host__ __device__ inline int ld_b(int cols) { return ((cols + 31) / 32) * 32 +
 // `ones` appends a column of ones to C (mout = mrow + 1), so row mrow of the result is sum_i V[i][c]; the
 // backward pass uses this to get the column sums of dY in the same sweep as C_Q^T dY.
 // =====================================================================================================
-template <typename T, int D, int TPW>
-__global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ CK, const T* __restrict__ V,
-                                                     float* __restrict__ part, int N, int mrow, int mout, int nsplit,
-                                                     int rows_per_split) {
+template <typename T, int D, int MT>
+__global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ C, const T* __restrict__ V,
+                                                     float* __restrict__ part, int N, int mrow, int ones,
+                                                     int nsplit, int rows_per_split) {
+  // LDS: the C chunk exactly as it lies in memory (64 rows of mrow floats, then MT*16 floats of zero pad that
+  // out-of-range landmark columns of the last row may touch), and the V chunk with a 16 mod 32 row stride.
   extern __shared__ float smem[];
-  const int g = blockIdx.x / nsplit, s = blockIdx.x % nsplit;
-  const int mt = (mout + 15) / 16;
   constexpr int DT = D / 16;
-  const int ntiles = mt * DT;
-  const int mp = mt * 16;
-  const int LDC = ld_b(mp), LDV = ld_b(D);
+  constexpr int CTW = (DT + 3) / 4;  // column tiles per wave
+  constexpr int LDV = ((D + 31) / 32) * 32 + 16;
+  constexpr int NQC = MT;            // float4 loads of C per thread for a full chunk (64 * mrow <= 1024 * MT)
+  constexpr int NQV = D / 16;        // 4-element loads of V per thread for a full chunk
+  const int mout = mrow + ones;
   float* sC = smem;
-  float* sV = smem + 64 * LDC;
-  const int wv = wave_id(), ln = lane_id();
-  f32x4 acc[TPW];
+  float* sV = smem + 64 * mrow + MT * 16;
+  const int g = blockIdx.x / nsplit, s = blockIdx.x % nsplit;
+  const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
+  for (int q = tid; q < MT * 16; q += 256) sC[64 * mrow + q] = 0.f;
+
+  f32x4 acc[MT][CTW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int b = 0; b < CTW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   const int r0 = s * rows_per_split, r1 = min(N, r0 + rows_per_split);
-  const float* ckg = CK + static_cast<size_t>(g) * N * mrow;
+  const float* cg = C + static_cast<size_t>(g) * N * mrow;
   const T* vg = V + static_cast<size_t>(g) * N * D;
   for (int c0 = r0; c0 < r1; c0 += 64) {
     const int nr = min(64, r1 - c0);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 64 * mp; idx += 256) {
-      const int rr = idx / mp, cc = idx % mp;
-      float v = 0.f;
-      if (rr < nr) v = (cc < mrow) ? ckg[static_cast<size_t>(c0 + rr) * mrow + cc] : (cc < mout ? 1.f : 0.f);
-      sC[rr * LDC + cc] = v;
-    }
-    for (int idx = threadIdx.x; idx < 64 * D; idx += 256) {
-      const int rr = idx / D, cc = idx % D;
-      sV[rr * LDV + cc] = (rr < nr) ? to_f32(vg[static_cast<size_t>(c0 + rr) * D + cc]) : 0.f;
-    }
-    __syncthreads();
-    const int ksteps = (nr + 3) / 4;
-    for (int ks = 0; ks < ksteps; ++ks) {
-      const int kr = ks * 4 + (ln >> 4);
+    const int nC = nr * mrow;  // floats of C in this chunk
+    const float* csrc = cg + static_cast<size_t>(c0) * mrow;
+    const T* vsrc = vg + static_cast<size_t>(c0) * D;
+    float4 cbuf[NQC];
+    float4 vbuf[NQV];
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const int tile = wv + 4 * t;
-        if (tile < ntiles) {
-          const int lt = tile / DT, ct = tile % DT;
-          const float a = sC[kr * LDC + lt * 16 + (ln & 15)];
-          const float b = sV[kr * LDV + ct * 16 + (ln & 15)];
-          acc[t] = mfma16x16x4(a, b, acc[t]);
+    for (int q = 0; q < NQC; ++q) {
+      const int e = 4 * (tid + 256 * q);
+      if (e + 3 < nC) {
+        cbuf[q] = load4(csrc + e);
+      } else {
+        cbuf[q].x = e + 0 < nC ? csrc[e + 0] : 0.f;
+        cbuf[q].y = e + 1 < nC ? csrc[e + 1] : 0.f;
+        cbuf[q].z = e + 2 < nC ? csrc[e + 2] : 0.f;
+        cbuf[q].w = e + 3 < nC ? csrc[e + 3] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NQV; ++q) {
+      const int e = 4 * (tid + 256 * q);
+      vbuf[q] = (e < nr * D) ? load4(vsrc + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();  // the previous chunk's MFMA reads are done
+#pragma unroll
+    for (int q = 0; q < NQC; ++q) {
+      const int e = 4 * (tid + 256 * q);
+      if (e < 64 * mrow) store4(sC + e, cbuf[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < NQV; ++q) {
+      const int e = 4 * (tid + 256 * q);
+      const int rr = e / D, cc = e % D;
+      store4(sV + rr * LDV + cc, vbuf[q]);
+    }
+    __syncthreads();
+    if (wv * CTW < DT) {
+#pragma unroll 4
+      for (int ks = 0; ks < 16; ++ks) {
+        const int kr = ks * 4 + (ln >> 4);
+        float b[CTW];
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) b[ct] = sV[kr * LDV + (wv * CTW + ct) * 16 + (ln & 15)];
+#pragma unroll
+        for (int lt = 0; lt < MT; ++lt) {
+          const int l = lt * 16 + (ln & 15);
+          float a = sC[kr * mrow + l];
+          if (l == mrow) a = (ones && kr < nr) ? 1.f : 0.f;
+#pragma unroll
+          for (int ct = 0; ct < CTW; ++ct) acc[lt][ct] = mfma16x16x4(a, b[ct], acc[lt][ct]);
         }
       }
     }
   }
-  float* pg = part + (static_cast<size_t>(g) * nsplit + s) * mout * D;
+  if (wv * CTW < DT) {
+    float* pg = part + (static_cast<size_t>(g) * nsplit + s) * mout * D;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int tile = wv + 4 * t;
-    if (tile < ntiles) {
-      const int lt = tile / DT, ct = tile % DT;
-      const int c = ct * 16 + (ln & 15);
+    for (int lt = 0; lt < MT; ++lt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int l = lt * 16 + 4 * (ln >> 4) + rr;
-        if (l < mout) pg[static_cast<size_t>(l) * D + c] = acc[t][rr];
+      for (int ct = 0; ct < CTW; ++ct) {
+        const int c = (wv * CTW + ct) * 16 + (ln & 15);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int l = lt * 16 + 4 * (ln >> 4) + rr;
+          if (l < mout && c < D) pg[static_cast<size_t>(l) * D + c] = acc[lt][ct][rr];
+        }
       }
-    }
   }
 }
 
@@ -222,148 +284,251 @@ __global__ __launch_bounds__(256) void k_ckv_finalize(const float* __restrict__ 
   const size_t g = t / md, e = t % md;
   const float* p = part + g * nsplit * md + e;
   float acc = 0.f;
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) acc += p[static_cast<size_t>(s) * md];
   S[t] = acc;
 }
 
 // =====================================================================================================
 // landmark_mix: P[g][l][c] = rstd[l] * sum_k X[g][l][k] S[g][k][c]   (X = Newton-Schulz pseudo-inverse,
-//   [note] Design 2 and 3; rstd from the diagonal whitening of Design 1). Small: m x m times m x D per slice.
-// Block: 16 landmark rows x D channels of one slice; thread (row, 16-column group).
+//   [note] Designs 2 and 3; rstd from the diagonal whitening of Design 1). m x m times m x D per slice.
+// Block: 16 landmark rows x D channels of one slice; X rows and 64-row chunks of S are staged in LDS.
 // =====================================================================================================
 template <int D>
 __global__ __launch_bounds__(256) void k_mix(const float* __restrict__ X, const float* __restrict__ S,
                                              const float* __restrict__ rstd, float* __restrict__ P,
                                              float* __restrict__ Praw, int m) {
-  const int g = blockIdx.y;
-  const int lr = threadIdx.x >> 4, cg = threadIdx.x & 15;
-  const int l = blockIdx.x * 16 + lr;
-  if (l >= m) return;
-  constexpr int NC = (D + 15) / 16;
+  __shared__ float sX[16 * 65];
+  __shared__ float sS[64 * D];
+  const int g = blockIdx.y, l0 = blockIdx.x * 16, tid = threadIdx.x;
+  constexpr int NC = (D * 16 + 255) / 256;  // outputs per thread
   float acc[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) acc[j] = 0.f;
-  const float* xr = X + (static_cast<size_t>(g) * m + l) * m;
+  const float* xg = X + static_cast<size_t>(g) * m * m;
   const float* sg = S + static_cast<size_t>(g) * m * D;
-  for (int k = 0; k < m; ++k) {
-    const float xv = xr[k];
+  for (int k0 = 0; k0 < m; k0 += 64) {
+    const int nk = min(64, m - k0);
+    constexpr int NQ = (64 * D / 4 + 255) / 256;
+    float4 buf[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = 4 * (tid + 256 * q);
+      buf[q] = (e < nk * D) ? load4(sg + static_cast<size_t>(k0) * D + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float xv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + 256 * q;
+      const int rr = e >> 6, kk = e & 63;
+      xv[q] = (l0 + rr < m && kk < nk) ? xg[static_cast<size_t>(l0 + rr) * m + k0 + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + 256 * q;
+      sX[(e >> 6) * 65 + (e & 63)] = xv[q];
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = 4 * (tid + 256 * q);
+      if (e < 64 * D) store4(sS + e, buf[q]);
+    }
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
-      const int c = cg + 16 * j;
-      if (c < D) acc[j] += xv * sg[static_cast<size_t>(k) * D + c];
+      const int o = tid + 256 * j;
+      if (o < 16 * D) {
+        const int rr = o / D, c = o % D;
+        float a = acc[j];
+        for (int kk = 0; kk < nk; ++kk) a += sX[rr * 65 + kk] * sS[kk * D + c];
+        acc[j] = a;
+      }
     }
   }
-  const float sc = rstd ? rstd[static_cast<size_t>(g) * m + l] : 1.f;
-  float* pr = P + (static_cast<size_t>(g) * m + l) * D;
-  float* prr = Praw ? Praw + (static_cast<size_t>(g) * m + l) * D : nullptr;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
-    const int c = cg + 16 * j;
-    if (c < D) {
-      pr[c] = acc[j] * sc;
-      if (prr) prr[c] = acc[j];
+    const int o = tid + 256 * j;
+    if (o < 16 * D) {
+      const int rr = o / D, c = o % D;
+      const int l = l0 + rr;
+      if (l < m) {
+        const float sc = rstd ? rstd[static_cast<size_t>(g) * m + l] : 1.f;
+        P[(static_cast<size_t>(g) * m + l) * D + c] = acc[j] * sc;
+        if (Praw) Praw[(static_cast<size_t>(g) * m + l) * D + c] = acc[j];
+      }
     }
   }
 }
 
 // =====================================================================================================
 // out_gemm_dwc: Y[g][i][c] = sum_l C_Q[g][i][l] P[g][l][c] - sum_l mu[g][l] P[g][l][c] + DWC(V)[g][i][c]
-//   With flip = 1 the 3x3 filter is rotated by 180 degrees, which makes the stencil the adjoint of DWC; the
-//   backward pass uses that for dV = C_K dS + DWC^T(dY).
 //   ([note] Design 1: output = ZV + DWC(V); flowchart nodes G, H, I). The whitening bias is the folded form of
-//   (C_Q - mu) rstd P with rstd already applied to P.
-// Block: 64 tokens x D channels of one slice, 4 waves of 16 tokens each. The K = m reduction runs on fp32
-// MFMA with 64-landmark chunks of C_Q and P staged in LDS; the depthwise 3x3 stencil and the bias are added
-// in the epilogue before the single store of Y.
+//   (C_Q - mu) rstd P with rstd already applied to P. With flip = 1 the 3x3 filter is rotated by 180 degrees,
+//   which makes the stencil the adjoint of DWC (the backward pass uses that for dV = C_K dS + DWC^T(dY)).
+// Block: an 8 x 8 patch of the token grid of one slice (64 tokens) and all D channels.
+//   1. The 10 x 10 halo of V around the patch is staged once in LDS (zero outside the grid).
+//   2. The K = m reduction runs on fp32 MFMA (wave w: tokens 16w..16w+15), with 64-landmark chunks of C_Q and
+//      P staged in LDS; all global loads of a chunk are issued before the LDS writes.
+//   3. The accumulators go through LDS to a (token, 4 channels) layout, where the bias and the 3x3 stencil are
+//      added and Y is written with 16-byte (fp32) or 8-byte (bf16) coalesced stores.
 // =====================================================================================================
-constexpr int OUT_LDA = 66;  // 2 mod 32: A-style reads (row = lane % 16, k = lane / 16) are conflict free
+template <int D>
+struct OutLds {
+  static constexpr int LDV = D + 4;                        // V halo row stride (float4 aligned)
+  static constexpr int LDA = 66;                           // 2 mod 32: conflict-free A-style reads
+  static constexpr int LDB = ((D + 31) / 32) * 32 + 16;    // 16 mod 32: conflict-free B-style reads
+  static constexpr int LDO = D + 4;
+  static constexpr int VH = 0;
+  static constexpr int A = VH + 100 * LDV;
+  static constexpr int B = A + 64 * LDA;
+  static constexpr int MU = B + 64 * LDB;
+  static constexpr int WT = MU + 64;
+  static constexpr int BIAS = WT + 9 * D;
+  static constexpr int TOTAL = BIAS + D;
+  static_assert(64 * LDO <= 64 * LDA + 64 * LDB, "output staging must fit in the A and B areas");
+};
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_out(const float* __restrict__ CQ, const float* __restrict__ P,
                                              const float* __restrict__ mu, const T* __restrict__ V,
                                              const float* __restrict__ w, T* __restrict__ Y, int N, int m, int H,
-                                             int W, int heads, int flip) {
-  constexpr int LDB = ((D + 31) / 32) * 32 + 16;
+                                             int W, int heads, int flip, int tiles_x) {
+  using Lay = OutLds<D>;
+  extern __shared__ float smem[];
+  float* sVh = smem + Lay::VH;
+  float* sA = smem + Lay::A;
+  float* sB = smem + Lay::B;
+  float* sMu = smem + Lay::MU;
+  float* sWt = smem + Lay::WT;
+  float* sBias = smem + Lay::BIAS;
+  float* sO = smem + Lay::A;  // reuses the A and B areas after the GEMM
   constexpr int DT = D / 16;
-  __shared__ float sA[64 * OUT_LDA];
-  __shared__ float sB[64 * LDB];
-  __shared__ float sBias[D];
+  constexpr int C4 = D / 4;
   const int g = blockIdx.y;
-  const int i0 = blockIdx.x * 64;
+  const int ty0 = (blockIdx.x / tiles_x) * 8, tx0 = (blockIdx.x % tiles_x) * 8;
   const int h = g % heads;
-  const int wv = wave_id(), ln = lane_id();
+  const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
   const float* cq = CQ + static_cast<size_t>(g) * N * m;
   const float* pg = P + static_cast<size_t>(g) * m * D;
+  const T* vg = V + static_cast<size_t>(g) * N * D;
+  const bool has_w = w != nullptr;
 
-  if (threadIdx.x < D) {
-    float b = 0.f;
-    if (mu) {
-      const float* mg = mu + static_cast<size_t>(g) * m;
-      for (int l = 0; l < m; ++l) b += mg[l] * pg[static_cast<size_t>(l) * D + threadIdx.x];
+  // 1. V halo and filter taps
+  if (has_w) {
+    constexpr int NQ = (100 * C4 + 255) / 256;
+    float4 vb[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = tid + 256 * q;
+      vb[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < 100 * C4) {
+        const int tok = e / C4, c4 = e % C4;
+        const int y = ty0 - 1 + tok / 10, x = tx0 - 1 + tok % 10;
+        if (y >= 0 && y < H && x >= 0 && x < W) vb[q] = load4(vg + static_cast<size_t>(y * W + x) * D + 4 * c4);
+      }
     }
-    sBias[threadIdx.x] = b;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = tid + 256 * q;
+      if (e < 100 * C4) store4(sVh + (e / C4) * Lay::LDV + 4 * (e % C4), vb[q]);
+    }
+    for (int e = tid; e < 9 * D; e += 256) {
+      const int q = e / D, c = e % D;
+      sWt[e] = w[(static_cast<size_t>(h) * D + c) * 9 + (flip ? 8 - q : q)];
+    }
   }
+  float bias_acc = 0.f;
 
+  // 2. C_Q (tile tokens x landmarks) times P, in 64-landmark chunks
   f32x4 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   for (int lc0 = 0; lc0 < m; lc0 += 64) {
     const int nl = min(64, m - lc0);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-      const int rr = idx >> 6, cc = idx & 63;
-      const int i = i0 + rr;
-      sA[rr * OUT_LDA + cc] = (i < N && cc < nl) ? cq[static_cast<size_t>(i) * m + lc0 + cc] : 0.f;
+    float av[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q;
+      const int u = e >> 6, cc = e & 63;
+      const int y = ty0 + (u >> 3), x = tx0 + (u & 7);
+      av[q] = (y < H && x < W && cc < nl) ? cq[static_cast<size_t>(y * W + x) * m + lc0 + cc] : 0.f;
     }
-    for (int idx = threadIdx.x; idx < 64 * D; idx += 256) {
-      const int rr = idx / D, cc = idx % D;
-      sB[rr * LDB + cc] = (rr < nl) ? pg[static_cast<size_t>(lc0 + rr) * D + cc] : 0.f;
+    constexpr int NQB = (16 * D + 255) / 256;
+    float4 bv[NQB];
+#pragma unroll
+    for (int q = 0; q < NQB; ++q) {
+      const int e = tid + 256 * q;
+      const int rr = e / C4, c4 = e % C4;
+      bv[q] = (e < 16 * D && rr < nl) ? load4(pg + static_cast<size_t>(lc0 + rr) * D + 4 * c4)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    const float muv = (mu && tid < 64 && tid < nl) ? mu[static_cast<size_t>(g) * m + lc0 + tid] : 0.f;
+    __syncthreads();  // previous chunk's reads are done
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q;
+      sA[(e >> 6) * Lay::LDA + (e & 63)] = av[q];
+    }
+#pragma unroll
+    for (int q = 0; q < NQB; ++q) {
+      const int e = tid + 256 * q;
+      if (e < 16 * D) store4(sB + (e / C4) * Lay::LDB + 4 * (e % C4), bv[q]);
+    }
+    if (tid < 64) sMu[tid] = muv;
     __syncthreads();
+    if (mu && tid < D) {
+      for (int kk = 0; kk < nl; ++kk) bias_acc += sMu[kk] * sB[kk * Lay::LDB + tid];
+    }
     const int ksteps = (nl + 3) / 4;
     for (int ks = 0; ks < ksteps; ++ks) {
       const int k = ks * 4 + (ln >> 4);
-      const float a = sA[(wv * 16 + (ln & 15)) * OUT_LDA + k];
+      const float a = sA[(wv * 16 + (ln & 15)) * Lay::LDA + k];
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const float bb = sB[k * LDB + t * 16 + (ln & 15)];
-        acc[t] = mfma16x16x4(a, bb, acc[t]);
-      }
+      for (int t = 0; t < DT; ++t) acc[t] = mfma16x16x4(a, sB[k * Lay::LDB + t * 16 + (ln & 15)], acc[t]);
     }
   }
-  __syncthreads();
-
-  const T* vg = V + static_cast<size_t>(g) * N * D;
-  T* yg = Y + static_cast<size_t>(g) * N * D;
+  __syncthreads();  // all GEMM reads done before sO overwrites the A and B areas
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
     const int c = t * 16 + (ln & 15);
-    float wk[9];
 #pragma unroll
-    for (int q = 0; q < 9; ++q) wk[q] = w ? w[(static_cast<size_t>(h) * D + c) * 9 + (flip ? 8 - q : q)] : 0.f;
-    const float bias = sBias[c];
+    for (int r = 0; r < 4; ++r) sO[(wv * 16 + 4 * (ln >> 4) + r) * Lay::LDO + c] = acc[t][r];
+  }
+  if (tid < D) sBias[tid] = bias_acc;
+  __syncthreads();
+
+  // 3. epilogue per (token, 4 channels)
+  T* yg = Y + static_cast<size_t>(g) * N * D;
+  constexpr int NI = (64 * C4 + 255) / 256;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int i = i0 + wv * 16 + 4 * (ln >> 4) + rr;
-      if (i >= N) continue;
-      float y = acc[t][rr] - bias;
-      if (w) {
-        const int yy = i / W, xx = i % W;
-        float dsum = 0.f;
+  for (int q = 0; q < NI; ++q) {
+    const int e = tid + 256 * q;
+    if (e >= 64 * C4) break;
+    const int u = e / C4, c4 = e % C4;
+    const int ty = u >> 3, tx = u & 7;
+    const int y = ty0 + ty, x = tx0 + tx;
+    if (y >= H || x >= W) continue;
+    float4 o = *reinterpret_cast<const float4*>(sO + u * Lay::LDO + 4 * c4);
+    const float4 b = *reinterpret_cast<const float4*>(sBias + 4 * c4);
+    o.x -= b.x;
+    o.y -= b.y;
+    o.z -= b.z;
+    o.w -= b.w;
+    if (has_w) {
 #pragma unroll
-        for (int a = -1; a <= 1; ++a) {
+      for (int a = 0; a < 3; ++a)
 #pragma unroll
-          for (int bb = -1; bb <= 1; ++bb) {
-            const int y2 = yy + a, x2 = xx + bb;
-            if (y2 >= 0 && y2 < H && x2 >= 0 && x2 < W)
-              dsum += wk[(a + 1) * 3 + (bb + 1)] * to_f32(vg[static_cast<size_t>(y2 * W + x2) * D + c]);
-          }
+        for (int bb = 0; bb < 3; ++bb) {
+          const float4 v = *reinterpret_cast<const float4*>(sVh + ((ty + a) * 10 + tx + bb) * Lay::LDV + 4 * c4);
+          const float4 k4 = *reinterpret_cast<const float4*>(sWt + (a * 3 + bb) * D + 4 * c4);
+          o.x += k4.x * v.x;
+          o.y += k4.y * v.y;
+          o.z += k4.z * v.z;
+          o.w += k4.w * v.w;
         }
-        y += dsum;
-      }
-      yg[static_cast<size_t>(i) * D + c] = from_f32<T>(y);
     }
+    store4(yg + static_cast<size_t>(y * W + x) * D + 4 * c4, o);
   }
 }
 
@@ -373,14 +538,19 @@ __global__ __launch_bounds__(256) void k_out(const float* __restrict__ CQ, const
 static inline int cdiv(long a, long b) { return static_cast<int>((a + b - 1) / b); }
 
 hipError_t launch_landmark_pool(const Shape& s, const void* Q, float* L, hipStream_t st) {
-  const size_t total = static_cast<size_t>(s.G) * s.m * s.d;
-  const dim3 grid(cdiv(static_cast<long>(total), 256));
+  const int c4n = s.d / 4;
+  int slots = s.r < 256 / c4n ? s.r : 256 / c4n;
+  if (slots < 1) slots = 1;
+  const int tpl = c4n * slots;
+  const int lpb = 256 / tpl;
+  const long total = static_cast<long>(s.G) * s.m;
+  const dim3 grid(cdiv(total, lpb));
   if (s.dtype == 1)
     hipLaunchKernelGGL(k_landmark_pool<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(Q), L, s.G, s.H,
-                       s.W, s.d, s.r, s.m);
+                       s.W, s.d, s.r, s.m, tpl, lpb);
   else
     hipLaunchKernelGGL(k_landmark_pool<float>, grid, dim3(256), 0, st, static_cast<const float*>(Q), L, s.G, s.H,
-                       s.W, s.d, s.r, s.m);
+                       s.W, s.d, s.r, s.m, tpl, lpb);
   return hipGetLastError();
 }
 
@@ -427,55 +597,49 @@ hipError_t launch_whiten_stats(const Shape& s, const float* CQ, float* mu, float
 }
 
 void ckv_split(const Shape& s, int* nsplit, int* rows_per_split) {
-  // Aim for ~256 blocks; each split covers a multiple of 64 rows.
-  int want = cdiv(256, s.G);
-  const int maxsplit = cdiv(s.N, 64);
-  if (want > maxsplit) want = maxsplit;
+  // At most ~512 blocks in all; each split covers whole 64-row chunks.
+  const int chunks = cdiv(s.N, 64);
+  int want = 512 / s.G;
+  if (want > chunks) want = chunks;
   if (want < 1) want = 1;
-  int rps = cdiv(cdiv(s.N, want), 64) * 64;
-  *rows_per_split = rps;
-  *nsplit = cdiv(s.N, rps);
+  const int cps = cdiv(chunks, want);
+  *rows_per_split = 64 * cps;
+  *nsplit = cdiv(chunks, cps);
 }
 
-template <typename T, int D, int TPW>
-static void ckv_launch(const Shape& s, const float* C, int mrow, int mout, const void* V, float* part, int nsplit,
-                       int rps, hipStream_t st) {
-  const int mp = cdiv(mout, 16) * 16;
-  const size_t lds = sizeof(float) * 64 * (ld_b(mp) + ld_b(D));
+template <typename T, int D, int MT>
+static void ckv_launch(const Shape& s, const float* C, int ones, const void* V, float* part, int nsplit, int rps,
+                       hipStream_t st) {
+  const size_t lds = sizeof(float) * (64 * s.m + MT * 16 + 64 * (((D + 31) / 32) * 32 + 16));
   if (lds > 64 * 1024)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ckv_partial<T, D, TPW>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ckv_partial<T, D, MT>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  hipLaunchKernelGGL((k_ckv_partial<T, D, TPW>), dim3(s.G * nsplit), dim3(256), lds, st, C, static_cast<const T*>(V),
-                     part, s.N, mrow, mout, nsplit, rps);
+  hipLaunchKernelGGL((k_ckv_partial<T, D, MT>), dim3(s.G * nsplit), dim3(256), lds, st, C, static_cast<const T*>(V),
+                     part, s.N, s.m, ones, nsplit, rps);
 }
 
 template <typename T, int D>
-static void ckv_tpw(const Shape& s, const float* C, int mrow, int mout, const void* V, float* part, int nsplit,
-                    int rps, hipStream_t st) {
-  const int ntiles = cdiv(mout, 16) * (D / 16);
-  const int tpw = cdiv(ntiles, 4);
-  if (tpw <= 1)
-    ckv_launch<T, D, 1>(s, C, mrow, mout, V, part, nsplit, rps, st);
-  else if (tpw <= 2)
-    ckv_launch<T, D, 2>(s, C, mrow, mout, V, part, nsplit, rps, st);
-  else if (tpw <= 4)
-    ckv_launch<T, D, 4>(s, C, mrow, mout, V, part, nsplit, rps, st);
-  else if (tpw <= 8)
-    ckv_launch<T, D, 8>(s, C, mrow, mout, V, part, nsplit, rps, st);
-  else if (tpw <= 16)
-    ckv_launch<T, D, 16>(s, C, mrow, mout, V, part, nsplit, rps, st);
-  else
-    ckv_launch<T, D, 32>(s, C, mrow, mout, V, part, nsplit, rps, st);
+static void ckv_mt(const Shape& s, const float* C, int ones, const void* V, float* part, int nsplit, int rps,
+                   hipStream_t st) {
+  const int mt = cdiv(s.m + ones, 16);
+  if (mt <= 1) ckv_launch<T, D, 1>(s, C, ones, V, part, nsplit, rps, st);
+  else if (mt <= 2) ckv_launch<T, D, 2>(s, C, ones, V, part, nsplit, rps, st);
+  else if (mt <= 3) ckv_launch<T, D, 3>(s, C, ones, V, part, nsplit, rps, st);
+  else if (mt <= 4) ckv_launch<T, D, 4>(s, C, ones, V, part, nsplit, rps, st);
+  else if (mt <= 5) ckv_launch<T, D, 5>(s, C, ones, V, part, nsplit, rps, st);
+  else if (mt <= 8) ckv_launch<T, D, 8>(s, C, ones, V, part, nsplit, rps, st);
+  else if (mt <= 12) ckv_launch<T, D, 12>(s, C, ones, V, part, nsplit, rps, st);
+  else ckv_launch<T, D, 16>(s, C, ones, V, part, nsplit, rps, st);
 }
 
 template <typename T>
-static void ckv_d(const Shape& s, const float* C, int mrow, int mout, const void* V, float* part, int nsplit, int rps,
+static void ckv_d(const Shape& s, const float* C, int ones, const void* V, float* part, int nsplit, int rps,
                   hipStream_t st) {
   switch (s.d) {
-    case 16: ckv_tpw<T, 16>(s, C, mrow, mout, V, part, nsplit, rps, st); break;
-    case 32: ckv_tpw<T, 32>(s, C, mrow, mout, V, part, nsplit, rps, st); break;
-    case 64: ckv_tpw<T, 64>(s, C, mrow, mout, V, part, nsplit, rps, st); break;
-    default: ckv_tpw<T, 128>(s, C, mrow, mout, V, part, nsplit, rps, st); break;
+    case 16: ckv_mt<T, 16>(s, C, ones, V, part, nsplit, rps, st); break;
+    case 32: ckv_mt<T, 32>(s, C, ones, V, part, nsplit, rps, st); break;
+    case 64: ckv_mt<T, 64>(s, C, ones, V, part, nsplit, rps, st); break;
+    default: ckv_mt<T, 128>(s, C, ones, V, part, nsplit, rps, st); break;
   }
 }
 
@@ -486,9 +650,9 @@ hipError_t launch_ckv_general(const Shape& s, const float* C, int ones, const vo
   const int mout = s.m + ones;
   float* dst = (nsplit == 1) ? S : partial;
   if (s.dtype == 1)
-    ckv_d<bf16_t>(s, C, s.m, mout, V, dst, nsplit, rps, st);
+    ckv_d<bf16_t>(s, C, ones, V, dst, nsplit, rps, st);
   else
-    ckv_d<float>(s, C, s.m, mout, V, dst, nsplit, rps, st);
+    ckv_d<float>(s, C, ones, V, dst, nsplit, rps, st);
   if (nsplit > 1) {
     const int md = mout * s.d;
     hipLaunchKernelGGL(k_ckv_finalize, dim3(cdiv(static_cast<long>(s.G) * md, 256)), dim3(256), 0, st, partial, S,
@@ -514,17 +678,26 @@ hipError_t launch_mix(const Shape& s, const float* X, const float* S, const floa
   return hipGetLastError();
 }
 
+template <typename T, int D>
+static void out_launch(const Shape& s, const float* CQ, const float* P, const float* mu, const void* V,
+                       const float* w, void* Y, int flip, hipStream_t st) {
+  const int tiles_x = cdiv(s.W, 8), tiles_y = cdiv(s.H, 8);
+  const size_t lds = sizeof(float) * OutLds<D>::TOTAL;
+  if (lds > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_out<T, D>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(lds));
+  hipLaunchKernelGGL((k_out<T, D>), dim3(tiles_x * tiles_y, s.G), dim3(256), lds, st, CQ, P, mu,
+                     static_cast<const T*>(V), w, static_cast<T*>(Y), s.N, s.m, s.H, s.W, s.heads, flip, tiles_x);
+}
+
 template <typename T>
 static void out_d(const Shape& s, const float* CQ, const float* P, const float* mu, const void* V, const float* w,
                   void* Y, int flip, hipStream_t st) {
-  const dim3 grid(cdiv(s.N, 64), s.G);
-  const T* v = static_cast<const T*>(V);
-  T* y = static_cast<T*>(Y);
   switch (s.d) {
-    case 16: hipLaunchKernelGGL((k_out<T, 16>), grid, dim3(256), 0, st, CQ, P, mu, v, w, y, s.N, s.m, s.H, s.W, s.heads, flip); break;
-    case 32: hipLaunchKernelGGL((k_out<T, 32>), grid, dim3(256), 0, st, CQ, P, mu, v, w, y, s.N, s.m, s.H, s.W, s.heads, flip); break;
-    case 64: hipLaunchKernelGGL((k_out<T, 64>), grid, dim3(256), 0, st, CQ, P, mu, v, w, y, s.N, s.m, s.H, s.W, s.heads, flip); break;
-    default: hipLaunchKernelGGL((k_out<T, 128>), grid, dim3(256), 0, st, CQ, P, mu, v, w, y, s.N, s.m, s.H, s.W, s.heads, flip); break;
+    case 16: out_launch<T, 16>(s, CQ, P, mu, V, w, Y, flip, st); break;
+    case 32: out_launch<T, 32>(s, CQ, P, mu, V, w, Y, flip, st); break;
+    case 64: out_launch<T, 64>(s, CQ, P, mu, V, w, Y, flip, st); break;
+    default: out_launch<T, 128>(s, CQ, P, mu, V, w, Y, flip, st); break;
   }
 }
 
