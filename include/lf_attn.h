@@ -15,8 +15,9 @@
  *  Shapes:   G = B*heads independent slices; N = H*W tokens, row-major (token n = y*W + x);
  *            m = (H/r)*(W/r) landmarks, landmark index l = Y*(W/r) + X for the r x r block at (Y, X).
  *  Tensors:  Q, K, V, Y, dY, dQ, dK, dV are [B][heads][N][d], contiguous, in params->dtype (float32 or the bf16
- *            bit pattern). Intermediates are float32: L [G][m][d], C_Q and C_K [G][N][m], W_eps and X [G][m][m],
- *            S and P [G][m][d], mu and rstd [G][m]. The DWC weight is float32 [heads*d][3][3].
+ *            bit pattern). Intermediates are float32: L [G][m][d]; C_Q and C_K landmark-major [G][m][N] (element
+ *            [g][l][i] is C[i][l] of the formulas); W_eps and X [G][m][m]; S and P [G][m][d]; mu and rstd [G][m].
+ *            The DWC weight is float32 [heads*d][3][3].
  *  Pointers: every pointer is a device pointer owned by the caller, 16-byte aligned. The library never allocates,
  *            frees or synchronises. Work is enqueued on `stream` (a hipStream_t; NULL means the null stream)
  *            and the call returns as soon as it is enqueued.
@@ -104,7 +105,7 @@ const char* lf_strerror(int code);
 /* L[g][l][c] = (1/r^2) sum_{a,b<r} Q[g][(Y r + a) W + X r + b][c]   ([note] Design 2: r x r average pooling). */
 int lf_landmark_pool(const lf_attn_params* p, const void* Q, float* L, lf_stream_t stream);
 
-/* C_Q[g][i][l] = exp(-sum_c |Q[g][i][c] - L[g][l][c]| / lambda); C_K likewise with K;
+/* C_Q[g][l][i] = exp(-sum_c |Q[g][i][c] - L[g][l][c]| / lambda) (landmark-major); C_K likewise with K;
  * W_eps[g][l][l'] = exp(-||L_l - L_l'||_1 / lambda) + eps [l == l']   ([note] motivation; Designs 2 and 3). */
 int lf_laplace_l1_exp(const lf_attn_params* p, const void* Q, const void* K, const float* L, float* CQ, float* CK,
                       float* We, lf_stream_t stream);
@@ -116,20 +117,20 @@ int lf_laplace_l1_exp(const lf_attn_params* p, const void* Q, const void* K, con
 int lf_ns_pinv(const lf_attn_params* p, const float* We, float* X, float* xs, float* alpha_out, float* resid,
                void* ws, size_t ws_bytes, lf_stream_t stream);
 
-/* S[g][l][c] = sum_i C_K[g][i][l] V[g][i][c]: the "K^T V first" association of linear attention, as a
+/* S[g][l][c] = sum_i C_K[g][l][i] V[g][i][c]: the "K^T V first" association of linear attention, as a
  * deterministic split-N reduction ([note] motivation; Design 2). ws: at least fwd_ws_bytes. */
 int lf_ckv_reduce(const lf_attn_params* p, const float* CK, const void* V, float* S, void* ws, size_t ws_bytes,
                   lf_stream_t stream);
 
-/* Diagonal whitening statistics of C_Q ([note] Design 1): mu[g][l] = mean_i C_Q[g][i][l],
- * rstd[g][l] = 1/sqrt(mean_i (C_Q[g][i][l] - mu)^2 + whiten_eps). */
+/* Diagonal whitening statistics of C_Q ([note] Design 1): mu[g][l] = mean_i C_Q[g][l][i],
+ * rstd[g][l] = 1/sqrt(mean_i (C_Q[g][l][i] - mu)^2 + whiten_eps). */
 int lf_whiten_stats(const lf_attn_params* p, const float* CQ, float* mu, float* rstd, lf_stream_t stream);
 
 /* P[g][l][c] = rstd[g][l] * sum_k X[g][l][k] S[g][k][c]; rstd may be NULL (then 1). */
 int lf_landmark_mix(const lf_attn_params* p, const float* X, const float* S, const float* rstd, float* P,
                     lf_stream_t stream);
 
-/* Y[g][i][c] = sum_l C_Q[g][i][l] P[g][l][c] - sum_l mu[g][l] P[g][l][c] + DWC(V)[g][i][c]
+/* Y[g][i][c] = sum_l C_Q[g][l][i] P[g][l][c] - sum_l mu[g][l] P[g][l][c] + DWC(V)[g][i][c]
  * ([note] Design 1 and flowchart nodes G, H, I). mu may be NULL (no whitening bias); dwc_w may be NULL. */
 int lf_out_gemm_dwc(const lf_attn_params* p, const float* CQ, const float* P, const float* mu, const void* V,
                     const float* dwc_w, void* Y, lf_stream_t stream);

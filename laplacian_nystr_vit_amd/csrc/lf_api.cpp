@@ -121,6 +121,7 @@ inline T* at(void* base, size_t off) {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? LF_OK : LF_EHIP; }
 
+
 #define LF_TRY(expr)                        \
   do {                                      \
     const int _rc = hip_status(expr);       \

@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
       if (t < ntile) acc[t] = mfma16x16x4(a, sB[k * LDB + t * 16 + (ln & 15)], acc[t]);
     }
   }
-  const float* cm = (side == 0 ? CQ : CK) + static_cast<size_t>(g) * N * m;
+  const float* cm = (side == 0 ? CQ : CK) + static_cast<size_t>(g) * m * N;  // landmark-major [m][N]
   float* out = (side == 0 ? Gq : Gk) + static_cast<size_t>(g) * N * m;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + wv * 16 + 4 * (ln >> 4) + r;
       if (i >= N) continue;
-      const float c = cm[static_cast<size_t>(i) * m + l];
+      const float c = cm[static_cast<size_t>(l) * N + i];
       float v = acc[t][r];
       if (side == 0 && whiten) {
         const float ahat = (c - mu_l) * rs_l;

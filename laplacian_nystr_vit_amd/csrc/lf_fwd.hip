@@ -77,23 +77,25 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void k_laplace(const T* __restrict__ Q, const T* __restrict__ K,
                                                 const float* __restrict__ L, float* __restrict__ CQ,
                                                 float* __restrict__ CK, float* __restrict__ We, int N, int m,
-                                                int tilesN, int tilesM, int nlc, int lc, float scale, float eps) {
+                                                int tilesQ, int tilesK, int tilesL, int nlc, int lc, float scale,
+                                                float eps) {
+  // tilesQ / tilesK / tilesL: 64-row tiles of Q, K and L rows per slice (0 leaves that source out).
   int b = blockIdx.x;
   const int lchunk = b % nlc;
   b /= nlc;
-  const int per_slice = 2 * tilesN + tilesM;
+  const int per_slice = tilesQ + tilesK + tilesL;
   const int local = b % per_slice;
   const int g = b / per_slice;
   int src, tile;
-  if (local < tilesN) {
+  if (local < tilesQ) {
     src = 0;
     tile = local;
-  } else if (local < 2 * tilesN) {
+  } else if (local < tilesQ + tilesK) {
     src = 1;
-    tile = local - tilesN;
+    tile = local - tilesQ;
   } else {
     src = 2;
-    tile = local - 2 * tilesN;
+    tile = local - tilesQ - tilesK;
   }
   const int rows = (src == 2) ? m : N;
   const int row = tile * 64 + static_cast<int>(threadIdx.x);
@@ -103,17 +105,22 @@ __global__ __launch_bounds__(64) void k_laplace(const T* __restrict__ Q, const T
   if (row >= rows) return;
 
   float x[D];
-  float* out;
+  float* out;       // this row's output, element l at out[l * ostride]
+  size_t ostride;
   if (src == 2) {
     const float* p = Lg + static_cast<size_t>(row) * D;
 #pragma unroll
     for (int c = 0; c < D; ++c) x[c] = p[c];
     out = We + (static_cast<size_t>(g) * m + row) * m;
+    ostride = 1;
   } else {
     const T* p = (src == 0 ? Q : K) + (static_cast<size_t>(g) * N + row) * D;
 #pragma unroll
     for (int c = 0; c < D; ++c) x[c] = to_f32(p[c]);
-    out = (src == 0 ? CQ : CK) + (static_cast<size_t>(g) * N + row) * m;
+    // C is stored landmark-major (C[g][l][i]): for a fixed landmark the 64 lanes of a wave write 64 consecutive
+    // floats, one 256-byte segment per store instruction.
+    out = (src == 0 ? CQ : CK) + static_cast<size_t>(g) * m * N + row;
+    ostride = static_cast<size_t>(N);
   }
 
   for (int l = l0; l < l1; ++l) {
@@ -128,38 +135,39 @@ __global__ __launch_bounds__(64) void k_laplace(const T* __restrict__ Q, const T
     }
     float v = __builtin_amdgcn_exp2f(((a0 + a1) + (a2 + a3)) * scale);
     if (src == 2 && l == row) v += eps;
-    out[l] = v;
+    out[l * ostride] = v;
   }
 }
 
 // =====================================================================================================
 // whiten_stats: per landmark column of C_Q, mean and 1/sqrt(biased variance + eps_w) over the N tokens
-//   ([note] Design 1, diagonal whitening). Two passes in float64, fixed reduction order.
+//   ([note] Design 1, diagonal whitening). One block per (landmark, slice): the column is one contiguous row of the
+//   landmark-major C_Q. Two passes in float64, fixed reduction order.
 // =====================================================================================================
+__device__ __forceinline__ double block_sum256(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 __global__ __launch_bounds__(256) void k_whiten_stats(const float* __restrict__ CQ, float* __restrict__ mu,
                                                       float* __restrict__ rstd, int N, int m, float weps) {
-  __shared__ double red[4][64];
-  const int g = blockIdx.y;
-  const int ln = threadIdx.x & 63, rg = threadIdx.x >> 6;
-  const int l = blockIdx.x * 64 + ln;
-  const float* c = CQ + static_cast<size_t>(g) * N * m;
+  __shared__ double red[4];
+  const int l = blockIdx.x, g = blockIdx.y;
+  const float* c = CQ + (static_cast<size_t>(g) * m + l) * N;
   double s = 0.0;
-  if (l < m)
-    for (int i = rg; i < N; i += 4) s += static_cast<double>(c[static_cast<size_t>(i) * m + l]);
-  red[rg][ln] = s;
-  __syncthreads();
-  const double mean = (red[0][ln] + red[1][ln] + red[2][ln] + red[3][ln]) / static_cast<double>(N);
-  __syncthreads();
+  for (int i = threadIdx.x; i < N; i += 256) s += static_cast<double>(c[i]);
+  const double mean = block_sum256(s, red) / static_cast<double>(N);
   double v = 0.0;
-  if (l < m)
-    for (int i = rg; i < N; i += 4) {
-      const double dd = static_cast<double>(c[static_cast<size_t>(i) * m + l]) - mean;
-      v += dd * dd;
-    }
-  red[rg][ln] = v;
-  __syncthreads();
-  if (rg == 0 && l < m) {
-    const double var = (red[0][ln] + red[1][ln] + red[2][ln] + red[3][ln]) / static_cast<double>(N);
+  for (int i = threadIdx.x; i < N; i += 256) {
+    const double dd = static_cast<double>(c[i]) - mean;
+    v += dd * dd;
+  }
+  const double var = block_sum256(v, red) / static_cast<double>(N);
+  if (threadIdx.x == 0) {
     mu[static_cast<size_t>(g) * m + l] = static_cast<float>(mean);
     rstd[static_cast<size_t>(g) * m + l] = static_cast<float>(1.0 / sqrt(var + static_cast<double>(weps)));
   }
@@ -182,20 +190,20 @@ template <typename T, int D, int MT>
 __global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ C, const T* __restrict__ V,
                                                      float* __restrict__ part, int N, int mrow, int ones,
                                                      int nsplit, int rows_per_split) {
-  // LDS: the C chunk exactly as it lies in memory (64 rows of mrow floats, then MT*16 floats of zero pad that
-  // out-of-range landmark columns of the last row may touch), and the V chunk with a 16 mod 32 row stride.
-  extern __shared__ float smem[];
+  // LDS: the C chunk as [landmark][64 tokens] (row stride 68) and the V chunk as [64 tokens][D] (stride 16 mod 32).
+  // Landmark rows >= mrow are never written; they only feed output rows that are not stored.
+  constexpr int LDC = 68;
   constexpr int DT = D / 16;
   constexpr int CTW = (DT + 3) / 4;  // column tiles per wave
   constexpr int LDV = ((D + 31) / 32) * 32 + 16;
-  constexpr int NQC = MT;            // float4 loads of C per thread for a full chunk (64 * mrow <= 1024 * MT)
+  constexpr int NQC = MT;            // float4 loads of C per thread: MT*16 landmarks x 16 float4
   constexpr int NQV = D / 16;        // 4-element loads of V per thread for a full chunk
+  __shared__ float sC[MT * 16 * LDC];
+  __shared__ float sV[64 * LDV];
   const int mout = mrow + ones;
-  float* sC = smem;
-  float* sV = smem + 64 * mrow + MT * 16;
   const int g = blockIdx.x / nsplit, s = blockIdx.x % nsplit;
   const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
-  for (int q = tid; q < MT * 16; q += 256) sC[64 * mrow + q] = 0.f;
+  const bool vec = (N & 3) == 0;  // landmark rows start 16-byte aligned
 
   f32x4 acc[MT][CTW];
 #pragma unroll
@@ -204,26 +212,30 @@ __global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ C
     for (int b = 0; b < CTW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int r0 = s * rows_per_split, r1 = min(N, r0 + rows_per_split);
-  const float* cg = C + static_cast<size_t>(g) * N * mrow;
+  const float* cg = C + static_cast<size_t>(g) * mrow * N;
   const T* vg = V + static_cast<size_t>(g) * N * D;
   for (int c0 = r0; c0 < r1; c0 += 64) {
     const int nr = min(64, r1 - c0);
-    const int nC = nr * mrow;  // floats of C in this chunk
-    const float* csrc = cg + static_cast<size_t>(c0) * mrow;
     const T* vsrc = vg + static_cast<size_t>(c0) * D;
     float4 cbuf[NQC];
     float4 vbuf[NQV];
 #pragma unroll
     for (int q = 0; q < NQC; ++q) {
-      const int e = 4 * (tid + 256 * q);
-      if (e + 3 < nC) {
-        cbuf[q] = load4(csrc + e);
-      } else {
-        cbuf[q].x = e + 0 < nC ? csrc[e + 0] : 0.f;
-        cbuf[q].y = e + 1 < nC ? csrc[e + 1] : 0.f;
-        cbuf[q].z = e + 2 < nC ? csrc[e + 2] : 0.f;
-        cbuf[q].w = e + 3 < nC ? csrc[e + 3] : 0.f;
+      const int e = tid + 256 * q;
+      const int l = e >> 4, i = 4 * (e & 15);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (l < mrow) {
+        const float* src = cg + static_cast<size_t>(l) * N + c0 + i;
+        if (vec && i + 3 < nr) {
+          v = load4(src);
+        } else {
+          v.x = i + 0 < nr ? src[0] : 0.f;
+          v.y = i + 1 < nr ? src[1] : 0.f;
+          v.z = i + 2 < nr ? src[2] : 0.f;
+          v.w = i + 3 < nr ? src[3] : 0.f;
+        }
       }
+      cbuf[q] = v;
     }
 #pragma unroll
     for (int q = 0; q < NQV; ++q) {
@@ -233,14 +245,13 @@ __global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ C
     __syncthreads();  // the previous chunk's MFMA reads are done
 #pragma unroll
     for (int q = 0; q < NQC; ++q) {
-      const int e = 4 * (tid + 256 * q);
-      if (e < 64 * mrow) store4(sC + e, cbuf[q]);
+      const int e = tid + 256 * q;
+      store4(sC + (e >> 4) * LDC + 4 * (e & 15), cbuf[q]);
     }
 #pragma unroll
     for (int q = 0; q < NQV; ++q) {
       const int e = 4 * (tid + 256 * q);
-      const int rr = e / D, cc = e % D;
-      store4(sV + rr * LDV + cc, vbuf[q]);
+      store4(sV + (e / D) * LDV + (e % D), vbuf[q]);
     }
     __syncthreads();
     if (wv * CTW < DT) {
@@ -253,7 +264,7 @@ __global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ C
 #pragma unroll
         for (int lt = 0; lt < MT; ++lt) {
           const int l = lt * 16 + (ln & 15);
-          float a = sC[kr * mrow + l];
+          float a = sC[l * LDC + kr];
           if (l == mrow) a = (ones && kr < nr) ? 1.f : 0.f;
 #pragma unroll
           for (int ct = 0; ct < CTW; ++ct) acc[lt][ct] = mfma16x16x4(a, b[ct], acc[lt][ct]);
@@ -362,31 +373,30 @@ __global__ __launch_bounds__(256) void k_mix(const float* __restrict__ X, const 
 }
 
 // =====================================================================================================
-// out_gemm_dwc: Y[g][i][c] = sum_l C_Q[g][i][l] P[g][l][c] - sum_l mu[g][l] P[g][l][c] + DWC(V)[g][i][c]
+// out_gemm_dwc: Y[g][i][c] = sum_l C_Q[g][l][i] P[g][l][c] - sum_l mu[g][l] P[g][l][c] + DWC(V)[g][i][c]
 //   ([note] Design 1: output = ZV + DWC(V); flowchart nodes G, H, I). The whitening bias is the folded form of
 //   (C_Q - mu) rstd P with rstd already applied to P. With flip = 1 the 3x3 filter is rotated by 180 degrees,
 //   which makes the stencil the adjoint of DWC (the backward pass uses that for dV = C_K dS + DWC^T(dY)).
 // Block: an 8 x 8 patch of the token grid of one slice (64 tokens) and all D channels.
 //   1. The 10 x 10 halo of V around the patch is staged once in LDS (zero outside the grid).
-//   2. The K = m reduction runs on fp32 MFMA (wave w: tokens 16w..16w+15), with 64-landmark chunks of C_Q and
-//      P staged in LDS; all global loads of a chunk are issued before the LDS writes.
-//   3. The accumulators go through LDS to a (token, 4 channels) layout, where the bias and the 3x3 stencil are
-//      added and Y is written with 16-byte (fp32) or 8-byte (bf16) coalesced stores.
+//   2. The product runs transposed on fp32 MFMA, Y^T[c][u] = sum_l P[l][c] C[l][u], so that both operands are
+//      read from their natural [landmark][...] layouts and each lane's accumulator holds 4 consecutive channels of
+//      one token. 64-landmark chunks of C (landmark-major) and P are staged in LDS; all global loads of a chunk
+//      are issued before the LDS writes.
+//   3. The epilogue adds the bias and the 3x3 stencil per float4 and stores Y per (token, 4 channels).
 // =====================================================================================================
 template <int D>
 struct OutLds {
-  static constexpr int LDV = D + 4;                        // V halo row stride (float4 aligned)
-  static constexpr int LDA = 66;                           // 2 mod 32: conflict-free A-style reads
-  static constexpr int LDB = ((D + 31) / 32) * 32 + 16;    // 16 mod 32: conflict-free B-style reads
-  static constexpr int LDO = D + 4;
+  static constexpr int LDV = D + 4;                       // V halo row stride (float4 aligned)
+  static constexpr int LDB = ((D + 31) / 32) * 32 + 16;   // P rows: 16 mod 32 (conflict-free MFMA reads)
+  static constexpr int LDC = 80;                          // C rows (64 tokens): 16 mod 32
   static constexpr int VH = 0;
-  static constexpr int A = VH + 100 * LDV;
-  static constexpr int B = A + 64 * LDA;
+  static constexpr int C = VH + 100 * LDV;
+  static constexpr int B = C + 64 * LDC;
   static constexpr int MU = B + 64 * LDB;
   static constexpr int WT = MU + 64;
   static constexpr int BIAS = WT + 9 * D;
   static constexpr int TOTAL = BIAS + D;
-  static_assert(64 * LDO <= 64 * LDA + 64 * LDB, "output staging must fit in the A and B areas");
 };
 
 template <typename T, int D>
@@ -397,19 +407,19 @@ __global__ __launch_bounds__(256) void k_out(const float* __restrict__ CQ, const
   using Lay = OutLds<D>;
   extern __shared__ float smem[];
   float* sVh = smem + Lay::VH;
-  float* sA = smem + Lay::A;
+  float* sC = smem + Lay::C;
   float* sB = smem + Lay::B;
   float* sMu = smem + Lay::MU;
   float* sWt = smem + Lay::WT;
   float* sBias = smem + Lay::BIAS;
-  float* sO = smem + Lay::A;  // reuses the A and B areas after the GEMM
-  constexpr int DT = D / 16;
+  constexpr int CS = D / 16;             // channel strips of 16
+  constexpr int SPW = (CS + 3) / 4;      // strips per wave
   constexpr int C4 = D / 4;
   const int g = blockIdx.y;
   const int ty0 = (blockIdx.x / tiles_x) * 8, tx0 = (blockIdx.x % tiles_x) * 8;
   const int h = g % heads;
   const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
-  const float* cq = CQ + static_cast<size_t>(g) * N * m;
+  const float* cg = CQ + static_cast<size_t>(g) * m * N;
   const float* pg = P + static_cast<size_t>(g) * m * D;
   const T* vg = V + static_cast<size_t>(g) * N * D;
   const bool has_w = w != nullptr;
@@ -440,19 +450,21 @@ __global__ __launch_bounds__(256) void k_out(const float* __restrict__ CQ, const
   }
   float bias_acc = 0.f;
 
-  // 2. C_Q (tile tokens x landmarks) times P, in 64-landmark chunks
-  f32x4 acc[DT];
+  // 2. Y^T = P^T C over 64-landmark chunks
+  f32x4 acc[SPW][4];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < SPW; ++a)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int lc0 = 0; lc0 < m; lc0 += 64) {
     const int nl = min(64, m - lc0);
-    float av[16];
+    float cv[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int e = tid + 256 * q;
-      const int u = e >> 6, cc = e & 63;
+      const int l = e >> 6, u = e & 63;
       const int y = ty0 + (u >> 3), x = tx0 + (u & 7);
-      av[q] = (y < H && x < W && cc < nl) ? cq[static_cast<size_t>(y * W + x) * m + lc0 + cc] : 0.f;
+      cv[q] = (l < nl && y < H && x < W) ? cg[static_cast<size_t>(lc0 + l) * N + y * W + x] : 0.f;
     }
     constexpr int NQB = (16 * D + 255) / 256;
     float4 bv[NQB];
@@ -468,7 +480,7 @@ __global__ __launch_bounds__(256) void k_out(const float* __restrict__ CQ, const
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int e = tid + 256 * q;
-      sA[(e >> 6) * Lay::LDA + (e & 63)] = av[q];
+      sC[(e >> 6) * Lay::LDC + (e & 63)] = cv[q];
     }
 #pragma unroll
     for (int q = 0; q < NQB; ++q) {
@@ -483,52 +495,58 @@ __global__ __launch_bounds__(256) void k_out(const float* __restrict__ CQ, const
     const int ksteps = (nl + 3) / 4;
     for (int ks = 0; ks < ksteps; ++ks) {
       const int k = ks * 4 + (ln >> 4);
-      const float a = sA[(wv * 16 + (ln & 15)) * Lay::LDA + k];
+      float bt[4];
 #pragma unroll
-      for (int t = 0; t < DT; ++t) acc[t] = mfma16x16x4(a, sB[k * Lay::LDB + t * 16 + (ln & 15)], acc[t]);
+      for (int t = 0; t < 4; ++t) bt[t] = sC[k * Lay::LDC + t * 16 + (ln & 15)];
+#pragma unroll
+      for (int a = 0; a < SPW; ++a) {
+        const int strip = wv * SPW + a;
+        if (strip < CS) {
+          const float av = sB[k * Lay::LDB + strip * 16 + (ln & 15)];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[a][t] = mfma16x16x4(av, bt[t], acc[a][t]);
+        }
+      }
     }
-  }
-  __syncthreads();  // all GEMM reads done before sO overwrites the A and B areas
-#pragma unroll
-  for (int t = 0; t < DT; ++t) {
-    const int c = t * 16 + (ln & 15);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sO[(wv * 16 + 4 * (ln >> 4) + r) * Lay::LDO + c] = acc[t][r];
   }
   if (tid < D) sBias[tid] = bias_acc;
   __syncthreads();
 
-  // 3. epilogue per (token, 4 channels)
+  // 3. epilogue: lane holds Y[token 16 t + ln%16][channels 16 strip + 4 (ln/16) .. +3]
   T* yg = Y + static_cast<size_t>(g) * N * D;
-  constexpr int NI = (64 * C4 + 255) / 256;
 #pragma unroll
-  for (int q = 0; q < NI; ++q) {
-    const int e = tid + 256 * q;
-    if (e >= 64 * C4) break;
-    const int u = e / C4, c4 = e % C4;
-    const int ty = u >> 3, tx = u & 7;
-    const int y = ty0 + ty, x = tx0 + tx;
-    if (y >= H || x >= W) continue;
-    float4 o = *reinterpret_cast<const float4*>(sO + u * Lay::LDO + 4 * c4);
-    const float4 b = *reinterpret_cast<const float4*>(sBias + 4 * c4);
-    o.x -= b.x;
-    o.y -= b.y;
-    o.z -= b.z;
-    o.w -= b.w;
+  for (int a = 0; a < SPW; ++a) {
+    const int strip = wv * SPW + a;
+    if (strip >= CS) continue;
+    const int c0 = strip * 16 + 4 * (ln >> 4);
+    const float4 b = *reinterpret_cast<const float4*>(sBias + c0);
+    float4 k9[9];
     if (has_w) {
 #pragma unroll
-      for (int a = 0; a < 3; ++a)
-#pragma unroll
-        for (int bb = 0; bb < 3; ++bb) {
-          const float4 v = *reinterpret_cast<const float4*>(sVh + ((ty + a) * 10 + tx + bb) * Lay::LDV + 4 * c4);
-          const float4 k4 = *reinterpret_cast<const float4*>(sWt + (a * 3 + bb) * D + 4 * c4);
-          o.x += k4.x * v.x;
-          o.y += k4.y * v.y;
-          o.z += k4.z * v.z;
-          o.w += k4.w * v.w;
-        }
+      for (int q = 0; q < 9; ++q) k9[q] = *reinterpret_cast<const float4*>(sWt + q * D + c0);
     }
-    store4(yg + static_cast<size_t>(y * W + x) * D + 4 * c4, o);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int u = t * 16 + (ln & 15);
+      const int ty = u >> 3, tx = u & 7;
+      const int y = ty0 + ty, x = tx0 + tx;
+      if (y >= H || x >= W) continue;
+      float4 o = make_float4(acc[a][t][0] - b.x, acc[a][t][1] - b.y, acc[a][t][2] - b.z, acc[a][t][3] - b.w);
+      if (has_w) {
+#pragma unroll
+        for (int aa = 0; aa < 3; ++aa)
+#pragma unroll
+          for (int bb = 0; bb < 3; ++bb) {
+            const float4 v = *reinterpret_cast<const float4*>(sVh + ((ty + aa) * 10 + tx + bb) * Lay::LDV + c0);
+            const float4 k4 = k9[aa * 3 + bb];
+            o.x += k4.x * v.x;
+            o.y += k4.y * v.y;
+            o.z += k4.z * v.z;
+            o.w += k4.w * v.w;
+          }
+      }
+      store4(yg + static_cast<size_t>(y * W + x) * D + c0, o);
+    }
   }
 }
 
@@ -556,9 +574,11 @@ hipError_t launch_landmark_pool(const Shape& s, const void* Q, float* L, hipStre
 
 template <typename T, int D>
 static void laplace_t(const Shape& s, const void* Q, const void* K, const float* L, float* CQ, float* CK, float* We,
-                      hipStream_t st) {
+                      int srcmask, hipStream_t st) {
   const int tilesN = cdiv(s.N, 64), tilesM = cdiv(s.m, 64);
-  const long waves = static_cast<long>(s.G) * (2 * tilesN + tilesM);
+  const int tq = (srcmask & 1) ? tilesN : 0, tk = (srcmask & 2) ? tilesN : 0, tl = (srcmask & 4) ? tilesM : 0;
+  const long waves = static_cast<long>(s.G) * (tq + tk + tl);
+  if (waves == 0) return;
   // Split the landmark loop until the chip holds about 12 waves per CU, keeping >= 8 landmarks per wave.
   int nlc = 1;
   while (waves * nlc < 3072 && cdiv(s.m, nlc * 2) >= 8) nlc *= 2;
@@ -567,32 +587,31 @@ static void laplace_t(const Shape& s, const void* Q, const void* K, const float*
   const float scale = static_cast<float>(-1.4426950408889634 / static_cast<double>(s.lambda));
   const dim3 grid(static_cast<unsigned>(waves * nlc));
   hipLaunchKernelGGL((k_laplace<T, D>), grid, dim3(64), 0, st, static_cast<const T*>(Q), static_cast<const T*>(K), L,
-                     CQ, CK, We, s.N, s.m, tilesN, tilesM, nlc, lc, scale, s.eps);
+                     CQ, CK, We, s.N, s.m, tq, tk, tl, nlc, lc, scale, s.eps);
 }
 
 template <typename T>
 static void laplace_d(const Shape& s, const void* Q, const void* K, const float* L, float* CQ, float* CK, float* We,
-                      hipStream_t st) {
+                      int srcmask, hipStream_t st) {
   switch (s.d) {
-    case 16: laplace_t<T, 16>(s, Q, K, L, CQ, CK, We, st); break;
-    case 32: laplace_t<T, 32>(s, Q, K, L, CQ, CK, We, st); break;
-    case 64: laplace_t<T, 64>(s, Q, K, L, CQ, CK, We, st); break;
-    default: laplace_t<T, 128>(s, Q, K, L, CQ, CK, We, st); break;
+    case 16: laplace_t<T, 16>(s, Q, K, L, CQ, CK, We, srcmask, st); break;
+    case 32: laplace_t<T, 32>(s, Q, K, L, CQ, CK, We, srcmask, st); break;
+    case 64: laplace_t<T, 64>(s, Q, K, L, CQ, CK, We, srcmask, st); break;
+    default: laplace_t<T, 128>(s, Q, K, L, CQ, CK, We, srcmask, st); break;
   }
 }
 
 hipError_t launch_laplace(const Shape& s, const void* Q, const void* K, const float* L, float* CQ, float* CK,
-                          float* We, hipStream_t st) {
+                          float* We, hipStream_t st, int srcmask) {
   if (s.dtype == 1)
-    laplace_d<bf16_t>(s, Q, K, L, CQ, CK, We, st);
+    laplace_d<bf16_t>(s, Q, K, L, CQ, CK, We, srcmask, st);
   else
-    laplace_d<float>(s, Q, K, L, CQ, CK, We, st);
+    laplace_d<float>(s, Q, K, L, CQ, CK, We, srcmask, st);
   return hipGetLastError();
 }
 
 hipError_t launch_whiten_stats(const Shape& s, const float* CQ, float* mu, float* rstd, hipStream_t st) {
-  hipLaunchKernelGGL(k_whiten_stats, dim3(cdiv(s.m, 64), s.G), dim3(256), 0, st, CQ, mu, rstd, s.N, s.m,
-                     s.whiten_eps);
+  hipLaunchKernelGGL(k_whiten_stats, dim3(s.m, s.G), dim3(256), 0, st, CQ, mu, rstd, s.N, s.m, s.whiten_eps);
   return hipGetLastError();
 }
 
@@ -610,11 +629,7 @@ void ckv_split(const Shape& s, int* nsplit, int* rows_per_split) {
 template <typename T, int D, int MT>
 static void ckv_launch(const Shape& s, const float* C, int ones, const void* V, float* part, int nsplit, int rps,
                        hipStream_t st) {
-  const size_t lds = sizeof(float) * (64 * s.m + MT * 16 + 64 * (((D + 31) / 32) * 32 + 16));
-  if (lds > 64 * 1024)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ckv_partial<T, D, MT>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  hipLaunchKernelGGL((k_ckv_partial<T, D, MT>), dim3(s.G * nsplit), dim3(256), lds, st, C, static_cast<const T*>(V),
+  hipLaunchKernelGGL((k_ckv_partial<T, D, MT>), dim3(s.G * nsplit), dim3(256), 0, st, C, static_cast<const T*>(V),
                      part, s.N, s.m, ones, nsplit, rps);
 }
 

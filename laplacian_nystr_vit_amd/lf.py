@@ -236,10 +236,10 @@ def lf_out_gemm_dwc(p, CQ, P, mu, V, dwc_w, Y, stream=None) -> None:
 # Conveniences built only from the calls above plus torch allocation.
 # ------------------------------------------------------------------------------------------------------------
 def saved_views(p: LfAttnParams, saved: torch.Tensor) -> dict:
-    """float32 views of the intermediates inside a `saved` buffer, shaped per slice."""
+    """float32 views of the intermediates inside a `saved` buffer, shaped per slice (C_Q, C_K landmark-major)."""
     lay = lf_attn_saved_layout(p)
     G, N, m, d, K = p.G, p.N, p.m, p.d, p.ns_iters
-    shapes = {"L": (G, m, d), "CQ": (G, N, m), "CK": (G, N, m), "We": (G, m, m), "xs": (G, K + 1, m, m),
+    shapes = {"L": (G, m, d), "CQ": (G, m, N), "CK": (G, m, N), "We": (G, m, m), "xs": (G, K + 1, m, m),
               "mu": (G, m), "rstd": (G, m), "S": (G, m, d), "P": (G, m, d), "alpha": (G,)}
     out = {}
     for k, shp in shapes.items():

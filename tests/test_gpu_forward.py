@@ -50,8 +50,9 @@ def test_forward_end_to_end(wl):
     # intermediates the forward kept in the saved buffer
     rs = lambda a: np.asarray(a).reshape((G,) + np.asarray(a).shape[2:])
     assert relF(host(sv["L"]), rs(ref["L"])) <= 1e-6
-    assert relF(host(sv["CQ"]), rs(ref["CQ"])) <= 1e-5
-    assert relF(host(sv["CK"]), rs(ref["CK"])) <= 1e-5
+    # the library stores C_Q and C_K landmark-major: [G][m][N]
+    assert relF(host(sv["CQ"]).transpose(0, 2, 1), rs(ref["CQ"])) <= 1e-5
+    assert relF(host(sv["CK"]).transpose(0, 2, 1), rs(ref["CK"])) <= 1e-5
     assert relF(host(sv["We"]), rs(ref["We"])) <= 1e-5
     Xk = host(sv["xs"])[:, wl.ns_iters]
     assert relF(Xk, rs(ref["X"])) <= tol(wl)
@@ -100,8 +101,8 @@ def test_stage_pool_and_laplace(wl):
     Lr = _r32(Lref)
     for g in range(G):
         q, k = inp["Q"].reshape(G, N, d)[g], inp["K"].reshape(G, N, d)[g]
-        assert relF(host(CQ).reshape(G, N, m)[g], O.laplacian_kernel(q, Lr[g], wl.lam)) <= 1e-5
-        assert relF(host(CK).reshape(G, N, m)[g], O.laplacian_kernel(k, Lr[g], wl.lam)) <= 1e-5
+        assert relF(host(CQ).reshape(G, m, N)[g].T, O.laplacian_kernel(q, Lr[g], wl.lam)) <= 1e-5
+        assert relF(host(CK).reshape(G, m, N)[g].T, O.laplacian_kernel(k, Lr[g], wl.lam)) <= 1e-5
         Wref = O.laplacian_kernel(Lr[g], Lr[g], wl.lam) + wl.eps * np.eye(m)
         assert relF(host(We).reshape(G, m, m)[g], Wref) <= 1e-5
 
@@ -169,13 +170,13 @@ def test_stage_ckv_mix_out(wl):
     fwd_b, _, _ = lf.lf_attn_query(p)
     ws = torch.empty(fwd_b, dtype=torch.uint8, device="cuda")
     S = torch.empty(G * m * d, device="cuda")
-    lf.lf_ckv_reduce(p, _f32(CK), t["V"], S, ws)
+    lf.lf_ckv_reduce(p, _f32(CK.transpose(0, 2, 1)), t["V"], S, ws)
     Sref = np.einsum("gil,gic->glc", CK, V)
     P = torch.empty(G * m * d, device="cuda")
     lf.lf_landmark_mix(p, _f32(X), _f32(Sref), None, P)
     Pref = np.einsum("glk,gkc->glc", X, _r32(Sref))
     Y = torch.empty_like(t["Q"])
-    lf.lf_out_gemm_dwc(p, _f32(CQ), _f32(Pref), None, t["V"], t["w"], Y)
+    lf.lf_out_gemm_dwc(p, _f32(CQ.transpose(0, 2, 1)), _f32(Pref), None, t["V"], t["w"], Y)
     torch.cuda.synchronize()
     assert relF(host(S).reshape(G, m, d), Sref) <= 1e-5
     assert relF(host(P).reshape(G, m, d), Pref) <= 1e-5
@@ -196,7 +197,7 @@ def test_stage_whiten_stats_and_folded_output():
     CQ = _r32(np.asarray(ref["CQ"]).reshape(G, N, m))
     mu = torch.empty(G * m, device="cuda")
     rstd = torch.empty(G * m, device="cuda")
-    lf.lf_whiten_stats(p, _f32(CQ), mu, rstd)
+    lf.lf_whiten_stats(p, _f32(CQ.transpose(0, 2, 1)), mu, rstd)
     torch.cuda.synchronize()
     A, muref, rsref = zip(*[O.whiten_columns(CQ[g], wl.whiten_eps) for g in range(G)])
     assert relF(host(mu).reshape(G, m), np.stack(muref)) <= 1e-6
