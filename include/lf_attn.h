@@ -135,6 +135,13 @@ int lf_landmark_mix(const lf_attn_params* p, const float* X, const float* S, con
 int lf_out_gemm_dwc(const lf_attn_params* p, const float* CQ, const float* P, const float* mu, const void* V,
                     const float* dwc_w, void* Y, lf_stream_t stream);
 
+/* The same output without a materialised C_Q (no whitening): every 8 x 8 token tile computes its C_Q block
+ * exp(-||q_i - l||_1 / lambda) from Q [B][heads][N][d] (the dtype of p) and the landmarks L [G][m][d] fp32, then
+ * Y = C_Q P + DWC(V). Distance fused with the product, as the output stage of [note] Design 3 suggests to save
+ * memory traffic. Same conventions and errors as lf_out_gemm_dwc. */
+int lf_out_gemm_dwc_fused(const lf_attn_params* p, const void* Q, const float* L, const float* P, const void* V,
+                          const float* dwc_w, void* Y, lf_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -205,6 +205,9 @@ int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const voi
   float* part = at<float>(ws, w.part);
   float* nstmp = at<float>(ws, w.nstmp);
 
+  // C_Q is materialised: the backward pass and the whitening statistics need it, and on the shapes measured so
+  // far the distance launch plus the output GEMM beats recomputing C_Q inside the output kernel
+  // (lf_out_gemm_dwc_fused).
   LF_TRY(lf::launch_landmark_pool(s, Q, L, st));
   LF_TRY(lf::launch_laplace(s, Q, K, L, CQ, CK, We, st));
   if (wh) LF_TRY(lf::launch_whiten_stats(s, CQ, mu, rstd, st));
@@ -304,6 +307,17 @@ int lf_landmark_mix(const lf_attn_params* p, const float* X, const float* S, con
   if (!X || !S || !P || !aligned16(X) || !aligned16(S) || !aligned16(P)) return LF_EINVAL;
   if (rstd && !aligned16(rstd)) return LF_EINVAL;
   return hip_status(lf::launch_mix(make_shape(p), X, S, rstd, P, nullptr, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int lf_out_gemm_dwc_fused(const lf_attn_params* p, const void* Q, const float* L, const float* P, const void* V,
+                          const float* dwc_w, void* Y, lf_stream_t stream) {
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  if (!Q || !L || !P || !V || !Y) return LF_EINVAL;
+  if (!aligned16(Q) || !aligned16(L) || !aligned16(P) || !aligned16(V) || !aligned16(Y)) return LF_EINVAL;
+  if (dwc_w && !aligned16(dwc_w)) return LF_EINVAL;
+  return hip_status(
+      lf::launch_out_fused(make_shape(p), Q, L, P, V, dwc_w, Y, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int lf_out_gemm_dwc(const lf_attn_params* p, const float* CQ, const float* P, const float* mu, const void* V,

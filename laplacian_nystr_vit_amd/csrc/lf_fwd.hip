@@ -399,12 +399,14 @@ struct OutLds {
   static constexpr int TOTAL = BIAS + D;
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_out(const float* __restrict__ CQ, const float* __restrict__ P,
+template <typename T, int D, bool FUSED>
+__global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const float* __restrict__ P,
                                              const float* __restrict__ mu, const T* __restrict__ V,
                                              const float* __restrict__ w, T* __restrict__ Y, int N, int m, int H,
-                                             int W, int heads, int flip, int tiles_x) {
+                                             int W, int heads, int flip, int tiles_x, const T* __restrict__ Q,
+                                             const float* __restrict__ L, float scale) {
   using Lay = OutLds<D>;
+  constexpr int NWV = 8, NT = 64 * NWV;  // 8 waves: two blocks per CU (LDS) give 4 waves per SIMD
   extern __shared__ float smem[];
   float* sVh = smem + Lay::VH;
   float* sC = smem + Lay::C;
@@ -412,9 +414,11 @@ __global__ __launch_bounds__(256) void k_out(const float* __restrict__ CQ, const
   float* sMu = smem + Lay::MU;
   float* sWt = smem + Lay::WT;
   float* sBias = smem + Lay::BIAS;
-  constexpr int CS = D / 16;             // channel strips of 16
-  constexpr int SPW = (CS + 3) / 4;      // strips per wave
+  constexpr int CS = D / 16;                     // channel strips of 16
+  constexpr int NP = CS * 4;                     // output tiles: (channel strip, 16-token tile) pairs
+  constexpr int PPW = (NP + NWV - 1) / NWV;      // tiles per wave
   constexpr int C4 = D / 4;
+  constexpr int LQM = 64 / NWV;                  // FUSED: most landmarks of a chunk per wave
   const int g = blockIdx.y;
   const int ty0 = (blockIdx.x / tiles_x) * 8, tx0 = (blockIdx.x % tiles_x) * 8;
   const int h = g % heads;
@@ -426,11 +430,11 @@ __global__ __launch_bounds__(256) void k_out(const float* __restrict__ CQ, const
 
   // 1. V halo and filter taps
   if (has_w) {
-    constexpr int NQ = (100 * C4 + 255) / 256;
+    constexpr int NQ = (100 * C4 + NT - 1) / NT;
     float4 vb[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       vb[q] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (e < 100 * C4) {
         const int tok = e / C4, c4 = e % C4;
@@ -440,51 +444,102 @@ __global__ __launch_bounds__(256) void k_out(const float* __restrict__ CQ, const
     }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       if (e < 100 * C4) store4(sVh + (e / C4) * Lay::LDV + 4 * (e % C4), vb[q]);
     }
-    for (int e = tid; e < 9 * D; e += 256) {
+    for (int e = tid; e < 9 * D; e += NT) {
       const int q = e / D, c = e % D;
       sWt[e] = w[(static_cast<size_t>(h) * D + c) * 9 + (flip ? 8 - q : q)];
     }
   }
   float bias_acc = 0.f;
 
+  // FUSED: C_Q is not read from memory but computed here. Every wave holds the Q rows of the patch's 64 tokens
+  // (lane = token) and computes its share of each landmark chunk, landmark coordinates arriving through scalar
+  // loads (the landmark index is wave-uniform).
+  float xq[FUSED ? D : 1];
+  bool tok_ok = false;
+  const float* Lg = nullptr;
+  int wq = 0;
+  if constexpr (FUSED) {
+    const int y = ty0 + (ln >> 3), x = tx0 + (ln & 7);
+    tok_ok = y < H && x < W;
+    const T* qp = Q + (static_cast<size_t>(g) * N + (tok_ok ? y * W + x : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < D; c += 4) {
+      const float4 v = tok_ok ? load4(qp + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      xq[c] = v.x;
+      xq[c + 1] = v.y;
+      xq[c + 2] = v.z;
+      xq[c + 3] = v.w;
+    }
+    Lg = L + static_cast<size_t>(g) * m * D;
+    wq = __builtin_amdgcn_readfirstlane(wv);
+  }
+
   // 2. Y^T = P^T C over 64-landmark chunks
-  f32x4 acc[SPW][4];
+  f32x4 acc[PPW];
 #pragma unroll
-  for (int a = 0; a < SPW; ++a)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < PPW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int lc0 = 0; lc0 < m; lc0 += 64) {
     const int nl = min(64, m - lc0);
-    float cv[16];
+    // FUSED: landmarks per wave; rows nl .. NWV lq - 1 (which cover the MFMA's 4-row padding) come out as zeros
+    const int lq = (nl + NWV - 1) / NWV;
+    constexpr int NCV = FUSED ? LQM : 4096 / NT;
+    float cv[NCV];
+    if constexpr (FUSED) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int e = tid + 256 * q;
-      const int l = e >> 6, u = e & 63;
-      const int y = ty0 + (u >> 3), x = tx0 + (u & 7);
-      cv[q] = (l < nl && y < H && x < W) ? cg[static_cast<size_t>(lc0 + l) * N + y * W + x] : 0.f;
+      for (int q = 0; q < LQM; ++q) {
+        const int l = wq * lq + q;
+        float v = 0.f;
+        if (q < lq && l < nl) {
+          const float* __restrict__ lp = Lg + static_cast<size_t>(lc0 + l) * D;
+          float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+          for (int c = 0; c < D; c += 4) {
+            a0 += fabsf(xq[c + 0] - lp[c + 0]);
+            a1 += fabsf(xq[c + 1] - lp[c + 1]);
+            a2 += fabsf(xq[c + 2] - lp[c + 2]);
+            a3 += fabsf(xq[c + 3] - lp[c + 3]);
+          }
+          v = tok_ok ? __builtin_amdgcn_exp2f(((a0 + a1) + (a2 + a3)) * scale) : 0.f;
+        }
+        cv[q] = v;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < NCV; ++q) {
+        const int e = tid + NT * q;
+        const int l = e >> 6, u = e & 63;
+        const int y = ty0 + (u >> 3), x = tx0 + (u & 7);
+        cv[q] = (l < nl && y < H && x < W) ? cg[static_cast<size_t>(lc0 + l) * N + y * W + x] : 0.f;
+      }
     }
-    constexpr int NQB = (16 * D + 255) / 256;
+    constexpr int NQB = (16 * D + NT - 1) / NT;
     float4 bv[NQB];
 #pragma unroll
     for (int q = 0; q < NQB; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       const int rr = e / C4, c4 = e % C4;
       bv[q] = (e < 16 * D && rr < nl) ? load4(pg + static_cast<size_t>(lc0 + rr) * D + 4 * c4)
                                       : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const float muv = (mu && tid < 64 && tid < nl) ? mu[static_cast<size_t>(g) * m + lc0 + tid] : 0.f;
     __syncthreads();  // previous chunk's reads are done
+    if constexpr (FUSED) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int e = tid + 256 * q;
-      sC[(e >> 6) * Lay::LDC + (e & 63)] = cv[q];
+      for (int q = 0; q < LQM; ++q)
+        if (q < lq) sC[(wq * lq + q) * Lay::LDC + ln] = cv[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < NCV; ++q) {
+        const int e = tid + NT * q;
+        sC[(e >> 6) * Lay::LDC + (e & 63)] = cv[q];
+      }
     }
 #pragma unroll
     for (int q = 0; q < NQB; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       if (e < 16 * D) store4(sB + (e / C4) * Lay::LDB + 4 * (e % C4), bv[q]);
     }
     if (tid < 64) sMu[tid] = muv;
@@ -495,16 +550,14 @@ __global__ __launch_bounds__(256) void k_out(const float* __restrict__ CQ, const
     const int ksteps = (nl + 3) / 4;
     for (int ks = 0; ks < ksteps; ++ks) {
       const int k = ks * 4 + (ln >> 4);
-      float bt[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) bt[t] = sC[k * Lay::LDC + t * 16 + (ln & 15)];
-#pragma unroll
-      for (int a = 0; a < SPW; ++a) {
-        const int strip = wv * SPW + a;
-        if (strip < CS) {
+      for (int j = 0; j < PPW; ++j) {
+        const int pr = wv * PPW + j;
+        if (pr < NP) {
+          const int strip = pr >> 2, tile = pr & 3;
           const float av = sB[k * Lay::LDB + strip * 16 + (ln & 15)];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc[a][t] = mfma16x16x4(av, bt[t], acc[a][t]);
+          const float bt = sC[k * Lay::LDC + tile * 16 + (ln & 15)];
+          acc[j] = mfma16x16x4(av, bt, acc[j]);
         }
       }
     }
@@ -512,41 +565,34 @@ __global__ __launch_bounds__(256) void k_out(const float* __restrict__ CQ, const
   if (tid < D) sBias[tid] = bias_acc;
   __syncthreads();
 
-  // 3. epilogue: lane holds Y[token 16 t + ln%16][channels 16 strip + 4 (ln/16) .. +3]
+  // 3. epilogue: for tile (strip, t) the lane holds Y[token 16 t + ln%16][channels 16 strip + 4 (ln/16) .. +3]
   T* yg = Y + static_cast<size_t>(g) * N * D;
 #pragma unroll
-  for (int a = 0; a < SPW; ++a) {
-    const int strip = wv * SPW + a;
-    if (strip >= CS) continue;
+  for (int j = 0; j < PPW; ++j) {
+    const int pr = wv * PPW + j;
+    if (pr >= NP) continue;
+    const int strip = pr >> 2, t = pr & 3;
     const int c0 = strip * 16 + 4 * (ln >> 4);
+    const int u = t * 16 + (ln & 15);
+    const int ty = u >> 3, tx = u & 7;
+    const int y = ty0 + ty, x = tx0 + tx;
+    if (y >= H || x >= W) continue;
     const float4 b = *reinterpret_cast<const float4*>(sBias + c0);
-    float4 k9[9];
+    float4 o = make_float4(acc[j][0] - b.x, acc[j][1] - b.y, acc[j][2] - b.z, acc[j][3] - b.w);
     if (has_w) {
 #pragma unroll
-      for (int q = 0; q < 9; ++q) k9[q] = *reinterpret_cast<const float4*>(sWt + q * D + c0);
+      for (int aa = 0; aa < 3; ++aa)
+#pragma unroll
+        for (int bb = 0; bb < 3; ++bb) {
+          const float4 v = *reinterpret_cast<const float4*>(sVh + ((ty + aa) * 10 + tx + bb) * Lay::LDV + c0);
+          const float4 k4 = *reinterpret_cast<const float4*>(sWt + (aa * 3 + bb) * D + c0);
+          o.x += k4.x * v.x;
+          o.y += k4.y * v.y;
+          o.z += k4.z * v.z;
+          o.w += k4.w * v.w;
+        }
     }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int u = t * 16 + (ln & 15);
-      const int ty = u >> 3, tx = u & 7;
-      const int y = ty0 + ty, x = tx0 + tx;
-      if (y >= H || x >= W) continue;
-      float4 o = make_float4(acc[a][t][0] - b.x, acc[a][t][1] - b.y, acc[a][t][2] - b.z, acc[a][t][3] - b.w);
-      if (has_w) {
-#pragma unroll
-        for (int aa = 0; aa < 3; ++aa)
-#pragma unroll
-          for (int bb = 0; bb < 3; ++bb) {
-            const float4 v = *reinterpret_cast<const float4*>(sVh + ((ty + aa) * 10 + tx + bb) * Lay::LDV + c0);
-            const float4 k4 = k9[aa * 3 + bb];
-            o.x += k4.x * v.x;
-            o.y += k4.y * v.y;
-            o.z += k4.z * v.z;
-            o.w += k4.w * v.w;
-          }
-      }
-      store4(yg + static_cast<size_t>(y * W + x) * D + c0, o);
-    }
+    store4(yg + static_cast<size_t>(y * W + x) * D + c0, o);
   }
 }
 
@@ -693,44 +739,55 @@ hipError_t launch_mix(const Shape& s, const float* X, const float* S, const floa
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FUSED>
 static void out_launch(const Shape& s, const float* CQ, const float* P, const float* mu, const void* V,
-                       const float* w, void* Y, int flip, hipStream_t st) {
+                       const float* w, void* Y, int flip, const void* Q, const float* L, hipStream_t st) {
   const int tiles_x = cdiv(s.W, 8), tiles_y = cdiv(s.H, 8);
   const size_t lds = sizeof(float) * OutLds<D>::TOTAL;
   if (lds > 64 * 1024)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_out<T, D>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(lds));
-  hipLaunchKernelGGL((k_out<T, D>), dim3(tiles_x * tiles_y, s.G), dim3(256), lds, st, CQ, P, mu,
-                     static_cast<const T*>(V), w, static_cast<T*>(Y), s.N, s.m, s.H, s.W, s.heads, flip, tiles_x);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_out<T, D, FUSED>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  const float scale = static_cast<float>(-1.4426950408889634 / static_cast<double>(s.lambda));
+  hipLaunchKernelGGL((k_out<T, D, FUSED>), dim3(tiles_x * tiles_y, s.G), dim3(512), lds, st, CQ, P, mu,
+                     static_cast<const T*>(V), w, static_cast<T*>(Y), s.N, s.m, s.H, s.W, s.heads, flip, tiles_x,
+                     static_cast<const T*>(Q), L, scale);
 }
 
-template <typename T>
+template <typename T, bool FUSED>
 static void out_d(const Shape& s, const float* CQ, const float* P, const float* mu, const void* V, const float* w,
-                  void* Y, int flip, hipStream_t st) {
+                  void* Y, int flip, const void* Q, const float* L, hipStream_t st) {
   switch (s.d) {
-    case 16: out_launch<T, 16>(s, CQ, P, mu, V, w, Y, flip, st); break;
-    case 32: out_launch<T, 32>(s, CQ, P, mu, V, w, Y, flip, st); break;
-    case 64: out_launch<T, 64>(s, CQ, P, mu, V, w, Y, flip, st); break;
-    default: out_launch<T, 128>(s, CQ, P, mu, V, w, Y, flip, st); break;
+    case 16: out_launch<T, 16, FUSED>(s, CQ, P, mu, V, w, Y, flip, Q, L, st); break;
+    case 32: out_launch<T, 32, FUSED>(s, CQ, P, mu, V, w, Y, flip, Q, L, st); break;
+    case 64: out_launch<T, 64, FUSED>(s, CQ, P, mu, V, w, Y, flip, Q, L, st); break;
+    default: out_launch<T, 128, FUSED>(s, CQ, P, mu, V, w, Y, flip, Q, L, st); break;
   }
 }
 
 hipError_t launch_out(const Shape& s, const float* CQ, const float* P, const float* mu, const void* V, const float* w,
                       void* Y, hipStream_t st) {
   if (s.dtype == 1)
-    out_d<bf16_t>(s, CQ, P, mu, V, w, Y, 0, st);
+    out_d<bf16_t, false>(s, CQ, P, mu, V, w, Y, 0, nullptr, nullptr, st);
   else
-    out_d<float>(s, CQ, P, mu, V, w, Y, 0, st);
+    out_d<float, false>(s, CQ, P, mu, V, w, Y, 0, nullptr, nullptr, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_out_fused(const Shape& s, const void* Q, const float* L, const float* P, const void* V,
+                            const float* w, void* Y, hipStream_t st) {
+  if (s.dtype == 1)
+    out_d<bf16_t, true>(s, nullptr, P, nullptr, V, w, Y, 0, Q, L, st);
+  else
+    out_d<float, true>(s, nullptr, P, nullptr, V, w, Y, 0, Q, L, st);
   return hipGetLastError();
 }
 
 hipError_t launch_out_adjoint(const Shape& s, const float* C, const float* P, const void* U, const float* w, void* out,
                               hipStream_t st) {
   if (s.dtype == 1)
-    out_d<bf16_t>(s, C, P, nullptr, U, w, out, 1, st);
+    out_d<bf16_t, false>(s, C, P, nullptr, U, w, out, 1, nullptr, nullptr, st);
   else
-    out_d<float>(s, C, P, nullptr, U, w, out, 1, st);
+    out_d<float, false>(s, C, P, nullptr, U, w, out, 1, nullptr, nullptr, st);
   return hipGetLastError();
 }
 

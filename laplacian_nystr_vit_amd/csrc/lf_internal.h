@@ -33,6 +33,9 @@ hipError_t launch_mix(const Shape& s, const float* X, const float* S, const floa
                       hipStream_t st);
 hipError_t launch_out(const Shape& s, const float* CQ, const float* P, const float* mu, const void* V,
                       const float* w, void* Y, hipStream_t st);
+// Y = C_Q P + DWC(V) with C_Q computed in the kernel from Q and L (no whitening); C_Q is never stored.
+hipError_t launch_out_fused(const Shape& s, const void* Q, const float* L, const float* P, const void* V,
+                            const float* w, void* Y, hipStream_t st);
 // out = C P + DWC^T(U): the output kernel with the 3x3 filter rotated by 180 degrees (adjoint stencil).
 hipError_t launch_out_adjoint(const Shape& s, const float* C, const float* P, const void* U, const float* w, void* out,
                               hipStream_t st);

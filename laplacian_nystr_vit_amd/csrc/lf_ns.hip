@@ -4,6 +4,8 @@
 // W is shifted by eps I, X_0 = alpha W^T and X_{k+1} = X_k (2I - W X_k): only matrix products and additions,
 // no inverse or SVD. alpha = 1/(||W||_1 ||W||_inf) (max column abs sum times max row abs sum) is the reading that
 // keeps every eigenvalue of alpha W W^T in (0, 1]; the page's 2/||W||_2 would diverge for a unit-diagonal W.
+#include <type_traits>
+
 #include "lf_device.h"
 #include "lf_internal.h"
 
@@ -102,28 +104,23 @@ __device__ __forceinline__ void mma_chunk(const Frags<TQ, KC>& A, const Frags<TQ
       acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.l[a][c], B.h[b][c], acc[a][b], 0, 0, 0);
 }
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
-// Splits two fp32 values into packed fp16 halves: hi2 = (hi(x), hi(y)) rounded to nearest, lo2 = (lo(x), lo(y))
-// with lo = round_f16(v - hi); v - hi is exact in fp32, so lo is its correctly rounded fp16 value. Three
-// instructions: a pack conversion and two mixed-precision FMAs that read hi as fp16.
-__device__ __forceinline__ void split2(float x, float y, unsigned int& hi2, unsigned int& lo2) {
-  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(hi2) : "v"(x), "v"(y));
-  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(lo2) : "v"(x), "v"(hi2));
-  asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(lo2) : "v"(y), "v"(hi2));
+// Splits fp32 values into fp16 halves, two at a time: hi = round_f16(v) and lo = round_f16(v - hi) (v - hi is
+// exact in fp32, so lo is its correctly rounded fp16 value). Written with vector conversions (a pack conversion
+// for each half pair) so that the compiler sees every instruction and keeps the wait states MFMA results need.
+__device__ __forceinline__ void split2(f32x2 v, half2v& h, half2v& l) {
+  h = __builtin_convertvector(v, half2v);
+  l = __builtin_convertvector(v - __builtin_convertvector(h, f32x2), half2v);
 }
 
 __device__ __forceinline__ void split4(f32x4 v, half4& h, half4& l) {
-  u32x2 hh, ll;
-  unsigned int h0, h1, l0, l1;
-  split2(v[0], v[1], h0, l0);
-  split2(v[2], v[3], h1, l1);
-  hh[0] = h0;
-  hh[1] = h1;
-  ll[0] = l0;
-  ll[1] = l1;
-  h = __builtin_bit_cast(half4, hh);
-  l = __builtin_bit_cast(half4, ll);
+  half2v h0, l0, h1, l1;
+  split2(f32x2{v[0], v[1]}, h0, l0);
+  split2(f32x2{v[2], v[3]}, h1, l1);
+  h = half4{h0[0], h0[1], h1[0], h1[1]};
+  l = half4{l0[0], l0[1], l1[0], l1[1]};
 }
 
 // The 4 rows i0 .. i0+3 of column j, stored transposed: Mt[j][i0 .. i0+3] (two 8-byte writes).
@@ -173,46 +170,57 @@ __device__ __forceinline__ void split_scaled4(f32x4 a, float s, half4& h, half4&
 }
 
 template <int ST, int KC>
-__global__ __launch_bounds__(256) void k_ns_small(const float* __restrict__ We, float* __restrict__ Xout,
+__global__ __launch_bounds__(512) void k_ns_small(const float* __restrict__ We, float* __restrict__ Xout,
                                                   float* __restrict__ xs, float* __restrict__ alpha_out,
                                                   float* __restrict__ resid, int m, int iters) {
   constexpr int TQ = ST >= 2 ? ST / 2 : 1;  // tiles per side of a wave's quadrant
-  constexpr int NWA = ST == 1 ? 1 : 4;      // waves with work
-  __shared__ SplitMat sX[2], sXt[2], sUt;
+  constexpr int NQA = ST == 1 ? 1 : 4;      // quadrants with work
+  constexpr int NTH = 512;
+  // sX: X by rows. sT: T = W X by rows (and X by columns where the final exact step needs it). sU: U = 2I - T by
+  // columns. Each is double-buffered by iteration parity.
+  __shared__ SplitMat sX[2], sT[2], sU[2];
   __shared__ double red[3][4][64];
   __shared__ float s_alpha, s_wmax;
-  __shared__ unsigned int s_max[2];  // bits of the largest |X| entry of the iterate written in an iteration
+  // Bits of the largest |X| entry of the iterate written in step k, in slot k % 3: slot k + 1 is cleared during
+  // step k (its last readers finished before the barrier of step k - 1), so the one barrier per step suffices.
+  __shared__ unsigned int s_max[3];
   const int g = blockIdx.x;
   const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
   const size_t mm = static_cast<size_t>(m) * m;
   const float* wg = We + g * mm;
-  float* wf = reinterpret_cast<float*>(&sUt);  // fp32 W (64 x 65) in the not yet used U area
-  const bool active = wv < NWA;
-  const int r0 = (wv & 1) * TQ, c0 = (wv >> 1) * TQ;  // first row strip and first column strip of the quadrant
+  float* wf = reinterpret_cast<float*>(&sU[1]);  // fp32 W (64 x 65) in a U buffer not used before iteration 0
+  // Eight waves, two per SIMD: waves 0-3 ("X waves") own the products that produce X, waves 4-7 ("T waves")
+  // those that produce T and U, each on quadrant wv & 3. On every SIMD one wave's split-and-store epilogue then
+  // runs while the other wave's MFMAs execute.
+  const int qd = wv & 3;
+  const bool active = qd < NQA;
+  const bool xw = active && wv < 4, tw = active && wv >= 4;
+  const int r0 = (qd & 1) * TQ, c0 = (qd >> 1) * TQ;  // first row strip and first column strip of the quadrant
+  constexpr int NZ = static_cast<int>(sizeof(SplitMat) / sizeof(uint4));
+  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
 
   if constexpr (ST == 1) {
     // K runs over 32 entries while the matrices are 16 wide: the padding must read as zero.
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    constexpr int NZ = static_cast<int>(sizeof(SplitMat) / sizeof(uint4));
-    for (int q = tid; q < NZ; q += 256) {
-      reinterpret_cast<uint4*>(&sX[0])[q] = zero;
-      reinterpret_cast<uint4*>(&sX[1])[q] = zero;
-      reinterpret_cast<uint4*>(&sXt[0])[q] = zero;
-      reinterpret_cast<uint4*>(&sXt[1])[q] = zero;
+    for (int q = tid; q < NZ; q += NTH) {
+      reinterpret_cast<uint4*>(&sX[0])[q] = zero4;
+      reinterpret_cast<uint4*>(&sX[1])[q] = zero4;
+      reinterpret_cast<uint4*>(&sT[0])[q] = zero4;
+      reinterpret_cast<uint4*>(&sT[1])[q] = zero4;
+      reinterpret_cast<uint4*>(&sU[0])[q] = zero4;
     }
   }
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int idx = tid + 256 * q;
+  for (int q = 0; q < 4096 / NTH; ++q) {
+    const int idx = tid + NTH * q;
     const int i = idx >> 6, j = idx & 63;
     wf[i * 65 + j] = (i < m && j < m) ? wg[i * m + j] : 0.f;
   }
-  if (tid < 2) s_max[tid] = 0u;
+  if (tid < 3) s_max[tid] = 0u;
   __syncthreads();
 
   // alpha = 1 / (max_j sum_i |W_ij| * max_i sum_j |W_ij|) in float64: thread (c, quarter) sums 16 entries of
   // column c and of row c, the quarters are combined, then wave 0 takes the maxima (and max |W_ij|).
-  {
+  if (tid < 256) {
     const int c = tid & 63, qtr = tid >> 6;
     double cs = 0.0, rs = 0.0, mx = 0.0;
 #pragma unroll
@@ -246,9 +254,9 @@ __global__ __launch_bounds__(256) void k_ns_small(const float* __restrict__ We, 
   const float alpha = s_alpha;
   if (tid == 0 && alpha_out) alpha_out[g] = alpha;
 
-  // W fragments of this wave's row strips (A operand of W X), and X_0 = alpha W^T in fp32 registers.
+  // W fragments of this wave's row strips (W is the A operand of every product with W), and X_0 = alpha W^T.
   Frags<TQ, KC> fw;
-  f32x4 x0c[TQ][TQ], x0r[TQ][TQ];  // X_0 = alpha W^T as quadrant tiles by columns, and by rows (see put_x)
+  f32x4 x0c[TQ][TQ], x0r[TQ][TQ];  // X_0 quadrant tiles in the by-columns and the by-rows lane layouts
 #pragma unroll
   for (int c = 0; c < KC; ++c)
 #pragma unroll
@@ -276,180 +284,248 @@ __global__ __launch_bounds__(256) void k_ns_small(const float* __restrict__ We, 
         inside[a][b][r] = i < m && j < m;
         two_i[a][b][r] = (i == j && i < m) ? 2.f : 0.f;
         x0c[a][b][r] = active ? alpha * wf[j * 65 + i] : 0.f;
-        // by rows: row (r0 + a) 16 + lane % 16, column (c0 + b) 16 + 4 (lane / 16) + r
-        const int ir = (r0 + a) * 16 + (ln & 15), jr = (c0 + b) * 16 + 4 * (ln >> 4) + r;
+        // by-rows tile (a, b): row (r0 + b) 16 + lane % 16, column (c0 + a) 16 + 4 (lane / 16) + r
+        const int ir = (r0 + b) * 16 + (ln & 15), jr = (c0 + a) * 16 + 4 * (ln >> 4) + r;
         x0r[a][b][r] = active ? alpha * wf[jr * 65 + ir] : 0.f;
       }
     }
-  __syncthreads();  // wf (inside sUt) is dead after this point
+  __syncthreads();  // wf (inside sU[1]) is dead after this point
   if constexpr (ST == 1) {
-    constexpr int NZ = static_cast<int>(sizeof(SplitMat) / sizeof(uint4));
-    for (int q = tid; q < NZ; q += 256) reinterpret_cast<uint4*>(&sUt)[q] = make_uint4(0u, 0u, 0u, 0u);
+    for (int q = tid; q < NZ; q += NTH) reinterpret_cast<uint4*>(&sU[1])[q] = zero4;
   }
 
-  // Tile (a, b) of the quadrant: column j and first row i0 of the lane's four entries.
-  auto tile_j = [&](int b) { return (c0 + b) * 16 + (ln & 15); };
-  auto tile_i0 = [&](int a) { return (r0 + a) * 16 + 4 * (ln >> 4); };
-  // Stores an iterate into buffer `buf`: px holds its quadrant tiles (by columns), pt the tiles of its
-  // transpose (by rows), both multiplied by s on the way.
-  auto put_x = [&](int buf, const f32x4 px[TQ][TQ], const f32x4 pt[TQ][TQ], float s) {
+  // Lane placement of quadrant tiles. By-columns tile (a, b), a product mma(rows of strips r0.., rows of strips
+  // c0..): the lane holds rows col_i0(a) .. +3 of column col_j(b). By-rows tile (a, b), the same product with the
+  // operand roles swapped, mma(strips c0.., strips r0..), so a indexes column strips and b row strips: the lane
+  // holds columns row_j0(a) .. +3 of row row_i(b).
+  auto col_j = [&](int b) { return (c0 + b) * 16 + (ln & 15); };
+  auto col_i0 = [&](int a) { return (r0 + a) * 16 + 4 * (ln >> 4); };
+  auto row_i = [&](int b) { return (r0 + b) * 16 + (ln & 15); };
+  auto row_j0 = [&](int a) { return (c0 + a) * 16 + 4 * (ln >> 4); };
+  // Split stores: by-columns tiles into a by-columns buffer, by-rows tiles into a by-rows buffer (8-byte writes).
+  auto put_cols = [&](SplitMat& M, const f32x4 v[TQ][TQ], float s) {
 #pragma unroll
     for (int a = 0; a < TQ; ++a)
 #pragma unroll
       for (int b = 0; b < TQ; ++b) {
         half4 h, l;
-        split_scaled4(px[a][b], s, h, l);
-        put_t4(sXt[buf], tile_j(b), tile_i0(a), h, l);
-        // pt[a][b]: entries (row (r0 + a) 16 + lane % 16, columns (c0 + b) 16 + 4 (lane / 16) + 0 .. 3)
-        split_scaled4(pt[a][b], s, h, l);
-        put_t4(sX[buf], (r0 + a) * 16 + (ln & 15), (c0 + b) * 16 + 4 * (ln >> 4), h, l);
+        split_scaled4(v[a][b], s, h, l);
+        put_t4(M, col_j(b), col_i0(a), h, l);
       }
   };
-  auto put_xs = [&](int k, const f32x4 px[TQ][TQ], float s) {
+  auto put_rows = [&](SplitMat& M, const f32x4 v[TQ][TQ], float s) {
+#pragma unroll
+    for (int a = 0; a < TQ; ++a)
+#pragma unroll
+      for (int b = 0; b < TQ; ++b) {
+        half4 h, l;
+        split_scaled4(v[a][b], s, h, l);
+        put_t4(M, row_i(b), row_j0(a), h, l);
+      }
+  };
+  // put_rows that also returns the largest |v| (before scaling).
+  auto put_rows_max = [&](SplitMat& M, const f32x4 v[TQ][TQ], float s) {
+    float lm = 0.f;
+#pragma unroll
+    for (int a = 0; a < TQ; ++a)
+#pragma unroll
+      for (int b = 0; b < TQ; ++b) {
+        const f32x4 t = v[a][b];
+        lm = fmaxf(lm, fmaxf(fmaxf(fabsf(t[0]), fabsf(t[1])), fmaxf(fabsf(t[2]), fabsf(t[3]))));
+        half4 h, l;
+        split_scaled4(t, s, h, l);
+        put_t4(M, row_i(b), row_j0(a), h, l);
+      }
+    return lm;
+  };
+  // U = 2I - s v from by-columns tiles of T (padding rows and columns of T are exact zeros, so U is zero there).
+  auto put_u = [&](SplitMat& M, const f32x4 v[TQ][TQ], float s) {
+#pragma unroll
+    for (int a = 0; a < TQ; ++a)
+#pragma unroll
+      for (int b = 0; b < TQ; ++b) {
+        f32x4 u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[r] = two_i[a][b][r] - v[a][b][r] * s;
+        half4 h, l;
+        split4(u, h, l);
+        put_t4(M, col_j(b), col_i0(a), h, l);
+      }
+  };
+  // Iterate k to the saved-iterates buffer, from by-rows tiles (rows_layout) or by-columns tiles.
+  auto put_xs = [&](int k, const f32x4 v[TQ][TQ], float s, bool rows_layout) {
     float* xg = xs + (static_cast<size_t>(g) * (iters + 1) + k) * mm;
 #pragma unroll
     for (int a = 0; a < TQ; ++a)
 #pragma unroll
       for (int b = 0; b < TQ; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (inside[a][b][r]) xg[(tile_i0(a) + r) * m + tile_j(b)] = px[a][b][r] * s;
+        for (int r = 0; r < 4; ++r) {
+          const int i = rows_layout ? row_i(b) : col_i0(a) + r;
+          const int j = rows_layout ? row_j0(a) + r : col_j(b);
+          if (i < m && j < m) xg[i * m + j] = v[a][b][r] * s;
+        }
+  };
+  auto frags_of = [&](const SplitMat& M, int s0, Frags<TQ, KC>& f) {
+#pragma unroll
+    for (int c = 0; c < KC; ++c) load_chunk<TQ, KC>(M, s0, ln, c, f);
+  };
+  auto mma = [&](const Frags<TQ, KC>& A, const Frags<TQ, KC>& B, f32x4 acc[TQ][TQ]) {
+    zero_acc<TQ>(acc);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) mma_chunk<TQ, KC>(A, B, acc, c);
   };
 
-  f32x4 accx[TQ][TQ], acct[TQ][TQ], acc[TQ][TQ];
-  int e_cur = store_exp(alpha * s_wmax);  // X_0's largest entry is alpha max |W_ij|
-  __syncthreads();                        // (ST == 1) padding of U cleared
-  if (active) {
-    put_x(0, x0c, x0r, ldexpf(1.f, -e_cur));
-    if (xs) put_xs(0, x0c, 1.f);
+
+  // The exact Newton-Schulz step X_{k+1} = X_k (2I - W X_k) equals, for T_k = W X_k, the pair
+  //   T_{k+1} = T_k (2I - T_k),  X_{k+1} = X_k (2I - T_k),
+  // whose two products share U_k = 2I - T_k and depend only on step k: one phase and one barrier per step
+  // instead of two. Carrying T separately drops the self-correction of the exact step (rounding in T is never
+  // compared with W X again), so steps 0 .. K-2 use the pair and the last step is the exact update from
+  // X_{K-1}, which restores it; in fp32 the result then tracks the exact-step iteration to rounding.
+  int e_cur = store_exp(alpha * s_wmax);  // storage exponent of the iterate in sX[cur]; X_0's max is alpha max|W|
+  const int xcol_first = 1;               // buffer of sT that receives X_0 by columns
+  if (xw) {
+    put_rows(sX[0], x0r, ldexpf(1.f, -e_cur));
+    if (xs) put_xs(0, x0c, 1.f, false);
   }
-#pragma unroll
-  for (int a = 0; a < TQ; ++a)
-#pragma unroll
-    for (int b = 0; b < TQ; ++b) accx[a][b] = x0c[a][b];  // the output when iters == 0
+  if (tw) put_cols(sT[xcol_first], x0c, ldexpf(1.f, -e_cur));
   __syncthreads();
 
+  f32x4 accA[TQ][TQ], accB[TQ][TQ], accC[TQ][TQ];
+  if (iters >= 2) {
+    // T_0 = W X_0: by columns (into U_0 = 2I - T_0) and, with the operands swapped, by rows.
+    if (tw) {
+      Frags<TQ, KC> fxc;
+      frags_of(sT[xcol_first], c0, fxc);
+      mma(fw, fxc, accA);
+      mma(fxc, fw, accB);
+      const float unscale = ldexpf(1.f, e_cur);
+      put_u(sU[0], accA, unscale);
+      put_rows(sT[0], accB, unscale);
+    }
+    __syncthreads();
+  }
+
   int e_next = e_cur;
-  float last_unscale = 1.f;
-  for (int it = 0; it < iters; ++it) {
-    const int cur = it & 1, nxt = cur ^ 1;
+  int xcol_buf = xcol_first;  // where X_{K-1} by columns sits for the exact step
+  // One pair step; the buffer parity is a template constant so that every LDS address is a fixed offset.
+  auto step = [&](auto parity, int k) __attribute__((always_inline)) {
+    constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
+    const bool last = k + 2 == iters;  // produces X_{K-1}: also by columns, and T_{K-1} / U_{K-1} are not needed
     const float unscale = ldexpf(1.f, e_cur);
-    // T = W X ; U = 2I - T, stored by columns. Padding rows and columns of T are exact zeros, so U is zero there.
-    if (active) {
-      Frags<TQ, KC> fx;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) load_chunk<TQ, KC>(sXt[cur], c0, ln, c, fx);
-      zero_acc<TQ>(acc);
-#pragma unroll
-      for (int c = 0; c < KC; ++c) mma_chunk<TQ, KC>(fw, fx, acc, c);
-#pragma unroll
-      for (int a = 0; a < TQ; ++a)
-#pragma unroll
-        for (int b = 0; b < TQ; ++b) {
-          f32x4 u;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) u[r] = two_i[a][b][r] - acc[a][b][r] * unscale;
-          half4 h, l;
-          split4(u, h, l);
-          put_t4(sUt, tile_j(b), tile_i0(a), h, l);
-        }
-    }
-    __syncthreads();
-    if (tid == 0) s_max[nxt] = 0u;  // read by every wave in the previous iteration, before the barrier above
-    // X_next = X U, and its transpose U^T X^T from the same fragments
-    if (active) {
-      Frags<TQ, KC> fa, fb;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        load_chunk<TQ, KC>(sX[cur], r0, ln, c, fa);
-        load_chunk<TQ, KC>(sUt, c0, ln, c, fb);
-      }
-      zero_acc<TQ>(accx);
-      zero_acc<TQ>(acct);
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        mma_chunk<TQ, KC>(fa, fb, accx, c);
-        mma_chunk<TQ, KC>(fb, fa, acct, c);
-      }
-      float lmax = 0.f;
-#pragma unroll
-      for (int a = 0; a < TQ; ++a)
-#pragma unroll
-        for (int b = 0; b < TQ; ++b)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) lmax = fmaxf(lmax, fabsf(accx[a][b][r]));
+    if (xw) {
+      Frags<TQ, KC> fu, fx;
+      frags_of(sU[cur], c0, fu);
+      frags_of(sX[cur], r0, fx);
+      mma(fu, fx, accC);  // (X_k U_k)^T: X_{k+1} by rows
+      float lmax = put_rows_max(sX[nxt], accC, ldexpf(1.f, e_cur - e_next));
+      if (xs) put_xs(k + 1, accC, unscale, true);
       lmax = wave_max_nonneg(lmax) * unscale;
-      if (ln == 0) atomicMax(&s_max[cur], __float_as_uint(lmax));
-      // acct[b][a] holds the transposed tile of (a, b): swap the indices into put_x's by-rows argument
-      f32x4 tt[TQ][TQ];
-#pragma unroll
-      for (int a = 0; a < TQ; ++a)
-#pragma unroll
-        for (int b = 0; b < TQ; ++b) tt[a][b] = acct[b][a];
-      put_x(nxt, accx, tt, ldexpf(1.f, e_cur - e_next));
-      if (xs) put_xs(it + 1, accx, unscale);
+      if (ln == 0) atomicMax(&s_max[k % 3], __float_as_uint(lmax));
+    } else if (tw) {
+      Frags<TQ, KC> fu, ft;
+      frags_of(sU[cur], c0, fu);
+      if (!last) {
+        frags_of(sT[cur], r0, ft);
+        mma(ft, fu, accA);  // T_k U_k by columns: U_{k+1}
+        mma(fu, ft, accB);  // (T_k U_k)^T: T_{k+1} by rows
+        put_u(sU[nxt], accA, 1.f);
+        put_rows(sT[nxt], accB, 1.f);
+      } else {
+        frags_of(sX[cur], r0, ft);
+        mma(ft, fu, accA);  // X_k U_k by columns: X_{K-1} for the exact step
+        put_cols(sT[nxt], accA, ldexpf(1.f, e_cur - e_next));
+      }
     }
+    if (tid == 0) s_max[(k + 1) % 3] = 0u;
     __syncthreads();
-    const float mx = __uint_as_float(s_max[cur]);
+    const float mx = __uint_as_float(s_max[k % 3]);
     if (mx >= ldexpf(1.f, e_next + kRestoreExp) || !(mx < 3.0e38f)) {
       // Rare: the iterate grew past the headroom of its exponent (or is not finite); store it again.
       const int e_new = store_exp(fminf(mx, 3.0e38f));
-      if (active) {
-        f32x4 tt[TQ][TQ];
-#pragma unroll
-        for (int a = 0; a < TQ; ++a)
-#pragma unroll
-          for (int b = 0; b < TQ; ++b) tt[a][b] = acct[b][a];
-        put_x(nxt, accx, tt, ldexpf(1.f, e_cur - e_new));
-      }
+      const float rel = ldexpf(1.f, e_cur - e_new);
+      if (xw) put_rows(sX[nxt], accC, rel);
+      if (tw && last) put_cols(sT[nxt], accA, rel);
       e_next = e_new;
       __syncthreads();
     }
-    last_unscale = unscale;
     e_cur = e_next;
     e_next = store_exp(mx);
+    if (last) xcol_buf = nxt;
+  };
+  for (int k = 0; k + 1 < iters; k += 2) {
+    step(std::integral_constant<int, 0>{}, k);
+    if (k + 2 < iters) step(std::integral_constant<int, 1>{}, k + 1);
   }
 
-  float* xo = Xout + g * mm;
-  if (active) {
+  // Final exact step (iters >= 1): X_K = X_{K-1} (2I - W X_{K-1}), X_K by columns in accC.
+  const int fin = (iters >= 1) ? ((iters - 1) & 1) : 0;  // buffers holding X_{K-1}
+  float out_unscale = 1.f;
+  if (iters >= 1) {
+    const float unscale = ldexpf(1.f, e_cur);
+    if (tw) {
+      Frags<TQ, KC> fxc;
+      frags_of(sT[xcol_buf], c0, fxc);
+      mma(fw, fxc, accA);
+      put_u(sU[fin], accA, unscale);
+    }
+    __syncthreads();
+    if (xw) {
+      Frags<TQ, KC> fx, fu;
+      frags_of(sX[fin], r0, fx);
+      frags_of(sU[fin], c0, fu);
+      mma(fx, fu, accC);
+    }
+    out_unscale = unscale;
+  } else {
+#pragma unroll
+    for (int a = 0; a < TQ; ++a)
+#pragma unroll
+      for (int b = 0; b < TQ; ++b) accC[a][b] = x0c[a][b];
+  }
+  if (xw) {
+    if (xs && iters >= 1) put_xs(iters, accC, out_unscale, false);
+    float* xo = Xout + g * mm;
 #pragma unroll
     for (int a = 0; a < TQ; ++a)
 #pragma unroll
       for (int b = 0; b < TQ; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (inside[a][b][r]) xo[(tile_i0(a) + r) * m + tile_j(b)] = accx[a][b][r] * last_unscale;
+          if (inside[a][b][r]) xo[(col_i0(a) + r) * m + col_j(b)] = accC[a][b][r] * out_unscale;
   }
 
   if (resid) {
-    // ||W X - I||_F with the same split products
+    // ||W X_K - I||_F with the same split products: X_K by columns goes through LDS once more.
+    __syncthreads();  // every read of the buffers below is done
+    const int rb = fin ^ 1;
+    // accC * out_unscale is X_K; store it with the exponent of the last iterate so the fp16 halves stay in range
+    const float st_scale = (iters >= 1) ? 1.f : ldexpf(1.f, -e_cur);
+    const float ru = out_unscale / st_scale;
+    if (xw) put_cols(sT[rb], accC, st_scale);
+    __syncthreads();
     double ss = 0.0;
-    if (active) {
-      Frags<TQ, KC> fx;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) load_chunk<TQ, KC>(sXt[iters & 1], c0, ln, c, fx);
-      zero_acc<TQ>(acc);
-#pragma unroll
-      for (int c = 0; c < KC; ++c) mma_chunk<TQ, KC>(fw, fx, acc, c);
-      const float unscale = ldexpf(1.f, e_cur);  // the exponent X_iters was stored with
+    if (tw) {
+      Frags<TQ, KC> fxc;
+      frags_of(sT[rb], c0, fxc);
+      mma(fw, fxc, accA);
 #pragma unroll
       for (int a = 0; a < TQ; ++a)
 #pragma unroll
-        for (int b = 0; b < TQ; ++b) {
-          const int j = (c0 + b) * 16 + (ln & 15);
-          const int i0 = (r0 + a) * 16 + 4 * (ln >> 4);
+        for (int b = 0; b < TQ; ++b)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (inside[a][b][r]) {
-              const double e2 = static_cast<double>(acc[a][b][r] * unscale) - (i0 + r == j ? 1.0 : 0.0);
+              const double e2 = static_cast<double>(accA[a][b][r] * ru) -
+                                (col_i0(a) + r == col_j(b) ? 1.0 : 0.0);
               ss += e2 * e2;
             }
-        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
     __syncthreads();
-    if (ln == 0) red[0][0][wv] = ss;
+    if (ln == 0 && wv >= 4) red[0][0][qd] = ss;
     __syncthreads();
     if (tid == 0) resid[g] = static_cast<float>(sqrt(red[0][0][0] + red[0][0][1] + red[0][0][2] + red[0][0][3]));
   }
@@ -573,7 +649,7 @@ hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float
   const int m = s.m, K = s.ns_iters;
   if (m <= 64) {
     const int nt = (m + 15) / 16;
-    const dim3 grid(s.G), block(256);
+    const dim3 grid(s.G), block(512);
     if (nt == 1)
       hipLaunchKernelGGL((k_ns_small<1, 1>), grid, block, 0, st, We, X, xs, alpha, resid, m, K);
     else if (nt == 2)

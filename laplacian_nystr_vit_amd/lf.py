@@ -26,6 +26,7 @@ LF_NS_ITERS_MAX = 64
 EXPORTS = (
     "lf_attn_query", "lf_attn_saved_layout", "lf_attn_fwd", "lf_attn_bwd", "lf_strerror", "lf_landmark_pool",
     "lf_laplace_l1_exp", "lf_ns_pinv", "lf_ckv_reduce", "lf_whiten_stats", "lf_landmark_mix", "lf_out_gemm_dwc",
+    "lf_out_gemm_dwc_fused",
 )
 
 
@@ -88,6 +89,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lf_whiten_stats": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp]),
         "lf_landmark_mix": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp]),
         "lf_out_gemm_dwc": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+        "lf_out_gemm_dwc_fused": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -230,6 +232,15 @@ def lf_out_gemm_dwc(p, CQ, P, mu, V, dwc_w, Y, stream=None) -> None:
         ctypes.byref(p), _ptr(CQ, "CQ", f32, p.G * p.N * p.m), _ptr(P, "P", f32, p.G * p.m * p.d),
         _ptr(mu, "mu", f32, p.G * p.m), _ptr(V, "V", dt, n), _ptr(dwc_w, "dwc_w", f32, p.heads * p.d * 9),
         _ptr(Y, "Y", dt, n), _stream(stream)), "lf_out_gemm_dwc")
+
+
+def lf_out_gemm_dwc_fused(p, Q, L, P, V, dwc_w, Y, stream=None) -> None:
+    """Y = C_Q P + DWC(V) with C_Q recomputed per tile from Q and the landmarks L (no whitening)."""
+    f32, dt, n = torch.float32, io_dtype(p), p.G * p.N * p.d
+    _check(load_library().lf_out_gemm_dwc_fused(
+        ctypes.byref(p), _ptr(Q, "Q", dt, n), _ptr(L, "L", f32, p.G * p.m * p.d), _ptr(P, "P", f32, p.G * p.m * p.d),
+        _ptr(V, "V", dt, n), _ptr(dwc_w, "dwc_w", f32, p.heads * p.d * 9), _ptr(Y, "Y", dt, n), _stream(stream)),
+        "lf_out_gemm_dwc_fused")
 
 
 # ------------------------------------------------------------------------------------------------------------

@@ -38,15 +38,23 @@ ALL = MAIN + EDGE
 def test_forward_end_to_end(wl):
     note(f"[gpu] forward {wl.name}")
     ref = oracle_forward(wl)
+    # With and without a saved buffer (the saved one receives every intermediate), with and without DWC.
     Y, sv, p = gpu_forward(wl, dwc=True, save=True)
+    Ya_s, _, _ = gpu_forward(wl, dwc=False, save=True)
+    Yf, _, _ = gpu_forward(wl, dwc=True, save=False)
     Ya, _, _ = gpu_forward(wl, dwc=False, save=False)
     e_full = relF(host(Y), ref["Y"])
     e_attn = relF(host(Ya), ref["Yattn"])
+    e_full_f = relF(host(Yf), ref["Y"])
+    e_attn_s = relF(host(Ya_s), ref["Yattn"])
     G = wl.G
     worst = max(relF(host(Ya).reshape(G, -1)[g], ref["Yattn"].reshape(G, -1)[g]) for g in range(G))
-    note(f"    relF full={e_full:.3e} attn={e_attn:.3e} worst-slice attn={worst:.3e}")
+    note(f"    relF full={e_full:.3e}/{e_full_f:.3e} attn={e_attn_s:.3e}/{e_attn:.3e} (saved/no saved) "
+         f"worst-slice attn={worst:.3e}")
     assert e_full <= tol(wl)
     assert e_attn <= tol(wl)
+    assert e_full_f <= tol(wl)
+    assert e_attn_s <= tol(wl)
     # intermediates the forward kept in the saved buffer
     rs = lambda a: np.asarray(a).reshape((G,) + np.asarray(a).shape[2:])
     assert relF(host(sv["L"]), rs(ref["L"])) <= 1e-6
@@ -186,6 +194,33 @@ def test_stage_ckv_mix_out(wl):
                      for g in range(G)])
     bar = 1e-5 if wl.dtype == WL.F32 else tol(wl)
     assert relF(host(Y).reshape(G, N, d), Yref) <= bar
+
+
+@pytest.mark.parametrize("wl", [WL.TINY, WL.PVT_S1, WL.PVT_S3, WL.HIRES_BF16, EDGE[1], EDGE[2]], ids=lambda w: w.name)
+def test_stage_out_fused(wl):
+    """Output stage with C_Q recomputed per tile from Q and L: against the oracle's C_Q P + DWC(V)."""
+    note(f"[gpu] stage out_gemm_dwc_fused {wl.name}")
+    p = params(wl)
+    inp = inputs(wl)
+    ref = oracle_forward(wl)
+    t = upload(wl)
+    G, N, m, d = p.G, p.N, p.m, p.d
+    Lr = _r32(np.asarray(ref["L"]).reshape(G, m, d))
+    P32 = _r32(np.asarray(ref["P"]).reshape(G, m, d))
+    Y = torch.empty_like(t["Q"])
+    lf.lf_out_gemm_dwc_fused(p, t["Q"], _f32(Lr), _f32(P32), t["V"], t["w"], Y)
+    Ya = torch.empty_like(t["Q"])
+    lf.lf_out_gemm_dwc_fused(p, t["Q"], _f32(Lr), _f32(P32), t["V"], None, Ya)
+    torch.cuda.synchronize()
+    Qg, V = inp["Q"].reshape(G, N, d), inp["V"].reshape(G, N, d)
+    w = inp["w64"]
+    Yattn = np.stack([O.laplacian_kernel(Qg[g], Lr[g], wl.lam) @ P32[g] for g in range(G)])
+    Yref = Yattn + np.stack([O.dwc(V[g], w[(g % wl.heads) * d:(g % wl.heads + 1) * d], wl.H, wl.W) for g in range(G)])
+    bar = 1e-5 if wl.dtype == WL.F32 else tol(wl)
+    e_a, e_f = relF(host(Ya).reshape(G, N, d), Yattn), relF(host(Y).reshape(G, N, d), Yref)
+    note(f"    relF attn={e_a:.3e} full={e_f:.3e}")
+    assert e_a <= bar
+    assert e_f <= bar
 
 
 def test_stage_whiten_stats_and_folded_output():
