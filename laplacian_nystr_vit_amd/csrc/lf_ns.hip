@@ -532,92 +532,185 @@ __global__ __launch_bounds__(512) void k_ns_small(const float* __restrict__ We, 
 }
 
 // =====================================================================================================
-// m > 64: the m x m matrices do not fit one CU's LDS, so each product is its own launch of a batched
-// 32 x 32-tile fp32 MFMA GEMM (4 waves of 16 x 16), with K staged through LDS in chunks of 32.
-//   EPI 0: C = 2I - A B   (U = 2I - W X)
-//   EPI 1: C = A B        (X_next = X U), optionally also written to C2
-//   EPI 2: C = A B - I    (residual W X - I)
+// m > 64: the m x m matrices do not fit one CU's LDS, so every product is a batched launch over 32 x 32 output
+// tiles (4 waves of 16 x 16, fp32 MFMA), K staged through LDS in chunks of 32 with the next chunk's float4 loads
+// in flight during the current chunk's MFMAs. The steps follow the small kernel: T_0 = W X_0, then for
+// k < K - 1 one launch computes both T_{k+1} = T_k U_k and X_{k+1} = X_k U_k with U_k = 2I - T_k formed while
+// staging, and the last step is the exact one, X_K = X_{K-1} (2I - W X_{K-1}), in two launches.
 // =====================================================================================================
-__global__ __launch_bounds__(256) void k_ns_init(const float* __restrict__ We, float* __restrict__ X0,
-                                                 float* __restrict__ X0b, size_t strideX0b,
-                                                 float* __restrict__ alpha_out, int m) {
-  __shared__ double red[2][256];
-  const int g = blockIdx.x, tid = threadIdx.x;
-  const size_t mm = static_cast<size_t>(m) * m;
-  const float* wg = We + g * mm;
-  double cmax = 0.0, rmax = 0.0;
+// alpha and X_0 = alpha W^T for m > 64, over (slice, 32-row chunk) blocks. Pass 1 writes per-chunk partial
+// column sums and the largest row sum of the chunk; pass 2 combines them in a fixed order (deterministic) and
+// writes the chunk's rows of X_0. part: G * nchunk * m doubles, rmx: G * nchunk doubles.
+__global__ __launch_bounds__(256) void k_ns_sums(const float* __restrict__ We, double* __restrict__ part,
+                                                 double* __restrict__ rmx, int m) {
+  __shared__ double red[4];
+  const int g = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
+  const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
+  const float* wg = We + static_cast<size_t>(g) * m * m;
+  const int r0 = ch * 32, r1 = min(m, r0 + 32);
   for (int j = tid; j < m; j += 256) {
-    double cs = 0.0, rs = 0.0;
-    for (int i = 0; i < m; ++i) {
-      cs += fabs(static_cast<double>(wg[static_cast<size_t>(i) * m + j]));
-      rs += fabs(static_cast<double>(wg[static_cast<size_t>(j) * m + i]));
-    }
-    cmax = fmax(cmax, cs);
+    double cs = 0.0;
+#pragma unroll 8
+    for (int i = r0; i < r1; ++i) cs += fabs(static_cast<double>(wg[static_cast<size_t>(i) * m + j]));
+    part[(static_cast<size_t>(g) * nch + ch) * m + j] = cs;
+  }
+  double rmax = 0.0;
+  for (int i = r0 + wv; i < r1; i += 4) {
+    double rs = 0.0;
+    for (int j = ln; j < m; j += 64) rs += fabs(static_cast<double>(wg[static_cast<size_t>(i) * m + j]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) rs += __shfl_xor(rs, off);
     rmax = fmax(rmax, rs);
   }
-  red[0][tid] = cmax;
-  red[1][tid] = rmax;
+  if (ln == 0) red[wv] = rmax;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) {
-      red[0][tid] = fmax(red[0][tid], red[0][tid + s]);
-      red[1][tid] = fmax(red[1][tid], red[1][tid + s]);
-    }
+  if (tid == 0) rmx[static_cast<size_t>(g) * nch + ch] = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+}
+
+__global__ __launch_bounds__(256) void k_ns_x0(const float* __restrict__ We, const double* __restrict__ part,
+                                               const double* __restrict__ rmx, float* __restrict__ X0,
+                                               float* __restrict__ X0b, size_t strideX0b,
+                                               float* __restrict__ alpha_out, int m) {
+  __shared__ double red[256];
+  __shared__ float s_alpha;
+  const int g = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
+  const int tid = threadIdx.x;
+  double cmax = 0.0;
+  for (int j = tid; j < m; j += 256) {
+    double cs = 0.0;
+    for (int c = 0; c < nch; ++c) cs += part[(static_cast<size_t>(g) * nch + c) * m + j];
+    cmax = fmax(cmax, cs);
+  }
+  red[tid] = cmax;
+  __syncthreads();
+  for (int s2 = 128; s2 > 0; s2 >>= 1) {
+    if (tid < s2) red[tid] = fmax(red[tid], red[tid + s2]);
     __syncthreads();
   }
-  const float alpha = static_cast<float>(1.0 / (red[0][0] * red[1][0]));
-  if (tid == 0 && alpha_out) alpha_out[g] = alpha;
+  if (tid == 0) {
+    double rmax = 0.0;
+    for (int c = 0; c < nch; ++c) rmax = fmax(rmax, rmx[static_cast<size_t>(g) * nch + c]);
+    s_alpha = static_cast<float>(1.0 / (red[0] * rmax));
+    if (ch == 0 && alpha_out) alpha_out[g] = s_alpha;
+  }
+  __syncthreads();
+  const float alpha = s_alpha;
+  const size_t mm = static_cast<size_t>(m) * m;
+  const float* wg = We + g * mm;
   float* x0 = X0 + g * mm;
   float* x0b = X0b ? X0b + g * strideX0b : nullptr;
-  for (size_t idx = tid; idx < mm; idx += 256) {
-    const size_t i = idx / m, j = idx % m;
-    const float v = alpha * wg[j * m + i];
-    x0[idx] = v;
-    if (x0b) x0b[idx] = v;
+  const int r0 = ch * 32, r1 = min(m, r0 + 32);
+  // X_0[i][j] = alpha W[j][i]: thread j reads the 32 consecutive entries W[j][r0 .. r1) of its row and writes
+  // column j of rows r0 .. r1 (each store instruction covers 256 consecutive floats of one row).
+  for (int j = tid; j < m; j += 256) {
+#pragma unroll 8
+    for (int i = r0; i < r1; ++i) {
+      const float v = alpha * wg[static_cast<size_t>(j) * m + i];
+      x0[static_cast<size_t>(i) * m + j] = v;
+      if (x0b) x0b[static_cast<size_t>(i) * m + j] = v;
+    }
   }
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256) void k_ns_gemm(const float* __restrict__ A, size_t strideA,
-                                                 const float* __restrict__ B, size_t strideB, float* __restrict__ C,
-                                                 size_t strideC, float* __restrict__ C2, size_t strideC2, int m) {
-  constexpr int LDA = 34;  // 2 mod 32
-  constexpr int LDB = 48;  // 16 mod 32
+constexpr int LF_NS_KMAX = 256;  // largest m of the batched path (the library's m limit)
+
+struct MMJob {
+  const float* A[2];
+  float* C[2];
+  float* C2;  // job 1 only
+  size_t strideC2;
+};
+
+template <int BOP, int EPI>
+__global__ __launch_bounds__(256) void k_ns_mm(MMJob job, const float* __restrict__ B, int m) {
+  // The whole K extent is staged at once: A strip [32 rows][m] and B strip [m][32 columns] (m <= 256), so a
+  // launch pays one round of global-load latency and then runs its MFMAs back to back.
+  constexpr int KMAX = LF_NS_KMAX;
+  constexpr int LDA = KMAX + 4;  // A rows: 4 mod 32
+  constexpr int LDB = 36;        // B rows (32 columns): 4 mod 32
+  constexpr int NCH = KMAX / 32;
   __shared__ float sA[32 * LDA];
-  __shared__ float sB[32 * LDB];
-  const int g = blockIdx.z;
+  __shared__ float sB[KMAX * LDB];
+  const int g = blockIdx.z >> 1, which = blockIdx.z & 1;
+  if (job.A[which] == nullptr) return;  // this launch has no such job (uniform over the block)
+  const size_t mm = static_cast<size_t>(m) * m;
+  const float* ag = job.A[which] + g * mm;
+  const float* bg = B + g * mm;
+  float* cg = job.C[which] + g * mm;
   const int tm = blockIdx.y * 32, tn = blockIdx.x * 32;
   const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
-  const float* ag = A + g * strideA;
-  const float* bg = B + g * strideB;
   const int wr = (wv >> 1) * 16, wc = (wv & 1) * 16;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kc = 0; kc < m; kc += 32) {
-    __syncthreads();
-    for (int idx = tid; idx < 32 * 32; idx += 256) {
-      const int rr = idx >> 5, cc = idx & 31;
-      const int ai = tm + rr, ak = kc + cc;
-      sA[rr * LDA + cc] = (ai < m && ak < m) ? ag[static_cast<size_t>(ai) * m + ak] : 0.f;
-      const int bk = kc + rr, bj = tn + cc;
-      sB[rr * LDB + cc] = (bk < m && bj < m) ? bg[static_cast<size_t>(bk) * m + bj] : 0.f;
-    }
-    __syncthreads();
+  // Staging map per 32 x 32 chunk: thread -> (row rr, columns cc .. cc + 3).
+  const int rr = tid >> 3, cc = 4 * (tid & 7);
+  const bool vec = (m & 3) == 0;
+  const int nch = (m + 31) / 32;
+  // Branch-free staging: every load address is clamped into the slice and out-of-range values are selected to
+  // zero, so all chunks' loads are issued before the first wait.
+  auto ld = [&](const float* base, int i, int k, bool ok) {
+    return ok ? base[static_cast<size_t>(i) * m + k] : 0.f;
+  };
+  float4 va[NCH], vb[NCH];
+  if (vec) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int k = ks * 4 + (ln >> 4);
-      acc = mfma16x16x4(sA[(wr + (ln & 15)) * LDA + k], sB[k * LDB + wc + (ln & 15)], acc);
+    for (int c = 0; c < NCH; ++c) {
+      const int ai = tm + rr, ak = 32 * c + cc;  // A[ai][ak .. ak + 3]
+      const int bk = 32 * c + rr, bj = tn + cc;  // B[bk][bj .. bj + 3]
+      const bool aok = c < nch && ai < m && ak + 3 < m, bok = c < nch && bk < m && bj + 3 < m;
+      const float4 x = load4(ag + (aok ? static_cast<size_t>(ai) * m + ak : 0));
+      const float4 y = load4(bg + (bok ? static_cast<size_t>(bk) * m + bj : 0));
+      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      va[c] = aok ? x : z;
+      vb[c] = bok ? y : z;
     }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ai = tm + rr, ak = 32 * c + cc;
+      const int bk = 32 * c + rr, bj = tn + cc;
+      const bool arow = c < nch && ai < m, brow = c < nch && bk < m;
+      va[c] = make_float4(ld(ag, arow ? ai : 0, arow && ak + 0 < m ? ak + 0 : 0, arow && ak + 0 < m),
+                          ld(ag, arow ? ai : 0, arow && ak + 1 < m ? ak + 1 : 0, arow && ak + 1 < m),
+                          ld(ag, arow ? ai : 0, arow && ak + 2 < m ? ak + 2 : 0, arow && ak + 2 < m),
+                          ld(ag, arow ? ai : 0, arow && ak + 3 < m ? ak + 3 : 0, arow && ak + 3 < m));
+      vb[c] = make_float4(ld(bg, brow ? bk : 0, brow && bj + 0 < m ? bj + 0 : 0, brow && bj + 0 < m),
+                          ld(bg, brow ? bk : 0, brow && bj + 1 < m ? bj + 1 : 0, brow && bj + 1 < m),
+                          ld(bg, brow ? bk : 0, brow && bj + 2 < m ? bj + 2 : 0, brow && bj + 2 < m),
+                          ld(bg, brow ? bk : 0, brow && bj + 3 < m ? bj + 3 : 0, brow && bj + 3 < m));
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (BOP == 1) {  // 2I - B, zero outside the m x m block
+      const int bk = 32 * c + rr, bj = tn + cc;
+      vb[c].x = (bk < m && bj + 0 < m) ? ((bk == bj + 0) ? 2.f : 0.f) - vb[c].x : 0.f;
+      vb[c].y = (bk < m && bj + 1 < m) ? ((bk == bj + 1) ? 2.f : 0.f) - vb[c].y : 0.f;
+      vb[c].z = (bk < m && bj + 2 < m) ? ((bk == bj + 2) ? 2.f : 0.f) - vb[c].z : 0.f;
+      vb[c].w = (bk < m && bj + 3 < m) ? ((bk == bj + 3) ? 2.f : 0.f) - vb[c].w : 0.f;
+    }
+    if (c < nch) {
+      *reinterpret_cast<float4*>(&sA[rr * LDA + 32 * c + cc]) = va[c];
+      *reinterpret_cast<float4*>(&sB[(32 * c + rr) * LDB + cc]) = vb[c];
+    }
+  }
+  __syncthreads();
+  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;  // two chains over alternate k-steps
+  const int ksteps = nch * 8;
+#pragma unroll 4
+  for (int ks = 0; ks < ksteps; ks += 2) {
+    const int k = ks * 4 + (ln >> 4);
+    acc0 = mfma16x16x4(sA[(wr + (ln & 15)) * LDA + k], sB[k * LDB + wc + (ln & 15)], acc0);
+    acc1 = mfma16x16x4(sA[(wr + (ln & 15)) * LDA + k + 4], sB[(k + 4) * LDB + wc + (ln & 15)], acc1);
   }
   const int j = tn + wc + (ln & 15);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = tm + wr + 4 * (ln >> 4) + r;
     if (i < m && j < m) {
-      float v = acc[r];
-      if (EPI == 0) v = (i == j ? 2.f : 0.f) - v;
+      float v = acc0[r] + acc1[r];
+      if (EPI == 1) v = (i == j ? 2.f : 0.f) - v;
       if (EPI == 2) v -= (i == j ? 1.f : 0.f);
-      C[g * strideC + static_cast<size_t>(i) * m + j] = v;
-      if (EPI == 1 && C2) C2[g * strideC2 + static_cast<size_t>(i) * m + j] = v;
+      cg[static_cast<size_t>(i) * m + j] = v;
+      if (which == 1 && job.C2) job.C2[g * job.strideC2 + static_cast<size_t>(i) * m + j] = v;
     }
   }
 }
@@ -641,7 +734,7 @@ __global__ __launch_bounds__(256) void k_frob(const float* __restrict__ E, float
 }
 
 size_t ns_tmp_floats(const Shape& s) {
-  return s.m > 64 ? 2 * static_cast<size_t>(s.G) * s.m * s.m : 0;
+  return s.m > 64 ? 3 * static_cast<size_t>(s.G) * s.m * s.m : 0;
 }
 
 hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float* alpha, float* resid, float* tmp,
@@ -658,26 +751,52 @@ hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float
       hipLaunchKernelGGL((k_ns_small<4, 2>), grid, block, 0, st, We, X, xs, alpha, resid, m, K);
     return hipGetLastError();
   }
-  const size_t mm = static_cast<size_t>(m) * m;
-  float* U = tmp;
-  float* Xalt = tmp + static_cast<size_t>(s.G) * mm;
-  // Iterate X_k into buffers that alternate so that X_K lands in X. With xs, X_k also goes to slot k.
-  float* bufs[2] = {X, Xalt};
-  int cur = (K % 2 == 0) ? 0 : 1;
+  const size_t mm = static_cast<size_t>(m) * m, Gmm = static_cast<size_t>(s.G) * mm;
+  float* Tb[2] = {tmp, tmp + Gmm};  // T_k by parity; Tb[..] also serves as U' and the residual
+  float* Xalt = tmp + 2 * Gmm;
+  // X_k alternates between two buffers so that X_K lands in X.
+  float* Xb[2] = {X, Xalt};
   const size_t xs_stride = static_cast<size_t>(K + 1) * mm;
-  hipLaunchKernelGGL(k_ns_init, dim3(s.G), dim3(256), 0, st, We, bufs[cur], xs, xs_stride, alpha, m);
   const int tiles = (m + 31) / 32;
-  const dim3 grid(tiles, tiles, s.G);
-  for (int it = 0; it < K; ++it) {
-    hipLaunchKernelGGL(k_ns_gemm<0>, grid, dim3(256), 0, st, We, mm, bufs[cur], mm, U, mm, nullptr, 0, m);
-    const int nxt = cur ^ 1;
-    float* xslot = xs ? xs + static_cast<size_t>(it + 1) * mm : nullptr;
-    hipLaunchKernelGGL(k_ns_gemm<1>, grid, dim3(256), 0, st, bufs[cur], mm, U, mm, bufs[nxt], mm, xslot, xs_stride, m);
-    cur = nxt;
+  const dim3 blk(256);
+  auto slot = [&](int k) { return xs ? xs + static_cast<size_t>(k) * mm : nullptr; };
+  // X_0 lands where the last exact step reads X_{K-1} from when K == 1, else where step 0 reads it.
+  int xc = (K % 2 == 0) ? 0 : 1;  // parity such that X_K ends in Xb[0] = X (K steps, one flip per step)
+  {
+    const int nch = (m + 31) / 32;
+    // G nch m + G nch doubles fit in one T buffer (m > 64); Tb[0] starts the 256-byte aligned scratch and is not
+    // written before T_0.
+    double* part = reinterpret_cast<double*>(Tb[0]);
+    double* rmx = part + static_cast<size_t>(s.G) * nch * m;
+    hipLaunchKernelGGL(k_ns_sums, dim3(s.G, nch), blk, 0, st, We, part, rmx, m);
+    hipLaunchKernelGGL(k_ns_x0, dim3(s.G, nch), blk, 0, st, We, part, rmx, Xb[xc], xs, xs_stride, alpha, m);
+  }
+  if (K >= 2) {
+    MMJob j0{{We, nullptr}, {Tb[0], nullptr}, nullptr, 0};
+    hipLaunchKernelGGL((k_ns_mm<0, 0>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, j0, Xb[xc], m);  // T_0 = W X_0
+  }
+  int tc = 0;
+  for (int k = 0; k + 1 < K; ++k) {
+    const bool last = k + 2 == K;
+    // pair step: job 0: T_{k+1} = T_k (2I - T_k) (skipped on the last step), job 1: X_{k+1} = X_k (2I - T_k)
+    MMJob jp{{last ? nullptr : Tb[tc], Xb[xc]}, {last ? nullptr : Tb[tc ^ 1], Xb[xc ^ 1]}, slot(k + 1), xs_stride};
+    hipLaunchKernelGGL((k_ns_mm<1, 0>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, jp, Tb[tc], m);
+    tc ^= 1;
+    xc ^= 1;
+  }
+  if (K >= 1) {
+    // exact step: U' = 2I - W X_{K-1} (into a T buffer), then X_K = X_{K-1} U'
+    float* Up = Tb[tc ^ 1];
+    MMJob ju{{We, nullptr}, {Up, nullptr}, nullptr, 0};
+    hipLaunchKernelGGL((k_ns_mm<0, 1>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, ju, Xb[xc], m);
+    MMJob jx{{nullptr, Xb[xc]}, {nullptr, Xb[xc ^ 1]}, slot(K), xs_stride};
+    hipLaunchKernelGGL((k_ns_mm<0, 0>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, jx, Up, m);
+    xc ^= 1;
   }
   if (resid) {
-    hipLaunchKernelGGL(k_ns_gemm<2>, grid, dim3(256), 0, st, We, mm, X, mm, U, mm, nullptr, 0, m);
-    hipLaunchKernelGGL(k_frob, dim3(s.G), dim3(256), 0, st, U, resid, m);
+    MMJob jr{{We, nullptr}, {Tb[tc], nullptr}, nullptr, 0};
+    hipLaunchKernelGGL((k_ns_mm<0, 2>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, jr, Xb[xc], m);
+    hipLaunchKernelGGL(k_frob, dim3(s.G), dim3(256), 0, st, Tb[tc], resid, m);
   }
   return hipGetLastError();
 }
