@@ -22,10 +22,114 @@ if ROOT not in sys.path:
 
 METRIC = "Laplacian-Nyström attention fwd tokens/s (B·heads·N) + % VALU/MFMA roofline"
 
+# HBM traffic of the distance kernel, from two rocprofv3 counter passes over `bench.py --counters` (FETCH_SIZE,
+# then WRITE_SIZE), each scaled by what the same counter reads for a device copy of known size. The file records a
+# hash of the kernel's source; when the source has changed since, the bench reports the traffic as unknown.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "laplace_l1_exp_pvt_s1_56x56_m49_traffic.json")
+CALIB_COPY_MIB = 256
+COUNTER_LAUNCHES = 10
+
 # MI355X: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz issue 39.3e12 fp32 lane-operations per second. The published
 # 157.3 TFLOP/s fp32 vector peak counts an FMA as two flops and packed-fp32 as two lanes; the distance kernel's
 # v_sub_f32 and v_add_f32 |.| are neither, so its peak is 157.3 / 4.
 VALU_PEAK_TFLOPS = 256 * 64 * 2.4e9 / 1e12
+
+
+def laplace_source_hash():
+    """Hash of the distance kernel and its launcher as they stand in the source tree (None if not found)."""
+    import hashlib
+
+    path = os.path.join(ROOT, "laplacian_nystr_vit_amd", "csrc", "lf_fwd.hip")
+    try:
+        src = open(path).read()
+        a = src.index("__global__ __launch_bounds__(64) void k_laplace(")
+        b = src.index("// ====", a)
+        c = src.index("static void laplace_t(")
+        e = src.index("static void laplace_d(", c)
+    except (OSError, ValueError):
+        return None
+    return hashlib.sha256((src[a:b] + src[c:e]).encode()).hexdigest()[:16]
+
+
+def load_traffic():
+    """Bytes per launch of the distance kernel from the committed counter summary, if it matches the source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != laplace_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def read_counter_csv(d, counter):
+    """Per-dispatch (kernel name, value) pairs of one counter from a rocprofv3 --pmc csv output directory."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    for row in csv.DictReader(open(files[0])):
+        if row.get("Counter_Name") != counter:
+            continue
+        key = row["Dispatch_Id"]
+        name, val = per.get(key, (row["Kernel_Name"], 0.0))
+        per[key] = (name, val + float(row["Counter_Value"]))
+    return list(per.values())
+
+
+def ingest_counters(fetch_dir, write_dir):
+    """Writes the traffic summary (JSON + markdown) from a FETCH_SIZE pass and a WRITE_SIZE pass."""
+    out = {"workload": "pvt_s1_56x56_m49", "kernel": "lf::k_laplace<float, 64>", "source_hash": laplace_source_hash(),
+           "calib_copy_bytes": CALIB_COPY_MIB * 2**20}
+    for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = read_counter_csv(d, counter)
+        lap = [v for n, v in rows if "k_laplace" in n]
+        cal = [v for n, v in rows if "copyBuffer" in n or "copy" in n.lower()]
+        if not lap or not cal:
+            raise SystemExit(f"{counter}: laplace dispatches {len(lap)}, copy dispatches {len(cal)}")
+        raw = sum(lap) / len(lap) * 1024.0            # bytes per launch as the counter reads them
+        cal_raw = max(cal) * 1024.0                   # the big copy is the largest copy dispatch
+        factor = out["calib_copy_bytes"] / cal_raw    # counter bytes -> true bytes, from the copy of known size
+        out[f"{label}_launches"] = len(lap)
+        out[f"{label}_raw_bytes_per_launch"] = raw
+        out[f"{label}_calib_raw_bytes"] = cal_raw
+        out[f"{label}_factor"] = factor
+        out[f"{label}_bytes_per_launch"] = raw * factor
+    out["traffic_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(out))
+
+
+def counters_workload():
+    """The distance kernel COUNTER_LAUNCHES times on the stage-1 shape, then one device copy of known size."""
+    import numpy as np
+    import torch
+
+    from laplacian_nystr_vit_amd import lf
+    from laplacian_nystr_vit_amd import workloads as WL
+
+    wl = WL.ALL["pvt_s1_56x56_m49"]
+    inp = WL.make_inputs(wl, seed=0)
+    Q, K = torch.from_numpy(inp["Q_raw"]).cuda(), torch.from_numpy(inp["K_raw"]).cuda()
+    p = lf.make_params(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.r, wl.lam, wl.eps, wl.ns_iters, wl.whiten, wl.whiten_eps,
+                       torch.float32)
+    G, N, m, d = p.G, p.N, p.m, p.d
+    L = torch.empty(G * m * d, device="cuda")
+    CQ = torch.empty(G * N * m, device="cuda")
+    CK = torch.empty_like(CQ)
+    We = torch.empty(G * m * m, device="cuda")
+    lf.lf_landmark_pool(p, Q, L)
+    for _ in range(COUNTER_LAUNCHES):
+        lf.lf_laplace_l1_exp(p, Q, K, L, CQ, CK, We)
+    n = CALIB_COPY_MIB * 2**20 // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"counters workload done: {COUNTER_LAUNCHES} distance launches, copy of {CALIB_COPY_MIB} MiB", flush=True)
 
 
 def parse():
@@ -37,6 +141,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall time budget of the oracle sample")
     ap.add_argument("--kernel-reps", type=int, default=100)
+    ap.add_argument("--counters", action="store_true",
+                    help="run only the distance kernel and a calibration copy (for rocprofv3 --pmc passes)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary from the two rocprofv3 --pmc output directories")
     return ap.parse_args()
 
 
@@ -66,10 +174,17 @@ def cpu_baseline(wl, inp, budget_s):
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the B*heads slices are "
               "independent, so a multi-GPU run would shard them with no communication.", file=sys.stderr)
         sys.exit(2)
+
+    if args.counters:
+        counters_workload()
+        return
 
     import numpy as np
     import torch
@@ -171,7 +286,8 @@ def main():
                    "r": wl.r, "m": wl.m, "lambda": wl.lam, "eps": wl.eps, "ns_iters": wl.ns_iters,
                    "tokens_per_step": wl.tokens},
         "roofline": {"kernel": "laplace_l1_exp", "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / VALU_PEAK_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / VALU_PEAK_TFLOPS,
+                     "traffic": load_traffic() if args.workload == "pvt_s1_56x56_m49" else None,
                      "avg_us": lap_us, "ops_per_launch": ops},
         "stages_us": stages,
     }

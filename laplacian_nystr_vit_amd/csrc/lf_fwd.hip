@@ -80,7 +80,14 @@ __global__ __launch_bounds__(64) void k_laplace(const T* __restrict__ Q, const T
                                                 int tilesQ, int tilesK, int tilesL, int nlc, int lc, float scale,
                                                 float eps) {
   // tilesQ / tilesK / tilesL: 64-row tiles of Q, K and L rows per slice (0 leaves that source out).
-  int b = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs round-robin by index, and each XCD has its own L2. The index is remapped
+  // so that consecutive logical blocks (the landmark chunks of one row tile) run on the same XCD and share the
+  // tile's rows through that L2 instead of each fetching them from HBM.
+  int b = static_cast<int>(blockIdx.x);
+  {
+    const int full = (static_cast<int>(gridDim.x) / 8) * 8;
+    if (b < full) b = (b % 8) * (full / 8) + b / 8;
+  }
   const int lchunk = b % nlc;
   b /= nlc;
   const int per_slice = tilesQ + tilesK + tilesL;
