@@ -213,8 +213,13 @@ int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const voi
   if (wh) LF_TRY(lf::launch_whiten_stats(s, CQ, mu, rstd, st));
   LF_TRY(lf::launch_ns(s, We, X, xs, alpha, nullptr, nstmp, st));
   LF_TRY(lf::launch_ckv(s, CK, V, part, S, st));
-  LF_TRY(lf::launch_mix(s, X, S, wh ? rstd : nullptr, P, Praw, st));
-  LF_TRY(lf::launch_out(s, CQ, P, wh ? mu : nullptr, V, dwc_w, Y, st));
+  if (!saved && !wh && lf::out_mix_supported(s)) {
+    // Inference: P = X S is formed inside the output kernel (no landmark-mix launch, P never stored).
+    LF_TRY(lf::launch_out_mix(s, CQ, X, S, V, dwc_w, Y, st));
+  } else {
+    LF_TRY(lf::launch_mix(s, X, S, wh ? rstd : nullptr, P, Praw, st));
+    LF_TRY(lf::launch_out(s, CQ, P, wh ? mu : nullptr, V, dwc_w, Y, st));
+  }
   return LF_OK;
 }
 

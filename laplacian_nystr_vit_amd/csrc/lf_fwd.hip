@@ -2,6 +2,8 @@
 //
 // Citations: papernotes.org ICLR 2026 reading note "LaplacianFormer：用拉普拉斯核重新思考线性注意力"
 // ([note] below), sections motivation ("core idea"), framework (flowchart), Design 1, Design 2 and Design 3.
+#include <cmath>
+
 #include "lf_device.h"
 #include "lf_internal.h"
 
@@ -406,12 +408,16 @@ struct OutLds {
   static constexpr int TOTAL = BIAS + D;
 };
 
-template <typename T, int D, bool FUSED>
+// MIX (m <= 64, no whitening): P = X S is formed in the block's prologue from the Newton-Schulz result X and
+// S = C_K^T V (P then stands for S, and Xm for X), instead of being read from memory: this replaces the separate
+// landmark-mix launch. X is staged in the C area and S in the V-halo area before either is needed, and the halo's
+// global loads are already in flight meanwhile.
+template <typename T, int D, bool FUSED, bool MIX>
 __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const float* __restrict__ P,
                                              const float* __restrict__ mu, const T* __restrict__ V,
                                              const float* __restrict__ w, T* __restrict__ Y, int N, int m, int H,
                                              int W, int heads, int flip, int tiles_x, const T* __restrict__ Q,
-                                             const float* __restrict__ L, float scale) {
+                                             const float* __restrict__ L, float scale, const float* __restrict__ Xm) {
   using Lay = OutLds<D>;
   constexpr int NWV = 8, NT = 64 * NWV;  // 8 waves: two blocks per CU (LDS) give 4 waves per SIMD
   extern __shared__ float smem[];
@@ -436,9 +442,9 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
   const bool has_w = w != nullptr;
 
   // 1. V halo and filter taps
+  constexpr int NQ = (100 * C4 + NT - 1) / NT;
+  float4 vb[NQ];
   if (has_w) {
-    constexpr int NQ = (100 * C4 + NT - 1) / NT;
-    float4 vb[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int e = tid + NT * q;
@@ -449,6 +455,62 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
         if (y >= 0 && y < H && x >= 0 && x < W) vb[q] = load4(vg + static_cast<size_t>(y * W + x) * D + 4 * c4);
       }
     }
+  }
+  // MIX: m <= 64 is a single landmark chunk; its C_Q tile is loaded up front so that its latency overlaps the
+  // prologue's X and S loads.
+  constexpr int NCV0 = MIX ? 4096 / NT : 1;
+  float cv0[NCV0];
+  if constexpr (MIX) {
+#pragma unroll
+    for (int q = 0; q < NCV0; ++q) {
+      const int e = tid + NT * q;
+      const int l = e >> 6, u = e & 63;
+      const int y = ty0 + (u >> 3), x = tx0 + (u & 7);
+      cv0[q] = (l < m && y < H && x < W) ? cg[static_cast<size_t>(l) * N + y * W + x] : 0.f;
+    }
+  }
+  if constexpr (MIX) {
+    // P = X S into the P area: X [m][m] staged in the C area (row stride 68), S [m][D] in the halo area (row
+    // stride LDB); both zero beyond m, so P's rows beyond m come out zero.
+    constexpr int LDX = 68;
+    float* sXm = sC;
+    float* sS = sVh;
+    const float* xg = Xm + static_cast<size_t>(g) * m * m;
+#pragma unroll
+    for (int q = 0; q < 4096 / NT; ++q) {
+      const int e = tid + NT * q;
+      const int l = e >> 6, k = e & 63;
+      sXm[l * LDX + k] = (l < m && k < m) ? xg[l * m + k] : 0.f;
+    }
+    static_assert(64 * Lay::LDB <= 100 * Lay::LDV && 64 * LDX <= 64 * Lay::LDC, "MIX staging must fit");
+#pragma unroll
+    for (int q = 0; q < (16 * D + NT - 1) / NT; ++q) {
+      const int e = tid + NT * q;  // float4 index over [64][D / 4]
+      const int k = e / C4, c4 = e % C4;
+      if (e < 16 * D)
+        store4(sS + k * Lay::LDB + 4 * c4, k < m ? load4(pg + static_cast<size_t>(k) * D + 4 * c4)
+                                                  : make_float4(0.f, 0.f, 0.f, 0.f));
+    }
+    __syncthreads();
+    constexpr int NPM = 4 * CS, PPM = (NPM + NWV - 1) / NWV;
+    const int ksteps = (m + 3) / 4;
+#pragma unroll
+    for (int jj = 0; jj < PPM; ++jj) {
+      const int pr = wv * PPM + jj;
+      if (pr < NPM) {
+        const int ti = pr / CS, tc = pr % CS;
+        f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < ksteps; ++ks) {
+          const int k = ks * 4 + (ln >> 4);
+          a4 = mfma16x16x4(sXm[(ti * 16 + (ln & 15)) * LDX + k], sS[k * Lay::LDB + tc * 16 + (ln & 15)], a4);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sB[(ti * 16 + 4 * (ln >> 4) + r) * Lay::LDB + tc * 16 + (ln & 15)] = a4[r];
+      }
+    }
+    __syncthreads();  // X and S are dead: the C and halo areas are free again
+  }
+  if (has_w) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int e = tid + NT * q;
@@ -513,6 +575,9 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
         }
         cv[q] = v;
       }
+    } else if constexpr (MIX) {
+#pragma unroll
+      for (int q = 0; q < NCV; ++q) cv[q] = cv0[q];
     } else {
 #pragma unroll
       for (int q = 0; q < NCV; ++q) {
@@ -524,12 +589,14 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
     }
     constexpr int NQB = (16 * D + NT - 1) / NT;
     float4 bv[NQB];
+    if constexpr (!MIX) {
 #pragma unroll
-    for (int q = 0; q < NQB; ++q) {
-      const int e = tid + NT * q;
-      const int rr = e / C4, c4 = e % C4;
-      bv[q] = (e < 16 * D && rr < nl) ? load4(pg + static_cast<size_t>(lc0 + rr) * D + 4 * c4)
-                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int q = 0; q < NQB; ++q) {
+        const int e = tid + NT * q;
+        const int rr = e / C4, c4 = e % C4;
+        bv[q] = (e < 16 * D && rr < nl) ? load4(pg + static_cast<size_t>(lc0 + rr) * D + 4 * c4)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
     const float muv = (mu && tid < 64 && tid < nl) ? mu[static_cast<size_t>(g) * m + lc0 + tid] : 0.f;
     __syncthreads();  // previous chunk's reads are done
@@ -544,10 +611,12 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
         sC[(e >> 6) * Lay::LDC + (e & 63)] = cv[q];
       }
     }
+    if constexpr (!MIX) {
 #pragma unroll
-    for (int q = 0; q < NQB; ++q) {
-      const int e = tid + NT * q;
-      if (e < 16 * D) store4(sB + (e / C4) * Lay::LDB + 4 * (e % C4), bv[q]);
+      for (int q = 0; q < NQB; ++q) {
+        const int e = tid + NT * q;
+        if (e < 16 * D) store4(sB + (e / C4) * Lay::LDB + 4 * (e % C4), bv[q]);
+      }
     }
     if (tid < 64) sMu[tid] = muv;
     __syncthreads();
@@ -632,9 +701,24 @@ static void laplace_t(const Shape& s, const void* Q, const void* K, const float*
   const int tq = (srcmask & 1) ? tilesN : 0, tk = (srcmask & 2) ? tilesN : 0, tl = (srcmask & 4) ? tilesM : 0;
   const long waves = static_cast<long>(s.G) * (tq + tk + tl);
   if (waves == 0) return;
-  // Split the landmark loop until the chip holds about 12 waves per CU, keeping >= 8 landmarks per wave.
+  // Split the landmark loop into nlc chunks (>= 8 landmarks each), keeping all W waves resident at once (6 per
+  // SIMD fit). The slowest SIMD is then the one dealt ceil(W / 1024) waves.
+  constexpr int kSimds = 1024;     // 256 CUs x 4 SIMDs
+  constexpr int kResident = 6;     // waves of this kernel that fit on one SIMD
   int nlc = 1;
-  while (waves * nlc < 3072 && cdiv(s.m, nlc * 2) >= 8) nlc *= 2;
+  double best = -1.0;
+  for (int c = 1; c <= 32 && cdiv(s.m, c) >= (c == 1 ? 1 : 8); ++c) {
+    const int cc = cdiv(s.m, cdiv(s.m, c));  // chunk count after rounding the chunk length
+    if (cc > 1 && waves * cc > static_cast<long>(kResident) * kSimds) break;
+    const double per = static_cast<double>(waves * cc) / kSimds;
+    // fewer waves than SIMDs: more chunks only add parallelism. Otherwise: balance of the last round, times how
+    // well per waves hide the scalar-load and memory latency, minus a small cost per extra row reload.
+    const double score = per < 1.0 ? per : per / std::ceil(per) * (per / (per + 0.5)) - 0.01 * cc;
+    if (score > best + 1e-9) {
+      best = score;
+      nlc = cc;
+    }
+  }
   const int lc = cdiv(s.m, nlc);
   nlc = cdiv(s.m, lc);
   const float scale = static_cast<float>(-1.4426950408889634 / static_cast<double>(s.lambda));
@@ -746,55 +830,78 @@ hipError_t launch_mix(const Shape& s, const float* X, const float* S, const floa
   return hipGetLastError();
 }
 
-template <typename T, int D, bool FUSED>
+template <typename T, int D, bool FUSED, bool MIX>
 static void out_launch(const Shape& s, const float* CQ, const float* P, const float* mu, const void* V,
-                       const float* w, void* Y, int flip, const void* Q, const float* L, hipStream_t st) {
+                       const float* w, void* Y, int flip, const void* Q, const float* L, const float* X,
+                       hipStream_t st) {
   const int tiles_x = cdiv(s.W, 8), tiles_y = cdiv(s.H, 8);
   const size_t lds = sizeof(float) * OutLds<D>::TOTAL;
   if (lds > 64 * 1024)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_out<T, D, FUSED>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_out<T, D, FUSED, MIX>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   const float scale = static_cast<float>(-1.4426950408889634 / static_cast<double>(s.lambda));
-  hipLaunchKernelGGL((k_out<T, D, FUSED>), dim3(tiles_x * tiles_y, s.G), dim3(512), lds, st, CQ, P, mu,
+  hipLaunchKernelGGL((k_out<T, D, FUSED, MIX>), dim3(tiles_x * tiles_y, s.G), dim3(512), lds, st, CQ, P, mu,
                      static_cast<const T*>(V), w, static_cast<T*>(Y), s.N, s.m, s.H, s.W, s.heads, flip, tiles_x,
-                     static_cast<const T*>(Q), L, scale);
+                     static_cast<const T*>(Q), L, scale, X);
 }
 
-template <typename T, bool FUSED>
+template <typename T, bool FUSED, bool MIX>
 static void out_d(const Shape& s, const float* CQ, const float* P, const float* mu, const void* V, const float* w,
-                  void* Y, int flip, const void* Q, const float* L, hipStream_t st) {
+                  void* Y, int flip, const void* Q, const float* L, const float* X, hipStream_t st) {
   switch (s.d) {
-    case 16: out_launch<T, 16, FUSED>(s, CQ, P, mu, V, w, Y, flip, Q, L, st); break;
-    case 32: out_launch<T, 32, FUSED>(s, CQ, P, mu, V, w, Y, flip, Q, L, st); break;
-    case 64: out_launch<T, 64, FUSED>(s, CQ, P, mu, V, w, Y, flip, Q, L, st); break;
-    default: out_launch<T, 128, FUSED>(s, CQ, P, mu, V, w, Y, flip, Q, L, st); break;
+    case 16: out_launch<T, 16, FUSED, MIX>(s, CQ, P, mu, V, w, Y, flip, Q, L, X, st); break;
+    case 32: out_launch<T, 32, FUSED, MIX>(s, CQ, P, mu, V, w, Y, flip, Q, L, X, st); break;
+    case 64: out_launch<T, 64, FUSED, MIX>(s, CQ, P, mu, V, w, Y, flip, Q, L, X, st); break;
+    default: out_launch<T, 128, FUSED, MIX>(s, CQ, P, mu, V, w, Y, flip, Q, L, X, st); break;
   }
 }
 
 hipError_t launch_out(const Shape& s, const float* CQ, const float* P, const float* mu, const void* V, const float* w,
                       void* Y, hipStream_t st) {
   if (s.dtype == 1)
-    out_d<bf16_t, false>(s, CQ, P, mu, V, w, Y, 0, nullptr, nullptr, st);
+    out_d<bf16_t, false, false>(s, CQ, P, mu, V, w, Y, 0, nullptr, nullptr, nullptr, st);
   else
-    out_d<float, false>(s, CQ, P, mu, V, w, Y, 0, nullptr, nullptr, st);
+    out_d<float, false, false>(s, CQ, P, mu, V, w, Y, 0, nullptr, nullptr, nullptr, st);
+  return hipGetLastError();
+}
+
+bool out_mix_supported(const Shape& s) { return s.m <= 64 && s.d >= 32; }
+
+template <typename T>
+static void out_mix_d(const Shape& s, const float* CQ, const float* X, const float* S, const void* V, const float* w,
+                      void* Y, hipStream_t st) {
+  switch (s.d) {
+    case 32: out_launch<T, 32, false, true>(s, CQ, S, nullptr, V, w, Y, 0, nullptr, nullptr, X, st); break;
+    case 64: out_launch<T, 64, false, true>(s, CQ, S, nullptr, V, w, Y, 0, nullptr, nullptr, X, st); break;
+    default: out_launch<T, 128, false, true>(s, CQ, S, nullptr, V, w, Y, 0, nullptr, nullptr, X, st); break;
+  }
+}
+
+hipError_t launch_out_mix(const Shape& s, const float* CQ, const float* X, const float* S, const void* V,
+                          const float* w, void* Y, hipStream_t st) {
+  if (!out_mix_supported(s)) return hipErrorInvalidValue;
+  if (s.dtype == 1)
+    out_mix_d<bf16_t>(s, CQ, X, S, V, w, Y, st);
+  else
+    out_mix_d<float>(s, CQ, X, S, V, w, Y, st);
   return hipGetLastError();
 }
 
 hipError_t launch_out_fused(const Shape& s, const void* Q, const float* L, const float* P, const void* V,
                             const float* w, void* Y, hipStream_t st) {
   if (s.dtype == 1)
-    out_d<bf16_t, true>(s, nullptr, P, nullptr, V, w, Y, 0, Q, L, st);
+    out_d<bf16_t, true, false>(s, nullptr, P, nullptr, V, w, Y, 0, Q, L, nullptr, st);
   else
-    out_d<float, true>(s, nullptr, P, nullptr, V, w, Y, 0, Q, L, st);
+    out_d<float, true, false>(s, nullptr, P, nullptr, V, w, Y, 0, Q, L, nullptr, st);
   return hipGetLastError();
 }
 
 hipError_t launch_out_adjoint(const Shape& s, const float* C, const float* P, const void* U, const float* w, void* out,
                               hipStream_t st) {
   if (s.dtype == 1)
-    out_d<bf16_t, false>(s, C, P, nullptr, U, w, out, 1, nullptr, nullptr, st);
+    out_d<bf16_t, false, false>(s, C, P, nullptr, U, w, out, 1, nullptr, nullptr, nullptr, st);
   else
-    out_d<float, false>(s, C, P, nullptr, U, w, out, 1, nullptr, nullptr, st);
+    out_d<float, false, false>(s, C, P, nullptr, U, w, out, 1, nullptr, nullptr, nullptr, st);
   return hipGetLastError();
 }
 

@@ -33,6 +33,10 @@ hipError_t launch_mix(const Shape& s, const float* X, const float* S, const floa
                       hipStream_t st);
 hipError_t launch_out(const Shape& s, const float* CQ, const float* P, const float* mu, const void* V,
                       const float* w, void* Y, hipStream_t st);
+// Y = C_Q (X S) + DWC(V) with P = X S formed in the output kernel (no whitening; out_mix_supported: m <= 64, d >= 32).
+bool out_mix_supported(const Shape& s);
+hipError_t launch_out_mix(const Shape& s, const float* CQ, const float* X, const float* S, const void* V,
+                          const float* w, void* Y, hipStream_t st);
 // Y = C_Q P + DWC(V) with C_Q computed in the kernel from Q and L (no whitening); C_Q is never stored.
 hipError_t launch_out_fused(const Shape& s, const void* Q, const float* L, const float* P, const void* V,
                             const float* w, void* Y, hipStream_t st);
