@@ -211,8 +211,13 @@ int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const voi
   LF_TRY(lf::launch_landmark_pool(s, Q, L, st));
   LF_TRY(lf::launch_laplace(s, Q, K, L, CQ, CK, We, st));
   if (wh) LF_TRY(lf::launch_whiten_stats(s, CQ, mu, rstd, st));
-  LF_TRY(lf::launch_ns(s, We, X, xs, alpha, nullptr, nstmp, st));
-  LF_TRY(lf::launch_ckv(s, CK, V, part, S, st));
+  if (lf::ns_side_supported(s)) {
+    // One launch: Newton-Schulz on G CUs, S = C_K^T V on the others.
+    LF_TRY(lf::launch_ns_side(s, We, X, xs, alpha, CK, V, S, st));
+  } else {
+    LF_TRY(lf::launch_ns(s, We, X, xs, alpha, nullptr, nstmp, st));
+    LF_TRY(lf::launch_ckv(s, CK, V, part, S, st));
+  }
   if (!saved && !wh && lf::out_mix_supported(s)) {
     // Inference: P = X S is formed inside the output kernel (no landmark-mix launch, P never stored).
     LF_TRY(lf::launch_out_mix(s, CQ, X, S, V, dwc_w, Y, st));

@@ -48,5 +48,10 @@ hipError_t launch_out_adjoint(const Shape& s, const float* C, const float* P, co
 size_t ns_tmp_floats(const Shape& s);
 hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float* alpha, float* resid, float* tmp,
                      hipStream_t st);
+// Newton-Schulz (m <= 64) in one launch with S = C_K^T V computed in the CUs the solver leaves idle.
+// ns_side_supported: m <= 64, d in {16, 32, 64} and fewer slices than CUs.
+bool ns_side_supported(const Shape& s);
+hipError_t launch_ns_side(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
+                          const void* V, float* S, hipStream_t st);
 
 }  // namespace lf

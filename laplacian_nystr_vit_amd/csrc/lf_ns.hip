@@ -4,6 +4,7 @@
 // W is shifted by eps I, X_0 = alpha W^T and X_{k+1} = X_k (2I - W X_k): only matrix products and additions,
 // no inverse or SVD. alpha = 1/(||W||_1 ||W||_inf) (max column abs sum times max row abs sum) is the reading that
 // keeps every eigenvalue of alpha W W^T in (0, 1]; the page's 2/||W||_2 would diverge for a unit-diagonal W.
+#include <cmath>
 #include <type_traits>
 
 #include "lf_device.h"
@@ -170,9 +171,9 @@ __device__ __forceinline__ void split_scaled4(f32x4 a, float s, half4& h, half4&
 }
 
 template <int ST, int KC>
-__global__ __launch_bounds__(512) void k_ns_small(const float* __restrict__ We, float* __restrict__ Xout,
-                                                  float* __restrict__ xs, float* __restrict__ alpha_out,
-                                                  float* __restrict__ resid, int m, int iters) {
+__device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ We, float* __restrict__ Xout,
+                                               float* __restrict__ xs, float* __restrict__ alpha_out,
+                                               float* __restrict__ resid, int m, int iters) {
   constexpr int TQ = ST >= 2 ? ST / 2 : 1;  // tiles per side of a wave's quadrant
   constexpr int NQA = ST == 1 ? 1 : 4;      // quadrants with work
   constexpr int NTH = 512;
@@ -184,7 +185,6 @@ __global__ __launch_bounds__(512) void k_ns_small(const float* __restrict__ We, 
   // Bits of the largest |X| entry of the iterate written in step k, in slot k % 3: slot k + 1 is cleared during
   // step k (its last readers finished before the barrier of step k - 1), so the one barrier per step suffices.
   __shared__ unsigned int s_max[3];
-  const int g = blockIdx.x;
   const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
   const size_t mm = static_cast<size_t>(m) * m;
   const float* wg = We + g * mm;
@@ -529,6 +529,151 @@ __global__ __launch_bounds__(512) void k_ns_small(const float* __restrict__ We, 
     __syncthreads();
     if (tid == 0) resid[g] = static_cast<float>(sqrt(red[0][0][0] + red[0][0][1] + red[0][0][2] + red[0][0][3]));
   }
+}
+
+template <int ST, int KC>
+__global__ __launch_bounds__(512) void k_ns_small(const float* __restrict__ We, float* __restrict__ Xout,
+                                                  float* __restrict__ xs, float* __restrict__ alpha_out,
+                                                  float* __restrict__ resid, int m, int iters) {
+  ns_small_block<ST, KC>(static_cast<int>(blockIdx.x), We, Xout, xs, alpha_out, resid, m, iters);
+}
+
+// =====================================================================================================
+// Newton-Schulz with side work. The m <= 64 solver occupies one CU per slice for its whole chain of dependent
+// steps while the rest of the chip would idle, and a second stream costs more in cross-queue synchronisation than
+// it saves at this size. So the same launch carries, after the G solver blocks, blocks that compute
+// S = C_K^T V, each one (slice, 16-landmark tile, 16-channel tile) of S over all N tokens. No block of this launch
+// waits for another: a cross-XCD hand-off of partial sums needs device-scope release and acquire fences, and
+// on this chip those write back and invalidate a whole L2, which costs more than the solver itself.
+// Each block holds the solver's LDS (one block per CU); the tiles fill the CUs the solver leaves free and finish
+// inside the solver's time.
+// =====================================================================================================
+
+// One S tile by one 512-thread block. Wave w sums a contiguous range of 16-token groups on fp32 MFMA
+// (A = C_K, landmark-major, B = V): in group q, lane (i, k) feeds landmark i and channel i of the tile with tokens
+// 16q + 4k + u at k-step u, loaded from global memory straight into the MFMA operand layout. The eight wave tiles
+// are then summed in LDS in wave order, so the result does not depend on timing.
+template <typename T, int D>
+__device__ __forceinline__ void ckv_tile_block(int blk, const float* __restrict__ C, const T* __restrict__ V,
+                                               float* __restrict__ S, int N, int m, float* sRed) {
+  constexpr int DT = D / 16;
+  const int LT = (m + 15) / 16;
+  const int ct = blk % DT;
+  const int lt = (blk / DT) % LT;
+  const int g = blk / (DT * LT);
+  const int wv = wave_id(), ln = lane_id();
+  const int i = ln & 15, k = ln >> 4;
+  const bool lok = lt * 16 + i < m;
+  const float* __restrict__ crow = C + (static_cast<size_t>(g) * m + (lok ? lt * 16 + i : 0)) * N;
+  const T* __restrict__ vcol = V + static_cast<size_t>(g) * N * D + ct * 16 + i;
+  const int groups = (N + 15) / 16, gpw = (groups + 7) / 8;
+  const int q0 = min(groups, wv * gpw), q1 = min(groups, q0 + gpw);
+  const int qf = max(q0, min(q1, N / 16));  // groups [q0, qf) have all 16 tokens in range
+  const float amask = lok ? 1.f : 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto full_groups = [&](auto vec) {
+#pragma unroll 4
+    for (int q = q0; q < qf; ++q) {
+      const int t = q * 16 + 4 * k;
+      float a[4], b[4];
+      if constexpr (decltype(vec)::value) {
+        const float4 c4 = load4(crow + t);
+        a[0] = c4.x;
+        a[1] = c4.y;
+        a[2] = c4.z;
+        a[3] = c4.w;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[u] = crow[t + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) b[u] = to_f32(vcol[static_cast<size_t>(t + u) * D]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc = mfma16x16x4(a[u] * amask, b[u], acc);
+    }
+  };
+  if ((N & 3) == 0)
+    full_groups(std::integral_constant<bool, true>{});
+  else
+    full_groups(std::integral_constant<bool, false>{});
+  for (int q = qf; q < q1; ++q) {  // the ragged last group
+    const int t = q * 16 + 4 * k;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool in = t + u < N;
+      const float a = in ? crow[t + u] * amask : 0.f;
+      const float b = in ? to_f32(vcol[static_cast<size_t>(t + u) * D]) : 0.f;
+      acc = mfma16x16x4(a, b, acc);
+    }
+  }
+  // acc[r] is row 4k + r, column i of this wave's tile
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sRed[wv * 256 + (4 * k + r) * 16 + i] = acc[r];
+  __syncthreads();
+  const int tid = static_cast<int>(threadIdx.x);
+  if (tid < 256) {
+    const int row = tid >> 4, col = tid & 15;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sum += sRed[w * 256 + tid];
+    if (lt * 16 + row < m) S[(static_cast<size_t>(g) * m + lt * 16 + row) * D + ct * 16 + col] = sum;
+  }
+}
+
+template <typename T, int D, int ST, int KC>
+__global__ __launch_bounds__(512) void k_ns_side(const float* __restrict__ We, float* __restrict__ Xout,
+                                                 float* __restrict__ xs, float* __restrict__ alpha_out, int m,
+                                                 int iters, int N, int G, const float* __restrict__ CK,
+                                                 const T* __restrict__ V, float* __restrict__ S) {
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < G) {
+    ns_small_block<ST, KC>(b, We, Xout, xs, alpha_out, nullptr, m, iters);
+    return;
+  }
+  __shared__ float sRed[8 * 256];
+  ckv_tile_block<T, D>(b - G, CK, V, S, N, m, sRed);
+}
+
+template <typename T, int D>
+static void ns_side_st(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
+                       const T* V, float* S, hipStream_t st) {
+  const int blocks = s.G * (1 + (s.m + 15) / 16 * (D / 16));
+  const int nt = (s.m + 15) / 16;
+#define LF_NS_SIDE(ST_, KC_)                                                                                        \
+  hipLaunchKernelGGL((k_ns_side<T, D, ST_, KC_>), dim3(blocks), dim3(512), 0, st, We, X, xs, alpha, s.m, s.ns_iters, \
+                     s.N, s.G, CK, V, S)
+  if (nt == 1)
+    LF_NS_SIDE(1, 1);
+  else if (nt == 2)
+    LF_NS_SIDE(2, 1);
+  else
+    LF_NS_SIDE(4, 2);
+#undef LF_NS_SIDE
+}
+
+bool ns_side_supported(const Shape& s) {
+  return s.m <= 64 && (s.d == 16 || s.d == 32 || s.d == 64) && s.G < 256;
+}
+
+template <typename T>
+static void ns_side_t(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
+                      const void* V, float* S, hipStream_t st) {
+  const T* v = static_cast<const T*>(V);
+  switch (s.d) {
+    case 16: ns_side_st<T, 16>(s, We, X, xs, alpha, CK, v, S, st); break;
+    case 32: ns_side_st<T, 32>(s, We, X, xs, alpha, CK, v, S, st); break;
+    default: ns_side_st<T, 64>(s, We, X, xs, alpha, CK, v, S, st); break;
+  }
+}
+
+hipError_t launch_ns_side(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
+                          const void* V, float* S, hipStream_t st) {
+  if (!ns_side_supported(s)) return hipErrorInvalidValue;
+  if (s.dtype == 1)
+    ns_side_t<bf16_t>(s, We, X, xs, alpha, CK, V, S, st);
+  else
+    ns_side_t<float>(s, We, X, xs, alpha, CK, V, S, st);
+  return hipGetLastError();
 }
 
 // =====================================================================================================
