@@ -42,9 +42,9 @@ def laplace_source_hash():
     path = os.path.join(ROOT, "laplacian_nystr_vit_amd", "csrc", "lf_fwd.hip")
     try:
         src = open(path).read()
-        a = src.index("__global__ __launch_bounds__(64) void k_laplace(")
+        a = src.index("__global__ __launch_bounds__(512) void k_laplace(")
         b = src.index("// ====", a)
-        c = src.index("static void laplace_t(")
+        c = src.index("struct LaplacePlan {")
         e = src.index("static void laplace_d(", c)
     except (OSError, ValueError):
         return None

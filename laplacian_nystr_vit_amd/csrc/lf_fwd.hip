@@ -2,6 +2,7 @@
 //
 // Citations: papernotes.org ICLR 2026 reading note "LaplacianFormer：用拉普拉斯核重新思考线性注意力"
 // ([note] below), sections motivation ("core idea"), framework (flowchart), Design 1, Design 2 and Design 3.
+#include <algorithm>
 #include <cmath>
 
 #include "lf_device.h"
@@ -72,26 +73,34 @@ __global__ __launch_bounds__(256) void k_landmark_pool(const T* __restrict__ Q, 
 // channel) the inner loop issues one v_sub_f32 and one v_add_f32 with an |.| source modifier, and no LDS or
 // vector-memory traffic. exp(-s/lambda) becomes one v_exp_f32 of s * (-log2(e)/lambda).
 //
-// Grid: one 64-thread block (one wave) per (slice, source, 64-row tile, landmark chunk). The landmark chunks
-// give each wave fewer landmarks so that the chip sees several waves per SIMD even at B*heads = 8.
+// Grid: one block per (slice, source, 64-row tile, landmark super-chunk) of nw waves. The block stages its 64 rows
+// in LDS once (as float32) and wave w of super-chunk sc takes the landmarks [(sc nw + w) lc, + lc): every row
+// leaves HBM once per super-chunk instead of once per wave, and the waves still split the landmark loop finely
+// enough that each SIMD holds several of them.
+// Block order: the super-chunks of one tile are consecutive, and blocks are remapped so that consecutive ones
+// run on one XCD (each XCD has its own L2 and the hardware deals blocks to the XCDs round-robin). A slice's
+// blocks then stay on few XCDs, so the CUs of an XCD share one slice's landmark rows in their scalar caches and
+// the super-chunks of a tile share its rows through L2.
 // =====================================================================================================
 template <typename T, int D>
-__global__ __launch_bounds__(64) void k_laplace(const T* __restrict__ Q, const T* __restrict__ K,
-                                                const float* __restrict__ L, float* __restrict__ CQ,
-                                                float* __restrict__ CK, float* __restrict__ We, int N, int m,
-                                                int tilesQ, int tilesK, int tilesL, int nlc, int lc, float scale,
-                                                float eps) {
+__global__ __launch_bounds__(512) void k_laplace(const T* __restrict__ Q, const T* __restrict__ K,
+                                                 const float* __restrict__ L, float* __restrict__ CQ,
+                                                 float* __restrict__ CK, float* __restrict__ We, int N, int m,
+                                                 int tilesQ, int tilesK, int tilesL, int nsc, int lc, float scale,
+                                                 float eps) {
   // tilesQ / tilesK / tilesL: 64-row tiles of Q, K and L rows per slice (0 leaves that source out).
-  // Workgroups are dealt to the 8 XCDs round-robin by index, and each XCD has its own L2. The index is remapped
-  // so that consecutive logical blocks (the landmark chunks of one row tile) run on the same XCD and share the
-  // tile's rows through that L2 instead of each fetching them from HBM.
+  constexpr int LDX = D + 4;  // row stride: 8 lanes of a float4 read cover all 32 banks
+  __shared__ float sX[64 * LDX];
   int b = static_cast<int>(blockIdx.x);
   {
     const int full = (static_cast<int>(gridDim.x) / 8) * 8;
     if (b < full) b = (b % 8) * (full / 8) + b / 8;
   }
-  const int lchunk = b % nlc;
-  b /= nlc;
+  const int nw = static_cast<int>(blockDim.x) >> 6;
+  const int tid = static_cast<int>(threadIdx.x), lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());  // uniform, so landmark loads stay scalar
+  const int sc = b % nsc;
+  b /= nsc;
   const int per_slice = tilesQ + tilesK + tilesL;
   const int local = b % per_slice;
   const int g = b / per_slice;
@@ -107,25 +116,37 @@ __global__ __launch_bounds__(64) void k_laplace(const T* __restrict__ Q, const T
     tile = local - tilesQ - tilesK;
   }
   const int rows = (src == 2) ? m : N;
-  const int row = tile * 64 + static_cast<int>(threadIdx.x);
-  const int l0 = lchunk * lc;
-  const int l1 = min(l0 + lc, m);
   const float* __restrict__ Lg = L + static_cast<size_t>(g) * m * D;
-  if (row >= rows) return;
+  const T* __restrict__ xg = (src == 0 ? Q : K) + static_cast<size_t>(g) * N * D;
+  for (int e = tid; e < 16 * D; e += 64 * nw) {  // float4 index over [64 rows][D / 4]
+    const int r = e / (D / 4), c4 = e % (D / 4);
+    const int row = tile * 64 + r;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < rows) v = (src == 2) ? load4(Lg + static_cast<size_t>(row) * D + 4 * c4)
+                                   : load4(xg + static_cast<size_t>(row) * D + 4 * c4);
+    store4(sX + r * LDX + 4 * c4, v);
+  }
+  __syncthreads();
+  const int row = tile * 64 + lane;
+  const int l0 = (sc * nw + wv) * lc;
+  const int l1 = min(l0 + lc, m);
+  if (row >= rows || l0 >= l1) return;
 
   float x[D];
-  float* out;       // this row's output, element l at out[l * ostride]
+#pragma unroll
+  for (int c = 0; c < D; c += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(sX + lane * LDX + c);
+    x[c] = v.x;
+    x[c + 1] = v.y;
+    x[c + 2] = v.z;
+    x[c + 3] = v.w;
+  }
+  float* out;  // this row's output, element l at out[l * ostride]
   size_t ostride;
   if (src == 2) {
-    const float* p = Lg + static_cast<size_t>(row) * D;
-#pragma unroll
-    for (int c = 0; c < D; ++c) x[c] = p[c];
     out = We + (static_cast<size_t>(g) * m + row) * m;
     ostride = 1;
   } else {
-    const T* p = (src == 0 ? Q : K) + (static_cast<size_t>(g) * N + row) * D;
-#pragma unroll
-    for (int c = 0; c < D; ++c) x[c] = to_f32(p[c]);
     // C is stored landmark-major (C[g][l][i]): for a fixed landmark the 64 lanes of a wave write 64 consecutive
     // floats, one 256-byte segment per store instruction.
     out = (src == 0 ? CQ : CK) + static_cast<size_t>(g) * m * N + row;
@@ -694,37 +715,60 @@ hipError_t launch_landmark_pool(const Shape& s, const void* Q, float* L, hipStre
   return hipGetLastError();
 }
 
+// Launch shape of the distance kernel for T row tiles: nsc landmark super-chunks per tile, nw waves per block,
+// lc landmarks per wave. A small model of the chip picks it: blocks are dealt in rounds of what fits on the 256 CUs
+// at once (waves per SIMD from the register use, blocks per CU from LDS); a round costs the work of its busiest
+// SIMD (its waves times lc + 2 landmarks, the 2 standing for a wave's fixed start-up cost), divided by how well w
+// waves per SIMD hide the memory and scalar-load latency, w / (w + 2); each super-chunk adds 1% for reloading the
+// rows. The constants were fitted to a sweep of all plans on the stage-1, stage-3 and high-resolution shapes, where
+// this picks the fastest plan of each.
+struct LaplacePlan {
+  int nsc, nw, lc;
+};
+
+static LaplacePlan laplace_plan(long tiles, int m, int d) {
+  const int resident = d <= 32 ? 8 : (d <= 64 ? 6 : 3);  // waves per SIMD that fit the kernel's registers
+  const int lds_blocks = (160 * 1024) / (64 * (d + 4) * 4);
+  auto eff = [](double w) { return w / (w + 2.0); };
+  LaplacePlan best{1, 1, m};
+  double best_t = 1e300;
+  for (int nw = 1; nw <= 8; ++nw) {
+    for (int nsc = 1; nsc <= 16; ++nsc) {
+      const int chunks = nsc * nw;
+      const int lc = cdiv(m, chunks);
+      if (chunks > 1 && lc < 4) continue;        // too little work per wave
+      if (static_cast<long>(chunks) * lc - m >= lc) continue;  // a wave with no landmarks
+      const int rb = std::min(4 * resident / nw, lds_blocks);
+      if (rb < 1) continue;
+      const long nb = tiles * nsc, per_round = 256L * rb;
+      auto round = [&](long bpc) {
+        const double w = static_cast<double>(bpc * nw) / 4.0;
+        return std::ceil(w) * (lc + 2) / eff(w);
+      };
+      double t = static_cast<double>(nb / per_round) * round(rb);
+      if (nb % per_round) t += round(cdiv(nb % per_round, 256));
+      t *= 1.0 + 0.01 * nsc;
+      if (t < best_t - 1e-9) {
+        best_t = t;
+        best = {nsc, nw, lc};
+      }
+    }
+  }
+  return best;
+}
+
 template <typename T, int D>
 static void laplace_t(const Shape& s, const void* Q, const void* K, const float* L, float* CQ, float* CK, float* We,
                       int srcmask, hipStream_t st) {
   const int tilesN = cdiv(s.N, 64), tilesM = cdiv(s.m, 64);
   const int tq = (srcmask & 1) ? tilesN : 0, tk = (srcmask & 2) ? tilesN : 0, tl = (srcmask & 4) ? tilesM : 0;
-  const long waves = static_cast<long>(s.G) * (tq + tk + tl);
-  if (waves == 0) return;
-  // Split the landmark loop into nlc chunks (>= 8 landmarks each), keeping all W waves resident at once (6 per
-  // SIMD fit). The slowest SIMD is then the one dealt ceil(W / 1024) waves.
-  constexpr int kSimds = 1024;     // 256 CUs x 4 SIMDs
-  constexpr int kResident = 6;     // waves of this kernel that fit on one SIMD
-  int nlc = 1;
-  double best = -1.0;
-  for (int c = 1; c <= 32 && cdiv(s.m, c) >= (c == 1 ? 1 : 8); ++c) {
-    const int cc = cdiv(s.m, cdiv(s.m, c));  // chunk count after rounding the chunk length
-    if (cc > 1 && waves * cc > static_cast<long>(kResident) * kSimds) break;
-    const double per = static_cast<double>(waves * cc) / kSimds;
-    // fewer waves than SIMDs: more chunks only add parallelism. Otherwise: balance of the last round, times how
-    // well per waves hide the scalar-load and memory latency, minus a small cost per extra row reload.
-    const double score = per < 1.0 ? per : per / std::ceil(per) * (per / (per + 0.5)) - 0.01 * cc;
-    if (score > best + 1e-9) {
-      best = score;
-      nlc = cc;
-    }
-  }
-  const int lc = cdiv(s.m, nlc);
-  nlc = cdiv(s.m, lc);
+  const long tiles = static_cast<long>(s.G) * (tq + tk + tl);
+  if (tiles == 0) return;
+  const LaplacePlan pl = laplace_plan(tiles, s.m, D);
   const float scale = static_cast<float>(-1.4426950408889634 / static_cast<double>(s.lambda));
-  const dim3 grid(static_cast<unsigned>(waves * nlc));
-  hipLaunchKernelGGL((k_laplace<T, D>), grid, dim3(64), 0, st, static_cast<const T*>(Q), static_cast<const T*>(K), L,
-                     CQ, CK, We, s.N, s.m, tq, tk, tl, nlc, lc, scale, s.eps);
+  hipLaunchKernelGGL((k_laplace<T, D>), dim3(static_cast<unsigned>(tiles * pl.nsc)), dim3(64 * pl.nw), 0, st,
+                     static_cast<const T*>(Q), static_cast<const T*>(K), L, CQ, CK, We, s.N, s.m, tq, tk, tl, pl.nsc,
+                     pl.lc, scale, s.eps);
 }
 
 template <typename T>
