@@ -451,16 +451,44 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
   constexpr int CS = D / 16;                     // channel strips of 16
   constexpr int NP = CS * 4;                     // output tiles: (channel strip, 16-token tile) pairs
   constexpr int PPW = (NP + NWV - 1) / NWV;      // tiles per wave
+  static_assert(NP % PPW == 0, "tiles per wave must divide the tile count");
   constexpr int C4 = D / 4;
   constexpr int LQM = 64 / NWV;                  // FUSED: most landmarks of a chunk per wave
   const int g = blockIdx.y;
   const int ty0 = (blockIdx.x / tiles_x) * 8, tx0 = (blockIdx.x % tiles_x) * 8;
   const int h = g % heads;
-  const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
+  // the wave index through readfirstlane: the compiler then knows it is uniform and keeps the per-wave tile
+  // guards below as scalar branches outside the MFMA sequences
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
   const float* cg = CQ + static_cast<size_t>(g) * m * N;
   const float* pg = P + static_cast<size_t>(g) * m * D;
   const T* vg = V + static_cast<size_t>(g) * N * D;
   const bool has_w = w != nullptr;
+
+  // MIX: X and S are loaded before anything else. Vector loads complete in issue order, so the prologue's product
+  // then waits only for these two small matrices while the V halo and the C_Q tile below are still in flight. The
+  // loads up to that point are branch-free (clamped address; out-of-range values are zeroed where they are stored
+  // to LDS), which lets the compiler wait for a count of outstanding loads instead of draining them all.
+  constexpr int LDX = 68;                               // MIX: X row stride in the C area
+  constexpr int NXQ = MIX ? 4096 / NT : 1;              // MIX: X elements per thread, [64][64] zero-padded
+  constexpr int NSQ = MIX ? (16 * D + NT - 1) / NT : 1;  // MIX: S float4 per thread, [64][D / 4]
+  float xr[NXQ];
+  float4 sr[NSQ];
+  if constexpr (MIX) {
+    const float* xg = Xm + static_cast<size_t>(g) * m * m;
+#pragma unroll
+    for (int q = 0; q < NXQ; ++q) {
+      const int e = tid + NT * q;
+      const int l = e >> 6, k = e & 63;
+      xr[q] = xg[(l < m && k < m) ? l * m + k : 0];
+    }
+#pragma unroll
+    for (int q = 0; q < NSQ; ++q) {
+      const int e = tid + NT * q;  // float4 index over [64][D / 4]
+      const int k = e / C4, c4 = e % C4;
+      sr[q] = load4(pg + ((e < 16 * D && k < m) ? static_cast<size_t>(k) * D + 4 * c4 : 0));
+    }
+  }
 
   // 1. V halo and filter taps
   constexpr int NQ = (100 * C4 + NT - 1) / NT;
@@ -469,16 +497,14 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int e = tid + NT * q;
-      vb[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e < 100 * C4) {
-        const int tok = e / C4, c4 = e % C4;
-        const int y = ty0 - 1 + tok / 10, x = tx0 - 1 + tok % 10;
-        if (y >= 0 && y < H && x >= 0 && x < W) vb[q] = load4(vg + static_cast<size_t>(y * W + x) * D + 4 * c4);
-      }
+      const int tok = e / C4, c4 = e % C4;
+      const int y = ty0 - 1 + tok / 10, x = tx0 - 1 + tok % 10;
+      const bool in = e < 100 * C4 && y >= 0 && y < H && x >= 0 && x < W;
+      vb[q] = load4(vg + (in ? static_cast<size_t>(y * W + x) * D + 4 * c4 : 0));  // zeroed when staged
     }
   }
   // MIX: m <= 64 is a single landmark chunk; its C_Q tile is loaded up front so that its latency overlaps the
-  // prologue's X and S loads.
+  // prologue's product.
   constexpr int NCV0 = MIX ? 4096 / NT : 1;
   float cv0[NCV0];
   if constexpr (MIX) {
@@ -487,46 +513,51 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
       const int e = tid + NT * q;
       const int l = e >> 6, u = e & 63;
       const int y = ty0 + (u >> 3), x = tx0 + (u & 7);
-      cv0[q] = (l < m && y < H && x < W) ? cg[static_cast<size_t>(l) * N + y * W + x] : 0.f;
+      cv0[q] = cg[(l < m && y < H && x < W) ? static_cast<size_t>(l) * N + y * W + x : 0];  // zeroed when staged
     }
   }
   if constexpr (MIX) {
     // P = X S into the P area: X [m][m] staged in the C area (row stride 68), S [m][D] in the halo area (row
     // stride LDB); both zero beyond m, so P's rows beyond m come out zero.
-    constexpr int LDX = 68;
     float* sXm = sC;
     float* sS = sVh;
-    const float* xg = Xm + static_cast<size_t>(g) * m * m;
 #pragma unroll
-    for (int q = 0; q < 4096 / NT; ++q) {
+    for (int q = 0; q < NXQ; ++q) {
       const int e = tid + NT * q;
       const int l = e >> 6, k = e & 63;
-      sXm[l * LDX + k] = (l < m && k < m) ? xg[l * m + k] : 0.f;
+      sXm[l * LDX + k] = (l < m && k < m) ? xr[q] : 0.f;
     }
     static_assert(64 * Lay::LDB <= 100 * Lay::LDV && 64 * LDX <= 64 * Lay::LDC, "MIX staging must fit");
 #pragma unroll
-    for (int q = 0; q < (16 * D + NT - 1) / NT; ++q) {
-      const int e = tid + NT * q;  // float4 index over [64][D / 4]
-      const int k = e / C4, c4 = e % C4;
+    for (int q = 0; q < NSQ; ++q) {
+      const int e = tid + NT * q;
       if (e < 16 * D)
-        store4(sS + k * Lay::LDB + 4 * c4, k < m ? load4(pg + static_cast<size_t>(k) * D + 4 * c4)
-                                                  : make_float4(0.f, 0.f, 0.f, 0.f));
+        store4(sS + (e / C4) * Lay::LDB + 4 * (e % C4), e / C4 < m ? sr[q] : make_float4(0.f, 0.f, 0.f, 0.f));
     }
     __syncthreads();
+    // All 16 k-steps of the zero-padded 64 x 64 X, fully unrolled with the wave's tiles interleaved, so the LDS
+    // reads of later steps are in flight during the MFMAs of earlier ones (the padding adds exact zeros).
+    // A wave owns PPM whole tiles or none (NPM is a multiple of PPM), so one uniform test covers them all.
     constexpr int NPM = 4 * CS, PPM = (NPM + NWV - 1) / NWV;
-    const int ksteps = (m + 3) / 4;
+    static_assert(NPM % PPM == 0, "tiles per wave must divide the tile count");
+    if (wv * PPM < NPM) {
+      f32x4 a4[PPM];
 #pragma unroll
-    for (int jj = 0; jj < PPM; ++jj) {
-      const int pr = wv * PPM + jj;
-      if (pr < NPM) {
-        const int ti = pr / CS, tc = pr % CS;
-        f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int ks = 0; ks < ksteps; ++ks) {
-          const int k = ks * 4 + (ln >> 4);
-          a4 = mfma16x16x4(sXm[(ti * 16 + (ln & 15)) * LDX + k], sS[k * Lay::LDB + tc * 16 + (ln & 15)], a4);
+      for (int jj = 0; jj < PPM; ++jj) a4[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const int k = ks * 4 + (ln >> 4);
+#pragma unroll
+        for (int jj = 0; jj < PPM; ++jj) {
+          const int ti = (wv * PPM + jj) / CS, tc = (wv * PPM + jj) % CS;
+          a4[jj] = mfma16x16x4(sXm[(ti * 16 + (ln & 15)) * LDX + k], sS[k * Lay::LDB + tc * 16 + (ln & 15)], a4[jj]);
         }
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sB[(ti * 16 + 4 * (ln >> 4) + r) * Lay::LDB + tc * 16 + (ln & 15)] = a4[r];
+      for (int jj = 0; jj < PPM; ++jj) {
+        const int ti = (wv * PPM + jj) / CS, tc = (wv * PPM + jj) % CS;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sB[(ti * 16 + 4 * (ln >> 4) + r) * Lay::LDB + tc * 16 + (ln & 15)] = a4[jj][r];
       }
     }
     __syncthreads();  // X and S are dead: the C and halo areas are free again
@@ -535,7 +566,10 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int e = tid + NT * q;
-      if (e < 100 * C4) store4(sVh + (e / C4) * Lay::LDV + 4 * (e % C4), vb[q]);
+      const int tok = e / C4;
+      const int y = ty0 - 1 + tok / 10, x = tx0 - 1 + tok % 10;
+      const bool in = y >= 0 && y < H && x >= 0 && x < W;
+      if (e < 100 * C4) store4(sVh + tok * Lay::LDV + 4 * (e % C4), in ? vb[q] : make_float4(0.f, 0.f, 0.f, 0.f));
     }
     for (int e = tid; e < 9 * D; e += NT) {
       const int q = e / D, c = e % D;
@@ -598,7 +632,11 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
       }
     } else if constexpr (MIX) {
 #pragma unroll
-      for (int q = 0; q < NCV; ++q) cv[q] = cv0[q];
+      for (int q = 0; q < NCV; ++q) {
+        const int e = tid + NT * q;
+        const int l = e >> 6, u = e & 63;
+        cv[q] = (l < m && ty0 + (u >> 3) < H && tx0 + (u & 7) < W) ? cv0[q] : 0.f;
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < NCV; ++q) {
@@ -644,18 +682,26 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
     if (mu && tid < D) {
       for (int kk = 0; kk < nl; ++kk) bias_acc += sMu[kk] * sB[kk * Lay::LDB + tid];
     }
-    const int ksteps = (nl + 3) / 4;
-    for (int ks = 0; ks < ksteps; ++ks) {
+    // a wave owns PPW whole tiles or none (NP is a multiple of PPW): one uniform test outside the k-steps
+    auto kstep = [&](int ks) {
       const int k = ks * 4 + (ln >> 4);
 #pragma unroll
       for (int j = 0; j < PPW; ++j) {
         const int pr = wv * PPW + j;
-        if (pr < NP) {
-          const int strip = pr >> 2, tile = pr & 3;
-          const float av = sB[k * Lay::LDB + strip * 16 + (ln & 15)];
-          const float bt = sC[k * Lay::LDC + tile * 16 + (ln & 15)];
-          acc[j] = mfma16x16x4(av, bt, acc[j]);
-        }
+        const int strip = pr >> 2, tile = pr & 3;
+        const float av = sB[k * Lay::LDB + strip * 16 + (ln & 15)];
+        const float bt = sC[k * Lay::LDC + tile * 16 + (ln & 15)];
+        acc[j] = mfma16x16x4(av, bt, acc[j]);
+      }
+    };
+    if (wv * PPW < NP) {
+      if constexpr (FUSED) {
+        // rows past the chunk's landmarks may be stale in the C area here: stop at nl
+        for (int ks = 0; ks < (nl + 3) / 4; ++ks) kstep(ks);
+      } else {
+        // the staged C and P rows past nl are zeros: all 16 k-steps, fully unrolled
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) kstep(ks);
       }
     }
   }
