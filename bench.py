@@ -8,6 +8,11 @@ output GEMM with the depthwise-conv epilogue. The default workload is the PVT st
 It prints one JSON line with the whole-job throughput (tokens/s = B*heads*N per step). It also prints the roofline
 of the dominant kernel (laplace_l1_exp: VALU-bound, timed with HIP events on its own stream) and the fp64 CPU
 oracle timed on a bounded sample of the same workload on the host cores.
+
+--workload picks another shape; for the training shape (whitening on) a step is lf_attn_fwd with the saved buffer
+followed by lf_attn_bwd. Besides the hot figure (one buffer set, as the contract's value) it reports a "cold" one:
+the same steps rotating over enough input/output/workspace sets (>= 512 MB in all) that no step finds its data in
+the 256 MB last-level cache (--no-cold skips it).
 """
 
 import argparse
@@ -21,6 +26,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "Laplacian-Nyström attention fwd tokens/s (B·heads·N) + % VALU/MFMA roofline"
+METRIC_TRAIN = "Laplacian-Nyström attention fwd+bwd tokens/s (B·heads·N) + % VALU/MFMA roofline"
+COLD_BYTES = 512 << 20
 
 # HBM traffic of the distance kernel, from two rocprofv3 counter passes over `bench.py --counters` (FETCH_SIZE,
 # then WRITE_SIZE), each scaled by what the same counter reads for a device copy of known size. The file records a
@@ -29,10 +36,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "laplace_l1_exp_pvt_s1_56x56_m49_t
 CALIB_COPY_MIB = 256
 COUNTER_LAUNCHES = 10
 
-# MI355X: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz issue 39.3e12 fp32 lane-operations per second. The published
-# 157.3 TFLOP/s fp32 vector peak counts an FMA as two flops and packed-fp32 as two lanes; the distance kernel's
-# v_sub_f32 and v_add_f32 |.| are neither, so its peak is 157.3 / 4.
-VALU_PEAK_TFLOPS = 256 * 64 * 2.4e9 / 1e12
+# MI355X: the published fp32 vector peak is 157.3 TFLOP/s, an FMA counted as two flops: 256 CUs x 4 SIMDs x 32
+# lanes per clock at 2.4 GHz, i.e. 78.6e12 fp32 lane-operations per second, which a stream of independent
+# v_add_f32 with register operands reaches to 80 % (63 T measured). The distance kernel's v_sub_f32 and
+# v_add_f32 |.| are one operation each.
+VALU_PEAK_TFLOPS = 256 * 4 * 32 * 2.4e9 / 1e12
 
 
 def laplace_source_hash():
@@ -141,6 +149,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall time budget of the oracle sample")
     ap.add_argument("--kernel-reps", type=int, default=100)
+    ap.add_argument("--no-cold", action="store_true", help="skip the timing over rotating buffer sets")
     ap.add_argument("--counters", action="store_true",
                     help="run only the distance kernel and a calibration copy (for rocprofv3 --pmc passes)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -157,19 +166,24 @@ def cpu_baseline(wl, inp, budget_s):
 
     op = O.Params(B=wl.B, heads=wl.heads, H=wl.H, W=wl.W, d=wl.d, r=wl.r, lam=wl.lam, eps=wl.eps,
                   ns_iters=wl.ns_iters, whiten=wl.whiten, whiten_eps=wl.whiten_eps)
+    train = bool(wl.whiten)
     slices = 0
     t0 = time.perf_counter()
     with threadpool_limits(limits=1):
         while True:
             b, h = divmod(slices % wl.G, wl.heads)
-            O.forward_slice(inp["Q"][b, h], inp["K"][b, h], inp["V"][b, h], inp["w64"][h * wl.d:(h + 1) * wl.d], op)
+            args = (inp["Q"][b, h], inp["K"][b, h], inp["V"][b, h], inp["w64"][h * wl.d:(h + 1) * wl.d])
+            fwd = O.forward_slice(*args, op)
+            if train:
+                O.backward_slice(*args, inp["dY"][b, h], op, fwd)
             slices += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
     dt = time.perf_counter() - t0
+    what = "forward + backward" if train else "forward"
     return {"value": slices * wl.N / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{slices} (batch, head) slices of {wl.name} ({wl.N} tokens each), fp64 numpy, one thread, "
-                      f"{dt:.1f} s"}
+            "sample": f"{what} of {slices} (batch, head) slices of {wl.name} ({wl.N} tokens each), fp64 numpy, "
+                      f"one thread, {dt:.1f} s"}
 
 
 def main():
@@ -202,27 +216,59 @@ def main():
             return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(x).cuda()
 
-    Q, K, V, w = dev(inp["Q_raw"]), dev(inp["K_raw"]), dev(inp["V_raw"]), dev(inp["w"])
     p = lf.make_params(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.r, wl.lam, wl.eps, wl.ns_iters, wl.whiten, wl.whiten_eps,
                        dt)
-    fwd_b, _, _ = lf.lf_attn_query(p)
-    ws = torch.empty(fwd_b, dtype=torch.uint8, device="cuda")
-    Y = torch.empty_like(Q)
+    train = bool(wl.whiten)
+    fwd_b, saved_b, bwd_b = lf.lf_attn_query(p)
     stream = torch.cuda.current_stream()
 
-    def step():
-        lf.lf_attn_fwd(p, Q, K, V, w, Y, None, ws, stream)
+    def make_set():
+        """One set of every buffer a step touches: inputs, outputs, workspaces (and the saved buffer, dY and the
+        gradients for a training step)."""
+        t = {"Q": dev(inp["Q_raw"]), "K": dev(inp["K_raw"]), "V": dev(inp["V_raw"]), "w": dev(inp["w"])}
+        t["Y"] = torch.empty_like(t["Q"])
+        t["ws"] = torch.empty(max(fwd_b, bwd_b if train else 0), dtype=torch.uint8, device="cuda")
+        if train:
+            t["saved"] = torch.empty(saved_b, dtype=torch.uint8, device="cuda")
+            t["dY"] = dev(inp["dY_raw"])
+            for g in ("dQ", "dK", "dV"):
+                t[g] = torch.empty_like(t["Q"])
+        return t
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    def run_step(t):
+        if train:
+            lf.lf_attn_fwd(p, t["Q"], t["K"], t["V"], t["w"], t["Y"], t["saved"], t["ws"], stream)
+            lf.lf_attn_bwd(p, t["Q"], t["K"], t["V"], t["w"], t["saved"], t["dY"], t["dQ"], t["dK"], t["dV"],
+                           t["ws"], stream)
+        else:
+            lf.lf_attn_fwd(p, t["Q"], t["K"], t["V"], t["w"], t["Y"], None, t["ws"], stream)
+
+    def timed(sets, steps, warmup):
+        for i in range(warmup):
+            run_step(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            run_step(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    hot = make_set()
+    Q, K, V, w, Y, ws = hot["Q"], hot["K"], hot["V"], hot["w"], hot["Y"], hot["ws"]
+    elapsed = timed([hot], args.steps, args.warmup)
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = wl.tokens * args.steps / elapsed
+
+    cold = None
+    if not args.no_cold:
+        set_bytes = sum(x.numel() * x.element_size() for x in hot.values())
+        nsets = max(2, -(-COLD_BYTES // set_bytes))
+        sets = [hot] + [make_set() for _ in range(nsets - 1)]
+        el = timed(sets, max(args.steps, 2 * nsets), 2 * nsets)
+        nsteps = max(args.steps, 2 * nsets)
+        cold = {"value": wl.tokens * nsteps / el, "ms_per_step": el / nsteps * 1e3, "sets": nsets,
+                "bytes_per_set": set_bytes}
+        del sets
 
     # Dominant kernel: laplace_l1_exp, through its own entry point on the same stream, bracketed by HIP events.
     G, N, m, d = p.G, p.N, p.m, p.d
@@ -270,7 +316,7 @@ def main():
     time_stage("out_gemm_dwc", lambda: lf.lf_out_gemm_dwc(p, CQ, P, None, V, w, Y, stream))
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC_TRAIN if train else METRIC,
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -282,7 +328,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if wl.dtype == WL.F32 else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name} forward", "B": wl.B, "heads": wl.heads, "H": wl.H, "W": wl.W, "d": wl.d,
+        "config": {"workload": f"{wl.name} {'forward+backward' if train else 'forward'}", "B": wl.B, "heads": wl.heads, "H": wl.H, "W": wl.W, "d": wl.d,
                    "r": wl.r, "m": wl.m, "lambda": wl.lam, "eps": wl.eps, "ns_iters": wl.ns_iters,
                    "tokens_per_step": wl.tokens},
         "roofline": {"kernel": "laplace_l1_exp", "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TFLOPS,
@@ -291,6 +337,8 @@ def main():
                      "avg_us": lap_us, "ops_per_launch": ops},
         "stages_us": stages,
     }
+    if cold is not None:
+        rec["cold"] = cold
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

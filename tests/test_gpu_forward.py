@@ -116,6 +116,26 @@ def test_stage_pool_and_laplace(wl):
         assert relF(host(We).reshape(G, m, m)[g], Wref) <= 1e-5
 
 
+@pytest.mark.parametrize("wl", [WL.TINY, WL.TINY.replace(name="m25_10x10", H=10, W=10, r=2, B=2),
+                                WL.PVT_S1.replace(name="s1_B2", B=2), EDGE[1], EDGE[8]],
+                         ids=lambda w: w.name)
+def test_forward_newton_schulz_iterates(wl):
+    """Every Newton-Schulz iterate the fused forward saves tracks the oracle's iterates on the same W (a case with
+    20 iterations included, where rounding that the iteration does not damp would show), and W = k(L, L) + eps I
+    and the result come out symmetric."""
+    note(f"[gpu] forward NS iterates {wl.name}")
+    Y, sv, p = gpu_forward(wl, dwc=True, save=True)
+    G, m, K = p.G, p.m, p.ns_iters
+    We = host(sv["We"]).reshape(G, m, m)
+    xs = host(sv["xs"]).reshape(G, K + 1, m, m)
+    for g in range(G):
+        assert np.array_equal(We[g], We[g].T)  # the distance kernel's W is bitwise symmetric
+        _, xs_ref, _ = O.newton_schulz(We[g].astype(np.float64), K)
+        for k in range(K + 1):
+            assert relF(xs[g, k], xs_ref[k]) <= tol(wl), (g, k)
+        assert relF(xs[g, K], xs[g, K].T) <= 1e-5
+
+
 @pytest.mark.parametrize("wl", [WL.TINY, WL.TINY_R1, WL.PVT_S1, WL.PVT_S3, WL.HIRES_BF16, EDGE[2]],
                          ids=lambda w: w.name)
 def test_stage_newton_schulz(wl):
