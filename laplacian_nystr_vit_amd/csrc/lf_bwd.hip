@@ -133,121 +133,155 @@ __global__ __launch_bounds__(256) void k_bwd_small1(const float* __restrict__ T1
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// Newton-Schulz reverse chain on fp32 MFMA, one block per slice, everything in LDS (64 x 64 padded).
+// Newton-Schulz reverse chain on fp32 MFMA, one block of 12 waves per slice, everything in LDS (64 x 64, zero
+// padded: every buffer starts at zero and only ever receives products of zero-padded operands, so all 16 k-steps
+// run fully unrolled). Per step k (from K - 1 down to 0), with G the current adjoint:
+//   phase 1: A1 = W X_k, A2 = X_k W, Z = X_k^T G           (12 waves = 3 products x 4 row strips)
+//   phase 2: dW -= Z X_k^T                                (waves 0-3, one row strip each)
+//            G <- 2G - (G A1^T + A2^T G)                  (waves 4-11, half a row strip each)
+// so every wave issues the same 64 MFMAs per phase. X_{k-1} is loaded into registers during step k.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int BL = 66;
+constexpr int NSB_WAVES = 12;
 
-template <bool TA, bool TB>
-__device__ __forceinline__ void mm64(const float* __restrict__ sA, const float* __restrict__ sB, int ksteps, int wv,
-                                     int ln, int ntile, f32x4 acc[4]) {
-  const int i = wv * 16 + (ln & 15);
-  for (int ks = 0; ks < ksteps; ++ks) {
+// acc[t] += op(A)[strip rows][:] op(B)[:][tile t0 + t] over k = 0..63, with op = transpose when TA / TB.
+template <bool TA, bool TB, int NT>
+__device__ __forceinline__ void mm64u(const float* __restrict__ sA, const float* __restrict__ sB, int strip, int t0,
+                                      int ln, f32x4 acc[NT]) {
+  const int i = strip * 16 + (ln & 15);
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
     const int k = ks * 4 + (ln >> 4);
     const float a = TA ? sA[k * BL + i] : sA[i * BL + k];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t < ntile) {
-        const int j = t * 16 + (ln & 15);
-        const float b = TB ? sB[j * BL + k] : sB[k * BL + j];
-        acc[t] = mfma16x16x4(a, b, acc[t]);
-      }
+    for (int t = 0; t < NT; ++t) {
+      const int j = (t0 + t) * 16 + (ln & 15);
+      const float b = TB ? sB[j * BL + k] : sB[k * BL + j];
+      acc[t] = mfma16x16x4(a, b, acc[t]);
     }
   }
 }
 
-__device__ __forceinline__ void zero4(f32x4 acc[4]) {
+template <int NT>
+__device__ __forceinline__ void zero_n(f32x4 acc[NT]) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-__device__ __forceinline__ void store4(float* __restrict__ sC, const f32x4 acc[4], int wv, int ln, int ntile) {
+// Row strip `strip`, tiles t0 .. t0 + NT - 1 of a 64 x 64 LDS matrix from accumulator tiles.
+template <int NT>
+__device__ __forceinline__ void store_tiles(float* __restrict__ sC, const f32x4 acc[NT], int strip, int t0, int ln) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (t < ntile) {
-      const int j = t * 16 + (ln & 15);
+  for (int t = 0; t < NT; ++t) {
+    const int j = (t0 + t) * 16 + (ln & 15);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sC[(wv * 16 + 4 * (ln >> 4) + r) * BL + j] = acc[t][r];
-    }
+    for (int r = 0; r < 4; ++r) sC[(strip * 16 + 4 * (ln >> 4) + r) * BL + j] = acc[t][r];
   }
 }
 
-__global__ __launch_bounds__(256) void k_bwd_ns(const float* __restrict__ We, const float* __restrict__ xs,
-                                                const float* __restrict__ alpha, const float* __restrict__ dX,
-                                                float* __restrict__ dWe, int m, int K) {
+__global__ __launch_bounds__(64 * NSB_WAVES) void k_bwd_ns(const float* __restrict__ We,
+                                                            const float* __restrict__ xs,
+                                                            const float* __restrict__ alpha,
+                                                            const float* __restrict__ dX, float* __restrict__ dWe,
+                                                            int m, int K) {
+  constexpr int NT = 64 * NSB_WAVES;
+  constexpr int PER = (64 * 64 + NT - 1) / NT;  // matrix elements per thread when staging
   __shared__ float sW[64 * BL];
   __shared__ float sXk[64 * BL];
   __shared__ float sG[2][64 * BL];
   __shared__ float sA1[64 * BL];
   __shared__ float sA2[64 * BL];
   __shared__ float sZ[64 * BL];
-  const int g = blockIdx.x, tid = threadIdx.x, wv = wave_id(), ln = lane_id();
+  const int g = blockIdx.x, tid = threadIdx.x, ln = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
   const size_t mm = static_cast<size_t>(m) * m;
-  for (int idx = tid; idx < 64 * 64; idx += 256) {
+  for (int idx = tid; idx < 64 * BL; idx += NT) {
+    sA1[idx] = 0.f;
+    sA2[idx] = 0.f;
+    sZ[idx] = 0.f;
+    sG[1][idx] = 0.f;
+  }
+  for (int idx = tid; idx < 64 * 64; idx += NT) {
     const int i = idx >> 6, j = idx & 63;
     const bool in = i < m && j < m;
     sW[i * BL + j] = in ? We[g * mm + i * m + j] : 0.f;
     sG[0][i * BL + j] = in ? dX[g * mm + i * m + j] : 0.f;
   }
-  const int ksteps = (m + 3) / 4, ntile = (m + 15) / 16;
-  const bool active = wv < ntile;
-  f32x4 dacc[4], acc[4];
-  zero4(dacc);
+  // X_{K-1} into registers; each step stores the iterate it holds and loads the next one
+  float xr[PER];
+  auto load_x = [&](int k) {
+    const float* xk = xs + (static_cast<size_t>(g) * (K + 1) + k) * mm;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = tid + NT * q;
+      const int i = idx >> 6, j = idx & 63;
+      xr[q] = (idx < 4096 && i < m && j < m) ? xk[i * m + j] : 0.f;
+    }
+  };
+  if (K > 0) load_x(K - 1);
+  f32x4 dacc[4];
+  zero_n<4>(dacc);
   int cur = 0;
   for (int k = K - 1; k >= 0; --k) {
-    const float* xk = xs + (static_cast<size_t>(g) * (K + 1) + k) * mm;
-    __syncthreads();
-    for (int idx = tid; idx < 64 * 64; idx += 256) {
-      const int i = idx >> 6, j = idx & 63;
-      sXk[i * BL + j] = (i < m && j < m) ? xk[i * m + j] : 0.f;
+    __syncthreads();  // previous step's reads of sXk are done
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = tid + NT * q;
+      if (idx < 4096) sXk[(idx >> 6) * BL + (idx & 63)] = xr[q];
     }
+    if (k > 0) load_x(k - 1);
     __syncthreads();
-    if (active) {
-      zero4(acc);
-      mm64<false, false>(sW, sXk, ksteps, wv, ln, ntile, acc);  // A1 = W X_k
-      store4(sA1, acc, wv, ln, ntile);
-      zero4(acc);
-      mm64<false, false>(sXk, sW, ksteps, wv, ln, ntile, acc);  // A2 = X_k W
-      store4(sA2, acc, wv, ln, ntile);
-      zero4(acc);
-      mm64<true, false>(sXk, sG[cur], ksteps, wv, ln, ntile, acc);  // Z = X_k^T G
-      store4(sZ, acc, wv, ln, ntile);
+    {
+      const int prod = wv >> 2, strip = wv & 3;
+      f32x4 acc[4];
+      zero_n<4>(acc);
+      if (prod == 0) {
+        mm64u<false, false, 4>(sW, sXk, strip, 0, ln, acc);  // A1 = W X_k
+        store_tiles<4>(sA1, acc, strip, 0, ln);
+      } else if (prod == 1) {
+        mm64u<false, false, 4>(sXk, sW, strip, 0, ln, acc);  // A2 = X_k W
+        store_tiles<4>(sA2, acc, strip, 0, ln);
+      } else {
+        mm64u<true, false, 4>(sXk, sG[cur], strip, 0, ln, acc);  // Z = X_k^T G
+        store_tiles<4>(sZ, acc, strip, 0, ln);
+      }
     }
     __syncthreads();
     const int nxt = cur ^ 1;
-    if (active) {
-      zero4(acc);
-      mm64<false, true>(sZ, sXk, ksteps, wv, ln, ntile, acc);  // Z X_k^T
+    if (wv < 4) {
+      f32x4 acc[4];
+      zero_n<4>(acc);
+      mm64u<false, true, 4>(sZ, sXk, wv, 0, ln, acc);  // Z X_k^T
 #pragma unroll
       for (int t = 0; t < 4; ++t) dacc[t] -= acc[t];
-      zero4(acc);
-      mm64<false, true>(sG[cur], sA1, ksteps, wv, ln, ntile, acc);  // G A1^T
-      mm64<true, false>(sA2, sG[cur], ksteps, wv, ln, ntile, acc);  // + A2^T G
+    } else {
+      const int strip = (wv - 4) & 3, t0 = 2 * ((wv - 4) >> 2);
+      f32x4 acc[2];
+      zero_n<2>(acc);
+      mm64u<false, true, 2>(sG[cur], sA1, strip, t0, ln, acc);  // G A1^T
+      mm64u<true, false, 2>(sA2, sG[cur], strip, t0, ln, acc);  // + A2^T G
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (t < ntile) {
-          const int j = t * 16 + (ln & 15);
+      for (int t = 0; t < 2; ++t) {
+        const int j = (t0 + t) * 16 + (ln & 15);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = wv * 16 + 4 * (ln >> 4) + r;
-            sG[nxt][i * BL + j] = 2.f * sG[cur][i * BL + j] - acc[t][r];
-          }
+        for (int r = 0; r < 4; ++r) {
+          const int i = strip * 16 + 4 * (ln >> 4) + r;
+          sG[nxt][i * BL + j] = 2.f * sG[cur][i * BL + j] - acc[t][r];
         }
       }
     }
     cur = nxt;
   }
   __syncthreads();
-  if (active) {
+  if (wv < 4) {
     const float a = alpha[g];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      if (t < ntile) {
-        const int j = t * 16 + (ln & 15);
+      const int j = t * 16 + (ln & 15);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = wv * 16 + 4 * (ln >> 4) + r;
-          if (i < m && j < m) dWe[g * mm + i * m + j] = dacc[t][r] + a * sG[cur][j * BL + i];
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int i = wv * 16 + 4 * (ln >> 4) + r;
+        if (i < m && j < m) dWe[g * mm + i * m + j] = dacc[t][r] + a * sG[cur][j * BL + i];
       }
     }
   }
@@ -320,7 +354,9 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
     }
   }
   const float* cm = (side == 0 ? CQ : CK) + static_cast<size_t>(g) * m * N;  // landmark-major [m][N]
-  float* out = (side == 0 ? Gq : Gk) + static_cast<size_t>(g) * N * m;
+  // Gq / Gk are written landmark-major too, [m][N]: the dL reduction then reads a landmark's weights for
+  // consecutive tokens as one contiguous run, and the token-row kernel reads them coalesced across its lanes.
+  float* out = (side == 0 ? Gq : Gk) + static_cast<size_t>(g) * m * N;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     if (t >= ntile) continue;
@@ -343,14 +379,16 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
         const float ahat = (c - mu_l) * rs_l;
         v = rs_l * (v - mA - ahat * mAA);
       }
-      out[static_cast<size_t>(i) * m + l] = v * c * inv_lam;
+      out[static_cast<size_t>(l) * N + i] = v * c * inv_lam;
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------------------------
 // dL partials: sum over a range of token rows of Gq sign(Q - L) + Gk sign(K - L). Thread = (landmark, channel);
-// with d = 64 every wave owns one landmark, so the Gq/Gk values it reads are wave-uniform.
+// with d = 64 every wave owns one landmark, so the Gq/Gk weights it reads are wave-uniform: with Gq/Gk stored
+// landmark-major, 16 consecutive rows' weights arrive in one scalar load each, and the 16 rows' token values are
+// independent vector loads, so a group of rows costs one memory round trip instead of one per row.
 // ---------------------------------------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_bwd_dl_partial(const T* __restrict__ Q, const T* __restrict__ K,
@@ -358,6 +396,7 @@ __global__ __launch_bounds__(256) void k_bwd_dl_partial(const T* __restrict__ Q,
                                                         const float* __restrict__ Gk, float* __restrict__ part, int N,
                                                         int m, int nsplit, int rps, int nlb) {
   constexpr int LPB = 256 / D;
+  constexpr int RG = 16;  // rows per group
   int b = blockIdx.x;
   const int lb = b % nlb;
   b /= nlb;
@@ -367,13 +406,30 @@ __global__ __launch_bounds__(256) void k_bwd_dl_partial(const T* __restrict__ Q,
   if (l >= m) return;
   const float lv = L[(static_cast<size_t>(g) * m + l) * D + c];
   const int r0 = s * rps, r1 = min(N, r0 + rps);
-  const size_t base = static_cast<size_t>(g) * N;
+  const float* gq = Gq + (static_cast<size_t>(g) * m + l) * N;
+  const float* gk = Gk + (static_cast<size_t>(g) * m + l) * N;
+  const T* qc = Q + static_cast<size_t>(g) * N * D + c;
+  const T* kc = K + static_cast<size_t>(g) * N * D + c;
   float acc = 0.f;
-  for (int i = r0; i < r1; ++i) {
-    const float gq = Gq[(base + i) * m + l];
-    const float gk = Gk[(base + i) * m + l];
-    acc += gq * sgnf(to_f32(Q[(base + i) * D + c]) - lv);
-    acc += gk * sgnf(to_f32(K[(base + i) * D + c]) - lv);
+  int i = r0;
+  for (; i + RG <= r1; i += RG) {
+    float wq[RG], wk[RG], xq[RG], xk[RG];
+#pragma unroll
+    for (int u = 0; u < RG; ++u) {
+      wq[u] = gq[i + u];
+      wk[u] = gk[i + u];
+      xq[u] = to_f32(qc[static_cast<size_t>(i + u) * D]);
+      xk[u] = to_f32(kc[static_cast<size_t>(i + u) * D]);
+    }
+#pragma unroll
+    for (int u = 0; u < RG; ++u) {
+      acc += wq[u] * sgnf(xq[u] - lv);
+      acc += wk[u] * sgnf(xk[u] - lv);
+    }
+  }
+  for (; i < r1; ++i) {
+    acc += gq[i] * sgnf(to_f32(qc[static_cast<size_t>(i) * D]) - lv);
+    acc += gk[i] * sgnf(to_f32(kc[static_cast<size_t>(i) * D]) - lv);
   }
   part[((static_cast<size_t>(g) * nsplit + s) * m + l) * D + c] = acc;
 }
@@ -401,7 +457,7 @@ __global__ __launch_bounds__(64) void k_bwd_rows(const T* __restrict__ Q, const 
   const int row = blockIdx.x * 64 + static_cast<int>(threadIdx.x);
   if (row >= N) return;
   const T* X = (side == 0 ? Q : K) + (static_cast<size_t>(g) * N + row) * D;
-  const float* gx = (side == 0 ? Gq : Gk) + (static_cast<size_t>(g) * N + row) * m;
+  const float* gx = (side == 0 ? Gq : Gk) + static_cast<size_t>(g) * m * N + row;  // landmark-major: gx[l * N]
   const float* __restrict__ Lg = L + static_cast<size_t>(g) * m * D;
   float x[D], acc[D];
 #pragma unroll
@@ -409,11 +465,25 @@ __global__ __launch_bounds__(64) void k_bwd_rows(const T* __restrict__ Q, const 
     x[c] = to_f32(X[c]);
     acc[c] = 0.f;
   }
-  for (int l = 0; l < m; ++l) {
-    const float gl = gx[l];
-    const float* __restrict__ lp = Lg + static_cast<size_t>(l) * D;
+  // The lane's weights for a chunk of 8 landmarks are loaded together (coalesced across the wave's rows), the
+  // next chunk's while this one is used.
+  constexpr int LC = 8;
+  float gc[LC], gn[LC];
 #pragma unroll
-    for (int c = 0; c < D; ++c) acc[c] = fmaf(-gl, sgnf(x[c] - lp[c]), acc[c]);
+  for (int u = 0; u < LC; ++u) gn[u] = u < m ? gx[static_cast<size_t>(u) * N] : 0.f;
+  for (int l0 = 0; l0 < m; l0 += LC) {
+#pragma unroll
+    for (int u = 0; u < LC; ++u) gc[u] = gn[u];
+#pragma unroll
+    for (int u = 0; u < LC; ++u) gn[u] = (l0 + LC + u < m) ? gx[static_cast<size_t>(l0 + LC + u) * N] : 0.f;
+#pragma unroll
+    for (int u = 0; u < LC; ++u) {
+      if (l0 + u < m) {
+        const float* __restrict__ lp = Lg + static_cast<size_t>(l0 + u) * D;
+#pragma unroll
+        for (int c = 0; c < D; ++c) acc[c] = fmaf(-gc[u], sgnf(x[c] - lp[c]), acc[c]);
+      }
+    }
   }
   if (side == 0) {
     const int yy = row / W, xx = row % W;
@@ -464,7 +534,8 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bwd_small1<D>, dim3(s.G), dim3(256), 0, st, T1, sp.S, sp.P, sp.xs, sp.mu, sp.rstd, dX, dS,
                      stats, s.m, s.ns_iters, s.N, wh);
-  hipLaunchKernelGGL(k_bwd_ns, dim3(s.G), dim3(256), 0, st, sp.We, sp.xs, sp.alpha, dX, dWe, s.m, s.ns_iters);
+  hipLaunchKernelGGL(k_bwd_ns, dim3(s.G), dim3(64 * NSB_WAVES), 0, st, sp.We, sp.xs, sp.alpha, dX, dWe, s.m,
+                     s.ns_iters);
   hipLaunchKernelGGL(k_bwd_wpart, dim3(cdiv(static_cast<long>(s.m) * D, 256), s.G), dim3(256), 0, st, sp.L, sp.We,
                      dWe, dLW, s.m, D, inv_lam);
   hipLaunchKernelGGL((k_bwd_rowgrad<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(256), 0, st, dY, V, sp.P, dS, sp.CQ,
