@@ -76,7 +76,8 @@ BwdWs plan(const Shape& s) {
 
 // ---------------------------------------------------------------------------------------------------------
 // Small per-slice products: dP from T1 = [C_Q | 1]^T dY, then dX = dP S^T, dS = X_K^T dP and the two whitening
-// column means. m x m x d work per slice, on the VALU.
+// column means. m x m x d work per slice, on the VALU. The slice's output rows are spread over gridDim.y blocks
+// (rows l = blockIdx.y, blockIdx.y + gridDim.y, ...); each block forms the whole dP, which every dS row needs.
 // ---------------------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_small1(const float* __restrict__ T1, const float* __restrict__ S,
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void k_bwd_small1(const float* __restrict__ T1
   __shared__ float sP[64 * D];
   __shared__ float sdP[64 * D];
   __shared__ float sX[64 * 64];
-  const int g = blockIdx.x, tid = threadIdx.x;
+  const int g = blockIdx.x, part = blockIdx.y, nparts = gridDim.y, tid = threadIdx.x;
   const size_t md = static_cast<size_t>(m) * D, mm = static_cast<size_t>(m) * m;
   const float* t1 = T1 + static_cast<size_t>(g) * (m + 1) * D;
   for (int idx = tid; idx < (m + 1) * D; idx += 256) sT1[idx] = t1[idx];
@@ -107,20 +108,24 @@ __global__ __launch_bounds__(256) void k_bwd_small1(const float* __restrict__ T1
     sdP[idx] = v;
   }
   __syncthreads();
-  for (int idx = tid; idx < m * m; idx += 256) {
-    const int l = idx / m, k = idx % m;
+  const int rows = (m - part + nparts - 1) / nparts;  // this block's rows: l = part + nparts q, q < rows
+  for (int idx = tid; idx < rows * m; idx += 256) {
+    const int l = part + nparts * (idx / m), k = idx % m;
     float acc = 0.f;
+#pragma unroll 8
     for (int c = 0; c < D; ++c) acc += sdP[l * D + c] * sS[k * D + c];
-    dX[g * mm + idx] = acc;
+    dX[g * mm + static_cast<size_t>(l) * m + k] = acc;
   }
-  for (int idx = tid; idx < m * D; idx += 256) {
-    const int l = idx / D, c = idx % D;
+  for (int idx = tid; idx < rows * D; idx += 256) {
+    const int l = part + nparts * (idx / D), c = idx % D;
     float acc = 0.f;
+#pragma unroll 7
     for (int k = 0; k < m; ++k) acc += sX[k * m + l] * sdP[k * D + c];
-    dS[g * md + idx] = acc;
+    dS[g * md + static_cast<size_t>(l) * D + c] = acc;
   }
   if (whiten) {
-    for (int l = tid; l < m; l += 256) {
+    for (int q = tid; q < rows; q += 256) {
+      const int l = part + nparts * q;
       float a = 0.f, b = 0.f;
       for (int c = 0; c < D; ++c) {
         a += sT1[m * D + c] * sP[l * D + c];
@@ -303,10 +308,13 @@ __global__ __launch_bounds__(256) void k_bwd_wpart(const float* __restrict__ L, 
   const float* dw = dWe + g * mm;
   const float ll = Lg[t];
   float acc = 0.f;
+  // unrolled, with the diagonal term selected away instead of skipped, so that the loads of several landmarks
+  // are in flight together
+#pragma unroll 7
   for (int l2 = 0; l2 < m; ++l2) {
-    if (l2 == l) continue;
     const float gw = (dw[l * m + l2] * wg[l * m + l2] + dw[l2 * m + l] * wg[l2 * m + l]) * inv_lam;
-    acc -= gw * sgnf(ll - Lg[l2 * D + c]);
+    const float term = gw * sgnf(ll - Lg[l2 * D + c]);
+    acc -= (l2 == l) ? 0.f : term;
   }
   dLW[static_cast<size_t>(g) * m * D + t] = acc;
 }
@@ -446,27 +454,32 @@ __global__ __launch_bounds__(256) void k_bwd_dl_finalize(const float* __restrict
 
 // ---------------------------------------------------------------------------------------------------------
 // Token rows: dQ_i = -sum_l Gq[i][l] sign(Q_i - L_l) + dL_owner(i) / r^2 ; dK_j = -sum_l Gk[j][l] sign(K_j - L_l).
-// One thread per row, row and accumulator in VGPRs; the landmark row is wave-uniform (scalar loads).
+// Block = 64 rows x all channels of one side; wave w owns channels [w CW, (w + 1) CW) of the 64 rows (lane = row),
+// keeping that slice of the row and of its accumulator in VGPRs. The landmark values of the wave's channels are
+// wave-uniform (one scalar load per landmark), the weights Gx[l][row] coalesced vector loads, fetched a chunk of
+// landmarks ahead.
 // ---------------------------------------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(64) void k_bwd_rows(const T* __restrict__ Q, const T* __restrict__ K,
-                                                 const float* __restrict__ L, const float* __restrict__ Gq,
-                                                 const float* __restrict__ Gk, const float* __restrict__ dL,
-                                                 T* __restrict__ dQ, T* __restrict__ dK, int N, int m, int W, int r) {
+__global__ __launch_bounds__(256) void k_bwd_rows(const T* __restrict__ Q, const T* __restrict__ K,
+                                                  const float* __restrict__ L, const float* __restrict__ Gq,
+                                                  const float* __restrict__ Gk, const float* __restrict__ dL,
+                                                  T* __restrict__ dQ, T* __restrict__ dK, int N, int m, int W, int r) {
+  constexpr int NWB = D >= 64 ? 4 : D / 16;  // waves per block
+  constexpr int CW = D / NWB;                 // channels per wave (16)
   const int side = blockIdx.z, g = blockIdx.y;
-  const int row = blockIdx.x * 64 + static_cast<int>(threadIdx.x);
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
+  const int row = blockIdx.x * 64 + lane_id();
   if (row >= N) return;
-  const T* X = (side == 0 ? Q : K) + (static_cast<size_t>(g) * N + row) * D;
+  const int c0 = wv * CW;
+  const T* X = (side == 0 ? Q : K) + (static_cast<size_t>(g) * N + row) * D + c0;
   const float* gx = (side == 0 ? Gq : Gk) + static_cast<size_t>(g) * m * N + row;  // landmark-major: gx[l * N]
-  const float* __restrict__ Lg = L + static_cast<size_t>(g) * m * D;
-  float x[D], acc[D];
+  const float* __restrict__ Lg = L + static_cast<size_t>(g) * m * D + c0;
+  float x[CW], acc[CW];
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
+  for (int c = 0; c < CW; ++c) {
     x[c] = to_f32(X[c]);
     acc[c] = 0.f;
   }
-  // The lane's weights for a chunk of 8 landmarks are loaded together (coalesced across the wave's rows), the
-  // next chunk's while this one is used.
   constexpr int LC = 8;
   float gc[LC], gn[LC];
 #pragma unroll
@@ -481,7 +494,7 @@ __global__ __launch_bounds__(64) void k_bwd_rows(const T* __restrict__ Q, const 
       if (l0 + u < m) {
         const float* __restrict__ lp = Lg + static_cast<size_t>(l0 + u) * D;
 #pragma unroll
-        for (int c = 0; c < D; ++c) acc[c] = fmaf(-gc[u], sgnf(x[c] - lp[c]), acc[c]);
+        for (int c = 0; c < CW; ++c) acc[c] = fmaf(-gc[u], sgnf(x[c] - lp[c]), acc[c]);
       }
     }
   }
@@ -489,13 +502,13 @@ __global__ __launch_bounds__(64) void k_bwd_rows(const T* __restrict__ Q, const 
     const int yy = row / W, xx = row % W;
     const int owner = (yy / r) * (W / r) + xx / r;
     const float inv = 1.f / static_cast<float>(r * r);
-    const float* dl = dL + (static_cast<size_t>(g) * m + owner) * D;
+    const float* dl = dL + (static_cast<size_t>(g) * m + owner) * D + c0;
 #pragma unroll
-    for (int c = 0; c < D; ++c) acc[c] += dl[c] * inv;
+    for (int c = 0; c < CW; ++c) acc[c] += dl[c] * inv;
   }
-  T* out = (side == 0 ? dQ : dK) + (static_cast<size_t>(g) * N + row) * D;
+  T* out = (side == 0 ? dQ : dK) + (static_cast<size_t>(g) * N + row) * D + c0;
 #pragma unroll
-  for (int c = 0; c < D; ++c) out[c] = from_f32<T>(acc[c]);
+  for (int c = 0; c < CW; ++c) out[c] = from_f32<T>(acc[c]);
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -532,8 +545,8 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
 
   hipError_t e = launch_ckv_general(s, sp.CQ, 1, dY, part, T1, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bwd_small1<D>, dim3(s.G), dim3(256), 0, st, T1, sp.S, sp.P, sp.xs, sp.mu, sp.rstd, dX, dS,
-                     stats, s.m, s.ns_iters, s.N, wh);
+  hipLaunchKernelGGL(k_bwd_small1<D>, dim3(s.G, s.m < 8 ? s.m : 8), dim3(256), 0, st, T1, sp.S, sp.P, sp.xs, sp.mu,
+                     sp.rstd, dX, dS, stats, s.m, s.ns_iters, s.N, wh);
   hipLaunchKernelGGL(k_bwd_ns, dim3(s.G), dim3(64 * NSB_WAVES), 0, st, sp.We, sp.xs, sp.alpha, dX, dWe, s.m,
                      s.ns_iters);
   hipLaunchKernelGGL(k_bwd_wpart, dim3(cdiv(static_cast<long>(s.m) * D, 256), s.G), dim3(256), 0, st, sp.L, sp.We,
@@ -547,8 +560,8 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
   const int md = s.m * D;
   hipLaunchKernelGGL(k_bwd_dl_finalize, dim3(cdiv(static_cast<long>(s.G) * md, 256)), dim3(256), 0, st, dLpart, dLW,
                      dL, s.G, p.nsplitL, md);
-  hipLaunchKernelGGL((k_bwd_rows<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(64), 0, st, Q, K, sp.L, Gq, Gk, dL, dQ, dK,
-                     s.N, s.m, s.W, s.r);
+  hipLaunchKernelGGL((k_bwd_rows<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(64 * (D >= 64 ? 4 : D / 16)), 0, st, Q,
+                     K, sp.L, Gq, Gk, dL, dQ, dK, s.N, s.m, s.W, s.r);
   return hipGetLastError();
 }
 
