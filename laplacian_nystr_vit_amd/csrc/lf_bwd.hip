@@ -26,6 +26,8 @@ namespace lf {
 
 static inline int cdiv(long a, long b) { return static_cast<int>((a + b - 1) / b); }
 
+constexpr int kDlLw = 8;  // landmarks per thread in the dL reduction
+
 __device__ __forceinline__ float sgnf(float x) { return x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f); }
 
 namespace {
@@ -43,13 +45,14 @@ BwdWs plan(const Shape& s) {
   int nsplit, rps;
   ckv_split(s, &nsplit, &rps);
   BwdWs w;
-  const int lpb = 256 / s.d;
-  w.nlb = cdiv(s.m, lpb);
-  int want = cdiv(512, static_cast<long>(s.G) * w.nlb);
-  const int maxs = cdiv(s.N, 64);
+  // dL partials: blocks of 256 / d landmark groups of kDlLw landmarks; the row range is split so that about 2048
+  // waves run, each split a multiple of 4 rows.
+  w.nlb = cdiv(s.m, (256 / s.d) * kDlLw);
+  int want = cdiv(2048, static_cast<long>(s.G) * w.nlb * 4);
+  const int maxs = cdiv(s.N, 16);
   if (want > maxs) want = maxs;
   if (want < 1) want = 1;
-  w.rpsL = cdiv(s.N, want);
+  w.rpsL = cdiv(cdiv(s.N, want), 4) * 4;
   w.nsplitL = cdiv(s.N, w.rpsL);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
   __shared__ float sA[64 * LDA];
   __shared__ float sB[D * LDB];
   const int side = blockIdx.z, g = blockIdx.y, i0 = blockIdx.x * 64;
-  const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
   const T* A = (side == 0 ? dY : V) + static_cast<size_t>(g) * N * D;
   const float* Bm = (side == 0 ? P : dS) + static_cast<size_t>(g) * m * D;
   for (int idx = tid; idx < 64 * D; idx += 256) {
@@ -349,25 +352,27 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
     sB[c * LDB + l] = (l < m) ? Bm[static_cast<size_t>(l) * D + c] : 0.f;
   }
   __syncthreads();
-  const int ntile = (m + 15) / 16;
+  // all 4 landmark tiles: the B columns past m are staged as zeros
   f32x4 acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
   for (int ks = 0; ks < D / 4; ++ks) {
     const int k = ks * 4 + (ln >> 4);
     const float a = sA[(wv * 16 + (ln & 15)) * LDA + k];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t < ntile) acc[t] = mfma16x16x4(a, sB[k * LDB + t * 16 + (ln & 15)], acc[t]);
-    }
+    for (int t = 0; t < 4; ++t) acc[t] = mfma16x16x4(a, sB[k * LDB + t * 16 + (ln & 15)], acc[t]);
   }
   const float* cm = (side == 0 ? CQ : CK) + static_cast<size_t>(g) * m * N;  // landmark-major [m][N]
   // Gq / Gk are written landmark-major too, [m][N]: the dL reduction then reads a landmark's weights for
   // consecutive tokens as one contiguous run, and the token-row kernel reads them coalesced across its lanes.
   float* out = (side == 0 ? Gq : Gk) + static_cast<size_t>(g) * m * N;
+  // the lane's 4 values are 4 consecutive tokens of one landmark: one 16-byte load of C and store of G each when
+  // they are all in range and N keeps them aligned
+  const int ib = i0 + wv * 16 + 4 * (ln >> 4);
+  const bool vec = (N & 3) == 0 && ib + 3 < N;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    if (t >= ntile) continue;
     const int l = t * 16 + (ln & 15);
     if (l >= m) continue;
     float mu_l = 0.f, rs_l = 1.f, mA = 0.f, mAA = 0.f;
@@ -377,69 +382,98 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
       mA = stats[static_cast<size_t>(g) * 2 * m + l];
       mAA = stats[static_cast<size_t>(g) * 2 * m + m + l];
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + wv * 16 + 4 * (ln >> 4) + r;
-      if (i >= N) continue;
-      const float c = cm[static_cast<size_t>(l) * N + i];
-      float v = acc[t][r];
+    auto grad = [&](float v, float c) {
       if (side == 0 && whiten) {
         const float ahat = (c - mu_l) * rs_l;
         v = rs_l * (v - mA - ahat * mAA);
       }
-      out[static_cast<size_t>(l) * N + i] = v * c * inv_lam;
+      return v * c * inv_lam;
+    };
+    if (vec) {
+      const float4 c4 = *reinterpret_cast<const float4*>(cm + static_cast<size_t>(l) * N + ib);
+      const float4 o = make_float4(grad(acc[t][0], c4.x), grad(acc[t][1], c4.y), grad(acc[t][2], c4.z),
+                                   grad(acc[t][3], c4.w));
+      *reinterpret_cast<float4*>(out + static_cast<size_t>(l) * N + ib) = o;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = ib + r;
+        if (i < N) out[static_cast<size_t>(l) * N + i] = grad(acc[t][r], cm[static_cast<size_t>(l) * N + i]);
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// dL partials: sum over a range of token rows of Gq sign(Q - L) + Gk sign(K - L). Thread = (landmark, channel);
-// with d = 64 every wave owns one landmark, so the Gq/Gk weights it reads are wave-uniform: with Gq/Gk stored
-// landmark-major, 16 consecutive rows' weights arrive in one scalar load each, and the 16 rows' token values are
-// independent vector loads, so a group of rows costs one memory round trip instead of one per row.
+// dL partials: sum over a range of token rows of Gq sign(Q - L) + Gk sign(K - L). Thread = (channel, group of
+// kDlLw landmarks), accumulators and landmark values in VGPRs, so each token value read serves kDlLw landmarks.
+// With d = 64 a wave is one landmark group and its Gq/Gk weights are wave-uniform (scalar loads of 4 consecutive
+// rows per landmark, Gq/Gk being landmark-major); rows go 4 at a time with all their loads issued together.
 // ---------------------------------------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_bwd_dl_partial(const T* __restrict__ Q, const T* __restrict__ K,
                                                         const float* __restrict__ L, const float* __restrict__ Gq,
                                                         const float* __restrict__ Gk, float* __restrict__ part, int N,
                                                         int m, int nsplit, int rps, int nlb) {
-  constexpr int LPB = 256 / D;
-  constexpr int RG = 16;  // rows per group
+  constexpr int LPB = 256 / D;  // landmark groups per block
+  constexpr int LW = kDlLw;
+  constexpr int RG = 4;  // rows per step
   int b = blockIdx.x;
   const int lb = b % nlb;
   b /= nlb;
   const int s = b % nsplit, g = b / nsplit;
-  const int ll = threadIdx.x / D, c = threadIdx.x % D;
-  const int l = lb * LPB + ll;
-  if (l >= m) return;
-  const float lv = L[(static_cast<size_t>(g) * m + l) * D + c];
+  const int c = threadIdx.x % D;
+  int grp = static_cast<int>(threadIdx.x) / D;
+  if constexpr (D == 64) grp = __builtin_amdgcn_readfirstlane(grp);  // one group per wave: let the compiler know
+  const int lbase = (lb * LPB + grp) * LW;
+  if (lbase >= m) return;
+  // landmarks past m repeat the last landmark's loads (branch-free) and are not stored
+  float lv[LW], acc[LW], wsel[LW];
+  const float* gq[LW];
+  const float* gk[LW];
+#pragma unroll
+  for (int j = 0; j < LW; ++j) {
+    const int l = min(lbase + j, m - 1);
+    lv[j] = L[(static_cast<size_t>(g) * m + l) * D + c];
+    wsel[j] = lbase + j < m ? 1.f : 0.f;
+    gq[j] = Gq + (static_cast<size_t>(g) * m + l) * N;
+    gk[j] = Gk + (static_cast<size_t>(g) * m + l) * N;
+    acc[j] = 0.f;
+  }
   const int r0 = s * rps, r1 = min(N, r0 + rps);
-  const float* gq = Gq + (static_cast<size_t>(g) * m + l) * N;
-  const float* gk = Gk + (static_cast<size_t>(g) * m + l) * N;
   const T* qc = Q + static_cast<size_t>(g) * N * D + c;
   const T* kc = K + static_cast<size_t>(g) * N * D + c;
-  float acc = 0.f;
   int i = r0;
   for (; i + RG <= r1; i += RG) {
-    float wq[RG], wk[RG], xq[RG], xk[RG];
+    float xq[RG], xk[RG], wq[LW][RG], wk[LW][RG];
 #pragma unroll
     for (int u = 0; u < RG; ++u) {
-      wq[u] = gq[i + u];
-      wk[u] = gk[i + u];
       xq[u] = to_f32(qc[static_cast<size_t>(i + u) * D]);
       xk[u] = to_f32(kc[static_cast<size_t>(i + u) * D]);
     }
 #pragma unroll
-    for (int u = 0; u < RG; ++u) {
-      acc += wq[u] * sgnf(xq[u] - lv);
-      acc += wk[u] * sgnf(xk[u] - lv);
-    }
+    for (int j = 0; j < LW; ++j)
+#pragma unroll
+      for (int u = 0; u < RG; ++u) {
+        wq[j][u] = gq[j][i + u];
+        wk[j][u] = gk[j][i + u];
+      }
+#pragma unroll
+    for (int j = 0; j < LW; ++j)
+#pragma unroll
+      for (int u = 0; u < RG; ++u) {
+        acc[j] += wq[j][u] * sgnf(xq[u] - lv[j]);
+        acc[j] += wk[j][u] * sgnf(xk[u] - lv[j]);
+      }
   }
   for (; i < r1; ++i) {
-    acc += gq[i] * sgnf(to_f32(qc[static_cast<size_t>(i) * D]) - lv);
-    acc += gk[i] * sgnf(to_f32(kc[static_cast<size_t>(i) * D]) - lv);
+    const float xq = to_f32(qc[static_cast<size_t>(i) * D]), xk = to_f32(kc[static_cast<size_t>(i) * D]);
+#pragma unroll
+    for (int j = 0; j < LW; ++j) acc[j] += gq[j][i] * sgnf(xq - lv[j]) + gk[j][i] * sgnf(xk - lv[j]);
   }
-  part[((static_cast<size_t>(g) * nsplit + s) * m + l) * D + c] = acc;
+#pragma unroll
+  for (int j = 0; j < LW; ++j)
+    if (wsel[j] != 0.f) part[((static_cast<size_t>(g) * nsplit + s) * m + lbase + j) * D + c] = acc[j];
 }
 
 __global__ __launch_bounds__(256) void k_bwd_dl_finalize(const float* __restrict__ part, const float* __restrict__ dLW,
@@ -448,6 +482,7 @@ __global__ __launch_bounds__(256) void k_bwd_dl_finalize(const float* __restrict
   if (t >= static_cast<size_t>(G) * md) return;
   const size_t g = t / md, e = t % md;
   float acc = 0.f;
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) acc += part[(g * nsplit + s) * md + e];
   dL[t] = acc + dLW[t];
 }
