@@ -38,7 +38,9 @@ Readings where the pages are silent, ambiguous or wrong (each one is listed in t
       satisfies 0 < alpha*mu^2 <= 1 for every eigenvalue mu.
   R4  dk/dx = -(1/lambda) sign(x - y) k (the page drops the minus sign); dk/dy = +(1/lambda) sign(x - y) k.
   R5  sign(0) = 0.
-  R6  alpha is treated as a constant in the backward pass.
+  R6  alpha is treated as a constant in the backward pass, unless the exact gradient through alpha is asked for:
+      then the adjoint of X_0 also flows through alpha = 1/(max column sum * max row sum) of |W_eps|, whose
+      derivative is taken at the first maximising column and row (the maximum is a kink only at ties).
   R7  whitening: columns of C_Q only, statistics per slice over its N tokens, biased variance, no row
       centring and no +1/N term.
   R8  no row normalisation and no 1/sqrt(d) scale; lambda is the only scale.
@@ -161,6 +163,21 @@ def dwc(v: np.ndarray, w: np.ndarray, H: int, W: int) -> np.ndarray:
     return out.reshape(N, d)
 
 
+def dwc_weight_grad(v: np.ndarray, dy: np.ndarray, H: int, W: int) -> np.ndarray:
+    """Gradient of <dy, dwc(v, w)> with respect to w: the DWC is linear in w and its tap (a, b) of channel c
+    multiplies v[(y+a-1, x+b-1), c] into out[(y,x), c], so the gradient is the sum over the grid of
+    dy[(y,x), c] * v[(y+a-1, x+b-1), c] (zero outside the grid). Returns [d, 3, 3]."""
+    N, d = v.shape
+    grid = np.zeros((H + 2, W + 2, d))
+    grid[1:H + 1, 1:W + 1] = v.reshape(H, W, d)
+    g = dy.reshape(H, W, d)
+    out = np.zeros((d, 3, 3))
+    for a in range(3):
+        for b in range(3):
+            out[:, a, b] = np.sum(g * grid[a:a + H, b:b + W], axis=(0, 1))
+    return out
+
+
 def dwc_adjoint(u: np.ndarray, w: np.ndarray, H: int, W: int) -> np.ndarray:
     """Adjoint of `dwc` in V: out[(y,x), c] = sum_{a,b} w[c, a+1, b+1] * u[(y-a, x-b), c] (zero outside)."""
     N, d = u.shape
@@ -202,11 +219,13 @@ def _sign(x: np.ndarray) -> np.ndarray:
 
 
 def backward_slice(q, k, v, w_dwc, dy, p: Params, fwd: Optional[Dict] = None,
-                   alpha: Optional[float] = None) -> Dict[str, np.ndarray]:
-    """Gradients of <dy, Y> with respect to q, k, v for one slice (alpha held constant, reading R6).
+                   alpha: Optional[float] = None, exact_alpha: bool = False) -> Dict[str, np.ndarray]:
+    """Gradients of <dy, Y> with respect to q, k, v, the DWC weights and lambda for one slice.
 
     Chain rule through the forward steps, last step first. The kernel derivative is reading R4:
     d/dx exp(-||x-y||_1/lambda) = -(1/lambda) sign(x - y) exp(...), and +(1/lambda) sign(x - y) exp(...) in y.
+    In lambda: d/dlambda exp(-D/lambda) = exp(-D/lambda) D / lambda^2 for the distance D. alpha is held constant
+    (reading R6) unless exact_alpha is set.
     """
     f = fwd if fwd is not None else forward_slice(q, k, v, w_dwc, p, alpha)
     A, P, S, X, xs, We = f["A"], f["P"], f["S"], f["X"], f["xs"], f["We"]
@@ -238,6 +257,17 @@ def backward_slice(q, k, v, w_dwc, dy, p: Params, fwd: Optional[Dict] = None,
         dWe += -Xk.T @ G @ Xk.T
         G = 2.0 * G - G @ (We @ Xk).T - (Xk @ We).T @ G
     dWe += f["alpha"] * G.T  # X_0 = alpha We^T
+    if exact_alpha:
+        # alpha = 1 / (c r), c = max_j sum_i |We_ij|, r = max_i sum_j |We_ij|; d alpha = <G, We^T> (X_0 = alpha We^T)
+        aw = np.abs(We)
+        colsum, rowsum = aw.sum(axis=0), aw.sum(axis=1)
+        jc, ir = int(np.argmax(colsum)), int(np.argmax(rowsum))
+        a = f["alpha"]
+        dalpha = float(np.sum(G * We.T))
+        dadW = np.zeros_like(We)
+        dadW[:, jc] -= a / colsum[jc] * np.sign(We[:, jc])
+        dadW[ir, :] -= a / rowsum[ir] * np.sign(We[ir, :])
+        dWe += dalpha * dadW
     # Kernel entries -> points. The eps diagonal carries no gradient to L.
     Gq = dCQ * CQ / lam
     Gk = dCK * CK / lam
@@ -254,7 +284,12 @@ def backward_slice(q, k, v, w_dwc, dy, p: Params, fwd: Optional[Dict] = None,
     ys, xs_ = np.divmod(np.arange(N), p.W)
     owner = (ys // p.r) * Wr + (xs_ // p.r)
     dQ = dQ + dL[owner] / float(p.r * p.r)
-    return dict(dQ=dQ, dK=dK, dV=dV, dL=dL, dWe=dWe, dCQ=dCQ, dCK=dCK, dA=dA, dP=dP, dS=dS, dX=dX)
+    # lambda: every kernel entry k = exp(-D/lambda) moves by k D / lambda^2 (the eps diagonal does not depend on it)
+    dlam = float(np.sum(dCQ * CQ * l1_distance(q, L)) + np.sum(dCK * CK * l1_distance(k, L))
+                 + np.sum(dWe * Wm * l1_distance(L, L))) / (lam * lam)
+    d_dwc = dwc_weight_grad(v, dy, p.H, p.W)
+    return dict(dQ=dQ, dK=dK, dV=dV, dL=dL, dWe=dWe, dCQ=dCQ, dCK=dCK, dA=dA, dP=dP, dS=dS, dX=dX, dlam=dlam,
+                d_dwc=d_dwc)
 
 
 # ----------------------------------------------------------------------------------------------------------
@@ -283,13 +318,19 @@ def forward(Q, K, V, w_dwc, p: Params, keep: Optional[List[str]] = None) -> Dict
     return res
 
 
-def backward(Q, K, V, w_dwc, dY, p: Params) -> Dict[str, np.ndarray]:
-    """dQ, dK, dV over [B, heads, N, d] inputs."""
+def backward(Q, K, V, w_dwc, dY, p: Params, exact_alpha: bool = False) -> Dict[str, np.ndarray]:
+    """dQ, dK, dV over [B, heads, N, d] inputs; the DWC weight gradient [heads*d, 3, 3] (summed over the batch)
+    and the lambda gradient (summed over every slice)."""
     dQ = np.empty_like(Q)
     dK = np.empty_like(K)
     dV = np.empty_like(V)
+    d_dwc = np.zeros((p.heads * p.d, 3, 3))
+    dlam = 0.0
     for b in range(p.B):
         for h in range(p.heads):
-            g = backward_slice(Q[b, h], K[b, h], V[b, h], _head_w(w_dwc, h, p.d), dY[b, h], p)
+            g = backward_slice(Q[b, h], K[b, h], V[b, h], _head_w(w_dwc, h, p.d), dY[b, h], p,
+                               exact_alpha=exact_alpha)
             dQ[b, h], dK[b, h], dV[b, h] = g["dQ"], g["dK"], g["dV"]
-    return dict(dQ=dQ, dK=dK, dV=dV)
+            d_dwc[h * p.d:(h + 1) * p.d] += g["d_dwc"]
+            dlam += g["dlam"]
+    return dict(dQ=dQ, dK=dK, dV=dV, d_dwc=d_dwc, dlam=dlam)

@@ -10,6 +10,8 @@ import json
 import math
 import os
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -429,3 +431,92 @@ def test_alpha_dependence_vanishes_at_convergence():
     f = O.forward_slice(q, k, v, None, p)
     f2 = O.forward_slice(q, k, v, None, p, alpha=f["alpha"] * 0.9)
     assert np.linalg.norm(f["Yattn"] - f2["Yattn"]) / np.linalg.norm(f["Yattn"]) < 1e-12
+
+
+# ------------------------------------------------------------------------------------------- parameter gradients
+def _crop_case(whiten, ns_iters=None):
+    wl = WL.TRAIN_S1
+    inp = WL.make_inputs(wl, seed=0)
+    c = _crop(wl, inp)
+    p = O.Params(B=1, heads=1, H=4, W=4, d=wl.d, r=2, lam=wl.lam, eps=wl.eps,
+                 ns_iters=wl.ns_iters if ns_iters is None else ns_iters, whiten=whiten, whiten_eps=wl.whiten_eps)
+    return p, c["Q"], c["K"], c["V"], c["dY"], inp["w64"][:wl.d]
+
+
+def test_dwc_weight_grad_matches_finite_differences():
+    """Y is linear in the DWC weights, so central differences of <dy, Y> give the weight gradient exactly (up to
+    rounding); every one of the d x 9 taps is checked, on a grid with border tokens in every direction."""
+    wl = WL.TINY
+    inp = WL.make_inputs(wl, seed=0)
+    p = _params(wl)
+    q, k, v, w = inp["Q"][0, 0], inp["K"][0, 0], inp["V"][0, 0], inp["w64"][:wl.d]
+    dy = np.random.default_rng(5).standard_normal(v.shape)
+    g = O.backward_slice(q, k, v, w, dy, p)
+    h = 1e-3
+    fd = np.zeros_like(w)
+    for c in range(w.shape[0]):
+        for a in range(3):
+            for b in range(3):
+                e = np.zeros_like(w)
+                e[c, a, b] = h
+                yp = O.forward_slice(q, k, v, w + e, p)["Y"]
+                ym = O.forward_slice(q, k, v, w - e, p)["Y"]
+                fd[c, a, b] = np.sum(dy * (yp - ym)) / (2 * h)
+    assert np.linalg.norm(g["d_dwc"] - fd) / np.linalg.norm(fd) < 1e-9
+
+
+@pytest.mark.parametrize("whiten", [True, False])
+def test_lambda_grad_matches_finite_differences(whiten):
+    """d<dy, Y>/dlambda with alpha held at its value (reading R6), against central differences on the crop."""
+    p, q, k, v, dy, w = _crop_case(whiten)
+    f = O.forward_slice(q, k, v, w, p)
+    g = O.backward_slice(q, k, v, w, dy, p, fwd=f)
+    h = 1e-6
+
+    def loss(lam):
+        pp = dataclasses.replace(p, lam=lam)
+        return float(np.sum(dy * O.forward_slice(q, k, v, None, pp, alpha=f["alpha"])["Y"]))
+
+    fd = (loss(p.lam + h) - loss(p.lam - h)) / (2 * h)
+    assert abs(g["dlam"] - fd) <= 1e-6 * abs(fd), (g["dlam"], fd)
+
+
+def test_exact_alpha_gradient_matches_finite_differences():
+    """With two Newton-Schulz steps X_K still depends on alpha. The exact gradient (alpha recomputed from W_eps in
+    the forward of every difference) must match central differences in Q, K and lambda, and the stop-gradient
+    reading must visibly miss them, so the alpha path is really exercised. lambda = 64 makes the landmark kernel
+    matrix far from diagonal (at lambda = 4 its off-diagonal entries are ~exp(-30) and alpha hardly moves)."""
+    p, q, k, v, dy, w = _crop_case(True, ns_iters=2)
+    p = dataclasses.replace(p, lam=64.0)
+    f = O.forward_slice(q, k, v, w, p)
+    g = O.backward_slice(q, k, v, w, dy, p, fwd=f, exact_alpha=True)
+    g0 = O.backward_slice(q, k, v, w, dy, p, fwd=f)
+    h = 1e-6
+    L = f["L"]
+
+    def loss(qq, kk, pp):
+        return float(np.sum(dy * O.forward_slice(qq, kk, v, None, pp)["Y"]))
+
+    for name, arr in (("dQ", q), ("dK", k)):
+        fd = np.zeros_like(arr)
+        for i in range(arr.shape[0]):
+            for cc in range(arr.shape[1]):
+                e = np.zeros_like(arr)
+                e[i, cc] = h
+                if name == "dQ":
+                    fd[i, cc] = (loss(q + e, k, p) - loss(q - e, k, p)) / (2 * h)
+                else:
+                    fd[i, cc] = (loss(q, k + e, p) - loss(q, k - e, p)) / (2 * h)
+        near = np.abs(arr[:, None, :] - L[None, :, :]).min(axis=1) < 1e-5
+        fd[near] = g[name][near]
+        err = np.linalg.norm(g[name] - fd) / np.linalg.norm(fd)
+        err0 = np.linalg.norm(g0[name] - fd) / np.linalg.norm(fd)
+        assert err < 1e-6, (name, err)
+        if name == "dQ":
+            assert err0 > 100 * err and err0 > 1e-4, (name, err0)
+        else:
+            # K enters neither W_eps nor alpha (the landmarks are pooled from Q): the alpha path leaves dK alone
+            assert np.array_equal(g["dK"], g0["dK"])
+    fd = (loss(q, k, dataclasses.replace(p, lam=p.lam + h)) - loss(q, k, dataclasses.replace(p, lam=p.lam - h))) / (2 * h)
+    assert abs(g["dlam"] - fd) <= 1e-6 * abs(fd), (g["dlam"], fd)
+    assert abs(g0["dlam"] - fd) > 1e-4 * abs(fd), (g0["dlam"], fd)
