@@ -97,6 +97,20 @@ int lf_attn_bwd(const lf_attn_params* p, const void* Q, const void* K, const voi
                 const void* saved, const void* dY, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
                 lf_stream_t stream);
 
+/* The training op's full set of gradients: everything lf_attn_bwd writes, plus, each optional (NULL skips it):
+ *   d_dwc_w: [heads*d][3][3] float32, the gradient of <dY, Y> with respect to the DWC weights, summed over the
+ *            batch ([note] Design 1: Y = ... + DWC(V), which is linear in the weights);
+ *   d_lambda: one float32, the gradient with respect to lambda, summed over every slice (each kernel entry
+ *            k = exp(-D/lambda) moves by k D / lambda^2; [note] motivation "core idea" for the kernel).
+ * flags: LF_BWD_EXACT_ALPHA takes the gradient through the Newton-Schulz start alpha = 1/(||W_eps||_1 ||W_eps||_inf)
+ *        ([note] Design 3 for X_0 = alpha W_eps^T), differentiated at the first largest column and row sum;
+ *        without it alpha is held constant as in lf_attn_bwd. Other bits: LF_EINVAL.
+ * Same saved buffer, workspace (bwd_ws_bytes), alignment and errors as lf_attn_bwd; d_dwc_w is 16-byte aligned. */
+#define LF_BWD_EXACT_ALPHA 1
+int lf_attn_bwd_ex(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
+                   const void* saved, const void* dY, void* dQ, void* dK, void* dV, float* d_dwc_w, float* d_lambda,
+                   int flags, void* ws, size_t ws_bytes, lf_stream_t stream);
+
 /* Static description of a status code. */
 const char* lf_strerror(int code);
 

@@ -231,6 +231,14 @@ int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const voi
 int lf_attn_bwd(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
                 const void* saved, const void* dY, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
                 lf_stream_t stream) {
+  return lf_attn_bwd_ex(p, Q, K, V, dwc_w, saved, dY, dQ, dK, dV, nullptr, nullptr, 0, ws, ws_bytes, stream);
+}
+
+int lf_attn_bwd_ex(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
+                   const void* saved, const void* dY, void* dQ, void* dK, void* dV, float* d_dwc_w, float* d_lambda,
+                   int flags, void* ws, size_t ws_bytes, lf_stream_t stream) {
+  if (flags & ~LF_BWD_EXACT_ALPHA) return LF_EINVAL;
+  if (d_dwc_w && !aligned16(d_dwc_w)) return LF_EINVAL;
   const int rc = validate(p);
   if (rc != LF_OK) return rc;
   const lf::Shape s = make_shape(p);
@@ -254,8 +262,12 @@ int lf_attn_bwd(const lf_attn_params* p, const void* Q, const void* K, const voi
   sp.S = reinterpret_cast<const float*>(sb + sl.S);
   sp.P = reinterpret_cast<const float*>(sb + sl.P);
   sp.alpha = reinterpret_cast<const float*>(sb + sl.alpha);
+  lf::BwdExtras ex;
+  ex.d_dwc_w = d_dwc_w;
+  ex.d_lambda = d_lambda;
+  ex.exact_alpha = (flags & LF_BWD_EXACT_ALPHA) != 0;
   return hip_status(lf::launch_backward(s, p->whiten == 1, Q, K, V, dwc_w, sp, dY, dQ, dK, dV, ws,
-                                        reinterpret_cast<hipStream_t>(stream)));
+                                        reinterpret_cast<hipStream_t>(stream), ex));
 }
 
 // ---- stage entry points ----

@@ -33,8 +33,9 @@ __device__ __forceinline__ float sgnf(float x) { return x > 0.f ? 1.f : (x < 0.f
 namespace {
 
 struct BwdWs {
-  size_t T1, part, dX, dS, stats, dWe, dLW, Gq, Gk, dLpart, dL, total;
+  size_t T1, part, dX, dS, stats, dWe, dLW, Gq, Gk, dLpart, dL, lampart, dwcpart, total;
   int nsplitL, rpsL, nlb;
+  int lamchunks, dwcbands, dwcrows;
 };
 
 constexpr size_t kAlign = 256;
@@ -71,6 +72,13 @@ BwdWs plan(const Shape& s) {
   w.Gk = take(4 * G * N * m);
   w.dLpart = take(4 * G * static_cast<size_t>(w.nsplitL) * m * d);
   w.dL = take(4 * G * m * d);
+  // lambda gradient: per slice, chunks of 64 landmarks' worth of kernel entries; DWC weight gradient: per slice,
+  // bands of dwcrows grid rows, each a [9][d] partial
+  w.lamchunks = cdiv(2L * m * N + m * m, 64L * 1024);
+  w.lampart = take(4 * G * static_cast<size_t>(w.lamchunks));
+  w.dwcrows = 8;
+  w.dwcbands = cdiv(s.H, w.dwcrows);
+  w.dwcpart = take(4 * G * static_cast<size_t>(w.dwcbands) * 9 * d);
   w.total = off;
   return w;
 }
@@ -187,11 +195,14 @@ __device__ __forceinline__ void store_tiles(float* __restrict__ sC, const f32x4 
   }
 }
 
+// exact_alpha: also the path through alpha = 1 / (c r), c the largest column sum and r the largest row sum of |W|:
+// d alpha = <G, W^T> for the final adjoint G of X_0 = alpha W^T, and dW += d alpha * d alpha / dW, taken at the
+// first largest column and row.
 __global__ __launch_bounds__(64 * NSB_WAVES) void k_bwd_ns(const float* __restrict__ We,
                                                             const float* __restrict__ xs,
                                                             const float* __restrict__ alpha,
                                                             const float* __restrict__ dX, float* __restrict__ dWe,
-                                                            int m, int K) {
+                                                            int m, int K, int exact_alpha) {
   constexpr int NT = 64 * NSB_WAVES;
   constexpr int PER = (64 * 64 + NT - 1) / NT;  // matrix elements per thread when staging
   __shared__ float sW[64 * BL];
@@ -281,15 +292,67 @@ __global__ __launch_bounds__(64 * NSB_WAVES) void k_bwd_ns(const float* __restri
     cur = nxt;
   }
   __syncthreads();
+  const float a = alpha[g];
+  float da = 0.f, inv_c = 0.f, inv_r = 0.f;
+  int jc = 0, ir = 0;
+  if (exact_alpha) {
+    // column / row sums of |W| and their first maxima, and d alpha = sum_ij G_ij W_ji (fixed-order reductions)
+    __shared__ float s_cs[64], s_rs[64], s_part[64 * NSB_WAVES / 64];
+    __shared__ int s_arg[2];
+    __shared__ float s_da;
+    if (tid < 64) {
+      float cs = 0.f, rs = 0.f;
+      for (int i = 0; i < m; ++i) {
+        cs += fabsf(sW[i * BL + tid]);
+        rs += fabsf(sW[tid * BL + i]);
+      }
+      s_cs[tid] = tid < m ? cs : -1.f;
+      s_rs[tid] = tid < m ? rs : -1.f;
+    }
+    float pd = 0.f;
+    for (int idx = tid; idx < 64 * 64; idx += 64 * NSB_WAVES) {
+      const int i = idx >> 6, j = idx & 63;
+      pd += sG[cur][i * BL + j] * sW[j * BL + i];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) pd += __shfl_xor(pd, off);
+    if (ln == 0) s_part[wv] = pd;
+    __syncthreads();
+    if (tid == 0) {
+      int bc = 0, br = 0;
+      for (int j = 1; j < m; ++j) {
+        if (s_cs[j] > s_cs[bc]) bc = j;
+        if (s_rs[j] > s_rs[br]) br = j;
+      }
+      s_arg[0] = bc;
+      s_arg[1] = br;
+      float t = 0.f;
+      for (int w2 = 0; w2 < NSB_WAVES; ++w2) t += s_part[w2];
+      s_da = t;
+    }
+    __syncthreads();
+    jc = s_arg[0];
+    ir = s_arg[1];
+    inv_c = 1.f / s_cs[jc];
+    inv_r = 1.f / s_rs[ir];
+    da = s_da;
+  }
   if (wv < 4) {
-    const float a = alpha[g];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int j = t * 16 + (ln & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = wv * 16 + 4 * (ln >> 4) + r;
-        if (i < m && j < m) dWe[g * mm + i * m + j] = dacc[t][r] + a * sG[cur][j * BL + i];
+        if (i < m && j < m) {
+          float v = dacc[t][r] + a * sG[cur][j * BL + i];
+          if (exact_alpha) {
+            const float w = sW[i * BL + j];
+            const float sg = w > 0.f ? 1.f : (w < 0.f ? -1.f : 0.f);
+            v += da * (-a * sg) * ((j == jc ? inv_c : 0.f) + (i == ir ? inv_r : 0.f));
+          }
+          dWe[g * mm + i * m + j] = v;
+        }
       }
     }
   }
@@ -547,6 +610,115 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const T* __restrict__ Q, const
 }
 
 // ---------------------------------------------------------------------------------------------------------
+// lambda gradient: every kernel entry k = exp(-D / lambda) moves by k D / lambda^2 = -k ln(k) / lambda, so
+// d/dlambda = -sum G ln(k) over G = dC C / lambda (Gq, Gk, and Gw = dW W / lambda off the diagonal, where W = W_eps
+// and the eps diagonal does not depend on lambda). Block (slice, chunk) sums its share of the 2 m N + m^2 entries in
+// a fixed order; an entry whose k underflowed to 0 has G = 0 and adds nothing.
+// ---------------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bwd_dlam_partial(const float* __restrict__ Gq, const float* __restrict__ Gk,
+                                                          const float* __restrict__ CQ, const float* __restrict__ CK,
+                                                          const float* __restrict__ dWe, const float* __restrict__ We,
+                                                          float* __restrict__ part, int N, int m, int chunks,
+                                                          float inv_lam) {
+  const int g = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
+  const long mn = static_cast<long>(m) * N, total = 2 * mn + static_cast<long>(m) * m;
+  const long per = (total + chunks - 1) / chunks;
+  const long e0 = ch * per, e1 = min(total, e0 + per);
+  const size_t gmn = static_cast<size_t>(g) * mn, gmm = static_cast<size_t>(g) * m * m;
+  float acc = 0.f;
+  for (long e = e0 + tid; e < e1; e += 256) {
+    float gv, kv;
+    if (e < mn) {
+      gv = Gq[gmn + e];
+      kv = CQ[gmn + e];
+    } else if (e < 2 * mn) {
+      gv = Gk[gmn + e - mn];
+      kv = CK[gmn + e - mn];
+    } else {
+      const long q = e - 2 * mn;
+      const int i = static_cast<int>(q / m), j = static_cast<int>(q % m);
+      kv = We[gmm + q];
+      gv = (i == j) ? 0.f : dWe[gmm + q] * kv * inv_lam;
+    }
+    acc += kv > 0.f ? -gv * logf(kv) : 0.f;
+  }
+  __shared__ float red[256];
+  red[tid] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) part[static_cast<size_t>(g) * chunks + ch] = red[0];
+}
+
+__global__ __launch_bounds__(64) void k_bwd_dlam_final(const float* __restrict__ part, float* __restrict__ out,
+                                                       int n) {
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int i = 0; i < n; ++i) t += part[i];
+    *out = t;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// DWC weight gradient: dw[h d + c][a][b] = sum over the batch and the grid of dY[(y, x), c] V[(y+a-1, x+b-1), c]
+// (zero outside the grid). Block (slice, band of grid rows): thread = (channel, token phase) accumulates the 9
+// taps, the phases are summed in LDS in order into a [9][d] partial; the final pass sums the partials of the batch
+// and bands in order.
+// ---------------------------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_dwc_wgrad_partial(const T* __restrict__ dY, const T* __restrict__ V,
+                                                           float* __restrict__ part, int H, int W, int rows,
+                                                           int bands) {
+  constexpr int PH = 256 / D;
+  const int g = blockIdx.y, band = blockIdx.x, tid = threadIdx.x;
+  const int c = tid % D, ph = tid / D;
+  const size_t N = static_cast<size_t>(H) * W;
+  const T* dy = dY + static_cast<size_t>(g) * N * D + c;
+  const T* v = V + static_cast<size_t>(g) * N * D + c;
+  const int y0 = band * rows, y1 = min(H, y0 + rows);
+  float acc[9];
+#pragma unroll
+  for (int q = 0; q < 9; ++q) acc[q] = 0.f;
+  for (int t = y0 * W + ph; t < y1 * W; t += PH) {
+    const int y = t / W, x = t % W;
+    const float gy = to_f32(dy[static_cast<size_t>(t) * D]);
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        const int yy = y + a - 1, xx = x + b - 1;
+        if (yy >= 0 && yy < H && xx >= 0 && xx < W)
+          acc[a * 3 + b] += gy * to_f32(v[static_cast<size_t>(yy * W + xx) * D]);
+      }
+  }
+  __shared__ float red[9][256];
+#pragma unroll
+  for (int q = 0; q < 9; ++q) red[q][tid] = acc[q];
+  __syncthreads();
+  for (int e = tid; e < 9 * D; e += 256) {
+    const int q = e / D, cc = e % D;
+    float t = 0.f;
+    for (int p2 = 0; p2 < PH; ++p2) t += red[q][p2 * D + cc];
+    part[((static_cast<size_t>(g) * bands + band) * 9 + q) * D + cc] = t;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_dwc_wgrad_final(const float* __restrict__ part, float* __restrict__ out,
+                                                         int B, int heads, int D, int bands) {
+  const int t = blockIdx.x * 256 + threadIdx.x;  // (h, c, q) of out[(h D + c) 9 + q]
+  if (t >= heads * D * 9) return;
+  const int q = t % 9, hc = t / 9, h = hc / D, c = hc % D;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const int g = b * heads + h;
+    for (int bd = 0; bd < bands; ++bd) s += part[((static_cast<size_t>(g) * bands + bd) * 9 + q) * D + c];
+  }
+  out[t] = s;
+}
+
+// ---------------------------------------------------------------------------------------------------------
 size_t bwd_ws_bytes(const Shape& s) {
   if (s.m > 64 || s.d > 64) return 0;
   return plan(s).total;
@@ -555,7 +727,7 @@ size_t bwd_ws_bytes(const Shape& s) {
 template <typename T, int D>
 static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void* Kv, const void* Vv, const float* w,
                         const SavedPtrs& sp, const void* dYv, void* dQv, void* dKv, void* dVv, void* ws,
-                        hipStream_t st) {
+                        hipStream_t st, const BwdExtras& ex) {
   const BwdWs p = plan(s);
   char* b = static_cast<char*>(ws);
   float* T1 = reinterpret_cast<float*>(b + p.T1);
@@ -583,7 +755,7 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
   hipLaunchKernelGGL(k_bwd_small1<D>, dim3(s.G, s.m < 8 ? s.m : 8), dim3(256), 0, st, T1, sp.S, sp.P, sp.xs, sp.mu,
                      sp.rstd, dX, dS, stats, s.m, s.ns_iters, s.N, wh);
   hipLaunchKernelGGL(k_bwd_ns, dim3(s.G), dim3(64 * NSB_WAVES), 0, st, sp.We, sp.xs, sp.alpha, dX, dWe, s.m,
-                     s.ns_iters);
+                     s.ns_iters, ex.exact_alpha ? 1 : 0);
   hipLaunchKernelGGL(k_bwd_wpart, dim3(cdiv(static_cast<long>(s.m) * D, 256), s.G), dim3(256), 0, st, sp.L, sp.We,
                      dWe, dLW, s.m, D, inv_lam);
   hipLaunchKernelGGL((k_bwd_rowgrad<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(256), 0, st, dY, V, sp.P, dS, sp.CQ,
@@ -597,24 +769,38 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
                      dL, s.G, p.nsplitL, md);
   hipLaunchKernelGGL((k_bwd_rows<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(64 * (D >= 64 ? 4 : D / 16)), 0, st, Q,
                      K, sp.L, Gq, Gk, dL, dQ, dK, s.N, s.m, s.W, s.r);
+  if (ex.d_lambda) {
+    float* lp = reinterpret_cast<float*>(b + p.lampart);
+    hipLaunchKernelGGL(k_bwd_dlam_partial, dim3(p.lamchunks, s.G), dim3(256), 0, st, Gq, Gk, sp.CQ, sp.CK, dWe,
+                       sp.We, lp, s.N, s.m, p.lamchunks, inv_lam);
+    hipLaunchKernelGGL(k_bwd_dlam_final, dim3(1), dim3(64), 0, st, lp, ex.d_lambda, s.G * p.lamchunks);
+  }
+  if (ex.d_dwc_w) {
+    float* dp = reinterpret_cast<float*>(b + p.dwcpart);
+    hipLaunchKernelGGL((k_dwc_wgrad_partial<T, D>), dim3(p.dwcbands, s.G), dim3(256), 0, st, dY, V, dp, s.H, s.W,
+                       p.dwcrows, p.dwcbands);
+    hipLaunchKernelGGL(k_dwc_wgrad_final, dim3(cdiv(static_cast<long>(s.heads) * D * 9, 256)), dim3(256), 0, st, dp,
+                       ex.d_dwc_w, s.G / s.heads, s.heads, D, p.dwcbands);
+  }
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t bwd_d(const Shape& s, bool whiten, const void* Q, const void* K, const void* V, const float* w,
-                        const SavedPtrs& sp, const void* dY, void* dQ, void* dK, void* dV, void* ws, hipStream_t st) {
+                        const SavedPtrs& sp, const void* dY, void* dQ, void* dK, void* dV, void* ws, hipStream_t st,
+                        const BwdExtras& ex) {
   switch (s.d) {
-    case 16: return bwd_t<T, 16>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st);
-    case 32: return bwd_t<T, 32>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st);
-    default: return bwd_t<T, 64>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st);
+    case 16: return bwd_t<T, 16>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex);
+    case 32: return bwd_t<T, 32>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex);
+    default: return bwd_t<T, 64>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex);
   }
 }
 
 hipError_t launch_backward(const Shape& s, bool whiten, const void* Q, const void* K, const void* V, const float* w,
                            const SavedPtrs& sp, const void* dY, void* dQ, void* dK, void* dV, void* ws,
-                           hipStream_t st) {
-  if (s.dtype == 1) return bwd_d<bf16_t>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st);
-  return bwd_d<float>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st);
+                           hipStream_t st, const BwdExtras& ex) {
+  if (s.dtype == 1) return bwd_d<bf16_t>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex);
+  return bwd_d<float>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex);
 }
 
 }  // namespace lf

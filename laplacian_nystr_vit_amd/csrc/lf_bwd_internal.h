@@ -16,8 +16,15 @@ struct SavedPtrs {
 // Backward workspace in bytes; 0 when the shape is outside what the backward kernels support (m or d > 64).
 size_t bwd_ws_bytes(const Shape& s);
 
+// Optional outputs of the training op beyond dQ, dK, dV.
+struct BwdExtras {
+  float* d_dwc_w = nullptr;   // [heads * d][3][3], summed over the batch
+  float* d_lambda = nullptr;  // one float, summed over every slice
+  bool exact_alpha = false;   // gradient through alpha instead of holding it constant
+};
+
 hipError_t launch_backward(const Shape& s, bool whiten, const void* Q, const void* K, const void* V, const float* w,
                            const SavedPtrs& sp, const void* dY, void* dQ, void* dK, void* dV, void* ws,
-                           hipStream_t st);
+                           hipStream_t st, const BwdExtras& ex = BwdExtras());
 
 }  // namespace lf

@@ -26,8 +26,9 @@ LF_NS_ITERS_MAX = 64
 EXPORTS = (
     "lf_attn_query", "lf_attn_saved_layout", "lf_attn_fwd", "lf_attn_bwd", "lf_strerror", "lf_landmark_pool",
     "lf_laplace_l1_exp", "lf_ns_pinv", "lf_ckv_reduce", "lf_whiten_stats", "lf_landmark_mix", "lf_out_gemm_dwc",
-    "lf_out_gemm_dwc_fused",
+    "lf_out_gemm_dwc_fused", "lf_attn_bwd_ex",
 )
+LF_BWD_EXACT_ALPHA = 1
 
 
 class LfAttnParams(ctypes.Structure):
@@ -81,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lf_attn_saved_layout": (ctypes.c_int, [_P, ctypes.POINTER(LfSavedLayout)]),
         "lf_attn_fwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "lf_attn_bwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "lf_attn_bwd_ex": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int,
+                                          _vp, _sz, _vp]),
         "lf_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "lf_landmark_pool": (ctypes.c_int, [_P, _vp, _vp, _vp]),
         "lf_laplace_l1_exp": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -180,6 +183,19 @@ def lf_attn_bwd(p, Q, K, V, dwc_w, saved, dY, dQ, dK, dV, ws, stream=None) -> No
         _ptr(dwc_w, "dwc_w", torch.float32, p.heads * p.d * 9), _ptr(saved, "saved"), _ptr(dY, "dY", dt, n),
         _ptr(dQ, "dQ", dt, n), _ptr(dK, "dK", dt, n), _ptr(dV, "dV", dt, n), _ptr(ws, "ws"), _nbytes(ws),
         _stream(stream)), "lf_attn_bwd")
+
+
+def lf_attn_bwd_ex(p, Q, K, V, dwc_w, saved, dY, dQ, dK, dV, d_dwc_w, d_lambda, flags, ws, stream=None) -> None:
+    dt, n = io_dtype(p), p.G * p.N * p.d
+    _, saved_b, _ = lf_attn_query(p)
+    if _nbytes(saved) < saved_b:
+        raise ValueError(f"saved needs {saved_b} bytes")
+    _check(load_library().lf_attn_bwd_ex(
+        ctypes.byref(p), _ptr(Q, "Q", dt, n), _ptr(K, "K", dt, n), _ptr(V, "V", dt, n),
+        _ptr(dwc_w, "dwc_w", torch.float32, p.heads * p.d * 9), _ptr(saved, "saved"), _ptr(dY, "dY", dt, n),
+        _ptr(dQ, "dQ", dt, n), _ptr(dK, "dK", dt, n), _ptr(dV, "dV", dt, n),
+        _ptr(d_dwc_w, "d_dwc_w", torch.float32, p.heads * p.d * 9), _ptr(d_lambda, "d_lambda", torch.float32, 1),
+        int(flags), _ptr(ws, "ws"), _nbytes(ws), _stream(stream)), "lf_attn_bwd_ex")
 
 
 def lf_landmark_pool(p, Q, L, stream=None) -> None:

@@ -120,3 +120,17 @@ def test_binding_rejects_host_tensors(lib):
     q = torch.zeros(p.G * p.N * p.d)
     with pytest.raises(TypeError):
         lf.lf_landmark_pool(p, q, torch.zeros(p.G * p.m * p.d))
+
+
+def test_bwd_ex_validates_flags_and_alignment_on_host(lib):
+    p = _p(WL.TRAIN_S1)
+    _, _, bwd = lf.lf_attn_query(p)
+    fake = ctypes.c_void_p(0x100000)
+    misaligned = ctypes.c_void_p(0x100004)
+    # unknown flag bits, then a misaligned d_dwc_w: both rejected before anything is launched
+    assert lib.lf_attn_bwd_ex(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, fake, None, None, 2,
+                              fake, bwd, None) == lf.LF_EINVAL
+    assert lib.lf_attn_bwd_ex(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, fake, misaligned,
+                              None, 0, fake, bwd, None) == lf.LF_EINVAL
+    assert lib.lf_attn_bwd_ex(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, fake, None, None,
+                              lf.LF_BWD_EXACT_ALPHA, fake, bwd - 1, None) == lf.LF_EWORKSPACE

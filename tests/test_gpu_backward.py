@@ -80,3 +80,64 @@ def test_backward_is_deterministic():
     b = _gpu_backward(wl)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+# ------------------------------------------------------------------------------- the training op's other gradients
+def _gpu_backward_ex(wl, flags):
+    p = params(wl)
+    t = upload(wl)
+    fwd_b, saved_b, bwd_b = lf.lf_attn_query(p)
+    ws = torch.empty(max(fwd_b, bwd_b), dtype=torch.uint8, device="cuda")
+    saved = torch.empty(saved_b, dtype=torch.uint8, device="cuda")
+    Y = torch.empty_like(t["Q"])
+    lf.lf_attn_fwd(p, t["Q"], t["K"], t["V"], t["w"], Y, saved, ws)
+    dQ, dK, dV = torch.empty_like(t["Q"]), torch.empty_like(t["K"]), torch.empty_like(t["V"])
+    dw = torch.empty(p.heads * p.d * 9, device="cuda")
+    dl = torch.empty(1, device="cuda")
+    lf.lf_attn_bwd_ex(p, t["Q"], t["K"], t["V"], t["w"], saved, t["dY"], dQ, dK, dV, dw, dl, flags, ws)
+    torch.cuda.synchronize()
+    return dict(dQ=host(dQ), dK=host(dK), dV=host(dV), d_dwc=host(dw).reshape(p.heads * p.d, 3, 3),
+                dlam=float(host(dl)[0]))
+
+
+PARAM_CASES = [
+    WL.TRAIN_S1.replace(name="train_s1_B2", B=2),
+    WL.TINY.replace(name="train_tiny_whiten_h2", B=2, heads=2, whiten=True, backward=True),
+    WL.TINY.replace(name="train_ragged_10x6_d32", H=10, W=6, d=32, r=2, whiten=True, backward=True),
+    WL.TRAIN_S1.replace(name="train_s1_bf16_B2", B=2, dtype=WL.BF16),
+]
+
+
+@pytest.mark.parametrize("wl", PARAM_CASES, ids=lambda w: w.name)
+def test_param_grads_match_oracle(wl):
+    """DWC weight gradient (summed over the batch per head) and lambda gradient, alpha held constant; dQ, dK and
+    dV of the extended call are bitwise those of lf_attn_bwd."""
+    note(f"[gpu] parameter gradients {wl.name}")
+    inp = inputs(wl)
+    ref = O.backward(inp["Q"], inp["K"], inp["V"], inp["w64"], inp["dY"], oparams(wl))
+    g = _gpu_backward_ex(wl, 0)
+    e_w = relF(g["d_dwc"], ref["d_dwc"])
+    e_l = abs(g["dlam"] - ref["dlam"]) / abs(ref["dlam"])
+    note(f"    d_dwc={e_w:.3e} dlambda={e_l:.3e} ({g['dlam']:.6e} vs {ref['dlam']:.6e})")
+    assert e_w <= tol(wl)
+    assert e_l <= tol(wl)
+    dQ, dK, dV = _gpu_backward(wl)
+    assert np.array_equal(dQ, g["dQ"]) and np.array_equal(dK, g["dK"]) and np.array_equal(dV, g["dV"])
+
+
+def test_exact_alpha_matches_oracle():
+    """One Newton-Schulz step and lambda = 16 (a landmark kernel matrix far from diagonal), so X_K depends on alpha:
+    the exact gradients match the oracle's, and they differ from the constant-alpha ones by more than the bar."""
+    wl = WL.TINY.replace(name="tiny_exact_alpha", B=2, lam=16.0, ns_iters=1, whiten=True, backward=True)
+    note(f"[gpu] exact alpha {wl.name}")
+    inp = inputs(wl)
+    ref = O.backward(inp["Q"], inp["K"], inp["V"], inp["w64"], inp["dY"], oparams(wl), exact_alpha=True)
+    ref0 = O.backward(inp["Q"], inp["K"], inp["V"], inp["w64"], inp["dY"], oparams(wl))
+    g = _gpu_backward_ex(wl, lf.LF_BWD_EXACT_ALPHA)
+    errs = {n: relF(g[n], ref[n]) for n in ("dQ", "dK", "dV")}
+    errs["dlam"] = abs(g["dlam"] - ref["dlam"]) / abs(ref["dlam"])
+    note("    " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()))
+    for n, e in errs.items():
+        assert e <= tol(wl), (n, e)
+    assert relF(ref0["dQ"], ref["dQ"]) > 10 * tol(wl)
+    assert abs(ref0["dlam"] - ref["dlam"]) > 10 * tol(wl) * abs(ref["dlam"])
