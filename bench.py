@@ -10,7 +10,8 @@ of the dominant kernel (laplace_l1_exp: VALU-bound, timed with HIP events on its
 oracle timed on a bounded sample of the same workload on the host cores.
 
 --workload picks another shape; for the training shape (whitening on) a step is lf_attn_fwd with the saved buffer
-followed by lf_attn_bwd. Besides the hot figure (one buffer set, as the contract's value) it reports a "cold" one:
+followed by lf_attn_bwd_ex (dQ, dK, dV and the DWC weight and lambda gradients). Besides the hot figure (one
+buffer set, as the contract's value) it reports a "cold" one:
 the same steps rotating over enough input/output/workspace sets (>= 512 MB in all) that no step finds its data in
 the 256 MB last-level cache (--no-cold skips it).
 """
@@ -233,13 +234,16 @@ def main():
             t["dY"] = dev(inp["dY_raw"])
             for g in ("dQ", "dK", "dV"):
                 t[g] = torch.empty_like(t["Q"])
+            t["dw"] = torch.empty(wl.heads * wl.d * 9, device="cuda")
+            t["dlam"] = torch.empty(1, device="cuda")
         return t
 
     def run_step(t):
         if train:
+            # the full training op: dQ, dK, dV and the DWC weight and lambda gradients
             lf.lf_attn_fwd(p, t["Q"], t["K"], t["V"], t["w"], t["Y"], t["saved"], t["ws"], stream)
-            lf.lf_attn_bwd(p, t["Q"], t["K"], t["V"], t["w"], t["saved"], t["dY"], t["dQ"], t["dK"], t["dV"],
-                           t["ws"], stream)
+            lf.lf_attn_bwd_ex(p, t["Q"], t["K"], t["V"], t["w"], t["saved"], t["dY"], t["dQ"], t["dK"], t["dV"],
+                              t["dw"], t["dlam"], 0, t["ws"], stream)
         else:
             lf.lf_attn_fwd(p, t["Q"], t["K"], t["V"], t["w"], t["Y"], None, t["ws"], stream)
 

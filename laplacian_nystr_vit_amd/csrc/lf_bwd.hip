@@ -74,10 +74,10 @@ BwdWs plan(const Shape& s) {
   w.dL = take(4 * G * m * d);
   // lambda gradient: per slice, chunks of 64 landmarks' worth of kernel entries; DWC weight gradient: per slice,
   // bands of dwcrows grid rows, each a [9][d] partial
-  w.lamchunks = cdiv(2L * m * N + m * m, 64L * 1024);
+  w.lamchunks = cdiv(2L * m * N + m * m, 4096);
   w.lampart = take(4 * G * static_cast<size_t>(w.lamchunks));
-  w.dwcrows = 8;
-  w.dwcbands = cdiv(s.H, w.dwcrows);
+  w.dwcrows = 1;
+  w.dwcbands = s.H;
   w.dwcpart = take(4 * G * static_cast<size_t>(w.dwcbands) * 9 * d);
   w.total = off;
   return w;
@@ -612,8 +612,9 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const T* __restrict__ Q, const
 // ---------------------------------------------------------------------------------------------------------
 // lambda gradient: every kernel entry k = exp(-D / lambda) moves by k D / lambda^2 = -k ln(k) / lambda, so
 // d/dlambda = -sum G ln(k) over G = dC C / lambda (Gq, Gk, and Gw = dW W / lambda off the diagonal, where W = W_eps
-// and the eps diagonal does not depend on lambda). Block (slice, chunk) sums its share of the 2 m N + m^2 entries in
-// a fixed order; an entry whose k underflowed to 0 has G = 0 and adds nothing.
+// and the eps diagonal does not depend on lambda). Block (slice, chunk of 4096 entries) sums its share of the
+// 2 m N + m^2 entries in a fixed order, 4 entries per thread at a time; an entry whose k underflowed to 0 has G = 0
+// and adds nothing.
 // ---------------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_bwd_dlam_partial(const float* __restrict__ Gq, const float* __restrict__ Gk,
                                                           const float* __restrict__ CQ, const float* __restrict__ CK,
@@ -626,6 +627,7 @@ __global__ __launch_bounds__(256) void k_bwd_dlam_partial(const float* __restric
   const long e0 = ch * per, e1 = min(total, e0 + per);
   const size_t gmn = static_cast<size_t>(g) * mn, gmm = static_cast<size_t>(g) * m * m;
   float acc = 0.f;
+#pragma unroll 4
   for (long e = e0 + tid; e < e1; e += 256) {
     float gv, kv;
     if (e < mn) {
@@ -652,26 +654,36 @@ __global__ __launch_bounds__(256) void k_bwd_dlam_partial(const float* __restric
   if (tid == 0) part[static_cast<size_t>(g) * chunks + ch] = red[0];
 }
 
-__global__ __launch_bounds__(64) void k_bwd_dlam_final(const float* __restrict__ part, float* __restrict__ out,
-                                                       int n) {
-  if (threadIdx.x == 0) {
-    float t = 0.f;
-    for (int i = 0; i < n; ++i) t += part[i];
-    *out = t;
+// One block: thread t sums the partials t, t + 256, ... in order, then a fixed tree in LDS.
+__global__ __launch_bounds__(256) void k_bwd_dlam_final(const float* __restrict__ part, float* __restrict__ out,
+                                                        int n) {
+  const int tid = threadIdx.x;
+  float t = 0.f;
+  for (int i = tid; i < n; i += 256) t += part[i];
+  __shared__ float red[256];
+  red[tid] = t;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
   }
+  if (tid == 0) *out = red[0];
 }
 
 // ---------------------------------------------------------------------------------------------------------
 // DWC weight gradient: dw[h d + c][a][b] = sum over the batch and the grid of dY[(y, x), c] V[(y+a-1, x+b-1), c]
-// (zero outside the grid). Block (slice, band of grid rows): thread = (channel, token phase) accumulates the 9
-// taps, the phases are summed in LDS in order into a [9][d] partial; the final pass sums the partials of the batch
-// and bands in order.
+// (zero outside the grid). Block (slice, band of grid rows, here one row): thread = (channel, token phase)
+// accumulates the 9 taps over its tokens (loop unrolled so their loads overlap), and the phases are summed in LDS in
+// order into a [9][d] partial. The final pass gives each (head, tap) a block whose threads sum strided runs of the
+// (batch, band) partials in order and then combine them in a fixed order.
 // ---------------------------------------------------------------------------------------------------------
+constexpr int kDwcThreads = 1024;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_dwc_wgrad_partial(const T* __restrict__ dY, const T* __restrict__ V,
-                                                           float* __restrict__ part, int H, int W, int rows,
-                                                           int bands) {
-  constexpr int PH = 256 / D;
+__global__ __launch_bounds__(kDwcThreads) void k_dwc_wgrad_partial(const T* __restrict__ dY, const T* __restrict__ V,
+                                                                   float* __restrict__ part, int H, int W, int rows,
+                                                                   int bands) {
+  constexpr int PH = kDwcThreads / D;
   const int g = blockIdx.y, band = blockIdx.x, tid = threadIdx.x;
   const int c = tid % D, ph = tid / D;
   const size_t N = static_cast<size_t>(H) * W;
@@ -681,6 +693,7 @@ __global__ __launch_bounds__(256) void k_dwc_wgrad_partial(const T* __restrict__
   float acc[9];
 #pragma unroll
   for (int q = 0; q < 9; ++q) acc[q] = 0.f;
+#pragma unroll 4
   for (int t = y0 * W + ph; t < y1 * W; t += PH) {
     const int y = t / W, x = t % W;
     const float gy = to_f32(dy[static_cast<size_t>(t) * D]);
@@ -693,11 +706,11 @@ __global__ __launch_bounds__(256) void k_dwc_wgrad_partial(const T* __restrict__
           acc[a * 3 + b] += gy * to_f32(v[static_cast<size_t>(yy * W + xx) * D]);
       }
   }
-  __shared__ float red[9][256];
+  __shared__ float red[9][kDwcThreads];
 #pragma unroll
   for (int q = 0; q < 9; ++q) red[q][tid] = acc[q];
   __syncthreads();
-  for (int e = tid; e < 9 * D; e += 256) {
+  for (int e = tid; e < 9 * D; e += kDwcThreads) {
     const int q = e / D, cc = e % D;
     float t = 0.f;
     for (int p2 = 0; p2 < PH; ++p2) t += red[q][p2 * D + cc];
@@ -705,17 +718,29 @@ __global__ __launch_bounds__(256) void k_dwc_wgrad_partial(const T* __restrict__
   }
 }
 
-__global__ __launch_bounds__(256) void k_dwc_wgrad_final(const float* __restrict__ part, float* __restrict__ out,
-                                                         int B, int heads, int D, int bands) {
-  const int t = blockIdx.x * 256 + threadIdx.x;  // (h, c, q) of out[(h D + c) 9 + q]
-  if (t >= heads * D * 9) return;
-  const int q = t % 9, hc = t / 9, h = hc / D, c = hc % D;
+template <int D>
+__global__ __launch_bounds__(kDwcThreads) void k_dwc_wgrad_final(const float* __restrict__ part,
+                                                                 float* __restrict__ out, int B, int heads,
+                                                                 int bands) {
+  constexpr int PH = kDwcThreads / D;
+  const int h = blockIdx.x / 9, q = blockIdx.x % 9, tid = threadIdx.x;
+  const int c = tid % D, ph = tid / D;
+  const int n = B * bands;  // terms j = b * bands + band
   float s = 0.f;
-  for (int b = 0; b < B; ++b) {
+#pragma unroll 4
+  for (int j = ph; j < n; j += PH) {
+    const int b = j / bands, bd = j % bands;
     const int g = b * heads + h;
-    for (int bd = 0; bd < bands; ++bd) s += part[((static_cast<size_t>(g) * bands + bd) * 9 + q) * D + c];
+    s += part[((static_cast<size_t>(g) * bands + bd) * 9 + q) * D + c];
   }
-  out[t] = s;
+  __shared__ float red[kDwcThreads];
+  red[tid] = s;
+  __syncthreads();
+  if (ph == 0) {
+    float t = 0.f;
+    for (int p2 = 0; p2 < PH; ++p2) t += red[p2 * D + c];
+    out[(static_cast<size_t>(h) * D + c) * 9 + q] = t;
+  }
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -773,14 +798,14 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
     float* lp = reinterpret_cast<float*>(b + p.lampart);
     hipLaunchKernelGGL(k_bwd_dlam_partial, dim3(p.lamchunks, s.G), dim3(256), 0, st, Gq, Gk, sp.CQ, sp.CK, dWe,
                        sp.We, lp, s.N, s.m, p.lamchunks, inv_lam);
-    hipLaunchKernelGGL(k_bwd_dlam_final, dim3(1), dim3(64), 0, st, lp, ex.d_lambda, s.G * p.lamchunks);
+    hipLaunchKernelGGL(k_bwd_dlam_final, dim3(1), dim3(256), 0, st, lp, ex.d_lambda, s.G * p.lamchunks);
   }
   if (ex.d_dwc_w) {
     float* dp = reinterpret_cast<float*>(b + p.dwcpart);
-    hipLaunchKernelGGL((k_dwc_wgrad_partial<T, D>), dim3(p.dwcbands, s.G), dim3(256), 0, st, dY, V, dp, s.H, s.W,
-                       p.dwcrows, p.dwcbands);
-    hipLaunchKernelGGL(k_dwc_wgrad_final, dim3(cdiv(static_cast<long>(s.heads) * D * 9, 256)), dim3(256), 0, st, dp,
-                       ex.d_dwc_w, s.G / s.heads, s.heads, D, p.dwcbands);
+    hipLaunchKernelGGL((k_dwc_wgrad_partial<T, D>), dim3(p.dwcbands, s.G), dim3(kDwcThreads), 0, st, dY, V, dp, s.H,
+                       s.W, p.dwcrows, p.dwcbands);
+    hipLaunchKernelGGL(k_dwc_wgrad_final<D>, dim3(s.heads * 9), dim3(kDwcThreads), 0, st, dp, ex.d_dwc_w,
+                       s.G / s.heads, s.heads, p.dwcbands);
   }
   return hipGetLastError();
 }
