@@ -143,3 +143,14 @@ def make_inputs(wl: Workload, seed: int = 0, with_dy: Optional[bool] = None) -> 
     result["w"] = w
     result["w64"] = w.astype(np.float64)
     return result
+
+
+def spd_matrix(m: int, kappa: float, seed: int) -> np.ndarray:
+    """Seeded synthetic symmetric positive definite m x m matrix with condition number kappa, rounded to float32
+    and returned as float64 (exactly the numbers the GPU receives): a random orthonormal basis (QR of a Gaussian
+    matrix) with eigenvalues spaced geometrically from 1 to kappa, symmetrised after the product. The solver
+    claim of the pages is stated at kappa = 50."""
+    rng = np.random.default_rng(seed)
+    basis, _ = np.linalg.qr(rng.standard_normal((m, m)))
+    a = (basis * np.geomspace(1.0, kappa, m)) @ basis.T
+    return (0.5 * (a + a.T)).astype(np.float32).astype(np.float64)

@@ -138,6 +138,35 @@ def newton_schulz(w_eps: np.ndarray, iters: int, alpha: Optional[float] = None):
 
 
 # ----------------------------------------------------------------------------------------------------------
+# Solver comparator: conjugate gradients for W_eps X = I  [note, Design 3 (the robustness claim against CG at a
+# condition number of 50); ablation table, solver row; key findings, second item]
+# ----------------------------------------------------------------------------------------------------------
+def cg_pinv(w_eps: np.ndarray, iters: int):
+    """Conjugate gradients for W_eps X = I. Column j is an independent CG solve of W_eps x = e_j from x = 0 with
+    the textbook recurrences (residual r = b - W x, search direction p, step a = r.r / p.Wp, then
+    p <- r' + (r'.r' / r.r) p). Returns X and, per iteration, the Frobenius norm of the residual W_eps X - I.
+    A column whose residual is exactly zero stops."""
+    m = w_eps.shape[0]
+    X = np.zeros((m, m))
+    R = np.eye(m)
+    P = R.copy()
+    rr = np.sum(R * R, axis=0)
+    hist = []
+    for _ in range(iters):
+        Q = w_eps @ P
+        pq = np.sum(P * Q, axis=0)
+        a = np.where(rr > 0, rr / np.where(pq != 0, pq, 1.0), 0.0)
+        X = X + P * a
+        R = R - Q * a
+        rr_new = np.sum(R * R, axis=0)
+        beta = np.where(rr > 0, rr_new / np.where(rr > 0, rr, 1.0), 0.0)
+        P = R + P * beta
+        rr = rr_new
+        hist.append(float(np.linalg.norm(w_eps @ X - np.eye(m))))
+    return X, hist
+
+
+# ----------------------------------------------------------------------------------------------------------
 # Step 4: diagonal whitening of the similarity vectors  [note, Design 1]
 # ----------------------------------------------------------------------------------------------------------
 def whiten_columns(c: np.ndarray, eps_w: float):

@@ -520,3 +520,47 @@ def test_exact_alpha_gradient_matches_finite_differences():
     fd = (loss(q, k, dataclasses.replace(p, lam=p.lam + h)) - loss(q, k, dataclasses.replace(p, lam=p.lam - h))) / (2 * h)
     assert abs(g["dlam"] - fd) <= 1e-6 * abs(fd), (g["dlam"], fd)
     assert abs(g0["dlam"] - fd) > 1e-4 * abs(fd), (g0["dlam"], fd)
+
+
+# ------------------------------------------------------------------------------------------------ CG comparator
+def test_cg_reaches_the_inverse():
+    """CG terminates in as many steps as W has distinct eigenvalues (exact arithmetic): a 32 x 32 SPD matrix with
+    three eigenvalues {1, 7, 50} is inverted to rounding after 3 steps and not after 2. With 32 distinct eigenvalues
+    (kappa = 50) rounding delays termination a little, so 1.5 m steps reach the inverse; so does a workload's
+    landmark kernel matrix after 2 m steps."""
+    rng = np.random.default_rng(3)
+    Qm, _ = np.linalg.qr(rng.standard_normal((32, 32)))
+    B = (Qm * np.repeat([1.0, 7.0, 50.0], [10, 12, 10])) @ Qm.T
+    B = 0.5 * (B + B.T)
+    inv = np.linalg.inv(B)
+    X2, _ = O.cg_pinv(B, 2)
+    X3, _ = O.cg_pinv(B, 3)
+    assert np.linalg.norm(X2 - inv) / np.linalg.norm(inv) > 0.1
+    assert np.linalg.norm(X3 - inv) / np.linalg.norm(inv) < 1e-12
+    A = WL.spd_matrix(32, 50.0, 3)
+    X, hist = O.cg_pinv(A, 48)
+    assert np.linalg.norm(X - np.linalg.inv(A)) / np.linalg.norm(np.linalg.inv(A)) < 1e-12
+    wl = WL.PVT_S1
+    inp = WL.make_inputs(wl, seed=0)
+    L = O.landmark_pool(inp["Q"][0, 0], wl.H, wl.W, wl.r)
+    We = O.laplacian_kernel(L, L, wl.lam) + wl.eps * np.eye(len(L))
+    X, hist = O.cg_pinv(We, 2 * len(L))
+    assert hist[-1] < 1e-8 * np.sqrt(len(L))
+
+
+def test_cg_energy_error_decreases_and_first_step_is_the_line_search():
+    """CG minimises the W-norm of the error over growing Krylov spaces, so it never increases; its first step from
+    x = 0 is the exact line search along b: x_1 = (b.b / b.Wb) b, column by column."""
+    A = WL.spd_matrix(24, 50.0, 4)
+    inv = np.linalg.inv(A)
+    prev = None
+    for k in range(1, 20):
+        X, _ = O.cg_pinv(A, k)
+        E = X - inv
+        energy = float(np.sum(E * (A @ E)))
+        if prev is not None:
+            assert energy <= prev * (1 + 1e-12)
+        prev = energy
+    X1, _ = O.cg_pinv(A, 1)
+    expect = np.eye(24) * (1.0 / np.diag(A))  # b = e_j: b.b = 1, b.Wb = A_jj
+    assert np.allclose(X1, expect, rtol=1e-14, atol=0)
