@@ -14,6 +14,11 @@ followed by lf_attn_bwd_ex (dQ, dK, dV and the DWC weight and lambda gradients).
 buffer set, as the contract's value) it reports a "cold" one:
 the same steps rotating over enough input/output/workspace sets (>= 512 MB in all) that no step finds its data in
 the 256 MB last-level cache (--no-cold skips it).
+
+--solver measures the solver comparison of the pages instead (Newton-Schulz against conjugate gradients for
+W_eps X = I, at the workload's landmark matrices and at synthetic kappa = 50 SPD matrices of the same batch): one JSON
+line with, per solver and step count, the residual ||W_eps X - I||_F (mean and max over the batch), the matrix
+products spent and the time per launch (HIP events), and the CG kernel's MFMA roofline.
 """
 
 import argparse
@@ -42,6 +47,8 @@ COUNTER_LAUNCHES = 10
 # v_add_f32 with register operands reaches to 80 % (63 T measured). The distance kernel's v_sub_f32 and
 # v_add_f32 |.| are one operation each.
 VALU_PEAK_TFLOPS = 256 * 4 * 32 * 2.4e9 / 1e12
+# MI355X published dense fp32 MFMA peak.
+MFMA_F32_PEAK_TFLOPS = 157.3
 
 
 def laplace_source_hash():
@@ -151,6 +158,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall time budget of the oracle sample")
     ap.add_argument("--kernel-reps", type=int, default=100)
     ap.add_argument("--no-cold", action="store_true", help="skip the timing over rotating buffer sets")
+    ap.add_argument("--solver", action="store_true",
+                    help="measure Newton-Schulz against conjugate gradients on the workload's W_eps batch")
     ap.add_argument("--counters", action="store_true",
                     help="run only the distance kernel and a calibration copy (for rocprofv3 --pmc passes)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -187,6 +196,90 @@ def cpu_baseline(wl, inp, budget_s):
                       f"one thread, {dt:.1f} s"}
 
 
+def solver_compare(args):
+    import numpy as np
+    import torch
+
+    from laplacian_nystr_vit_amd import lf
+    from laplacian_nystr_vit_amd import workloads as WL
+
+    wl = WL.ALL[args.workload]
+    if wl.m > 64:
+        sys.exit(f"bench.py --solver: the CG kernel covers m <= 64 landmarks; {wl.name} has m = {wl.m}")
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    inp = WL.make_inputs(wl, seed=0)
+    dt = torch.bfloat16 if wl.dtype == WL.BF16 else torch.float32
+    p0 = lf.make_params(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.r, wl.lam, wl.eps, wl.ns_iters, False, 1e-5, dt)
+    G, N, m, d = p0.G, p0.N, p0.m, p0.d
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    # the workload's landmark matrices, by the library's pooling and distance stages
+    Q, K = dev(inp["Q_raw"]), dev(inp["K_raw"])
+    L = torch.empty(G * m * d, device="cuda")
+    CQ = torch.empty(G * N * m, device="cuda")
+    CK = torch.empty_like(CQ)
+    We = torch.empty(G * m * m, device="cuda")
+    lf.lf_landmark_pool(p0, Q, L, stream)
+    lf.lf_laplace_l1_exp(p0, Q, K, L, CQ, CK, We, stream)
+    torch.cuda.synchronize()
+    del CQ, CK
+    batches = {"landmark_W_eps": We.cpu().numpy().astype(np.float64).reshape(G, m, m),
+               "spd_kappa50": np.stack([WL.spd_matrix(m, 50.0, 1000 + g) for g in range(G)])}
+
+    def event_us(fn, reps):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    out = {"metric": "W_eps solver comparison: Newton-Schulz vs conjugate gradients (residual, products, us)",
+           "unit": "us per launch", "n_gpus": 1, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"{wl.name} W_eps batch", "G": G, "m": m}, "batches": {}}
+    X = torch.empty(G * m * m, device="cuda")
+    for name, W64 in batches.items():
+        Wd = torch.from_numpy(np.ascontiguousarray(W64.astype(np.float32))).cuda()
+        ev = np.linalg.eigvalsh(W64)
+        rows = {"kappa_mean": float(np.mean(ev[:, -1] / ev[:, 0])), "ns": [], "cg": []}
+        for K in (8, 12, 16, 20, 24):
+            p = lf.make_params(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.r, wl.lam, wl.eps, K, False, 1e-5, dt)
+            fwd_b, _, _ = lf.lf_attn_query(p)
+            ws = torch.empty(max(fwd_b, 1), dtype=torch.uint8, device="cuda")
+            res = torch.empty(G, device="cuda")
+            lf.lf_ns_pinv(p, Wd, X, None, None, res, ws, stream)
+            torch.cuda.synchronize()
+            r = res.cpu().numpy()
+            us = event_us(lambda: lf.lf_ns_pinv(p, Wd, X, None, None, None, ws, stream), args.kernel_reps)
+            rows["ns"].append({"steps": K, "products": 2 * K, "resid_mean": float(r.mean()),
+                               "resid_max": float(r.max()), "us": round(us, 2)})
+        p = p0
+        for k in (12, 24, 36, 49, 64, 98):
+            res = torch.empty(G * k, device="cuda")
+            lf.lf_cg_pinv(p, Wd, X, res, k, stream)
+            torch.cuda.synchronize()
+            r = res.view(G, k)[:, -1].cpu().numpy()
+            us = event_us(lambda: lf.lf_cg_pinv(p, Wd, X, None, k, stream), args.kernel_reps)
+            rows["cg"].append({"steps": k, "products": k, "resid_mean": float(r.mean()), "resid_max": float(r.max()),
+                               "us": round(us, 2)})
+        out["batches"][name] = rows
+    # CG kernel roofline: one W*P product (2 m^3 flops per slice) per step, at the longest run.
+    last = out["batches"]["spd_kappa50"]["cg"][-1]
+    flops = 2.0 * G * m ** 3 * last["steps"]
+    achieved = flops / (last["us"] * 1e-6) / 1e12
+    out["roofline"] = {"kernel": "cg_pinv", "bound": "mfma", "achieved": achieved, "peak": MFMA_F32_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": achieved / MFMA_F32_PEAK_TFLOPS, "traffic": None,
+                       "avg_us": last["us"], "flops_per_launch": flops}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.ingest_counters:
@@ -199,6 +292,9 @@ def main():
 
     if args.counters:
         counters_workload()
+        return
+    if args.solver:
+        solver_compare(args)
         return
 
     import numpy as np

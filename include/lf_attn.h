@@ -156,6 +156,17 @@ int lf_out_gemm_dwc(const lf_attn_params* p, const float* CQ, const float* P, co
 int lf_out_gemm_dwc_fused(const lf_attn_params* p, const void* Q, const float* L, const float* P, const void* V,
                           const float* dwc_w, void* Y, lf_stream_t stream);
 
+/* Conjugate gradients for W_eps X = I: the solver that [note] Design 3 (and the solver row of its ablation table)
+ * finds less robust than Newton-Schulz at a condition number of 50, provided to measure that claim. Column j of
+ * X[g] is the CG solve of W_eps[g] x = e_j from x = 0: r = e_j, p = r; each step a = r.r / p.(W p), x += a p,
+ * r -= a W p, p = r + (r'.r' / r.r) p. `iters` steps (0..LF_CG_ITERS_MAX), no early exit; a column whose r.r is
+ * exactly 0 holds still. We: [G][m][m] float32, meant to be symmetric positive definite (not checked); X: [G][m][m]
+ * float32 output. resid: NULL or [G][iters] float32 receiving ||W_eps X_k - I||_F after steps k = 1..iters,
+ * formed from X_k itself (a second product per step). p is validated as for every entry point; only its G and m
+ * are used, and m > 64 gives LF_EUNSUPPORTED. */
+#define LF_CG_ITERS_MAX 256
+int lf_cg_pinv(const lf_attn_params* p, const float* We, float* X, float* resid, int32_t iters, lf_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -303,6 +303,17 @@ int lf_ns_pinv(const lf_attn_params* p, const float* We, float* X, float* xs, fl
   return hip_status(lf::launch_ns(s, We, X, xs, alpha_out, resid, tmp, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int lf_cg_pinv(const lf_attn_params* p, const float* We, float* X, float* resid, int32_t iters, lf_stream_t stream) {
+  static_assert(LF_CG_ITERS_MAX == lf::kCgItersMax, "CG step limit of the header and the kernel differ");
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  if (!We || !X || !aligned16(We) || !aligned16(X) || (resid && !aligned16(resid))) return LF_EINVAL;
+  if (iters < 0 || iters > LF_CG_ITERS_MAX) return LF_EINVAL;
+  const lf::Shape s = make_shape(p);
+  if (!lf::cg_supported(s)) return LF_EUNSUPPORTED;
+  return hip_status(lf::launch_cg(s, We, X, resid, iters, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int lf_ckv_reduce(const lf_attn_params* p, const float* CK, const void* V, float* S, void* ws, size_t ws_bytes,
                   lf_stream_t stream) {
   const int rc = validate(p);

@@ -54,4 +54,10 @@ bool ns_side_supported(const Shape& s);
 hipError_t launch_ns_side(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
                           const void* V, float* S, hipStream_t st);
 
+// Conjugate gradients for W_eps X = I, one column per CG solve (cg_supported: 1 <= m <= 64). resid: NULL or
+// [G][iters] receiving ||W_eps X_k - I||_F after every step. iters <= kCgItersMax.
+constexpr int kCgItersMax = 256;
+bool cg_supported(const Shape& s);
+hipError_t launch_cg(const Shape& s, const float* We, float* X, float* resid, int iters, hipStream_t st);
+
 }  // namespace lf

@@ -26,9 +26,10 @@ LF_NS_ITERS_MAX = 64
 EXPORTS = (
     "lf_attn_query", "lf_attn_saved_layout", "lf_attn_fwd", "lf_attn_bwd", "lf_strerror", "lf_landmark_pool",
     "lf_laplace_l1_exp", "lf_ns_pinv", "lf_ckv_reduce", "lf_whiten_stats", "lf_landmark_mix", "lf_out_gemm_dwc",
-    "lf_out_gemm_dwc_fused", "lf_attn_bwd_ex",
+    "lf_out_gemm_dwc_fused", "lf_attn_bwd_ex", "lf_cg_pinv",
 )
 LF_BWD_EXACT_ALPHA = 1
+LF_CG_ITERS_MAX = 256
 
 
 class LfAttnParams(ctypes.Structure):
@@ -93,6 +94,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lf_landmark_mix": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp]),
         "lf_out_gemm_dwc": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
         "lf_out_gemm_dwc_fused": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+        "lf_cg_pinv": (ctypes.c_int, [_P, _vp, _vp, _vp, ctypes.c_int32, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -219,6 +221,13 @@ def lf_ns_pinv(p, We, X, xs, alpha, resid, ws, stream=None) -> None:
         ctypes.byref(p), _ptr(We, "We", f32, mm), _ptr(X, "X", f32, mm),
         _ptr(xs, "xs", f32, mm * (p.ns_iters + 1)), _ptr(alpha, "alpha", f32, p.G), _ptr(resid, "resid", f32, p.G),
         _ptr(ws, "ws"), _nbytes(ws), _stream(stream)), "lf_ns_pinv")
+
+
+def lf_cg_pinv(p, We, X, resid, iters, stream=None) -> None:
+    f32, mm = torch.float32, p.G * p.m * p.m
+    _check(load_library().lf_cg_pinv(
+        ctypes.byref(p), _ptr(We, "We", f32, mm), _ptr(X, "X", f32, mm),
+        _ptr(resid, "resid", f32, p.G * max(int(iters), 0)), int(iters), _stream(stream)), "lf_cg_pinv")
 
 
 def lf_ckv_reduce(p, CK, V, S, ws, stream=None) -> None:

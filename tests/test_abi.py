@@ -134,3 +134,16 @@ def test_bwd_ex_validates_flags_and_alignment_on_host(lib):
                               None, 0, fake, bwd, None) == lf.LF_EINVAL
     assert lib.lf_attn_bwd_ex(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, fake, None, None,
                               lf.LF_BWD_EXACT_ALPHA, fake, bwd - 1, None) == lf.LF_EWORKSPACE
+
+
+def test_cg_validates_on_host(lib):
+    """lf_cg_pinv rejects a step count outside 0..LF_CG_ITERS_MAX, misaligned pointers and m > 64 before launching."""
+    p = _p(WL.PVT_S1)
+    fake = ctypes.c_void_p(0x100000)
+    misaligned = ctypes.c_void_p(0x100004)
+    assert lib.lf_cg_pinv(ctypes.byref(p), fake, fake, None, -1, None) == lf.LF_EINVAL
+    assert lib.lf_cg_pinv(ctypes.byref(p), fake, fake, None, lf.LF_CG_ITERS_MAX + 1, None) == lf.LF_EINVAL
+    assert lib.lf_cg_pinv(ctypes.byref(p), fake, misaligned, None, 4, None) == lf.LF_EINVAL
+    assert lib.lf_cg_pinv(ctypes.byref(p), None, fake, None, 4, None) == lf.LF_EINVAL
+    assert lib.lf_cg_pinv(ctypes.byref(p), fake, fake, misaligned, 4, None) == lf.LF_EINVAL
+    assert lib.lf_cg_pinv(ctypes.byref(_p(WL.HIRES_BF16)), fake, fake, None, 4, None) == lf.LF_EUNSUPPORTED
