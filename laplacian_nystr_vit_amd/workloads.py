@@ -44,6 +44,7 @@ class Workload:
     whiten_eps: float = 1e-5
     backward: bool = False
     dwc: bool = True
+    kernel: str = "laplace"  # or "gauss": exp(-||x - y||_2^2 / lambda) in place of the Laplacian kernel
 
     @property
     def N(self) -> int:
@@ -78,8 +79,11 @@ HIRES_BF16 = Workload("hires_128x128_m256_bf16", B=2, heads=1, H=128, W=128, d=6
                       ns_iters=16, dtype=BF16)
 # Training step at the PVT stage-1 shape: diagonal whitening on, forward + backward.
 TRAIN_S1 = PVT_S1.replace(name="train_pvt_s1_56x56_m49", whiten=True, backward=True)
+# The Gaussian-kernel variant at the stage-1 shape. Its landmark matrix is far worse conditioned (kappa ~ 740
+# against ~ 13 for the Laplacian one on these inputs), so Newton-Schulz needs 24 steps to converge instead of 12.
+GAUSS_S1 = PVT_S1.replace(name="gauss_pvt_s1_56x56_m49", kernel="gauss", ns_iters=24)
 
-ALL = {w.name: w for w in (TINY, TINY_R1, PVT_S1, PVT_S3, HIRES_BF16, TRAIN_S1)}
+ALL = {w.name: w for w in (TINY, TINY_R1, PVT_S1, PVT_S3, HIRES_BF16, TRAIN_S1, GAUSS_S1)}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:

@@ -46,6 +46,9 @@ Readings where the pages are silent, ambiguous or wrong (each one is listed in t
   R8  no row normalisation and no 1/sqrt(d) scale; lambda is the only scale.
   R9  non-overlapping r x r pooling with stride r; H and W divisible by r; tokens row-major n = y*W + x.
   R10 DWC is a 3x3 cross-correlation, stride 1, zero padding 1, no bias, one filter per channel h*d + c.
+  R18 the Gaussian-kernel variant that the pages compare against (motivation: the Gaussian kernel decays with the
+      squared l2 distance) is k(x, y) = exp(-||x - y||_2^2 / lambda): the same lambda slot, nothing else
+      changed (same landmarks, eps shift, solver, whitening, DWC). Forward only.
 
 Layouts: Q, K, V, Y, dY are [B, heads, N, d] float64; the DWC weight is [heads*d, 3, 3].
 """
@@ -71,6 +74,7 @@ class Params:
     ns_iters: int
     whiten: bool = False
     whiten_eps: float = 1e-5
+    kernel: str = "laplace"  # or "gauss" (reading R18)
 
     @property
     def N(self) -> int:
@@ -107,6 +111,31 @@ def l1_distance(x: np.ndarray, y: np.ndarray, row_chunk: int = 512) -> np.ndarra
 def laplacian_kernel(x: np.ndarray, y: np.ndarray, lam: float) -> np.ndarray:
     """K[i, l] = exp(-||x_i - y_l||_1 / lambda)."""
     return np.exp(-l1_distance(x, y) / lam)
+
+
+# Gaussian-kernel variant  [note, motivation: the Gaussian kernel of earlier linear attentions decays with the
+# squared l2 distance; key findings, first item: swapping that kernel for the Laplacian one; reading R18]
+def sq_l2_distance(x: np.ndarray, y: np.ndarray, row_chunk: int = 512) -> np.ndarray:
+    """D[i, l] = sum_c (x[i, c] - y[l, c])^2 from the differences themselves, in row chunks."""
+    out = np.empty((x.shape[0], y.shape[0]), dtype=np.float64)
+    for s in range(0, x.shape[0], row_chunk):
+        diff = x[s:s + row_chunk][:, None, :] - y[None, :, :]
+        out[s:s + row_chunk] = (diff * diff).sum(axis=2)
+    return out
+
+
+def gaussian_kernel(x: np.ndarray, y: np.ndarray, lam: float) -> np.ndarray:
+    """K[i, l] = exp(-||x_i - y_l||_2^2 / lambda)."""
+    return np.exp(-sq_l2_distance(x, y) / lam)
+
+
+def kernel_of(p: "Params"):
+    """The similarity kernel a parameter set names: Laplacian (the method) or Gaussian (the variant, R18)."""
+    if p.kernel == "laplace":
+        return laplacian_kernel
+    if p.kernel == "gauss":
+        return gaussian_kernel
+    raise ValueError(f"unknown kernel {p.kernel!r}")
 
 
 # ----------------------------------------------------------------------------------------------------------
@@ -225,9 +254,10 @@ def dwc_adjoint(u: np.ndarray, w: np.ndarray, H: int, W: int) -> np.ndarray:
 def forward_slice(q, k, v, w_dwc, p: Params, alpha: Optional[float] = None) -> Dict[str, np.ndarray]:
     """Forward of one (batch, head) slice. w_dwc is this head's [d, 3, 3] filter bank or None."""
     L = landmark_pool(q, p.H, p.W, p.r)
-    CQ = laplacian_kernel(q, L, p.lam)
-    CK = laplacian_kernel(k, L, p.lam)
-    Wm = laplacian_kernel(L, L, p.lam)
+    kern = kernel_of(p)
+    CQ = kern(q, L, p.lam)
+    CK = kern(k, L, p.lam)
+    Wm = kern(L, L, p.lam)
     We = Wm + p.eps * np.eye(L.shape[0])
     X, xs, alpha = newton_schulz(We, p.ns_iters, alpha)
     if p.whiten:
@@ -254,8 +284,10 @@ def backward_slice(q, k, v, w_dwc, dy, p: Params, fwd: Optional[Dict] = None,
     Chain rule through the forward steps, last step first. The kernel derivative is reading R4:
     d/dx exp(-||x-y||_1/lambda) = -(1/lambda) sign(x - y) exp(...), and +(1/lambda) sign(x - y) exp(...) in y.
     In lambda: d/dlambda exp(-D/lambda) = exp(-D/lambda) D / lambda^2 for the distance D. alpha is held constant
-    (reading R6) unless exact_alpha is set.
+    (reading R6) unless exact_alpha is set. The Gaussian-kernel variant has no backward here (reading R18).
     """
+    if p.kernel != "laplace":
+        raise NotImplementedError("the Gaussian-kernel variant is forward only")
     f = fwd if fwd is not None else forward_slice(q, k, v, w_dwc, p, alpha)
     A, P, S, X, xs, We = f["A"], f["P"], f["S"], f["X"], f["xs"], f["We"]
     CQ, CK, Wm, L = f["CQ"], f["CK"], f["W"], f["L"]

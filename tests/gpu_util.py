@@ -35,7 +35,7 @@ def params(wl, **kw) -> lf.LfAttnParams:
 
 def oparams(wl) -> O.Params:
     return O.Params(B=wl.B, heads=wl.heads, H=wl.H, W=wl.W, d=wl.d, r=wl.r, lam=wl.lam, eps=wl.eps,
-                    ns_iters=wl.ns_iters, whiten=wl.whiten, whiten_eps=wl.whiten_eps)
+                    ns_iters=wl.ns_iters, whiten=wl.whiten, whiten_eps=wl.whiten_eps, kernel=wl.kernel)
 
 
 def dev(x: np.ndarray, dtype=None) -> torch.Tensor:

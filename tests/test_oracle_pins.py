@@ -35,7 +35,7 @@ def _ev(expr, **env):
 
 def _params(wl, **kw):
     p = O.Params(B=wl.B, heads=wl.heads, H=wl.H, W=wl.W, d=wl.d, r=wl.r, lam=wl.lam, eps=wl.eps,
-                 ns_iters=wl.ns_iters, whiten=wl.whiten, whiten_eps=wl.whiten_eps)
+                 ns_iters=wl.ns_iters, whiten=wl.whiten, whiten_eps=wl.whiten_eps, kernel=wl.kernel)
     for k, v in kw.items():
         setattr(p, k, v)
     return p
@@ -564,3 +564,77 @@ def test_cg_energy_error_decreases_and_first_step_is_the_line_search():
     X1, _ = O.cg_pinv(A, 1)
     expect = np.eye(24) * (1.0 / np.diag(A))  # b = e_j: b.b = 1, b.Wb = A_jj
     assert np.allclose(X1, expect, rtol=1e-14, atol=0)
+
+
+# ------------------------------------------------------------------------------------- Gaussian-kernel variant
+def test_gaussian_kernel_bruteforce():
+    rng = _rng(30)
+    x, y, lam = rng.standard_normal((7, 5)), rng.standard_normal((4, 5)), 4.0
+    K = O.gaussian_kernel(x, y, lam)
+    for i in range(7):
+        for l in range(4):
+            ref = math.exp(-math.fsum((x[i, c] - y[l, c]) ** 2 for c in range(5)) / lam)
+            assert abs(K[i, l] - ref) <= 1e-15 * ref + 1e-300
+
+
+def test_gaussian_kernel_identity_symmetry_scale_separable_and_definite():
+    rng = _rng(31)
+    x = rng.standard_normal((9, 6))
+    Kxx = O.gaussian_kernel(x, x, 3.0)
+    assert np.array_equal(np.diag(Kxx), np.ones(9)) and np.array_equal(Kxx, Kxx.T)
+    y = rng.standard_normal((4, 6))
+    # k(s x, s y; s^2 lambda) = k(x, y; lambda): the distance is squared
+    assert np.allclose(O.gaussian_kernel(3 * x, 3 * y, 27.0), O.gaussian_kernel(x, y, 3.0), rtol=1e-13)
+    # separable: the kernel is the product over coordinates of one-dimensional kernels
+    prod = np.ones((9, 4))
+    for c in range(6):
+        prod *= O.gaussian_kernel(x[:, c:c + 1], y[:, c:c + 1], 3.0)
+    assert np.allclose(O.gaussian_kernel(x, y, 3.0), prod, rtol=1e-13)
+    # the Gram matrix of distinct points is positive definite
+    assert np.linalg.eigvalsh(Kxx).min() > 0
+
+
+def test_gaussian_variant_changes_only_the_kernel():
+    """kernel = "gauss" swaps C_Q, C_K and W for their Gaussian versions and keeps every other step: the landmarks
+    are the same, W_eps is the Gaussian Gram matrix of the landmarks plus eps I, and the Nystrom output follows
+    from those with the same solver. Also translation invariant, like the Laplacian block."""
+    wl = WL.TINY
+    inp = WL.make_inputs(wl, seed=5)
+    q, k, v = inp["Q"][0, 0], inp["K"][0, 0], inp["V"][0, 0]
+    fl = O.forward_slice(q, k, v, None, _params(wl))
+    fg = O.forward_slice(q, k, v, None, _params(wl, kernel="gauss"))
+    assert np.array_equal(fl["L"], fg["L"])
+    L = fg["L"]
+    G = np.array([[math.exp(-math.fsum((L[a, c] - L[b, c]) ** 2 for c in range(wl.d)) / wl.lam)
+                   for b in range(wl.m)] for a in range(wl.m)])
+    assert np.allclose(fg["We"], G + wl.eps * np.eye(wl.m), rtol=1e-14, atol=0)
+    X, _, _ = O.newton_schulz(fg["We"], wl.ns_iters)
+    Y = fg["CQ"] @ X @ (fg["CK"].T @ v)
+    assert np.linalg.norm(fg["Yattn"] - Y) / np.linalg.norm(Y) < 1e-12
+    assert np.linalg.norm(fg["Yattn"] - fl["Yattn"]) > 1e-3 * np.linalg.norm(fl["Yattn"])
+    shift = _rng(6).standard_normal(wl.d)
+    f1 = O.forward_slice(q + shift, k + shift, v, None, _params(wl, kernel="gauss"))
+    for key in ("CQ", "CK", "We", "Yattn"):
+        assert np.allclose(fg[key], f1[key], rtol=1e-11, atol=1e-14), key
+
+
+def test_gaussian_nystrom_r1_equals_regularised_exact_kernel():
+    """r = 1 with the Gaussian kernel: Y_attn = W (W + eps I)^-1 G V with G_ij = exp(-||q_i - k_j||^2 / lambda)."""
+    wl = WL.TINY_R1
+    inp = WL.make_inputs(wl, seed=0)
+    p = _params(wl, kernel="gauss", ns_iters=40)
+    q, k, v = inp["Q"][0, 0], inp["K"][0, 0], inp["V"][0, 0]
+    f = O.forward_slice(q, k, v, None, p)
+    G = np.array([[math.exp(-math.fsum((q[i, c] - k[j, c]) ** 2 for c in range(wl.d)) / wl.lam)
+                   for j in range(wl.N)] for i in range(wl.N)])
+    Wm = f["W"]
+    closed = Wm @ np.linalg.solve(Wm + wl.eps * np.eye(wl.N), G @ v)
+    assert np.linalg.norm(f["Yattn"] - closed) / np.linalg.norm(closed) < 1e-9
+
+
+def test_gaussian_variant_has_no_backward():
+    wl = WL.TINY
+    inp = WL.make_inputs(wl, seed=0, with_dy=True)
+    with pytest.raises(NotImplementedError):
+        O.backward_slice(inp["Q"][0, 0], inp["K"][0, 0], inp["V"][0, 0], None, inp["dY"][0, 0],
+                         _params(wl, kernel="gauss"))
