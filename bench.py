@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 
 METRIC = "Laplacian-Nyström attention fwd tokens/s (B·heads·N) + % VALU/MFMA roofline"
 METRIC_TRAIN = "Laplacian-Nyström attention fwd+bwd tokens/s (B·heads·N) + % VALU/MFMA roofline"
+METRIC_GAUSS = "Gaussian-kernel Nyström attention fwd tokens/s (B·heads·N) + % MFMA roofline"
 COLD_BYTES = 512 << 20
 
 # HBM traffic of the distance kernel, from two rocprofv3 counter passes over `bench.py --counters` (FETCH_SIZE,
@@ -175,7 +176,7 @@ def cpu_baseline(wl, inp, budget_s):
     import oracle as O
 
     op = O.Params(B=wl.B, heads=wl.heads, H=wl.H, W=wl.W, d=wl.d, r=wl.r, lam=wl.lam, eps=wl.eps,
-                  ns_iters=wl.ns_iters, whiten=wl.whiten, whiten_eps=wl.whiten_eps)
+                  ns_iters=wl.ns_iters, whiten=wl.whiten, whiten_eps=wl.whiten_eps, kernel=wl.kernel)
     train = bool(wl.whiten)
     slices = 0
     t0 = time.perf_counter()
@@ -196,6 +197,11 @@ def cpu_baseline(wl, inp, budget_s):
                       f"one thread, {dt:.1f} s"}
 
 
+def distance_stage(wl, lf):
+    """The stage entry point that forms C_Q, C_K and W_eps for the workload's kernel."""
+    return lf.lf_gauss_l2_exp if wl.kernel == "gauss" else lf.lf_laplace_l1_exp
+
+
 def solver_compare(args):
     import numpy as np
     import torch
@@ -210,7 +216,8 @@ def solver_compare(args):
     stream = torch.cuda.current_stream()
     inp = WL.make_inputs(wl, seed=0)
     dt = torch.bfloat16 if wl.dtype == WL.BF16 else torch.float32
-    p0 = lf.make_params(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.r, wl.lam, wl.eps, wl.ns_iters, False, 1e-5, dt)
+    p0 = lf.make_params(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.r, wl.lam, wl.eps, wl.ns_iters, False, 1e-5, dt,
+                        wl.kernel)
     G, N, m, d = p0.G, p0.N, p0.m, p0.d
 
     def dev(x):
@@ -225,7 +232,7 @@ def solver_compare(args):
     CK = torch.empty_like(CQ)
     We = torch.empty(G * m * m, device="cuda")
     lf.lf_landmark_pool(p0, Q, L, stream)
-    lf.lf_laplace_l1_exp(p0, Q, K, L, CQ, CK, We, stream)
+    distance_stage(wl, lf)(p0, Q, K, L, CQ, CK, We, stream)
     torch.cuda.synchronize()
     del CQ, CK
     batches = {"landmark_W_eps": We.cpu().numpy().astype(np.float64).reshape(G, m, m),
@@ -250,7 +257,7 @@ def solver_compare(args):
         ev = np.linalg.eigvalsh(W64)
         rows = {"kappa_mean": float(np.mean(ev[:, -1] / ev[:, 0])), "ns": [], "cg": []}
         for K in (8, 12, 16, 20, 24):
-            p = lf.make_params(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.r, wl.lam, wl.eps, K, False, 1e-5, dt)
+            p = lf.make_params(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.r, wl.lam, wl.eps, K, False, 1e-5, dt, wl.kernel)
             fwd_b, _, _ = lf.lf_attn_query(p)
             ws = torch.empty(max(fwd_b, 1), dtype=torch.uint8, device="cuda")
             res = torch.empty(G, device="cuda")
@@ -314,7 +321,7 @@ def main():
         return torch.from_numpy(x).cuda()
 
     p = lf.make_params(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.r, wl.lam, wl.eps, wl.ns_iters, wl.whiten, wl.whiten_eps,
-                       dt)
+                       dt, wl.kernel)
     train = bool(wl.whiten)
     fwd_b, saved_b, bwd_b = lf.lf_attn_query(p)
     stream = torch.cuda.current_stream()
@@ -370,27 +377,40 @@ def main():
                 "bytes_per_set": set_bytes}
         del sets
 
-    # Dominant kernel: laplace_l1_exp, through its own entry point on the same stream, bracketed by HIP events.
+    # Dominant kernel: the distance stage (laplace_l1_exp, or gauss_l2_exp for the Gaussian variant), through its
+    # own entry point on the same stream, bracketed by HIP events.
     G, N, m, d = p.G, p.N, p.m, p.d
+    gauss = wl.kernel == "gauss"
+    dist = distance_stage(wl, lf)
     L = torch.empty(G * m * d, device="cuda")
     CQ = torch.empty(G * N * m, device="cuda")
     CK = torch.empty_like(CQ)
     We = torch.empty(G * m * m, device="cuda")
     lf.lf_landmark_pool(p, Q, L, stream)
     for _ in range(5):
-        lf.lf_laplace_l1_exp(p, Q, K, L, CQ, CK, We, stream)
+        dist(p, Q, K, L, CQ, CK, We, stream)
     # Back-to-back launches between two events on the kernel's own stream: the average is the kernel's duration
     # (the GPU never idles between launches), which is what rocprofv3's kernel trace reports for it.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.kernel_reps):
-        lf.lf_laplace_l1_exp(p, Q, K, L, CQ, CK, We, stream)
+        dist(p, Q, K, L, CQ, CK, We, stream)
     e1.record(stream)
     torch.cuda.synchronize()
     lap_us = e0.elapsed_time(e1) / args.kernel_reps * 1e3
-    # Algorithmic work: per (row, landmark, channel) one subtract and one |.|-add, over 2N + m rows per slice.
+    # Algorithmic work over the 2N + m rows per slice, per (row, landmark, channel): Laplacian, one subtract and one
+    # |.|-add (VALU operations); Gaussian, one multiply-add of x.l (2 flops, fp32 MFMA).
     ops = 2.0 * G * (2 * N + m) * m * d
     achieved = ops / (lap_us * 1e-6) / 1e12
+    if gauss:
+        roof = {"kernel": "gauss_l2_exp", "bound": "mfma", "achieved": achieved, "peak": MFMA_F32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_F32_PEAK_TFLOPS, "traffic": None, "avg_us": lap_us,
+                "flops_per_launch": ops}
+    else:
+        roof = {"kernel": "laplace_l1_exp", "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / VALU_PEAK_TFLOPS,
+                "traffic": load_traffic() if args.workload == "pvt_s1_56x56_m49" else None,
+                "avg_us": lap_us, "ops_per_launch": ops}
 
     # Per-stage event times (each stage entry point alone, same stream), for context.
     stages = {}
@@ -409,14 +429,14 @@ def main():
     S = torch.empty(G * m * d, device="cuda")
     P = torch.empty(G * m * d, device="cuda")
     time_stage("landmark_pool", lambda: lf.lf_landmark_pool(p, Q, L, stream))
-    time_stage("laplace_l1_exp", lambda: lf.lf_laplace_l1_exp(p, Q, K, L, CQ, CK, We, stream))
+    time_stage("gauss_l2_exp" if gauss else "laplace_l1_exp", lambda: dist(p, Q, K, L, CQ, CK, We, stream))
     time_stage("ns_pinv", lambda: lf.lf_ns_pinv(p, We, X, None, None, None, ws, stream))
     time_stage("ckv_reduce", lambda: lf.lf_ckv_reduce(p, CK, V, S, ws, stream))
     time_stage("landmark_mix", lambda: lf.lf_landmark_mix(p, X, S, None, P, stream))
     time_stage("out_gemm_dwc", lambda: lf.lf_out_gemm_dwc(p, CQ, P, None, V, w, Y, stream))
 
     rec = {
-        "metric": METRIC_TRAIN if train else METRIC,
+        "metric": METRIC_TRAIN if train else (METRIC_GAUSS if gauss else METRIC),
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -428,13 +448,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if wl.dtype == WL.F32 else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name} {'forward+backward' if train else 'forward'}", "B": wl.B, "heads": wl.heads, "H": wl.H, "W": wl.W, "d": wl.d,
-                   "r": wl.r, "m": wl.m, "lambda": wl.lam, "eps": wl.eps, "ns_iters": wl.ns_iters,
-                   "tokens_per_step": wl.tokens},
-        "roofline": {"kernel": "laplace_l1_exp", "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / VALU_PEAK_TFLOPS,
-                     "traffic": load_traffic() if args.workload == "pvt_s1_56x56_m49" else None,
-                     "avg_us": lap_us, "ops_per_launch": ops},
+        "config": {"workload": f"{wl.name} {'forward+backward' if train else 'forward'}", "B": wl.B,
+                   "heads": wl.heads, "H": wl.H, "W": wl.W, "d": wl.d, "r": wl.r, "m": wl.m, "lambda": wl.lam,
+                   "eps": wl.eps, "ns_iters": wl.ns_iters, "kernel": wl.kernel, "tokens_per_step": wl.tokens},
+        "roofline": roof,
         "stages_us": stages,
     }
     if cold is not None:

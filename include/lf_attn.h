@@ -52,6 +52,13 @@ enum lf_status {
 
 enum lf_dtype { LF_F32 = 0, LF_BF16 = 1 };
 
+/* Similarity kernel of the block. LF_KERNEL_LAPLACE is the method: k(x,y) = exp(-||x-y||_1/lambda) ([note]
+ * motivation, "core idea"). LF_KERNEL_GAUSS is the kernel the note sets it against (its motivation: the Gaussian
+ * kernel of earlier linear attentions decays with the squared l2 distance; its key findings: replacing it by the
+ * Laplacian one): k(x,y) = exp(-||x-y||_2^2/lambda), with every other step unchanged. The Gaussian variant is
+ * forward only (backward and the fused output stage return LF_EUNSUPPORTED). */
+enum lf_kernel { LF_KERNEL_LAPLACE = 0, LF_KERNEL_GAUSS = 1 };
+
 #define LF_M_MAX 256
 #define LF_NS_ITERS_MAX 64
 
@@ -64,6 +71,8 @@ typedef struct lf_attn_params {
   int32_t whiten;            /* 0 or 1: diagonal whitening of C_Q's landmark columns ([note] Design 1) */
   float whiten_eps;          /* > 0, added to the column variance when whiten = 1 */
   int32_t dtype;             /* LF_F32 or LF_BF16: type of Q, K, V, Y, dY, dQ, dK, dV */
+  int32_t kernel;            /* LF_KERNEL_LAPLACE (0, a zero-initialised struct) or LF_KERNEL_GAUSS: the kernel
+                                lf_attn_fwd uses for C_Q, C_K and W */
 } lf_attn_params;
 
 /* Byte offsets of the intermediates inside the `saved` buffer written by lf_attn_fwd (each 256-byte aligned).
@@ -80,7 +89,7 @@ int lf_attn_query(const lf_attn_params* p, size_t* fwd_ws_bytes, size_t* saved_b
 /* Layout of the saved buffer (host-only). */
 int lf_attn_saved_layout(const lf_attn_params* p, lf_saved_layout* out);
 
-/* Forward pass ([note] framework flowchart; Designs 1-3):
+/* Forward pass ([note] framework flowchart; Designs 1-3), k the kernel p->kernel names:
  *   L = pool_r(Q); C_Q = k(Q, L); C_K = k(K, L); W_eps = k(L, L) + eps I; X = NS^{ns_iters}(W_eps);
  *   A_hat = C_Q, or its whitened form when whiten = 1; Y = A_hat X (C_K^T V) + DWC(V).
  * dwc_w: [heads*d][3][3] float32, or NULL for the attention branch alone (Y = A_hat X C_K^T V).
@@ -92,7 +101,7 @@ int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const voi
 /* Backward pass of <dY, Y> with respect to Q, K and V ([abs]: forward and backward; [note] motivation "core idea"
  * for the kernel gradient, with the sign read as d/dx exp(-||x-y||_1/lambda) = -(1/lambda) sign(x-y) k).
  * saved: the buffer filled by lf_attn_fwd with the same params and inputs. ws: at least bwd_ws_bytes.
- * dQ, dK, dV are overwritten. Supports m <= 64 and d <= 64 (LF_EUNSUPPORTED otherwise). */
+ * dQ, dK, dV are overwritten. Supports m <= 64, d <= 64 and the Laplacian kernel (LF_EUNSUPPORTED otherwise). */
 int lf_attn_bwd(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
                 const void* saved, const void* dY, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
                 lf_stream_t stream);
@@ -124,6 +133,14 @@ int lf_landmark_pool(const lf_attn_params* p, const void* Q, float* L, lf_stream
 int lf_laplace_l1_exp(const lf_attn_params* p, const void* Q, const void* K, const float* L, float* CQ, float* CK,
                       float* We, lf_stream_t stream);
 
+/* The Gaussian-kernel variant of the same stage (see lf_kernel): C_Q[g][l][i] = exp(-||Q[g][i] - L[g][l]||_2^2 /
+ * lambda) (landmark-major), C_K likewise with K, W_eps[g][l][l'] = exp(-||L_l - L_l'||_2^2 / lambda) + eps [l == l'].
+ * C_Q and C_K come from ||x||^2 + ||l||^2 - 2 x.l (fp32 MFMA for x.l, clamped at 0); W_eps from the differences,
+ * so it is exactly symmetric with a unit diagonal before the shift. Computes the Gaussian kernel whatever
+ * p->kernel holds; same layouts, pointer rules and errors as lf_laplace_l1_exp. */
+int lf_gauss_l2_exp(const lf_attn_params* p, const void* Q, const void* K, const float* L, float* CQ, float* CK,
+                    float* We, lf_stream_t stream);
+
 /* Newton-Schulz pseudo-inverse ([note] Design 3): alpha = 1/(||W_eps||_1 ||W_eps||_inf), X_0 = alpha W_eps^T,
  * X_{k+1} = X_k (2I - W_eps X_k) for p->ns_iters steps. X: [G][m][m] receives X_{ns_iters}.
  * xs: NULL or [G][ns_iters+1][m][m] receiving X_0..X_{ns_iters}; alpha_out: NULL or [G];
@@ -152,7 +169,8 @@ int lf_out_gemm_dwc(const lf_attn_params* p, const float* CQ, const float* P, co
 /* The same output without a materialised C_Q (no whitening): every 8 x 8 token tile computes its C_Q block
  * exp(-||q_i - l||_1 / lambda) from Q [B][heads][N][d] (the dtype of p) and the landmarks L [G][m][d] fp32, then
  * Y = C_Q P + DWC(V). Distance fused with the product, as the output stage of [note] Design 3 suggests to save
- * memory traffic. Same conventions and errors as lf_out_gemm_dwc. */
+ * memory traffic. Same conventions and errors as lf_out_gemm_dwc; p->kernel must be LF_KERNEL_LAPLACE
+ * (LF_EUNSUPPORTED otherwise). */
 int lf_out_gemm_dwc_fused(const lf_attn_params* p, const void* Q, const float* L, const float* P, const void* V,
                           const float* dwc_w, void* Y, lf_stream_t stream);
 

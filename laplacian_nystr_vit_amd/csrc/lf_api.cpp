@@ -1,5 +1,5 @@
 // C ABI of liblf_attn: parameter validation, workspace planning and the launch sequence of the forward and
-// backward passes. Host code only; the kernels live in lf_fwd.hip, lf_ns.hip and lf_bwd.hip.
+// backward passes. Host code only; the kernels live in lf_fwd.hip, lf_ns.hip, lf_bwd.hip, lf_cg.hip and lf_gauss.hip.
 #include <hip/hip_runtime_api.h>
 
 #include <cmath>
@@ -27,6 +27,7 @@ int validate(const lf_attn_params* p) {
   if (p->whiten != 0 && p->whiten != 1) return LF_EINVAL;
   if (p->whiten == 1 && (!(p->whiten_eps > 0.f) || !std::isfinite(p->whiten_eps))) return LF_EINVAL;
   if (p->dtype != LF_F32 && p->dtype != LF_BF16) return LF_EINVAL;
+  if (p->kernel != LF_KERNEL_LAPLACE && p->kernel != LF_KERNEL_GAUSS) return LF_EINVAL;
   // Sizes: keep every element index inside int range for the per-slice arithmetic, and totals in size_t.
   const int64_t N = static_cast<int64_t>(p->H) * p->W;
   if (N > (1 << 24)) return LF_EUNSUPPORTED;
@@ -209,7 +210,10 @@ int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const voi
   // far the distance launch plus the output GEMM beats recomputing C_Q inside the output kernel
   // (lf_out_gemm_dwc_fused).
   LF_TRY(lf::launch_landmark_pool(s, Q, L, st));
-  LF_TRY(lf::launch_laplace(s, Q, K, L, CQ, CK, We, st));
+  if (p->kernel == LF_KERNEL_GAUSS)
+    LF_TRY(lf::launch_gauss(s, Q, K, L, CQ, CK, We, st));
+  else
+    LF_TRY(lf::launch_laplace(s, Q, K, L, CQ, CK, We, st));
   if (wh) LF_TRY(lf::launch_whiten_stats(s, CQ, mu, rstd, st));
   if (lf::ns_side_supported(s)) {
     // One launch: Newton-Schulz on G CUs, S = C_K^T V on the others.
@@ -242,7 +246,7 @@ int lf_attn_bwd_ex(const lf_attn_params* p, const void* Q, const void* K, const 
   const int rc = validate(p);
   if (rc != LF_OK) return rc;
   const lf::Shape s = make_shape(p);
-  if (s.m > 64 || s.d > 64) return LF_EUNSUPPORTED;
+  if (s.m > 64 || s.d > 64 || p->kernel != LF_KERNEL_LAPLACE) return LF_EUNSUPPORTED;
   if (!Q || !K || !V || !saved || !dY || !dQ || !dK || !dV || !ws) return LF_EINVAL;
   const void* ptrs[] = {Q, K, V, saved, dY, dQ, dK, dV, ws};
   for (const void* ptr : ptrs)
@@ -287,6 +291,16 @@ int lf_laplace_l1_exp(const lf_attn_params* p, const void* Q, const void* K, con
   for (const void* ptr : ptrs)
     if (!ptr || !aligned16(ptr)) return LF_EINVAL;
   return hip_status(lf::launch_laplace(make_shape(p), Q, K, L, CQ, CK, We, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int lf_gauss_l2_exp(const lf_attn_params* p, const void* Q, const void* K, const float* L, float* CQ, float* CK,
+                    float* We, lf_stream_t stream) {
+  const int rc = validate(p);
+  if (rc != LF_OK) return rc;
+  const void* ptrs[] = {Q, K, L, CQ, CK, We};
+  for (const void* ptr : ptrs)
+    if (!ptr || !aligned16(ptr)) return LF_EINVAL;
+  return hip_status(lf::launch_gauss(make_shape(p), Q, K, L, CQ, CK, We, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int lf_ns_pinv(const lf_attn_params* p, const float* We, float* X, float* xs, float* alpha_out, float* resid,
@@ -349,6 +363,7 @@ int lf_out_gemm_dwc_fused(const lf_attn_params* p, const void* Q, const float* L
   if (!Q || !L || !P || !V || !Y) return LF_EINVAL;
   if (!aligned16(Q) || !aligned16(L) || !aligned16(P) || !aligned16(V) || !aligned16(Y)) return LF_EINVAL;
   if (dwc_w && !aligned16(dwc_w)) return LF_EINVAL;
+  if (p->kernel != LF_KERNEL_LAPLACE) return LF_EUNSUPPORTED;
   return hip_status(
       lf::launch_out_fused(make_shape(p), Q, L, P, V, dwc_w, Y, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -23,6 +23,10 @@ hipError_t launch_landmark_pool(const Shape& s, const void* Q, float* L, hipStre
 // srcmask selects the row sources: 1 = Q rows (C_Q), 2 = K rows (C_K), 4 = landmark rows (W_eps).
 hipError_t launch_laplace(const Shape& s, const void* Q, const void* K, const float* L, float* CQ, float* CK,
                           float* We, hipStream_t st, int srcmask = 7);
+// Gaussian-kernel variant of launch_laplace (all three sources): C_Q, C_K from ||x||^2 + ||l||^2 - 2 x.l on fp32
+// MFMA, W_eps from the differences.
+hipError_t launch_gauss(const Shape& s, const void* Q, const void* K, const float* L, float* CQ, float* CK,
+                        float* We, hipStream_t st);
 hipError_t launch_whiten_stats(const Shape& s, const float* CQ, float* mu, float* rstd, hipStream_t st);
 hipError_t launch_ckv(const Shape& s, const float* CK, const void* V, float* partial, float* S, hipStream_t st);
 // Same reduction with an optional appended column of ones in C (ones = 1): S gets m + ones rows.

@@ -148,6 +148,10 @@ __device__ __forceinline__ int exp_of(float v) {
 // Storage exponent for an iterate whose largest entry is about mx: entries land in [2^12, 2^13).
 __device__ __forceinline__ int store_exp(float mx) { return mx > 0.f ? exp_of(mx) - 12 : 0; }
 constexpr int kRestoreExp = 15;  // an entry at or above 2^15 * 2^e triggers a re-store with a fresh exponent
+// Longest run of coupled T/X steps before T is formed again as W X: 2^kPairRun times the relative rounding of
+// one product must stay well below 1 (split-fp16 products: 2^-22; the fp32 products of the m > 64 path: 2^-24).
+constexpr int kPairRun = 11;
+constexpr int kPairRunF32 = 12;
 
 // Maximum over the wave of a non-negative value, returned wave-uniform: DPP steps inside each row of 16 lanes
 // (quad swaps, then rotations by 4 and 8), then the four row results through scalar registers.
@@ -380,9 +384,12 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
   // The exact Newton-Schulz step X_{k+1} = X_k (2I - W X_k) equals, for T_k = W X_k, the pair
   //   T_{k+1} = T_k (2I - T_k),  X_{k+1} = X_k (2I - T_k),
   // whose two products share U_k = 2I - T_k and depend only on step k: one phase and one barrier per step
-  // instead of two. Carrying T separately drops the self-correction of the exact step (rounding in T is never
-  // compared with W X again), so steps 0 .. K-2 use the pair and the last step is the exact update from
-  // X_{K-1}, which restores it; in fp32 the result then tracks the exact-step iteration to rounding.
+  // instead of two. Carrying T separately drops the self-correction of the exact step: a mismatch D = T - W X
+  // becomes D (2I - T) in the next step, so it can double per step while T has eigenvalues far below 1, about
+  // 1 / (alpha mu_min^2) ~ kappa^2 overall. Pair steps therefore run in segments of at most kPairRun, each
+  // starting from T = W X formed afresh (the mismatch stays below 2^kPairRun times the rounding of one split
+  // product, 2^-22), and the last step is the exact update from X_{K-1}, which squares what is left; the result
+  // then tracks the exact-step iteration to rounding.
   int e_cur = store_exp(alpha * s_wmax);  // storage exponent of the iterate in sX[cur]; X_0's max is alpha max|W|
   const int xcol_first = 1;               // buffer of sT that receives X_0 by columns
   if (xw) {
@@ -393,26 +400,30 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
   __syncthreads();
 
   f32x4 accA[TQ][TQ], accB[TQ][TQ], accC[TQ][TQ];
-  if (iters >= 2) {
-    // T_0 = W X_0: by columns (into U_0 = 2I - T_0) and, with the operands swapped, by rows.
+  int xcol_buf = xcol_first;  // where the latest X by columns sits (the segment start and the exact step read it)
+  // Segment start at step k: T_k = W X_k by columns (into U_k = 2I - T_k) and, with the operands swapped, by rows.
+  // After the first segment, X_k by columns sits in sT[k & 1], the buffer T_k goes to: every T wave loads its
+  // fragments before any of them stores.
+  auto resync = [&](int k) {
+    const int cur = k & 1;
+    Frags<TQ, KC> fxc;
+    if (tw) frags_of(sT[xcol_buf], c0, fxc);
+    if (xcol_buf == cur) __syncthreads();
     if (tw) {
-      Frags<TQ, KC> fxc;
-      frags_of(sT[xcol_first], c0, fxc);
       mma(fw, fxc, accA);
       mma(fxc, fw, accB);
       const float unscale = ldexpf(1.f, e_cur);
-      put_u(sU[0], accA, unscale);
-      put_rows(sT[0], accB, unscale);
+      put_u(sU[cur], accA, unscale);
+      put_rows(sT[cur], accB, unscale);
     }
     __syncthreads();
-  }
+  };
 
   int e_next = e_cur;
-  int xcol_buf = xcol_first;  // where X_{K-1} by columns sits for the exact step
   // One pair step; the buffer parity is a template constant so that every LDS address is a fixed offset.
-  auto step = [&](auto parity, int k) __attribute__((always_inline)) {
+  // last: the step ends a segment, so it produces X_{k+1} by columns as well and no T_{k+1} / U_{k+1}.
+  auto step = [&](auto parity, int k, bool last) __attribute__((always_inline)) {
     constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
-    const bool last = k + 2 == iters;  // produces X_{K-1}: also by columns, and T_{K-1} / U_{K-1} are not needed
     const float unscale = ldexpf(1.f, e_cur);
     if (xw) {
       Frags<TQ, KC> fu, fx;
@@ -454,9 +465,15 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
     e_next = store_exp(mx);
     if (last) xcol_buf = nxt;
   };
-  for (int k = 0; k + 1 < iters; k += 2) {
-    step(std::integral_constant<int, 0>{}, k);
-    if (k + 2 < iters) step(std::integral_constant<int, 1>{}, k + 1);
+  for (int k = 0; k + 1 < iters;) {
+    resync(k);
+    const int end = min(k + kPairRun, iters - 1);  // pair steps k .. end - 1; step K - 1 is the exact one
+    for (; k < end; ++k) {
+      if (k & 1)
+        step(std::integral_constant<int, 1>{}, k, k + 1 == end);
+      else
+        step(std::integral_constant<int, 0>{}, k, k + 1 == end);
+    }
   }
 
   // Final exact step (iters >= 1): X_K = X_{K-1} (2I - W X_{K-1}), X_K by columns in accC.
@@ -679,9 +696,10 @@ hipError_t launch_ns_side(const Shape& s, const float* We, float* X, float* xs, 
 // =====================================================================================================
 // m > 64: the m x m matrices do not fit one CU's LDS, so every product is a batched launch over 32 x 32 output
 // tiles (4 waves of 16 x 16, fp32 MFMA), K staged through LDS in chunks of 32 with the next chunk's float4 loads
-// in flight during the current chunk's MFMAs. The steps follow the small kernel: T_0 = W X_0, then for
-// k < K - 1 one launch computes both T_{k+1} = T_k U_k and X_{k+1} = X_k U_k with U_k = 2I - T_k formed while
-// staging, and the last step is the exact one, X_K = X_{K-1} (2I - W X_{K-1}), in two launches.
+// in flight during the current chunk's MFMAs. The steps follow the small kernel: segments of at most kPairRunF32
+// steps start from T_k = W X_k, then one launch per step computes both T_{k+1} = T_k U_k and X_{k+1} = X_k U_k
+// with U_k = 2I - T_k formed while staging, and the last step is the exact one, X_K = X_{K-1} (2I - W X_{K-1}),
+// in two launches.
 // =====================================================================================================
 // alpha and X_0 = alpha W^T for m > 64, over (slice, 32-row chunk) blocks. Pass 1 writes per-chunk partial
 // column sums and the largest row sum of the chunk; pass 2 combines them in a fixed order (deterministic) and
@@ -916,18 +934,21 @@ hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float
     hipLaunchKernelGGL(k_ns_sums, dim3(s.G, nch), blk, 0, st, We, part, rmx, m);
     hipLaunchKernelGGL(k_ns_x0, dim3(s.G, nch), blk, 0, st, We, part, rmx, Xb[xc], xs, xs_stride, alpha, m);
   }
-  if (K >= 2) {
-    MMJob j0{{We, nullptr}, {Tb[0], nullptr}, nullptr, 0};
-    hipLaunchKernelGGL((k_ns_mm<0, 0>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, j0, Xb[xc], m);  // T_0 = W X_0
-  }
   int tc = 0;
-  for (int k = 0; k + 1 < K; ++k) {
-    const bool last = k + 2 == K;
-    // pair step: job 0: T_{k+1} = T_k (2I - T_k) (skipped on the last step), job 1: X_{k+1} = X_k (2I - T_k)
-    MMJob jp{{last ? nullptr : Tb[tc], Xb[xc]}, {last ? nullptr : Tb[tc ^ 1], Xb[xc ^ 1]}, slot(k + 1), xs_stride};
-    hipLaunchKernelGGL((k_ns_mm<1, 0>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, jp, Tb[tc], m);
-    tc ^= 1;
-    xc ^= 1;
+  for (int k = 0; k + 1 < K;) {
+    // segment start: T_k = W X_k
+    MMJob j0{{We, nullptr}, {Tb[tc], nullptr}, nullptr, 0};
+    hipLaunchKernelGGL((k_ns_mm<0, 0>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, j0, Xb[xc], m);
+    const int end = std::min(k + kPairRunF32, K - 1);
+    for (; k < end; ++k) {
+      const bool last = k + 1 == end;
+      // pair step: job 0: T_{k+1} = T_k (2I - T_k) (skipped at a segment's end), job 1: X_{k+1} = X_k (2I - T_k)
+      MMJob jp{{last ? nullptr : Tb[tc], Xb[xc]}, {last ? nullptr : Tb[tc ^ 1], Xb[xc ^ 1]}, slot(k + 1),
+               xs_stride};
+      hipLaunchKernelGGL((k_ns_mm<1, 0>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, jp, Tb[tc], m);
+      tc ^= 1;
+      xc ^= 1;
+    }
   }
   if (K >= 1) {
     // exact step: U' = 2I - W X_{K-1} (into a T buffer), then X_K = X_{K-1} U'

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "liblf_attn.so")
 
 LF_OK, LF_EINVAL, LF_EWORKSPACE, LF_EUNSUPPORTED, LF_EHIP = 0, -1, -2, -3, -4
 LF_F32, LF_BF16 = 0, 1
+LF_KERNEL_LAPLACE, LF_KERNEL_GAUSS = 0, 1
 LF_M_MAX = 256
 LF_NS_ITERS_MAX = 64
 
@@ -26,7 +27,7 @@ LF_NS_ITERS_MAX = 64
 EXPORTS = (
     "lf_attn_query", "lf_attn_saved_layout", "lf_attn_fwd", "lf_attn_bwd", "lf_strerror", "lf_landmark_pool",
     "lf_laplace_l1_exp", "lf_ns_pinv", "lf_ckv_reduce", "lf_whiten_stats", "lf_landmark_mix", "lf_out_gemm_dwc",
-    "lf_out_gemm_dwc_fused", "lf_attn_bwd_ex", "lf_cg_pinv",
+    "lf_out_gemm_dwc_fused", "lf_attn_bwd_ex", "lf_cg_pinv", "lf_gauss_l2_exp",
 )
 LF_BWD_EXACT_ALPHA = 1
 LF_CG_ITERS_MAX = 256
@@ -37,7 +38,7 @@ class LfAttnParams(ctypes.Structure):
         ("B", ctypes.c_int32), ("heads", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
         ("d", ctypes.c_int32), ("r", ctypes.c_int32), ("lambda_", ctypes.c_float), ("eps", ctypes.c_float),
         ("ns_iters", ctypes.c_int32), ("whiten", ctypes.c_int32), ("whiten_eps", ctypes.c_float),
-        ("dtype", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("kernel", ctypes.c_int32),
     ]
 
     @property
@@ -88,6 +89,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lf_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "lf_landmark_pool": (ctypes.c_int, [_P, _vp, _vp, _vp]),
         "lf_laplace_l1_exp": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+        "lf_gauss_l2_exp": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
         "lf_ns_pinv": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "lf_ckv_reduce": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _sz, _vp]),
         "lf_whiten_stats": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp]),
@@ -106,11 +108,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 def make_params(B: int, heads: int, H: int, W: int, d: int, r: int, lam: float = 4.0, eps: float = 1e-3,
                 ns_iters: int = 12, whiten: bool = False, whiten_eps: float = 1e-5,
-                dtype: torch.dtype = torch.float32) -> LfAttnParams:
+                dtype: torch.dtype = torch.float32, kernel: str = "laplace") -> LfAttnParams:
+    """kernel: "laplace" (exp(-||x-y||_1/lambda), the method) or "gauss" (exp(-||x-y||_2^2/lambda))."""
     if dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("dtype must be torch.float32 or torch.bfloat16")
+    kernels = {"laplace": LF_KERNEL_LAPLACE, "gauss": LF_KERNEL_GAUSS}
+    if kernel not in kernels:
+        raise ValueError('kernel must be "laplace" or "gauss"')
     return LfAttnParams(B, heads, H, W, d, r, lam, eps, ns_iters, 1 if whiten else 0, whiten_eps,
-                        LF_BF16 if dtype == torch.bfloat16 else LF_F32)
+                        LF_BF16 if dtype == torch.bfloat16 else LF_F32, kernels[kernel])
 
 
 def io_dtype(p: LfAttnParams) -> torch.dtype:
@@ -213,6 +219,15 @@ def lf_laplace_l1_exp(p, Q, K, L, CQ, CK, We, stream=None) -> None:
         ctypes.byref(p), _ptr(Q, "Q", dt, n), _ptr(K, "K", dt, n), _ptr(L, "L", f32, p.G * p.m * p.d),
         _ptr(CQ, "CQ", f32, nm), _ptr(CK, "CK", f32, nm), _ptr(We, "We", f32, p.G * p.m * p.m), _stream(stream)),
         "lf_laplace_l1_exp")
+
+
+def lf_gauss_l2_exp(p, Q, K, L, CQ, CK, We, stream=None) -> None:
+    dt, n = io_dtype(p), p.G * p.N * p.d
+    f32, nm = torch.float32, p.G * p.N * p.m
+    _check(load_library().lf_gauss_l2_exp(
+        ctypes.byref(p), _ptr(Q, "Q", dt, n), _ptr(K, "K", dt, n), _ptr(L, "L", f32, p.G * p.m * p.d),
+        _ptr(CQ, "CQ", f32, nm), _ptr(CK, "CK", f32, nm), _ptr(We, "We", f32, p.G * p.m * p.m), _stream(stream)),
+        "lf_gauss_l2_exp")
 
 
 def lf_ns_pinv(p, We, X, xs, alpha, resid, ws, stream=None) -> None:

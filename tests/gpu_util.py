@@ -27,7 +27,7 @@ def note(msg: str) -> None:
 
 def params(wl, **kw) -> lf.LfAttnParams:
     p = lf.make_params(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.r, wl.lam, wl.eps, wl.ns_iters, wl.whiten,
-                       wl.whiten_eps, torch.bfloat16 if wl.dtype == WL.BF16 else torch.float32)
+                       wl.whiten_eps, torch.bfloat16 if wl.dtype == WL.BF16 else torch.float32, wl.kernel)
     for k, v in kw.items():
         setattr(p, k, v)
     return p

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def _p(wl, **kw):
     p = lf.make_params(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.r, wl.lam, wl.eps, wl.ns_iters, wl.whiten,
-                       wl.whiten_eps, torch.bfloat16 if wl.dtype == WL.BF16 else torch.float32)
+                       wl.whiten_eps, torch.bfloat16 if wl.dtype == WL.BF16 else torch.float32, wl.kernel)
     for k, v in kw.items():
         setattr(p, k, v)
     return p
@@ -74,6 +74,7 @@ def test_query_sizes_and_saved_layout(lib, wl):
     ("lambda_", 0.0, lf.LF_EINVAL), ("lambda_", float("nan"), lf.LF_EINVAL), ("eps", -1e-3, lf.LF_EINVAL),
     ("ns_iters", -1, lf.LF_EINVAL), ("ns_iters", 65, lf.LF_EINVAL), ("whiten", 2, lf.LF_EINVAL),
     ("dtype", 7, lf.LF_EINVAL), ("d", 48, lf.LF_EUNSUPPORTED), ("r", 1, lf.LF_EUNSUPPORTED),
+    ("kernel", 2, lf.LF_EINVAL), ("kernel", -1, lf.LF_EINVAL),
 ])
 def test_query_rejects_bad_params(lib, field, value, code):
     p = _p(WL.PVT_S1)  # 56x56 grid: r=1 gives m=3136 > LF_M_MAX, r=3 does not divide 56
@@ -147,3 +148,24 @@ def test_cg_validates_on_host(lib):
     assert lib.lf_cg_pinv(ctypes.byref(p), None, fake, None, 4, None) == lf.LF_EINVAL
     assert lib.lf_cg_pinv(ctypes.byref(p), fake, fake, misaligned, 4, None) == lf.LF_EINVAL
     assert lib.lf_cg_pinv(ctypes.byref(_p(WL.HIRES_BF16)), fake, fake, None, 4, None) == lf.LF_EUNSUPPORTED
+
+
+def test_gaussian_variant_is_forward_only_on_host(lib):
+    """The Gaussian-kernel parameter set is valid for the forward pass and its stage call, and the backward pass and
+    the fused (Laplacian) output stage reject it with LF_EUNSUPPORTED before launching."""
+    p = _p(WL.GAUSS_S1)
+    assert p.kernel == lf.LF_KERNEL_GAUSS
+    fwd, saved, bwd = lf.lf_attn_query(p)
+    assert fwd > 0 and saved > 0
+    fake = ctypes.c_void_p(0x100000)
+    assert lib.lf_attn_bwd(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, fake, fake, bwd,
+                           None) == lf.LF_EUNSUPPORTED
+    assert lib.lf_attn_bwd_ex(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, fake, None, None, 0,
+                              fake, bwd, None) == lf.LF_EUNSUPPORTED
+    assert lib.lf_out_gemm_dwc_fused(ctypes.byref(p), fake, fake, fake, fake, None, fake, None) == lf.LF_EUNSUPPORTED
+    # the stage call validates its pointers before launching
+    misaligned = ctypes.c_void_p(0x100004)
+    assert lib.lf_gauss_l2_exp(ctypes.byref(p), fake, fake, fake, fake, misaligned, fake, None) == lf.LF_EINVAL
+    assert lib.lf_gauss_l2_exp(ctypes.byref(p), fake, None, fake, fake, fake, fake, None) == lf.LF_EINVAL
+    with pytest.raises(ValueError):
+        lf.make_params(1, 1, 8, 8, 16, 2, kernel="cosine")
