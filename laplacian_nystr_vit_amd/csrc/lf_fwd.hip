@@ -454,8 +454,18 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
   static_assert(NP % PPW == 0, "tiles per wave must divide the tile count");
   constexpr int C4 = D / 4;
   constexpr int LQM = 64 / NWV;                  // FUSED: most landmarks of a chunk per wave
-  const int g = blockIdx.y;
-  const int ty0 = (blockIdx.x / tiles_x) * 8, tx0 = (blockIdx.x % tiles_x) * 8;
+  // Block order: the hardware deals workgroups to the 8 XCDs round-robin by linear index (x fastest), and each XCD
+  // has its own L2. The linear index is remapped so that consecutive patches run on one XCD: the patches of one
+  // patch row read their C_Q runs (32 bytes per landmark row) from shared 128-byte lines and overlap in their V
+  // halos, so those lines leave HBM once instead of once per XCD.
+  long lin = static_cast<long>(blockIdx.y) * gridDim.x + blockIdx.x;
+  {
+    const long total = static_cast<long>(gridDim.x) * gridDim.y, full = (total / 8) * 8;
+    if (lin < full) lin = (lin % 8) * (full / 8) + lin / 8;
+  }
+  const int g = static_cast<int>(lin / gridDim.x);
+  const int pt = static_cast<int>(lin % gridDim.x);
+  const int ty0 = (pt / tiles_x) * 8, tx0 = (pt % tiles_x) * 8;
   const int h = g % heads;
   // the wave index through readfirstlane: the compiler then knows it is uniform and keeps the per-wave tile
   // guards below as scalar branches outside the MFMA sequences
