@@ -647,14 +647,25 @@ __global__ __launch_bounds__(512) void k_ns_side(const float* __restrict__ We, f
     ns_small_block<ST, KC>(b, We, Xout, xs, alpha_out, nullptr, m, iters);
     return;
   }
+  // The S tiles start at the first multiple of 8 after the solver blocks (the blocks in between exit at once), so
+  // that tile j runs on XCD j % 8 (the hardware deals blocks to the 8 XCDs round-robin). Their order is remapped so
+  // that the tiles of one slice share an XCD: each slice's C_K rows and V columns are read by several tiles, and
+  // one L2 then serves the repeats.
+  const int s0 = (G + 7) & ~7;
+  if (b < s0) return;
+  int j = b - s0;
+  {
+    const int total = static_cast<int>(gridDim.x) - s0, full = (total / 8) * 8;
+    if (j < full) j = (j % 8) * (full / 8) + j / 8;
+  }
   __shared__ float sRed[8 * 256];
-  ckv_tile_block<T, D>(b - G, CK, V, S, N, m, sRed);
+  ckv_tile_block<T, D>(j, CK, V, S, N, m, sRed);
 }
 
 template <typename T, int D>
 static void ns_side_st(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
                        const T* V, float* S, hipStream_t st) {
-  const int blocks = s.G * (1 + (s.m + 15) / 16 * (D / 16));
+  const int blocks = ((s.G + 7) & ~7) + s.G * ((s.m + 15) / 16 * (D / 16));  // solver blocks, padding, S tiles
   const int nt = (s.m + 15) / 16;
 #define LF_NS_SIDE(ST_, KC_)                                                                                        \
   hipLaunchKernelGGL((k_ns_side<T, D, ST_, KC_>), dim3(blocks), dim3(512), 0, st, We, X, xs, alpha, s.m, s.ns_iters, \
