@@ -465,14 +465,23 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
     e_next = store_exp(mx);
     if (last) xcol_buf = nxt;
   };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   for (int k = 0; k + 1 < iters;) {
     resync(k);
     const int end = min(k + kPairRun, iters - 1);  // pair steps k .. end - 1; step K - 1 is the exact one
-    for (; k < end; ++k) {
-      if (k & 1)
-        step(std::integral_constant<int, 1>{}, k, k + 1 == end);
-      else
-        step(std::integral_constant<int, 0>{}, k, k + 1 == end);
+    // steps in (even, odd) pairs so that each step's buffer parity is a compile-time constant
+    if (k & 1) {
+      step(P1{}, k, k + 1 == end);
+      ++k;
+    }
+    for (; k + 1 < end; k += 2) {
+      step(P0{}, k, false);
+      step(P1{}, k + 1, k + 2 == end);
+    }
+    if (k < end) {
+      step(P0{}, k, true);
+      ++k;
     }
   }
 
