@@ -46,10 +46,10 @@ BwdWs plan(const Shape& s) {
   int nsplit, rps;
   ckv_split(s, &nsplit, &rps);
   BwdWs w;
-  // dL partials: blocks of 256 / d landmark groups of kDlLw landmarks; the row range is split so that about 2048
-  // waves run, each split a multiple of 4 rows.
+  // dL partials: blocks of 256 / d landmark groups of kDlLw landmarks; the row range is split so that about 4096
+  // waves run (four per SIMD), each split a multiple of 4 rows.
   w.nlb = cdiv(s.m, (256 / s.d) * kDlLw);
-  int want = cdiv(2048, static_cast<long>(s.G) * w.nlb * 4);
+  int want = cdiv(4096, static_cast<long>(s.G) * w.nlb * 4);
   const int maxs = cdiv(s.N, 16);
   if (want > maxs) want = maxs;
   if (want < 1) want = 1;
@@ -482,6 +482,12 @@ __global__ __launch_bounds__(256) void k_bwd_dl_partial(const T* __restrict__ Q,
   constexpr int LW = kDlLw;
   constexpr int RG = 4;  // rows per step
   int b = blockIdx.x;
+  {
+    // Consecutive blocks on one XCD (the hardware deals blocks to the 8 XCDs round-robin): the landmark groups of
+    // one row range then read its Q and K rows through one L2.
+    const int full = (static_cast<int>(gridDim.x) / 8) * 8;
+    if (b < full) b = (b % 8) * (full / 8) + b / 8;
+  }
   const int lb = b % nlb;
   b /= nlb;
   const int s = b % nsplit, g = b / nsplit;
