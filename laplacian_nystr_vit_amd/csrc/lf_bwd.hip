@@ -27,6 +27,9 @@ namespace lf {
 static inline int cdiv(long a, long b) { return static_cast<int>((a + b - 1) / b); }
 
 constexpr int kDlLw = 8;  // landmarks per thread in the dL reduction
+// Waves per block of the token-row gradient kernel: 8-channel slices, so a block of 64 rows holds d / 8 waves.
+template <int D>
+constexpr int kRowsWaves = D / 8;
 
 __device__ __forceinline__ float sgnf(float x) { return x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f); }
 
@@ -558,18 +561,18 @@ __global__ __launch_bounds__(256) void k_bwd_dl_finalize(const float* __restrict
 
 // ---------------------------------------------------------------------------------------------------------
 // Token rows: dQ_i = -sum_l Gq[i][l] sign(Q_i - L_l) + dL_owner(i) / r^2 ; dK_j = -sum_l Gk[j][l] sign(K_j - L_l).
-// Block = 64 rows x all channels of one side; wave w owns channels [w CW, (w + 1) CW) of the 64 rows (lane = row),
+// Block = 64 rows x all channels of one side; wave w owns 8 channels [w CW, (w + 1) CW) of the 64 rows (lane = row),
 // keeping that slice of the row and of its accumulator in VGPRs. The landmark values of the wave's channels are
 // wave-uniform (one scalar load per landmark), the weights Gx[l][row] coalesced vector loads, fetched a chunk of
 // landmarks ahead.
 // ---------------------------------------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_bwd_rows(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(512) void k_bwd_rows(const T* __restrict__ Q, const T* __restrict__ K,
                                                   const float* __restrict__ L, const float* __restrict__ Gq,
                                                   const float* __restrict__ Gk, const float* __restrict__ dL,
                                                   T* __restrict__ dQ, T* __restrict__ dK, int N, int m, int W, int r) {
-  constexpr int NWB = D >= 64 ? 4 : D / 16;  // waves per block
-  constexpr int CW = D / NWB;                 // channels per wave (16)
+  constexpr int NWB = kRowsWaves<D>;  // waves per block
+  constexpr int CW = D / NWB;         // channels per wave (8)
   const int side = blockIdx.z, g = blockIdx.y;
   const int wv = __builtin_amdgcn_readfirstlane(wave_id());
   const int row = blockIdx.x * 64 + lane_id();
@@ -798,7 +801,7 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
   const int md = s.m * D;
   hipLaunchKernelGGL(k_bwd_dl_finalize, dim3(cdiv(static_cast<long>(s.G) * md, 256)), dim3(256), 0, st, dLpart, dLW,
                      dL, s.G, p.nsplitL, md);
-  hipLaunchKernelGGL((k_bwd_rows<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(64 * (D >= 64 ? 4 : D / 16)), 0, st, Q,
+  hipLaunchKernelGGL((k_bwd_rows<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(64 * kRowsWaves<D>), 0, st, Q,
                      K, sp.L, Gq, Gk, dL, dQ, dK, s.N, s.m, s.W, s.r);
   if (ex.d_lambda) {
     float* lp = reinterpret_cast<float*>(b + p.lampart);
