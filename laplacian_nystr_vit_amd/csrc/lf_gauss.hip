@@ -7,8 +7,12 @@
 //
 // Unlike the l1 distance, the squared l2 distance is a dense contraction plus two norms:
 //   ||x - l||^2 = ||x||^2 + ||l||^2 - 2 x.l,
-// so the cross-kernels run on fp32 MFMA (v_mfma_f32_16x16x4_f32), which issues twice the fp32 work per cycle of a
-// VALU difference-and-square loop. The landmark kernel W is computed from the differences themselves on the VALU:
+// so the cross-kernels run on MFMA. x.l is formed from split fp16 operands, x = x_hi + x_lo with
+// x_hi = fp16(x) and x_lo = fp16(x - x_hi), as x_hi.l_hi + x_hi.l_lo + x_lo.l_hi on v_mfma_f32_16x16x32_f16 with
+// fp32 accumulation: about 22 bits of each operand, three fp16 MFMAs at a fifth of the issue time of the fp32 MFMA
+// product. Rows and landmarks are scaled by powers of two (largest entry near 2^12) so that the halves stay clear
+// of fp16 overflow and subnormals; the scales come back out exactly in the epilogue. The landmark kernel W is
+// computed from the differences themselves on the VALU:
 // it is tiny (m^2 d per slice), and (a - b)^2 == (b - a)^2 in float32 makes W bitwise symmetric with an exact
 // zero distance on its diagonal, which Newton-Schulz relies on.
 #include <hip/hip_runtime.h>
@@ -20,36 +24,54 @@
 
 namespace lf {
 
-// Grid: G * (tilesQ + tilesK) row blocks of 64 rows, then wblocks blocks of 256 landmark pairs.
+typedef _Float16 gh8 __attribute__((ext_vector_type(8)));
+typedef float gf8 __attribute__((ext_vector_type(8)));
+
+// Exponent e of |v| = f 2^e, f in [1, 2), for v != 0 (subnormals count as 2^-126); the scale exponent of a row or
+// landmark whose largest entry is mx puts that entry in [2^12, 2^13).
+__device__ __forceinline__ int scale_exp(float mx) {
+  if (!(mx > 0.f)) return 0;
+  const int bexp = static_cast<int>((__float_as_uint(mx) >> 23) & 0xffu);
+  return (bexp == 0 ? 1 : bexp) - 127 - 12;
+}
+
+// v 2^-e split into fp16 halves, eight values.
+__device__ __forceinline__ void split8(gf8 v, int e, gh8& h, gh8& l) {
+  gf8 sv;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) sv[t] = ldexpf(v[t], -e);
+  h = __builtin_convertvector(sv, gh8);
+  l = __builtin_convertvector(sv - __builtin_convertvector(h, gf8), gh8);
+}
+
+// Grid: pairblocks blocks of 256 landmark pairs, then G * (tilesQ + tilesK) row blocks of 64 rows.
 // Row block (4 waves): the block stages its 64 rows of one source (Q or K) of one slice in LDS with coalesced
-// 16-byte loads, together with their squared norms. Wave w then takes the 16-landmark tiles w, w + 4, ... and, for
-// each, all four 16-row tiles: four independent MFMA accumulation chains that share one landmark operand. Lane
-// (r16, q) = (lane % 16, lane / 16) supplies channels [q D/4, (q+1) D/4) of row r16 of a row tile and of landmark
-// r16 of the landmark tile (read straight from L2: one slice's landmarks are m*D*4 bytes); in MFMA step t, k-slot
-// q carries channel q D/4 + t for both operands, so no cross-lane exchange feeds the contraction. The accumulator
-// of lane (r16, q) holds x.l for rows 4q + {0..3} of the row tile and landmark r16: adding the two norms and one
-// v_exp_f32 gives four consecutive tokens of one landmark column, stored as one 16-byte write into the
-// landmark-major C.
+// 16-byte loads, together with their squared norms and scale exponents. Wave w then takes the 16-landmark tiles
+// w, w + 4, ... and, for each, all four 16-row tiles: four independent MFMA accumulation chains that share one
+// landmark operand. In the 16x16x32 fp16 MFMA, lane (r16, q) = (lane % 16, lane / 16) supplies channels
+// 32c + 8q .. 32c + 8q + 7 of chunk c, of row r16 of a row tile (A, from LDS) and of landmark r16 of the landmark
+// tile (B, read straight from L2: one slice's landmarks are m*D*4 bytes). The accumulator of lane (r16, q) holds
+// x.l for rows 4q + {0..3} of the row tile and landmark r16: rescaling, adding the two norms and one v_exp_f32
+// give four consecutive tokens of one landmark column, stored as one 16-byte write into the landmark-major C.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_gauss(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256, D <= 64 ? 4 : 2) void k_gauss(const T* __restrict__ Q, const T* __restrict__ K,
                                                const float* __restrict__ L, float* __restrict__ CQ,
                                                float* __restrict__ CK, float* __restrict__ We, int N, int m,
-                                               int tilesQ, int tilesK, int rowblocks, long npairs, float scale,
-                                               float eps) {
-  constexpr int CPL = D / 4;  // channels per lane
-  constexpr int LDX = D + 4;  // LDS row stride: 16 lanes reading one column offset of 16 rows hit distinct banks
+                                               int tilesQ, int tilesK, int rowblocks, int pairblocks, long npairs,
+                                               float scale, float eps) {
+  constexpr int CPL = D / 4;             // channels per thread in the norm pass
+  constexpr int KC = (D + 31) / 32;      // 32-channel MFMA chunks (D = 16 pads its chunk with zeros)
+  constexpr int LDX = D + 4;             // LDS row stride: 16 rows at one column offset hit distinct banks
   __shared__ float sX[64 * LDX];
   __shared__ float sN[64];
-  int b = static_cast<int>(blockIdx.x);
-  {
-    // Consecutive blocks on one XCD (blocks are dealt to the 8 XCDs round-robin): a slice's row blocks then share
-    // its landmarks through one L2.
-    const int full = (static_cast<int>(gridDim.x) / 8) * 8;
-    if (b < full) b = (b % 8) * (full / 8) + b / 8;
-  }
-  if (b >= rowblocks) {
+  __shared__ int sE[64];
+  // Blocks [0, pairblocks) (a multiple of 8) form W, spread over all XCDs; the row blocks follow, remapped so that
+  // consecutive row blocks run on one XCD (blocks are dealt to the 8 XCDs round-robin) and a slice's row blocks
+  // share its landmarks through one L2.
+  const int hw = static_cast<int>(blockIdx.x);
+  if (hw < pairblocks) {
     // Landmark pairs: W[g][l][l2] = exp(-sum_c (L_lc - L_l2c)^2 / lambda) + eps [l == l2].
-    const long e = static_cast<long>(b - rowblocks) * 256 + threadIdx.x;
+    const long e = static_cast<long>(hw) * 256 + threadIdx.x;
     if (e >= npairs) return;
     const long mm = static_cast<long>(m) * m;
     const int g = static_cast<int>(e / mm);
@@ -72,6 +94,11 @@ __global__ __launch_bounds__(256) void k_gauss(const T* __restrict__ Q, const T*
     We[e] = val;
     return;
   }
+  int b = hw - pairblocks;
+  {
+    const int full = (rowblocks / 8) * 8;
+    if (b < full) b = (b % 8) * (full / 8) + b / 8;
+  }
 
   const int per_slice = tilesQ + tilesK;
   const int g = b / per_slice;
@@ -93,9 +120,9 @@ __global__ __launch_bounds__(256) void k_gauss(const T* __restrict__ Q, const T*
   }
   __syncthreads();
   {
-    // Squared norm of row tid / 4 from its four channel quarters, summed in a fixed order.
+    // Squared norm and largest |x| of row tid / 4 from its four channel quarters, summed in a fixed order.
     const float* src = sX + (tid >> 2) * LDX + (tid & 3) * CPL;
-    float p = 0.f;
+    float p = 0.f, mx = 0.f;
 #pragma unroll
     for (int c = 0; c < CPL; c += 4) {
       const float4 v = *reinterpret_cast<const float4*>(src + c);
@@ -103,63 +130,89 @@ __global__ __launch_bounds__(256) void k_gauss(const T* __restrict__ Q, const T*
       p = fmaf(v.y, v.y, p);
       p = fmaf(v.z, v.z, p);
       p = fmaf(v.w, v.w, p);
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
     p += __shfl_xor(p, 1);
     p += __shfl_xor(p, 2);
-    if ((tid & 3) == 0) sN[tid >> 2] = p;
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    if ((tid & 3) == 0) {
+      sN[tid >> 2] = p;
+      sE[tid >> 2] = scale_exp(mx);
+    }
   }
   __syncthreads();
 
   const int ntiles = (m + 15) >> 4;
   if (w >= ntiles) return;
-  // A operands: channels [q CPL, (q+1) CPL) of row rt*16 + r16, for the four row tiles.
-  float xa[4][CPL];
+  // A operands: the lane's channels of row rt*16 + r16 in each chunk, scaled by the row's exponent and split.
+  gh8 ah[4][KC], al[4][KC];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < 4; ++rt) {
+    const int row = rt * 16 + r16;
+    const int er = sE[row];
 #pragma unroll
-    for (int c = 0; c < CPL; c += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(sX + (rt * 16 + r16) * LDX + q * CPL + c);
-      xa[rt][c] = v.x;
-      xa[rt][c + 1] = v.y;
-      xa[rt][c + 2] = v.z;
-      xa[rt][c + 3] = v.w;
+    for (int c = 0; c < KC; ++c) {
+      const int k0 = c * 32 + 8 * q;
+      gf8 v;
+      if (k0 < D) {
+        const float4 u0 = *reinterpret_cast<const float4*>(sX + row * LDX + k0);
+        const float4 u1 = *reinterpret_cast<const float4*>(sX + row * LDX + k0 + 4);
+        v = gf8{u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      } else {
+        v = gf8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      }
+      split8(v, er, ah[rt][c], al[rt][c]);
     }
-  // Norms of the rows each accumulator element belongs to: row rt*16 + 4q + j.
-  float xr[4][4];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xr[rt][j] = sN[rt * 16 + 4 * q + j];
+  }
   const bool vec = (N & 3) == 0;
   const float* __restrict__ Lg = L + static_cast<size_t>(g) * m * D;
   float* __restrict__ Cg = (isq ? CQ : CK) + static_cast<size_t>(g) * m * N;
 
   for (int lt = w; lt < ntiles; lt += 4) {
-    float lb[CPL];
+    gf8 lv[KC];
     {
-      const float* __restrict__ src = Lg + static_cast<size_t>(min(lt * 16 + r16, m - 1)) * D + q * CPL;
+      const float* __restrict__ src = Lg + static_cast<size_t>(min(lt * 16 + r16, m - 1)) * D;
 #pragma unroll
-      for (int c = 0; c < CPL; c += 4) {
-        const float4 v = load4(src + c);
-        lb[c] = v.x;
-        lb[c + 1] = v.y;
-        lb[c + 2] = v.z;
-        lb[c + 3] = v.w;
+      for (int c = 0; c < KC; ++c) {
+        const int k0 = c * 32 + 8 * q;
+        if (k0 < D) {
+          const float4 u0 = load4(src + k0), u1 = load4(src + k0 + 4);
+          lv[c] = gf8{u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        } else {
+          lv[c] = gf8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        }
       }
     }
-    float ln = 0.f;
+    float ln = 0.f, lm = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) ln = fmaf(lb[c], lb[c], ln);
+    for (int c = 0; c < KC; ++c)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        ln = fmaf(lv[c][t], lv[c][t], ln);
+        lm = fmaxf(lm, fabsf(lv[c][t]));
+      }
     ln += __shfl_xor(ln, 16);
     ln += __shfl_xor(ln, 32);  // ||L_{lt*16 + r16}||^2, identical bits in the four lanes of landmark r16
+    lm = fmaxf(lm, __shfl_xor(lm, 16));
+    lm = fmaxf(lm, __shfl_xor(lm, 32));
+    const int el = scale_exp(lm);
+    gh8 bh[KC], bl[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) split8(lv[c], el, bh[c], bl[c]);
 
     f32x4 acc[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < CPL; ++t)
+    for (int c = 0; c < KC; ++c) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma16x16x4(xa[rt][t], lb[t], acc[rt]);
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt][c], bh[c], acc[rt], 0, 0, 0);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt][c], bl[c], acc[rt], 0, 0, 0);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rt][c], bh[c], acc[rt], 0, 0, 0);
+    }
 
     const int l = lt * 16 + r16;
     if (l < m) {
@@ -170,7 +223,10 @@ __global__ __launch_bounds__(256) void k_gauss(const T* __restrict__ Q, const T*
         float o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float d2 = fmaxf(fmaf(-2.f, acc[rt][j], xr[rt][j] + ln), 0.f);
+          // norm and scale exponent of row rt*16 + 4q + j, the row this accumulator element belongs to
+          const int row = rt * 16 + 4 * q + j;
+          const float dot = ldexpf(acc[rt][j], sE[row] + el);
+          const float d2 = fmaxf(fmaf(-2.f, dot, sN[row] + ln), 0.f);
           o[j] = __builtin_amdgcn_exp2f(d2 * scale);
         }
         if (vec && rb + 3 < N) {
@@ -191,13 +247,14 @@ static hipError_t gauss_t(const Shape& s, const void* Q, const void* K, const fl
   const long tilesN = (static_cast<long>(s.N) + 63) / 64;
   const long rowblocks = static_cast<long>(s.G) * 2 * tilesN;
   const long npairs = static_cast<long>(s.G) * s.m * s.m;
-  const long blocks = rowblocks + (npairs + 255) / 256;
+  const long pairblocks = ((npairs + 255) / 256 + 7) / 8 * 8;  // a multiple of 8 keeps the row blocks' XCD order
+  const long blocks = rowblocks + pairblocks;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
   const float scale = static_cast<float>(-1.4426950408889634 / static_cast<double>(s.lambda));
   hipLaunchKernelGGL((k_gauss<T, D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
                      static_cast<const T*>(Q), static_cast<const T*>(K), L, CQ, CK, We, s.N, s.m,
-                     static_cast<int>(tilesN), static_cast<int>(tilesN), static_cast<int>(rowblocks), npairs, scale,
-                     s.eps);
+                     static_cast<int>(tilesN), static_cast<int>(tilesN), static_cast<int>(rowblocks),
+                     static_cast<int>(pairblocks), npairs, scale, s.eps);
   return hipGetLastError();
 }
 
