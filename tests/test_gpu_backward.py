@@ -20,6 +20,10 @@ CASES = [
     WL.TINY.replace(name="train_ragged_10x6_d32", H=10, W=6, d=32, r=2, whiten=True, backward=True),
     WL.TINY.replace(name="train_r1_m64", r=1, whiten=False, backward=True),
     WL.TRAIN_S1.replace(name="train_s1_bf16_B2", B=2, dtype=WL.BF16),
+    # 26 Newton-Schulz steps: the forward's saved iterates come from three runs of coupled steps, each started from
+    # T = W X formed afresh, and the reverse chain walks back through all of them.
+    WL.TINY.replace(name="train_12x12_K26", B=2, H=12, W=12, r=2, ns_iters=26, whiten=True, backward=True,
+                    qk_dist="student_t"),
 ]
 
 
@@ -105,6 +109,10 @@ PARAM_CASES = [
     WL.TINY.replace(name="train_tiny_whiten_h2", B=2, heads=2, whiten=True, backward=True),
     WL.TINY.replace(name="train_ragged_10x6_d32", H=10, W=6, d=32, r=2, whiten=True, backward=True),
     WL.TRAIN_S1.replace(name="train_s1_bf16_B2", B=2, dtype=WL.BF16),
+    # 26 Newton-Schulz steps: the forward's saved iterates come from three runs of coupled steps, each started from
+    # T = W X formed afresh, and the reverse chain walks back through all of them.
+    WL.TINY.replace(name="train_12x12_K26", B=2, H=12, W=12, r=2, ns_iters=26, whiten=True, backward=True,
+                    qk_dist="student_t"),
 ]
 
 
