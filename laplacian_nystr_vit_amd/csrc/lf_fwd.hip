@@ -211,7 +211,9 @@ __host__ __device__ inline int ld_b(int cols) { return ((cols + 31) / 32) * 32 +
 // ckv_reduce: S[g][l][c] = sum_i C_K[g][i][l] V[g][i][c], deterministic split-N reduction
 //   ([note] motivation: linear attention forms K^T V first; Design 2).
 // Stage 1: each block reduces `rows_per_split` token rows of one slice into a partial [mout][D] on fp32 MFMA
-// (M = landmarks, N = channels, K = tokens), staging 64-row chunks of C and V through LDS.
+// (M = landmarks, N = channels, K = tokens), staging 64-row chunks of C and V through LDS. With more than 64
+// landmarks the landmarks are split over blocks too (64 per block), so that each split covers more rows and the
+// partials stay small next to the C_K bytes they summarise.
 // Stage 2: the partials are summed in split order.
 // `ones` appends a column of ones to C (mout = mrow + 1), so row mrow of the result is sum_i V[i][c]; the
 // backward pass uses this to get the column sums of dY in the same sweep as C_Q^T dY.
@@ -219,7 +221,7 @@ __host__ __device__ inline int ld_b(int cols) { return ((cols + 31) / 32) * 32 +
 template <typename T, int D, int MT>
 __global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ C, const T* __restrict__ V,
                                                      float* __restrict__ part, int N, int mrow, int ones,
-                                                     int nsplit, int rows_per_split) {
+                                                     int nsplit, int rows_per_split, int lsplit) {
   // LDS: the C chunk as [landmark][64 tokens] (row stride 68) and the V chunk as [64 tokens][D] (stride 16 mod 32).
   // Landmark rows >= mrow are never written; they only feed output rows that are not stored.
   constexpr int LDC = 68;
@@ -231,7 +233,18 @@ __global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ C
   __shared__ float sC[MT * 16 * LDC];
   __shared__ float sV[64 * LDV];
   const int mout = mrow + ones;
-  const int g = blockIdx.x / nsplit, s = blockIdx.x % nsplit;
+  // Block = (slice, token split, landmark block of MT*16 landmarks), landmark block fastest. Consecutive blocks run on
+  // one XCD (blocks are dealt to the 8 XCDs round-robin), so the landmark blocks of one split read its V rows
+  // through one L2.
+  int b = static_cast<int>(blockIdx.x);
+  {
+    const int full = (static_cast<int>(gridDim.x) / 8) * 8;
+    if (lsplit > 1 && b < full) b = (b % 8) * (full / 8) + b / 8;
+  }
+  const int lsb = b % lsplit;
+  b /= lsplit;
+  const int g = b / nsplit, s = b % nsplit;
+  const int lbase = lsb * MT * 16;  // first landmark of this block
   const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
   const bool vec = (N & 3) == 0;  // landmark rows start 16-byte aligned
 
@@ -252,7 +265,7 @@ __global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ C
 #pragma unroll
     for (int q = 0; q < NQC; ++q) {
       const int e = tid + 256 * q;
-      const int l = e >> 4, i = 4 * (e & 15);
+      const int l = lbase + (e >> 4), i = 4 * (e & 15);
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (l < mrow) {
         const float* src = cg + static_cast<size_t>(l) * N + c0 + i;
@@ -295,7 +308,7 @@ __global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ C
         for (int lt = 0; lt < MT; ++lt) {
           const int l = lt * 16 + (ln & 15);
           float a = sC[l * LDC + kr];
-          if (l == mrow) a = (ones && kr < nr) ? 1.f : 0.f;
+          if (lbase + l == mrow) a = (ones && kr < nr) ? 1.f : 0.f;
 #pragma unroll
           for (int ct = 0; ct < CTW; ++ct) acc[lt][ct] = mfma16x16x4(a, b[ct], acc[lt][ct]);
         }
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ C
         const int c = (wv * CTW + ct) * 16 + (ln & 15);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int l = lt * 16 + 4 * (ln >> 4) + rr;
+          const int l = lbase + lt * 16 + 4 * (ln >> 4) + rr;
           if (l < mout && c < D) pg[static_cast<size_t>(l) * D + c] = acc[lt][ct][rr];
         }
       }
@@ -852,10 +865,12 @@ hipError_t launch_whiten_stats(const Shape& s, const float* CQ, float* mu, float
   return hipGetLastError();
 }
 
+int ckv_lsplit(const Shape& s) { return s.m > 64 ? cdiv(s.m, 64) : 1; }
+
 void ckv_split(const Shape& s, int* nsplit, int* rows_per_split) {
-  // At most ~512 blocks in all; each split covers whole 64-row chunks.
+  // At most ~512 blocks in all (splits times landmark blocks); each split covers whole 64-row chunks.
   const int chunks = cdiv(s.N, 64);
-  int want = 512 / s.G;
+  int want = 512 / (s.G * ckv_lsplit(s));
   if (want > chunks) want = chunks;
   if (want < 1) want = 1;
   const int cps = cdiv(chunks, want);
@@ -865,23 +880,29 @@ void ckv_split(const Shape& s, int* nsplit, int* rows_per_split) {
 
 template <typename T, int D, int MT>
 static void ckv_launch(const Shape& s, const float* C, int ones, const void* V, float* part, int nsplit, int rps,
-                       hipStream_t st) {
-  hipLaunchKernelGGL((k_ckv_partial<T, D, MT>), dim3(s.G * nsplit), dim3(256), 0, st, C, static_cast<const T*>(V),
-                     part, s.N, s.m, ones, nsplit, rps);
+                       int lsplit, hipStream_t st) {
+  hipLaunchKernelGGL((k_ckv_partial<T, D, MT>), dim3(s.G * nsplit * lsplit), dim3(256), 0, st, C,
+                     static_cast<const T*>(V), part, s.N, s.m, ones, nsplit, rps, lsplit);
 }
 
 template <typename T, int D>
 static void ckv_mt(const Shape& s, const float* C, int ones, const void* V, float* part, int nsplit, int rps,
                    hipStream_t st) {
+  // landmark blocks of 64 when m > 64 (the ones column is only used with m <= 64)
+  const int lsplit = ones ? 1 : ckv_lsplit(s);
+  if (lsplit > 1) {
+    ckv_launch<T, D, 4>(s, C, ones, V, part, nsplit, rps, lsplit, st);
+    return;
+  }
   const int mt = cdiv(s.m + ones, 16);
-  if (mt <= 1) ckv_launch<T, D, 1>(s, C, ones, V, part, nsplit, rps, st);
-  else if (mt <= 2) ckv_launch<T, D, 2>(s, C, ones, V, part, nsplit, rps, st);
-  else if (mt <= 3) ckv_launch<T, D, 3>(s, C, ones, V, part, nsplit, rps, st);
-  else if (mt <= 4) ckv_launch<T, D, 4>(s, C, ones, V, part, nsplit, rps, st);
-  else if (mt <= 5) ckv_launch<T, D, 5>(s, C, ones, V, part, nsplit, rps, st);
-  else if (mt <= 8) ckv_launch<T, D, 8>(s, C, ones, V, part, nsplit, rps, st);
-  else if (mt <= 12) ckv_launch<T, D, 12>(s, C, ones, V, part, nsplit, rps, st);
-  else ckv_launch<T, D, 16>(s, C, ones, V, part, nsplit, rps, st);
+  if (mt <= 1) ckv_launch<T, D, 1>(s, C, ones, V, part, nsplit, rps, 1, st);
+  else if (mt <= 2) ckv_launch<T, D, 2>(s, C, ones, V, part, nsplit, rps, 1, st);
+  else if (mt <= 3) ckv_launch<T, D, 3>(s, C, ones, V, part, nsplit, rps, 1, st);
+  else if (mt <= 4) ckv_launch<T, D, 4>(s, C, ones, V, part, nsplit, rps, 1, st);
+  else if (mt <= 5) ckv_launch<T, D, 5>(s, C, ones, V, part, nsplit, rps, 1, st);
+  else if (mt <= 8) ckv_launch<T, D, 8>(s, C, ones, V, part, nsplit, rps, 1, st);
+  else if (mt <= 12) ckv_launch<T, D, 12>(s, C, ones, V, part, nsplit, rps, 1, st);
+  else ckv_launch<T, D, 16>(s, C, ones, V, part, nsplit, rps, 1, st);
 }
 
 template <typename T>
