@@ -32,9 +32,7 @@ namespace lf {
 // barriers: after U is written and after X_next is written. The MFMA result layout (four consecutive rows of
 // one column per lane) gives the by-columns copy of X_next with 8-byte stores; the by-rows copy comes from a
 // second product with the operand roles swapped, (X U)^T = U^T X^T, which reuses the same fragments and yields
-// four consecutive columns of one row per lane. The two copies differ only by rounding. T is formed once per step
-// (by columns) and written twice from the same numbers: as U = 2I - T by columns and, with 2-byte writes, as T by
-// rows.
+// four consecutive columns of one row per lane. The two copies differ only by rounding.
 //
 // X carries a power-of-two scale 2^-e in its fp16 halves: e follows the largest entry of the previous iterate
 // so that entries sit near 2^12 (far from fp16's subnormals and its 65504 limit); an iterate that still comes
@@ -329,19 +327,6 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
         put_t4(M, row_i(b), row_j0(a), h, l);
       }
   };
-  // By-columns tiles stored row-major: the lane's rows col_i0(a) .. +3 of column col_j(b) go to M[row][col_j(b)]
-  // (2-byte writes). T by rows is stored this way from the same product that gives U, so T and U = 2I - T come
-  // from identical numbers and no second, transposed product is needed.
-  auto put_rows_t = [&](SplitMat& M, const f32x4 v[TQ][TQ], float s) {
-#pragma unroll
-    for (int a = 0; a < TQ; ++a)
-#pragma unroll
-      for (int b = 0; b < TQ; ++b) {
-        half4 h, l;
-        split_scaled4(v[a][b], s, h, l);
-        put_rows4(M, col_i0(a), col_j(b), h, l);
-      }
-  };
   // put_rows that also returns the largest |v| (before scaling).
   auto put_rows_max = [&](SplitMat& M, const f32x4 v[TQ][TQ], float s) {
     float lm = 0.f;
@@ -414,9 +399,9 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
   if (tw) put_cols(sT[xcol_first], x0c, ldexpf(1.f, -e_cur));
   __syncthreads();
 
-  f32x4 accA[TQ][TQ], accC[TQ][TQ];
+  f32x4 accA[TQ][TQ], accB[TQ][TQ], accC[TQ][TQ];
   int xcol_buf = xcol_first;  // where the latest X by columns sits (the segment start and the exact step read it)
-  // Segment start at step k: T_k = W X_k by columns, stored as U_k = 2I - T_k (by columns) and as T_k by rows.
+  // Segment start at step k: T_k = W X_k by columns (into U_k = 2I - T_k) and, with the operands swapped, by rows.
   // After the first segment, X_k by columns sits in sT[k & 1], the buffer T_k goes to: every T wave loads its
   // fragments before any of them stores.
   auto resync = [&](int k) {
@@ -426,9 +411,10 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
     if (xcol_buf == cur) __syncthreads();
     if (tw) {
       mma(fw, fxc, accA);
+      mma(fxc, fw, accB);
       const float unscale = ldexpf(1.f, e_cur);
       put_u(sU[cur], accA, unscale);
-      put_rows_t(sT[cur], accA, unscale);
+      put_rows(sT[cur], accB, unscale);
     }
     __syncthreads();
   };
@@ -453,9 +439,10 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
       frags_of(sU[cur], c0, fu);
       if (!last) {
         frags_of(sT[cur], r0, ft);
-        mma(ft, fu, accA);  // T_k U_k = T_{k+1} by columns
+        mma(ft, fu, accA);  // T_k U_k by columns: U_{k+1}
+        mma(fu, ft, accB);  // (T_k U_k)^T: T_{k+1} by rows
         put_u(sU[nxt], accA, 1.f);
-        put_rows_t(sT[nxt], accA, 1.f);
+        put_rows(sT[nxt], accB, 1.f);
       } else {
         frags_of(sX[cur], r0, ft);
         mma(ft, fu, accA);  // X_k U_k by columns: X_{K-1} for the exact step
