@@ -19,7 +19,8 @@ pytestmark = pytest.mark.gpu
 
 # The five workload shapes plus edge cases: m = 1; N < 64 with several heads (channel h*d + c); a ragged grid with
 # m = 99 > 64 (multi-launch Newton-Schulz with ragged tiles) and d = 128; no NS steps; bf16 at the stage-1 shape;
-# whitening on a small grid; N = 196 tokens that end in a ragged 64-row tile; N = m = 63 (rows not a multiple of 4).
+# whitening on a small grid; N = 196 tokens that end in a ragged 64-row tile; N = m = 63 (rows not a multiple of 4);
+# the largest step count on both solver variants and on the m > 64 path.
 MAIN = [WL.TINY, WL.TINY_R1, WL.PVT_S1, WL.PVT_S3, WL.HIRES_BF16, WL.TRAIN_S1]
 EDGE = [
     WL.TINY.replace(name="m1_8x8_r8", r=8),
@@ -31,6 +32,11 @@ EDGE = [
     WL.PVT_S3.replace(name="s3_B2_h5", B=2),
     WL.TINY.replace(name="d64_20x20_m100_bf16", H=20, W=20, d=64, r=2, dtype=WL.BF16, qk_dist="student_t"),
     WL.TINY.replace(name="odd_9x7_r1_m63", H=9, W=7, r=1),
+    # the most Newton-Schulz steps the library accepts (LF_NS_ITERS_MAX = 64): six runs of coupled steps
+    WL.TINY.replace(name="tiny_K64_m16", ns_iters=64),
+    WL.PVT_S1.replace(name="s1_B1_K64", B=1, ns_iters=64),
+    # the m > 64 path (fp32 products, one launch per step) over four runs of coupled steps
+    WL.TINY.replace(name="ragged_20x20_m100_K40", H=20, W=20, d=64, r=2, ns_iters=40, qk_dist="student_t"),
 ]
 ALL = MAIN + EDGE
 
