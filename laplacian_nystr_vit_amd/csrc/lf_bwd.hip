@@ -36,7 +36,7 @@ __device__ __forceinline__ float sgnf(float x) { return x > 0.f ? 1.f : (x < 0.f
 namespace {
 
 struct BwdWs {
-  size_t T1, part, dX, dS, stats, dWe, dLW, Gq, Gk, dLpart, dL, lampart, dwcpart, total;
+  size_t T1, part, dX, dS, stats, dWe, dLW, Gq, Gk, dLpart, dL, lampart, dwcpart, nsA1, nsA2, nsG, nsD, nsGf, total;
   int nsplitL, rpsL, nlb;
   int lamchunks, dwcbands, dwcrows;
 };
@@ -82,6 +82,13 @@ BwdWs plan(const Shape& s) {
   w.dwcrows = 1;
   w.dwcbands = s.H;
   w.dwcpart = take(4 * G * static_cast<size_t>(w.dwcbands) * 9 * d);
+  // Newton-Schulz reverse chain: A1_k, A2_k, G_k and D_k for every step, and the final adjoint, each m x m
+  const size_t nsk = 4 * G * static_cast<size_t>(s.ns_iters) * m * m;
+  w.nsA1 = take(nsk);
+  w.nsA2 = take(nsk);
+  w.nsG = take(nsk);
+  w.nsD = take(nsk);
+  w.nsGf = take(4 * G * m * m);
   w.total = off;
   return w;
 }
@@ -152,16 +159,20 @@ __global__ __launch_bounds__(256) void k_bwd_small1(const float* __restrict__ T1
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// Newton-Schulz reverse chain on fp32 MFMA, one block of 12 waves per slice, everything in LDS (64 x 64, zero
-// padded: every buffer starts at zero and only ever receives products of zero-padded operands, so all 16 k-steps
-// run fully unrolled). Per step k (from K - 1 down to 0), with G the current adjoint:
-//   phase 1: A1 = W X_k, A2 = X_k W, Z = X_k^T G           (12 waves = 3 products x 4 row strips)
-//   phase 2: dW -= Z X_k^T                                (waves 0-3, one row strip each)
-//            G <- 2G - (G A1^T + A2^T G)                  (waves 4-11, half a row strip each)
-// so every wave issues the same 64 MFMAs per phase. X_{k-1} is loaded into registers during step k.
+// Newton-Schulz reverse chain. With X_{k+1} = 2 X_k - X_k W X_k and G the adjoint of X_{k+1}, step k (from K - 1
+// down to 0) gives
+//   dW -= X_k^T G X_k^T,    G <- 2G - G (W X_k)^T - (X_k W)^T G.
+// Only the second line is a chain: A1_k = W X_k and A2_k = X_k W depend on the saved iterates alone, and the dW
+// terms feed nothing back. So the work runs as four launches on fp32 MFMA (64 x 64 zero-padded tiles in LDS):
+//   k_bwd_ns_pre   A1_k and A2_k for every (slice, step), all in parallel;
+//   k_bwd_ns_chain one block (16 waves) per slice: per step one phase of two products, G <- 2G - (G A1_k^T + A2_k^T G),
+//                  storing each step's G_k and prefetching the next A1, A2 into registers;
+//   k_bwd_ns_dk    D_k = X_k^T G_k X_k^T for every (slice, step), all in parallel;
+//   k_bwd_ns_final dW = -sum_k D_k (k from K - 1 down to 0) + alpha G_0^T (X_0 = alpha W^T), plus the path through
+//                  alpha when asked; blocks of 256 entries.
+// A1, A2, G_k and D_k are [G][K][m][m] float32 in the workspace (the layout of the saved iterates).
 // ---------------------------------------------------------------------------------------------------------
 constexpr int BL = 66;
-constexpr int NSB_WAVES = 12;
 
 // acc[t] += op(A)[strip rows][:] op(B)[:][tile t0 + t] over k = 0..63, with op = transpose when TA / TB.
 template <bool TA, bool TB, int NT>
@@ -198,124 +209,185 @@ __device__ __forceinline__ void store_tiles(float* __restrict__ sC, const f32x4 
   }
 }
 
-// exact_alpha: also the path through alpha = 1 / (c r), c the largest column sum and r the largest row sum of |W|:
-// d alpha = <G, W^T> for the final adjoint G of X_0 = alpha W^T, and dW += d alpha * d alpha / dW, taken at the
-// first largest column and row.
-__global__ __launch_bounds__(64 * NSB_WAVES) void k_bwd_ns(const float* __restrict__ We,
-                                                            const float* __restrict__ xs,
-                                                            const float* __restrict__ alpha,
-                                                            const float* __restrict__ dX, float* __restrict__ dWe,
-                                                            int m, int K, int exact_alpha) {
-  constexpr int NT = 64 * NSB_WAVES;
-  constexpr int PER = (64 * 64 + NT - 1) / NT;  // matrix elements per thread when staging
+// Zero-padded 64 x 64 copy (row stride BL) of an m x m matrix from global memory, by all threads of the block.
+__device__ __forceinline__ void stage_mm(float* __restrict__ sM, const float* __restrict__ src, int m, int nt) {
+  for (int idx = static_cast<int>(threadIdx.x); idx < 64 * 64; idx += nt) {
+    const int i = idx >> 6, j = idx & 63;
+    sM[i * BL + j] = (i < m && j < m) ? src[i * m + j] : 0.f;
+  }
+}
+
+// Accumulator tiles of row strip `strip`, tiles t0 .. t0 + NT - 1, to an m x m matrix in global memory.
+template <int NT>
+__device__ __forceinline__ void store_tiles_mm(float* __restrict__ dst, const f32x4 acc[NT], int strip, int t0, int ln,
+                                               int m) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int j = (t0 + t) * 16 + (ln & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = strip * 16 + 4 * (ln >> 4) + r;
+      if (i < m && j < m) dst[i * m + j] = acc[t][r];
+    }
+  }
+}
+
+constexpr int NSB_THREADS = 512;  // 8 waves
+
+// Block (k, g): A1_k = W X_k (waves 0-3, one row strip each) and A2_k = X_k W (waves 4-7).
+__global__ __launch_bounds__(NSB_THREADS) void k_bwd_ns_pre(const float* __restrict__ We, const float* __restrict__ xs,
+                                                             float* __restrict__ A1s, float* __restrict__ A2s, int m,
+                                                             int K) {
   __shared__ float sW[64 * BL];
-  __shared__ float sXk[64 * BL];
+  __shared__ float sX[64 * BL];
+  const int k = blockIdx.x, g = blockIdx.y, ln = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
+  const size_t mm = static_cast<size_t>(m) * m;
+  stage_mm(sW, We + g * mm, m, NSB_THREADS);
+  stage_mm(sX, xs + (static_cast<size_t>(g) * (K + 1) + k) * mm, m, NSB_THREADS);
+  __syncthreads();
+  f32x4 acc[4];
+  zero_n<4>(acc);
+  const size_t o = (static_cast<size_t>(g) * K + k) * mm;
+  if (wv < 4) {
+    mm64u<false, false, 4>(sW, sX, wv, 0, ln, acc);  // W X_k
+    store_tiles_mm<4>(A1s + o, acc, wv, 0, ln, m);
+  } else {
+    mm64u<false, false, 4>(sX, sW, wv - 4, 0, ln, acc);  // X_k W
+    store_tiles_mm<4>(A2s + o, acc, wv - 4, 0, ln, m);
+  }
+}
+
+// One block per slice: the adjoint chain. Sixteen waves, wave w owning tile (row strip w & 3, column strip w >> 2)
+// of the update: four waves per SIMD hide the LDS operand reads of the fp32 MFMA steps.
+constexpr int NSC_THREADS = 1024;
+__global__ __launch_bounds__(NSC_THREADS) void k_bwd_ns_chain(const float* __restrict__ A1s,
+                                                               const float* __restrict__ A2s,
+                                                               const float* __restrict__ dX, float* __restrict__ Gs,
+                                                               float* __restrict__ Gfin, int m, int K) {
+  constexpr int PER = 64 * 64 / NSC_THREADS;
   __shared__ float sG[2][64 * BL];
   __shared__ float sA1[64 * BL];
   __shared__ float sA2[64 * BL];
-  __shared__ float sZ[64 * BL];
   const int g = blockIdx.x, tid = threadIdx.x, ln = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(wave_id());
   const size_t mm = static_cast<size_t>(m) * m;
-  for (int idx = tid; idx < 64 * BL; idx += NT) {
-    sA1[idx] = 0.f;
-    sA2[idx] = 0.f;
-    sZ[idx] = 0.f;
-    sG[1][idx] = 0.f;
-  }
-  for (int idx = tid; idx < 64 * 64; idx += NT) {
-    const int i = idx >> 6, j = idx & 63;
-    const bool in = i < m && j < m;
-    sW[i * BL + j] = in ? We[g * mm + i * m + j] : 0.f;
-    sG[0][i * BL + j] = in ? dX[g * mm + i * m + j] : 0.f;
-  }
-  // X_{K-1} into registers; each step stores the iterate it holds and loads the next one
-  float xr[PER];
-  auto load_x = [&](int k) {
-    const float* xk = xs + (static_cast<size_t>(g) * (K + 1) + k) * mm;
+  stage_mm(sG[0], dX + g * mm, m, NSC_THREADS);
+  float r1[PER], r2[PER];
+  auto load_a = [&](int k) {
+    const float* a1 = A1s + (static_cast<size_t>(g) * K + k) * mm;
+    const float* a2 = A2s + (static_cast<size_t>(g) * K + k) * mm;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-      const int idx = tid + NT * q;
+      const int idx = tid + NSC_THREADS * q;
       const int i = idx >> 6, j = idx & 63;
-      xr[q] = (idx < 4096 && i < m && j < m) ? xk[i * m + j] : 0.f;
+      const bool in = i < m && j < m;
+      r1[q] = in ? a1[i * m + j] : 0.f;
+      r2[q] = in ? a2[i * m + j] : 0.f;
     }
   };
-  if (K > 0) load_x(K - 1);
-  f32x4 dacc[4];
-  zero_n<4>(dacc);
+  if (K > 0) load_a(K - 1);
   int cur = 0;
+  const int strip = wv & 3, t0 = wv >> 2;
   for (int k = K - 1; k >= 0; --k) {
-    __syncthreads();  // previous step's reads of sXk are done
+    __syncthreads();  // the previous step's reads of sA1 / sA2 are done and sG[cur] is complete
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-      const int idx = tid + NT * q;
-      if (idx < 4096) sXk[(idx >> 6) * BL + (idx & 63)] = xr[q];
+      const int idx = tid + NSC_THREADS * q;
+      const int i = idx >> 6, j = idx & 63;
+      sA1[i * BL + j] = r1[q];
+      sA2[i * BL + j] = r2[q];
+      if (i < m && j < m) Gs[(static_cast<size_t>(g) * K + k) * mm + i * m + j] = sG[cur][i * BL + j];
     }
-    if (k > 0) load_x(k - 1);
-    __syncthreads();
-    {
-      const int prod = wv >> 2, strip = wv & 3;
-      f32x4 acc[4];
-      zero_n<4>(acc);
-      if (prod == 0) {
-        mm64u<false, false, 4>(sW, sXk, strip, 0, ln, acc);  // A1 = W X_k
-        store_tiles<4>(sA1, acc, strip, 0, ln);
-      } else if (prod == 1) {
-        mm64u<false, false, 4>(sXk, sW, strip, 0, ln, acc);  // A2 = X_k W
-        store_tiles<4>(sA2, acc, strip, 0, ln);
-      } else {
-        mm64u<true, false, 4>(sXk, sG[cur], strip, 0, ln, acc);  // Z = X_k^T G
-        store_tiles<4>(sZ, acc, strip, 0, ln);
-      }
-    }
+    if (k > 0) load_a(k - 1);
     __syncthreads();
     const int nxt = cur ^ 1;
-    if (wv < 4) {
-      f32x4 acc[4];
-      zero_n<4>(acc);
-      mm64u<false, true, 4>(sZ, sXk, wv, 0, ln, acc);  // Z X_k^T
+    f32x4 acc[1];
+    zero_n<1>(acc);
+    mm64u<false, true, 1>(sG[cur], sA1, strip, t0, ln, acc);  // G A1^T
+    mm64u<true, false, 1>(sA2, sG[cur], strip, t0, ln, acc);  // + A2^T G
 #pragma unroll
-      for (int t = 0; t < 4; ++t) dacc[t] -= acc[t];
-    } else {
-      const int strip = (wv - 4) & 3, t0 = 2 * ((wv - 4) >> 2);
-      f32x4 acc[2];
-      zero_n<2>(acc);
-      mm64u<false, true, 2>(sG[cur], sA1, strip, t0, ln, acc);  // G A1^T
-      mm64u<true, false, 2>(sA2, sG[cur], strip, t0, ln, acc);  // + A2^T G
+    for (int t = 0; t < 1; ++t) {
+      const int j = (t0 + t) * 16 + (ln & 15);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int j = (t0 + t) * 16 + (ln & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = strip * 16 + 4 * (ln >> 4) + r;
-          sG[nxt][i * BL + j] = 2.f * sG[cur][i * BL + j] - acc[t][r];
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int i = strip * 16 + 4 * (ln >> 4) + r;
+        sG[nxt][i * BL + j] = 2.f * sG[cur][i * BL + j] - acc[t][r];
       }
     }
     cur = nxt;
   }
   __syncthreads();
+  for (int idx = tid; idx < 64 * 64; idx += NSC_THREADS) {
+    const int i = idx >> 6, j = idx & 63;
+    if (i < m && j < m) Gfin[g * mm + i * m + j] = sG[cur][i * BL + j];
+  }
+}
+
+// Block (k, g): D_k = X_k^T (G_k X_k^T), each product on all 8 waves (row strip w & 3, tiles 2 (w >> 2) .. + 1).
+__global__ __launch_bounds__(NSB_THREADS) void k_bwd_ns_dk(const float* __restrict__ xs, const float* __restrict__ Gs,
+                                                            float* __restrict__ Dk, int m, int K) {
+  __shared__ float sX[64 * BL];
+  __shared__ float sG[64 * BL];
+  __shared__ float sY[64 * BL];
+  const int k = blockIdx.x, g = blockIdx.y, ln = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
+  const size_t mm = static_cast<size_t>(m) * m;
+  stage_mm(sX, xs + (static_cast<size_t>(g) * (K + 1) + k) * mm, m, NSB_THREADS);
+  stage_mm(sG, Gs + (static_cast<size_t>(g) * K + k) * mm, m, NSB_THREADS);
+  __syncthreads();
+  const int strip = wv & 3, t0 = 2 * (wv >> 2);
+  f32x4 acc[2];
+  zero_n<2>(acc);
+  mm64u<false, true, 2>(sG, sX, strip, t0, ln, acc);  // G_k X_k^T
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = (t0 + t) * 16 + (ln & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sY[(strip * 16 + 4 * (ln >> 4) + r) * BL + j] = acc[t][r];
+  }
+  __syncthreads();
+  zero_n<2>(acc);
+  mm64u<true, false, 2>(sX, sY, strip, t0, ln, acc);  // X_k^T (G_k X_k^T)
+  store_tiles_mm<2>(Dk + (static_cast<size_t>(g) * K + k) * mm, acc, strip, t0, ln, m);
+}
+
+// Block (chunk of 256 entries, g): dW = -sum_k D_k (k from K - 1 down to 0) + alpha G_0^T, eight D_k loads in
+// flight per thread. With exact_alpha also the path through alpha = 1 / (c r), c the largest column sum and r the
+// largest row sum of |W|: d alpha = <G_0, W^T> and dW += d alpha * d alpha / dW, taken at the first largest column
+// and row (every block of the slice forms these few reductions itself, in a fixed order).
+constexpr int NSF_THREADS = 256;
+__global__ __launch_bounds__(NSF_THREADS) void k_bwd_ns_final(const float* __restrict__ We,
+                                                               const float* __restrict__ alpha,
+                                                               const float* __restrict__ Dk,
+                                                               const float* __restrict__ Gfin,
+                                                               float* __restrict__ dWe, int m, int K,
+                                                               int exact_alpha) {
+  constexpr int NW = NSF_THREADS / 64;
+  __shared__ float s_cs[64], s_rs[64], s_part[NW];
+  __shared__ int s_arg[2];
+  __shared__ float s_da;
+  const int g = blockIdx.y, tid = threadIdx.x, ln = lane_id(), wv = wave_id();
+  const size_t mm = static_cast<size_t>(m) * m;
+  const float* wg = We + g * mm;
+  const float* gf = Gfin + g * mm;
   const float a = alpha[g];
   float da = 0.f, inv_c = 0.f, inv_r = 0.f;
   int jc = 0, ir = 0;
   if (exact_alpha) {
-    // column / row sums of |W| and their first maxima, and d alpha = sum_ij G_ij W_ji (fixed-order reductions)
-    __shared__ float s_cs[64], s_rs[64], s_part[64 * NSB_WAVES / 64];
-    __shared__ int s_arg[2];
-    __shared__ float s_da;
     if (tid < 64) {
       float cs = 0.f, rs = 0.f;
       for (int i = 0; i < m; ++i) {
-        cs += fabsf(sW[i * BL + tid]);
-        rs += fabsf(sW[tid * BL + i]);
+        cs += fabsf(tid < m ? wg[i * m + tid] : 0.f);
+        rs += fabsf(tid < m ? wg[tid * m + i] : 0.f);
       }
       s_cs[tid] = tid < m ? cs : -1.f;
       s_rs[tid] = tid < m ? rs : -1.f;
     }
     float pd = 0.f;
-    for (int idx = tid; idx < 64 * 64; idx += 64 * NSB_WAVES) {
+    for (int idx = tid; idx < 64 * 64; idx += NSF_THREADS) {
       const int i = idx >> 6, j = idx & 63;
-      pd += sG[cur][i * BL + j] * sW[j * BL + i];
+      if (i < m && j < m) pd += gf[i * m + j] * wg[j * m + i];
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) pd += __shfl_xor(pd, off);
@@ -330,7 +402,7 @@ __global__ __launch_bounds__(64 * NSB_WAVES) void k_bwd_ns(const float* __restri
       s_arg[0] = bc;
       s_arg[1] = br;
       float t = 0.f;
-      for (int w2 = 0; w2 < NSB_WAVES; ++w2) t += s_part[w2];
+      for (int w2 = 0; w2 < NW; ++w2) t += s_part[w2];
       s_da = t;
     }
     __syncthreads();
@@ -340,25 +412,27 @@ __global__ __launch_bounds__(64 * NSB_WAVES) void k_bwd_ns(const float* __restri
     inv_r = 1.f / s_rs[ir];
     da = s_da;
   }
-  if (wv < 4) {
+  const int idx = blockIdx.x * NSF_THREADS + tid;
+  if (idx >= m * m) return;
+  const int i = idx / m, j = idx - i * m;
+  const float* dk = Dk + static_cast<size_t>(g) * K * mm + idx;
+  float v = 0.f;
+  int k = K - 1;
+  for (; k >= 7; k -= 8) {
+    float t[8];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int j = t * 16 + (ln & 15);
+    for (int u = 0; u < 8; ++u) t[u] = dk[static_cast<size_t>(k - u) * mm];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = wv * 16 + 4 * (ln >> 4) + r;
-        if (i < m && j < m) {
-          float v = dacc[t][r] + a * sG[cur][j * BL + i];
-          if (exact_alpha) {
-            const float w = sW[i * BL + j];
-            const float sg = w > 0.f ? 1.f : (w < 0.f ? -1.f : 0.f);
-            v += da * (-a * sg) * ((j == jc ? inv_c : 0.f) + (i == ir ? inv_r : 0.f));
-          }
-          dWe[g * mm + i * m + j] = v;
-        }
-      }
-    }
+    for (int u = 0; u < 8; ++u) v -= t[u];
   }
+  for (; k >= 0; --k) v -= dk[static_cast<size_t>(k) * mm];
+  v += a * gf[j * m + i];
+  if (exact_alpha) {
+    const float w = wg[idx];
+    const float sg = w > 0.f ? 1.f : (w < 0.f ? -1.f : 0.f);
+    v += da * (-a * sg) * ((j == jc ? inv_c : 0.f) + (i == ir ? inv_r : 0.f));
+  }
+  dWe[g * mm + idx] = v;
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -788,8 +862,21 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bwd_small1<D>, dim3(s.G, s.m < 8 ? s.m : 8), dim3(256), 0, st, T1, sp.S, sp.P, sp.xs, sp.mu,
                      sp.rstd, dX, dS, stats, s.m, s.ns_iters, s.N, wh);
-  hipLaunchKernelGGL(k_bwd_ns, dim3(s.G), dim3(64 * NSB_WAVES), 0, st, sp.We, sp.xs, sp.alpha, dX, dWe, s.m,
-                     s.ns_iters, ex.exact_alpha ? 1 : 0);
+  {
+    float* A1s = reinterpret_cast<float*>(b + p.nsA1);
+    float* A2s = reinterpret_cast<float*>(b + p.nsA2);
+    float* Gs = reinterpret_cast<float*>(b + p.nsG);
+    float* Dk = reinterpret_cast<float*>(b + p.nsD);
+    float* Gf = reinterpret_cast<float*>(b + p.nsGf);
+    const int Kn = s.ns_iters;
+    if (Kn > 0)
+      hipLaunchKernelGGL(k_bwd_ns_pre, dim3(Kn, s.G), dim3(NSB_THREADS), 0, st, sp.We, sp.xs, A1s, A2s, s.m, Kn);
+    hipLaunchKernelGGL(k_bwd_ns_chain, dim3(s.G), dim3(NSC_THREADS), 0, st, A1s, A2s, dX, Gs, Gf, s.m, Kn);
+    if (Kn > 0)
+      hipLaunchKernelGGL(k_bwd_ns_dk, dim3(Kn, s.G), dim3(NSB_THREADS), 0, st, sp.xs, Gs, Dk, s.m, Kn);
+    hipLaunchKernelGGL(k_bwd_ns_final, dim3(cdiv(static_cast<long>(s.m) * s.m, NSF_THREADS), s.G),
+                       dim3(NSF_THREADS), 0, st, sp.We, sp.alpha, Dk, Gf, dWe, s.m, Kn, ex.exact_alpha ? 1 : 0);
+  }
   hipLaunchKernelGGL(k_bwd_wpart, dim3(cdiv(static_cast<long>(s.m) * D, 256), s.G), dim3(256), 0, st, sp.L, sp.We,
                      dWe, dLW, s.m, D, inv_lam);
   hipLaunchKernelGGL((k_bwd_rowgrad<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(256), 0, st, dY, V, sp.P, dS, sp.CQ,
