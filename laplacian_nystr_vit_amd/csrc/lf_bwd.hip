@@ -19,6 +19,9 @@
 //   dQ_i += dL_{owner(i)} / r^2 (landmarks are r x r block means of Q).
 // Both column means of the whitening backward come from m x d products: mean_i dA_hat[:, l] = (1/N) P_l . (1^T dY)
 // and mean_i (dA_hat A_hat)[:, l] = (1/N) P_l . dP_l, so no extra pass over the N x m matrices is needed.
+#include <type_traits>
+
+#include "../../include/lf_attn.h"
 #include "lf_bwd_internal.h"
 #include "lf_device.h"
 
@@ -27,6 +30,7 @@ namespace lf {
 static inline int cdiv(long a, long b) { return static_cast<int>((a + b - 1) / b); }
 
 constexpr int kDlLw = 8;  // landmarks per thread in the dL reduction
+constexpr int kFragUnits = 2048;  // 16-byte units of the backward Newton-Schulz chain's fragments per (slice, step)
 // Waves per block of the token-row gradient kernel: 8-channel slices, so a block of 64 rows holds d / 8 waves.
 template <int D>
 constexpr int kRowsWaves = D / 8;
@@ -84,9 +88,9 @@ BwdWs plan(const Shape& s) {
   w.dwcpart = take(4 * G * static_cast<size_t>(w.dwcbands) * 9 * d);
   // Newton-Schulz reverse chain: A1_k, A2_k, G_k and D_k for every step, and the final adjoint, each m x m
   const size_t nsk = 4 * G * static_cast<size_t>(s.ns_iters) * m * m;
-  w.nsA1 = take(nsk);
-  w.nsA2 = take(nsk);
-  w.nsG = take(nsk);
+  w.nsA1 = take(G * static_cast<size_t>(s.ns_iters) * kFragUnits * 16);  // split fragments of A1_k and A2_k^T
+  w.nsA2 = take(8 * G * static_cast<size_t>(s.ns_iters));                 // per-step scale exponent and bound
+  w.nsG = take(4 * G * static_cast<size_t>(s.ns_iters) * 4096);  // G_k as zero-padded 64 x 64 tiles
   w.nsD = take(nsk);
   w.nsGf = take(4 * G * m * m);
   w.total = off;
@@ -163,14 +167,15 @@ __global__ __launch_bounds__(256) void k_bwd_small1(const float* __restrict__ T1
 // down to 0) gives
 //   dW -= X_k^T G X_k^T,    G <- 2G - G (W X_k)^T - (X_k W)^T G.
 // Only the second line is a chain: A1_k = W X_k and A2_k = X_k W depend on the saved iterates alone, and the dW
-// terms feed nothing back. So the work runs as four launches on fp32 MFMA (64 x 64 zero-padded tiles in LDS):
-//   k_bwd_ns_pre   A1_k and A2_k for every (slice, step), all in parallel;
-//   k_bwd_ns_chain one block (16 waves) per slice: per step one phase of two products, G <- 2G - (G A1_k^T + A2_k^T G),
-//                  storing each step's G_k and prefetching the next A1, A2 into registers;
+// terms feed nothing back. So the work runs as four launches (64 x 64 zero-padded tiles in LDS):
+//   k_bwd_ns_pre   A1_k and A2_k for every (slice, step), all in parallel (fp32 MFMA), written as scaled
+//                  split-fp16 operand fragments;
+//   k_bwd_ns_chain one block (16 waves) per slice: per step one phase of two split-fp16 products,
+//                  G <- 2G - (G A1_k^T + A2_k^T G), storing each step's G_k;
 //   k_bwd_ns_dk    D_k = X_k^T G_k X_k^T for every (slice, step), all in parallel;
 //   k_bwd_ns_final dW = -sum_k D_k (k from K - 1 down to 0) + alpha G_0^T (X_0 = alpha W^T), plus the path through
 //                  alpha when asked; blocks of 256 entries.
-// A1, A2, G_k and D_k are [G][K][m][m] float32 in the workspace (the layout of the saved iterates).
+// G_k is [G][K][64][64] float32 (zero-padded) and D_k [G][K][m][m] float32 in the workspace.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int BL = 66;
 
@@ -234,13 +239,63 @@ __device__ __forceinline__ void store_tiles_mm(float* __restrict__ dst, const f3
 
 constexpr int NSB_THREADS = 512;  // 8 waves
 
-// Block (k, g): A1_k = W X_k (waves 0-3, one row strip each) and A2_k = X_k W (waves 4-7).
+// The per-(slice, step) launches deal their blocks so that every block of slice g runs on the XCD that runs the
+// chain block of slice g (blocks go to the 8 XCDs round-robin by linear index): what they write for the chain, and
+// what they read of its output, stays in that XCD's L2. False for the padding blocks when G is not a multiple of 8.
+__device__ __forceinline__ bool slice_step_of(int b, int K, int G, int& g, int& k) {
+  const int q = b >> 3;
+  const int grp = q / K;
+  g = grp * 8 + (b & 7);
+  k = q - grp * K;
+  return g < G;
+}
+
+typedef _Float16 bh8 __attribute__((ext_vector_type(8)));
+typedef _Float16 bh4 __attribute__((ext_vector_type(4)));
+typedef float bf8 __attribute__((ext_vector_type(8)));
+
+// Exponent e with mx 2^-e in [2^12, 2^13) (0 for mx = 0; subnormals count as 2^-126).
+__device__ __forceinline__ int ns_scale_exp(float mx) {
+  if (!(mx > 0.f)) return 0;
+  const int bexp = static_cast<int>((__float_as_uint(mx) >> 23) & 0xffu);
+  return (bexp == 0 ? 1 : bexp) - 127 - 12;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Largest v over the wave, in every lane: max within quads (quad_perm [1,0,3,2], [2,3,0,1]), across the quads of a
+// 16-lane row (row_ror 4, 8), then over the four rows through scalar reads of lanes 0, 16, 32, 48.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x124>(v));
+  v = fmaxf(v, dpp_f<0x128>(v));
+  const int b = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+}
+
+// Split-fp16 operand fragments of the chain, per (slice, step) kFragUnits units of 16 bytes. Unit
+// (((mat * 4 + strip) * 2 + c) * 2 + h) * 64 + lane holds half h (0: hi = round_f16(v), 1: lo = round_f16(v - hi))
+// of entries 32 c + 8 (lane / 16) .. + 7 of row strip * 16 + lane % 16 of A1_k 2^-f (mat 0) or A2_k^T 2^-f
+// (mat 1): the operand a lane supplies to v_mfma_f32_16x16x32_f16 as B of G A1_k^T and as A of A2_k^T G.
+
+// Block (slice, step) as dealt by slice_step_of: A1_k = W X_k (waves 0-3, one row strip each) and A2_k = X_k W
+// (waves 4-7), both scaled by 2^-f so that the largest entry of either sits in [2^12, 2^13), written as chain
+// fragments. sc[2 (g K + k)] = f and sc[2 (g K + k) + 1] = gamma_k = 2 + m (max|A1_k| + max|A2_k|), a bound on
+// max|G_new| / max|G| over one chain step (each entry of G A1^T is a sum of m terms |G| |A1|, and likewise A2^T G).
 __global__ __launch_bounds__(NSB_THREADS) void k_bwd_ns_pre(const float* __restrict__ We, const float* __restrict__ xs,
-                                                             float* __restrict__ A1s, float* __restrict__ A2s, int m,
-                                                             int K) {
+                                                             bh8* __restrict__ frag, float* __restrict__ sc, int m,
+                                                             int K, int G) {
   __shared__ float sW[64 * BL];
   __shared__ float sX[64 * BL];
-  const int k = blockIdx.x, g = blockIdx.y, ln = lane_id();
+  __shared__ float s_red[8];
+  int g, k;
+  if (!slice_step_of(static_cast<int>(blockIdx.x), K, G, g, k)) return;
+  const int tid = threadIdx.x, ln = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(wave_id());
   const size_t mm = static_cast<size_t>(m) * m;
   stage_mm(sW, We + g * mm, m, NSB_THREADS);
@@ -248,93 +303,218 @@ __global__ __launch_bounds__(NSB_THREADS) void k_bwd_ns_pre(const float* __restr
   __syncthreads();
   f32x4 acc[4];
   zero_n<4>(acc);
-  const size_t o = (static_cast<size_t>(g) * K + k) * mm;
-  if (wv < 4) {
+  if (wv < 4)
     mm64u<false, false, 4>(sW, sX, wv, 0, ln, acc);  // W X_k
-    store_tiles_mm<4>(A1s + o, acc, wv, 0, ln, m);
-  } else {
+  else
     mm64u<false, false, 4>(sX, sW, wv - 4, 0, ln, acc);  // X_k W
-    store_tiles_mm<4>(A2s + o, acc, wv - 4, 0, ln, m);
-  }
-}
-
-// One block per slice: the adjoint chain. Sixteen waves, wave w owning tile (row strip w & 3, column strip w >> 2)
-// of the update: four waves per SIMD hide the LDS operand reads of the fp32 MFMA steps.
-constexpr int NSC_THREADS = 1024;
-__global__ __launch_bounds__(NSC_THREADS) void k_bwd_ns_chain(const float* __restrict__ A1s,
-                                                               const float* __restrict__ A2s,
-                                                               const float* __restrict__ dX, float* __restrict__ Gs,
-                                                               float* __restrict__ Gfin, int m, int K) {
-  constexpr int PER = 64 * 64 / NSC_THREADS;
-  __shared__ float sG[2][64 * BL];
-  __shared__ float sA1[64 * BL];
-  __shared__ float sA2[64 * BL];
-  const int g = blockIdx.x, tid = threadIdx.x, ln = lane_id();
-  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
-  const size_t mm = static_cast<size_t>(m) * m;
-  stage_mm(sG[0], dX + g * mm, m, NSC_THREADS);
-  float r1[PER], r2[PER];
-  auto load_a = [&](int k) {
-    const float* a1 = A1s + (static_cast<size_t>(g) * K + k) * mm;
-    const float* a2 = A2s + (static_cast<size_t>(g) * K + k) * mm;
+  float mx = 0.f;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int idx = tid + NSC_THREADS * q;
-      const int i = idx >> 6, j = idx & 63;
-      const bool in = i < m && j < m;
-      r1[q] = in ? a1[i * m + j] : 0.f;
-      r2[q] = in ? a2[i * m + j] : 0.f;
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[t][r]));
+  mx = wave_max(mx);
+  if (ln == 0) s_red[wv] = mx;
+  __syncthreads();  // also: every wave is done reading sW and sX
+  const float m1 = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  const float m2 = fmaxf(fmaxf(s_red[4], s_red[5]), fmaxf(s_red[6], s_red[7]));
+  const int f = ns_scale_exp(fmaxf(m1, m2));
+  const int strip = wv & 3;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int j = t * 16 + (ln & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = strip * 16 + 4 * (ln >> 4) + r;
+      const float v = ldexpf(acc[t][r], -f);
+      if (wv < 4)
+        sW[i * BL + j] = v;  // A1 2^-f
+      else
+        sX[j * BL + i] = v;  // A2^T 2^-f
     }
-  };
-  if (K > 0) load_a(K - 1);
-  int cur = 0;
-  const int strip = wv & 3, t0 = wv >> 2;
-  for (int k = K - 1; k >= 0; --k) {
-    __syncthreads();  // the previous step's reads of sA1 / sA2 are done and sG[cur] is complete
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int idx = tid + NSC_THREADS * q;
-      const int i = idx >> 6, j = idx & 63;
-      sA1[i * BL + j] = r1[q];
-      sA2[i * BL + j] = r2[q];
-      if (i < m && j < m) Gs[(static_cast<size_t>(g) * K + k) * mm + i * m + j] = sG[cur][i * BL + j];
-    }
-    if (k > 0) load_a(k - 1);
-    __syncthreads();
-    const int nxt = cur ^ 1;
-    f32x4 acc[1];
-    zero_n<1>(acc);
-    mm64u<false, true, 1>(sG[cur], sA1, strip, t0, ln, acc);  // G A1^T
-    mm64u<true, false, 1>(sA2, sG[cur], strip, t0, ln, acc);  // + A2^T G
-#pragma unroll
-    for (int t = 0; t < 1; ++t) {
-      const int j = (t0 + t) * 16 + (ln & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = strip * 16 + 4 * (ln >> 4) + r;
-        sG[nxt][i * BL + j] = 2.f * sG[cur][i * BL + j] - acc[t][r];
-      }
-    }
-    cur = nxt;
   }
   __syncthreads();
-  for (int idx = tid; idx < 64 * 64; idx += NSC_THREADS) {
-    const int i = idx >> 6, j = idx & 63;
-    if (i < m && j < m) Gfin[g * mm + i * m + j] = sG[cur][i * BL + j];
+  bh8* out = frag + (static_cast<size_t>(g) * K + k) * kFragUnits;
+  for (int u = tid; u < kFragUnits / 2; u += NSB_THREADS) {
+    const int L = u & 63, c = (u >> 6) & 1, s = (u >> 7) & 3, mat = u >> 9;
+    const float* row = (mat ? sX : sW) + (s * 16 + (L & 15)) * BL + 32 * c + 8 * (L >> 4);
+    bf8 v;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = row[t];
+    const bh8 h = __builtin_convertvector(v, bh8);
+    const bh8 l = __builtin_convertvector(v - __builtin_convertvector(h, bf8), bh8);
+    const int base = ((mat * 4 + s) * 2 + c) * 2;
+    out[base * 64 + L] = h;
+    out[(base + 1) * 64 + L] = l;
+  }
+  if (tid == 0) {
+    sc[2 * (static_cast<size_t>(g) * K + k)] = static_cast<float>(f);
+    sc[2 * (static_cast<size_t>(g) * K + k) + 1] = 2.f + static_cast<float>(m) * (m1 + m2);
   }
 }
 
-// Block (k, g): D_k = X_k^T (G_k X_k^T), each product on all 8 waves (row strip w & 3, tiles 2 (w >> 2) .. + 1).
+// Barrier for data exchanged through LDS only: waits for this wave's LDS operations, not for its global loads and
+// stores (a __syncthreads() fence would also drain those, so a prefetch would cost its full latency every step).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+constexpr int NHB = 72;  // fp16 per LDS row of the split adjoint: 144-byte stride, conflict-free 16-byte reads
+
+// The 4 entries G[i0 .. i0+3][j] of a lane's tile, scaled by 2^-e and split into fp16 halves, into the row-major
+// (rh, rl) and transposed (ch, cl) copies of the split adjoint.
+__device__ __forceinline__ void put_split(_Float16* __restrict__ rh, _Float16* __restrict__ rl,
+                                          _Float16* __restrict__ ch, _Float16* __restrict__ cl, const float Gr[4],
+                                          int e, int i0, int j) {
+  f32x4 v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = ldexpf(Gr[r], -e);
+  const bh4 h = __builtin_convertvector(v, bh4);
+  const bh4 l = __builtin_convertvector(v - __builtin_convertvector(h, f32x4), bh4);
+  *reinterpret_cast<bh4*>(&ch[j * NHB + i0]) = h;
+  *reinterpret_cast<bh4*>(&cl[j * NHB + i0]) = l;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    rh[(i0 + r) * NHB + j] = h[r];
+    rl[(i0 + r) * NHB + j] = l[r];
+  }
+}
+
+// One block per slice: the adjoint chain G <- 2G - (G A1_k^T + A2_k^T G), k = K-1 .. 0, one barrier per step.
+// Sixteen waves; wave w owns tile (row strip w & 3, column strip w >> 2) of G and keeps it in fp32 registers (the
+// 2G term, the stored G_k and the final G are exact fp32). The products run on v_mfma_f32_16x16x32_f16 with split
+// operands (hi hi + hi lo + lo hi, fp32 accumulation): G is kept in LDS as G 2^-e in fp16 halves, row-major (A of
+// G A1^T) and transposed (B of A2^T G), double-buffered; the step's A1 / A2 fragments come from the precompute,
+// staged into LDS (double-buffered) from registers loaded one step ahead. The exponent of the next G follows from
+// max|G_k| (reduced through LDS in the previous step) and the bound gamma_k, so the new G is split before the
+// barrier with its largest entry below 2^14: no fp16 overflow, and fp16 subnormals sit 2^-38 below it.
+constexpr int NSC_THREADS = 1024;
+__global__ __launch_bounds__(NSC_THREADS) void k_bwd_ns_chain(const bh8* __restrict__ frag,
+                                                               const float* __restrict__ sc,
+                                                               const float* __restrict__ dX, float* __restrict__ Gs,
+                                                               float* __restrict__ Gfin, int m, int K) {
+  __shared__ __attribute__((aligned(16))) _Float16 sGr[2][2][64 * NHB];
+  __shared__ __attribute__((aligned(16))) _Float16 sGc[2][2][64 * NHB];
+  __shared__ bh8 sA[2][kFragUnits];
+  __shared__ float s_max[2][16];
+  __shared__ float s_sc[2 * LF_NS_ITERS_MAX];
+  const int g = blockIdx.x, tid = threadIdx.x, ln = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
+  const int si = wv & 3, sj = wv >> 2;
+  const int i0 = si * 16 + 4 * (ln >> 4), jj = sj * 16 + (ln & 15);
+  const size_t mm = static_cast<size_t>(m) * m;
+  for (int q = tid; q < 2 * K; q += NSC_THREADS) s_sc[q] = sc[2 * static_cast<size_t>(g) * K + q];
+  float Gr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) Gr[r] = (i0 + r < m && jj < m) ? dX[g * mm + (i0 + r) * m + jj] : 0.f;
+  const bh8* fg = frag + static_cast<size_t>(g) * K * kFragUnits;
+  // Fragments of later steps in flight in three register slots: step j (the t-th step run, t = K - 1 - j) uses
+  // slot t % 3, loaded four steps ahead of its use and copied to LDS one step ahead.
+  bh8 pr[3][2];
+  auto issue = [&](bh8 (&slot)[2], int j) {
+    slot[0] = fg[static_cast<size_t>(j) * kFragUnits + tid];
+    slot[1] = fg[static_cast<size_t>(j) * kFragUnits + tid + NSC_THREADS];
+  };
+  if (K > 0) {
+    sA[0][tid] = fg[static_cast<size_t>(K - 1) * kFragUnits + tid];
+    sA[0][tid + NSC_THREADS] = fg[static_cast<size_t>(K - 1) * kFragUnits + tid + NSC_THREADS];
+  }
+  if (K > 1) issue(pr[1], K - 2);
+  if (K > 2) issue(pr[2], K - 3);
+  if (K > 3) issue(pr[0], K - 4);
+  float lm = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lm = fmaxf(lm, fabsf(Gr[r]));
+  lm = wave_max(lm);
+  if (ln == 0) s_max[0][wv] = lm;
+  lds_barrier();
+  float M = s_max[0][0];
+#pragma unroll
+  for (int q = 1; q < 16; ++q) M = fmaxf(M, s_max[0][q]);
+  int e = ns_scale_exp(M);
+  put_split(sGr[0][0], sGr[0][1], sGc[0][0], sGc[0][1], Gr, e, i0, jj);
+  int cur = 0;
+  // G_k goes out as a 64 x 64 tile (zero padding included) with unconditional stores, so the count of memory
+  // operations in flight is the same on every path and the waits for the fragment slots stay partial.
+  float* gs_base = Gs + static_cast<size_t>(g) * K * 4096 + i0 * 64 + jj;
+  auto step = [&](auto tc, int k) __attribute__((always_inline)) {
+    constexpr int sw = (decltype(tc)::value + 1) % 3;  // slot of step k - 1
+    lds_barrier();  // split G_k, the step's fragments and max|G_k| are complete; step k + 1's reads are done
+    const int nxt = cur ^ 1;
+    M = s_max[cur][0];
+#pragma unroll
+    for (int q = 1; q < 16; ++q) M = fmaxf(M, s_max[cur][q]);
+    if (k > 0) {
+      sA[nxt][tid] = pr[sw][0];
+      sA[nxt][tid + NSC_THREADS] = pr[sw][1];
+      if (k > 3) issue(pr[sw], k - 4);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) gs_base[static_cast<size_t>(k) * 4096 + r * 64] = Gr[r];
+    f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int k0 = 32 * c + 8 * (ln >> 4);
+      const bh8 gh = *reinterpret_cast<const bh8*>(&sGr[cur][0][(si * 16 + (ln & 15)) * NHB + k0]);
+      const bh8 gl = *reinterpret_cast<const bh8*>(&sGr[cur][1][(si * 16 + (ln & 15)) * NHB + k0]);
+      const bh8 th = *reinterpret_cast<const bh8*>(&sGc[cur][0][(sj * 16 + (ln & 15)) * NHB + k0]);
+      const bh8 tl = *reinterpret_cast<const bh8*>(&sGc[cur][1][(sj * 16 + (ln & 15)) * NHB + k0]);
+      const int u1 = ((sj * 2 + c) * 2) * 64 + ln;       // mat 0, strip sj
+      const int u2 = (((4 + si) * 2 + c) * 2) * 64 + ln;  // mat 1, strip si
+      const bh8 b1h = sA[cur][u1], b1l = sA[cur][u1 + 64];
+      const bh8 a2h = sA[cur][u2], a2l = sA[cur][u2 + 64];
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(gh, b1h, a1, 0, 0, 0);
+      a2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2h, th, a2, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(gh, b1l, a1, 0, 0, 0);
+      a2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2h, tl, a2, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(gl, b1h, a1, 0, 0, 0);
+      a2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2l, th, a2, 0, 0, 0);
+    }
+    const int f = static_cast<int>(s_sc[2 * k]);
+    const int en = M > 0.f ? ns_scale_exp(M * s_sc[2 * k + 1]) - 1 : 0;
+    lm = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      Gr[r] = 2.f * Gr[r] - ldexpf(a1[r] + a2[r], e + f);
+      lm = fmaxf(lm, fabsf(Gr[r]));
+    }
+    lm = wave_max(lm);
+    if (ln == 0) s_max[nxt][wv] = lm;
+    put_split(sGr[nxt][0], sGr[nxt][1], sGc[nxt][0], sGc[nxt][1], Gr, en, i0, jj);
+    e = en;
+    cur = nxt;
+  };
+  using T0 = std::integral_constant<int, 0>;
+  using T1 = std::integral_constant<int, 1>;
+  using T2 = std::integral_constant<int, 2>;
+  int k = K - 1;
+  for (; k >= 2; k -= 3) {
+    step(T0{}, k);
+    step(T1{}, k - 1);
+    step(T2{}, k - 2);
+  }
+  if (k >= 0) step(T0{}, k);
+  if (k >= 1) step(T1{}, k - 1);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (i0 + r < m && jj < m) Gfin[g * mm + (i0 + r) * m + jj] = Gr[r];
+}
+
+// Block (slice, step) as dealt by slice_step_of: D_k = X_k^T (G_k X_k^T), each product on all 8 waves (row
+// strip w & 3, tiles 2 (w >> 2) .. + 1).
 __global__ __launch_bounds__(NSB_THREADS) void k_bwd_ns_dk(const float* __restrict__ xs, const float* __restrict__ Gs,
-                                                            float* __restrict__ Dk, int m, int K) {
+                                                            float* __restrict__ Dk, int m, int K, int G) {
   __shared__ float sX[64 * BL];
   __shared__ float sG[64 * BL];
   __shared__ float sY[64 * BL];
-  const int k = blockIdx.x, g = blockIdx.y, ln = lane_id();
+  int g, k;
+  if (!slice_step_of(static_cast<int>(blockIdx.x), K, G, g, k)) return;
+  const int ln = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(wave_id());
   const size_t mm = static_cast<size_t>(m) * m;
   stage_mm(sX, xs + (static_cast<size_t>(g) * (K + 1) + k) * mm, m, NSB_THREADS);
-  stage_mm(sG, Gs + (static_cast<size_t>(g) * K + k) * mm, m, NSB_THREADS);
+  {
+    const float* src = Gs + (static_cast<size_t>(g) * K + k) * 4096;  // 64 x 64 tiles, zero-padded
+    for (int idx = static_cast<int>(threadIdx.x); idx < 64 * 64; idx += NSB_THREADS)
+      sG[(idx >> 6) * BL + (idx & 63)] = src[idx];
+  }
   __syncthreads();
   const int strip = wv & 3, t0 = 2 * (wv >> 2);
   f32x4 acc[2];
@@ -863,17 +1043,19 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
   hipLaunchKernelGGL(k_bwd_small1<D>, dim3(s.G, s.m < 8 ? s.m : 8), dim3(256), 0, st, T1, sp.S, sp.P, sp.xs, sp.mu,
                      sp.rstd, dX, dS, stats, s.m, s.ns_iters, s.N, wh);
   {
-    float* A1s = reinterpret_cast<float*>(b + p.nsA1);
-    float* A2s = reinterpret_cast<float*>(b + p.nsA2);
+    bh8* frag = reinterpret_cast<bh8*>(b + p.nsA1);
+    float* nsc = reinterpret_cast<float*>(b + p.nsA2);
     float* Gs = reinterpret_cast<float*>(b + p.nsG);
     float* Dk = reinterpret_cast<float*>(b + p.nsD);
     float* Gf = reinterpret_cast<float*>(b + p.nsGf);
     const int Kn = s.ns_iters;
+    const int sliceblocks = 8 * cdiv(s.G, 8) * Kn;  // slice_step_of's grid
     if (Kn > 0)
-      hipLaunchKernelGGL(k_bwd_ns_pre, dim3(Kn, s.G), dim3(NSB_THREADS), 0, st, sp.We, sp.xs, A1s, A2s, s.m, Kn);
-    hipLaunchKernelGGL(k_bwd_ns_chain, dim3(s.G), dim3(NSC_THREADS), 0, st, A1s, A2s, dX, Gs, Gf, s.m, Kn);
+      hipLaunchKernelGGL(k_bwd_ns_pre, dim3(sliceblocks), dim3(NSB_THREADS), 0, st, sp.We, sp.xs, frag, nsc, s.m, Kn,
+                         s.G);
+    hipLaunchKernelGGL(k_bwd_ns_chain, dim3(s.G), dim3(NSC_THREADS), 0, st, frag, nsc, dX, Gs, Gf, s.m, Kn);
     if (Kn > 0)
-      hipLaunchKernelGGL(k_bwd_ns_dk, dim3(Kn, s.G), dim3(NSB_THREADS), 0, st, sp.xs, Gs, Dk, s.m, Kn);
+      hipLaunchKernelGGL(k_bwd_ns_dk, dim3(sliceblocks), dim3(NSB_THREADS), 0, st, sp.xs, Gs, Dk, s.m, Kn, s.G);
     hipLaunchKernelGGL(k_bwd_ns_final, dim3(cdiv(static_cast<long>(s.m) * s.m, NSF_THREADS), s.G),
                        dim3(NSF_THREADS), 0, st, sp.We, sp.alpha, Dk, Gf, dWe, s.m, Kn, ex.exact_alpha ? 1 : 0);
   }

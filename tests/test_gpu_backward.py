@@ -24,6 +24,10 @@ CASES = [
     # T = W X formed afresh, and the reverse chain walks back through all of them.
     WL.TINY.replace(name="train_12x12_K26", B=2, H=12, W=12, r=2, ns_iters=26, whiten=True, backward=True,
                     qk_dist="student_t"),
+] + [
+    # Short reverse chains: no step, and step counts below the depth (four steps) at which the chain prefetches
+    # its operands, or that end on each remainder of its three-step unrolled loop.
+    WL.TINY.replace(name=f"train_tiny_K{k}", B=2, ns_iters=k, whiten=True, backward=True) for k in (0, 2, 3, 4, 5)
 ]
 
 
