@@ -19,6 +19,7 @@
 //   dQ_i += dL_{owner(i)} / r^2 (landmarks are r x r block means of Q).
 // Both column means of the whitening backward come from m x d products: mean_i dA_hat[:, l] = (1/N) P_l . (1^T dY)
 // and mean_i (dA_hat A_hat)[:, l] = (1/N) P_l . dP_l, so no extra pass over the N x m matrices is needed.
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/lf_attn.h"
@@ -1012,6 +1013,38 @@ size_t bwd_ws_bytes(const Shape& s) {
   return plan(s).total;
 }
 
+// The reverse Newton-Schulz group (k_bwd_ns_*, then k_bwd_wpart) depends only on dX and produces dW_eps and dL's
+// landmark-kernel term; the row gradients, the dV adjoint, the dL partials and the DWC weight gradient depend
+// only on dS and the whitening statistics. The group runs on one block per slice for most of its time, so it goes
+// to a second stream of the library's own and overlaps those kernels; the caller's stream waits for it before the
+// first kernel that reads its output. One side stream and one pair of events per device, created on first use
+// (non-blocking, default priority); a mutex keeps the fork and join of concurrent calls on one device paired.
+namespace {
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ok = false, tried = false;
+  std::mutex mu;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_init;
+
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  std::lock_guard<std::mutex> lk(g_side_init);
+  if (!ss.tried) {
+    ss.tried = true;
+    ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+  }
+  return ss.ok ? &ss : nullptr;
+}
+}  // namespace
+
 template <typename T, int D>
 static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void* Kv, const void* Vv, const float* w,
                         const SavedPtrs& sp, const void* dYv, void* dQv, void* dKv, void* dVv, void* ws,
@@ -1042,6 +1075,15 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bwd_small1<D>, dim3(s.G, s.m < 8 ? s.m : 8), dim3(256), 0, st, T1, sp.S, sp.P, sp.xs, sp.mu,
                      sp.rstd, dX, dS, stats, s.m, s.ns_iters, s.N, wh);
+  SideStream* side = side_stream();
+  std::unique_lock<std::mutex> lk;
+  hipStream_t ns_st = st;
+  if (side) {
+    lk = std::unique_lock<std::mutex>(side->mu);
+    if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
+    ns_st = side->s;
+  }
   {
     bh8* frag = reinterpret_cast<bh8*>(b + p.nsA1);
     float* nsc = reinterpret_cast<float*>(b + p.nsA2);
@@ -1051,22 +1093,34 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
     const int Kn = s.ns_iters;
     const int sliceblocks = 8 * cdiv(s.G, 8) * Kn;  // slice_step_of's grid
     if (Kn > 0)
-      hipLaunchKernelGGL(k_bwd_ns_pre, dim3(sliceblocks), dim3(NSB_THREADS), 0, st, sp.We, sp.xs, frag, nsc, s.m, Kn,
-                         s.G);
-    hipLaunchKernelGGL(k_bwd_ns_chain, dim3(s.G), dim3(NSC_THREADS), 0, st, frag, nsc, dX, Gs, Gf, s.m, Kn);
+      hipLaunchKernelGGL(k_bwd_ns_pre, dim3(sliceblocks), dim3(NSB_THREADS), 0, ns_st, sp.We, sp.xs, frag, nsc, s.m,
+                         Kn, s.G);
+    hipLaunchKernelGGL(k_bwd_ns_chain, dim3(s.G), dim3(NSC_THREADS), 0, ns_st, frag, nsc, dX, Gs, Gf, s.m, Kn);
     if (Kn > 0)
-      hipLaunchKernelGGL(k_bwd_ns_dk, dim3(sliceblocks), dim3(NSB_THREADS), 0, st, sp.xs, Gs, Dk, s.m, Kn, s.G);
+      hipLaunchKernelGGL(k_bwd_ns_dk, dim3(sliceblocks), dim3(NSB_THREADS), 0, ns_st, sp.xs, Gs, Dk, s.m, Kn, s.G);
     hipLaunchKernelGGL(k_bwd_ns_final, dim3(cdiv(static_cast<long>(s.m) * s.m, NSF_THREADS), s.G),
-                       dim3(NSF_THREADS), 0, st, sp.We, sp.alpha, Dk, Gf, dWe, s.m, Kn, ex.exact_alpha ? 1 : 0);
+                       dim3(NSF_THREADS), 0, ns_st, sp.We, sp.alpha, Dk, Gf, dWe, s.m, Kn, ex.exact_alpha ? 1 : 0);
   }
-  hipLaunchKernelGGL(k_bwd_wpart, dim3(cdiv(static_cast<long>(s.m) * D, 256), s.G), dim3(256), 0, st, sp.L, sp.We,
+  hipLaunchKernelGGL(k_bwd_wpart, dim3(cdiv(static_cast<long>(s.m) * D, 256), s.G), dim3(256), 0, ns_st, sp.L, sp.We,
                      dWe, dLW, s.m, D, inv_lam);
+  if (side && (e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_bwd_rowgrad<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(256), 0, st, dY, V, sp.P, dS, sp.CQ,
                      sp.CK, sp.mu, sp.rstd, stats, Gq, Gk, s.N, s.m, inv_lam, wh);
   e = launch_out_adjoint(s, sp.CK, dS, dY, w, dVv, st);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess) {
+    if (side) (void)hipStreamWaitEvent(st, side->join, 0);  // the caller's stream still ends after the group
+    return e;
+  }
   hipLaunchKernelGGL((k_bwd_dl_partial<T, D>), dim3(s.G * p.nsplitL * p.nlb), dim3(256), 0, st, Q, K, sp.L, Gq, Gk,
                      dLpart, s.N, s.m, p.nsplitL, p.rpsL, p.nlb);
+  if (ex.d_dwc_w) {
+    float* dp = reinterpret_cast<float*>(b + p.dwcpart);
+    hipLaunchKernelGGL((k_dwc_wgrad_partial<T, D>), dim3(p.dwcbands, s.G), dim3(kDwcThreads), 0, st, dY, V, dp, s.H,
+                       s.W, p.dwcrows, p.dwcbands);
+    hipLaunchKernelGGL(k_dwc_wgrad_final<D>, dim3(s.heads * 9), dim3(kDwcThreads), 0, st, dp, ex.d_dwc_w,
+                       s.G / s.heads, s.heads, p.dwcbands);
+  }
+  if (side && (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return e;
   const int md = s.m * D;
   hipLaunchKernelGGL(k_bwd_dl_finalize, dim3(cdiv(static_cast<long>(s.G) * md, 256)), dim3(256), 0, st, dLpart, dLW,
                      dL, s.G, p.nsplitL, md);
@@ -1077,13 +1131,6 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
     hipLaunchKernelGGL(k_bwd_dlam_partial, dim3(p.lamchunks, s.G), dim3(256), 0, st, Gq, Gk, sp.CQ, sp.CK, dWe,
                        sp.We, lp, s.N, s.m, p.lamchunks, inv_lam);
     hipLaunchKernelGGL(k_bwd_dlam_final, dim3(1), dim3(256), 0, st, lp, ex.d_lambda, s.G * p.lamchunks);
-  }
-  if (ex.d_dwc_w) {
-    float* dp = reinterpret_cast<float*>(b + p.dwcpart);
-    hipLaunchKernelGGL((k_dwc_wgrad_partial<T, D>), dim3(p.dwcbands, s.G), dim3(kDwcThreads), 0, st, dY, V, dp, s.H,
-                       s.W, p.dwcrows, p.dwcbands);
-    hipLaunchKernelGGL(k_dwc_wgrad_final<D>, dim3(s.heads * 9), dim3(kDwcThreads), 0, st, dp, ex.d_dwc_w,
-                       s.G / s.heads, s.heads, p.dwcbands);
   }
   return hipGetLastError();
 }
