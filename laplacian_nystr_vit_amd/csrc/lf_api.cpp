@@ -10,6 +10,30 @@
 #include "lf_internal.h"
 #include "lf_bwd_internal.h"
 
+namespace lf {
+
+namespace {
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_init;
+}  // namespace
+
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  std::lock_guard<std::mutex> lk(g_side_init);
+  if (!ss.tried) {
+    ss.tried = true;
+    ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+  }
+  return ss.ok ? &ss : nullptr;
+}
+
+}  // namespace lf
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -215,6 +239,8 @@ int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const voi
   else
     LF_TRY(lf::launch_laplace(s, Q, K, L, CQ, CK, We, st));
   if (wh) LF_TRY(lf::launch_whiten_stats(s, CQ, mu, rstd, st));
+  // The solver stays on the caller's stream: a fork of it to the side stream, concurrent with the C_Q / C_K launch
+  // and S = C_K^T V, measured slower on every shape (the event hand-off costs more than the ~21 us solver hides).
   if (lf::ns_side_supported(s)) {
     // One launch: Newton-Schulz on G CUs, S = C_K^T V on the others.
     LF_TRY(lf::launch_ns_side(s, We, X, xs, alpha, CK, V, S, st));

@@ -19,7 +19,6 @@
 //   dQ_i += dL_{owner(i)} / r^2 (landmarks are r x r block means of Q).
 // Both column means of the whitening backward come from m x d products: mean_i dA_hat[:, l] = (1/N) P_l . (1^T dY)
 // and mean_i (dA_hat A_hat)[:, l] = (1/N) P_l . dP_l, so no extra pass over the N x m matrices is needed.
-#include <mutex>
 #include <type_traits>
 
 #include "../../include/lf_attn.h"
@@ -1016,35 +1015,7 @@ size_t bwd_ws_bytes(const Shape& s) {
 // The reverse Newton-Schulz group (k_bwd_ns_*, then k_bwd_wpart) depends only on dX and produces dW_eps and dL's
 // landmark-kernel term; the row gradients, the dV adjoint, the dL partials and the DWC weight gradient depend
 // only on dS and the whitening statistics. The group runs on one block per slice for most of its time, so it goes
-// to a second stream of the library's own and overlaps those kernels; the caller's stream waits for it before the
-// first kernel that reads its output. One side stream and one pair of events per device, created on first use
-// (non-blocking, default priority); a mutex keeps the fork and join of concurrent calls on one device paired.
-namespace {
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool ok = false, tried = false;
-  std::mutex mu;
-};
-constexpr int kMaxDevices = 64;
-SideStream g_side[kMaxDevices];
-std::mutex g_side_init;
-
-SideStream* side_stream() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& ss = g_side[dev];
-  std::lock_guard<std::mutex> lk(g_side_init);
-  if (!ss.tried) {
-    ss.tried = true;
-    ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
-  }
-  return ss.ok ? &ss : nullptr;
-}
-}  // namespace
-
+// to the side stream and overlaps those kernels.
 template <typename T, int D>
 static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void* Kv, const void* Vv, const float* w,
                         const SavedPtrs& sp, const void* dYv, void* dQv, void* dKv, void* dVv, void* ws,
