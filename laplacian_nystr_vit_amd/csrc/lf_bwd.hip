@@ -30,7 +30,9 @@ namespace lf {
 static inline int cdiv(long a, long b) { return static_cast<int>((a + b - 1) / b); }
 
 constexpr int kDlLw = 8;  // landmarks per thread in the dL reduction
-constexpr int kFragUnits = 2048;  // 16-byte units of the backward Newton-Schulz chain's fragments per (slice, step)
+constexpr int kFragUnits = 2048;
+constexpr int kDwcThreads = 256;  // DWC weight gradient: threads per block
+constexpr int kDwcRun = 8;        // DWC weight gradient: tokens per work item (a run along a grid row)  // 16-byte units of the backward Newton-Schulz chain's fragments per (slice, step)
 // Waves per block of the token-row gradient kernel: 8-channel slices, so a block of 64 rows holds d / 8 waves.
 template <int D>
 constexpr int kRowsWaves = D / 8;
@@ -42,7 +44,7 @@ namespace {
 struct BwdWs {
   size_t T1, part, dX, dS, stats, dWe, dLW, Gq, Gk, dLpart, dL, lampart, dwcpart, nsA1, nsA2, nsG, nsD, nsGf, total;
   int nsplitL, rpsL, nlb;
-  int lamchunks, dwcbands, dwcrows;
+  int lamchunks, dwcseg, dwcblocks;
 };
 
 constexpr size_t kAlign = 256;
@@ -80,12 +82,12 @@ BwdWs plan(const Shape& s) {
   w.dLpart = take(4 * G * static_cast<size_t>(w.nsplitL) * m * d);
   w.dL = take(4 * G * m * d);
   // lambda gradient: per slice, chunks of 64 landmarks' worth of kernel entries; DWC weight gradient: per slice,
-  // bands of dwcrows grid rows, each a [9][d] partial
+  // one [9][d] partial per block of runs of kDwcRun tokens (dwcseg runs per grid row)
   w.lamchunks = cdiv(2L * m * N + m * m, 4096);
   w.lampart = take(4 * G * static_cast<size_t>(w.lamchunks));
-  w.dwcrows = 1;
-  w.dwcbands = s.H;
-  w.dwcpart = take(4 * G * static_cast<size_t>(w.dwcbands) * 9 * d);
+  w.dwcseg = cdiv(s.W, kDwcRun);
+  w.dwcblocks = cdiv(static_cast<long>(s.H) * w.dwcseg, kDwcThreads / (s.d / 4));
+  w.dwcpart = take(4 * G * static_cast<size_t>(w.dwcblocks) * 9 * d);
   // Newton-Schulz reverse chain: A1_k, A2_k, G_k and D_k for every step, and the final adjoint, each m x m
   const size_t nsk = 4 * G * static_cast<size_t>(s.ns_iters) * m * m;
   w.nsA1 = take(G * static_cast<size_t>(s.ns_iters) * kFragUnits * 16);  // split fragments of A1_k and A2_k^T
@@ -935,73 +937,94 @@ __global__ __launch_bounds__(256) void k_bwd_dlam_final(const float* __restrict_
 
 // ---------------------------------------------------------------------------------------------------------
 // DWC weight gradient: dw[h d + c][a][b] = sum over the batch and the grid of dY[(y, x), c] V[(y+a-1, x+b-1), c]
-// (zero outside the grid). Block (slice, band of grid rows, here one row): thread = (channel, token phase)
-// accumulates the 9 taps over its tokens (loop unrolled so their loads overlap), and the phases are summed in LDS in
-// order into a [9][d] partial. The final pass gives each (head, tap) a block whose threads sum strided runs of the
-// (batch, band) partials in order and then combine them in a fixed order.
+// (zero outside the grid). Work item = one run of kDwcRun tokens along a grid row; thread = (4-channel group,
+// item): it keeps the 3 x 3 window of V in registers and slides it along the run, so each token costs one 16-byte
+// load of dY and three of V, and accumulates the 9 taps of its 4 channels. A block's items are summed in LDS in
+// item order into a [9][d] partial per (slice, block); the final pass gives each (head, tap, 16 channels) a block
+// whose threads sum strided runs of the (batch, block) partials in order and then combine them in a fixed order.
 // ---------------------------------------------------------------------------------------------------------
-constexpr int kDwcThreads = 1024;
-
 template <typename T, int D>
 __global__ __launch_bounds__(kDwcThreads) void k_dwc_wgrad_partial(const T* __restrict__ dY, const T* __restrict__ V,
-                                                                   float* __restrict__ part, int H, int W, int rows,
-                                                                   int bands) {
-  constexpr int PH = kDwcThreads / D;
-  const int g = blockIdx.y, band = blockIdx.x, tid = threadIdx.x;
-  const int c = tid % D, ph = tid / D;
+                                                                   float* __restrict__ part, int H, int W, int nseg,
+                                                                   int nblk) {
+  constexpr int CQ = D / 4;                // channel groups of 4
+  constexpr int SLOTS = kDwcThreads / CQ;  // items per block
+  const int g = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
+  const int cq = tid % CQ, slot = tid / CQ;
+  const int item = blk * SLOTS + slot;
   const size_t N = static_cast<size_t>(H) * W;
-  const T* dy = dY + static_cast<size_t>(g) * N * D + c;
-  const T* v = V + static_cast<size_t>(g) * N * D + c;
-  const int y0 = band * rows, y1 = min(H, y0 + rows);
-  float acc[9];
+  const T* dy = dY + static_cast<size_t>(g) * N * D + 4 * cq;
+  const T* v = V + static_cast<size_t>(g) * N * D + 4 * cq;
+  float4 acc[9];
 #pragma unroll
-  for (int q = 0; q < 9; ++q) acc[q] = 0.f;
-#pragma unroll 4
-  for (int t = y0 * W + ph; t < y1 * W; t += PH) {
-    const int y = t / W, x = t % W;
-    const float gy = to_f32(dy[static_cast<size_t>(t) * D]);
+  for (int q = 0; q < 9; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (item < H * nseg) {
+    const int y = item / nseg, x0 = (item - y * nseg) * kDwcRun;
+    auto ldv = [&](int yy, int xx) {
+      return (yy >= 0 && yy < H && xx >= 0 && xx < W) ? load4(v + static_cast<size_t>(yy * W + xx) * D)
+                                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    float4 win[3][3];  // win[a][b] = V(y + a - 1, x + b - 1) for the current x
 #pragma unroll
-    for (int a = 0; a < 3; ++a)
+    for (int a = 0; a < 3; ++a) {
+      win[a][0] = ldv(y + a - 1, x0 - 1);
+      win[a][1] = ldv(y + a - 1, x0);
+    }
 #pragma unroll
-      for (int b = 0; b < 3; ++b) {
-        const int yy = y + a - 1, xx = x + b - 1;
-        if (yy >= 0 && yy < H && xx >= 0 && xx < W)
-          acc[a * 3 + b] += gy * to_f32(v[static_cast<size_t>(yy * W + xx) * D]);
+    for (int t = 0; t < kDwcRun; ++t) {
+      const int x = x0 + t;
+#pragma unroll
+      for (int a = 0; a < 3; ++a) win[a][2] = ldv(y + a - 1, x + 1);
+      const float4 gy = x < W ? load4(dy + static_cast<size_t>(y * W + x) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int b = 0; b < 3; ++b) {
+          float4& r = acc[a * 3 + b];
+          r.x += gy.x * win[a][b].x;
+          r.y += gy.y * win[a][b].y;
+          r.z += gy.z * win[a][b].z;
+          r.w += gy.w * win[a][b].w;
+        }
+#pragma unroll
+      for (int a = 0; a < 3; ++a) {
+        win[a][0] = win[a][1];
+        win[a][1] = win[a][2];
       }
+    }
   }
-  __shared__ float red[9][kDwcThreads];
+  __shared__ float4 red[SLOTS][9][CQ];
 #pragma unroll
-  for (int q = 0; q < 9; ++q) red[q][tid] = acc[q];
+  for (int q = 0; q < 9; ++q) red[slot][q][cq] = acc[q];
   __syncthreads();
-  for (int e = tid; e < 9 * D; e += kDwcThreads) {
-    const int q = e / D, cc = e % D;
+  const float* rf = reinterpret_cast<const float*>(&red[0][0][0]);
+  for (int e = tid; e < 9 * D; e += kDwcThreads) {  // e = q * D + c
     float t = 0.f;
-    for (int p2 = 0; p2 < PH; ++p2) t += red[q][p2 * D + cc];
-    part[((static_cast<size_t>(g) * bands + band) * 9 + q) * D + cc] = t;
+    for (int s2 = 0; s2 < SLOTS; ++s2) t += rf[s2 * 9 * D + e];
+    part[(static_cast<size_t>(g) * nblk + blk) * 9 * D + e] = t;
   }
 }
 
+// Block (head h, tap q; channels 16 blockIdx.y ..): thread (channel, phase) sums the partials j = phase, phase + 16,
+// ... of the B * nblk (batch, block) partials of head h, then phase 0 adds the 16 phase sums in order.
 template <int D>
-__global__ __launch_bounds__(kDwcThreads) void k_dwc_wgrad_final(const float* __restrict__ part,
-                                                                 float* __restrict__ out, int B, int heads,
-                                                                 int bands) {
-  constexpr int PH = kDwcThreads / D;
+__global__ __launch_bounds__(256) void k_dwc_wgrad_final(const float* __restrict__ part, float* __restrict__ out,
+                                                         int B, int heads, int nblk) {
   const int h = blockIdx.x / 9, q = blockIdx.x % 9, tid = threadIdx.x;
-  const int c = tid % D, ph = tid / D;
-  const int n = B * bands;  // terms j = b * bands + band
+  const int c = blockIdx.y * 16 + (tid & 15), ph = tid >> 4;
+  const int n = B * nblk;
   float s = 0.f;
 #pragma unroll 4
-  for (int j = ph; j < n; j += PH) {
-    const int b = j / bands, bd = j % bands;
-    const int g = b * heads + h;
-    s += part[((static_cast<size_t>(g) * bands + bd) * 9 + q) * D + c];
+  for (int j = ph; j < n; j += 16) {
+    const int b = j / nblk, k = j - b * nblk;
+    s += part[((static_cast<size_t>(b) * heads + h) * nblk + k) * 9 * D + q * D + c];
   }
-  __shared__ float red[kDwcThreads];
+  __shared__ float red[256];
   red[tid] = s;
   __syncthreads();
   if (ph == 0) {
     float t = 0.f;
-    for (int p2 = 0; p2 < PH; ++p2) t += red[p2 * D + c];
+    for (int p2 = 0; p2 < 16; ++p2) t += red[p2 * 16 + (tid & 15)];
     out[(static_cast<size_t>(h) * D + c) * 9 + q] = t;
   }
 }
@@ -1086,10 +1109,10 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
                      dLpart, s.N, s.m, p.nsplitL, p.rpsL, p.nlb);
   if (ex.d_dwc_w) {
     float* dp = reinterpret_cast<float*>(b + p.dwcpart);
-    hipLaunchKernelGGL((k_dwc_wgrad_partial<T, D>), dim3(p.dwcbands, s.G), dim3(kDwcThreads), 0, st, dY, V, dp, s.H,
-                       s.W, p.dwcrows, p.dwcbands);
-    hipLaunchKernelGGL(k_dwc_wgrad_final<D>, dim3(s.heads * 9), dim3(kDwcThreads), 0, st, dp, ex.d_dwc_w,
-                       s.G / s.heads, s.heads, p.dwcbands);
+    hipLaunchKernelGGL((k_dwc_wgrad_partial<T, D>), dim3(p.dwcblocks, s.G), dim3(kDwcThreads), 0, st, dY, V, dp,
+                       s.H, s.W, p.dwcseg, p.dwcblocks);
+    hipLaunchKernelGGL(k_dwc_wgrad_final<D>, dim3(s.heads * 9, D / 16), dim3(256), 0, st, dp, ex.d_dwc_w,
+                       s.G / s.heads, s.heads, p.dwcblocks);
   }
   if (side && (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return e;
   const int md = s.m * D;
