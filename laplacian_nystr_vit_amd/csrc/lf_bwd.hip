@@ -39,6 +39,15 @@ constexpr int kRowsWaves = D / 8;
 
 __device__ __forceinline__ float sgnf(float x) { return x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f); }
 
+// sign(x - l) from xs = x 2^100 (exact): fmaf(l, -2^100, xs) is (x - l) 2^100 rounded once, and its median with -1
+// and 1 is the sign whenever x == l or |x - l| >= 2^-100 (for |l| < 2^28; a larger difference may round to +-inf,
+// which keeps its sign). Two VALU operations where the three-way sign takes two compares and two selects; an fp32
+// difference of values of order one is 0 or at least 2^-24 in magnitude.
+constexpr float kSgnScale = 0x1p100f;
+__device__ __forceinline__ float sgn_of_scaled(float xs, float l) {
+  return __builtin_amdgcn_fmed3f(fmaf(l, -kSgnScale, xs), -1.f, 1.f);
+}
+
 namespace {
 
 struct BwdWs {
@@ -776,8 +785,8 @@ __global__ __launch_bounds__(256) void k_bwd_dl_partial(const T* __restrict__ Q,
     float xq[RG], xk[RG], wq[LW][RG], wk[LW][RG];
 #pragma unroll
     for (int u = 0; u < RG; ++u) {
-      xq[u] = to_f32(qc[static_cast<size_t>(i + u) * D]);
-      xk[u] = to_f32(kc[static_cast<size_t>(i + u) * D]);
+      xq[u] = to_f32(qc[static_cast<size_t>(i + u) * D]) * kSgnScale;
+      xk[u] = to_f32(kc[static_cast<size_t>(i + u) * D]) * kSgnScale;
     }
 #pragma unroll
     for (int j = 0; j < LW; ++j)
@@ -790,14 +799,18 @@ __global__ __launch_bounds__(256) void k_bwd_dl_partial(const T* __restrict__ Q,
     for (int j = 0; j < LW; ++j)
 #pragma unroll
       for (int u = 0; u < RG; ++u) {
-        acc[j] += wq[j][u] * sgnf(xq[u] - lv[j]);
-        acc[j] += wk[j][u] * sgnf(xk[u] - lv[j]);
+        acc[j] = fmaf(wq[j][u], sgn_of_scaled(xq[u], lv[j]), acc[j]);
+        acc[j] = fmaf(wk[j][u], sgn_of_scaled(xk[u], lv[j]), acc[j]);
       }
   }
   for (; i < r1; ++i) {
-    const float xq = to_f32(qc[static_cast<size_t>(i) * D]), xk = to_f32(kc[static_cast<size_t>(i) * D]);
+    const float xq = to_f32(qc[static_cast<size_t>(i) * D]) * kSgnScale;
+    const float xk = to_f32(kc[static_cast<size_t>(i) * D]) * kSgnScale;
 #pragma unroll
-    for (int j = 0; j < LW; ++j) acc[j] += gq[j][i] * sgnf(xq - lv[j]) + gk[j][i] * sgnf(xk - lv[j]);
+    for (int j = 0; j < LW; ++j) {
+      acc[j] = fmaf(gq[j][i], sgn_of_scaled(xq, lv[j]), acc[j]);
+      acc[j] = fmaf(gk[j][i], sgn_of_scaled(xk, lv[j]), acc[j]);
+    }
   }
 #pragma unroll
   for (int j = 0; j < LW; ++j)
@@ -837,10 +850,10 @@ __global__ __launch_bounds__(512) void k_bwd_rows(const T* __restrict__ Q, const
   const T* X = (side == 0 ? Q : K) + (static_cast<size_t>(g) * N + row) * D + c0;
   const float* gx = (side == 0 ? Gq : Gk) + static_cast<size_t>(g) * m * N + row;  // landmark-major: gx[l * N]
   const float* __restrict__ Lg = L + static_cast<size_t>(g) * m * D + c0;
-  float x[CW], acc[CW];
+  float x[CW], acc[CW];  // x: the row's values times kSgnScale
 #pragma unroll
   for (int c = 0; c < CW; ++c) {
-    x[c] = to_f32(X[c]);
+    x[c] = to_f32(X[c]) * kSgnScale;
     acc[c] = 0.f;
   }
   constexpr int LC = 8;
@@ -857,7 +870,7 @@ __global__ __launch_bounds__(512) void k_bwd_rows(const T* __restrict__ Q, const
       if (l0 + u < m) {
         const float* __restrict__ lp = Lg + static_cast<size_t>(l0 + u) * D;
 #pragma unroll
-        for (int c = 0; c < CW; ++c) acc[c] = fmaf(-gc[u], sgnf(x[c] - lp[c]), acc[c]);
+        for (int c = 0; c < CW; ++c) acc[c] = fmaf(-gc[u], sgn_of_scaled(x[c], lp[c]), acc[c]);
       }
     }
   }
