@@ -110,6 +110,8 @@ def _gpu_backward_ex(wl, flags):
 
 PARAM_CASES = [
     WL.TRAIN_S1.replace(name="train_s1_B2", B=2),
+    # m N = 729, not a multiple of 4: the lambda reduction takes its entry-by-entry path throughout
+    WL.TINY.replace(name="train_9x9_r3", B=2, H=9, W=9, r=3, whiten=True, backward=True),
     WL.TINY.replace(name="train_tiny_whiten_h2", B=2, heads=2, whiten=True, backward=True),
     WL.TINY.replace(name="train_ragged_10x6_d32", H=10, W=6, d=32, r=2, whiten=True, backward=True),
     WL.TRAIN_S1.replace(name="train_s1_bf16_B2", B=2, dtype=WL.BF16),
