@@ -115,6 +115,24 @@ BwdWs plan(const Shape& s) {
 // column means. m x m x d work per slice, on the VALU. The slice's output rows are spread over gridDim.y blocks
 // (rows l = blockIdx.y, blockIdx.y + gridDim.y, ...); each block forms the whole dP, which every dS row needs.
 // ---------------------------------------------------------------------------------------------------------
+// Copy of n <= MAXN floats from global memory to LDS by the NT threads of a block: every load is issued before the
+// first store, so the block waits for one memory round trip instead of one per strided pass.
+template <int NT, int MAXN>
+__device__ __forceinline__ void stage_flat(float* __restrict__ dst, const float* __restrict__ src, int n) {
+  constexpr int IT = (MAXN + NT - 1) / NT;
+  float v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = static_cast<int>(threadIdx.x) + it * NT;
+    v[it] = idx < n ? src[idx] : 0.f;
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = static_cast<int>(threadIdx.x) + it * NT;
+    if (idx < n) dst[idx] = v[it];
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_small1(const float* __restrict__ T1, const float* __restrict__ S,
                                                     const float* __restrict__ P, const float* __restrict__ xs,
@@ -129,13 +147,10 @@ __global__ __launch_bounds__(256) void k_bwd_small1(const float* __restrict__ T1
   const int g = blockIdx.x, part = blockIdx.y, nparts = gridDim.y, tid = threadIdx.x;
   const size_t md = static_cast<size_t>(m) * D, mm = static_cast<size_t>(m) * m;
   const float* t1 = T1 + static_cast<size_t>(g) * (m + 1) * D;
-  for (int idx = tid; idx < (m + 1) * D; idx += 256) sT1[idx] = t1[idx];
-  for (int idx = tid; idx < m * D; idx += 256) {
-    sS[idx] = S[g * md + idx];
-    sP[idx] = P[g * md + idx];
-  }
-  const float* xk = xs + (static_cast<size_t>(g) * (K + 1) + K) * mm;
-  for (int idx = tid; idx < m * m; idx += 256) sX[idx] = xk[idx];
+  stage_flat<256, 65 * D>(sT1, t1, (m + 1) * D);
+  stage_flat<256, 64 * D>(sS, S + g * md, m * D);
+  stage_flat<256, 64 * D>(sP, P + g * md, m * D);
+  stage_flat<256, 64 * 64>(sX, xs + (static_cast<size_t>(g) * (K + 1) + K) * mm, m * m);
   __syncthreads();
   for (int idx = tid; idx < m * D; idx += 256) {
     const int l = idx / D, c = idx % D;
@@ -225,11 +240,22 @@ __device__ __forceinline__ void store_tiles(float* __restrict__ sC, const f32x4 
   }
 }
 
-// Zero-padded 64 x 64 copy (row stride BL) of an m x m matrix from global memory, by all threads of the block.
-__device__ __forceinline__ void stage_mm(float* __restrict__ sM, const float* __restrict__ src, int m, int nt) {
-  for (int idx = static_cast<int>(threadIdx.x); idx < 64 * 64; idx += nt) {
+// Zero-padded 64 x 64 copy (row stride BL) of an m x m matrix from global memory, by the NT threads of the block,
+// every load issued before the first store.
+template <int NT>
+__device__ __forceinline__ void stage_mm(float* __restrict__ sM, const float* __restrict__ src, int m) {
+  constexpr int IT = 64 * 64 / NT;
+  float v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = static_cast<int>(threadIdx.x) + it * NT;
     const int i = idx >> 6, j = idx & 63;
-    sM[i * BL + j] = (i < m && j < m) ? src[i * m + j] : 0.f;
+    v[it] = (i < m && j < m) ? src[i * m + j] : 0.f;
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = static_cast<int>(threadIdx.x) + it * NT;
+    sM[(idx >> 6) * BL + (idx & 63)] = v[it];
   }
 }
 
@@ -309,8 +335,8 @@ __global__ __launch_bounds__(NSB_THREADS) void k_bwd_ns_pre(const float* __restr
   const int tid = threadIdx.x, ln = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(wave_id());
   const size_t mm = static_cast<size_t>(m) * m;
-  stage_mm(sW, We + g * mm, m, NSB_THREADS);
-  stage_mm(sX, xs + (static_cast<size_t>(g) * (K + 1) + k) * mm, m, NSB_THREADS);
+  stage_mm<NSB_THREADS>(sW, We + g * mm, m);
+  stage_mm<NSB_THREADS>(sX, xs + (static_cast<size_t>(g) * (K + 1) + k) * mm, m);
   __syncthreads();
   f32x4 acc[4];
   zero_n<4>(acc);
@@ -520,11 +546,18 @@ __global__ __launch_bounds__(NSB_THREADS) void k_bwd_ns_dk(const float* __restri
   const int ln = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(wave_id());
   const size_t mm = static_cast<size_t>(m) * m;
-  stage_mm(sX, xs + (static_cast<size_t>(g) * (K + 1) + k) * mm, m, NSB_THREADS);
+  stage_mm<NSB_THREADS>(sX, xs + (static_cast<size_t>(g) * (K + 1) + k) * mm, m);
   {
     const float* src = Gs + (static_cast<size_t>(g) * K + k) * 4096;  // 64 x 64 tiles, zero-padded
-    for (int idx = static_cast<int>(threadIdx.x); idx < 64 * 64; idx += NSB_THREADS)
-      sG[(idx >> 6) * BL + (idx & 63)] = src[idx];
+    constexpr int IT = 64 * 64 / NSB_THREADS;
+    float v[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) v[it] = src[threadIdx.x + it * NSB_THREADS];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = static_cast<int>(threadIdx.x) + it * NSB_THREADS;
+      sG[(idx >> 6) * BL + (idx & 63)] = v[it];
+    }
   }
   __syncthreads();
   const int strip = wv & 3, t0 = 2 * (wv >> 2);
