@@ -707,13 +707,24 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
   const T* A = (side == 0 ? dY : V) + static_cast<size_t>(g) * N * D;
   const float* Bm = (side == 0 ? P : dS) + static_cast<size_t>(g) * m * D;
-  for (int idx = tid; idx < 64 * D; idx += 256) {
-    const int rr = idx / D, c = idx % D;
-    sA[rr * LDA + c] = (i0 + rr < N) ? to_f32(A[static_cast<size_t>(i0 + rr) * D + c]) : 0.f;
-  }
-  for (int idx = tid; idx < D * 64; idx += 256) {
-    const int l = idx / D, c = idx % D;
-    sB[c * LDB + l] = (l < m) ? Bm[static_cast<size_t>(l) * D + c] : 0.f;
+  {
+    // both tiles' loads in flight before the first LDS store
+    constexpr int IT = 64 * D / 256;
+    float va[IT], vb[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = tid + it * 256;
+      const int r = idx / D, c = idx % D;  // token row of A, landmark of B
+      va[it] = (i0 + r < N) ? to_f32(A[static_cast<size_t>(i0 + r) * D + c]) : 0.f;
+      vb[it] = (r < m) ? Bm[static_cast<size_t>(r) * D + c] : 0.f;
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = tid + it * 256;
+      const int r = idx / D, c = idx % D;
+      sA[r * LDA + c] = va[it];
+      sB[c * LDB + r] = vb[it];
+    }
   }
   __syncthreads();
   // all 4 landmark tiles: the B columns past m are staged as zeros
