@@ -389,10 +389,6 @@ __global__ __launch_bounds__(NSB_THREADS) void k_bwd_ns_pre(const float* __restr
   }
 }
 
-// Barrier for data exchanged through LDS only: waits for this wave's LDS operations, not for its global loads and
-// stores (a __syncthreads() fence would also drain those, so a prefetch would cost its full latency every step).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 constexpr int NHB = 72;  // fp16 per LDS row of the split adjoint: 144-byte stride, conflict-free 16-byte reads
 
 // The 4 entries G[i0 .. i0+3][j] of a lane's tile, scaled by 2^-e and split into fp16 halves, into the row-major

@@ -63,6 +63,11 @@ __device__ __forceinline__ void store4(bf16_t* p, float4 v) {
   *reinterpret_cast<uint2*>(p) = u;
 }
 
+// Barrier for data exchanged through LDS only: waits for this wave's LDS operations, not for its global loads and
+// stores (the fence of __syncthreads() also drains those, so a store or prefetch in flight would cost its full
+// latency at every barrier of a loop).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
