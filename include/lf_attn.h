@@ -18,9 +18,13 @@
  *            bit pattern). Intermediates are float32: L [G][m][d]; C_Q and C_K landmark-major [G][m][N] (element
  *            [g][l][i] is C[i][l] of the formulas); W_eps and X [G][m][m]; S and P [G][m][d]; mu and rstd [G][m].
  *            The DWC weight is float32 [heads*d][3][3].
- *  Pointers: every pointer is a device pointer owned by the caller, 16-byte aligned. The library never allocates,
- *            frees or synchronises. Work is enqueued on `stream` (a hipStream_t; NULL means the null stream)
- *            and the call returns as soon as it is enqueued.
+ *  Pointers: every pointer is a device pointer owned by the caller, 16-byte aligned. The library never allocates
+ *            or frees memory and never synchronises. Work is enqueued on `stream` (a hipStream_t; NULL means the
+ *            null stream) and the call returns as soon as it is enqueued. The backward calls also use one
+ *            non-blocking stream of the library's own per device (default priority), created with two events on
+ *            their first call on that device and kept until the process ends: part of their work forks to it
+ *            after an event recorded on `stream`, and `stream` waits for it before the call's last kernels, so
+ *            everything the call does is complete when work enqueued on `stream` after it starts.
  *  Errors:   every entry point returns LF_OK (0) or a negative code. Parameters, pointers and workspace sizes are
  *            checked on the host before anything is launched; on an error nothing is launched. LF_EHIP reports a
  *            failed launch (hipGetLastError). Nothing throws across this ABI. Calls are reentrant; calls that
