@@ -155,3 +155,39 @@ def test_exact_alpha_matches_oracle():
         assert e <= tol(wl), (n, e)
     assert relF(ref0["dQ"], ref["dQ"]) > 10 * tol(wl)
     assert abs(ref0["dlam"] - ref["dlam"]) > 10 * tol(wl) * abs(ref["dlam"])
+
+
+def test_backward_on_a_user_stream_is_ordered_and_bitwise_stable():
+    """The backward forks part of its work to the library's own stream and joins it back onto the caller's stream.
+    On a user stream, two calls in a row, the second with other dY and a workspace filled with garbage, must give
+    the gradients of a call on the current stream bit for bit, and each output must be complete when the user
+    stream's next work (a copy) runs."""
+    note("[gpu] backward on a user stream")
+    wl = WL.TRAIN_S1.replace(name="train_s1_B2", B=2)
+    p = params(wl)
+    t = upload(wl)
+    fwd_b, saved_b, bwd_b = lf.lf_attn_query(p)
+    ws = torch.empty(max(fwd_b, bwd_b), dtype=torch.uint8, device="cuda")
+    saved = torch.empty(saved_b, dtype=torch.uint8, device="cuda")
+    Y = torch.empty_like(t["Q"])
+    lf.lf_attn_fwd(p, t["Q"], t["K"], t["V"], t["w"], Y, saved, ws)
+    dY2 = torch.flip(t["dY"], dims=[0]).contiguous()
+    outs_ref = []
+    for dy in (t["dY"], dY2):
+        dQ, dK, dV = torch.empty_like(t["Q"]), torch.empty_like(t["K"]), torch.empty_like(t["V"])
+        lf.lf_attn_bwd(p, t["Q"], t["K"], t["V"], t["w"], saved, dy, dQ, dK, dV, ws)
+        outs_ref.append((dQ, dK, dV))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    copies = []
+    with torch.cuda.stream(s):
+        ws.fill_(0xA5)
+        for dy in (t["dY"], dY2):
+            dQ, dK, dV = torch.empty_like(t["Q"]), torch.empty_like(t["K"]), torch.empty_like(t["V"])
+            lf.lf_attn_bwd(p, t["Q"], t["K"], t["V"], t["w"], saved, dy, dQ, dK, dV, ws, stream=s)
+            copies.append(tuple(x.clone() for x in (dQ, dK, dV)))  # runs on s right after the call's work
+    s.synchronize()
+    for got, ref in zip(copies, outs_ref):
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b)
