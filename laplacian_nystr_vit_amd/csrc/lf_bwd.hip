@@ -415,9 +415,10 @@ __device__ __forceinline__ void put_split(_Float16* __restrict__ rh, _Float16* _
 // 2G term, the stored G_k and the final G are exact fp32). The products run on v_mfma_f32_16x16x32_f16 with split
 // operands (hi hi + hi lo + lo hi, fp32 accumulation): G is kept in LDS as G 2^-e in fp16 halves, row-major (A of
 // G A1^T) and transposed (B of A2^T G), double-buffered; the step's A1 / A2 fragments come from the precompute,
-// staged into LDS (double-buffered) from registers loaded one step ahead. The exponent of the next G follows from
-// max|G_k| (reduced through LDS in the previous step) and the bound gamma_k, so the new G is split before the
-// barrier with its largest entry below 2^14: no fp16 overflow, and fp16 subnormals sit 2^-38 below it.
+// loaded into registers four steps ahead and copied into LDS (double-buffered) one step ahead. The exponent of
+// the next G follows from max|G_k| (a DPP wave maximum, combined through LDS in the previous step) and the bound
+// gamma_k, so the new G is split before the barrier with its bound below 2^14: no fp16 overflow, and the fp16
+// subnormal range starts 2^-38 below that bound.
 constexpr int NSC_THREADS = 1024;
 __global__ __launch_bounds__(NSC_THREADS) void k_bwd_ns_chain(const bh8* __restrict__ frag,
                                                                const float* __restrict__ sc,
