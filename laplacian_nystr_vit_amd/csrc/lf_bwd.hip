@@ -1092,7 +1092,8 @@ size_t bwd_ws_bytes(const Shape& s) {
 // The reverse Newton-Schulz group (k_bwd_ns_*, then k_bwd_wpart) depends only on dX and produces dW_eps and dL's
 // landmark-kernel term; the row gradients, the dV adjoint, the dL partials and the DWC weight gradient depend
 // only on dS and the whitening statistics. The group runs on one block per slice for most of its time, so it goes
-// to the side stream and overlaps those kernels.
+// to the side stream and overlaps those kernels. After the join the lambda gradient, which needs only Gq, Gk and
+// dW_eps, forks to the side stream once more, next to the dL finalisation and the token rows.
 template <typename T, int D>
 static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void* Kv, const void* Vv, const float* w,
                         const SavedPtrs& sp, const void* dYv, void* dQv, void* dKv, void* dVv, void* ws,
@@ -1169,17 +1170,27 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
                        s.G / s.heads, s.heads, p.dwcblocks);
   }
   if (side && (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return e;
+  if (ex.d_lambda) {
+    // The lambda gradient reads Gq, Gk and dW_eps, all complete here, and nothing reads it: it goes to the side
+    // stream again, next to dL and the token rows, and the caller's stream waits for it at the end.
+    hipStream_t lam_st = st;
+    if (side) {
+      if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
+      lam_st = side->s;
+    }
+    float* lp = reinterpret_cast<float*>(b + p.lampart);
+    hipLaunchKernelGGL(k_bwd_dlam_partial, dim3(p.lamchunks, s.G), dim3(256), 0, lam_st, Gq, Gk, sp.CQ, sp.CK, dWe,
+                       sp.We, lp, s.N, s.m, p.lamchunks, inv_lam);
+    hipLaunchKernelGGL(k_bwd_dlam_final, dim3(1), dim3(256), 0, lam_st, lp, ex.d_lambda, s.G * p.lamchunks);
+    if (side && (e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
+  }
   const int md = s.m * D;
   hipLaunchKernelGGL(k_bwd_dl_finalize, dim3(cdiv(static_cast<long>(s.G) * md, 256)), dim3(256), 0, st, dLpart, dLW,
                      dL, s.G, p.nsplitL, md);
   hipLaunchKernelGGL((k_bwd_rows<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(64 * kRowsWaves<D>), 0, st, Q,
                      K, sp.L, Gq, Gk, dL, dQ, dK, s.N, s.m, s.W, s.r);
-  if (ex.d_lambda) {
-    float* lp = reinterpret_cast<float*>(b + p.lampart);
-    hipLaunchKernelGGL(k_bwd_dlam_partial, dim3(p.lamchunks, s.G), dim3(256), 0, st, Gq, Gk, sp.CQ, sp.CK, dWe,
-                       sp.We, lp, s.N, s.m, p.lamchunks, inv_lam);
-    hipLaunchKernelGGL(k_bwd_dlam_final, dim3(1), dim3(256), 0, st, lp, ex.d_lambda, s.G * p.lamchunks);
-  }
+  if (side && ex.d_lambda && (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return e;
   return hipGetLastError();
 }
 
