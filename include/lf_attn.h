@@ -22,8 +22,8 @@
  *            or frees memory and never synchronises. Work is enqueued on `stream` (a hipStream_t; NULL means the
  *            null stream) and the call returns as soon as it is enqueued. The backward calls also use one
  *            non-blocking stream of the library's own per device (default priority), created with two events on
- *            their first call on that device and kept until the process ends: part of their work forks to it
- *            after an event recorded on `stream`, and `stream` waits for it before the call's last kernels, so
+ *            their first call on that device and kept until the process ends: parts of their work fork to it
+ *            after events recorded on `stream`, and `stream` waits on events recorded after each part, so
  *            everything the call does is complete when work enqueued on `stream` after it starts.
  *  Errors:   every entry point returns LF_OK (0) or a negative code. Parameters, pointers and workspace sizes are
  *            checked on the host before anything is launched; on an error nothing is launched. LF_EHIP reports a
