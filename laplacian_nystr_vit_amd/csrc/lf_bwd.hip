@@ -1122,7 +1122,7 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
 
   hipError_t e = launch_ckv_general(s, sp.CQ, 1, dY, part, T1, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bwd_small1<D>, dim3(s.G, s.m < 8 ? s.m : 8), dim3(256), 0, st, T1, sp.S, sp.P, sp.xs, sp.mu,
+  hipLaunchKernelGGL(k_bwd_small1<D>, dim3(s.G, s.m < 32 ? s.m : 32), dim3(256), 0, st, T1, sp.S, sp.P, sp.xs, sp.mu,
                      sp.rstd, dX, dS, stats, s.m, s.ns_iters, s.N, wh);
   SideStream* side = side_stream();
   std::unique_lock<std::mutex> lk;
