@@ -346,42 +346,43 @@ __global__ __launch_bounds__(256) void k_ckv_finalize(const float* __restrict__ 
 // =====================================================================================================
 // landmark_mix: P[g][l][c] = rstd[l] * sum_k X[g][l][k] S[g][k][c]   (X = Newton-Schulz pseudo-inverse,
 //   [note] Designs 2 and 3; rstd from the diagonal whitening of Design 1). m x m times m x D per slice.
-// Block: 16 landmark rows x D channels of one slice; X rows and 64-row chunks of S are staged in LDS.
+// Block: 256 / D landmark rows x D channels of one slice, one output per thread; X rows and 64-row chunks of S are
+// staged in LDS, and each output sums its landmarks in order.
 // =====================================================================================================
 template <int D>
 __global__ __launch_bounds__(256) void k_mix(const float* __restrict__ X, const float* __restrict__ S,
                                              const float* __restrict__ rstd, float* __restrict__ P,
                                              float* __restrict__ Praw, int m) {
-  __shared__ float sX[16 * 65];
+  constexpr int RB = 256 / D;  // landmark rows per block: one output (row, channel) per thread
+  __shared__ float sX[RB * 65];
   __shared__ float sS[64 * D];
-  const int g = blockIdx.y, l0 = blockIdx.x * 16, tid = threadIdx.x;
-  constexpr int NC = (D * 16 + 255) / 256;  // outputs per thread
-  float acc[NC];
-#pragma unroll
-  for (int j = 0; j < NC; ++j) acc[j] = 0.f;
+  const int g = blockIdx.y, l0 = blockIdx.x * RB, tid = threadIdx.x;
+  const int rr = tid / D, c = tid % D;
+  float acc = 0.f;
   const float* xg = X + static_cast<size_t>(g) * m * m;
   const float* sg = S + static_cast<size_t>(g) * m * D;
   for (int k0 = 0; k0 < m; k0 += 64) {
     const int nk = min(64, m - k0);
     constexpr int NQ = (64 * D / 4 + 255) / 256;
+    constexpr int NXV = (RB * 64 + 255) / 256;
     float4 buf[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int e = 4 * (tid + 256 * q);
       buf[q] = (e < nk * D) ? load4(sg + static_cast<size_t>(k0) * D + e) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    float xv[4];
+    float xv[NXV];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NXV; ++q) {
       const int e = tid + 256 * q;
-      const int rr = e >> 6, kk = e & 63;
-      xv[q] = (l0 + rr < m && kk < nk) ? xg[static_cast<size_t>(l0 + rr) * m + k0 + kk] : 0.f;
+      const int xr = e >> 6, kk = e & 63;
+      xv[q] = (xr < RB && l0 + xr < m && kk < nk) ? xg[static_cast<size_t>(l0 + xr) * m + k0 + kk] : 0.f;
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NXV; ++q) {
       const int e = tid + 256 * q;
-      sX[(e >> 6) * 65 + (e & 63)] = xv[q];
+      if ((e >> 6) < RB) sX[(e >> 6) * 65 + (e & 63)] = xv[q];
     }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
@@ -389,29 +390,14 @@ __global__ __launch_bounds__(256) void k_mix(const float* __restrict__ X, const 
       if (e < 64 * D) store4(sS + e, buf[q]);
     }
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      const int o = tid + 256 * j;
-      if (o < 16 * D) {
-        const int rr = o / D, c = o % D;
-        float a = acc[j];
-        for (int kk = 0; kk < nk; ++kk) a += sX[rr * 65 + kk] * sS[kk * D + c];
-        acc[j] = a;
-      }
-    }
+#pragma unroll 8
+    for (int kk = 0; kk < nk; ++kk) acc += sX[rr * 65 + kk] * sS[kk * D + c];
   }
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    const int o = tid + 256 * j;
-    if (o < 16 * D) {
-      const int rr = o / D, c = o % D;
-      const int l = l0 + rr;
-      if (l < m) {
-        const float sc = rstd ? rstd[static_cast<size_t>(g) * m + l] : 1.f;
-        P[(static_cast<size_t>(g) * m + l) * D + c] = acc[j] * sc;
-        if (Praw) Praw[(static_cast<size_t>(g) * m + l) * D + c] = acc[j];
-      }
-    }
+  const int l = l0 + rr;
+  if (l < m) {
+    const float sc = rstd ? rstd[static_cast<size_t>(g) * m + l] : 1.f;
+    P[(static_cast<size_t>(g) * m + l) * D + c] = acc * sc;
+    if (Praw) Praw[(static_cast<size_t>(g) * m + l) * D + c] = acc;
   }
 }
 
@@ -941,7 +927,7 @@ hipError_t launch_ckv(const Shape& s, const float* CK, const void* V, float* par
 hipError_t launch_mix(const Shape& s, const float* X, const float* S, const float* rstd, float* P, float* Praw,
                       hipStream_t st) {
   // P = rstd * (X S) (rstd == nullptr means 1); Praw, when given, receives the unscaled X S.
-  const dim3 grid(cdiv(s.m, 16), s.G);
+  const dim3 grid(cdiv(s.m, 256 / s.d), s.G);  // 256 / d landmark rows per block (k_mix)
   switch (s.d) {
     case 16: hipLaunchKernelGGL(k_mix<16>, grid, dim3(256), 0, st, X, S, rstd, P, Praw, s.m); break;
     case 32: hipLaunchKernelGGL(k_mix<32>, grid, dim3(256), 0, st, X, S, rstd, P, Praw, s.m); break;
