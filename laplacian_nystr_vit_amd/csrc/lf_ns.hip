@@ -721,16 +721,18 @@ hipError_t launch_ns_side(const Shape& s, const float* We, float* X, float* xs, 
 // with U_k = 2I - T_k formed while staging, and the last step is the exact one, X_K = X_{K-1} (2I - W X_{K-1}),
 // in two launches.
 // =====================================================================================================
-// alpha and X_0 = alpha W^T for m > 64, over (slice, 32-row chunk) blocks. Pass 1 writes per-chunk partial
+// alpha and X_0 = alpha W^T for m > 64, over (slice, kNsRows-row chunk) blocks. Pass 1 writes per-chunk partial
 // column sums and the largest row sum of the chunk; pass 2 combines them in a fixed order (deterministic) and
 // writes the chunk's rows of X_0. part: G * nchunk * m doubles, rmx: G * nchunk doubles.
+constexpr int kNsRows = 8;  // rows per chunk of the alpha sums and of X_0: m / 8 chunks spread a slice over blocks
+
 __global__ __launch_bounds__(256) void k_ns_sums(const float* __restrict__ We, double* __restrict__ part,
                                                  double* __restrict__ rmx, int m) {
   __shared__ double red[4];
   const int g = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
   const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
   const float* wg = We + static_cast<size_t>(g) * m * m;
-  const int r0 = ch * 32, r1 = min(m, r0 + 32);
+  const int r0 = ch * kNsRows, r1 = min(m, r0 + kNsRows);
   for (int j = tid; j < m; j += 256) {
     double cs = 0.0;
 #pragma unroll 8
@@ -759,9 +761,15 @@ __global__ __launch_bounds__(256) void k_ns_x0(const float* __restrict__ We, con
   const int g = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
   const int tid = threadIdx.x;
   double cmax = 0.0;
+  constexpr int kMaxCh = 256 / kNsRows;  // chunks of the largest m
   for (int j = tid; j < m; j += 256) {
+    double pv[kMaxCh];  // every chunk's partial in flight, then summed in chunk order
+#pragma unroll
+    for (int c = 0; c < kMaxCh; ++c) pv[c] = c < nch ? part[(static_cast<size_t>(g) * nch + c) * m + j] : 0.0;
     double cs = 0.0;
-    for (int c = 0; c < nch; ++c) cs += part[(static_cast<size_t>(g) * nch + c) * m + j];
+#pragma unroll
+    for (int c = 0; c < kMaxCh; ++c)
+      if (c < nch) cs += pv[c];
     cmax = fmax(cmax, cs);
   }
   red[tid] = cmax;
@@ -772,7 +780,9 @@ __global__ __launch_bounds__(256) void k_ns_x0(const float* __restrict__ We, con
   }
   if (tid == 0) {
     double rmax = 0.0;
-    for (int c = 0; c < nch; ++c) rmax = fmax(rmax, rmx[static_cast<size_t>(g) * nch + c]);
+#pragma unroll
+    for (int c = 0; c < kMaxCh; ++c)
+      if (c < nch) rmax = fmax(rmax, rmx[static_cast<size_t>(g) * nch + c]);
     s_alpha = static_cast<float>(1.0 / (red[0] * rmax));
     if (ch == 0 && alpha_out) alpha_out[g] = s_alpha;
   }
@@ -782,8 +792,8 @@ __global__ __launch_bounds__(256) void k_ns_x0(const float* __restrict__ We, con
   const float* wg = We + g * mm;
   float* x0 = X0 + g * mm;
   float* x0b = X0b ? X0b + g * strideX0b : nullptr;
-  const int r0 = ch * 32, r1 = min(m, r0 + 32);
-  // X_0[i][j] = alpha W[j][i]: thread j reads the 32 consecutive entries W[j][r0 .. r1) of its row and writes
+  const int r0 = ch * kNsRows, r1 = min(m, r0 + kNsRows);
+  // X_0[i][j] = alpha W[j][i]: thread j reads the consecutive entries W[j][r0 .. r1) of its row and writes
   // column j of rows r0 .. r1 (each store instruction covers 256 consecutive floats of one row).
   for (int j = tid; j < m; j += 256) {
 #pragma unroll 8
@@ -946,7 +956,7 @@ hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float
   // X_0 lands where the last exact step reads X_{K-1} from when K == 1, else where step 0 reads it.
   int xc = (K % 2 == 0) ? 0 : 1;  // parity such that X_K ends in Xb[0] = X (K steps, one flip per step)
   {
-    const int nch = (m + 31) / 32;
+    const int nch = (m + kNsRows - 1) / kNsRows;
     // G nch m + G nch doubles fit in one T buffer (m > 64); Tb[0] starts the 256-byte aligned scratch and is not
     // written before T_0.
     double* part = reinterpret_cast<double*>(Tb[0]);
