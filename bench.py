@@ -168,33 +168,119 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(wl, inp, budget_s):
-    """The fp64 oracle as it stands, on one thread, over whole slices of the same workload until the budget."""
-    import numpy as np
+# ---------------------------------------------------------------------------------------------- CPU baseline
+_ORACLE_STATE = {}
+
+
+def _oracle_init(wl):
+    """Worker set-up: the workload's inputs, once per worker process, and BLAS limited to one thread."""
     from threadpoolctl import threadpool_limits
 
+    from laplacian_nystr_vit_amd import workloads as WL
+
+    _ORACLE_STATE["wl"] = wl
+    _ORACLE_STATE["inp"] = WL.make_inputs(wl, seed=0, with_dy=bool(wl.whiten))
+    _ORACLE_STATE["limits"] = threadpool_limits(limits=1)
+
+
+def _oracle_run(args):
+    """One worker's share of a timed run: whole (batch, head) slices from `first` on, until `budget_s` has passed
+    (at least one). Returns (slices, seconds)."""
     import oracle as O
 
+    first, budget_s = args
+    wl, inp = _ORACLE_STATE["wl"], _ORACLE_STATE["inp"]
     op = O.Params(B=wl.B, heads=wl.heads, H=wl.H, W=wl.W, d=wl.d, r=wl.r, lam=wl.lam, eps=wl.eps,
                   ns_iters=wl.ns_iters, whiten=wl.whiten, whiten_eps=wl.whiten_eps, kernel=wl.kernel)
-    train = bool(wl.whiten)
     slices = 0
     t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while True:
-            b, h = divmod(slices % wl.G, wl.heads)
-            args = (inp["Q"][b, h], inp["K"][b, h], inp["V"][b, h], inp["w64"][h * wl.d:(h + 1) * wl.d])
-            fwd = O.forward_slice(*args, op)
-            if train:
-                O.backward_slice(*args, inp["dY"][b, h], op, fwd)
-            slices += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-    dt = time.perf_counter() - t0
-    what = "forward + backward" if train else "forward"
-    return {"value": slices * wl.N / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what} of {slices} (batch, head) slices of {wl.name} ({wl.N} tokens each), fp64 numpy, "
-                      f"one thread, {dt:.1f} s"}
+    while True:
+        b, h = divmod((first + slices) % wl.G, wl.heads)
+        args = (inp["Q"][b, h], inp["K"][b, h], inp["V"][b, h], inp["w64"][h * wl.d:(h + 1) * wl.d])
+        fwd = O.forward_slice(*args, op)
+        if wl.whiten:
+            O.backward_slice(*args, inp["dY"][b, h], op, fwd)
+        slices += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    return slices, time.perf_counter() - t0
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_workers():
+    """Host cores the oracle may use: the process's CPU affinity, capped by the thread budget the environment sets
+    (OMP_NUM_THREADS) and at 16, the host share of one GPU."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+    except ValueError:
+        pass
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(wl, budget_s):
+    """The fp64 oracle as it stands, one single-threaded process per host core (spawned, so no child inherits GPU
+    state), over whole slices of the same workload. Three timed runs of budget_s / 3 each; the median is reported."""
+    import multiprocessing as mp
+
+    workers = oracle_workers()
+    ctx = mp.get_context("spawn")
+    runs = []
+    with ctx.Pool(workers, initializer=_oracle_init, initargs=(wl,)) as pool:
+        pool.map(_oracle_run, [(k, 0.0) for k in range(workers)])  # start-up and first-touch outside the timing
+        for _ in range(3):
+            res = pool.map(_oracle_run, [(k * 7, budget_s / 3) for k in range(workers)])
+            slices = sum(r[0] for r in res)
+            secs = max(r[1] for r in res)
+            runs.append((slices * wl.N / secs, slices, secs))
+    runs.sort()
+    value, slices, secs = runs[1]
+    what = "forward + backward" if wl.whiten else "forward"
+    return {"value": value, "unit": "tokens/s", "cores": workers, "kind": "oracle", "cpu_model": cpu_model(),
+            "runs_tokens_per_s": [r[0] for r in runs],
+            "sample": f"{what} of whole (batch, head) slices of {wl.name} ({wl.N} tokens each), fp64 numpy, "
+                      f"{workers} single-threaded processes; median of 3 runs of {budget_s / 3:.1f} s "
+                      f"(median run: {slices} slices in {secs:.2f} s)"}
+
+
+def observed_sclk_mhz(run_for_s, work):
+    """Highest shader clock rocm-smi reports while `work` runs for about run_for_s seconds (None if unavailable)."""
+    import re
+    import subprocess
+    import threading
+
+    samples = []
+    done = threading.Event()
+
+    def poll():
+        while not done.is_set():
+            try:
+                out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10).stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            for line in out.splitlines():
+                if "sclk" in line.lower():
+                    m = re.search(r"\((\d+)\s*Mhz\)", line, flags=re.I)
+                    if m:
+                        samples.append(int(m.group(1)))
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < run_for_s:
+        work()
+    done.set()
+    th.join(timeout=15)
+    return max(samples) if samples else None
 
 
 def distance_stage(wl, lf):
@@ -341,12 +427,15 @@ def main():
             t["dlam"] = torch.empty(1, device="cuda")
         return t
 
+    # the training op lends the library a second stream for the backward's independent parts
+    aux = lf.AuxStream() if train else None
+
     def run_step(t):
         if train:
             # the full training op: dQ, dK, dV and the DWC weight and lambda gradients
             lf.lf_attn_fwd(p, t["Q"], t["K"], t["V"], t["w"], t["Y"], t["saved"], t["ws"], stream)
             lf.lf_attn_bwd_ex(p, t["Q"], t["K"], t["V"], t["w"], t["saved"], t["dY"], t["dQ"], t["dK"], t["dV"],
-                              t["dw"], t["dlam"], 0, t["ws"], stream)
+                              t["dw"], t["dlam"], 0, t["ws"], stream, aux=aux)
         else:
             lf.lf_attn_fwd(p, t["Q"], t["K"], t["V"], t["w"], t["Y"], None, t["ws"], stream)
 
@@ -365,6 +454,21 @@ def main():
     elapsed = timed([hot], args.steps, args.warmup)
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = wl.tokens * args.steps / elapsed
+
+    # The same steps with a HIP event recorded on the stream between consecutive steps: the distribution of the
+    # device time per step (its median is robust to a stray slow step, which the wall-clock mean is not).
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        run_step(hot)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    step_events = {"median_ms": per[len(per) // 2], "p10_ms": per[len(per) // 10],
+                   "p90_ms": per[min(len(per) - 1, (9 * len(per)) // 10)], "steps": len(per),
+                   "median_tokens_per_s": wl.tokens / (per[len(per) // 2] * 1e-3)}
+    sclk = observed_sclk_mhz(1.5, lambda: run_step(hot))
+    torch.cuda.synchronize()
 
     cold = None
     if not args.no_cold:
@@ -434,6 +538,21 @@ def main():
     time_stage("ckv_reduce", lambda: lf.lf_ckv_reduce(p, CK, V, S, ws, stream))
     time_stage("landmark_mix", lambda: lf.lf_landmark_mix(p, X, S, None, P, stream))
     time_stage("out_gemm_dwc", lambda: lf.lf_out_gemm_dwc(p, CQ, P, None, V, w, Y, stream))
+    # The forward's solver launch as lf_attn_fwd makes it (m <= 64: Newton-Schulz with S = C_K^T V beside it),
+    # through the stage entry points: the solver's own share is ns_pinv above.
+    # MFMA stages against the fp32 MFMA peak, algorithmic flops per call: Newton-Schulz 4 K m^3 per slice (two
+    # m x m products per step), C_K^T V and the output product 2 N m d, the landmark mix 2 m^2 d. The solver's
+    # fraction is chip-wide; it holds one CU per slice, so per_cu_frac scales it by the CUs it occupies.
+    flops = {"ns_pinv": 4.0 * G * wl.ns_iters * m ** 3, "ckv_reduce": 2.0 * G * N * m * d,
+             "landmark_mix": 2.0 * G * m * m * d, "out_gemm_dwc": 2.0 * G * N * m * d}
+    mfma = {}
+    for name, fl in flops.items():
+        us = stages[name]
+        ach = fl / (us * 1e-6) / 1e12
+        mfma[name] = {"flops": fl, "us": us, "achieved_tflops": round(ach, 3),
+                      "frac": round(ach / MFMA_F32_PEAK_TFLOPS, 5)}
+    if m <= 64:
+        mfma["ns_pinv"]["per_cu_frac"] = round(mfma["ns_pinv"]["frac"] * 256 / min(256, G), 5)
 
     rec = {
         "metric": METRIC_TRAIN if train else (METRIC_GAUSS if gauss else METRIC),
@@ -452,12 +571,15 @@ def main():
                    "heads": wl.heads, "H": wl.H, "W": wl.W, "d": wl.d, "r": wl.r, "m": wl.m, "lambda": wl.lam,
                    "eps": wl.eps, "ns_iters": wl.ns_iters, "kernel": wl.kernel, "tokens_per_step": wl.tokens},
         "roofline": roof,
+        "mfma_stages": mfma,
         "stages_us": stages,
+        "step_events": step_events,
+        "sclk_mhz": sclk,
     }
     if cold is not None:
         rec["cold"] = cold
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
 

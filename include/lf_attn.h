@@ -19,12 +19,10 @@
  *            [g][l][i] is C[i][l] of the formulas); W_eps and X [G][m][m]; S and P [G][m][d]; mu and rstd [G][m].
  *            The DWC weight is float32 [heads*d][3][3].
  *  Pointers: every pointer is a device pointer owned by the caller, 16-byte aligned. The library never allocates
- *            or frees memory and never synchronises. Work is enqueued on `stream` (a hipStream_t; NULL means the
- *            null stream) and the call returns as soon as it is enqueued. The backward calls also use one
- *            non-blocking stream of the library's own per device (default priority), created with two events on
- *            their first call on that device and kept until the process ends: parts of their work fork to it
- *            after events recorded on `stream`, and `stream` waits on events recorded after each part, so
- *            everything the call does is complete when work enqueued on `stream` after it starts.
+ *            or frees memory, never synchronises and holds no state between calls: no stream, event or buffer of
+ *            its own. Work is enqueued on `stream` (a hipStream_t; NULL means the null stream) and the call returns
+ *            as soon as it is enqueued. Only lf_attn_bwd_ex can spread its work over a second stream, and only one
+ *            the caller lends it (lf_aux_stream).
  *  Errors:   every entry point returns LF_OK (0) or a negative code. Parameters, pointers and workspace sizes are
  *            checked on the host before anything is launched; on an error nothing is launched. LF_EHIP reports a
  *            failed launch (hipGetLastError). Nothing throws across this ABI. Calls are reentrant; calls that
@@ -45,6 +43,7 @@ extern "C" {
 #endif
 
 typedef struct ihipStream_t* lf_stream_t; /* same type as hipStream_t */
+typedef struct ihipEvent_t* lf_event_t;   /* same type as hipEvent_t */
 
 enum lf_status {
   LF_OK = 0,
@@ -105,10 +104,22 @@ int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const voi
 /* Backward pass of <dY, Y> with respect to Q, K and V ([abs]: forward and backward; [note] motivation "core idea"
  * for the kernel gradient, with the sign read as d/dx exp(-||x-y||_1/lambda) = -(1/lambda) sign(x-y) k).
  * saved: the buffer filled by lf_attn_fwd with the same params and inputs. ws: at least bwd_ws_bytes.
- * dQ, dK, dV are overwritten. Supports m <= 64, d <= 64 and the Laplacian kernel (LF_EUNSUPPORTED otherwise). */
+ * dQ, dK, dV are overwritten. Every launch goes to `stream`. Supports m <= 64, d <= 64 and the Laplacian kernel
+ * (LF_EUNSUPPORTED otherwise). */
 int lf_attn_bwd(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
                 const void* saved, const void* dY, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
                 lf_stream_t stream);
+
+/* A second stream lent by the caller to lf_attn_bwd_ex, with two events of the caller's (create them with
+ * hipEventDisableTiming). Parts of the call's work that do not depend on each other run on `stream` after an
+ * event recorded on the call's stream (`fork`); the call's stream then waits on `join`, recorded after those parts,
+ * so everything the call does is complete when work enqueued on the call's stream after it starts. The stream must
+ * be another stream than the call's, on the same device (LF_EINVAL otherwise). The library keeps none of these
+ * handles after the call returns; calls that lend the same lf_aux_stream must be ordered by the caller. */
+typedef struct lf_aux_stream {
+  lf_stream_t stream;
+  lf_event_t fork, join;
+} lf_aux_stream;
 
 /* The training op's full set of gradients: everything lf_attn_bwd writes, plus, each optional (NULL skips it):
  *   d_dwc_w: [heads*d][3][3] float32, the gradient of <dY, Y> with respect to the DWC weights, summed over the
@@ -118,11 +129,13 @@ int lf_attn_bwd(const lf_attn_params* p, const void* Q, const void* K, const voi
  * flags: LF_BWD_EXACT_ALPHA takes the gradient through the Newton-Schulz start alpha = 1/(||W_eps||_1 ||W_eps||_inf)
  *        ([note] Design 3 for X_0 = alpha W_eps^T), differentiated at the first largest column and row sum;
  *        without it alpha is held constant as in lf_attn_bwd. Other bits: LF_EINVAL.
+ * aux:   NULL runs everything on `stream` (as lf_attn_bwd does), or a lent second stream (lf_aux_stream): the
+ *        reverse Newton-Schulz chain and the lambda gradient then overlap the row gradients.
  * Same saved buffer, workspace (bwd_ws_bytes), alignment and errors as lf_attn_bwd; d_dwc_w is 16-byte aligned. */
 #define LF_BWD_EXACT_ALPHA 1
 int lf_attn_bwd_ex(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
                    const void* saved, const void* dY, void* dQ, void* dK, void* dV, float* d_dwc_w, float* d_lambda,
-                   int flags, void* ws, size_t ws_bytes, lf_stream_t stream);
+                   int flags, void* ws, size_t ws_bytes, lf_stream_t stream, const lf_aux_stream* aux);
 
 /* Static description of a status code. */
 const char* lf_strerror(int code);

@@ -10,30 +10,6 @@
 #include "lf_internal.h"
 #include "lf_bwd_internal.h"
 
-namespace lf {
-
-namespace {
-constexpr int kMaxDevices = 64;
-SideStream g_side[kMaxDevices];
-std::mutex g_side_init;
-}  // namespace
-
-SideStream* side_stream() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& ss = g_side[dev];
-  std::lock_guard<std::mutex> lk(g_side_init);
-  if (!ss.tried) {
-    ss.tried = true;
-    ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
-  }
-  return ss.ok ? &ss : nullptr;
-}
-
-}  // namespace lf
-
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -186,18 +162,27 @@ int lf_attn_saved_layout(const lf_attn_params* p, lf_saved_layout* out) {
   return LF_OK;
 }
 
-int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w, void* Y,
-                void* saved, void* ws, size_t ws_bytes, lf_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of the forward's arguments other than the workspace.
+int validate_fwd(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
+                 const void* Y, const void* saved) {
   const int rc = validate(p);
   if (rc != LF_OK) return rc;
-  if (!Q || !K || !V || !Y || !ws) return LF_EINVAL;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(Y) || !aligned16(ws)) return LF_EINVAL;
+  if (!Q || !K || !V || !Y) return LF_EINVAL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(Y)) return LF_EINVAL;
   if ((dwc_w && !aligned16(dwc_w)) || (saved && !aligned16(saved))) return LF_EINVAL;
   if (Y == Q || Y == K || Y == V) return LF_EINVAL;
+  return LF_OK;
+}
+
+// The forward launch sequence on a validated call; ws holds at least fwd_ws(s).total bytes.
+int fwd_launch(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w, void* Y,
+               void* saved, void* ws, hipStream_t st) {
   const lf::Shape s = make_shape(p);
   const FwdWs w = fwd_ws(s);
-  if (ws_bytes < w.total) return LF_EWORKSPACE;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool wh = p->whiten == 1;
 
   float *L, *CQ, *CK, *We, *xs, *mu, *rstd, *S, *Praw, *alpha;
@@ -258,17 +243,44 @@ int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const voi
   return LF_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w, void* Y,
+                void* saved, void* ws, size_t ws_bytes, lf_stream_t stream) {
+  const int rc = validate_fwd(p, Q, K, V, dwc_w, Y, saved);
+  if (rc != LF_OK) return rc;
+  if (!ws || !aligned16(ws)) return LF_EINVAL;
+  if (ws_bytes < fwd_ws(make_shape(p)).total) return LF_EWORKSPACE;
+  return fwd_launch(p, Q, K, V, dwc_w, Y, saved, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
 int lf_attn_bwd(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
                 const void* saved, const void* dY, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
                 lf_stream_t stream) {
-  return lf_attn_bwd_ex(p, Q, K, V, dwc_w, saved, dY, dQ, dK, dV, nullptr, nullptr, 0, ws, ws_bytes, stream);
+  return lf_attn_bwd_ex(p, Q, K, V, dwc_w, saved, dY, dQ, dK, dV, nullptr, nullptr, 0, ws, ws_bytes, stream,
+                        nullptr);
 }
 
 int lf_attn_bwd_ex(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
                    const void* saved, const void* dY, void* dQ, void* dK, void* dV, float* d_dwc_w, float* d_lambda,
-                   int flags, void* ws, size_t ws_bytes, lf_stream_t stream) {
+                   int flags, void* ws, size_t ws_bytes, lf_stream_t stream, const lf_aux_stream* aux) {
   if (flags & ~LF_BWD_EXACT_ALPHA) return LF_EINVAL;
   if (d_dwc_w && !aligned16(d_dwc_w)) return LF_EINVAL;
+  lf::AuxStream side{};
+  if (aux) {
+    if (!aux->stream || !aux->fork || !aux->join || aux->fork == aux->join) return LF_EINVAL;
+    side.s = reinterpret_cast<hipStream_t>(aux->stream);
+    side.fork = reinterpret_cast<hipEvent_t>(aux->fork);
+    side.join = reinterpret_cast<hipEvent_t>(aux->join);
+    if (side.s == reinterpret_cast<hipStream_t>(stream)) return LF_EINVAL;
+    // Both streams must belong to one device (the events are recorded on both).
+    hipDevice_t da = 0, dc = 0;
+    if (hipStreamGetDevice(side.s, &da) != hipSuccess ||
+        hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &dc) != hipSuccess || da != dc)
+      return LF_EINVAL;
+  }
   const int rc = validate(p);
   if (rc != LF_OK) return rc;
   const lf::Shape s = make_shape(p);
@@ -297,7 +309,7 @@ int lf_attn_bwd_ex(const lf_attn_params* p, const void* Q, const void* K, const 
   ex.d_lambda = d_lambda;
   ex.exact_alpha = (flags & LF_BWD_EXACT_ALPHA) != 0;
   return hip_status(lf::launch_backward(s, p->whiten == 1, Q, K, V, dwc_w, sp, dY, dQ, dK, dV, ws,
-                                        reinterpret_cast<hipStream_t>(stream), ex));
+                                        reinterpret_cast<hipStream_t>(stream), ex, aux ? &side : nullptr));
 }
 
 // ---- stage entry points ----

@@ -1091,13 +1091,14 @@ size_t bwd_ws_bytes(const Shape& s) {
 
 // The reverse Newton-Schulz group (k_bwd_ns_*, then k_bwd_wpart) depends only on dX and produces dW_eps and dL's
 // landmark-kernel term; the row gradients, the dV adjoint, the dL partials and the DWC weight gradient depend
-// only on dS and the whitening statistics. The group runs on one block per slice for most of its time, so it goes
-// to the side stream and overlaps those kernels. After the join the lambda gradient, which needs only Gq, Gk and
-// dW_eps, forks to the side stream once more, next to the dL finalisation and the token rows.
+// only on dS and the whitening statistics. The group runs on one block per slice for most of its time, so when the
+// caller lends a second stream (side) it goes there and overlaps those kernels. After the join the lambda gradient,
+// which needs only Gq, Gk and dW_eps, forks to that stream once more, next to the dL finalisation and the token
+// rows. Without it every launch stays on st in the same order.
 template <typename T, int D>
 static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void* Kv, const void* Vv, const float* w,
                         const SavedPtrs& sp, const void* dYv, void* dQv, void* dKv, void* dVv, void* ws,
-                        hipStream_t st, const BwdExtras& ex) {
+                        hipStream_t st, const BwdExtras& ex, const AuxStream* side) {
   const BwdWs p = plan(s);
   char* b = static_cast<char*>(ws);
   float* T1 = reinterpret_cast<float*>(b + p.T1);
@@ -1124,11 +1125,8 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bwd_small1<D>, dim3(s.G, s.m < 32 ? s.m : 32), dim3(256), 0, st, T1, sp.S, sp.P, sp.xs, sp.mu,
                      sp.rstd, dX, dS, stats, s.m, s.ns_iters, s.N, wh);
-  SideStream* side = side_stream();
-  std::unique_lock<std::mutex> lk;
   hipStream_t ns_st = st;
   if (side) {
-    lk = std::unique_lock<std::mutex>(side->mu);
     if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
     ns_st = side->s;
@@ -1197,19 +1195,19 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
 template <typename T>
 static hipError_t bwd_d(const Shape& s, bool whiten, const void* Q, const void* K, const void* V, const float* w,
                         const SavedPtrs& sp, const void* dY, void* dQ, void* dK, void* dV, void* ws, hipStream_t st,
-                        const BwdExtras& ex) {
+                        const BwdExtras& ex, const AuxStream* aux) {
   switch (s.d) {
-    case 16: return bwd_t<T, 16>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex);
-    case 32: return bwd_t<T, 32>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex);
-    default: return bwd_t<T, 64>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex);
+    case 16: return bwd_t<T, 16>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex, aux);
+    case 32: return bwd_t<T, 32>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex, aux);
+    default: return bwd_t<T, 64>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex, aux);
   }
 }
 
 hipError_t launch_backward(const Shape& s, bool whiten, const void* Q, const void* K, const void* V, const float* w,
                            const SavedPtrs& sp, const void* dY, void* dQ, void* dK, void* dV, void* ws,
-                           hipStream_t st, const BwdExtras& ex) {
-  if (s.dtype == 1) return bwd_d<bf16_t>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex);
-  return bwd_d<float>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex);
+                           hipStream_t st, const BwdExtras& ex, const AuxStream* aux) {
+  if (s.dtype == 1) return bwd_d<bf16_t>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex, aux);
+  return bwd_d<float>(s, whiten, Q, K, V, w, sp, dY, dQ, dK, dV, ws, st, ex, aux);
 }
 
 }  // namespace lf

@@ -23,8 +23,9 @@ struct BwdExtras {
   bool exact_alpha = false;   // gradient through alpha instead of holding it constant
 };
 
+// aux: NULL keeps every launch on st; otherwise the independent parts run on aux->s (see lf_bwd.hip).
 hipError_t launch_backward(const Shape& s, bool whiten, const void* Q, const void* K, const void* V, const float* w,
                            const SavedPtrs& sp, const void* dY, void* dQ, void* dK, void* dV, void* ws,
-                           hipStream_t st, const BwdExtras& ex = BwdExtras());
+                           hipStream_t st, const BwdExtras& ex, const AuxStream* aux);
 
 }  // namespace lf

@@ -6,8 +6,6 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <mutex>
-
 namespace lf {
 
 struct Shape {
@@ -60,22 +58,15 @@ bool ns_side_supported(const Shape& s);
 hipError_t launch_ns_side(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
                           const void* V, float* S, hipStream_t st);
 
+// A second stream the caller owns, with two events of its own, for backward work that does not depend on the
+// rest: the caller's stream forks to it through `fork` and waits on `join`. Null members are never passed here.
+struct AuxStream {
+  hipStream_t s;
+  hipEvent_t fork, join;
+};
+
 // Conjugate gradients for W_eps X = I, one column per CG solve (cg_supported: 1 <= m <= 64). resid: NULL or
 // [G][iters] receiving ||W_eps X_k - I||_F after every step. iters <= kCgItersMax.
-// A second stream of the library's own for the launches whose only input is the landmark kernel matrix (the
-// Newton-Schulz solver forward and backward, which hold one CU per slice for a chain of dependent steps): the
-// caller's stream forks to it with `fork` and waits on `join` before the first launch that reads its output.
-// One per device, created on first use (non-blocking, default priority); `mu` is held from the fork to the join
-// so that concurrent calls on one device keep their events paired. nullptr when it cannot be created (the
-// launches then stay on the caller's stream).
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool ok = false, tried = false;
-  std::mutex mu;
-};
-SideStream* side_stream();
-
 constexpr int kCgItersMax = 256;
 bool cg_supported(const Shape& s);
 hipError_t launch_cg(const Shape& s, const float* We, float* X, float* resid, int iters, hipStream_t st);

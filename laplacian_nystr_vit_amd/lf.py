@@ -58,6 +58,27 @@ class LfSavedLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("L", "CQ", "CK", "We", "xs", "mu", "rstd", "S", "P", "alpha", "total")]
 
 
+class LfAuxStream(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("fork", ctypes.c_void_p), ("join", ctypes.c_void_p)]
+
+
+class AuxStream:
+    """A second stream and two events the caller lends to lf_attn_bwd_ex (the library keeps no stream or event of
+    its own). Owned by this object; torch creates them (default priority, events without timing)."""
+
+    def __init__(self, device=None):
+        self.stream = torch.cuda.Stream(device=device)
+        self.fork = torch.cuda.Event(enable_timing=False)
+        self.join = torch.cuda.Event(enable_timing=False)
+        # torch creates an event's HIP handle on its first record
+        self.fork.record(self.stream)
+        self.join.record(self.stream)
+        self.stream.synchronize()
+
+    def as_c(self) -> LfAuxStream:
+        return LfAuxStream(self.stream.cuda_stream, self.fork.cuda_event, self.join.cuda_event)
+
+
 class LfError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
@@ -85,7 +106,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lf_attn_fwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "lf_attn_bwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "lf_attn_bwd_ex": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int,
-                                          _vp, _sz, _vp]),
+                                          _vp, _sz, _vp, ctypes.POINTER(LfAuxStream)]),
         "lf_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "lf_landmark_pool": (ctypes.c_int, [_P, _vp, _vp, _vp]),
         "lf_laplace_l1_exp": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -193,17 +214,20 @@ def lf_attn_bwd(p, Q, K, V, dwc_w, saved, dY, dQ, dK, dV, ws, stream=None) -> No
         _stream(stream)), "lf_attn_bwd")
 
 
-def lf_attn_bwd_ex(p, Q, K, V, dwc_w, saved, dY, dQ, dK, dV, d_dwc_w, d_lambda, flags, ws, stream=None) -> None:
+def lf_attn_bwd_ex(p, Q, K, V, dwc_w, saved, dY, dQ, dK, dV, d_dwc_w, d_lambda, flags, ws, stream=None,
+                   aux: Optional[AuxStream] = None) -> None:
+    """aux: None (every launch on `stream`) or an AuxStream lent for the independent parts of the work."""
     dt, n = io_dtype(p), p.G * p.N * p.d
     _, saved_b, _ = lf_attn_query(p)
     if _nbytes(saved) < saved_b:
         raise ValueError(f"saved needs {saved_b} bytes")
+    ca = ctypes.byref(aux.as_c()) if aux is not None else None
     _check(load_library().lf_attn_bwd_ex(
         ctypes.byref(p), _ptr(Q, "Q", dt, n), _ptr(K, "K", dt, n), _ptr(V, "V", dt, n),
         _ptr(dwc_w, "dwc_w", torch.float32, p.heads * p.d * 9), _ptr(saved, "saved"), _ptr(dY, "dY", dt, n),
         _ptr(dQ, "dQ", dt, n), _ptr(dK, "dK", dt, n), _ptr(dV, "dV", dt, n),
         _ptr(d_dwc_w, "d_dwc_w", torch.float32, p.heads * p.d * 9), _ptr(d_lambda, "d_lambda", torch.float32, 1),
-        int(flags), _ptr(ws, "ws"), _nbytes(ws), _stream(stream)), "lf_attn_bwd_ex")
+        int(flags), _ptr(ws, "ws"), _nbytes(ws), _stream(stream), ca), "lf_attn_bwd_ex")
 
 
 def lf_landmark_pool(p, Q, L, stream=None) -> None:

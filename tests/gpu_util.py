@@ -15,6 +15,9 @@ from laplacian_nystr_vit_amd import workloads as WL
 # Bars from the contract: relative Frobenius error of the GPU result against the fp64 oracle.
 TOL_F32 = 1e-4
 TOL_BF16 = 2e-2
+# Intermediates computed in float32 (L, the kernel matrices, X_K, S, P) are gated at the float32 bar whatever the
+# input dtype: a bf16 input only changes the numbers they start from, which the oracle receives too.
+TOL_STAGE = TOL_F32
 
 
 def tol(wl) -> float:

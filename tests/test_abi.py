@@ -130,11 +130,28 @@ def test_bwd_ex_validates_flags_and_alignment_on_host(lib):
     misaligned = ctypes.c_void_p(0x100004)
     # unknown flag bits, then a misaligned d_dwc_w: both rejected before anything is launched
     assert lib.lf_attn_bwd_ex(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, fake, None, None, 2,
-                              fake, bwd, None) == lf.LF_EINVAL
+                              fake, bwd, None, None) == lf.LF_EINVAL
     assert lib.lf_attn_bwd_ex(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, fake, misaligned,
-                              None, 0, fake, bwd, None) == lf.LF_EINVAL
+                              None, 0, fake, bwd, None, None) == lf.LF_EINVAL
     assert lib.lf_attn_bwd_ex(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, fake, None, None,
-                              lf.LF_BWD_EXACT_ALPHA, fake, bwd - 1, None) == lf.LF_EWORKSPACE
+                              lf.LF_BWD_EXACT_ALPHA, fake, bwd - 1, None, None) == lf.LF_EWORKSPACE
+
+
+def test_bwd_ex_validates_the_lent_stream_on_host(lib):
+    """A lent second stream with a missing handle, one event for both roles, or the call's own stream is rejected
+    before anything is launched."""
+    p = _p(WL.TRAIN_S1)
+    _, _, bwd = lf.lf_attn_query(p)
+    fake = ctypes.c_void_p(0x100000)
+    st, ev1, ev2 = 0x200000, 0x300000, 0x400000
+    bad = [lf.LfAuxStream(None, ev1, ev2), lf.LfAuxStream(st, None, ev2), lf.LfAuxStream(st, ev1, None),
+           lf.LfAuxStream(st, ev1, ev1)]
+    for aux in bad:
+        assert lib.lf_attn_bwd_ex(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, fake, None, None,
+                                  0, fake, bwd, None, ctypes.byref(aux)) == lf.LF_EINVAL
+    same = lf.LfAuxStream(st, ev1, ev2)
+    assert lib.lf_attn_bwd_ex(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, fake, None, None, 0,
+                              fake, bwd, ctypes.c_void_p(st), ctypes.byref(same)) == lf.LF_EINVAL
 
 
 def test_cg_validates_on_host(lib):
@@ -161,7 +178,7 @@ def test_gaussian_variant_is_forward_only_on_host(lib):
     assert lib.lf_attn_bwd(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, fake, fake, bwd,
                            None) == lf.LF_EUNSUPPORTED
     assert lib.lf_attn_bwd_ex(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, fake, None, None, 0,
-                              fake, bwd, None) == lf.LF_EUNSUPPORTED
+                              fake, bwd, None, None) == lf.LF_EUNSUPPORTED
     assert lib.lf_out_gemm_dwc_fused(ctypes.byref(p), fake, fake, fake, fake, None, fake, None) == lf.LF_EUNSUPPORTED
     # the stage call validates its pointers before launching
     misaligned = ctypes.c_void_p(0x100004)
@@ -169,3 +186,4 @@ def test_gaussian_variant_is_forward_only_on_host(lib):
     assert lib.lf_gauss_l2_exp(ctypes.byref(p), fake, None, fake, fake, fake, fake, None) == lf.LF_EINVAL
     with pytest.raises(ValueError):
         lf.make_params(1, 1, 8, 8, 16, 2, kernel="cosine")
+

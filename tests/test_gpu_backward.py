@@ -1,6 +1,10 @@
 """GPU parity of the backward pass (lf_attn_bwd) against the fp64 oracle's gradients, which are themselves pinned to
 finite differences of the whole block (tests/test_oracle_pins.py). Bar: relative Frobenius error <= 1e-4 (float32)
-and <= 2e-2 (bf16) for each of dQ, dK, dV."""
+and <= 2e-2 (bf16) for each of dQ, dK, dV.
+
+Every case runs with the DWC weights and without them. With them, dV is dominated by the adjoint stencil of dY
+(the attention part C_K dS is ~1e-2 of it at the training shape and ~1e-4 without whitening), so only the run
+without DWC gates the attention branch of dV."""
 
 import numpy as np
 import pytest
@@ -31,26 +35,28 @@ CASES = [
 ]
 
 
-def _gpu_backward(wl):
+def _gpu_backward(wl, dwc=True):
     p = params(wl)
     t = upload(wl)
+    w = t["w"] if dwc else None
     fwd_b, saved_b, bwd_b = lf.lf_attn_query(p)
     ws = torch.empty(max(fwd_b, bwd_b), dtype=torch.uint8, device="cuda")
     saved = torch.empty(saved_b, dtype=torch.uint8, device="cuda")
     Y = torch.empty_like(t["Q"])
-    lf.lf_attn_fwd(p, t["Q"], t["K"], t["V"], t["w"], Y, saved, ws)
+    lf.lf_attn_fwd(p, t["Q"], t["K"], t["V"], w, Y, saved, ws)
     dQ, dK, dV = torch.empty_like(t["Q"]), torch.empty_like(t["K"]), torch.empty_like(t["V"])
-    lf.lf_attn_bwd(p, t["Q"], t["K"], t["V"], t["w"], saved, t["dY"], dQ, dK, dV, ws)
+    lf.lf_attn_bwd(p, t["Q"], t["K"], t["V"], w, saved, t["dY"], dQ, dK, dV, ws)
     torch.cuda.synchronize()
     return host(dQ), host(dK), host(dV)
 
 
+@pytest.mark.parametrize("dwc", [True, False], ids=["dwc", "attn_only"])
 @pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
-def test_backward_matches_oracle(wl):
-    note(f"[gpu] backward {wl.name}")
+def test_backward_matches_oracle(wl, dwc):
+    note(f"[gpu] backward {wl.name} dwc={dwc}")
     inp = inputs(wl)
-    ref = O.backward(inp["Q"], inp["K"], inp["V"], inp["w64"], inp["dY"], oparams(wl))
-    dQ, dK, dV = _gpu_backward(wl)
+    ref = O.backward(inp["Q"], inp["K"], inp["V"], inp["w64"] if dwc else None, inp["dY"], oparams(wl))
+    dQ, dK, dV = _gpu_backward(wl, dwc)
     errs = {n: relF(a, ref[n]) for n, a in (("dQ", dQ), ("dK", dK), ("dV", dV))}
     note("    " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()))
     for n, e in errs.items():
@@ -58,7 +64,8 @@ def test_backward_matches_oracle(wl):
 
 
 def test_backward_on_fd_crop():
-    """The 4x4 crop (r=2, m=4, d=64, whitening on) on which the oracle's gradient is checked by finite differences."""
+    """The 4x4 crop (r=2, m=4, d=64, whitening on) on which the oracle's gradient is checked by finite differences,
+    with and without the DWC weights."""
     wl = WL.TRAIN_S1
     inp = inputs(wl)
     idx = np.array([y * wl.W + x for y in range(4) for x in range(4)])
@@ -71,14 +78,15 @@ def test_backward_on_fd_crop():
     fwd_b, saved_b, bwd_b = lf.lf_attn_query(p)
     ws = torch.empty(max(fwd_b, bwd_b), dtype=torch.uint8, device="cuda")
     saved = torch.empty(saved_b, dtype=torch.uint8, device="cuda")
-    Y = torch.empty_like(tt["Q"])
-    lf.lf_attn_fwd(p, tt["Q"], tt["K"], tt["V"], w, Y, saved, ws)
-    dQ, dK, dV = (torch.empty_like(tt["Q"]) for _ in range(3))
-    lf.lf_attn_bwd(p, tt["Q"], tt["K"], tt["V"], w, saved, tt["dY"], dQ, dK, dV, ws)
-    torch.cuda.synchronize()
-    ref = O.backward(arrs["Q"], arrs["K"], arrs["V"], inp["w64"], arrs["dY"], oparams(crop))
-    for n, a in (("dQ", dQ), ("dK", dK), ("dV", dV)):
-        assert relF(host(a), ref[n]) <= 1e-4, n
+    for ww, w64 in ((w, inp["w64"]), (None, None)):
+        Y = torch.empty_like(tt["Q"])
+        lf.lf_attn_fwd(p, tt["Q"], tt["K"], tt["V"], ww, Y, saved, ws)
+        dQ, dK, dV = (torch.empty_like(tt["Q"]) for _ in range(3))
+        lf.lf_attn_bwd(p, tt["Q"], tt["K"], tt["V"], ww, saved, tt["dY"], dQ, dK, dV, ws)
+        torch.cuda.synchronize()
+        ref = O.backward(arrs["Q"], arrs["K"], arrs["V"], w64, arrs["dY"], oparams(crop))
+        for n, a in (("dQ", dQ), ("dK", dK), ("dV", dV)):
+            assert relF(host(a), ref[n]) <= 1e-4, (n, ww is None)
 
 
 def test_backward_is_deterministic():
@@ -158,10 +166,10 @@ def test_exact_alpha_matches_oracle():
 
 
 def test_backward_on_a_user_stream_is_ordered_and_bitwise_stable():
-    """The backward forks part of its work to the library's own stream and joins it back onto the caller's stream.
-    On a user stream, two calls in a row, the second with other dY and a workspace filled with garbage, must give
-    the gradients of a call on the current stream bit for bit, and each output must be complete when the user
-    stream's next work (a copy) runs."""
+    """On a user stream, two calls in a row (the second with other dY and a workspace filled with garbage) give the
+    gradients of calls on the current stream bit for bit, and each output is complete when the user stream's next
+    work (a copy) runs: lf_attn_bwd on the one stream, and lf_attn_bwd_ex with a lent second stream (its fork and
+    join events are the caller's)."""
     note("[gpu] backward on a user stream")
     wl = WL.TRAIN_S1.replace(name="train_s1_B2", B=2)
     p = params(wl)
@@ -174,20 +182,67 @@ def test_backward_on_a_user_stream_is_ordered_and_bitwise_stable():
     dY2 = torch.flip(t["dY"], dims=[0]).contiguous()
     outs_ref = []
     for dy in (t["dY"], dY2):
-        dQ, dK, dV = torch.empty_like(t["Q"]), torch.empty_like(t["K"]), torch.empty_like(t["V"])
-        lf.lf_attn_bwd(p, t["Q"], t["K"], t["V"], t["w"], saved, dy, dQ, dK, dV, ws)
-        outs_ref.append((dQ, dK, dV))
+        g = [torch.empty_like(t["Q"]) for _ in range(3)] + [torch.empty(p.heads * p.d * 9, device="cuda"),
+                                                            torch.empty(1, device="cuda")]
+        lf.lf_attn_bwd_ex(p, t["Q"], t["K"], t["V"], t["w"], saved, dy, *g, 0, ws)
+        outs_ref.append(g)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
+    aux = lf.AuxStream()
     s.wait_stream(torch.cuda.current_stream())
-    copies = []
+    single, lent = [], []
     with torch.cuda.stream(s):
         ws.fill_(0xA5)
         for dy in (t["dY"], dY2):
             dQ, dK, dV = torch.empty_like(t["Q"]), torch.empty_like(t["K"]), torch.empty_like(t["V"])
             lf.lf_attn_bwd(p, t["Q"], t["K"], t["V"], t["w"], saved, dy, dQ, dK, dV, ws, stream=s)
-            copies.append(tuple(x.clone() for x in (dQ, dK, dV)))  # runs on s right after the call's work
+            single.append(tuple(x.clone() for x in (dQ, dK, dV)))  # runs on s right after the call's work
+        ws.fill_(0x5A)
+        for dy in (t["dY"], dY2):
+            g = [torch.empty_like(t["Q"]) for _ in range(3)] + [torch.empty(p.heads * p.d * 9, device="cuda"),
+                                                                torch.empty(1, device="cuda")]
+            lf.lf_attn_bwd_ex(p, t["Q"], t["K"], t["V"], t["w"], saved, dy, *g, 0, ws, stream=s, aux=aux)
+            lent.append(tuple(x.clone() for x in g))
     s.synchronize()
-    for got, ref in zip(copies, outs_ref):
+    for got, ref in zip(single, outs_ref):
+        for a, b in zip(got, ref[:3]):
+            assert torch.equal(a, b)
+    for got, ref in zip(lent, outs_ref):
         for a, b in zip(got, ref):
             assert torch.equal(a, b)
+
+
+def test_training_op_is_equivariant_under_slice_permutation():
+    """Reordering the batch entries and the heads (with each head's DWC filters) reorders dQ, dK and dV bit for bit
+    and the per-head DWC weight gradient with the heads; the batch sums (DWC weights, lambda) change only by the
+    order of their additions."""
+    wl = WL.TRAIN_S1.replace(name="train_B4_h2_14x14", B=4, heads=2, H=14, W=14, r=2)
+    note(f"[gpu] training op slice permutation {wl.name}")
+    rng = np.random.default_rng(4)
+    pb, ph = rng.permutation(wl.B), rng.permutation(wl.heads)
+    inp = inputs(wl)
+    d = wl.d
+    sets = [{k: inp[k + "_raw"] for k in ("Q", "K", "V", "dY")} | {"w": inp["w"]},
+            {k: np.ascontiguousarray(inp[k + "_raw"][pb][:, ph]) for k in ("Q", "K", "V", "dY")}
+            | {"w": np.ascontiguousarray(np.concatenate([inp["w"][h * d:(h + 1) * d] for h in ph]))}]
+    p = params(wl)
+    fwd_b, saved_b, bwd_b = lf.lf_attn_query(p)
+    ws = torch.empty(max(fwd_b, bwd_b), dtype=torch.uint8, device="cuda")
+    saved = torch.empty(saved_b, dtype=torch.uint8, device="cuda")
+    res = []
+    for s in sets:
+        t = {k: dev(v) for k, v in s.items()}
+        Y = torch.empty_like(t["Q"])
+        lf.lf_attn_fwd(p, t["Q"], t["K"], t["V"], t["w"], Y, saved, ws)
+        g = [torch.empty_like(t["Q"]) for _ in range(3)]
+        dw = torch.empty(wl.heads * d * 9, device="cuda")
+        dl = torch.empty(1, device="cuda")
+        lf.lf_attn_bwd_ex(p, t["Q"], t["K"], t["V"], t["w"], saved, t["dY"], *g, dw, dl, 0, ws)
+        torch.cuda.synchronize()
+        res.append(([x.cpu() for x in g], dw.cpu().view(wl.heads, d * 9), float(dl.cpu()[0])))
+    (g0, dw0, dl0), (g1, dw1, dl1) = res
+    ib, ih = torch.as_tensor(pb), torch.as_tensor(ph)
+    for a, b in zip(g1, g0):
+        assert torch.equal(a, b[ib][:, ih])
+    assert relF(dw1.numpy(), dw0[ih].numpy()) <= 1e-6
+    assert abs(dl1 - dl0) <= 1e-6 * abs(dl0)

@@ -10,8 +10,8 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import (dev, gpu_forward, host, inputs, note, oparams, oracle_forward, params, relF, tol,
-                      upload)
+from gpu_util import (TOL_STAGE, dev, gpu_forward, host, inputs, note, oparams, oracle_forward, params, relF,
+                      tol, upload)
 from laplacian_nystr_vit_amd import lf
 from laplacian_nystr_vit_amd import workloads as WL
 
@@ -37,6 +37,8 @@ EDGE = [
     WL.PVT_S1.replace(name="s1_B1_K64", B=1, ns_iters=64),
     # the m > 64 path (fp32 products, one launch per step) over four runs of coupled steps
     WL.TINY.replace(name="ragged_20x20_m100_K40", H=20, W=20, d=64, r=2, ns_iters=40, qk_dist="student_t"),
+    # d = 128 with m <= 64: the output kernel forms P = X S in its prologue with more than 64 KB of LDS
+    WL.TINY.replace(name="d128_14x14_m49_B2", B=2, H=14, W=14, d=128, r=2, qk_dist="student_t"),
 ]
 ALL = MAIN + EDGE
 
@@ -70,9 +72,11 @@ def test_forward_end_to_end(wl):
     assert relF(host(sv["CK"]).transpose(0, 2, 1), rs(ref["CK"])) <= 1e-5
     assert relF(host(sv["We"]), rs(ref["We"])) <= 1e-5
     Xk = host(sv["xs"])[:, wl.ns_iters]
-    assert relF(Xk, rs(ref["X"])) <= tol(wl)
-    assert relF(host(sv["S"]), rs(ref["S"])) <= tol(wl)
-    assert relF(host(sv["P"]), rs(ref["P"])) <= tol(wl)
+    e_x, e_s, e_p = (relF(Xk, rs(ref["X"])), relF(host(sv["S"]), rs(ref["S"])), relF(host(sv["P"]), rs(ref["P"])))
+    note(f"    relF X_K={e_x:.3e} S={e_s:.3e} P={e_p:.3e}")
+    assert e_x <= TOL_STAGE
+    assert e_s <= TOL_STAGE
+    assert e_p <= TOL_STAGE
     if wl.whiten:
         assert relF(host(sv["mu"]), rs(ref["mu"])) <= 1e-5
         assert relF(host(sv["rstd"]), rs(ref["rstd"])) <= 1e-5
@@ -138,7 +142,7 @@ def test_forward_newton_schulz_iterates(wl):
         assert np.array_equal(We[g], We[g].T)  # the distance kernel's W is bitwise symmetric
         _, xs_ref, _ = O.newton_schulz(We[g].astype(np.float64), K)
         for k in range(K + 1):
-            assert relF(xs[g, k], xs_ref[k]) <= tol(wl), (g, k)
+            assert relF(xs[g, k], xs_ref[k]) <= TOL_STAGE, (g, k)
         assert relF(xs[g, K], xs[g, K].T) <= 1e-5
 
 
@@ -162,7 +166,9 @@ def test_stage_newton_schulz(wl):
     for g in range(G):
         Xref, xs_ref, aref = O.newton_schulz(We64[g], K)
         assert abs(host(alpha)[g] - aref) <= 1e-6 * aref
-        assert relF(Xh[g], Xref) <= tol(wl)
+        e_x = relF(Xh[g], Xref)
+        note(f"    slice {g}: X_K relF {e_x:.3e}")
+        assert e_x <= TOL_STAGE
         assert relF(host(xs).reshape(G, K + 1, m, m)[g, 0], xs_ref[0]) <= 1e-6
         assert np.array_equal(host(xs).reshape(G, K + 1, m, m)[g, K], Xh[g])
         r_ref = np.linalg.norm(We64[g] @ Xref - np.eye(m))
@@ -292,3 +298,39 @@ def test_stage_whiten_stats_and_folded_output():
     A, muref, rsref = zip(*[O.whiten_columns(CQ[g], wl.whiten_eps) for g in range(G)])
     assert relF(host(mu).reshape(G, m), np.stack(muref)) <= 1e-6
     assert relF(host(rstd).reshape(G, m), np.stack(rsref)) <= 1e-6
+
+
+# --------------------------------------------------------------------------------------------------- invariants
+def _permuted(wl, pb, ph, seed=0):
+    """The workload's inputs with batch entries reordered by pb and heads by ph (each head's DWC filters with it)."""
+    inp = inputs(wl, seed)
+    out = {k: np.ascontiguousarray(inp[k + "_raw"][pb][:, ph]) for k in ("Q", "K", "V", "dY") if k + "_raw" in inp}
+    d = wl.d
+    out["w"] = np.ascontiguousarray(np.concatenate([inp["w"][h * d:(h + 1) * d] for h in ph]))
+    return out
+
+
+@pytest.mark.parametrize("wl", [WL.PVT_S3.replace(name="s3_B4_h3", B=4, heads=3),
+                                WL.PVT_S1.replace(name="s1_B4_bf16", B=4, dtype=WL.BF16),
+                                WL.TINY.replace(name="m100_B3_h2", B=3, heads=2, H=20, W=20, r=2,
+                                                qk_dist="student_t")],
+                         ids=lambda w: w.name)
+def test_forward_is_equivariant_under_slice_permutation(wl):
+    """The (batch, head) slices are independent: reordering the batch entries and the heads (with each head's DWC
+    filters) reorders the outputs bit for bit, whatever CU or XCD each slice lands on."""
+    note(f"[gpu] slice permutation {wl.name}")
+    rng = np.random.default_rng(3)
+    pb, ph = rng.permutation(wl.B), rng.permutation(wl.heads)
+    p = params(wl)
+    fwd_b, _, _ = lf.lf_attn_query(p)
+    ws = torch.empty(fwd_b, dtype=torch.uint8, device="cuda")
+    inp = inputs(wl)
+    outs = []
+    for src in ({k: inp[k + "_raw"] for k in ("Q", "K", "V")} | {"w": inp["w"]}, _permuted(wl, pb, ph)):
+        t = {k: dev(src[k]) for k in ("Q", "K", "V", "w")}
+        Y = torch.empty_like(t["Q"])
+        lf.lf_attn_fwd(p, t["Q"], t["K"], t["V"], t["w"], Y, None, ws)
+        torch.cuda.synchronize()
+        outs.append(Y.cpu())
+    Y0, Yp = outs
+    assert torch.equal(Yp, Y0[torch.as_tensor(pb)][:, torch.as_tensor(ph)])

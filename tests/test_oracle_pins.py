@@ -393,6 +393,7 @@ def test_backward_matches_finite_differences_on_crop(whiten):
     f = O.forward_slice(q, k, v, w, p)
     alpha = f["alpha"]
     g = O.backward_slice(q, k, v, w, dy, p, fwd=f)
+    g0 = O.backward_slice(q, k, v, None, dy, p, fwd=O.forward_slice(q, k, v, None, p))
     h = 1e-6
 
     def loss(qq, kk, vv, ww):
@@ -410,16 +411,26 @@ def test_backward_matches_finite_differences_on_crop(whiten):
                 slot = {"dQ": 0, "dK": 1, "dV": 2}[name]
                 args_p[slot] = arr + e
                 args_m[slot] = arr - e
-                # DWC(V) does not depend on Q or K and is ~1e4 times larger than the attention branch, so the
-                # Q/K differences are taken on the attention branch alone to keep FD roundoff below the bar.
-                ww = w if name == "dV" else None
-                fd[i, cc] = (loss(*args_p, ww) - loss(*args_m, ww)) / (2 * h)
+                # Every difference is taken on the attention branch alone. DWC(V) does not depend on Q or K, and
+                # its part of dV (the adjoint stencil of dY) is ~1e2-1e4 times the attention part C_K dS, so with
+                # DWC on, a dV check at 1e-6 would barely see C_K dS. The DWC part is pinned below.
+                fd[i, cc] = (loss(*args_p, None) - loss(*args_m, None)) / (2 * h)
         # skip coordinates within the FD step of a kink of |x - l| (none expected for continuous draws)
         if name != "dV":
             near = np.abs(arr[:, None, :] - L[None, :, :]).min(axis=1) < 1e-5
-            fd[near] = g[name][near]
-        err = np.linalg.norm(g[name] - fd) / np.linalg.norm(fd)
+            fd[near] = g0[name][near]
+        err = np.linalg.norm(g0[name] - fd) / np.linalg.norm(fd)
         assert err < 1e-6, (name, err)
+    # With DWC on, dQ and dK do not change and dV gains exactly the adjoint stencil of dy: the difference of the two
+    # gradients is the gradient of <dy, DWC(V)>, which is linear in V, so central differences give it exactly.
+    assert np.array_equal(g["dQ"], g0["dQ"]) and np.array_equal(g["dK"], g0["dK"])
+    fd_dwc = np.zeros_like(v)
+    for i in range(v.shape[0]):
+        for cc in range(v.shape[1]):
+            e = np.zeros_like(v)
+            e[i, cc] = 1.0
+            fd_dwc[i, cc] = 0.5 * float(np.sum(dy * (O.dwc(v + e, w, p.H, p.W) - O.dwc(v - e, w, p.H, p.W))))
+    assert np.linalg.norm((g["dV"] - g0["dV"]) - fd_dwc) <= 1e-12 * np.linalg.norm(fd_dwc)
 
 
 def test_alpha_dependence_vanishes_at_convergence():
@@ -479,6 +490,46 @@ def test_lambda_grad_matches_finite_differences(whiten):
 
     fd = (loss(p.lam + h) - loss(p.lam - h)) / (2 * h)
     assert abs(g["dlam"] - fd) <= 1e-6 * abs(fd), (g["dlam"], fd)
+
+
+def test_batched_backward_accumulates_per_head_and_over_slices():
+    """The batched backward() adds each (batch, head) slice's DWC weight gradient into the filter bank of its own
+    head (channels h*d .. h*d + d - 1) and sums the lambda gradient over every slice. Pinned by central differences
+    of the total loss sum_{b,h} <dY[b,h], Y[b,h]>: Y is linear in the weights, so unit differences of the batched
+    forward give their gradient exactly; for lambda each slice keeps its own alpha fixed (reading R6). Two batch
+    entries and three heads, so that overwriting instead of adding, or filing a slice under the wrong head, fails."""
+    wl = WL.TINY.replace(B=2, heads=3, H=6, W=6, d=8, r=2, whiten=True, backward=True, qk_dist="student_t")
+    inp = WL.make_inputs(wl, seed=21, with_dy=True)
+    p = _params(wl)
+    Q, K, V, w, dY = inp["Q"], inp["K"], inp["V"], inp["w64"], inp["dY"]
+    g = O.backward(Q, K, V, w, dY, p)
+
+    def total(ww):
+        return float(np.sum(dY * O.forward(Q, K, V, ww, p, keep=["Y"])["Y"]))
+
+    fd = np.zeros_like(w)
+    for idx in np.ndindex(*w.shape):
+        e = np.zeros_like(w)
+        e[idx] = 1.0
+        fd[idx] = 0.5 * (total(w + e) - total(w - e))
+    assert np.linalg.norm(g["d_dwc"] - fd) <= 1e-12 * np.linalg.norm(fd)
+
+    alphas = {(b, h): O.forward_slice(Q[b, h], K[b, h], V[b, h], None, p)["alpha"]
+              for b in range(wl.B) for h in range(wl.heads)}
+
+    def total_lam(lam):
+        pp = dataclasses.replace(p, lam=lam)
+        return math.fsum(float(np.sum(dY[b, h] * O.forward_slice(Q[b, h], K[b, h], V[b, h], None, pp,
+                                                                  alpha=alphas[b, h])["Y"]))
+                         for b in range(wl.B) for h in range(wl.heads))
+
+    hl = 1e-6
+    fd_lam = (total_lam(p.lam + hl) - total_lam(p.lam - hl)) / (2 * hl)
+    assert abs(g["dlam"] - fd_lam) <= 1e-6 * abs(fd_lam), (g["dlam"], fd_lam)
+    # every slice contributes: the sum is not carried by one of them
+    per = [O.backward_slice(Q[b, h], K[b, h], V[b, h], None, dY[b, h], p)["dlam"]
+           for b in range(wl.B) for h in range(wl.heads)]
+    assert min(abs(x) for x in per) > 1e-3 * max(abs(x) for x in per)
 
 
 def test_exact_alpha_gradient_matches_finite_differences():
