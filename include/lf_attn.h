@@ -101,6 +101,20 @@ int lf_attn_saved_layout(const lf_attn_params* p, lf_saved_layout* out);
 int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w, void* Y,
                 void* saved, void* ws, size_t ws_bytes, lf_stream_t stream);
 
+/* The same forward pass (saved = NULL) for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Instead of a workspace argument it uses a static device
+ * array of the library's, LF_NOALLOC_SCRATCH_BYTES (128 MiB), which every GPU the library runs on holds from the
+ * first launch on it until the process ends; its address on a device is looked up once, on the first call for that
+ * device. The call allocates nothing (no hipMalloc, no library that does) and launches the kernels lf_attn_fwd
+ * launches, so Y is bitwise lf_attn_fwd's. Every call on one GPU shares that GPU's array: calls on one device that
+ * may overlap in time (other streams, other host threads) race, and the caller must order them. No kernel reads
+ * the array before the same call has written it, so nothing in it needs clearing between calls. Shapes whose
+ * forward workspace (lf_attn_query's fwd_ws_bytes) exceeds the array return LF_EWORKSPACE before anything is
+ * launched. Other arguments, rules and errors as lf_attn_fwd; LF_EHIP if the array's address cannot be found. */
+#define LF_NOALLOC_SCRATCH_BYTES (128 * 1024 * 1024)
+int lf_attn_fwd_noalloc(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
+                        void* Y, lf_stream_t stream);
+
 /* Backward pass of <dY, Y> with respect to Q, K and V ([abs]: forward and backward; [note] motivation "core idea"
  * for the kernel gradient, with the sign read as d/dx exp(-||x-y||_1/lambda) = -(1/lambda) sign(x-y) k).
  * saved: the buffer filled by lf_attn_fwd with the same params and inputs. ws: at least bwd_ws_bytes.

@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblf_attn.so")
-SOURCES = ["lf_api.cpp", "lf_fwd.hip", "lf_ns.hip", "lf_bwd.hip", "lf_cg.hip", "lf_gauss.hip"]
+SOURCES = ["lf_api.cpp", "lf_fwd.hip", "lf_ns.hip", "lf_bwd.hip", "lf_cg.hip", "lf_gauss.hip", "lf_noalloc.hip"]
 ARCH = "gfx950"
 
 

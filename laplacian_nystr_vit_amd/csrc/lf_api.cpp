@@ -256,6 +256,18 @@ int lf_attn_fwd(const lf_attn_params* p, const void* Q, const void* K, const voi
   return fwd_launch(p, Q, K, V, dwc_w, Y, saved, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
+int lf_attn_fwd_noalloc(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
+                        void* Y, lf_stream_t stream) {
+  static_assert(LF_NOALLOC_SCRATCH_BYTES % 256 == 0, "the scratch size keeps the workspace carve aligned");
+  const int rc = validate_fwd(p, Q, K, V, dwc_w, Y, nullptr);
+  if (rc != LF_OK) return rc;
+  if (fwd_ws(make_shape(p)).total > static_cast<size_t>(LF_NOALLOC_SCRATCH_BYTES)) return LF_EWORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  void* scratch = nullptr;
+  if (lf::noalloc_scratch(st, &scratch) != hipSuccess) return LF_EHIP;
+  return fwd_launch(p, Q, K, V, dwc_w, Y, nullptr, scratch, st);
+}
+
 int lf_attn_bwd(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,
                 const void* saved, const void* dY, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
                 lf_stream_t stream) {

@@ -58,6 +58,10 @@ bool ns_side_supported(const Shape& s);
 hipError_t launch_ns_side(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
                           const void* V, float* S, hipStream_t st);
 
+// Device address of this device's copy of the static scratch array behind lf_attn_fwd_noalloc
+// (LF_NOALLOC_SCRATCH_BYTES bytes), for the device `st` belongs to; looked up on the first call per device.
+hipError_t noalloc_scratch(hipStream_t st, void** out);
+
 // A second stream the caller owns, with two events of its own, for backward work that does not depend on the
 // rest: the caller's stream forks to it through `fork` and waits on `join`. Null members are never passed here.
 struct AuxStream {

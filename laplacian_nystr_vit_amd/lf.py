@@ -27,8 +27,9 @@ LF_NS_ITERS_MAX = 64
 EXPORTS = (
     "lf_attn_query", "lf_attn_saved_layout", "lf_attn_fwd", "lf_attn_bwd", "lf_strerror", "lf_landmark_pool",
     "lf_laplace_l1_exp", "lf_ns_pinv", "lf_ckv_reduce", "lf_whiten_stats", "lf_landmark_mix", "lf_out_gemm_dwc",
-    "lf_out_gemm_dwc_fused", "lf_attn_bwd_ex", "lf_cg_pinv", "lf_gauss_l2_exp",
+    "lf_out_gemm_dwc_fused", "lf_attn_bwd_ex", "lf_cg_pinv", "lf_gauss_l2_exp", "lf_attn_fwd_noalloc",
 )
+LF_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 LF_BWD_EXACT_ALPHA = 1
 LF_CG_ITERS_MAX = 256
 
@@ -104,6 +105,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lf_attn_query": (ctypes.c_int, [_P, ctypes.POINTER(_sz), ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
         "lf_attn_saved_layout": (ctypes.c_int, [_P, ctypes.POINTER(LfSavedLayout)]),
         "lf_attn_fwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "lf_attn_fwd_noalloc": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp]),
         "lf_attn_bwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "lf_attn_bwd_ex": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int,
                                           _vp, _sz, _vp, ctypes.POINTER(LfAuxStream)]),
@@ -200,6 +202,15 @@ def lf_attn_fwd(p, Q, K, V, dwc_w, Y, saved, ws, stream=None) -> None:
         raise ValueError(f"saved needs {saved_b} bytes")
     _check(load_library().lf_attn_fwd(ctypes.byref(p), *args, _ptr(saved, "saved"), _ptr(ws, "ws"), _nbytes(ws),
                                       _stream(stream)), "lf_attn_fwd")
+
+
+def lf_attn_fwd_noalloc(p, Q, K, V, dwc_w, Y, stream=None) -> None:
+    """The forward pass on the library's static device scratch array (no workspace argument, nothing allocated)."""
+    dt, n = io_dtype(p), p.G * p.N * p.d
+    _check(load_library().lf_attn_fwd_noalloc(
+        ctypes.byref(p), _ptr(Q, "Q", dt, n), _ptr(K, "K", dt, n), _ptr(V, "V", dt, n),
+        _ptr(dwc_w, "dwc_w", torch.float32, p.heads * p.d * 9), _ptr(Y, "Y", dt, n), _stream(stream)),
+        "lf_attn_fwd_noalloc")
 
 
 def lf_attn_bwd(p, Q, K, V, dwc_w, saved, dY, dQ, dK, dV, ws, stream=None) -> None:

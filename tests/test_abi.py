@@ -187,3 +187,27 @@ def test_gaussian_variant_is_forward_only_on_host(lib):
     with pytest.raises(ValueError):
         lf.make_params(1, 1, 8, 8, 16, 2, kernel="cosine")
 
+
+def test_fwd_noalloc_rejects_on_host(lib):
+    """The allocation-free forward rejects, before touching the device, a shape whose forward workspace exceeds its
+    static scratch array (LF_EWORKSPACE), and bad pointers or parameters (LF_EINVAL), like lf_attn_fwd."""
+    m = re.search(r"#define LF_NOALLOC_SCRATCH_BYTES \(([0-9 *]+)\)", open(HEADER).read())
+    assert m and eval(m.group(1), {"__builtins__": {}}) == lf.LF_NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(0x100000)
+    misaligned = ctypes.c_void_p(0x100004)
+    big = _p(WL.HIRES_BF16.replace(B=4))
+    fwd, _, _ = lf.lf_attn_query(big)
+    assert fwd > lf.LF_NOALLOC_SCRATCH_BYTES
+    assert lib.lf_attn_fwd_noalloc(ctypes.byref(big), fake, fake, fake, None, ctypes.c_void_p(0x200000),
+                                   None) == lf.LF_EWORKSPACE
+    p = _p(WL.PVT_S1)
+    fwd, _, _ = lf.lf_attn_query(p)
+    assert fwd <= lf.LF_NOALLOC_SCRATCH_BYTES
+    assert lib.lf_attn_fwd_noalloc(ctypes.byref(p), misaligned, fake, fake, None, ctypes.c_void_p(0x200000),
+                                   None) == lf.LF_EINVAL
+    assert lib.lf_attn_fwd_noalloc(ctypes.byref(p), fake, fake, fake, None, fake, None) == lf.LF_EINVAL  # Y == Q
+    assert lib.lf_attn_fwd_noalloc(ctypes.byref(p), fake, fake, fake, None, None, None) == lf.LF_EINVAL
+    bad = _p(WL.PVT_S1)
+    bad.r = 5  # 56 % 5 != 0
+    assert lib.lf_attn_fwd_noalloc(ctypes.byref(bad), fake, fake, fake, None, ctypes.c_void_p(0x200000),
+                                   None) == lf.LF_EINVAL
