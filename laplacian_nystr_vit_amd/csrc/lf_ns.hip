@@ -13,7 +13,7 @@
 namespace lf {
 
 // =====================================================================================================
-// m <= 64: one 256-thread block per slice runs every iteration out of LDS.
+// m <= 64: one 512-thread block (eight waves, two per SIMD) per slice runs every iteration out of LDS.
 //
 // Products run on the fp16 MFMA (v_mfma_f32_16x16x32_f16, 16x the fp32 MFMA rate on gfx950) with every fp32
 // operand split as x = hi + lo (two fp16 values, about 22 significant bits) and
@@ -21,28 +21,34 @@ namespace lf {
 // accumulated in fp32. Three fp16 MFMAs cost less than a fifth of one fp32 MFMA product, and the result tracks an
 // fp32 product to a few units of 1e-7.
 //
-// Matrices are zero-padded to 16 ST x 16 ST (ST = 1, 2 or 4 strips of 16) and kept K-contiguous in LDS, so each
-// lane's 8-element fragment is one 16-byte read: U = 2I - W X by columns (B operand of X U) and X twice, by rows
-// (A operand of X U) and by columns (B operand of W X). W, the A operand of W X, never changes: each wave keeps
-// its fragments in registers. (X_k is symmetric in exact arithmetic, but feeding its transpose to the update
-// doubles the antisymmetric part of the rounding error every step, so both layouts are kept.)
+// Every matrix is zero-padded to 16 ST x 16 ST (ST = 1, 2 or 4 strips of 16) and stored in LDS by columns (the
+// entries of column j contiguous), which is the layout the MFMA result has (four consecutive rows of one column
+// per lane, one 8-byte store per split half). A product reads its B operand (columns, K-contiguous) with plain
+// 16-byte reads and its A operand (rows) with gfx950's transposing LDS read, ds_read_b64_tr_b16: within each group
+// of 16 lanes, result lane j, element s comes from element j % 4 of the 8 bytes lane 4 s + j / 4 addressed, so
+// two such reads at columns k = 8 (lane / 16) + 4 h + (lane % 16) / 4 give a lane its row's eight consecutive K
+// values. Each matrix is therefore read as itself, never as its transpose: X_k is symmetric only in exact
+// arithmetic, and feeding X_k^T where the recurrence has X_k doubles the antisymmetric part of the rounding error
+// every step. W, the A operand of W X, never changes: its fragments stay in registers.
 //
-// Work split: wave w owns the (w & 1, w >> 1) quadrant of every product (TQ x TQ tiles of 16 x 16), which reads
-// half of each operand instead of one full operand per wave. X is double-buffered, so an iteration needs two
-// barriers: after U is written and after X_next is written. The MFMA result layout (four consecutive rows of
-// one column per lane) gives the by-columns copy of X_next with 8-byte stores; the by-rows copy comes from a
-// second product with the operand roles swapped, (X U)^T = U^T X^T, which reuses the same fragments and yields
-// four consecutive columns of one row per lane. The two copies differ only by rounding.
+// A step of the coupled recurrence (below) is two products that share their B operand U_k = 2I - T_k:
+// T_{k+1} = T_k U_k and X_{k+1} = X_k U_k. With 64-wide matrices each wave takes one row strip and two column
+// strips of a quadrant in both products (24 MFMAs, 16 KB of fragments, T_{k+1}, U_{k+1} = 2I - T_{k+1} and
+// X_{k+1} stored from its accumulators), so the two waves of a SIMD carry equal work and each one's epilogue
+// overlaps the other's MFMAs. With narrower matrices (one tile per quadrant) waves 0-3 form T and U and waves 4-7
+// form X. Every buffer is double-buffered by step parity, so a step needs one barrier.
 //
 // X carries a power-of-two scale 2^-e in its fp16 halves: e follows the largest entry of the previous iterate
 // so that entries sit near 2^12 (far from fp16's subnormals and its 65504 limit); an iterate that still comes
 // out above 2^15 is stored again with a fresh exponent. W needs no scale (entries at most 1 + eps) and neither
-// does U (the eigenvalues of W X stay in (0, 1]).
+// do T and U (the eigenvalues of W X stay in (0, 1]).
 // =====================================================================================================
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
 
-constexpr int NH = 72;  // fp16 elements per LDS row: 64 + 8 (144-byte stride, 16-byte aligned)
+constexpr int NH = 72;  // fp16 elements per LDS column: 64 + 8 (144-byte stride, 16-byte aligned)
 
 struct alignas(16) SplitMat {
   _Float16 hi[64 * NH];
@@ -60,48 +66,69 @@ struct Frags {
   half8 h[TQ][KC], l[TQ][KC];
 };
 
-// Chunk c (K entries 32 c .. 32 c + 31) of the fragments of strips s0 .. s0+TQ-1 of a K-contiguous split
-// matrix (row i holds its K entries at i*NH ...).
+// B operand: chunk c (K entries 32 c .. 32 c + 31) of column strips s0 .. s0+TQ-1 of a by-columns split matrix
+// (element (k, j) at j*NH + k): one 16-byte read per lane and half.
 template <int TQ, int KC>
-__device__ __forceinline__ void load_chunk(const SplitMat& M, int s0, int ln, int c, Frags<TQ, KC>& f) {
+__device__ __forceinline__ void load_chunk_b(const SplitMat& M, int s0, int ln, int c, Frags<TQ, KC>& f) {
 #pragma unroll
   for (int a = 0; a < TQ; ++a) {
-    const int i = (s0 + a) * 16 + (ln & 15);
+    const int j = (s0 + a) * 16 + (ln & 15);
     const int k0 = c * 32 + 8 * (ln >> 4);
-    f.h[a][c] = *reinterpret_cast<const half8*>(&M.hi[i * NH + k0]);
-    f.l[a][c] = *reinterpret_cast<const half8*>(&M.lo[i * NH + k0]);
+    f.h[a][c] = *reinterpret_cast<const half8*>(&M.hi[j * NH + k0]);
+    f.l[a][c] = *reinterpret_cast<const half8*>(&M.lo[j * NH + k0]);
   }
 }
 
-template <int TQ>
-__device__ __forceinline__ void zero_acc(f32x4 acc[TQ][TQ]) {
+__device__ __forceinline__ short4v lds_read_tr(const _Float16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p));
+}
+
+// A operand: chunk c of row strips s0 .. s0+TQ-1 of the same by-columns matrix (element (i, k) at k*NH + i), by
+// transposing reads: lane t of lane group g addresses column k = 32 c + 8 g + 4 h + t / 4, rows 4 (t % 4) .. + 3
+// of the strip, and receives row 16 strip + t at K = 32 c + 8 g + 4 h .. + 3.
+template <int TQ, int KC>
+__device__ __forceinline__ void load_chunk_a(const SplitMat& M, int s0, int ln, int c, Frags<TQ, KC>& f) {
+  const int g = ln >> 4, t = ln & 15;
 #pragma unroll
-  for (int a = 0; a < TQ; ++a)
+  for (int a = 0; a < TQ; ++a) {
+    const int i = (s0 + a) * 16 + 4 * (t & 3);
+    const int k0 = c * 32 + 8 * g + (t >> 2);
+    const short4v h0 = lds_read_tr(&M.hi[k0 * NH + i]), h1 = lds_read_tr(&M.hi[(k0 + 4) * NH + i]);
+    const short4v l0 = lds_read_tr(&M.lo[k0 * NH + i]), l1 = lds_read_tr(&M.lo[(k0 + 4) * NH + i]);
+    const half4 hh0 = __builtin_bit_cast(half4, h0), hh1 = __builtin_bit_cast(half4, h1);
+    const half4 ll0 = __builtin_bit_cast(half4, l0), ll1 = __builtin_bit_cast(half4, l1);
+    f.h[a][c] = half8{hh0[0], hh0[1], hh0[2], hh0[3], hh1[0], hh1[1], hh1[2], hh1[3]};
+    f.l[a][c] = half8{ll0[0], ll0[1], ll0[2], ll0[3], ll1[0], ll1[1], ll1[2], ll1[3]};
+  }
+}
+
+template <int TA, int TB>
+__device__ __forceinline__ void zero_acc(f32x4 acc[TA][TB]) {
 #pragma unroll
-    for (int b = 0; b < TQ; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < TA; ++a)
+#pragma unroll
+    for (int b = 0; b < TB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // acc[a][b] += A-strip a times B-strip b over chunk c. One fp32 accumulator per tile takes hi*hi and both cross
 // terms: each MFMA step rounds at fp32 relative to the running sum, which keeps the product at fp32 accuracy.
-// Loads are issued chunk by chunk and consumed in the same order, so the MFMAs of chunk 0 can overlap the LDS
-// reads of chunk 1.
-template <int TQ, int KC>
-__device__ __forceinline__ void mma_chunk(const Frags<TQ, KC>& A, const Frags<TQ, KC>& B, f32x4 acc[TQ][TQ],
+template <int TA, int TB, int KC>
+__device__ __forceinline__ void mma_chunk(const Frags<TA, KC>& A, const Frags<TB, KC>& B, f32x4 acc[TA][TB],
                                           int c) {
 #pragma unroll
-  for (int a = 0; a < TQ; ++a)
+  for (int a = 0; a < TA; ++a)
 #pragma unroll
-    for (int b = 0; b < TQ; ++b)
+    for (int b = 0; b < TB; ++b)
       acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.h[a][c], B.h[b][c], acc[a][b], 0, 0, 0);
 #pragma unroll
-  for (int a = 0; a < TQ; ++a)
+  for (int a = 0; a < TA; ++a)
 #pragma unroll
-    for (int b = 0; b < TQ; ++b)
+    for (int b = 0; b < TB; ++b)
       acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.h[a][c], B.l[b][c], acc[a][b], 0, 0, 0);
 #pragma unroll
-  for (int a = 0; a < TQ; ++a)
+  for (int a = 0; a < TA; ++a)
 #pragma unroll
-    for (int b = 0; b < TQ; ++b)
+    for (int b = 0; b < TB; ++b)
       acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.l[a][c], B.h[b][c], acc[a][b], 0, 0, 0);
 }
 
@@ -124,19 +151,10 @@ __device__ __forceinline__ void split4(f32x4 v, half4& h, half4& l) {
   l = half4{l0[0], l0[1], l1[0], l1[1]};
 }
 
-// The 4 rows i0 .. i0+3 of column j, stored transposed: Mt[j][i0 .. i0+3] (two 8-byte writes).
-__device__ __forceinline__ void put_t4(SplitMat& Mt, int j, int i0, half4 h, half4 l) {
-  *reinterpret_cast<half4*>(&Mt.hi[j * NH + i0]) = h;
-  *reinterpret_cast<half4*>(&Mt.lo[j * NH + i0]) = l;
-}
-
-// The same 4 entries stored row-major: M[i0 + r][j].
-__device__ __forceinline__ void put_rows4(SplitMat& M, int i0, int j, half4 h, half4 l) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    M.hi[(i0 + r) * NH + j] = h[r];
-    M.lo[(i0 + r) * NH + j] = l[r];
-  }
+// The 4 rows i0 .. i0+3 of column j into a by-columns matrix: M[j][i0 .. i0+3] (two 8-byte writes).
+__device__ __forceinline__ void put_t4(SplitMat& M, int j, int i0, half4 h, half4 l) {
+  *reinterpret_cast<half4*>(&M.hi[j * NH + i0]) = h;
+  *reinterpret_cast<half4*>(&M.lo[j * NH + i0]) = l;
 }
 
 // Largest exponent e of an fp32 value (v = f * 2^e, f in [1, 2)) for v > 0; -126 for 0 and subnormals.
@@ -178,13 +196,15 @@ template <int ST, int KC>
 __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ We, float* __restrict__ Xout,
                                                float* __restrict__ xs, float* __restrict__ alpha_out,
                                                float* __restrict__ resid, int m, int iters) {
-  constexpr int TQ = ST >= 2 ? ST / 2 : 1;  // tiles per side of a wave's quadrant
+  constexpr int TQ = ST >= 2 ? ST / 2 : 1;  // tiles per side of a quadrant
   constexpr int NQA = ST == 1 ? 1 : 4;      // quadrants with work
+  constexpr int CS = TQ;                    // column strips (B operand) per wave
+  constexpr bool kBoth = TQ >= 2;           // each wave takes part in both products (else one product per wave)
   constexpr int NTH = 512;
-  // sX: X by rows. sT: T = W X by rows (and X by columns where the final exact step needs it). sU: U = 2I - T by
-  // columns. Each is double-buffered by iteration parity.
-  __shared__ SplitMat sX[2], sT[2], sU[2];
+  // sT, sU, sX: T_k, U_k = 2I - T_k and X_k (times 2^-e) by columns, each double-buffered by step parity.
+  __shared__ SplitMat sT[2], sU[2], sX[2];
   __shared__ double red[3][4][64];
+  __shared__ double red_res[8];
   __shared__ float s_alpha, s_wmax;
   // Bits of the largest |X| entry of the iterate written in step k, in slot k % 3: slot k + 1 is cleared during
   // step k (its last readers finished before the barrier of step k - 1), so the one barrier per step suffices.
@@ -193,13 +213,14 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
   const size_t mm = static_cast<size_t>(m) * m;
   const float* wg = We + g * mm;
   float* wf = reinterpret_cast<float*>(&sU[1]);  // fp32 W (64 x 65) in a U buffer not used before iteration 0
-  // Eight waves, two per SIMD: waves 0-3 ("X waves") own the products that produce X, waves 4-7 ("T waves")
-  // those that produce T and U, each on quadrant wv & 3. On every SIMD one wave's split-and-store epilogue then
-  // runs while the other wave's MFMAs execute.
-  const int qd = wv & 3;
-  const bool active = qd < NQA;
-  const bool xw = active && wv < 4, tw = active && wv >= 4;
-  const int r0 = (qd & 1) * TQ, c0 = (qd >> 1) * TQ;  // first row strip and first column strip of the quadrant
+  // Wave w works on quadrant w & 3 of the products. With 64-wide matrices (two strips per quadrant side) wave half
+  // w >> 2 takes one row strip of the quadrant and both of its column strips, in both products; with narrower
+  // matrices (one tile per quadrant) half 0 forms T_{k+1} and U_{k+1}, half 1 forms X_{k+1}.
+  const int qd = wv & 3, hf = wv >> 2;
+  const bool act = qd < NQA;
+  const bool doT = act && (kBoth || hf == 0), doX = act && (kBoth || hf == 1);
+  const int rs = (qd & 1) * TQ + (kBoth ? hf : 0);  // the wave's row strip
+  const int c0 = (qd >> 1) * TQ;                    // its first column strip
   constexpr int NZ = static_cast<int>(sizeof(SplitMat) / sizeof(uint4));
   const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
 
@@ -226,31 +247,31 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
   // column c and of row c, the quarters are combined, then wave 0 takes the maxima (and max |W_ij|).
   if (tid < 256) {
     const int c = tid & 63, qtr = tid >> 6;
-    double cs = 0.0, rs = 0.0, mx = 0.0;
+    double cs = 0.0, rsum = 0.0, mx = 0.0;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const double a = fabs(static_cast<double>(wf[(qtr * 16 + k) * 65 + c]));
       cs += a;
       mx = fmax(mx, a);
-      rs += fabs(static_cast<double>(wf[c * 65 + qtr * 16 + k]));
+      rsum += fabs(static_cast<double>(wf[c * 65 + qtr * 16 + k]));
     }
     red[0][qtr][c] = cs;
-    red[1][qtr][c] = rs;
+    red[1][qtr][c] = rsum;
     red[2][qtr][c] = mx;
   }
   __syncthreads();
   if (wv == 0) {
     double cs = red[0][0][ln] + red[0][1][ln] + red[0][2][ln] + red[0][3][ln];
-    double rs = red[1][0][ln] + red[1][1][ln] + red[1][2][ln] + red[1][3][ln];
+    double rsum = red[1][0][ln] + red[1][1][ln] + red[1][2][ln] + red[1][3][ln];
     double mx = fmax(fmax(red[2][0][ln], red[2][1][ln]), fmax(red[2][2][ln], red[2][3][ln]));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       cs = fmax(cs, __shfl_xor(cs, off));
-      rs = fmax(rs, __shfl_xor(rs, off));
+      rsum = fmax(rsum, __shfl_xor(rsum, off));
       mx = fmax(mx, __shfl_xor(mx, off));
     }
     if (ln == 0) {
-      s_alpha = static_cast<float>(1.0 / (cs * rs));
+      s_alpha = static_cast<float>(1.0 / (cs * rsum));
       s_wmax = static_cast<float>(mx);
     }
   }
@@ -258,128 +279,96 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
   const float alpha = s_alpha;
   if (tid == 0 && alpha_out) alpha_out[g] = alpha;
 
-  // W fragments of this wave's row strips (W is the A operand of every product with W), and X_0 = alpha W^T.
-  Frags<TQ, KC> fw;
-  f32x4 x0c[TQ][TQ], x0r[TQ][TQ];  // X_0 quadrant tiles in the by-columns and the by-rows lane layouts
+  // W fragments of this wave's row strip (W is the A operand of every product with W).
+  Frags<1, KC> fw;
 #pragma unroll
-  for (int c = 0; c < KC; ++c)
+  for (int c = 0; c < KC; ++c) {
+    const int i = rs * 16 + (ln & 15);
+    const int k0 = c * 32 + 8 * (ln >> 4);
 #pragma unroll
-    for (int a = 0; a < TQ; ++a) {
-      const int i = (r0 + a) * 16 + (ln & 15);
-      const int k0 = c * 32 + 8 * (ln >> 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        _Float16 h, l;
-        split_f16(active ? wf[i * 65 + k0 + e] : 0.f, h, l);
-        fw.h[a][c][e] = h;
-        fw.l[a][c][e] = l;
-      }
+    for (int e = 0; e < 8; ++e) {
+      _Float16 h, l;
+      split_f16(doT ? wf[i * 65 + k0 + e] : 0.f, h, l);
+      fw.h[0][c][e] = h;
+      fw.l[0][c][e] = l;
     }
-  bool inside[TQ][TQ][4];
-  float two_i[TQ][TQ][4];  // 2 on the diagonal of the m x m block, 0 elsewhere (padding included)
+  }
+  // Lane placement of the wave's tile b: rows row_i0() .. +3 of column col_j(b).
+  auto col_j = [&](int b) { return (c0 + b) * 16 + (ln & 15); };
+  auto row_i0 = [&]() { return rs * 16 + 4 * (ln >> 4); };
+  // 2 on the diagonal of the m x m block, 0 elsewhere (padding included); whether an entry is inside the block
+  auto two_i = [&](int b, int r) { return (row_i0() + r == col_j(b) && col_j(b) < m) ? 2.f : 0.f; };
+  auto inside = [&](int b, int r) { return row_i0() + r < m && col_j(b) < m; };
+  f32x4 accT[1][CS], accX[1][CS];
 #pragma unroll
-  for (int a = 0; a < TQ; ++a)
+  for (int b = 0; b < CS; ++b)
 #pragma unroll
-    for (int b = 0; b < TQ; ++b) {
-      const int j = (c0 + b) * 16 + (ln & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = (r0 + a) * 16 + 4 * (ln >> 4) + r;
-        inside[a][b][r] = i < m && j < m;
-        two_i[a][b][r] = (i == j && i < m) ? 2.f : 0.f;
-        x0c[a][b][r] = active ? alpha * wf[j * 65 + i] : 0.f;
-        // by-rows tile (a, b): row (r0 + b) 16 + lane % 16, column (c0 + a) 16 + 4 (lane / 16) + r
-        const int ir = (r0 + b) * 16 + (ln & 15), jr = (c0 + a) * 16 + 4 * (ln >> 4) + r;
-        x0r[a][b][r] = active ? alpha * wf[jr * 65 + ir] : 0.f;
-      }
-    }
+    for (int r = 0; r < 4; ++r) accX[0][b][r] = doX ? alpha * wf[col_j(b) * 65 + row_i0() + r] : 0.f;  // X_0
   __syncthreads();  // wf (inside sU[1]) is dead after this point
   if constexpr (ST == 1) {
     for (int q = tid; q < NZ; q += NTH) reinterpret_cast<uint4*>(&sU[1])[q] = zero4;
   }
 
-  // Lane placement of quadrant tiles. By-columns tile (a, b), a product mma(rows of strips r0.., rows of strips
-  // c0..): the lane holds rows col_i0(a) .. +3 of column col_j(b). By-rows tile (a, b), the same product with the
-  // operand roles swapped, mma(strips c0.., strips r0..), so a indexes column strips and b row strips: the lane
-  // holds columns row_j0(a) .. +3 of row row_i(b).
-  auto col_j = [&](int b) { return (c0 + b) * 16 + (ln & 15); };
-  auto col_i0 = [&](int a) { return (r0 + a) * 16 + 4 * (ln >> 4); };
-  auto row_i = [&](int b) { return (r0 + b) * 16 + (ln & 15); };
-  auto row_j0 = [&](int a) { return (c0 + a) * 16 + 4 * (ln >> 4); };
-  // Split stores: by-columns tiles into a by-columns buffer, by-rows tiles into a by-rows buffer (8-byte writes).
-  auto put_cols = [&](SplitMat& M, const f32x4 v[TQ][TQ], float s) {
+  // Split stores of the wave's tiles into a by-columns buffer (8-byte writes).
+  auto put_cols = [&](SplitMat& M, const f32x4 v[1][CS], float s) {
 #pragma unroll
-    for (int a = 0; a < TQ; ++a)
-#pragma unroll
-      for (int b = 0; b < TQ; ++b) {
-        half4 h, l;
-        split_scaled4(v[a][b], s, h, l);
-        put_t4(M, col_j(b), col_i0(a), h, l);
-      }
+    for (int b = 0; b < CS; ++b) {
+      half4 h, l;
+      split_scaled4(v[0][b], s, h, l);
+      put_t4(M, col_j(b), row_i0(), h, l);
+    }
   };
-  auto put_rows = [&](SplitMat& M, const f32x4 v[TQ][TQ], float s) {
-#pragma unroll
-    for (int a = 0; a < TQ; ++a)
-#pragma unroll
-      for (int b = 0; b < TQ; ++b) {
-        half4 h, l;
-        split_scaled4(v[a][b], s, h, l);
-        put_t4(M, row_i(b), row_j0(a), h, l);
-      }
-  };
-  // put_rows that also returns the largest |v| (before scaling).
-  auto put_rows_max = [&](SplitMat& M, const f32x4 v[TQ][TQ], float s) {
+  // put_cols that also returns the largest |v| (before scaling).
+  auto put_cols_max = [&](SplitMat& M, const f32x4 v[1][CS], float s) {
     float lm = 0.f;
 #pragma unroll
-    for (int a = 0; a < TQ; ++a)
-#pragma unroll
-      for (int b = 0; b < TQ; ++b) {
-        const f32x4 t = v[a][b];
-        lm = fmaxf(lm, fmaxf(fmaxf(fabsf(t[0]), fabsf(t[1])), fmaxf(fabsf(t[2]), fabsf(t[3]))));
-        half4 h, l;
-        split_scaled4(t, s, h, l);
-        put_t4(M, row_i(b), row_j0(a), h, l);
-      }
+    for (int b = 0; b < CS; ++b) {
+      const f32x4 t = v[0][b];
+      lm = fmaxf(lm, fmaxf(fmaxf(fabsf(t[0]), fabsf(t[1])), fmaxf(fabsf(t[2]), fabsf(t[3]))));
+      half4 h, l;
+      split_scaled4(t, s, h, l);
+      put_t4(M, col_j(b), row_i0(), h, l);
+    }
     return lm;
   };
-  // U = 2I - s v from by-columns tiles of T (padding rows and columns of T are exact zeros, so U is zero there).
-  auto put_u = [&](SplitMat& M, const f32x4 v[TQ][TQ], float s) {
+  // T = s v and U = 2I - s v from the same tiles (padding rows and columns of T are exact zeros, so U is zero
+  // there); U alone when T is not needed.
+  auto put_tu = [&](SplitMat* Mt, SplitMat& Mu, const f32x4 v[1][CS], float s) {
 #pragma unroll
-    for (int a = 0; a < TQ; ++a)
+    for (int b = 0; b < CS; ++b) {
+      f32x4 t, u;
 #pragma unroll
-      for (int b = 0; b < TQ; ++b) {
-        f32x4 u;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) u[r] = two_i[a][b][r] - v[a][b][r] * s;
-        half4 h, l;
-        split4(u, h, l);
-        put_t4(M, col_j(b), col_i0(a), h, l);
+      for (int r = 0; r < 4; ++r) {
+        t[r] = v[0][b][r] * s;
+        u[r] = two_i(b, r) - t[r];
       }
+      half4 h, l;
+      if (Mt) {
+        split4(t, h, l);
+        put_t4(*Mt, col_j(b), row_i0(), h, l);
+      }
+      split4(u, h, l);
+      put_t4(Mu, col_j(b), row_i0(), h, l);
+    }
   };
-  // Iterate k to the saved-iterates buffer, from by-rows tiles (rows_layout) or by-columns tiles.
-  auto put_xs = [&](int k, const f32x4 v[TQ][TQ], float s, bool rows_layout) {
+  // Iterate k to the saved-iterates buffer, from the wave's tiles.
+  auto put_xs = [&](int k, const f32x4 v[1][CS], float s) {
     float* xg = xs + (static_cast<size_t>(g) * (iters + 1) + k) * mm;
 #pragma unroll
-    for (int a = 0; a < TQ; ++a)
+    for (int b = 0; b < CS; ++b)
 #pragma unroll
-      for (int b = 0; b < TQ; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = rows_layout ? row_i(b) : col_i0(a) + r;
-          const int j = rows_layout ? row_j0(a) + r : col_j(b);
-          if (i < m && j < m) xg[i * m + j] = v[a][b][r] * s;
-        }
+      for (int r = 0; r < 4; ++r)
+        if (inside(b, r)) xg[(row_i0() + r) * m + col_j(b)] = v[0][b][r] * s;
   };
-  auto frags_of = [&](const SplitMat& M, int s0, Frags<TQ, KC>& f) {
+  // W * B over the wave's tiles, W's fragments from registers.
+  auto mma_w = [&](const SplitMat& B, f32x4 acc[1][CS]) {
+    Frags<CS, KC> fb;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) load_chunk<TQ, KC>(M, s0, ln, c, f);
-  };
-  auto mma = [&](const Frags<TQ, KC>& A, const Frags<TQ, KC>& B, f32x4 acc[TQ][TQ]) {
-    zero_acc<TQ>(acc);
+    for (int c = 0; c < KC; ++c) load_chunk_b<CS, KC>(B, c0, ln, c, fb);
+    zero_acc<1, CS>(acc);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) mma_chunk<TQ, KC>(A, B, acc, c);
+    for (int c = 0; c < KC; ++c) mma_chunk<1, CS, KC>(fw, fb, acc, c);
   };
-
 
   // The exact Newton-Schulz step X_{k+1} = X_k (2I - W X_k) equals, for T_k = W X_k, the pair
   //   T_{k+1} = T_k (2I - T_k),  X_{k+1} = X_k (2I - T_k),
@@ -391,62 +380,56 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
   // product, 2^-22), and the last step is the exact update from X_{K-1}, which squares what is left; the result
   // then tracks the exact-step iteration to rounding.
   int e_cur = store_exp(alpha * s_wmax);  // storage exponent of the iterate in sX[cur]; X_0's max is alpha max|W|
-  const int xcol_first = 1;               // buffer of sT that receives X_0 by columns
-  if (xw) {
-    put_rows(sX[0], x0r, ldexpf(1.f, -e_cur));
-    if (xs) put_xs(0, x0c, 1.f, false);
+  if (doX) {
+    put_cols(sX[0], accX, ldexpf(1.f, -e_cur));
+    if (xs) put_xs(0, accX, 1.f);
   }
-  if (tw) put_cols(sT[xcol_first], x0c, ldexpf(1.f, -e_cur));
   __syncthreads();
 
-  f32x4 accA[TQ][TQ], accB[TQ][TQ], accC[TQ][TQ];
-  int xcol_buf = xcol_first;  // where the latest X by columns sits (the segment start and the exact step read it)
-  // Segment start at step k: T_k = W X_k by columns (into U_k = 2I - T_k) and, with the operands swapped, by rows.
-  // After the first segment, X_k by columns sits in sT[k & 1], the buffer T_k goes to: every T wave loads its
-  // fragments before any of them stores.
+  // Segment start at step k: T_k = W X_k (and U_k) into the buffers of parity k & 1, which no wave reads now.
   auto resync = [&](int k) {
     const int cur = k & 1;
-    Frags<TQ, KC> fxc;
-    if (tw) frags_of(sT[xcol_buf], c0, fxc);
-    if (xcol_buf == cur) __syncthreads();
-    if (tw) {
-      mma(fw, fxc, accA);
-      mma(fxc, fw, accB);
-      const float unscale = ldexpf(1.f, e_cur);
-      put_u(sU[cur], accA, unscale);
-      put_rows(sT[cur], accB, unscale);
+    if (doT) {
+      mma_w(sX[cur], accT);
+      put_tu(&sT[cur], sU[cur], accT, ldexpf(1.f, e_cur));
     }
     __syncthreads();
   };
 
   int e_next = e_cur;
   // One pair step; the buffer parity is a template constant so that every LDS address is a fixed offset.
-  // last: the step ends a segment, so it produces X_{k+1} by columns as well and no T_{k+1} / U_{k+1}.
-  auto step = [&](auto parity, int k, bool last) __attribute__((always_inline)) {
+  // last: the step ends a segment, so it produces only X_{k+1} (the next segment forms T afresh).
+  auto step = [&](auto parity, auto last, int k) __attribute__((always_inline)) {
     constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
+    constexpr bool kLast = decltype(last)::value;
     const float unscale = ldexpf(1.f, e_cur);
-    if (xw) {
-      Frags<TQ, KC> fu, fx;
-      frags_of(sU[cur], c0, fu);
-      frags_of(sX[cur], r0, fx);
-      mma(fu, fx, accC);  // (X_k U_k)^T: X_{k+1} by rows
-      float lmax = put_rows_max(sX[nxt], accC, ldexpf(1.f, e_cur - e_next));
-      if (xs) put_xs(k + 1, accC, unscale, true);
-      lmax = wave_max_nonneg(lmax) * unscale;
-      if (ln == 0) atomicMax(&s_max[k % 3], __float_as_uint(lmax));
-    } else if (tw) {
-      Frags<TQ, KC> fu, ft;
-      frags_of(sU[cur], c0, fu);
-      if (!last) {
-        frags_of(sT[cur], r0, ft);
-        mma(ft, fu, accA);  // T_k U_k by columns: U_{k+1}
-        mma(fu, ft, accB);  // (T_k U_k)^T: T_{k+1} by rows
-        put_u(sU[nxt], accA, 1.f);
-        put_rows(sT[nxt], accB, 1.f);
-      } else {
-        frags_of(sX[cur], r0, ft);
-        mma(ft, fu, accA);  // X_k U_k by columns: X_{K-1} for the exact step
-        put_cols(sT[nxt], accA, ldexpf(1.f, e_cur - e_next));
+    const bool wt = doT && !kLast;
+    if (wt || doX) {
+      // every read of both chunks is issued before the first MFMA, so chunk 0's MFMAs overlap chunk 1's reads
+      Frags<CS, KC> fu;
+      Frags<1, KC> ft, fx;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        load_chunk_b<CS, KC>(sU[cur], c0, ln, c, fu);
+        if (wt) load_chunk_a<1, KC>(sT[cur], rs, ln, c, ft);
+        if (doX) load_chunk_a<1, KC>(sX[cur], rs, ln, c, fx);
+      }
+      if (wt) {
+        zero_acc<1, CS>(accT);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) mma_chunk<1, CS, KC>(ft, fu, accT, c);  // T_{k+1} = T_k U_k
+      }
+      if (doX) {
+        zero_acc<1, CS>(accX);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) mma_chunk<1, CS, KC>(fx, fu, accX, c);  // X_{k+1} = X_k U_k, times 2^-e_cur
+      }
+      if (wt) put_tu(&sT[nxt], sU[nxt], accT, 1.f);
+      if (doX) {
+        float lmax = put_cols_max(sX[nxt], accX, ldexpf(1.f, e_cur - e_next));
+        if (xs) put_xs(k + 1, accX, unscale);
+        lmax = wave_max_nonneg(lmax) * unscale;
+        if (ln == 0) atomicMax(&s_max[k % 3], __float_as_uint(lmax));
       }
     }
     if (tid == 0) s_max[(k + 1) % 3] = 0u;
@@ -455,105 +438,95 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
     if (mx >= ldexpf(1.f, e_next + kRestoreExp) || !(mx < 3.0e38f)) {
       // Rare: the iterate grew past the headroom of its exponent (or is not finite); store it again.
       const int e_new = store_exp(fminf(mx, 3.0e38f));
-      const float rel = ldexpf(1.f, e_cur - e_new);
-      if (xw) put_rows(sX[nxt], accC, rel);
-      if (tw && last) put_cols(sT[nxt], accA, rel);
+      if (doX) put_cols(sX[nxt], accX, ldexpf(1.f, e_cur - e_new));
       e_next = e_new;
       __syncthreads();
     }
     e_cur = e_next;
     e_next = store_exp(mx);
-    if (last) xcol_buf = nxt;
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
+  using Mid = std::integral_constant<bool, false>;
+  using End = std::integral_constant<bool, true>;
   for (int k = 0; k + 1 < iters;) {
     resync(k);
     const int end = min(k + kPairRun, iters - 1);  // pair steps k .. end - 1; step K - 1 is the exact one
-    // steps in (even, odd) pairs so that each step's buffer parity is a compile-time constant
-    if (k & 1) {
-      step(P1{}, k, k + 1 == end);
-      ++k;
-    }
-    for (; k + 1 < end; k += 2) {
-      step(P0{}, k, false);
-      step(P1{}, k + 1, k + 2 == end);
-    }
-    if (k < end) {
-      step(P0{}, k, true);
-      ++k;
+    for (; k < end; ++k) {
+      const bool lst = k + 1 == end;
+      if (k & 1) {
+        if (lst) step(P1{}, End{}, k); else step(P1{}, Mid{}, k);
+      } else {
+        if (lst) step(P0{}, End{}, k); else step(P0{}, Mid{}, k);
+      }
     }
   }
 
-  // Final exact step (iters >= 1): X_K = X_{K-1} (2I - W X_{K-1}), X_K by columns in accC.
-  const int fin = (iters >= 1) ? ((iters - 1) & 1) : 0;  // buffers holding X_{K-1}
+  // Final exact step (iters >= 1): X_K = X_{K-1} (2I - W X_{K-1}), with X_{K-1} in sX[fin]. The U buffer of that
+  // parity was neither written nor read by the last pair step.
+  const int fin = (iters >= 1) ? ((iters - 1) & 1) : 0;
   float out_unscale = 1.f;
   if (iters >= 1) {
     const float unscale = ldexpf(1.f, e_cur);
-    if (tw) {
-      Frags<TQ, KC> fxc;
-      frags_of(sT[xcol_buf], c0, fxc);
-      mma(fw, fxc, accA);
-      put_u(sU[fin], accA, unscale);
+    if (doT) {
+      mma_w(sX[fin], accT);
+      put_tu(nullptr, sU[fin], accT, unscale);
     }
     __syncthreads();
-    if (xw) {
-      Frags<TQ, KC> fx, fu;
-      frags_of(sX[fin], r0, fx);
-      frags_of(sU[fin], c0, fu);
-      mma(fx, fu, accC);
+    if (doX) {
+      Frags<CS, KC> fu;
+      Frags<1, KC> fx;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        load_chunk_b<CS, KC>(sU[fin], c0, ln, c, fu);
+        load_chunk_a<1, KC>(sX[fin], rs, ln, c, fx);
+      }
+      zero_acc<1, CS>(accX);
+#pragma unroll
+      for (int c = 0; c < KC; ++c) mma_chunk<1, CS, KC>(fx, fu, accX, c);
     }
     out_unscale = unscale;
-  } else {
-#pragma unroll
-    for (int a = 0; a < TQ; ++a)
-#pragma unroll
-      for (int b = 0; b < TQ; ++b) accC[a][b] = x0c[a][b];
-  }
-  if (xw) {
-    if (xs && iters >= 1) put_xs(iters, accC, out_unscale, false);
+  }  // with no step accX still holds X_0
+  if (doX) {
+    if (xs && iters >= 1) put_xs(iters, accX, out_unscale);
     float* xo = Xout + g * mm;
 #pragma unroll
-    for (int a = 0; a < TQ; ++a)
+    for (int b = 0; b < CS; ++b)
 #pragma unroll
-      for (int b = 0; b < TQ; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (inside[a][b][r]) xo[(col_i0(a) + r) * m + col_j(b)] = accC[a][b][r] * out_unscale;
+      for (int r = 0; r < 4; ++r)
+        if (inside(b, r)) xo[(row_i0() + r) * m + col_j(b)] = accX[0][b][r] * out_unscale;
   }
 
   if (resid) {
-    // ||W X_K - I||_F with the same split products: X_K by columns goes through LDS once more.
+    // ||W X_K - I||_F with the same split products: X_K goes through LDS once more.
     __syncthreads();  // every read of the buffers below is done
     const int rb = fin ^ 1;
-    // accC * out_unscale is X_K; store it with the exponent of the last iterate so the fp16 halves stay in range
+    // accX * out_unscale is X_K; store it with the exponent of the last iterate so the fp16 halves stay in range
     const float st_scale = (iters >= 1) ? 1.f : ldexpf(1.f, -e_cur);
     const float ru = out_unscale / st_scale;
-    if (xw) put_cols(sT[rb], accC, st_scale);
+    if (doX) put_cols(sX[rb], accX, st_scale);
     __syncthreads();
     double ss = 0.0;
-    if (tw) {
-      Frags<TQ, KC> fxc;
-      frags_of(sT[rb], c0, fxc);
-      mma(fw, fxc, accA);
+    if (doT) {
+      mma_w(sX[rb], accT);
 #pragma unroll
-      for (int a = 0; a < TQ; ++a)
+      for (int b = 0; b < CS; ++b)
 #pragma unroll
-        for (int b = 0; b < TQ; ++b)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (inside[a][b][r]) {
-              const double e2 = static_cast<double>(accA[a][b][r] * ru) -
-                                (col_i0(a) + r == col_j(b) ? 1.0 : 0.0);
-              ss += e2 * e2;
-            }
+        for (int r = 0; r < 4; ++r)
+          if (inside(b, r)) {
+            const double e2 = static_cast<double>(accT[0][b][r] * ru) - (row_i0() + r == col_j(b) ? 1.0 : 0.0);
+            ss += e2 * e2;
+          }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if (ln == 0) red_res[wv] = ss;
     __syncthreads();
-    if (ln == 0 && wv >= 4) red[0][0][qd] = ss;
-    __syncthreads();
-    if (tid == 0) resid[g] = static_cast<float>(sqrt(red[0][0][0] + red[0][0][1] + red[0][0][2] + red[0][0][3]));
+    if (tid == 0) {
+      double tot = 0.0;
+      for (int q = 0; q < 8; ++q) tot += red_res[q];
+      resid[g] = static_cast<float>(sqrt(tot));
+    }
   }
 }
 
@@ -575,10 +548,12 @@ __global__ __launch_bounds__(512) void k_ns_small(const float* __restrict__ We, 
 // inside the solver's time.
 // =====================================================================================================
 
-// One S tile by one 512-thread block. Wave w sums a contiguous range of 16-token groups on fp32 MFMA
-// (A = C_K, landmark-major, B = V): in group q, lane (i, k) feeds landmark i and channel i of the tile with tokens
-// 16q + 4k + u at k-step u, loaded from global memory straight into the MFMA operand layout. The eight wave tiles
-// are then summed in LDS in wave order, so the result does not depend on timing.
+// One S tile by one block of kSideWaves waves (the solver's block size). Wave w sums a contiguous range of 16-token
+// groups on fp32 MFMA (A = C_K, landmark-major, B = V): in group q, lane (i, k) feeds landmark i and channel i of
+// the tile with tokens 16q + 4k + u at k-step u, loaded from global memory straight into the MFMA operand layout.
+// The wave tiles are then summed in LDS in wave order, so the result does not depend on timing.
+constexpr int kSideWaves = 8;
+
 template <typename T, int D>
 __device__ __forceinline__ void ckv_tile_block(int blk, const float* __restrict__ C, const T* __restrict__ V,
                                                float* __restrict__ S, int N, int m, float* sRed) {
@@ -592,7 +567,7 @@ __device__ __forceinline__ void ckv_tile_block(int blk, const float* __restrict_
   const bool lok = lt * 16 + i < m;
   const float* __restrict__ crow = C + (static_cast<size_t>(g) * m + (lok ? lt * 16 + i : 0)) * N;
   const T* __restrict__ vcol = V + static_cast<size_t>(g) * N * D + ct * 16 + i;
-  const int groups = (N + 15) / 16, gpw = (groups + 7) / 8;
+  const int groups = (N + 15) / 16, gpw = (groups + kSideWaves - 1) / kSideWaves;
   const int q0 = min(groups, wv * gpw), q1 = min(groups, q0 + gpw);
   const int qf = max(q0, min(q1, N / 16));  // groups [q0, qf) have all 16 tokens in range
   const float amask = lok ? 1.f : 0.f;
@@ -637,11 +612,11 @@ __device__ __forceinline__ void ckv_tile_block(int blk, const float* __restrict_
   for (int r = 0; r < 4; ++r) sRed[wv * 256 + (4 * k + r) * 16 + i] = acc[r];
   __syncthreads();
   const int tid = static_cast<int>(threadIdx.x);
-  if (tid < 256) {
+  if (tid < 256) {  // one thread per entry of the 16 x 16 tile
     const int row = tid >> 4, col = tid & 15;
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) sum += sRed[w * 256 + tid];
+    for (int w = 0; w < kSideWaves; ++w) sum += sRed[w * 256 + tid];
     if (lt * 16 + row < m) S[(static_cast<size_t>(g) * m + lt * 16 + row) * D + ct * 16 + col] = sum;
   }
 }
@@ -667,7 +642,7 @@ __global__ __launch_bounds__(512) void k_ns_side(const float* __restrict__ We, f
     const int total = static_cast<int>(gridDim.x) - s0, full = (total / 8) * 8;
     if (j < full) j = (j % 8) * (full / 8) + j / 8;
   }
-  __shared__ float sRed[8 * 256];
+  __shared__ float sRed[kSideWaves * 256];
   ckv_tile_block<T, D>(j, CK, V, S, N, m, sRed);
 }
 
