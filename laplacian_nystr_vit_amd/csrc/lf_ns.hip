@@ -167,9 +167,8 @@ __device__ __forceinline__ int exp_of(float v) {
 __device__ __forceinline__ int store_exp(float mx) { return mx > 0.f ? exp_of(mx) - 12 : 0; }
 constexpr int kRestoreExp = 15;  // an entry at or above 2^15 * 2^e triggers a re-store with a fresh exponent
 // Longest run of coupled T/X steps before T is formed again as W X: 2^kPairRun times the relative rounding of
-// one product must stay well below 1 (split-fp16 products: 2^-22; the fp32 products of the m > 64 path: 2^-24).
+// one split-fp16 product (2^-22) must stay well below 1.
 constexpr int kPairRun = 11;
-constexpr int kPairRunF32 = 12;
 
 // Maximum over the wave of a non-negative value, returned wave-uniform: DPP steps inside each row of 16 lanes
 // (quad swaps, then rotations by 4 and 8), then the four row results through scalar registers.
@@ -690,16 +689,22 @@ hipError_t launch_ns_side(const Shape& s, const float* We, float* X, float* xs, 
 
 // =====================================================================================================
 // m > 64: the m x m matrices do not fit one CU's LDS, so every product is a batched launch over 32 x 32 output
-// tiles (4 waves of 16 x 16, fp32 MFMA), K staged through LDS in chunks of 32 with the next chunk's float4 loads
-// in flight during the current chunk's MFMAs. The steps follow the small kernel: segments of at most kPairRunF32
-// steps start from T_k = W X_k, then one launch per step computes both T_{k+1} = T_k U_k and X_{k+1} = X_k U_k
-// with U_k = 2I - T_k formed while staging, and the last step is the exact one, X_K = X_{K-1} (2I - W X_{K-1}),
-// in two launches.
+// tiles of 256-thread blocks (4 waves of 16 x 16), each staging its 32-row A strip and 32-column B strip whole
+// in LDS (one round of global-load latency per launch) and running split-fp16 MFMAs as the small kernel does.
+// The iterates live in global memory in the layout the MFMA result has: split fp16 (hi, lo), by columns,
+// zero-padded to mp = 32 ceil(m / 32) in both dimensions, so that staging is unguarded 16-byte copies, the B
+// strip is plain LDS reads and the A strip is read with the transposing LDS read. X, whose entries start near
+// alpha and end near those of W^-1, carries one power-of-two exponent per 32 x 32 tile, chosen from the tile's
+// own largest entry when it is written; a product folds the exponents of its A and B tiles in per 32-wide K
+// chunk. W is read as fp32 and split while it is staged.
+// The steps follow the small kernel: segments of at most kPairRun steps start from T_k = W X_k, then one launch
+// per step computes T_{k+1} = T_k U_k and X_{k+1} = X_k U_k (U_k = 2I - T_k stored beside T_k), and the last
+// step is the exact one, X_K = X_{K-1} (2I - W X_{K-1}), in two launches. The first product launch also forms
+// alpha, X_0 = alpha W^T and T_0 = W X_0 = alpha W W^T.
 // =====================================================================================================
-// alpha and X_0 = alpha W^T for m > 64, over (slice, kNsRows-row chunk) blocks. Pass 1 writes per-chunk partial
-// column sums and the largest row sum of the chunk; pass 2 combines them in a fixed order (deterministic) and
-// writes the chunk's rows of X_0. part: G * nchunk * m doubles, rmx: G * nchunk doubles.
-constexpr int kNsRows = 8;  // rows per chunk of the alpha sums and of X_0: m / 8 chunks spread a slice over blocks
+// Partial sums for alpha over (slice, kNsRows-row chunk) blocks: per-chunk column sums and the largest row sum of
+// the chunk, combined later in a fixed order (deterministic). part: G * nchunk * m doubles, rmx: G * nchunk.
+constexpr int kNsRows = 8;  // rows per chunk: m / 8 chunks spread a slice over blocks
 
 __global__ __launch_bounds__(256) void k_ns_sums(const float* __restrict__ We, double* __restrict__ part,
                                                  double* __restrict__ rmx, int m) {
@@ -727,160 +732,346 @@ __global__ __launch_bounds__(256) void k_ns_sums(const float* __restrict__ We, d
   if (tid == 0) rmx[static_cast<size_t>(g) * nch + ch] = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
 }
 
-__global__ __launch_bounds__(256) void k_ns_x0(const float* __restrict__ We, const double* __restrict__ part,
-                                               const double* __restrict__ rmx, float* __restrict__ X0,
-                                               float* __restrict__ X0b, size_t strideX0b,
-                                               float* __restrict__ alpha_out, int m) {
-  __shared__ double red[256];
-  __shared__ float s_alpha;
-  const int g = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
+constexpr int LF_NS_KMAX = 256;            // largest m of the batched path (the library's m limit)
+constexpr int kTile = 32;                  // output tile side and K chunk
+constexpr int kLdA = kTile + 8;            // A strip in LDS by columns: 32 rows + 8 (80-byte columns)
+constexpr int kLdK = LF_NS_KMAX + 8;       // K-contiguous rows of the B strip and of W: 256 + 8 (528 bytes)
+
+// One m x m matrix per slice in split fp16 by columns, [G][mp][mp] halves in each of hi and lo.
+struct SplitG {
+  _Float16* hi;
+  _Float16* lo;
+};
+
+// What a launch writes from a product P (times `scale`) of its tiles; every pointer may be null.
+struct NsOut {
+  SplitG t;          // P
+  SplitG u;          // 2I - P
+  SplitG x;          // P 2^-e with e per tile, the tile's e in x_exp[g][ti][tj]
+  int* x_exp;
+  float* f32;        // P as fp32 [m][m] per slice, slice stride f32_stride (minus I when minus_eye)
+  size_t f32_stride;
+  float* f32b;       // a second fp32 copy (a saved iterate)
+  size_t f32b_stride;
+  int minus_eye;
+};
+
+// A product job: P = A B for one slice. A is W (fp32, split while staged) or a split matrix read by transposing
+// reads; B is W^T (W's rows as its columns) or a split matrix; a_exp / b_exp hold per-tile exponents (null: 0).
+struct NsJob {
+  SplitG a;
+  const int* a_exp;
+  SplitG b;
+  const int* b_exp;
+  NsOut out;
+};
+
+// The first product launch's extra work: alpha from the k_ns_sums partials and X_0 = alpha W^T, tile by tile.
+struct NsInit {
+  const double* part;  // null: not the first launch
+  const double* rmx;
+  int nch;
+  float* alpha_out;    // [G] or null
+  SplitG x0;
+  int* x0_exp;
+  float* f32;          // X_0 as fp32 (when it is the result, no steps), or null
+  float* f32b;         // the saved iterate X_0, or null
+  size_t f32b_stride;
+};
+
+__device__ __forceinline__ float block4_max_nonneg(float v, float* s_red) {
+  v = wave_max_nonneg(v);
+  __syncthreads();  // the previous use of s_red is over
+  if (lane_id() == 0) s_red[wave_id()] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+}
+
+// W's rows r0 .. r0+31, all 32 NT columns (zero beyond m), split into LDS as [row][k] halves (hi at dh, lo at dl).
+// The 4 NT values of a thread are all loaded (clamped addresses, zeroed outside W) before the first store.
+template <int NT>
+__device__ __forceinline__ void stage_w_rows(const float* __restrict__ wg, int r0, _Float16* dh, _Float16* dl, int m) {
+  constexpr int mp = NT * kTile, NV = kTile * mp / 256;
   const int tid = threadIdx.x;
-  double cmax = 0.0;
-  constexpr int kMaxCh = 256 / kNsRows;  // chunks of the largest m
-  for (int j = tid; j < m; j += 256) {
-    double pv[kMaxCh];  // every chunk's partial in flight, then summed in chunk order
+  if ((m & 3) == 0) {  // rows start 16-byte aligned: four values per load, 8-byte split stores
+    constexpr int NQ = NV / 4, mq = mp / 4;
+    float4 v4[NQ];
 #pragma unroll
-    for (int c = 0; c < kMaxCh; ++c) pv[c] = c < nch ? part[(static_cast<size_t>(g) * nch + c) * m + j] : 0.0;
+    for (int q = 0; q < NQ; ++q) {
+      const int idx = tid + 256 * q, rr = idx / mq, k = 4 * (idx % mq), r = r0 + rr;
+      const bool ok = r < m && k < m;
+      const float4 x = *reinterpret_cast<const float4*>(wg + (ok ? static_cast<size_t>(r) * m + k : 0));
+      v4[q] = ok ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int idx = tid + 256 * q, rr = idx / mq, k = 4 * (idx % mq);
+      half4 h, l;
+      split4(f32x4{v4[q].x, v4[q].y, v4[q].z, v4[q].w}, h, l);
+      *reinterpret_cast<half4*>(&dh[rr * kLdK + k]) = h;
+      *reinterpret_cast<half4*>(&dl[rr * kLdK + k]) = l;
+    }
+    return;
+  }
+  float v[NV];
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const int idx = tid + 256 * q, rr = idx / mp, k = idx % mp, r = r0 + rr;
+    const bool ok = r < m && k < m;
+    const float x = wg[ok ? static_cast<size_t>(r) * m + k : 0];
+    v[q] = ok ? x : 0.f;
+  }
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const int idx = tid + 256 * q, rr = idx / mp, k = idx % mp;
+    _Float16 h, l;
+    split_f16(v[q], h, l);
+    dh[rr * kLdK + k] = h;
+    dl[rr * kLdK + k] = l;
+  }
+}
+
+constexpr int kA = (LF_NS_KMAX * kLdA > kTile * kLdK) ? LF_NS_KMAX * kLdA : kTile * kLdK;  // A strip halves
+
+struct NsTileLds {
+  alignas(16) _Float16 a[2 * kA];  // hi then lo
+  alignas(16) _Float16 b[2 * kTile * kLdK];
+  float red[4];
+  double cmax[4], rmax[4];
+  float alpha;
+};
+
+// One block's work on tile (ti, tj) of slice g for job J; NT = mp / 32 tiles per side.
+template <bool AW, bool BW, int NT>
+__device__ __forceinline__ void ns_tile_body(const NsJob& J, const NsInit& init, const float* __restrict__ We, int m,
+                                             int g, NsTileLds& L) {
+  constexpr int mp = NT * kTile, nt = NT;
+  _Float16* sA = L.a;
+  _Float16* sB = L.b;
+  float* s_red = L.red;
+  double* s_cmax = L.cmax;
+  double* s_rmax = L.rmax;
+  const int tj = blockIdx.x, ti = blockIdx.y;
+  const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
+  const size_t mpp = static_cast<size_t>(mp) * mp, mm = static_cast<size_t>(m) * m;
+  const float* wg = We + g * mm;
+
+  // 1. Stage both strips: every global load is issued before the first LDS store.
+  // Each strip is 8 mp 16-byte pieces, NT per thread; a thread's loads are all issued before its first store.
+  if constexpr (AW) {
+    stage_w_rows<NT>(wg, ti * kTile, sA, sA + kA, m);
+  } else {
+    uint4 buf[NT];  // A strip: rows ti*32 .. +31 of every column k, 64 bytes per (column, half)
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      const int idx = tid + 256 * q, half = idx / (4 * mp), rem = idx % (4 * mp);
+      const int k = rem >> 2, p8 = (rem & 3) * 8;
+      const _Float16* src = (half ? J.a.lo : J.a.hi) + g * mpp + static_cast<size_t>(k) * mp + ti * kTile + p8;
+      buf[q] = *reinterpret_cast<const uint4*>(src);
+    }
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      const int idx = tid + 256 * q, half = idx / (4 * mp), rem = idx % (4 * mp);
+      const int k = rem >> 2, p8 = (rem & 3) * 8;
+      *reinterpret_cast<uint4*>(&sA[half * kA + k * kLdA + p8]) = buf[q];
+    }
+  }
+  if constexpr (BW) {
+    stage_w_rows<NT>(wg, tj * kTile, sB, sB + kTile * kLdK, m);
+  } else {
+    constexpr int pc = mp / 8;  // 16-byte pieces per column
+    uint4 buf[NT];              // B strip: columns tj*32 .. +31, all mp rows
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      const int idx = tid + 256 * q, half = idx / (kTile * pc), rem = idx % (kTile * pc);
+      const int jj = rem / pc, p8 = (rem % pc) * 8;
+      const _Float16* src = (half ? J.b.lo : J.b.hi) + g * mpp + static_cast<size_t>(tj * kTile + jj) * mp + p8;
+      buf[q] = *reinterpret_cast<const uint4*>(src);
+    }
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      const int idx = tid + 256 * q, half = idx / (kTile * pc), rem = idx % (kTile * pc);
+      const int jj = rem / pc, p8 = (rem % pc) * 8;
+      *reinterpret_cast<uint4*>(&sB[half * kTile * kLdK + jj * kLdK + p8]) = buf[q];
+    }
+  }
+  // alpha = 1 / (max column sum * max row sum) of |W| from the chunk partials, in a fixed order.
+  float scale = 1.f;
+  if (init.part) {
+    // thread j sums column j's chunk partials (m <= 256 columns, at most 32 chunks), every load in flight first
+    constexpr int kMaxCh = LF_NS_KMAX / kNsRows;
+    double pv[kMaxCh];
+    const int j = tid < m ? tid : 0;
+#pragma unroll
+    for (int c = 0; c < kMaxCh; ++c)
+      pv[c] = init.part[(static_cast<size_t>(g) * init.nch + (c < init.nch ? c : 0)) * m + j];
     double cs = 0.0;
 #pragma unroll
     for (int c = 0; c < kMaxCh; ++c)
-      if (c < nch) cs += pv[c];
-    cmax = fmax(cmax, cs);
-  }
-  red[tid] = cmax;
-  __syncthreads();
-  for (int s2 = 128; s2 > 0; s2 >>= 1) {
-    if (tid < s2) red[tid] = fmax(red[tid], red[tid + s2]);
+      if (c < init.nch) cs += pv[c];
+    double cmax = tid < m ? cs : 0.0;
+    // chunk c's largest row sum comes from thread c (at most 32 chunks)
+    double rmax = tid < init.nch ? init.rmx[static_cast<size_t>(g) * init.nch + tid] : 0.0;
+    for (int off = 32; off > 0; off >>= 1) {
+      cmax = fmax(cmax, __shfl_xor(cmax, off));
+      rmax = fmax(rmax, __shfl_xor(rmax, off));
+    }
+    if (ln == 0) {
+      s_cmax[wv] = cmax;
+      s_rmax[wv] = rmax;
+    }
     __syncthreads();
-  }
-  if (tid == 0) {
-    double rmax = 0.0;
-#pragma unroll
-    for (int c = 0; c < kMaxCh; ++c)
-      if (c < nch) rmax = fmax(rmax, rmx[static_cast<size_t>(g) * nch + c]);
-    s_alpha = static_cast<float>(1.0 / (red[0] * rmax));
-    if (ch == 0 && alpha_out) alpha_out[g] = s_alpha;
+    if (tid == 0) {
+      const double cm = fmax(fmax(s_cmax[0], s_cmax[1]), fmax(s_cmax[2], s_cmax[3]));
+      const double rm = fmax(fmax(s_rmax[0], s_rmax[1]), fmax(s_rmax[2], s_rmax[3]));
+      L.alpha = static_cast<float>(1.0 / (cm * rm));
+      if (ti == 0 && tj == 0 && init.alpha_out) init.alpha_out[g] = L.alpha;
+    }
   }
   __syncthreads();
-  const float alpha = s_alpha;
-  const size_t mm = static_cast<size_t>(m) * m;
-  const float* wg = We + g * mm;
-  float* x0 = X0 + g * mm;
-  float* x0b = X0b ? X0b + g * strideX0b : nullptr;
-  const int r0 = ch * kNsRows, r1 = min(m, r0 + kNsRows);
-  // X_0[i][j] = alpha W[j][i]: thread j reads the consecutive entries W[j][r0 .. r1) of its row and writes
-  // column j of rows r0 .. r1 (each store instruction covers 256 consecutive floats of one row).
-  for (int j = tid; j < m; j += 256) {
-#pragma unroll 8
-    for (int i = r0; i < r1; ++i) {
-      const float v = alpha * wg[static_cast<size_t>(j) * m + i];
-      x0[static_cast<size_t>(i) * m + j] = v;
-      if (x0b) x0b[static_cast<size_t>(i) * m + j] = v;
+  if (init.part) scale = L.alpha;
+
+  // 2. The wave's 16 x 16 sub-tile (wi, wj), chunk by chunk: three split-fp16 MFMAs per chunk into a fresh
+  //    accumulator, folded into the sum with the chunk's power of two (the exponents of A's row of tiles and B's
+  //    column of tiles, read before the first chunk).
+  const int wi = wv & 1, wj = wv >> 1;
+  int ech[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    const int ea = J.a_exp ? J.a_exp[(static_cast<size_t>(g) * nt + ti) * nt + c] : 0;
+    const int eb = J.b_exp ? J.b_exp[(static_cast<size_t>(g) * nt + c) * nt + tj] : 0;
+    ech[c] = ea + eb;
+  }
+  const int gq = ln >> 4, t = ln & 15;
+  half8 ah[NT], al[NT], bh[NT], bl[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    if constexpr (AW) {
+      const int o = (wi * 16 + t) * kLdK + c * kTile + 8 * gq;
+      ah[c] = *reinterpret_cast<const half8*>(&sA[o]);
+      al[c] = *reinterpret_cast<const half8*>(&sA[kA + o]);
+    } else {
+      const int k0 = c * kTile + 8 * gq + (t >> 2), i = wi * 16 + 4 * (t & 3);
+      const half4 h0 = __builtin_bit_cast(half4, lds_read_tr(&sA[k0 * kLdA + i]));
+      const half4 h1 = __builtin_bit_cast(half4, lds_read_tr(&sA[(k0 + 4) * kLdA + i]));
+      const half4 l0 = __builtin_bit_cast(half4, lds_read_tr(&sA[kA + k0 * kLdA + i]));
+      const half4 l1 = __builtin_bit_cast(half4, lds_read_tr(&sA[kA + (k0 + 4) * kLdA + i]));
+      ah[c] = half8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      al[c] = half8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+    }
+    const int o = (wj * 16 + t) * kLdK + c * kTile + 8 * gq;
+    bh[c] = *reinterpret_cast<const half8*>(&sB[o]);
+    bl[c] = *reinterpret_cast<const half8*>(&sB[kTile * kLdK + o]);
+  }
+  f32x4 p[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) p[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NT; ++c) p[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[c], bh[c], p[c], 0, 0, 0);
+#pragma unroll
+  for (int c = 0; c < NT; ++c) p[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[c], bl[c], p[c], 0, 0, 0);
+#pragma unroll
+  for (int c = 0; c < NT; ++c) p[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[c], bh[c], p[c], 0, 0, 0);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    const float f = ldexpf(1.f, ech[c]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = fmaf(p[c][r], f, acc[r]);
+  }
+
+  // 3. Outputs. The lane holds rows i0 .. i0+3 of column j.
+  const int i0 = ti * kTile + wi * 16 + 4 * gq, j = tj * kTile + wj * 16 + t;
+  f32x4 v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = acc[r] * scale;
+  const size_t so = g * mpp + static_cast<size_t>(j) * mp + i0;  // split-store offset of the lane's 4 rows
+  const NsOut& O = J.out;
+  if (O.t.hi) {
+    half4 h, l;
+    split4(v, h, l);
+    *reinterpret_cast<half4*>(&O.t.hi[so]) = h;
+    *reinterpret_cast<half4*>(&O.t.lo[so]) = l;
+  }
+  if (O.u.hi) {
+    f32x4 u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) u[r] = ((i0 + r == j && j < m) ? 2.f : 0.f) - v[r];
+    half4 h, l;
+    split4(u, h, l);
+    *reinterpret_cast<half4*>(&O.u.hi[so]) = h;
+    *reinterpret_cast<half4*>(&O.u.lo[so]) = l;
+  }
+  if (O.x.hi) {  // uniform over the block
+    const float mx = block4_max_nonneg(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
+                                       s_red);
+    const int e = store_exp(mx);
+    half4 h, l;
+    split_scaled4(v, ldexpf(1.f, -e), h, l);
+    *reinterpret_cast<half4*>(&O.x.hi[so]) = h;
+    *reinterpret_cast<half4*>(&O.x.lo[so]) = l;
+    if (tid == 0) O.x_exp[(static_cast<size_t>(g) * nt + ti) * nt + tj] = e;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = i0 + r;
+    if (i < m && j < m) {
+      const float o = v[r] - ((O.minus_eye && i == j) ? 1.f : 0.f);
+      if (O.f32) O.f32[g * O.f32_stride + static_cast<size_t>(i) * m + j] = o;
+      if (O.f32b) O.f32b[g * O.f32b_stride + static_cast<size_t>(i) * m + j] = o;
+    }
+  }
+  if (init.part) {
+    // X_0 = alpha W^T over this tile: X_0[i][j] = alpha W[j][i] (rows i0 .. i0+3 of column j, contiguous in W).
+    f32x4 x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = (i0 + r < m && j < m) ? scale * wg[static_cast<size_t>(j) * m + i0 + r] : 0.f;
+    const float mx = block4_max_nonneg(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))),
+                                       s_red);
+    const int e = store_exp(mx);
+    half4 h, l;
+    split_scaled4(x, ldexpf(1.f, -e), h, l);
+    *reinterpret_cast<half4*>(&init.x0.hi[so]) = h;
+    *reinterpret_cast<half4*>(&init.x0.lo[so]) = l;
+    if (tid == 0) init.x0_exp[(static_cast<size_t>(g) * nt + ti) * nt + tj] = e;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + r;
+      if (i < m && j < m) {
+        if (init.f32) init.f32[g * mm + static_cast<size_t>(i) * m + j] = x[r];
+        if (init.f32b) init.f32b[g * init.f32b_stride + static_cast<size_t>(i) * m + j] = x[r];
+      }
     }
   }
 }
 
-constexpr int LF_NS_KMAX = 256;  // largest m of the batched path (the library's m limit)
+// Block (tj, ti, z): tile (ti, tj) of slice z / njobs for job z % njobs (j0 or j1).
+template <bool AW, bool BW, int NT>
+__global__ __launch_bounds__(256) void k_ns_tile(NsJob j0, NsJob j1, int njobs, NsInit init,
+                                                 const float* __restrict__ We, int m) {
+  __shared__ NsTileLds lds;
+  const int g = blockIdx.z / njobs;
+  if (blockIdx.z % njobs == 0)
+    ns_tile_body<AW, BW, NT>(j0, init, We, m, g, lds);
+  else
+    ns_tile_body<AW, BW, NT>(j1, init, We, m, g, lds);
+}
 
-struct MMJob {
-  const float* A[2];
-  float* C[2];
-  float* C2;  // job 1 only
-  size_t strideC2;
-};
-
-template <int BOP, int EPI>
-__global__ __launch_bounds__(256) void k_ns_mm(MMJob job, const float* __restrict__ B, int m) {
-  // The whole K extent is staged at once: A strip [32 rows][m] and B strip [m][32 columns] (m <= 256), so a
-  // launch pays one round of global-load latency and then runs its MFMAs back to back.
-  constexpr int KMAX = LF_NS_KMAX;
-  constexpr int LDA = KMAX + 4;  // A rows: 4 mod 32
-  constexpr int LDB = 36;        // B rows (32 columns): 4 mod 32
-  constexpr int NCH = KMAX / 32;
-  __shared__ float sA[32 * LDA];
-  __shared__ float sB[KMAX * LDB];
-  const int g = blockIdx.z >> 1, which = blockIdx.z & 1;
-  if (job.A[which] == nullptr) return;  // this launch has no such job (uniform over the block)
-  const size_t mm = static_cast<size_t>(m) * m;
-  const float* ag = job.A[which] + g * mm;
-  const float* bg = B + g * mm;
-  float* cg = job.C[which] + g * mm;
-  const int tm = blockIdx.y * 32, tn = blockIdx.x * 32;
-  const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
-  const int wr = (wv >> 1) * 16, wc = (wv & 1) * 16;
-  // Staging map per 32 x 32 chunk: thread -> (row rr, columns cc .. cc + 3).
-  const int rr = tid >> 3, cc = 4 * (tid & 7);
-  const bool vec = (m & 3) == 0;
-  const int nch = (m + 31) / 32;
-  // Branch-free staging: every load address is clamped into the slice and out-of-range values are selected to
-  // zero, so all chunks' loads are issued before the first wait.
-  auto ld = [&](const float* base, int i, int k, bool ok) {
-    return ok ? base[static_cast<size_t>(i) * m + k] : 0.f;
-  };
-  float4 va[NCH], vb[NCH];
-  if (vec) {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int ai = tm + rr, ak = 32 * c + cc;  // A[ai][ak .. ak + 3]
-      const int bk = 32 * c + rr, bj = tn + cc;  // B[bk][bj .. bj + 3]
-      const bool aok = c < nch && ai < m && ak + 3 < m, bok = c < nch && bk < m && bj + 3 < m;
-      const float4 x = load4(ag + (aok ? static_cast<size_t>(ai) * m + ak : 0));
-      const float4 y = load4(bg + (bok ? static_cast<size_t>(bk) * m + bj : 0));
-      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-      va[c] = aok ? x : z;
-      vb[c] = bok ? y : z;
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int ai = tm + rr, ak = 32 * c + cc;
-      const int bk = 32 * c + rr, bj = tn + cc;
-      const bool arow = c < nch && ai < m, brow = c < nch && bk < m;
-      va[c] = make_float4(ld(ag, arow ? ai : 0, arow && ak + 0 < m ? ak + 0 : 0, arow && ak + 0 < m),
-                          ld(ag, arow ? ai : 0, arow && ak + 1 < m ? ak + 1 : 0, arow && ak + 1 < m),
-                          ld(ag, arow ? ai : 0, arow && ak + 2 < m ? ak + 2 : 0, arow && ak + 2 < m),
-                          ld(ag, arow ? ai : 0, arow && ak + 3 < m ? ak + 3 : 0, arow && ak + 3 < m));
-      vb[c] = make_float4(ld(bg, brow ? bk : 0, brow && bj + 0 < m ? bj + 0 : 0, brow && bj + 0 < m),
-                          ld(bg, brow ? bk : 0, brow && bj + 1 < m ? bj + 1 : 0, brow && bj + 1 < m),
-                          ld(bg, brow ? bk : 0, brow && bj + 2 < m ? bj + 2 : 0, brow && bj + 2 < m),
-                          ld(bg, brow ? bk : 0, brow && bj + 3 < m ? bj + 3 : 0, brow && bj + 3 < m));
-    }
+// k_ns_tile for the tile count of m: 3 .. 8 (65 <= m <= 256).
+template <bool AW, bool BW>
+static void ns_tile_launch(int nt, dim3 grid, hipStream_t st, const NsJob& j0, const NsJob& j1, int njobs,
+                           const NsInit& init, const float* We, int m) {
+#define LF_NS_TILE(NT_)                                                                                        \
+  hipLaunchKernelGGL((k_ns_tile<AW, BW, NT_>), grid, dim3(256), 0, st, j0, j1, njobs, init, We, m)
+  switch (nt) {
+    case 3: LF_NS_TILE(3); break;
+    case 4: LF_NS_TILE(4); break;
+    case 5: LF_NS_TILE(5); break;
+    case 6: LF_NS_TILE(6); break;
+    case 7: LF_NS_TILE(7); break;
+    default: LF_NS_TILE(8); break;
   }
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    if (BOP == 1) {  // 2I - B, zero outside the m x m block
-      const int bk = 32 * c + rr, bj = tn + cc;
-      vb[c].x = (bk < m && bj + 0 < m) ? ((bk == bj + 0) ? 2.f : 0.f) - vb[c].x : 0.f;
-      vb[c].y = (bk < m && bj + 1 < m) ? ((bk == bj + 1) ? 2.f : 0.f) - vb[c].y : 0.f;
-      vb[c].z = (bk < m && bj + 2 < m) ? ((bk == bj + 2) ? 2.f : 0.f) - vb[c].z : 0.f;
-      vb[c].w = (bk < m && bj + 3 < m) ? ((bk == bj + 3) ? 2.f : 0.f) - vb[c].w : 0.f;
-    }
-    if (c < nch) {
-      *reinterpret_cast<float4*>(&sA[rr * LDA + 32 * c + cc]) = va[c];
-      *reinterpret_cast<float4*>(&sB[(32 * c + rr) * LDB + cc]) = vb[c];
-    }
-  }
-  __syncthreads();
-  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;  // two chains over alternate k-steps
-  const int ksteps = nch * 8;
-#pragma unroll 4
-  for (int ks = 0; ks < ksteps; ks += 2) {
-    const int k = ks * 4 + (ln >> 4);
-    acc0 = mfma16x16x4(sA[(wr + (ln & 15)) * LDA + k], sB[k * LDB + wc + (ln & 15)], acc0);
-    acc1 = mfma16x16x4(sA[(wr + (ln & 15)) * LDA + k + 4], sB[(k + 4) * LDB + wc + (ln & 15)], acc1);
-  }
-  const int j = tn + wc + (ln & 15);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = tm + wr + 4 * (ln >> 4) + r;
-    if (i < m && j < m) {
-      float v = acc0[r] + acc1[r];
-      if (EPI == 1) v = (i == j ? 2.f : 0.f) - v;
-      if (EPI == 2) v -= (i == j ? 1.f : 0.f);
-      cg[static_cast<size_t>(i) * m + j] = v;
-      if (which == 1 && job.C2) job.C2[g * job.strideC2 + static_cast<size_t>(i) * m + j] = v;
-    }
-  }
+#undef LF_NS_TILE
 }
 
 __global__ __launch_bounds__(256) void k_frob(const float* __restrict__ E, float* __restrict__ out, int m) {
@@ -901,8 +1092,14 @@ __global__ __launch_bounds__(256) void k_frob(const float* __restrict__ E, float
   if (threadIdx.x == 0) out[blockIdx.x] = static_cast<float>(sqrt(red[0]));
 }
 
+// Scratch of the batched path, in floats: six split matrices (T, U and X by parity), the per-tile exponents of
+// the two X buffers and the alpha partials.
+static inline int ns_mp(int m) { return (m + kTile - 1) / kTile * kTile; }
+
 size_t ns_tmp_floats(const Shape& s) {
-  return s.m > 64 ? 3 * static_cast<size_t>(s.G) * s.m * s.m : 0;
+  if (s.m <= 64) return 0;
+  const size_t G = s.G, mp = ns_mp(s.m), nt = mp / kTile, nch = (s.m + kNsRows - 1) / kNsRows;
+  return 6 * G * mp * mp + 2 * G * nt * nt + 2 * G * nch * (s.m + 1) + 64;
 }
 
 hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float* alpha, float* resid, float* tmp,
@@ -919,55 +1116,103 @@ hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float
       hipLaunchKernelGGL((k_ns_small<4, 2>), grid, block, 0, st, We, X, xs, alpha, resid, m, K);
     return hipGetLastError();
   }
-  const size_t mm = static_cast<size_t>(m) * m, Gmm = static_cast<size_t>(s.G) * mm;
-  float* Tb[2] = {tmp, tmp + Gmm};  // T_k by parity; Tb[..] also serves as U' and the residual
-  float* Xalt = tmp + 2 * Gmm;
-  // X_k alternates between two buffers so that X_K lands in X.
-  float* Xb[2] = {X, Xalt};
+  const int G = s.G, mp = ns_mp(m), nt = mp / kTile, nch = (m + kNsRows - 1) / kNsRows;
+  const size_t mm = static_cast<size_t>(m) * m, Gmpp = static_cast<size_t>(G) * mp * mp;
+  // carve: 6 split matrices (Gmpp floats each = 2 Gmpp halves), then the exponents, then the alpha partials
+  auto split_at = [&](int i) {
+    _Float16* h = reinterpret_cast<_Float16*>(tmp + static_cast<size_t>(i) * Gmpp);
+    return SplitG{h, h + Gmpp};
+  };
+  const SplitG Tb[2] = {split_at(0), split_at(1)}, Ub[2] = {split_at(2), split_at(3)},
+               Xb[2] = {split_at(4), split_at(5)};
+  int* ex = reinterpret_cast<int*>(tmp + 6 * Gmpp);
+  int* Xe[2] = {ex, ex + static_cast<size_t>(G) * nt * nt};
+  double* part = reinterpret_cast<double*>(tmp + 6 * Gmpp + 2 * static_cast<size_t>(G) * nt * nt + 2);
+  part = reinterpret_cast<double*>((reinterpret_cast<uintptr_t>(part) + 7) & ~static_cast<uintptr_t>(7));
+  double* rmx = part + static_cast<size_t>(G) * nch * m;
   const size_t xs_stride = static_cast<size_t>(K + 1) * mm;
-  const int tiles = (m + 31) / 32;
-  const dim3 blk(256);
   auto slot = [&](int k) { return xs ? xs + static_cast<size_t>(k) * mm : nullptr; };
-  // X_0 lands where the last exact step reads X_{K-1} from when K == 1, else where step 0 reads it.
-  int xc = (K % 2 == 0) ? 0 : 1;  // parity such that X_K ends in Xb[0] = X (K steps, one flip per step)
+  const dim3 blk(256);
+  const NsInit noinit{};
+  const NsJob none{};
+
+  hipLaunchKernelGGL(k_ns_sums, dim3(G, nch), blk, 0, st, We, part, rmx, m);
+  // T_0 = W X_0 = alpha W W^T, U_0, and X_0 = alpha W^T (the result itself when there is no step)
   {
-    const int nch = (m + kNsRows - 1) / kNsRows;
-    // G nch m + G nch doubles fit in one T buffer (m > 64); Tb[0] starts the 256-byte aligned scratch and is not
-    // written before T_0.
-    double* part = reinterpret_cast<double*>(Tb[0]);
-    double* rmx = part + static_cast<size_t>(s.G) * nch * m;
-    hipLaunchKernelGGL(k_ns_sums, dim3(s.G, nch), blk, 0, st, We, part, rmx, m);
-    hipLaunchKernelGGL(k_ns_x0, dim3(s.G, nch), blk, 0, st, We, part, rmx, Xb[xc], xs, xs_stride, alpha, m);
+    NsJob j{};
+    j.out.t = Tb[0];
+    j.out.u = Ub[0];
+    NsInit in{part, rmx, nch, alpha, Xb[0], Xe[0], K == 0 ? X : nullptr, slot(0), xs_stride};
+    ns_tile_launch<true, true>(nt, dim3(nt, nt, G), st, j, none, 1, in, We, m);
   }
-  int tc = 0;
+  int tc = 0, xc = 0;  // buffers holding T_k, U_k and X_k
   for (int k = 0; k + 1 < K;) {
-    // segment start: T_k = W X_k
-    MMJob j0{{We, nullptr}, {Tb[tc], nullptr}, nullptr, 0};
-    hipLaunchKernelGGL((k_ns_mm<0, 0>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, j0, Xb[xc], m);
-    const int end = std::min(k + kPairRunF32, K - 1);
+    if (k > 0) {
+      // segment start: T_k = W X_k, U_k
+      NsJob j{};
+      j.b = Xb[xc];
+      j.b_exp = Xe[xc];
+      j.out.t = Tb[tc];
+      j.out.u = Ub[tc];
+      ns_tile_launch<true, false>(nt, dim3(nt, nt, G), st, j, none, 1, noinit, We, m);
+    }
+    const int end = std::min(k + kPairRun, K - 1);
     for (; k < end; ++k) {
       const bool last = k + 1 == end;
-      // pair step: job 0: T_{k+1} = T_k (2I - T_k) (skipped at a segment's end), job 1: X_{k+1} = X_k (2I - T_k)
-      MMJob jp{{last ? nullptr : Tb[tc], Xb[xc]}, {last ? nullptr : Tb[tc ^ 1], Xb[xc ^ 1]}, slot(k + 1),
-               xs_stride};
-      hipLaunchKernelGGL((k_ns_mm<1, 0>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, jp, Tb[tc], m);
+      // X_{k+1} = X_k U_k and (unless the segment ends) T_{k+1} = T_k U_k, U_{k+1}
+      NsJob jx{};
+      jx.a = Xb[xc];
+      jx.a_exp = Xe[xc];
+      jx.b = Ub[tc];
+      jx.out.x = Xb[xc ^ 1];
+      jx.out.x_exp = Xe[xc ^ 1];
+      jx.out.f32b = slot(k + 1);
+      jx.out.f32b_stride = xs_stride;
+      NsJob jt{};
+      jt.a = Tb[tc];
+      jt.b = Ub[tc];
+      jt.out.t = Tb[tc ^ 1];
+      jt.out.u = Ub[tc ^ 1];
+      const int nj = last ? 1 : 2;
+      ns_tile_launch<false, false>(nt, dim3(nt, nt, nj * G), st, jx, jt, nj, noinit, We, m);
       tc ^= 1;
       xc ^= 1;
     }
   }
   if (K >= 1) {
-    // exact step: U' = 2I - W X_{K-1} (into a T buffer), then X_K = X_{K-1} U'
-    float* Up = Tb[tc ^ 1];
-    MMJob ju{{We, nullptr}, {Up, nullptr}, nullptr, 0};
-    hipLaunchKernelGGL((k_ns_mm<0, 1>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, ju, Xb[xc], m);
-    MMJob jx{{nullptr, Xb[xc]}, {nullptr, Xb[xc ^ 1]}, slot(K), xs_stride};
-    hipLaunchKernelGGL((k_ns_mm<0, 0>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, jx, Up, m);
+    // exact step: U' = 2I - W X_{K-1} (into the U buffer the last pair step neither read nor wrote), then
+    // X_K = X_{K-1} U'
+    NsJob ju{};
+    ju.b = Xb[xc];
+    ju.b_exp = Xe[xc];
+    ju.out.u = Ub[tc];
+    ns_tile_launch<true, false>(nt, dim3(nt, nt, G), st, ju, none, 1, noinit, We, m);
+    NsJob jx{};
+    jx.a = Xb[xc];
+    jx.a_exp = Xe[xc];
+    jx.b = Ub[tc];
+    jx.out.f32 = X;
+    jx.out.f32_stride = mm;
+    jx.out.f32b = slot(K);
+    jx.out.f32b_stride = xs_stride;
+    if (resid) {  // the residual needs X_K as a split B operand
+      jx.out.x = Xb[xc ^ 1];
+      jx.out.x_exp = Xe[xc ^ 1];
+    }
+    ns_tile_launch<false, false>(nt, dim3(nt, nt, G), st, jx, none, 1, noinit, We, m);
     xc ^= 1;
   }
   if (resid) {
-    MMJob jr{{We, nullptr}, {Tb[tc], nullptr}, nullptr, 0};
-    hipLaunchKernelGGL((k_ns_mm<0, 2>), dim3(tiles, tiles, 2 * s.G), blk, 0, st, jr, Xb[xc], m);
-    hipLaunchKernelGGL(k_frob, dim3(s.G), dim3(256), 0, st, Tb[tc], resid, m);
+    // E = W X_K - I in fp32 (into the T buffers, free now), then its Frobenius norm per slice
+    float* E = tmp;
+    NsJob jr{};
+    jr.b = Xb[xc];  // X_K (X_0 in buffer 0 when there is no step)
+    jr.b_exp = Xe[xc];
+    jr.out.f32 = E;
+    jr.out.f32_stride = mm;
+    jr.out.minus_eye = 1;
+    ns_tile_launch<true, false>(nt, dim3(nt, nt, G), st, jr, none, 1, noinit, We, m);
+    hipLaunchKernelGGL(k_frob, dim3(G), dim3(256), 0, st, E, resid, m);
   }
   return hipGetLastError();
 }
