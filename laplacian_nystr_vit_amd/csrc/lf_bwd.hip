@@ -29,14 +29,9 @@ namespace lf {
 
 static inline int cdiv(long a, long b) { return static_cast<int>((a + b - 1) / b); }
 
-constexpr int kDlLw = 8;  // landmarks per thread in the dL reduction
 constexpr int kFragUnits = 2048;
 constexpr int kDwcThreads = 256;  // DWC weight gradient: threads per block
 constexpr int kDwcRun = 8;        // DWC weight gradient: tokens per work item (a run along a grid row)  // 16-byte units of the backward Newton-Schulz chain's fragments per (slice, step)
-// Waves per block of the token-row gradient kernel: 8-channel slices, so a block of 64 rows holds d / 8 waves.
-template <int D>
-constexpr int kRowsWaves = D / 8;
-
 __device__ __forceinline__ float sgnf(float x) { return x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f); }
 
 // sign(x - l) from xs = x 2^100 (exact): fmaf(l, -2^100, xs) is (x - l) 2^100 rounded once, and its median with -1
@@ -48,11 +43,16 @@ __device__ __forceinline__ float sgn_of_scaled(float xs, float l) {
   return __builtin_amdgcn_fmed3f(fmaf(l, -kSgnScale, xs), -1.f, 1.f);
 }
 
+// Sign reductions (k_bwd_sign): row sub-tiles per block (the block has kSignSub * D threads) and token rows per
+// thread.
+constexpr int kSignSub = 8;
+constexpr int kSignRt = 8;
+
 namespace {
 
 struct BwdWs {
-  size_t T1, part, dX, dS, stats, dWe, dLW, Gq, Gk, dLpart, dL, lampart, dwcpart, nsA1, nsA2, nsG, nsD, nsGf, total;
-  int nsplitL, rpsL, nlb;
+  size_t T1, part, dX, dS, stats, dWe, dLW, Gq, Gk, dLpart, dQp, lampart, dwcpart, nsA1, nsA2, nsG, nsD, nsGf, total;
+  int nsplitS;
   int lamchunks, dwcseg, dwcblocks;
 };
 
@@ -64,15 +64,8 @@ BwdWs plan(const Shape& s) {
   int nsplit, rps;
   ckv_split(s, &nsplit, &rps);
   BwdWs w;
-  // dL partials: blocks of 256 / d landmark groups of kDlLw landmarks; the row range is split so that about 4096
-  // waves run (four per SIMD), each split a multiple of 4 rows.
-  w.nlb = cdiv(s.m, (256 / s.d) * kDlLw);
-  int want = cdiv(4096, static_cast<long>(s.G) * w.nlb * 4);
-  const int maxs = cdiv(s.N, 16);
-  if (want > maxs) want = maxs;
-  if (want < 1) want = 1;
-  w.rpsL = cdiv(cdiv(s.N, want), 4) * 4;
-  w.nsplitL = cdiv(s.N, w.rpsL);
+  // Sign reductions (k_bwd_sign): blocks of kSignSub * kSignRt token rows per slice.
+  w.nsplitS = cdiv(s.N, kSignSub * kSignRt);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -88,8 +81,8 @@ BwdWs plan(const Shape& s) {
   w.dLW = take(4 * G * m * d);
   w.Gq = take(4 * G * N * m);
   w.Gk = take(4 * G * N * m);
-  w.dLpart = take(4 * G * static_cast<size_t>(w.nsplitL) * m * d);
-  w.dL = take(4 * G * m * d);
+  w.dLpart = take(4 * G * static_cast<size_t>(w.nsplitS) * m * d);
+  w.dQp = take(4 * G * N * d);
   // lambda gradient: per slice, chunks of 64 landmarks' worth of kernel entries; DWC weight gradient: per slice,
   // one [9][d] partial per block of runs of kDwcRun tokens (dwcseg runs per grid row)
   w.lamchunks = cdiv(2L * m * N + m * m, 4096);
@@ -777,155 +770,236 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// dL partials: sum over a range of token rows of Gq sign(Q - L) + Gk sign(K - L). Thread = (channel, group of
-// kDlLw landmarks), accumulators and landmark values in VGPRs, so each token value read serves kDlLw landmarks.
-// With d = 64 a wave is one landmark group and its Gq/Gk weights are wave-uniform (scalar loads of 4 consecutive
-// rows per landmark, Gq/Gk being landmark-major); rows go 4 at a time with all their loads issued together.
+// The two sign reductions of the kernel gradient in one pass ([note] motivation "core idea": d/dx exp(-|x - l|_1 /
+// lambda) = -(1/lambda) sign(x - l) k, with G = dC C / lambda already formed): for a token row x of Q (side 0) or K
+// (side 1), landmark l and channel c, s = sign(x_c - L_lc) is evaluated once and feeds
+//   dX_c  -= G[l][x] s   (summed over the landmarks: dQ before its pooling term, dK), and
+//   dL_lc += G[l][x] s   (summed over the token rows of both sides).
+// Block = kSignSub x RT token rows of one slice; thread = (channel c, sub-tile of RT rows). A thread runs over all
+// MP landmarks (m itself, or m rounded up to 8 with zero weights) with its RT row values and dX sums in VGPRs, so
+// dX leaves complete and in one piece (dK final, dQ as an fp32 partial: its pooling term comes with dL), and dL
+// for every landmark accumulates in VGPRs across both sides. Per (row, landmark): s = med3(x 2^100 - l 2^100,
+// -1, 1), then one fma into dL and one into dX, all register operands: the block stages Gq and Gk for its rows
+// (landmark-major, as stored) and -2^100 L in LDS and reads each landmark's RT weights as 16-byte broadcasts. At
+// the end the sub-tiles' dL are added through LDS in sub-tile order, 8 landmarks at a time, and the block writes
+// one [m][D] partial, summed in fixed order by k_bwd_dq_final.
 // ---------------------------------------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_bwd_dl_partial(const T* __restrict__ Q, const T* __restrict__ K,
-                                                        const float* __restrict__ L, const float* __restrict__ Gq,
-                                                        const float* __restrict__ Gk, float* __restrict__ part, int N,
-                                                        int m, int nsplit, int rps, int nlb) {
-  constexpr int LPB = 256 / D;  // landmark groups per block
-  constexpr int LW = kDlLw;
-  constexpr int RG = 4;  // rows per step
-  int b = blockIdx.x;
+template <int RT>
+__device__ __forceinline__ void load_w(const float* p, float (&w)[RT]) {
+#pragma unroll
+  for (int q = 0; q < RT / 4; ++q) {
+    const float4 v = *reinterpret_cast<const float4*>(p + 4 * q);
+    w[4 * q] = v.x;
+    w[4 * q + 1] = v.y;
+    w[4 * q + 2] = v.z;
+    w[4 * q + 3] = v.w;
+  }
+}
+
+// RT consecutive rows of one channel (p points at the first, rows D apart); rows past `rlast` read row `rlast`
+// (the last row of the slice, finite; their weights are zero).
+template <typename T, int RT, int D>
+__device__ __forceinline__ void load_rows(const T* p, int rlast, float (&x)[RT]) {
+  if (rlast >= RT - 1) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) x[r] = to_f32(p[r * D]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) x[r] = to_f32(p[min(r, rlast) * D]);
+  }
+}
+
+template <typename T, int D, int MP>
+__global__ __launch_bounds__(kSignSub * 64) void k_bwd_sign(const T* __restrict__ Q, const T* __restrict__ K,
+                                                           const float* __restrict__ L, const float* __restrict__ Gq,
+                                                           const float* __restrict__ Gk, float* __restrict__ dQp,
+                                                           T* __restrict__ dK, float* __restrict__ dLpart, int N,
+                                                           int m, int nsplit) {
+  constexpr int RT = kSignRt, RB = kSignSub * RT, NTH = kSignSub * D;
+  constexpr int kGs = 2 * MP * RB, kRed = kSignSub * 8 * D, kLs = MP * D;
+  constexpr int kFirst = kGs > kRed ? kGs : kRed;
+  __shared__ __align__(16) float smem[kFirst + kLs];
+  float* Gs = smem;          // [2][MP][RB] weights, zero past m and past N; later [kSignSub][8][D] for dL
+  float* Ls = smem + kFirst;  // [MP][D] landmark values times -2^100
+  const int g = static_cast<int>(blockIdx.x) / nsplit, sp = static_cast<int>(blockIdx.x) % nsplit;
+  const int r0 = sp * RB;
+  const int tid = threadIdx.x, c = tid % D;
+  int sub = tid / D;
+  if constexpr (D == 64) sub = __builtin_amdgcn_readfirstlane(sub);  // one sub-tile per wave
+
+  // Staging: every load is issued before the first LDS store (a fixed count per thread; NTH is a multiple of RB,
+  // so a thread's row within the block is the same for all its weights). Rows past N and landmarks past m read
+  // in-bounds entries and store zero.
+  constexpr int KS = (kGs + NTH - 1) / NTH, KL = (kLs + NTH - 1) / NTH;
+  const int rb = sub * RT;
+  const int rlast = N - 1 - (r0 + rb);  // the sub-tile's rows past this one are past N
+  const size_t base = (static_cast<size_t>(g) * N + r0 + rb) * D + c;
+  float xn[RT];  // the next side's raw row values
+  load_rows<T, RT, D>(Q + base, rlast, xn);
   {
-    // Consecutive blocks on one XCD (the hardware deals blocks to the 8 XCDs round-robin): the landmark groups of
-    // one row range then read its Q and K rows through one L2.
-    const int full = (static_cast<int>(gridDim.x) / 8) * 8;
-    if (b < full) b = (b % 8) * (full / 8) + b / 8;
-  }
-  const int lb = b % nlb;
-  b /= nlb;
-  const int s = b % nsplit, g = b / nsplit;
-  const int c = threadIdx.x % D;
-  int grp = static_cast<int>(threadIdx.x) / D;
-  if constexpr (D == 64) grp = __builtin_amdgcn_readfirstlane(grp);  // one group per wave: let the compiler know
-  const int lbase = (lb * LPB + grp) * LW;
-  if (lbase >= m) return;
-  // landmarks past m repeat the last landmark's loads (branch-free) and are not stored
-  float lv[LW], acc[LW], wsel[LW];
-  const float* gq[LW];
-  const float* gk[LW];
+    constexpr int KB = 16;  // loads in flight per thread
+    const int rr = tid % RB, rowc = min(r0 + rr, N - 1);
+    const bool rowok = r0 + rr < N;
 #pragma unroll
-  for (int j = 0; j < LW; ++j) {
-    const int l = min(lbase + j, m - 1);
-    lv[j] = L[(static_cast<size_t>(g) * m + l) * D + c];
-    wsel[j] = lbase + j < m ? 1.f : 0.f;
-    gq[j] = Gq + (static_cast<size_t>(g) * m + l) * N;
-    gk[j] = Gk + (static_cast<size_t>(g) * m + l) * N;
-    acc[j] = 0.f;
-  }
-  const int r0 = s * rps, r1 = min(N, r0 + rps);
-  const T* qc = Q + static_cast<size_t>(g) * N * D + c;
-  const T* kc = K + static_cast<size_t>(g) * N * D + c;
-  int i = r0;
-  for (; i + RG <= r1; i += RG) {
-    float xq[RG], xk[RG], wq[LW][RG], wk[LW][RG];
+    for (int k0 = 0; k0 < KS; k0 += KB) {
+      float gv[KB];
 #pragma unroll
-    for (int u = 0; u < RG; ++u) {
-      xq[u] = to_f32(qc[static_cast<size_t>(i + u) * D]) * kSgnScale;
-      xk[u] = to_f32(kc[static_cast<size_t>(i + u) * D]) * kSgnScale;
-    }
-#pragma unroll
-    for (int j = 0; j < LW; ++j)
-#pragma unroll
-      for (int u = 0; u < RG; ++u) {
-        wq[j][u] = gq[j][i + u];
-        wk[j][u] = gk[j][i + u];
+      for (int k = 0; k < KB; ++k) {
+        if (k0 + k < KS) {
+          const int sl = min((tid + (k0 + k) * NTH) / RB, 2 * MP - 1), side = sl / MP;
+          const int lc = min(sl - side * MP, m - 1);
+          gv[k] = (side ? Gk : Gq)[(static_cast<size_t>(g) * m + lc) * N + rowc];
+        }
       }
 #pragma unroll
-    for (int j = 0; j < LW; ++j)
-#pragma unroll
-      for (int u = 0; u < RG; ++u) {
-        acc[j] = fmaf(wq[j][u], sgn_of_scaled(xq[u], lv[j]), acc[j]);
-        acc[j] = fmaf(wk[j][u], sgn_of_scaled(xk[u], lv[j]), acc[j]);
+      for (int k = 0; k < KB; ++k) {
+        const int e = tid + (k0 + k) * NTH, l = (e / RB) % MP;
+        if (k0 + k < KS && e < kGs) Gs[e] = rowok && l < m ? gv[k] : 0.f;
       }
-  }
-  for (; i < r1; ++i) {
-    const float xq = to_f32(qc[static_cast<size_t>(i) * D]) * kSgnScale;
-    const float xk = to_f32(kc[static_cast<size_t>(i) * D]) * kSgnScale;
+    }
 #pragma unroll
-    for (int j = 0; j < LW; ++j) {
-      acc[j] = fmaf(gq[j][i], sgn_of_scaled(xq, lv[j]), acc[j]);
-      acc[j] = fmaf(gk[j][i], sgn_of_scaled(xk, lv[j]), acc[j]);
+    for (int k0 = 0; k0 < KL; k0 += KB) {
+      float lvv[KB];
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        if (k0 + k < KL) {
+          const int lc = min((tid + (k0 + k) * NTH) / D, m - 1);
+          lvv[k] = L[(static_cast<size_t>(g) * m + lc) * D + c];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int e = tid + (k0 + k) * NTH;
+        if (k0 + k < KL && e < kLs) Ls[e] = e / D < m ? lvv[k] * -kSgnScale : 0.f;
+      }
     }
   }
+  __syncthreads();
+
+  float dl[MP];
 #pragma unroll
-  for (int j = 0; j < LW; ++j)
-    if (wsel[j] != 0.f) part[((static_cast<size_t>(g) * nsplit + s) * m + lbase + j) * D + c] = acc[j];
+  for (int l = 0; l < MP; ++l) dl[l] = 0.f;
+#pragma unroll 1
+  for (int side = 0; side < 2; ++side) {
+    float x[RT], xs[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      x[r] = xn[r] * kSgnScale;
+      asm volatile("" : "+v"(x[r]));  // keeps x 2^100 in a VGPR: no literal-operand fma per term
+      xs[r] = 0.f;
+    }
+    if (side == 0) load_rows<T, RT, D>(K + base, rlast, xn);  // in flight during side 0
+    // Landmark l + 1's weights and value are read while landmark l is processed. After each landmark its sums are
+    // pinned (an empty asm that takes and returns them) and a scheduling barrier follows, so the compiler neither
+    // hoists every landmark's reads up front nor defers the dL chains (either would hold MP x RT values in VGPRs).
+    const float* gw = Gs + side * MP * RB + rb;
+    float w[RT], wn[RT], lv, lvn;
+    load_w<RT>(gw, wn);
+    lvn = Ls[c];
+#pragma unroll
+    for (int l = 0; l < MP; ++l) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) w[r] = wn[r];
+      lv = lvn;
+      if (l + 1 < MP) {
+        load_w<RT>(gw + (l + 1) * RB, wn);
+        lvn = Ls[(l + 1) * D + c];
+      }
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const float sg = __builtin_amdgcn_fmed3f(x[r] + lv, -1.f, 1.f);
+        dl[l] = fmaf(w[r], sg, dl[l]);
+        xs[r] = fmaf(w[r], sg, xs[r]);  // dX = -xs: both sums are then plain multiply-adds
+      }
+      asm volatile("" : "+v"(dl[l]));
+#pragma unroll
+      for (int r = 0; r < RT; ++r) asm volatile("" : "+v"(xs[r]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (side == 0) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+        if (r <= rlast) dQp[base + r * D] = -xs[r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+        if (r <= rlast) dK[base + r * D] = from_f32<T>(-xs[r]);
+    }
+  }
+
+  __syncthreads();  // the weights are no longer read: their space takes the dL sums
+  float* red = smem;
+#pragma unroll
+  for (int k = 0; k < (MP + 7) / 8; ++k) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[(sub * 8 + j) * D + c] = 8 * k + j < MP ? dl[8 * k + j] : 0.f;
+    __syncthreads();
+    for (int j = sub; j < 8; j += kSignSub) {  // output (landmark 8k + j, channel c)
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < kSignSub; ++q) v += red[(q * 8 + j) * D + c];
+      if (8 * k + j < m) dLpart[((static_cast<size_t>(g) * nsplit + sp) * m + 8 * k + j) * D + c] = v;
+    }
+    __syncthreads();
+  }
 }
 
-__global__ __launch_bounds__(256) void k_bwd_dl_finalize(const float* __restrict__ part, const float* __restrict__ dLW,
-                                                         float* __restrict__ dL, int G, int nsplit, int md) {
-  const size_t t = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (t >= static_cast<size_t>(G) * md) return;
-  const size_t g = t / md, e = t % md;
-  float acc = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < nsplit; ++s) acc += part[(g * nsplit + s) * md + e];
-  dL[t] = acc + dLW[t];
-}
+// dL = sum of the sign blocks' partials (in block order) + the landmark-kernel term dLW, then the pooling term of
+// dQ: every token i of landmark l's r x r block gets dQ_i = dQp_i + dL_l / r^2. Block = (landmark, slice); each
+// thread takes up to kDqPer of the block's r^2 D token entries, whose dQp loads are issued before the dL sum.
+constexpr int kDqPer = 16;
 
-// ---------------------------------------------------------------------------------------------------------
-// Token rows: dQ_i = -sum_l Gq[i][l] sign(Q_i - L_l) + dL_owner(i) / r^2 ; dK_j = -sum_l Gk[j][l] sign(K_j - L_l).
-// Block = 64 rows x all channels of one side; wave w owns 8 channels [w CW, (w + 1) CW) of the 64 rows (lane = row),
-// keeping that slice of the row and of its accumulator in VGPRs. The landmark values of the wave's channels are
-// wave-uniform (one scalar load per landmark), the weights Gx[l][row] coalesced vector loads, fetched a chunk of
-// landmarks ahead.
-// ---------------------------------------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(512) void k_bwd_rows(const T* __restrict__ Q, const T* __restrict__ K,
-                                                  const float* __restrict__ L, const float* __restrict__ Gq,
-                                                  const float* __restrict__ Gk, const float* __restrict__ dL,
-                                                  T* __restrict__ dQ, T* __restrict__ dK, int N, int m, int W, int r) {
-  constexpr int NWB = kRowsWaves<D>;  // waves per block
-  constexpr int CW = D / NWB;         // channels per wave (8)
-  const int side = blockIdx.z, g = blockIdx.y;
-  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
-  const int row = blockIdx.x * 64 + lane_id();
-  if (row >= N) return;
-  const int c0 = wv * CW;
-  const T* X = (side == 0 ? Q : K) + (static_cast<size_t>(g) * N + row) * D + c0;
-  const float* gx = (side == 0 ? Gq : Gk) + static_cast<size_t>(g) * m * N + row;  // landmark-major: gx[l * N]
-  const float* __restrict__ Lg = L + static_cast<size_t>(g) * m * D + c0;
-  float x[CW], acc[CW];  // x: the row's values times kSgnScale
+__global__ __launch_bounds__(256) void k_bwd_dq_final(const float* __restrict__ dLpart, const float* __restrict__ dLW,
+                                                      const float* __restrict__ dQp, T* __restrict__ dQ, int N, int m,
+                                                      int W, int r, int nsplit) {
+  constexpr int P = 256 / D;
+  __shared__ float part[256];
+  __shared__ float add[D];
+  const int l = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, c = tid % D, q = tid / D;
+  const int wr = W / r, yb = l / wr, xb = l % wr, total = r * r * D;
+  // entry e = e0 + tid + 256 u (u < kDqPer): token e / D of the block, channel e % D = c
+  size_t o[kDqPer];
+  float t[kDqPer];
+  auto load_chunk = [&](int e0) {
 #pragma unroll
-  for (int c = 0; c < CW; ++c) {
-    x[c] = to_f32(X[c]) * kSgnScale;
-    acc[c] = 0.f;
-  }
-  constexpr int LC = 8;
-  float gc[LC], gn[LC];
-#pragma unroll
-  for (int u = 0; u < LC; ++u) gn[u] = u < m ? gx[static_cast<size_t>(u) * N] : 0.f;
-  for (int l0 = 0; l0 < m; l0 += LC) {
-#pragma unroll
-    for (int u = 0; u < LC; ++u) gc[u] = gn[u];
-#pragma unroll
-    for (int u = 0; u < LC; ++u) gn[u] = (l0 + LC + u < m) ? gx[static_cast<size_t>(l0 + LC + u) * N] : 0.f;
-#pragma unroll
-    for (int u = 0; u < LC; ++u) {
-      if (l0 + u < m) {
-        const float* __restrict__ lp = Lg + static_cast<size_t>(l0 + u) * D;
-#pragma unroll
-        for (int c = 0; c < CW; ++c) acc[c] = fmaf(-gc[u], sgn_of_scaled(x[c], lp[c]), acc[c]);
-      }
+    for (int u = 0; u < kDqPer; ++u) {
+      const int tk = min(e0 + tid + u * 256, total - 1) / D;
+      o[u] = (static_cast<size_t>(g) * N + static_cast<size_t>(yb * r + tk / r) * W + xb * r + tk % r) * D + c;
+      t[u] = dQp[o[u]];
     }
-  }
-  if (side == 0) {
-    const int yy = row / W, xx = row % W;
-    const int owner = (yy / r) * (W / r) + xx / r;
-    const float inv = 1.f / static_cast<float>(r * r);
-    const float* dl = dL + (static_cast<size_t>(g) * m + owner) * D + c0;
+  };
+  load_chunk(0);
+  float v = 0.f;  // partials q, q + P, q + 2P, ... in that order, loaded 8 at a time
+  for (int s0 = q; s0 < nsplit; s0 += 8 * P) {
+    float pv[8];
 #pragma unroll
-    for (int c = 0; c < CW; ++c) acc[c] += dl[c] * inv;
-  }
-  T* out = (side == 0 ? dQ : dK) + (static_cast<size_t>(g) * N + row) * D + c0;
+    for (int u = 0; u < 8; ++u) {
+      const int sidx = min(s0 + u * P, nsplit - 1);
+      pv[u] = dLpart[((static_cast<size_t>(g) * nsplit + sidx) * m + l) * D + c];
+    }
 #pragma unroll
-  for (int c = 0; c < CW; ++c) out[c] = from_f32<T>(acc[c]);
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u * P < nsplit) v += pv[u];
+  }
+  part[tid] = v;
+  __syncthreads();
+  if (tid < D) {
+    float a = 0.f;
+#pragma unroll
+    for (int u = 0; u < P; ++u) a += part[u * D + tid];
+    add[tid] = (a + dLW[(static_cast<size_t>(g) * m + l) * D + tid]) * (1.f / static_cast<float>(r * r));
+  }
+  __syncthreads();
+  const float ad = add[c];
+  for (int e0 = 0;;) {
+#pragma unroll
+    for (int u = 0; u < kDqPer; ++u)
+      if (e0 + tid + u * 256 < total) dQ[o[u]] = from_f32<T>(t[u] + ad);
+    e0 += kDqPer * 256;
+    if (e0 >= total) break;
+    load_chunk(e0);  // r^2 D above kDqPer x 256
+  }
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -1111,7 +1185,7 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
   float* Gq = reinterpret_cast<float*>(b + p.Gq);
   float* Gk = reinterpret_cast<float*>(b + p.Gk);
   float* dLpart = reinterpret_cast<float*>(b + p.dLpart);
-  float* dL = reinterpret_cast<float*>(b + p.dL);
+  float* dQp = reinterpret_cast<float*>(b + p.dQp);
   const T* Q = static_cast<const T*>(Qv);
   const T* K = static_cast<const T*>(Kv);
   const T* V = static_cast<const T*>(Vv);
@@ -1158,8 +1232,33 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
     if (side) (void)hipStreamWaitEvent(st, side->join, 0);  // the caller's stream still ends after the group
     return e;
   }
-  hipLaunchKernelGGL((k_bwd_dl_partial<T, D>), dim3(s.G * p.nsplitL * p.nlb), dim3(256), 0, st, Q, K, sp.L, Gq, Gk,
-                     dLpart, s.N, s.m, p.nsplitL, p.rpsL, p.nlb);
+  {
+    const dim3 grid(s.G * p.nsplitS), block(kSignSub * D);
+#define LF_SIGN(MP_)                                                                                                \
+  case MP_:                                                                                                         \
+    hipLaunchKernelGGL((k_bwd_sign<T, D, MP_>), grid, block, 0, st, Q, K, sp.L, Gq, Gk, dQp, dK, dLpart, s.N, s.m,  \
+                       p.nsplitS);                                                                                  \
+    break
+    // the landmark counts of square grids run unpadded; others are padded to a multiple of 8 with zero weights
+    const bool square = s.m == 4 || s.m == 9 || s.m == 25 || s.m == 36 || s.m == 49;
+    switch (square ? s.m : cdiv(s.m, 8) * 8) {
+      LF_SIGN(4);
+      LF_SIGN(9);
+      LF_SIGN(25);
+      LF_SIGN(36);
+      LF_SIGN(49);
+      LF_SIGN(8);
+      LF_SIGN(16);
+      LF_SIGN(24);
+      LF_SIGN(32);
+      LF_SIGN(40);
+      LF_SIGN(48);
+      LF_SIGN(56);
+      LF_SIGN(64);
+      default: return hipErrorInvalidValue;  // the backward takes m <= 64 (checked at the boundary)
+    }
+#undef LF_SIGN
+  }
   if (ex.d_dwc_w) {
     float* dp = reinterpret_cast<float*>(b + p.dwcpart);
     hipLaunchKernelGGL((k_dwc_wgrad_partial<T, D>), dim3(p.dwcblocks, s.G), dim3(kDwcThreads), 0, st, dY, V, dp,
@@ -1183,11 +1282,8 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
     hipLaunchKernelGGL(k_bwd_dlam_final, dim3(1), dim3(256), 0, lam_st, lp, ex.d_lambda, s.G * p.lamchunks);
     if (side && (e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
   }
-  const int md = s.m * D;
-  hipLaunchKernelGGL(k_bwd_dl_finalize, dim3(cdiv(static_cast<long>(s.G) * md, 256)), dim3(256), 0, st, dLpart, dLW,
-                     dL, s.G, p.nsplitL, md);
-  hipLaunchKernelGGL((k_bwd_rows<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(64 * kRowsWaves<D>), 0, st, Q,
-                     K, sp.L, Gq, Gk, dL, dQ, dK, s.N, s.m, s.W, s.r);
+  hipLaunchKernelGGL((k_bwd_dq_final<T, D>), dim3(s.m, s.G), dim3(256), 0, st, dLpart, dLW, dQp, dQ, s.N, s.m, s.W,
+                     s.r, p.nsplitS);
   if (side && ex.d_lambda && (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return e;
   return hipGetLastError();
 }
