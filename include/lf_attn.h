@@ -144,7 +144,8 @@ typedef struct lf_aux_stream {
  *        ([note] Design 3 for X_0 = alpha W_eps^T), differentiated at the first largest column and row sum;
  *        without it alpha is held constant as in lf_attn_bwd. Other bits: LF_EINVAL.
  * aux:   NULL runs everything on `stream` (as lf_attn_bwd does), or a lent second stream (lf_aux_stream): the
- *        reverse Newton-Schulz chain and the lambda gradient then overlap the row gradients.
+ *        reverse Newton-Schulz chain, the landmark-matrix terms of dL and of the lambda gradient, and the DWC
+ *        weight gradient then overlap the row gradients and the sign reductions (one fork, one join).
  * Same saved buffer, workspace (bwd_ws_bytes), alignment and errors as lf_attn_bwd; d_dwc_w is 16-byte aligned. */
 #define LF_BWD_EXACT_ALPHA 1
 int lf_attn_bwd_ex(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,

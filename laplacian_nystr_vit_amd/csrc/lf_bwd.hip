@@ -85,7 +85,8 @@ BwdWs plan(const Shape& s) {
   w.dQp = take(4 * G * N * d);
   // lambda gradient: per slice, chunks of 64 landmarks' worth of kernel entries; DWC weight gradient: per slice,
   // one [9][d] partial per block of runs of kDwcRun tokens (dwcseg runs per grid row)
-  w.lamchunks = cdiv(2L * m * N + m * m, 4096);
+  // lambda-gradient partials: one per row-gradient block (2 sides x 64-token tiles) and one per landmark row of W
+  w.lamchunks = 2 * cdiv(N, 64) + m;
   w.lampart = take(4 * G * static_cast<size_t>(w.lamchunks));
   w.dwcseg = cdiv(s.W, kDwcRun);
   w.dwcblocks = cdiv(static_cast<long>(s.H) * w.dwcseg, kDwcThreads / (s.d / 4));
@@ -653,8 +654,9 @@ __global__ __launch_bounds__(NSF_THREADS) void k_bwd_ns_final(const float* __res
 // Landmark-kernel part of dL: dLW[l][c] = -sum_{l' != l} (Gw[l][l'] + Gw[l'][l]) sign(L[l][c] - L[l'][c]).
 // ---------------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_bwd_wpart(const float* __restrict__ L, const float* __restrict__ We,
-                                                   const float* __restrict__ dWe, float* __restrict__ dLW, int m,
-                                                   int D, float inv_lam) {
+                                                   const float* __restrict__ dWe, float* __restrict__ dLW,
+                                                   float* __restrict__ lam_part, int lam_stride, int m, int D,
+                                                   float inv_lam) {
   const int g = blockIdx.y;
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= m * D) return;
@@ -663,6 +665,18 @@ __global__ __launch_bounds__(256) void k_bwd_wpart(const float* __restrict__ L, 
   const float* Lg = L + static_cast<size_t>(g) * m * D;
   const float* wg = We + g * mm;
   const float* dw = dWe + g * mm;
+  if (lam_part) {
+    // row l of the lambda gradient's W term: -sum over l2 != l of (dW W / lambda) ln(W) (the eps diagonal does
+    // not depend on lambda). The row's D threads (D consecutive lanes of one wave) take l2 = c, c + D, ... and
+    // add their shares by a butterfly within the group.
+    float a = 0.f;
+    for (int l2 = c; l2 < m; l2 += D) {
+      const float kv = wg[l * m + l2];
+      if (l2 != l && kv > 0.f) a -= dw[l * m + l2] * kv * inv_lam * __logf(kv);
+    }
+    for (int o = D / 2; o > 0; o >>= 1) a += __shfl_xor(a, o);
+    if (c == 0) lam_part[static_cast<size_t>(g) * lam_stride + lam_stride - m + l] = a;
+  }
   const float ll = Lg[t];
   float acc = 0.f;
   // unrolled, with the diagonal term selected away instead of skipped, so that the loads of several landmarks
@@ -687,8 +701,8 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
                                                      const float* __restrict__ CQ, const float* __restrict__ CK,
                                                      const float* __restrict__ mu, const float* __restrict__ rstd,
                                                      const float* __restrict__ stats, float* __restrict__ Gq,
-                                                     float* __restrict__ Gk, int N, int m, float inv_lam,
-                                                     int whiten) {
+                                                     float* __restrict__ Gk, float* __restrict__ lam_part, int N,
+                                                     int m, float inv_lam, int whiten) {
   constexpr int LDA = D + 2;  // 2 mod 4 with LDA/2 odd: conflict-free A-style reads
   constexpr int LDB = 80;     // 16 mod 32
   __shared__ float sA[64 * LDA];
@@ -736,6 +750,8 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
   // they are all in range and N keeps them aligned
   const int ib = i0 + wv * 16 + 4 * (ln >> 4);
   const bool vec = (N & 3) == 0 && ib + 3 < N;
+  float lam = 0.f;  // this lane's share of -sum G ln(C) (the lambda gradient)
+  auto lam_term = [](float gv, float c) { return c > 0.f ? -gv * __logf(c) : 0.f; };
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int l = t * 16 + (ln & 15);
@@ -759,13 +775,29 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
       const float4 o = make_float4(grad(acc[t][0], c4.x), grad(acc[t][1], c4.y), grad(acc[t][2], c4.z),
                                    grad(acc[t][3], c4.w));
       *reinterpret_cast<float4*>(out + static_cast<size_t>(l) * N + ib) = o;
+      lam += lam_term(o.x, c4.x) + lam_term(o.y, c4.y) + lam_term(o.z, c4.z) + lam_term(o.w, c4.w);
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = ib + r;
-        if (i < N) out[static_cast<size_t>(l) * N + i] = grad(acc[t][r], cm[static_cast<size_t>(l) * N + i]);
+        if (i < N) {
+          const float c = cm[static_cast<size_t>(l) * N + i], o = grad(acc[t][r], c);
+          out[static_cast<size_t>(l) * N + i] = o;
+          lam += lam_term(o, c);
+        }
       }
     }
+  }
+  if (lam_part) {
+    // the block's sum in a fixed order: butterfly within each wave, then the 4 waves in order
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lam += __shfl_xor(lam, o);
+    __shared__ float wsum[4];
+    if (ln == 0) wsum[wv] = lam;
+    __syncthreads();
+    if (tid == 0)
+      lam_part[static_cast<size_t>(g) * (2 * gridDim.x + m) + side * gridDim.x + blockIdx.x] =
+          ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
   }
 }
 
@@ -1005,48 +1037,10 @@ __global__ __launch_bounds__(256) void k_bwd_dq_final(const float* __restrict__ 
 // ---------------------------------------------------------------------------------------------------------
 // lambda gradient: every kernel entry k = exp(-D / lambda) moves by k D / lambda^2 = -k ln(k) / lambda, so
 // d/dlambda = -sum G ln(k) over G = dC C / lambda (Gq, Gk, and Gw = dW W / lambda off the diagonal, where W = W_eps
-// and the eps diagonal does not depend on lambda). Block (slice, chunk of 4096 entries) sums its share of the
-// 2 m N + m^2 entries in a fixed order, 4 entries per thread at a time; an entry whose k underflowed to 0 has G = 0
-// and adds nothing.
+// and the eps diagonal does not depend on lambda). The row-gradient kernel sums the Gq and Gk terms of each of
+// its blocks (it forms those G values), k_bwd_wpart the Gw terms of each landmark row; an entry whose k
+// underflowed to 0 has G = 0 and adds nothing. k_bwd_dlam_final adds the partials in a fixed order.
 // ---------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_bwd_dlam_partial(const float* __restrict__ Gq, const float* __restrict__ Gk,
-                                                          const float* __restrict__ CQ, const float* __restrict__ CK,
-                                                          const float* __restrict__ dWe, const float* __restrict__ We,
-                                                          float* __restrict__ part, int N, int m, int chunks,
-                                                          float inv_lam) {
-  const int g = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
-  const long mn = static_cast<long>(m) * N, total = 2 * mn + static_cast<long>(m) * m;
-  const long per = (total + chunks - 1) / chunks;
-  const long e0 = ch * per, e1 = min(total, e0 + per);
-  const size_t gmn = static_cast<size_t>(g) * mn, gmm = static_cast<size_t>(g) * m * m;
-  float acc = 0.f;
-#pragma unroll 4
-  for (long e = e0 + tid; e < e1; e += 256) {
-    float gv, kv;
-    if (e < mn) {
-      gv = Gq[gmn + e];
-      kv = CQ[gmn + e];
-    } else if (e < 2 * mn) {
-      gv = Gk[gmn + e - mn];
-      kv = CK[gmn + e - mn];
-    } else {
-      const long q = e - 2 * mn;
-      const int i = static_cast<int>(q / m), j = static_cast<int>(q % m);
-      kv = We[gmm + q];
-      gv = (i == j) ? 0.f : dWe[gmm + q] * kv * inv_lam;
-    }
-    acc += kv > 0.f ? -gv * logf(kv) : 0.f;
-  }
-  __shared__ float red[256];
-  red[tid] = acc;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0) part[static_cast<size_t>(g) * chunks + ch] = red[0];
-}
-
 // One block: thread t sums the partials t, t + 256, ... in order, then a fixed tree in LDS.
 __global__ __launch_bounds__(256) void k_bwd_dlam_final(const float* __restrict__ part, float* __restrict__ out,
                                                         int n) {
@@ -1195,43 +1189,30 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
   const float inv_lam = static_cast<float>(1.0 / static_cast<double>(s.lambda));
   const int wh = whiten ? 1 : 0;
 
-  hipError_t e = launch_ckv_general(s, sp.CQ, 1, dY, part, T1, st);
-  if (e != hipSuccess) return e;
+  // With a side stream, one fork and one join (an event wait costs the host about as much as two launches): after
+  // the first small products the side stream takes the reverse Newton-Schulz chain, dL's landmark-kernel term
+  // with the lambda gradient's W terms, and the DWC weight gradient, while the call's stream forms the row
+  // gradients, dV and the sign reductions; it then waits for the side stream before the last two kernels.
+  hipError_t e = hipSuccess;
+  hipStream_t ns_st = side ? side->s : st;
+  bool forked = false;
+  // on an error after the fork the call's stream still ends after everything enqueued on the side stream
+  auto bail = [&](hipError_t err) -> hipError_t {
+    if (forked && hipEventRecord(side->join, side->s) == hipSuccess) (void)hipStreamWaitEvent(st, side->join, 0);
+    return err;
+  };
+  if ((e = launch_ckv_general(s, sp.CQ, 1, dY, part, T1, st)) != hipSuccess) return bail(e);
   hipLaunchKernelGGL(k_bwd_small1<D>, dim3(s.G, s.m < 32 ? s.m : 32), dim3(256), 0, st, T1, sp.S, sp.P, sp.xs, sp.mu,
                      sp.rstd, dX, dS, stats, s.m, s.ns_iters, s.N, wh);
-  hipStream_t ns_st = st;
   if (side) {
     if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
-    ns_st = side->s;
+    forked = true;
   }
-  {
-    bh8* frag = reinterpret_cast<bh8*>(b + p.nsA1);
-    float* nsc = reinterpret_cast<float*>(b + p.nsA2);
-    float* Gs = reinterpret_cast<float*>(b + p.nsG);
-    float* Dk = reinterpret_cast<float*>(b + p.nsD);
-    float* Gf = reinterpret_cast<float*>(b + p.nsGf);
-    const int Kn = s.ns_iters;
-    const int sliceblocks = 8 * cdiv(s.G, 8) * Kn;  // slice_step_of's grid
-    if (Kn > 0)
-      hipLaunchKernelGGL(k_bwd_ns_pre, dim3(sliceblocks), dim3(NSB_THREADS), 0, ns_st, sp.We, sp.xs, frag, nsc, s.m,
-                         Kn, s.G);
-    hipLaunchKernelGGL(k_bwd_ns_chain, dim3(s.G), dim3(NSC_THREADS), 0, ns_st, frag, nsc, dX, Gs, Gf, s.m, Kn);
-    if (Kn > 0)
-      hipLaunchKernelGGL(k_bwd_ns_dk, dim3(sliceblocks), dim3(NSB_THREADS), 0, ns_st, sp.xs, Gs, Dk, s.m, Kn, s.G);
-    hipLaunchKernelGGL(k_bwd_ns_final, dim3(cdiv(static_cast<long>(s.m) * s.m, NSF_THREADS), s.G),
-                       dim3(NSF_THREADS), 0, ns_st, sp.We, sp.alpha, Dk, Gf, dWe, s.m, Kn, ex.exact_alpha ? 1 : 0);
-  }
-  hipLaunchKernelGGL(k_bwd_wpart, dim3(cdiv(static_cast<long>(s.m) * D, 256), s.G), dim3(256), 0, ns_st, sp.L, sp.We,
-                     dWe, dLW, s.m, D, inv_lam);
-  if (side && (e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
+  float* lp = ex.d_lambda ? reinterpret_cast<float*>(b + p.lampart) : nullptr;
   hipLaunchKernelGGL((k_bwd_rowgrad<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(256), 0, st, dY, V, sp.P, dS, sp.CQ,
-                     sp.CK, sp.mu, sp.rstd, stats, Gq, Gk, s.N, s.m, inv_lam, wh);
-  e = launch_out_adjoint(s, sp.CK, dS, dY, w, dVv, st);
-  if (e != hipSuccess) {
-    if (side) (void)hipStreamWaitEvent(st, side->join, 0);  // the caller's stream still ends after the group
-    return e;
-  }
+                     sp.CK, sp.mu, sp.rstd, stats, Gq, Gk, lp, s.N, s.m, inv_lam, wh);
+  if ((e = launch_out_adjoint(s, sp.CK, dS, dY, w, dVv, st)) != hipSuccess) return bail(e);
   {
     const dim3 grid(s.G * p.nsplitS), block(kSignSub * D);
 #define LF_SIGN(MP_)                                                                                                \
@@ -1255,36 +1236,43 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
       LF_SIGN(48);
       LF_SIGN(56);
       LF_SIGN(64);
-      default: return hipErrorInvalidValue;  // the backward takes m <= 64 (checked at the boundary)
+      default: return bail(hipErrorInvalidValue);  // the backward takes m <= 64 (checked at the boundary)
     }
 #undef LF_SIGN
   }
+  // the side stream's part, enqueued after the call's stream's (both are queued ahead of the GPU either way)
+  {
+    bh8* frag = reinterpret_cast<bh8*>(b + p.nsA1);
+    float* nsc = reinterpret_cast<float*>(b + p.nsA2);
+    float* Gs = reinterpret_cast<float*>(b + p.nsG);
+    float* Dk = reinterpret_cast<float*>(b + p.nsD);
+    float* Gf = reinterpret_cast<float*>(b + p.nsGf);
+    const int Kn = s.ns_iters;
+    const int sliceblocks = 8 * cdiv(s.G, 8) * Kn;  // slice_step_of's grid
+    if (Kn > 0)
+      hipLaunchKernelGGL(k_bwd_ns_pre, dim3(sliceblocks), dim3(NSB_THREADS), 0, ns_st, sp.We, sp.xs, frag, nsc, s.m,
+                         Kn, s.G);
+    hipLaunchKernelGGL(k_bwd_ns_chain, dim3(s.G), dim3(NSC_THREADS), 0, ns_st, frag, nsc, dX, Gs, Gf, s.m, Kn);
+    if (Kn > 0)
+      hipLaunchKernelGGL(k_bwd_ns_dk, dim3(sliceblocks), dim3(NSB_THREADS), 0, ns_st, sp.xs, Gs, Dk, s.m, Kn, s.G);
+    hipLaunchKernelGGL(k_bwd_ns_final, dim3(cdiv(static_cast<long>(s.m) * s.m, NSF_THREADS), s.G),
+                       dim3(NSF_THREADS), 0, ns_st, sp.We, sp.alpha, Dk, Gf, dWe, s.m, Kn, ex.exact_alpha ? 1 : 0);
+  }
+  hipLaunchKernelGGL(k_bwd_wpart, dim3(cdiv(static_cast<long>(s.m) * D, 256), s.G), dim3(256), 0, ns_st, sp.L, sp.We,
+                     dWe, dLW, lp, p.lamchunks, s.m, D, inv_lam);
   if (ex.d_dwc_w) {
     float* dp = reinterpret_cast<float*>(b + p.dwcpart);
-    hipLaunchKernelGGL((k_dwc_wgrad_partial<T, D>), dim3(p.dwcblocks, s.G), dim3(kDwcThreads), 0, st, dY, V, dp,
+    hipLaunchKernelGGL((k_dwc_wgrad_partial<T, D>), dim3(p.dwcblocks, s.G), dim3(kDwcThreads), 0, ns_st, dY, V, dp,
                        s.H, s.W, p.dwcseg, p.dwcblocks);
-    hipLaunchKernelGGL(k_dwc_wgrad_final<D>, dim3(s.heads * 9, D / 16), dim3(256), 0, st, dp, ex.d_dwc_w,
+    hipLaunchKernelGGL(k_dwc_wgrad_final<D>, dim3(s.heads * 9, D / 16), dim3(256), 0, ns_st, dp, ex.d_dwc_w,
                        s.G / s.heads, s.heads, p.dwcblocks);
   }
-  if (side && (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return e;
-  if (ex.d_lambda) {
-    // The lambda gradient reads Gq, Gk and dW_eps, all complete here, and nothing reads it: it goes to the side
-    // stream again, next to dL and the token rows, and the caller's stream waits for it at the end.
-    hipStream_t lam_st = st;
-    if (side) {
-      if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
-      if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
-      lam_st = side->s;
-    }
-    float* lp = reinterpret_cast<float*>(b + p.lampart);
-    hipLaunchKernelGGL(k_bwd_dlam_partial, dim3(p.lamchunks, s.G), dim3(256), 0, lam_st, Gq, Gk, sp.CQ, sp.CK, dWe,
-                       sp.We, lp, s.N, s.m, p.lamchunks, inv_lam);
-    hipLaunchKernelGGL(k_bwd_dlam_final, dim3(1), dim3(256), 0, lam_st, lp, ex.d_lambda, s.G * p.lamchunks);
-    if (side && (e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
-  }
+  if (side && (e = hipEventRecord(side->join, side->s)) != hipSuccess) return bail(e);
+  if (side && (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return bail(e);  // dLW, Gw's lambda terms
+  if (ex.d_lambda)
+    hipLaunchKernelGGL(k_bwd_dlam_final, dim3(1), dim3(256), 0, st, lp, ex.d_lambda, s.G * p.lamchunks);
   hipLaunchKernelGGL((k_bwd_dq_final<T, D>), dim3(s.m, s.G), dim3(256), 0, st, dLpart, dLW, dQp, dQ, s.N, s.m, s.W,
                      s.r, p.nsplitS);
-  if (side && ex.d_lambda && (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return e;
   return hipGetLastError();
 }
 
