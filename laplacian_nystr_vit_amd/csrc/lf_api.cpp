@@ -215,14 +215,16 @@ int fwd_launch(const lf_attn_params* p, const void* Q, const void* K, const void
   float* part = at<float>(ws, w.part);
   float* nstmp = at<float>(ws, w.nstmp);
 
-  // C_Q is materialised: the backward pass and the whitening statistics need it, and on the shapes measured so
-  // far the distance launch plus the output GEMM beats recomputing C_Q inside the output kernel
-  // (lf_out_gemm_dwc_fused).
+  // C_Q is either materialised by the distance launch and read back by the output kernel, or recomputed inside the
+  // output kernel from Q and the landmarks (the distance launch then forms C_K and W_eps only). The backward pass
+  // and the whitening statistics need the stored C_Q; for inference the choice follows measurement
+  // (lf::out_fused_pays).
+  const bool fuse_cq = !saved && !wh && p->kernel != LF_KERNEL_GAUSS && lf::out_fused_pays(s);
   LF_TRY(lf::launch_landmark_pool(s, Q, L, st));
   if (p->kernel == LF_KERNEL_GAUSS)
     LF_TRY(lf::launch_gauss(s, Q, K, L, CQ, CK, We, st));
   else
-    LF_TRY(lf::launch_laplace(s, Q, K, L, CQ, CK, We, st));
+    LF_TRY(lf::launch_laplace(s, Q, K, L, CQ, CK, We, st, fuse_cq ? 6 : 7));
   if (wh) LF_TRY(lf::launch_whiten_stats(s, CQ, mu, rstd, st));
   // The solver stays on the caller's stream: a fork of it to the side stream, concurrent with the C_Q / C_K launch
   // and S = C_K^T V, measured slower on every shape (the event hand-off costs more than the ~21 us solver hides).
@@ -233,7 +235,10 @@ int fwd_launch(const lf_attn_params* p, const void* Q, const void* K, const void
     LF_TRY(lf::launch_ns(s, We, X, xs, alpha, nullptr, nstmp, st));
     LF_TRY(lf::launch_ckv(s, CK, V, part, S, st));
   }
-  if (!saved && !wh && lf::out_mix_supported(s)) {
+  if (fuse_cq) {
+    LF_TRY(lf::launch_mix(s, X, S, nullptr, P, nullptr, st));
+    LF_TRY(lf::launch_out_fused(s, Q, L, P, V, dwc_w, Y, st));
+  } else if (!saved && !wh && lf::out_mix_supported(s)) {
     // Inference: P = X S is formed inside the output kernel (no landmark-mix launch, P never stored).
     LF_TRY(lf::launch_out_mix(s, CQ, X, S, V, dwc_w, Y, st));
   } else {

@@ -974,6 +974,13 @@ hipError_t launch_out(const Shape& s, const float* CQ, const float* P, const flo
 
 bool out_mix_supported(const Shape& s) { return s.m <= 64 && s.d >= 32; }
 
+// Recomputing C_Q inside the output kernel saves writing and reading C_Q (2 G m N 4 bytes: 9.8 MB at the stage-1
+// shape, about 1.3 us of HBM time) but moves the G N m d distance terms into a kernel that runs them slower than
+// the distance kernel does. Measured end to end (forward, inference, both paths green against the oracle):
+// stage-1 56x56 m=49 fp32 49.6 us stored / 52.6 us recomputed; stage-3 14x14 m=49 121.2 / 140.5; 128x128 m=256
+// bf16 225.0 / 239.5; 8x8 d=16 27.7 / 27.6 (within noise). The stored path is kept on every shape.
+bool out_fused_pays(const Shape&) { return false; }
+
 template <typename T>
 static void out_mix_d(const Shape& s, const float* CQ, const float* X, const float* S, const void* V, const float* w,
                       void* Y, hipStream_t st) {

@@ -39,6 +39,9 @@ hipError_t launch_out(const Shape& s, const float* CQ, const float* P, const flo
                       const float* w, void* Y, hipStream_t st);
 // Y = C_Q (X S) + DWC(V) with P = X S formed in the output kernel (no whitening; out_mix_supported: m <= 64, d >= 32).
 bool out_mix_supported(const Shape& s);
+// Whether the inference forward recomputes C_Q inside the output kernel (launch_out_fused) rather than storing it
+// from the distance launch and reading it back (measured per shape).
+bool out_fused_pays(const Shape& s);
 hipError_t launch_out_mix(const Shape& s, const float* CQ, const float* X, const float* S, const void* V,
                           const float* w, void* Y, hipStream_t st);
 // Y = C_Q P + DWC(V) with C_Q computed in the kernel from Q and L (no whitening); C_Q is never stored.
