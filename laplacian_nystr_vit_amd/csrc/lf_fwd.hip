@@ -7,6 +7,7 @@
 
 #include "lf_device.h"
 #include "lf_internal.h"
+#include "lf_split.h"
 
 namespace lf {
 
@@ -118,6 +119,16 @@ __global__ __launch_bounds__(512) void k_laplace(const T* __restrict__ Q, const 
   const int rows = (src == 2) ? m : N;
   const float* __restrict__ Lg = L + static_cast<size_t>(g) * m * D;
   const T* __restrict__ xg = (src == 0 ? Q : K) + static_cast<size_t>(g) * N * D;
+  const int l0 = (sc * nw + wv) * lc;
+  const int l1 = min(l0 + lc, m);
+  // The wave's first landmark row is fetched (scalar loads, wave-uniform address) before the rows are staged, so
+  // its latency overlaps the staging instead of following it.
+  float lfirst[D];
+  {
+    const float* __restrict__ lp = Lg + static_cast<size_t>(min(l0, m - 1)) * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) lfirst[c] = lp[c];
+  }
   for (int e = tid; e < 16 * D; e += 64 * nw) {  // float4 index over [64 rows][D / 4]
     const int r = e / (D / 4), c4 = e % (D / 4);
     const int row = tile * 64 + r;
@@ -128,8 +139,6 @@ __global__ __launch_bounds__(512) void k_laplace(const T* __restrict__ Q, const 
   }
   __syncthreads();
   const int row = tile * 64 + lane;
-  const int l0 = (sc * nw + wv) * lc;
-  const int l1 = min(l0 + lc, m);
   if (row >= rows || l0 >= l1) return;
 
   float x[D];
@@ -153,8 +162,7 @@ __global__ __launch_bounds__(512) void k_laplace(const T* __restrict__ Q, const 
     ostride = static_cast<size_t>(N);
   }
 
-  for (int l = l0; l < l1; ++l) {
-    const float* __restrict__ lp = Lg + static_cast<size_t>(l) * D;
+  auto one = [&](int l, const float* lp) {
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
     for (int c = 0; c < D; c += 4) {
@@ -166,7 +174,9 @@ __global__ __launch_bounds__(512) void k_laplace(const T* __restrict__ Q, const 
     float v = __builtin_amdgcn_exp2f(((a0 + a1) + (a2 + a3)) * scale);
     if (src == 2 && l == row) v += eps;
     out[l * ostride] = v;
-  }
+  };
+  one(l0, lfirst);
+  for (int l = l0 + 1; l < l1; ++l) one(l, Lg + static_cast<size_t>(l) * D);
 }
 
 // =====================================================================================================
@@ -408,30 +418,99 @@ __global__ __launch_bounds__(256) void k_mix(const float* __restrict__ X, const 
 //   which makes the stencil the adjoint of DWC (the backward pass uses that for dV = C_K dS + DWC^T(dY)).
 // Block: an 8 x 8 patch of the token grid of one slice (64 tokens) and all D channels.
 //   1. The 10 x 10 halo of V around the patch is staged once in LDS (zero outside the grid).
-//   2. The product runs transposed on fp32 MFMA, Y^T[c][u] = sum_l P[l][c] C[l][u], so that both operands are
-//      read from their natural [landmark][...] layouts and each lane's accumulator holds 4 consecutive channels of
-//      one token. 64-landmark chunks of C (landmark-major) and P are staged in LDS; all global loads of a chunk
-//      are issued before the LDS writes.
+//   2. The product runs transposed, Y^T[c][u] = sum_l P[l][c] C[l][u], on the fp16 MFMA with both operands split
+//      into fp16 halves (hi + lo; three MFMAs per product: hi hi, hi lo, lo hi, fp32 accumulation), which tracks
+//      the fp32 product to a few units of 1e-7 at a fifth of the fp32 MFMA's cost. 64-landmark chunks of C and P
+//      are staged in LDS as split halves in their natural [landmark][...] layouts; both operands are read with
+//      gfx950's transposing LDS read (each lane gets 8 consecutive landmarks of its channel or token). Both carry
+//      power-of-two scales that put their largest entries near 2^12, far from fp16's limits: P one per chunk,
+//      C one per token and chunk (a token far from every landmark has all its entries of C many decades below 1,
+//      which unscaled fp16 halves would flush to zero); each chunk's product is accumulated apart and added to
+//      the token's total with both scales undone. Each lane's accumulator holds 4 consecutive channels of one
+//      token.
 //   3. The epilogue adds the bias and the 3x3 stencil per float4 and stores Y per (token, 4 channels).
 // =====================================================================================================
 template <int D>
-struct OutLds {
-  static constexpr int LDV = D + 4;                       // V halo row stride (float4 aligned)
-  static constexpr int LDB = ((D + 31) / 32) * 32 + 16;   // P rows: 16 mod 32 (conflict-free MFMA reads)
-  static constexpr int LDC = 80;                          // C rows (64 tokens): 16 mod 32
-  static constexpr int VH = 0;
-  static constexpr int C = VH + 100 * LDV;
-  static constexpr int B = C + 64 * LDC;
-  static constexpr int MU = B + 64 * LDB;
-  static constexpr int WT = MU + 64;
-  static constexpr int BIAS = WT + 9 * D;
-  static constexpr int TOTAL = BIAS + D;
+struct OutLds {  // byte offsets
+  static constexpr int NHC = 72;     // C (and X) rows: 64 tokens (or landmarks) + 8 halves
+  static constexpr int NHP = D + 8;  // P^T (and S) rows: D channels + 8 halves
+  static constexpr int LDV = D + 4;  // V halo row stride in floats (float4 aligned)
+  static constexpr int SPLIT_C = 2 * 64 * NHC * 2;
+  static constexpr int SPLIT_P = 2 * 64 * NHP * 2;
+  static constexpr int HALO = 100 * LDV * 4;
+  static constexpr int CA = 0;                 // C tile (MIX: X first)
+  static constexpr int PA = CA + SPLIT_C;      // P^T
+  static constexpr int VA = PA + SPLIT_P;      // V halo (MIX: S first)
+  static constexpr int MU = VA + (HALO > SPLIT_P ? HALO : SPLIT_P);
+  static constexpr int WT = MU + 64 * 4;
+  static constexpr int BIAS = WT + 9 * D * 4;
+  static constexpr int RED = BIAS + D * 4;     // 16 floats of block reductions
+  static constexpr int CMAX = RED + 16 * 4;    // [8 waves][64 tokens]: largest C of each token per wave
+  static constexpr int TOTAL = CMAX + 8 * 64 * 4;
 };
+
+// Fragment of a split matrix stored with element (k, x) at k * stride + x (x contiguous): lane t of 16-lane group
+// g receives x = 16 strip + t at K = 32 c + 8 g .. + 7 (two transposing 8-byte reads per half). With x a row this
+// is an A operand, with x a column a B operand.
+__device__ __forceinline__ void frag_tr(const _Float16* hi, const _Float16* lo, int stride, int strip, int ln, int c,
+                                        half8& h, half8& l) {
+  const int g = ln >> 4, t = ln & 15;
+  const int x = strip * 16 + 4 * (t & 3);
+  const int k0 = c * 32 + 8 * g + (t >> 2);
+  const short4v h0 = lds_read_tr(hi + k0 * stride + x), h1 = lds_read_tr(hi + (k0 + 4) * stride + x);
+  const short4v l0 = lds_read_tr(lo + k0 * stride + x), l1 = lds_read_tr(lo + (k0 + 4) * stride + x);
+  const half4 hh0 = __builtin_bit_cast(half4, h0), hh1 = __builtin_bit_cast(half4, h1);
+  const half4 ll0 = __builtin_bit_cast(half4, l0), ll1 = __builtin_bit_cast(half4, l1);
+  h = half8{hh0[0], hh0[1], hh0[2], hh0[3], hh1[0], hh1[1], hh1[2], hh1[3]};
+  l = half8{ll0[0], ll0[1], ll0[2], ll0[3], ll1[0], ll1[1], ll1[2], ll1[3]};
+}
+
+// Fragment of a split matrix stored with element (x, k) at x * stride + k (k contiguous): one 16-byte read per half.
+__device__ __forceinline__ void frag_rows(const _Float16* hi, const _Float16* lo, int stride, int strip, int ln,
+                                          int c, half8& h, half8& l) {
+  const int x = strip * 16 + (ln & 15), k0 = c * 32 + 8 * (ln >> 4);
+  h = *reinterpret_cast<const half8*>(hi + x * stride + k0);
+  l = *reinterpret_cast<const half8*>(lo + x * stride + k0);
+}
+
+// acc += A B for one 32-wide K chunk of split operands.
+__device__ __forceinline__ f32x4 mma_split(half8 ah, half8 al, half8 bh, half8 bl, f32x4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc, 0, 0, 0);
+  return acc;
+}
+
+// 2^-e for a storage exponent, kept inside float's normal range.
+__device__ __forceinline__ float pow2_neg(int e) {
+  e = max(-100, min(100, e));
+  return __int_as_float((127 - e) << 23);
+}
+
+// Largest of the block's non-negative values a and b (8 waves), through red[0..15]; every thread gets both.
+// The caller keeps red untouched until all threads have passed the next barrier.
+__device__ __forceinline__ void block_max2(float a, float b, float* red, int wv, float& ma, float& mb) {
+  a = wave_max_nonneg(a);
+  b = wave_max_nonneg(b);
+  if ((threadIdx.x & 63) == 0) {
+    red[wv] = a;
+    red[8 + wv] = b;
+  }
+  __syncthreads();
+  ma = red[0];
+  mb = red[8];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    ma = fmaxf(ma, red[i]);
+    mb = fmaxf(mb, red[8 + i]);
+  }
+}
 
 // MIX (m <= 64, no whitening): P = X S is formed in the block's prologue from the Newton-Schulz result X and
 // S = C_K^T V (P then stands for S, and Xm for X), instead of being read from memory: this replaces the separate
-// landmark-mix launch. X is staged in the C area and S in the V-halo area before either is needed, and the halo's
-// global loads are already in flight meanwhile.
+// landmark-mix launch. It runs as P^T = S^T X^T on the same split MFMA, with S and X staged in the halo and C areas
+// (each with its own power-of-two scale) before either is needed, and the halo's and the C tile's global loads
+// already in flight meanwhile.
 template <typename T, int D, bool FUSED, bool MIX>
 __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const float* __restrict__ P,
                                              const float* __restrict__ mu, const T* __restrict__ V,
@@ -440,13 +519,18 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
                                              const float* __restrict__ L, float scale, const float* __restrict__ Xm) {
   using Lay = OutLds<D>;
   constexpr int NWV = 8, NT = 64 * NWV;  // 8 waves: two blocks per CU (LDS) give 4 waves per SIMD
-  extern __shared__ float smem[];
-  float* sVh = smem + Lay::VH;
-  float* sC = smem + Lay::C;
-  float* sB = smem + Lay::B;
-  float* sMu = smem + Lay::MU;
-  float* sWt = smem + Lay::WT;
-  float* sBias = smem + Lay::BIAS;
+  constexpr int NHC = Lay::NHC, NHP = Lay::NHP;
+  extern __shared__ __align__(16) unsigned char smem[];
+  _Float16* sChi = reinterpret_cast<_Float16*>(smem + Lay::CA);
+  _Float16* sClo = sChi + 64 * NHC;
+  _Float16* sPhi = reinterpret_cast<_Float16*>(smem + Lay::PA);
+  _Float16* sPlo = sPhi + 64 * NHP;
+  float* sVh = reinterpret_cast<float*>(smem + Lay::VA);
+  float* sMu = reinterpret_cast<float*>(smem + Lay::MU);
+  float* sWt = reinterpret_cast<float*>(smem + Lay::WT);
+  float* sBias = reinterpret_cast<float*>(smem + Lay::BIAS);
+  float* sRed = reinterpret_cast<float*>(smem + Lay::RED);
+  float* sCmax = reinterpret_cast<float*>(smem + Lay::CMAX);
   constexpr int CS = D / 16;                     // channel strips of 16
   constexpr int NP = CS * 4;                     // output tiles: (channel strip, 16-token tile) pairs
   constexpr int PPW = (NP + NWV - 1) / NWV;      // tiles per wave
@@ -476,9 +560,8 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
 
   // MIX: X and S are loaded before anything else. Vector loads complete in issue order, so the prologue's product
   // then waits only for these two small matrices while the V halo and the C_Q tile below are still in flight. The
-  // loads up to that point are branch-free (clamped address; out-of-range values are zeroed where they are stored
-  // to LDS), which lets the compiler wait for a count of outstanding loads instead of draining them all.
-  constexpr int LDX = 68;                               // MIX: X row stride in the C area
+  // loads up to that point are branch-free (clamped address; out-of-range values are zeroed where they are
+  // staged), which lets the compiler wait for a count of outstanding loads instead of draining them all.
   constexpr int NXQ = MIX ? 4096 / NT : 1;              // MIX: X elements per thread, [64][64] zero-padded
   constexpr int NSQ = MIX ? (16 * D + NT - 1) / NT : 1;  // MIX: S float4 per thread, [64][D / 4]
   float xr[NXQ];
@@ -525,51 +608,95 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
       cv0[q] = cg[(l < m && y < H && x < W) ? static_cast<size_t>(l) * N + y * W + x : 0];  // zeroed when staged
     }
   }
+  int pexp = 0;  // MIX: P^T is stored times 2^-pexp
   if constexpr (MIX) {
-    // P = X S into the P area: X [m][m] staged in the C area (row stride 68), S [m][D] in the halo area (row
-    // stride LDB); both zero beyond m, so P's rows beyond m come out zero.
-    float* sXm = sC;
-    float* sS = sVh;
+    // P^T = S^T X^T, S^T by transposing reads of S ([k][c], the halo area) and X^T by plain reads of X ([l][k],
+    // the C area), each scaled so that its largest entry lands near 2^12.
+    float mx = 0.f, ms = 0.f;
+#pragma unroll
+    for (int q = 0; q < NXQ; ++q) {
+      const int e = tid + NT * q;
+      if ((e >> 6) < m && (e & 63) < m) mx = fmaxf(mx, fabsf(xr[q]));
+    }
+#pragma unroll
+    for (int q = 0; q < NSQ; ++q) {
+      const int e = tid + NT * q;
+      if (e < 16 * D && e / C4 < m)
+        ms = fmaxf(ms, fmaxf(fmaxf(fabsf(sr[q].x), fabsf(sr[q].y)), fmaxf(fabsf(sr[q].z), fabsf(sr[q].w))));
+    }
+    float bmx, bms;
+    block_max2(mx, ms, sRed, wv, bmx, bms);
+    const int ex = store_exp(bmx), es = store_exp(bms);
+    const float fx = pow2_neg(ex), fs = pow2_neg(es);
+    _Float16* sXhi = sChi;
+    _Float16* sXlo = sClo;
+    _Float16* sShi = reinterpret_cast<_Float16*>(sVh);
+    _Float16* sSlo = sShi + 64 * NHP;
+    static_assert(Lay::SPLIT_P <= Lay::MU - Lay::VA, "S must fit the halo area");
 #pragma unroll
     for (int q = 0; q < NXQ; ++q) {
       const int e = tid + NT * q;
       const int l = e >> 6, k = e & 63;
-      sXm[l * LDX + k] = (l < m && k < m) ? xr[q] : 0.f;
+      _Float16 hh, ll;
+      split_f16((l < m && k < m) ? xr[q] * fx : 0.f, hh, ll);
+      sXhi[l * NHC + k] = hh;
+      sXlo[l * NHC + k] = ll;
     }
-    static_assert(64 * Lay::LDB <= 100 * Lay::LDV && 64 * LDX <= 64 * Lay::LDC, "MIX staging must fit");
 #pragma unroll
     for (int q = 0; q < NSQ; ++q) {
       const int e = tid + NT * q;
-      if (e < 16 * D)
-        store4(sS + (e / C4) * Lay::LDB + 4 * (e % C4), e / C4 < m ? sr[q] : make_float4(0.f, 0.f, 0.f, 0.f));
+      if (e < 16 * D) {
+        const int k = e / C4, c4 = e % C4;
+        half4 hh, ll;
+        const float4 v = k < m ? sr[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        split_scaled4(f32x4{v.x, v.y, v.z, v.w}, fs, hh, ll);
+        *reinterpret_cast<half4*>(sShi + k * NHP + 4 * c4) = hh;
+        *reinterpret_cast<half4*>(sSlo + k * NHP + 4 * c4) = ll;
+      }
     }
     __syncthreads();
-    // All 16 k-steps of the zero-padded 64 x 64 X, fully unrolled with the wave's tiles interleaved, so the LDS
-    // reads of later steps are in flight during the MFMAs of earlier ones (the padding adds exact zeros).
-    // A wave owns PPM whole tiles or none (NPM is a multiple of PPM), so one uniform test covers them all.
+    // A wave owns PPM whole tiles or none (NPM is a multiple of PPM), so one uniform test covers them all. Tile
+    // (channel strip cs, landmark tile lt).
     constexpr int NPM = 4 * CS, PPM = (NPM + NWV - 1) / NWV;
     static_assert(NPM % PPM == 0, "tiles per wave must divide the tile count");
+    f32x4 a4[PPM];
+#pragma unroll
+    for (int jj = 0; jj < PPM; ++jj) a4[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float pm = 0.f;
     if (wv * PPM < NPM) {
-      f32x4 a4[PPM];
 #pragma unroll
-      for (int jj = 0; jj < PPM; ++jj) a4[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const int k = ks * 4 + (ln >> 4);
+      for (int c = 0; c < 2; ++c) {
 #pragma unroll
         for (int jj = 0; jj < PPM; ++jj) {
-          const int ti = (wv * PPM + jj) / CS, tc = (wv * PPM + jj) % CS;
-          a4[jj] = mfma16x16x4(sXm[(ti * 16 + (ln & 15)) * LDX + k], sS[k * Lay::LDB + tc * 16 + (ln & 15)], a4[jj]);
+          const int cs = (wv * PPM + jj) / 4, lt = (wv * PPM + jj) % 4;
+          half8 ah, al, bh, bl;
+          frag_tr(sShi, sSlo, NHP, cs, ln, c, ah, al);
+          frag_rows(sXhi, sXlo, NHC, lt, ln, c, bh, bl);
+          a4[jj] = mma_split(ah, al, bh, bl, a4[jj]);
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < PPM; ++jj) {
-        const int ti = (wv * PPM + jj) / CS, tc = (wv * PPM + jj) % CS;
+      for (int jj = 0; jj < PPM; ++jj)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sB[(ti * 16 + 4 * (ln >> 4) + r) * Lay::LDB + tc * 16 + (ln & 15)] = a4[jj][r];
+        for (int r = 0; r < 4; ++r) pm = fmaxf(pm, fabsf(a4[jj][r]));
+    }
+    // the barrier inside also retires every read of X and S
+    float bpm, unused;
+    block_max2(pm, 0.f, sRed, wv, bpm, unused);
+    const int e1 = store_exp(bpm);
+    pexp = ex + es + e1;
+    const float f1 = pow2_neg(e1);
+    if (wv * PPM < NPM) {
+#pragma unroll
+      for (int jj = 0; jj < PPM; ++jj) {
+        const int cs = (wv * PPM + jj) / 4, lt = (wv * PPM + jj) % 4;
+        const int c0 = cs * 16 + 4 * (ln >> 4), l = lt * 16 + (ln & 15);
+        half4 hh, ll;
+        split_scaled4(a4[jj], f1, hh, ll);
+        *reinterpret_cast<half4*>(sPhi + l * NHP + c0) = hh;
+        *reinterpret_cast<half4*>(sPlo + l * NHP + c0) = ll;
       }
     }
-    __syncthreads();  // X and S are dead: the C and halo areas are free again
   }
   if (has_w) {
 #pragma unroll
@@ -585,7 +712,14 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
       sWt[e] = w[(static_cast<size_t>(h) * D + c) * 9 + (flip ? 8 - q : q)];
     }
   }
-  float bias_acc = 0.f;
+  if constexpr (FUSED) {
+    // chunk rows a wave does not write keep finite values: zero them once (their P^T columns are staged as zero)
+    for (int e = tid; e < 64 * NHC; e += NT) {
+      sChi[e] = static_cast<_Float16>(0.f);
+      sClo[e] = static_cast<_Float16>(0.f);
+    }
+  }
+  float bias_acc = 0.f;  // the whitening bias of channel tid, in true units
 
   // FUSED: C_Q is not read from memory but computed here. Every wave holds the Q rows of the patch's 64 tokens
   // (lane = token) and computes its share of each landmark chunk, landmark coordinates arriving through scalar
@@ -616,7 +750,7 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
   for (int j = 0; j < PPW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int lc0 = 0; lc0 < m; lc0 += 64) {
     const int nl = min(64, m - lc0);
-    // FUSED: landmarks per wave; rows nl .. NWV lq - 1 (which cover the MFMA's 4-row padding) come out as zeros
+    // FUSED: landmarks per wave
     const int lq = (nl + NWV - 1) / NWV;
     constexpr int NCV = FUSED ? LQM : 4096 / NT;
     float cv[NCV];
@@ -667,50 +801,103 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
       }
     }
     const float muv = (mu && tid < 64 && tid < nl) ? mu[static_cast<size_t>(g) * m + lc0 + tid] : 0.f;
-    __syncthreads();  // previous chunk's reads are done
-    if constexpr (FUSED) {
+    // Scales of the chunk: every value of C this thread holds belongs to token ln (NT is a multiple of 64;
+    // FUSED: lane = token), and P's largest entry. The per-wave maxima go to LDS before the barrier below, which
+    // every thread passes only after the previous chunk's reads of them.
+    float cm = 0.f;
 #pragma unroll
-      for (int q = 0; q < LQM; ++q)
-        if (q < lq) sC[(wq * lq + q) * Lay::LDC + ln] = cv[q];
-    } else {
-#pragma unroll
-      for (int q = 0; q < NCV; ++q) {
-        const int e = tid + NT * q;
-        sC[(e >> 6) * Lay::LDC + (e & 63)] = cv[q];
-      }
-    }
+    for (int q = 0; q < NCV; ++q) cm = fmaxf(cm, cv[q]);
+    sCmax[wv * 64 + ln] = cm;
     if constexpr (!MIX) {
+      float pm = 0.f;
+#pragma unroll
+      for (int q = 0; q < NQB; ++q)
+        pm = fmaxf(pm, fmaxf(fmaxf(fabsf(bv[q].x), fabsf(bv[q].y)), fmaxf(fabsf(bv[q].z), fabsf(bv[q].w))));
+      pm = wave_max_nonneg(pm);
+      if (ln == 0) sRed[wv] = pm;
+    }
+    __syncthreads();  // previous chunk's reads are done
+    int eP = pexp;    // P of this chunk is stored times 2^-eP
+    if constexpr (!MIX) {
+      float bpm = sRed[0];
+#pragma unroll
+      for (int i = 1; i < NWV; ++i) bpm = fmaxf(bpm, sRed[i]);
+      eP = store_exp(bpm);
+      const float fp = pow2_neg(eP);
 #pragma unroll
       for (int q = 0; q < NQB; ++q) {
         const int e = tid + NT * q;
-        if (e < 16 * D) store4(sB + (e / C4) * Lay::LDB + 4 * (e % C4), bv[q]);
+        if (e < 16 * D) {
+          half4 hh, ll;
+          split_scaled4(f32x4{bv[q].x, bv[q].y, bv[q].z, bv[q].w}, fp, hh, ll);
+          *reinterpret_cast<half4*>(sPhi + (e / C4) * NHP + 4 * (e % C4)) = hh;
+          *reinterpret_cast<half4*>(sPlo + (e / C4) * NHP + 4 * (e % C4)) = ll;
+        }
       }
     }
     if (tid < 64) sMu[tid] = muv;
     __syncthreads();
-    if (mu && tid < D) {
-      for (int kk = 0; kk < nl; ++kk) bias_acc += sMu[kk] * sB[kk * Lay::LDB + tid];
+    {
+      // C of token ln scaled by 2^-e, its largest entry in the chunk near 2^12
+      float tm = sCmax[ln];
+#pragma unroll
+      for (int i = 1; i < NWV; ++i) tm = fmaxf(tm, sCmax[i * 64 + ln]);
+      const float fc = pow2_neg(store_exp(tm));
+      if constexpr (FUSED) {
+#pragma unroll
+        for (int q = 0; q < LQM; ++q)
+          if (q < lq) {
+            _Float16 hh, ll;
+            split_f16(cv[q] * fc, hh, ll);
+            sChi[(wq * lq + q) * NHC + ln] = hh;
+            sClo[(wq * lq + q) * NHC + ln] = ll;
+          }
+      } else {
+#pragma unroll
+        for (int q = 0; q < NCV; ++q) {
+          const int e = tid + NT * q;
+          _Float16 hh, ll;
+          split_f16(cv[q] * fc, hh, ll);
+          sChi[(e >> 6) * NHC + (e & 63)] = hh;
+          sClo[(e >> 6) * NHC + (e & 63)] = ll;
+        }
+      }
     }
-    // a wave owns PPW whole tiles or none (NP is a multiple of PPW): one uniform test outside the k-steps
-    auto kstep = [&](int ks) {
-      const int k = ks * 4 + (ln >> 4);
+    __syncthreads();
+    if (mu && tid < D) {
+      // the chunk's share of the bias, from the two halves of P
+      float b = 0.f;
+      for (int kk = 0; kk < nl; ++kk)
+        b += sMu[kk] * (static_cast<float>(sPhi[kk * NHP + tid]) + static_cast<float>(sPlo[kk * NHP + tid]));
+      bias_acc += ldexpf(b, eP);
+    }
+    // a wave owns PPW whole tiles or none (NP is a multiple of PPW): one uniform test outside the MFMA sequence
+    if (wv * PPW < NP) {
+      const int strip = (wv * PPW) >> 2;  // the wave's tiles share their channel strip
+      f32x4 ac[PPW];
+#pragma unroll
+      for (int j = 0; j < PPW; ++j) ac[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        half8 ah, al;
+        frag_tr(sPhi, sPlo, NHP, strip, ln, c, ah, al);
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) {
+          half8 bh, bl;
+          frag_tr(sChi, sClo, NHC, (wv * PPW + j) & 3, ln, c, bh, bl);
+          ac[j] = mma_split(ah, al, bh, bl, ac[j]);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < PPW; ++j) {
-        const int pr = wv * PPW + j;
-        const int strip = pr >> 2, tile = pr & 3;
-        const float av = sB[k * Lay::LDB + strip * 16 + (ln & 15)];
-        const float bt = sC[k * Lay::LDC + tile * 16 + (ln & 15)];
-        acc[j] = mfma16x16x4(av, bt, acc[j]);
-      }
-    };
-    if (wv * PPW < NP) {
-      if constexpr (FUSED) {
-        // rows past the chunk's landmarks may be stale in the C area here: stop at nl
-        for (int ks = 0; ks < (nl + 3) / 4; ++ks) kstep(ks);
-      } else {
-        // the staged C and P rows past nl are zeros: all 16 k-steps, fully unrolled
+        // undo the scales of P and of this lane's token u (tile column ln % 16)
+        const int u = ((wv * PPW + j) & 3) * 16 + (ln & 15);
+        float tm = sCmax[u];
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) kstep(ks);
+        for (int i = 1; i < NWV; ++i) tm = fmaxf(tm, sCmax[i * 64 + u]);
+        const int eu = max(-100, min(100, store_exp(tm))) + eP;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] += ldexpf(ac[j][r], eu);
       }
     }
   }
@@ -942,7 +1129,7 @@ static void out_launch(const Shape& s, const float* CQ, const float* P, const fl
                        const float* w, void* Y, int flip, const void* Q, const float* L, const float* X,
                        hipStream_t st) {
   const int tiles_x = cdiv(s.W, 8), tiles_y = cdiv(s.H, 8);
-  const size_t lds = sizeof(float) * OutLds<D>::TOTAL;
+  const size_t lds = OutLds<D>::TOTAL;
   if (lds > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_out<T, D, FUSED, MIX>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
