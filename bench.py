@@ -159,6 +159,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall time budget of the oracle sample")
     ap.add_argument("--kernel-reps", type=int, default=100)
     ap.add_argument("--no-cold", action="store_true", help="skip the timing over rotating buffer sets")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="skip the 1.5 s shader-clock observation (for profiler and counter runs)")
     ap.add_argument("--solver", action="store_true",
                     help="measure Newton-Schulz against conjugate gradients on the workload's W_eps batch")
     ap.add_argument("--counters", action="store_true",
@@ -467,7 +469,7 @@ def main():
     step_events = {"median_ms": per[len(per) // 2], "p10_ms": per[len(per) // 10],
                    "p90_ms": per[min(len(per) - 1, (9 * len(per)) // 10)], "steps": len(per),
                    "median_tokens_per_s": wl.tokens / (per[len(per) // 2] * 1e-3)}
-    sclk = observed_sclk_mhz(1.5, lambda: run_step(hot))
+    sclk = None if args.no_sclk else observed_sclk_mhz(1.5, lambda: run_step(hot))
     torch.cuda.synchronize()
 
     cold = None
