@@ -35,7 +35,7 @@ EDGE = [
     # the most Newton-Schulz steps the library accepts (LF_NS_ITERS_MAX = 64): six runs of coupled steps
     WL.TINY.replace(name="tiny_K64_m16", ns_iters=64),
     WL.PVT_S1.replace(name="s1_B1_K64", B=1, ns_iters=64),
-    # the m > 64 path (fp32 products, one launch per step) over four runs of coupled steps
+    # the m > 64 path (split-fp16 tile products, one launch per coupled step) over four runs of coupled steps
     WL.TINY.replace(name="ragged_20x20_m100_K40", H=20, W=20, d=64, r=2, ns_iters=40, qk_dist="student_t"),
     # d = 128 with m <= 64: the output kernel forms P = X S in its prologue with more than 64 KB of LDS
     WL.TINY.replace(name="d128_14x14_m49_B2", B=2, H=14, W=14, d=128, r=2, qk_dist="student_t"),
