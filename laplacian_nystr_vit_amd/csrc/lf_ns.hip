@@ -14,7 +14,8 @@
 namespace lf {
 
 // =====================================================================================================
-// m <= 64: one 512-thread block (eight waves, two per SIMD) per slice runs every iteration out of LDS.
+// m <= 64: one 256-thread block (four waves, one per SIMD) per slice runs every iteration, with both carried
+// matrices in registers.
 //
 // Products run on the fp16 MFMA (v_mfma_f32_16x16x32_f16, 16x the fp32 MFMA rate on gfx950) with every fp32
 // operand split as x = hi + lo (two fp16 values, about 22 significant bits) and
@@ -22,201 +23,183 @@ namespace lf {
 // accumulated in fp32. Three fp16 MFMAs cost less than a fifth of one fp32 MFMA product, and the result tracks an
 // fp32 product to a few units of 1e-7.
 //
-// Every matrix is zero-padded to 16 ST x 16 ST (ST = 1, 2 or 4 strips of 16) and stored in LDS by columns (the
-// entries of column j contiguous), which is the layout the MFMA result has (four consecutive rows of one column
-// per lane, one 8-byte store per split half). A product reads its B operand (columns, K-contiguous) with plain
-// 16-byte reads and its A operand (rows) with gfx950's transposing LDS read, ds_read_b64_tr_b16: within each group
-// of 16 lanes, result lane j, element s comes from element j % 4 of the 8 bytes lane 4 s + j / 4 addressed, so
-// two such reads at columns k = 8 (lane / 16) + 4 h + (lane % 16) / 4 give a lane its row's eight consecutive K
-// values. Each matrix is therefore read as itself, never as its transpose: X_k is symmetric only in exact
-// arithmetic, and feeding X_k^T where the recurrence has X_k doubles the antisymmetric part of the rounding error
-// every step. W, the A operand of W X, never changes: its fragments stay in registers.
+// The coupled recurrence (below) forms T_{k+1} = T_k U_k and X_{k+1} = X_k U_k with U_k = 2I - T_k. The kernel
+// carries the transposes A_k = X_k^T and B_k = T_k^T, zero-padded to 16 ST x 16 ST, and computes
+//   A_{k+1} = U_k^T A_k = 2 A_k - B_k A_k,   B_{k+1} = U_k^T B_k = 2 B_k - B_k B_k,
+// the same sums, so that the carried matrices are the B operands: wave w holds column strip w (16 columns) of A
+// and of B in the MFMA result layout (lane (g, t): rows 4g .. 4g+3 of column t of each 16-row tile), and one
+// 32-deep K chunk of its next product takes, for lane (g, t), those four rows of two 16-row tiles (slots 0-3 from
+// the first tile, 4-7 from the second). The A operand B_k is read in that same K order, so the carried strips
+// feed the MFMA where they stand: no lane exchanges and no LDS round trip. Per step a wave writes its strip of
+// B_{k+1} (4 KB) and reads all of B_k (16 KB); every product operand through LDS would be four times the reads
+// and three times the writes. Each matrix is read as itself, never as its transpose: X_k is symmetric only in
+// exact arithmetic, and feeding X_k^T where the recurrence has X_k doubles the antisymmetric part of the rounding
+// error every step.
 //
-// A step of the coupled recurrence (below) is two products that share their B operand U_k = 2I - T_k:
-// T_{k+1} = T_k U_k and X_{k+1} = X_k U_k. With 64-wide matrices each wave takes one row strip and two column
-// strips of a quadrant in both products (24 MFMAs, 16 KB of fragments, T_{k+1}, U_{k+1} = 2I - T_{k+1} and
-// X_{k+1} stored from its accumulators), so the two waves of a SIMD carry equal work and each one's epilogue
-// overlaps the other's MFMAs. With narrower matrices (one tile per quadrant) waves 0-3 form T and U and waves 4-7
-// form X. Every buffer is double-buffered by step parity, so a step needs one barrier.
+// B is stored by columns (the rows of column j contiguous, 160-byte pitch) and its rows are read with gfx950's
+// transposing LDS read, ds_read_b64_tr_b16: within each group of 16 lanes, result lane j, element s comes from
+// element j % 4 of the 8 bytes lane 4 s + j / 4 addressed, so lanes that address columns k0 + (lane % 16) / 4,
+// rows 4 (lane % 4) .. + 3 of a tile receive their row at K = k0 .. k0 + 3. In columns 8 .. 15 of every 16 the
+// 4-row quads are swapped in pairs (quad q at q ^ 2): with the 160-byte pitch both the tile writes (16 columns x
+// 8 bytes per half-wave) and these reads (8 columns x 32 bytes) then touch every LDS bank once.
 //
-// X carries a power-of-two scale 2^-e in its fp16 halves: e follows the largest entry of the previous iterate
-// so that entries sit near 2^12 (far from fp16's subnormals and its 65504 limit); an iterate that still comes
-// out above 2^15 is stored again with a fresh exponent. W needs no scale (entries at most 1 + eps) and neither
-// do T and U (the eigenvalues of W X stay in (0, 1]).
+// A carries a power-of-two scale 2^-e per wave (its column strip alone enters its products): entries sit near
+// 2^12, far from fp16's subnormals and its 65504 limit, and the strip is scaled again when its largest entry
+// leaves [2^8, 2^14). W needs no scale (entries at most 1 + eps) and neither do T and U (the eigenvalues of W X
+// stay in (0, 1]).
 // =====================================================================================================
 
-constexpr int NH = 72;  // fp16 elements per LDS column: 64 + 8 (144-byte stride, 16-byte aligned)
+constexpr int kRegPitch = 80;              // fp16 elements per stored column: 64 rows + 16 (160 bytes)
+constexpr int kRegPlane = 64 * kRegPitch;  // fp16 elements per plane (hi or lo) of a stored matrix
 
-struct alignas(16) SplitMat {
-  _Float16 hi[64 * NH];
-  _Float16 lo[64 * NH];
+struct alignas(16) RegSplit {
+  _Float16 hi[kRegPlane];
+  _Float16 lo[kRegPlane];
 };
 
-
-// Operand fragments of TQ consecutive 16-row (or 16-column) strips over KC chunks of 32 along K.
-template <int TQ, int KC>
-struct Frags {
-  half8 h[TQ][KC], l[TQ][KC];
-};
-
-// B operand: chunk c (K entries 32 c .. 32 c + 31) of column strips s0 .. s0+TQ-1 of a by-columns split matrix
-// (element (k, j) at j*NH + k): one 16-byte read per lane and half.
-template <int TQ, int KC>
-__device__ __forceinline__ void load_chunk_b(const SplitMat& M, int s0, int ln, int c, Frags<TQ, KC>& f) {
-#pragma unroll
-  for (int a = 0; a < TQ; ++a) {
-    const int j = (s0 + a) * 16 + (ln & 15);
-    const int k0 = c * 32 + 8 * (ln >> 4);
-    f.h[a][c] = *reinterpret_cast<const half8*>(&M.hi[j * NH + k0]);
-    f.l[a][c] = *reinterpret_cast<const half8*>(&M.lo[j * NH + k0]);
-  }
-}
-
-
-// A operand: chunk c of row strips s0 .. s0+TQ-1 of the same by-columns matrix (element (i, k) at k*NH + i), by
-// transposing reads: lane t of lane group g addresses column k = 32 c + 8 g + 4 h + t / 4, rows 4 (t % 4) .. + 3
-// of the strip, and receives row 16 strip + t at K = 32 c + 8 g + 4 h .. + 3.
-template <int TQ, int KC>
-__device__ __forceinline__ void load_chunk_a(const SplitMat& M, int s0, int ln, int c, Frags<TQ, KC>& f) {
-  const int g = ln >> 4, t = ln & 15;
-#pragma unroll
-  for (int a = 0; a < TQ; ++a) {
-    const int i = (s0 + a) * 16 + 4 * (t & 3);
-    const int k0 = c * 32 + 8 * g + (t >> 2);
-    const short4v h0 = lds_read_tr(&M.hi[k0 * NH + i]), h1 = lds_read_tr(&M.hi[(k0 + 4) * NH + i]);
-    const short4v l0 = lds_read_tr(&M.lo[k0 * NH + i]), l1 = lds_read_tr(&M.lo[(k0 + 4) * NH + i]);
-    const half4 hh0 = __builtin_bit_cast(half4, h0), hh1 = __builtin_bit_cast(half4, h1);
-    const half4 ll0 = __builtin_bit_cast(half4, l0), ll1 = __builtin_bit_cast(half4, l1);
-    f.h[a][c] = half8{hh0[0], hh0[1], hh0[2], hh0[3], hh1[0], hh1[1], hh1[2], hh1[3]};
-    f.l[a][c] = half8{ll0[0], ll0[1], ll0[2], ll0[3], ll1[0], ll1[1], ll1[2], ll1[3]};
-  }
-}
-
-template <int TA, int TB>
-__device__ __forceinline__ void zero_acc(f32x4 acc[TA][TB]) {
-#pragma unroll
-  for (int a = 0; a < TA; ++a)
-#pragma unroll
-    for (int b = 0; b < TB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-}
-
-// acc[a][b] += A-strip a times B-strip b over chunk c. One fp32 accumulator per tile takes hi*hi and both cross
-// terms: each MFMA step rounds at fp32 relative to the running sum, which keeps the product at fp32 accuracy.
-template <int TA, int TB, int KC>
-__device__ __forceinline__ void mma_chunk(const Frags<TA, KC>& A, const Frags<TB, KC>& B, f32x4 acc[TA][TB],
-                                          int c) {
-#pragma unroll
-  for (int a = 0; a < TA; ++a)
-#pragma unroll
-    for (int b = 0; b < TB; ++b)
-      acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.h[a][c], B.h[b][c], acc[a][b], 0, 0, 0);
-#pragma unroll
-  for (int a = 0; a < TA; ++a)
-#pragma unroll
-    for (int b = 0; b < TB; ++b)
-      acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.h[a][c], B.l[b][c], acc[a][b], 0, 0, 0);
-#pragma unroll
-  for (int a = 0; a < TA; ++a)
-#pragma unroll
-    for (int b = 0; b < TB; ++b)
-      acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.l[a][c], B.h[b][c], acc[a][b], 0, 0, 0);
-}
-
-
-
-// The 4 rows i0 .. i0+3 of column j into a by-columns matrix: M[j][i0 .. i0+3] (two 8-byte writes).
-__device__ __forceinline__ void put_t4(SplitMat& M, int j, int i0, half4 h, half4 l) {
-  *reinterpret_cast<half4*>(&M.hi[j * NH + i0]) = h;
-  *reinterpret_cast<half4*>(&M.lo[j * NH + i0]) = l;
-}
-
-constexpr int kRestoreExp = 15;  // an entry at or above 2^15 * 2^e triggers a re-store with a fresh exponent
 // Longest run of coupled T/X steps before T is formed again as W X: 2^kPairRun times the relative rounding of
 // one split-fp16 product (2^-22) must stay well below 1.
 constexpr int kPairRun = 11;
 
+// Split of two result tiles into one B operand chunk: slots 0-3 from tile a, 4-7 from tile b. lo = fma(v, one,
+// -hi) is exact (hi is v rounded to fp16), and with one not a compile-time constant it stays a single
+// mixed-precision fma.
+__device__ __forceinline__ void split_chunk(f32x4 a, f32x4 b, float one, half8& h, half8& l) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const _Float16 ha = static_cast<_Float16>(a[e]), hb = static_cast<_Float16>(b[e]);
+    h[e] = ha;
+    h[4 + e] = hb;
+    l[e] = static_cast<_Float16>(__builtin_fmaf(a[e], one, -static_cast<float>(ha)));
+    l[4 + e] = static_cast<_Float16>(__builtin_fmaf(b[e], one, -static_cast<float>(hb)));
+  }
+}
 
+// acc + A B over one 32-deep chunk, A and B split: three fp16 products into one fp32 accumulator.
+__device__ __forceinline__ f32x4 mma_split3(half8 ah, half8 al, half8 bh, half8 bl, f32x4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc, 0, 0, 0);
+}
 
-template <int ST, int KC>
+// A operand chunk c of row tile p of a stored matrix: K tiles 2c and 2c + 1 in B-chunk order. lane_r is the
+// lane's offset for row tile 0, K tile 0 (see ns_small_block); a 16-row step is 16 elements, a 16-column step
+// 16 * kRegPitch.
+template <int ST>
+__device__ __forceinline__ void load_rows(const RegSplit& M, int lane_r, int c, int p, half8& h, half8& l) {
+  const int oa = lane_r + 16 * p + 2 * c * 16 * kRegPitch;
+  const half4 h0 = __builtin_bit_cast(half4, lds_read_tr(&M.hi[oa]));
+  const half4 l0 = __builtin_bit_cast(half4, lds_read_tr(&M.lo[oa]));
+  half4 h1 = {0, 0, 0, 0}, l1 = {0, 0, 0, 0};
+  if constexpr (ST >= 2) {
+    h1 = __builtin_bit_cast(half4, lds_read_tr(&M.hi[oa + 16 * kRegPitch]));
+    l1 = __builtin_bit_cast(half4, lds_read_tr(&M.lo[oa + 16 * kRegPitch]));
+  }
+  h = half8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+  l = half8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+}
+
+// Maximum over the wave of a non-negative double, returned wave-uniform (non-negative doubles order like their
+// bit patterns): DPP steps inside each row of 16 lanes on both halves, then the four row results.
+__device__ __forceinline__ double wave_max_nonneg_f64(double v) {
+  unsigned long long x = static_cast<unsigned long long>(__double_as_longlong(v));
+  auto dpp_max = [&](auto ctrl) {
+    constexpr int c = decltype(ctrl)::value;
+    const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), c, 0xf, 0xf, false));
+    const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(x >> 32), c, 0xf, 0xf, false));
+    const unsigned long long y = (static_cast<unsigned long long>(hi) << 32) | lo;
+    x = x > y ? x : y;
+  };
+  dpp_max(std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+  dpp_max(std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+  dpp_max(std::integral_constant<int, 0x124>{});  // row_ror:4
+  dpp_max(std::integral_constant<int, 0x128>{});  // row_ror:8
+  unsigned long long r = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(x), 16 * q));
+    const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(x >> 32), 16 * q));
+    const unsigned long long y = (static_cast<unsigned long long>(hi) << 32) | lo;
+    r = r > y ? r : y;
+  }
+  return __longlong_as_double(static_cast<long long>(r));
+}
+
+template <int ST>
 __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ We, float* __restrict__ Xout,
                                                float* __restrict__ xs, float* __restrict__ alpha_out,
                                                float* __restrict__ resid, int m, int iters) {
-  constexpr int TQ = ST >= 2 ? ST / 2 : 1;  // tiles per side of a quadrant
-  constexpr int NQA = ST == 1 ? 1 : 4;      // quadrants with work
-  constexpr int CS = TQ;                    // column strips (B operand) per wave
-  constexpr bool kBoth = TQ >= 2;           // each wave takes part in both products (else one product per wave)
-  constexpr int NTH = 512;
-  // sT, sU, sX: T_k, U_k = 2I - T_k and X_k (times 2^-e) by columns, each double-buffered by step parity.
-  __shared__ SplitMat sT[2], sU[2], sX[2];
+  constexpr int NT = ST;            // 16-row tiles per strip
+  constexpr int KC = (ST + 1) / 2;  // 32-deep K chunks
+  constexpr int NTH = 256;
+  // sU: -B_k split, by step parity; sX: -A_k split with one block-wide exponent at a segment start.
+  __shared__ RegSplit sU[2], sX;
   __shared__ double red[3][4][64];
-  __shared__ double red_res[8];
   __shared__ float s_alpha, s_wmax;
-  // Bits of the largest |X| entry of the iterate written in step k, in slot k % 3: slot k + 1 is cleared during
-  // step k (its last readers finished before the barrier of step k - 1), so the one barrier per step suffices.
-  __shared__ unsigned int s_max[3];
-  const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
+  __shared__ float s_part[4];
+  const int tid = threadIdx.x, ln = lane_id();
+  const int cs = __builtin_amdgcn_readfirstlane(wave_id());  // the wave's column strip
+  const bool act = cs < ST;
   const size_t mm = static_cast<size_t>(m) * m;
   const float* wg = We + g * mm;
-  float* wf = reinterpret_cast<float*>(&sU[1]);  // fp32 W (64 x 65) in a U buffer not used before iteration 0
-  // Wave w works on quadrant w & 3 of the products. With 64-wide matrices (two strips per quadrant side) wave half
-  // w >> 2 takes one row strip of the quadrant and both of its column strips, in both products; with narrower
-  // matrices (one tile per quadrant) half 0 forms T_{k+1} and U_{k+1}, half 1 forms X_{k+1}.
-  const int qd = wv & 3, hf = wv >> 2;
-  const bool act = qd < NQA;
-  const bool doT = act && (kBoth || hf == 0), doX = act && (kBoth || hf == 1);
-  const int rs = (qd & 1) * TQ + (kBoth ? hf : 0);  // the wave's row strip
-  const int c0 = (qd >> 1) * TQ;                    // its first column strip
-  constexpr int NZ = static_cast<int>(sizeof(SplitMat) / sizeof(uint4));
-  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+  const float one = m > 0 ? 1.f : 0.f;  // 1 for every call that reaches here, unknown to the compiler
+  const int gq = ln >> 4, t = ln & 15;
+  const int col = cs * 16 + t;  // the lane's column of the strip
+  // lane offsets: transposing reads (row tile 0, K tile 0) and tile writes (row tile 0) of a stored matrix
+  const int lane_r = (4 * gq + (t >> 2)) * kRegPitch + 4 * ((t & 3) ^ ((gq >> 1) << 1));
+  const int lane_w = col * kRegPitch + 4 * (gq ^ (((t >> 3) & 1) << 1));
 
-  if constexpr (ST == 1) {
-    // K runs over 32 entries while the matrices are 16 wide: the padding must read as zero.
-    for (int q = tid; q < NZ; q += NTH) {
-      reinterpret_cast<uint4*>(&sX[0])[q] = zero4;
-      reinterpret_cast<uint4*>(&sX[1])[q] = zero4;
-      reinterpret_cast<uint4*>(&sT[0])[q] = zero4;
-      reinterpret_cast<uint4*>(&sT[1])[q] = zero4;
-      reinterpret_cast<uint4*>(&sU[0])[q] = zero4;
+  // W and W^T in fp32, zero-padded to 64 x 64, rows of kWp floats (four consecutive entries are one 16-byte
+  // read), inside the U buffers, which no step uses yet. Every load of a thread is issued before any is used.
+  constexpr int kWp = 68;
+  float* wrow = reinterpret_cast<float*>(&sU[0]);  // W[i][j] at i * kWp + j
+  float* wcol = wrow + 64 * kWp;                   // W[i][j] at j * kWp + i
+  {
+    const int mc = m - 1;
+    float v[4096 / NTH];
+#pragma unroll
+    for (int q = 0; q < 4096 / NTH; ++q) {
+      const int idx = tid + NTH * q, i = idx >> 6, j = idx & 63;
+      v[q] = wg[min(i, mc) * m + min(j, mc)];
+    }
+#pragma unroll
+    for (int q = 0; q < 4096 / NTH; ++q) {
+      const int idx = tid + NTH * q, i = idx >> 6, j = idx & 63;
+      const float w = (i < m && j < m) ? v[q] : 0.f;
+      wrow[i * kWp + j] = w;
+      wcol[j * kWp + i] = w;
     }
   }
-#pragma unroll
-  for (int q = 0; q < 4096 / NTH; ++q) {
-    const int idx = tid + NTH * q;
-    const int i = idx >> 6, j = idx & 63;
-    wf[i * 65 + j] = (i < m && j < m) ? wg[i * m + j] : 0.f;
-  }
-  if (tid < 3) s_max[tid] = 0u;
   __syncthreads();
 
   // alpha = 1 / (max_j sum_i |W_ij| * max_i sum_j |W_ij|) in float64: thread (c, quarter) sums 16 entries of
   // column c and of row c, the quarters are combined, then wave 0 takes the maxima (and max |W_ij|).
-  if (tid < 256) {
+  {
     const int c = tid & 63, qtr = tid >> 6;
-    double cs = 0.0, rsum = 0.0, mx = 0.0;
+    double csum = 0.0, rsum = 0.0, mx = 0.0;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const double a = fabs(static_cast<double>(wf[(qtr * 16 + k) * 65 + c]));
-      cs += a;
-      mx = fmax(mx, a);
-      rsum += fabs(static_cast<double>(wf[c * 65 + qtr * 16 + k]));
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const float4 a = *reinterpret_cast<const float4*>(&wcol[c * kWp + qtr * 16 + 4 * k4]);
+      const float4 r = *reinterpret_cast<const float4*>(&wrow[c * kWp + qtr * 16 + 4 * k4]);
+      const double a0 = fabs(static_cast<double>(a.x)), a1 = fabs(static_cast<double>(a.y));
+      const double a2 = fabs(static_cast<double>(a.z)), a3 = fabs(static_cast<double>(a.w));
+      csum += (a0 + a1) + (a2 + a3);
+      mx = fmax(mx, fmax(fmax(a0, a1), fmax(a2, a3)));
+      rsum += (fabs(static_cast<double>(r.x)) + fabs(static_cast<double>(r.y))) +
+              (fabs(static_cast<double>(r.z)) + fabs(static_cast<double>(r.w)));
     }
-    red[0][qtr][c] = cs;
+    red[0][qtr][c] = csum;
     red[1][qtr][c] = rsum;
     red[2][qtr][c] = mx;
   }
   __syncthreads();
-  if (wv == 0) {
-    double cs = red[0][0][ln] + red[0][1][ln] + red[0][2][ln] + red[0][3][ln];
-    double rsum = red[1][0][ln] + red[1][1][ln] + red[1][2][ln] + red[1][3][ln];
-    double mx = fmax(fmax(red[2][0][ln], red[2][1][ln]), fmax(red[2][2][ln], red[2][3][ln]));
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      cs = fmax(cs, __shfl_xor(cs, off));
-      rsum = fmax(rsum, __shfl_xor(rsum, off));
-      mx = fmax(mx, __shfl_xor(mx, off));
-    }
+  if (cs == 0) {
+    const double csum = wave_max_nonneg_f64(red[0][0][ln] + red[0][1][ln] + red[0][2][ln] + red[0][3][ln]);
+    const double rsum = wave_max_nonneg_f64(red[1][0][ln] + red[1][1][ln] + red[1][2][ln] + red[1][3][ln]);
+    const double mx =
+        wave_max_nonneg_f64(fmax(fmax(red[2][0][ln], red[2][1][ln]), fmax(red[2][2][ln], red[2][3][ln])));
     if (ln == 0) {
-      s_alpha = static_cast<float>(1.0 / (cs * rsum));
+      s_alpha = static_cast<float>(1.0 / (csum * rsum));
       s_wmax = static_cast<float>(mx);
     }
   }
@@ -224,95 +207,113 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
   const float alpha = s_alpha;
   if (tid == 0 && alpha_out) alpha_out[g] = alpha;
 
-  // W fragments of this wave's row strip (W is the A operand of every product with W).
-  Frags<1, KC> fw;
+  // W^T as the B operand of B_k = A_k W^T: chunk c, lane (g, t) holds W^T rows (K) 32c + 4g .. +3 and
+  // 32c + 16 + 4g .. +3 of column col, i.e. W[col][K].
+  half8 wth[KC], wtl[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
-    const int i = rs * 16 + (ln & 15);
-    const int k0 = c * 32 + 8 * (ln >> 4);
+    const float4 a = *reinterpret_cast<const float4*>(&wrow[col * kWp + 32 * c + 4 * gq]);
+    const float4 b = *reinterpret_cast<const float4*>(&wrow[col * kWp + 32 * c + 16 * (ST >= 2) + 4 * gq]);
+    split_chunk(act ? f32x4{a.x, a.y, a.z, a.w} : f32x4{0.f, 0.f, 0.f, 0.f},
+                (act && ST >= 2) ? f32x4{b.x, b.y, b.z, b.w} : f32x4{0.f, 0.f, 0.f, 0.f}, one, wth[c], wtl[c]);
+  }
+  // The kernel carries -A and -B (see below). -A_0 = -X_0^T = -alpha W, times 2^-ex: lane (g, t) of tile p holds
+  // rows 16p + 4g .. +3 of column col.
+  int ex = store_exp(alpha * s_wmax);
+  f32x4 ax[NT];
+  {
+    const float s0 = act ? -alpha * ldexpf(1.f, -ex) : 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      _Float16 h, l;
-      split_f16(doT ? wf[i * 65 + k0 + e] : 0.f, h, l);
-      fw.h[0][c][e] = h;
-      fw.l[0][c][e] = l;
+    for (int p = 0; p < NT; ++p) {
+      const float4 w = *reinterpret_cast<const float4*>(&wcol[col * kWp + 16 * p + 4 * gq]);
+      ax[p] = f32x4{w.x, w.y, w.z, w.w} * s0;
     }
   }
-  // Lane placement of the wave's tile b: rows row_i0() .. +3 of column col_j(b).
-  auto col_j = [&](int b) { return (c0 + b) * 16 + (ln & 15); };
-  auto row_i0 = [&]() { return rs * 16 + 4 * (ln >> 4); };
-  // 2 on the diagonal of the m x m block, 0 elsewhere (padding included); whether an entry is inside the block
-  auto two_i = [&](int b, int r) { return (row_i0() + r == col_j(b) && col_j(b) < m) ? 2.f : 0.f; };
-  auto inside = [&](int b, int r) { return row_i0() + r < m && col_j(b) < m; };
-  f32x4 accT[1][CS], accX[1][CS];
+  // X_k = -(the strip)^T to global memory: row col, columns 16p + 4g .. +3.
+  auto store_x = [&](float* __restrict__ dst) {
+    if (!act || col >= m) return;
+    const float s = -ldexpf(1.f, ex);
 #pragma unroll
-  for (int b = 0; b < CS; ++b)
+    for (int p = 0; p < NT; ++p)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) accX[0][b][r] = doX ? alpha * wf[col_j(b) * 65 + row_i0() + r] : 0.f;  // X_0
-  __syncthreads();  // wf (inside sU[1]) is dead after this point
-  if constexpr (ST == 1) {
-    for (int q = tid; q < NZ; q += NTH) reinterpret_cast<uint4*>(&sU[1])[q] = zero4;
-  }
-
-  // Split stores of the wave's tiles into a by-columns buffer (8-byte writes).
-  auto put_cols = [&](SplitMat& M, const f32x4 v[1][CS], float s) {
-#pragma unroll
-    for (int b = 0; b < CS; ++b) {
-      half4 h, l;
-      split_scaled4(v[0][b], s, h, l);
-      put_t4(M, col_j(b), row_i0(), h, l);
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * p + 4 * gq + r;
+        if (j < m) dst[static_cast<size_t>(col) * m + j] = ax[p][r] * s;
+      }
   };
-  // put_cols that also returns the largest |v| (before scaling).
-  auto put_cols_max = [&](SplitMat& M, const f32x4 v[1][CS], float s) {
+  auto xs_slot = [&](int k) { return xs + (static_cast<size_t>(g) * (iters + 1) + k) * mm; };
+  if (xs) store_x(xs_slot(0));
+  __syncthreads();  // W and W^T (inside sU) are dead after this point
+
+  // Keep the strip's scale near 2^12: its largest entry (returned, wave-uniform, times 2^-ex), then, rarely, one
+  // multiply per entry.
+  auto rescale = [&]() {
     float lm = 0.f;
 #pragma unroll
-    for (int b = 0; b < CS; ++b) {
-      const f32x4 t = v[0][b];
-      lm = fmaxf(lm, fmaxf(fmaxf(fabsf(t[0]), fabsf(t[1])), fmaxf(fabsf(t[2]), fabsf(t[3]))));
-      half4 h, l;
-      split_scaled4(t, s, h, l);
-      put_t4(M, col_j(b), row_i0(), h, l);
+    for (int p = 0; p < NT; ++p)
+      lm = fmaxf(lm, fmaxf(fmaxf(fabsf(ax[p][0]), fabsf(ax[p][1])), fmaxf(fabsf(ax[p][2]), fabsf(ax[p][3]))));
+    lm = wave_max_nonneg(lm);
+    if (lm >= 16384.f || (lm < 256.f && lm > 0.f)) {
+      const int d = exp_of(lm) - 12;
+      const float s = ldexpf(1.f, -d);
+#pragma unroll
+      for (int p = 0; p < NT; ++p) ax[p] *= s;
+      ex += d;
+      lm *= s;
     }
     return lm;
   };
-  // T = s v and U = 2I - s v from the same tiles (padding rows and columns of T are exact zeros, so U is zero
-  // there); U alone when T is not needed.
-  auto put_tu = [&](SplitMat* Mt, SplitMat& Mu, const f32x4 v[1][CS], float s) {
+
+  f32x4 bt[NT];            // -B_k
+  half8 bth[KC], btl[KC];  // its split: the B operand of the T product and, stored, the A operand of both
+  // Split -B into bth/btl and store it (by columns) into M.
+  auto put_b = [&](RegSplit& M) {
 #pragma unroll
-    for (int b = 0; b < CS; ++b) {
-      f32x4 t, u;
+    for (int c = 0; c < KC; ++c)
+      split_chunk(bt[2 * c], (ST >= 2) ? bt[2 * c + 1] : f32x4{0.f, 0.f, 0.f, 0.f}, one, bth[c], btl[c]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        t[r] = v[0][b][r] * s;
-        u[r] = two_i(b, r) - t[r];
-      }
-      half4 h, l;
-      if (Mt) {
-        split4(t, h, l);
-        put_t4(*Mt, col_j(b), row_i0(), h, l);
-      }
-      split4(u, h, l);
-      put_t4(Mu, col_j(b), row_i0(), h, l);
+    for (int p = 0; p < NT; ++p) {
+      const int c = p >> 1, o = (p & 1) * 4;
+      *reinterpret_cast<half4*>(&M.hi[lane_w + 16 * p]) = half4{bth[c][o], bth[c][o + 1], bth[c][o + 2], bth[c][o + 3]};
+      *reinterpret_cast<half4*>(&M.lo[lane_w + 16 * p]) = half4{btl[c][o], btl[c][o + 1], btl[c][o + 2], btl[c][o + 3]};
     }
   };
-  // Iterate k to the saved-iterates buffer, from the wave's tiles.
-  auto put_xs = [&](int k, const f32x4 v[1][CS], float s) {
-    float* xg = xs + (static_cast<size_t>(g) * (iters + 1) + k) * mm;
+
+  // -B_k = (-A_k) W^T into bt: -A_k goes through sX with one block-wide exponent eb, the product comes back
+  // times 2^-eb.
+  auto form_t = [&]() {
+    if (act) s_part[cs] = rescale() * ldexpf(1.f, ex);
+    __syncthreads();
+    float bm = s_part[0];
 #pragma unroll
-    for (int b = 0; b < CS; ++b)
+    for (int w = 1; w < ST; ++w) bm = fmaxf(bm, s_part[w]);
+    const int eb = store_exp(fminf(bm, 3.0e38f));
+    if (act) {
+      const float s = ldexpf(1.f, ex - eb);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (inside(b, r)) xg[(row_i0() + r) * m + col_j(b)] = v[0][b][r] * s;
-  };
-  // W * B over the wave's tiles, W's fragments from registers.
-  auto mma_w = [&](const SplitMat& B, f32x4 acc[1][CS]) {
-    Frags<CS, KC> fb;
+      for (int p = 0; p < NT; ++p) {
+        half8 h, l;
+        split_chunk(ax[p] * s, ax[p] * s, one, h, l);
+        *reinterpret_cast<half4*>(&sX.hi[lane_w + 16 * p]) = half4{h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<half4*>(&sX.lo[lane_w + 16 * p]) = half4{l[0], l[1], l[2], l[3]};
+      }
+    }
+    __syncthreads();
+    if (act) {
+      half8 ah[NT][KC], al[NT][KC];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) load_chunk_b<CS, KC>(B, c0, ln, c, fb);
-    zero_acc<1, CS>(acc);
+      for (int c = 0; c < KC; ++c)
 #pragma unroll
-    for (int c = 0; c < KC; ++c) mma_chunk<1, CS, KC>(fw, fb, acc, c);
+        for (int p = 0; p < NT; ++p) load_rows<ST>(sX, lane_r, c, p, ah[p][c], al[p][c]);
+      const float us = ldexpf(1.f, eb);
+#pragma unroll
+      for (int p = 0; p < NT; ++p) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) acc = mma_split3(ah[p][c], al[p][c], wth[c], wtl[c], acc);
+        bt[p] = acc * us;
+      }
+    }
   };
 
   // The exact Newton-Schulz step X_{k+1} = X_k (2I - W X_k) equals, for T_k = W X_k, the pair
@@ -324,164 +325,110 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
   // starting from T = W X formed afresh (the mismatch stays below 2^kPairRun times the rounding of one split
   // product, 2^-22), and the last step is the exact update from X_{K-1}, which squares what is left; the result
   // then tracks the exact-step iteration to rounding.
-  int e_cur = store_exp(alpha * s_wmax);  // storage exponent of the iterate in sX[cur]; X_0's max is alpha max|W|
-  if (doX) {
-    put_cols(sX[0], accX, ldexpf(1.f, -e_cur));
-    if (xs) put_xs(0, accX, 1.f);
-  }
-  __syncthreads();
-
-  // Segment start at step k: T_k = W X_k (and U_k) into the buffers of parity k & 1, which no wave reads now.
+  //
+  // Transposed (A = X^T, B = T^T), the pair is A' = 2A - B A and B' = 2B - B B, and with the negated matrices
+  // that the kernel carries, -A' = 2 (-A) + (-B)(-A) and -B' = 2 (-B) + (-B)(-B): each product starts from twice
+  // the carried strip (exact in fp32) and adds the stored split of -B times the strip's own split. No 2I term is
+  // formed (the identity enters through the 2 (-A) start), and the stored matrix is the split the T product
+  // uses as its B operand anyway.
+  //
+  // Segment start at step k: -B_k = -(W X_k)^T, stored into the buffer of parity k & 1, which no wave reads now.
   auto resync = [&](int k) {
-    const int cur = k & 1;
-    if (doT) {
-      mma_w(sX[cur], accT);
-      put_tu(&sT[cur], sU[cur], accT, ldexpf(1.f, e_cur));
-    }
+    form_t();
+    if (act) put_b(sU[k & 1]);
     __syncthreads();
   };
 
-  int e_next = e_cur;
   // One pair step; the buffer parity is a template constant so that every LDS address is a fixed offset.
-  // last: the step ends a segment, so it produces only X_{k+1} (the next segment forms T afresh).
+  // last: the step ends a segment (or is the exact last step), so it forms only X_{k+1}.
+  // Order: the first chunk's reads, the scale check and split of the A strip (while they are in flight), the
+  // second chunk's reads, then the products chunk by chunk, T before X, and the T epilogue.
   auto step = [&](auto parity, auto last, int k) __attribute__((always_inline)) {
     constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
     constexpr bool kLast = decltype(last)::value;
-    const float unscale = ldexpf(1.f, e_cur);
-    const bool wt = doT && !kLast;
-    if (wt || doX) {
-      // every read of both chunks is issued before the first MFMA, so chunk 0's MFMAs overlap chunk 1's reads
-      Frags<CS, KC> fu;
-      Frags<1, KC> ft, fx;
+    if (act) {
+      half8 uh[NT][KC], ul[NT][KC];
+#pragma unroll
+      for (int p = 0; p < NT; ++p) load_rows<ST>(sU[cur], lane_r, 0, p, uh[p][0], ul[p][0]);
+      __builtin_amdgcn_sched_barrier(0);
+      rescale();
+      half8 bxh[KC], bxl[KC];
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        split_chunk(ax[2 * c], (ST >= 2) ? ax[2 * c + 1] : f32x4{0.f, 0.f, 0.f, 0.f}, one, bxh[c], bxl[c]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 1; c < KC; ++c)
+#pragma unroll
+        for (int p = 0; p < NT; ++p) load_rows<ST>(sU[cur], lane_r, c, p, uh[p][c], ul[p][c]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int p = 0; p < NT; ++p) {
+        if constexpr (!kLast) bt[p] += bt[p];
+        ax[p] += ax[p];
+      }
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        load_chunk_b<CS, KC>(sU[cur], c0, ln, c, fu);
-        if (wt) load_chunk_a<1, KC>(sT[cur], rs, ln, c, ft);
-        if (doX) load_chunk_a<1, KC>(sX[cur], rs, ln, c, fx);
-      }
-      if (wt) {
-        zero_acc<1, CS>(accT);
+        if constexpr (!kLast) {
 #pragma unroll
-        for (int c = 0; c < KC; ++c) mma_chunk<1, CS, KC>(ft, fu, accT, c);  // T_{k+1} = T_k U_k
-      }
-      if (doX) {
-        zero_acc<1, CS>(accX);
+          for (int p = 0; p < NT; ++p) bt[p] = mma_split3(uh[p][c], ul[p][c], bth[c], btl[c], bt[p]);
+        }
 #pragma unroll
-        for (int c = 0; c < KC; ++c) mma_chunk<1, CS, KC>(fx, fu, accX, c);  // X_{k+1} = X_k U_k, times 2^-e_cur
+        for (int p = 0; p < NT; ++p) ax[p] = mma_split3(uh[p][c], ul[p][c], bxh[c], bxl[c], ax[p]);
       }
-      if (wt) put_tu(&sT[nxt], sU[nxt], accT, 1.f);
-      if (doX) {
-        float lmax = put_cols_max(sX[nxt], accX, ldexpf(1.f, e_cur - e_next));
-        if (xs) put_xs(k + 1, accX, unscale);
-        lmax = wave_max_nonneg(lmax) * unscale;
-        if (ln == 0) atomicMax(&s_max[k % 3], __float_as_uint(lmax));
-      }
+      if constexpr (!kLast) put_b(sU[nxt]);
+      if (xs) store_x(xs_slot(k + 1));
     }
-    if (tid == 0) s_max[(k + 1) % 3] = 0u;
     __syncthreads();
-    const float mx = __uint_as_float(s_max[k % 3]);
-    if (mx >= ldexpf(1.f, e_next + kRestoreExp) || !(mx < 3.0e38f)) {
-      // Rare: the iterate grew past the headroom of its exponent (or is not finite); store it again.
-      const int e_new = store_exp(fminf(mx, 3.0e38f));
-      if (doX) put_cols(sX[nxt], accX, ldexpf(1.f, e_cur - e_new));
-      e_next = e_new;
-      __syncthreads();
-    }
-    e_cur = e_next;
-    e_next = store_exp(mx);
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using Mid = std::integral_constant<bool, false>;
   using End = std::integral_constant<bool, true>;
-  for (int k = 0; k + 1 < iters;) {
-    resync(k);
-    const int end = min(k + kPairRun, iters - 1);  // pair steps k .. end - 1; step K - 1 is the exact one
-    for (; k < end; ++k) {
-      const bool lst = k + 1 == end;
-      if (k & 1) {
-        if (lst) step(P1{}, End{}, k); else step(P1{}, Mid{}, k);
-      } else {
-        if (lst) step(P0{}, End{}, k); else step(P0{}, Mid{}, k);
-      }
+  auto seg_start = [&](int k) { return k % kPairRun == 0 || k == iters - 1; };
+  for (int k = 0; k < iters; ++k) {
+    if (seg_start(k)) resync(k);
+    const bool lst = k == iters - 1 || seg_start(k + 1);
+    if (k & 1) {
+      if (lst) step(P1{}, End{}, k); else step(P1{}, Mid{}, k);
+    } else {
+      if (lst) step(P0{}, End{}, k); else step(P0{}, Mid{}, k);
     }
   }
 
-  // Final exact step (iters >= 1): X_K = X_{K-1} (2I - W X_{K-1}), with X_{K-1} in sX[fin]. The U buffer of that
-  // parity was neither written nor read by the last pair step.
-  const int fin = (iters >= 1) ? ((iters - 1) & 1) : 0;
-  float out_unscale = 1.f;
-  if (iters >= 1) {
-    const float unscale = ldexpf(1.f, e_cur);
-    if (doT) {
-      mma_w(sX[fin], accT);
-      put_tu(nullptr, sU[fin], accT, unscale);
-    }
-    __syncthreads();
-    if (doX) {
-      Frags<CS, KC> fu;
-      Frags<1, KC> fx;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        load_chunk_b<CS, KC>(sU[fin], c0, ln, c, fu);
-        load_chunk_a<1, KC>(sX[fin], rs, ln, c, fx);
-      }
-      zero_acc<1, CS>(accX);
-#pragma unroll
-      for (int c = 0; c < KC; ++c) mma_chunk<1, CS, KC>(fx, fu, accX, c);
-    }
-    out_unscale = unscale;
-  }  // with no step accX still holds X_0
-  if (doX) {
-    if (xs && iters >= 1) put_xs(iters, accX, out_unscale);
-    float* xo = Xout + g * mm;
-#pragma unroll
-    for (int b = 0; b < CS; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (inside(b, r)) xo[(row_i0() + r) * m + col_j(b)] = accX[0][b][r] * out_unscale;
-  }
+  store_x(Xout + g * mm);
 
   if (resid) {
-    // ||W X_K - I||_F with the same split products: X_K goes through LDS once more.
-    __syncthreads();  // every read of the buffers below is done
-    const int rb = fin ^ 1;
-    // accX * out_unscale is X_K; store it with the exponent of the last iterate so the fp16 halves stay in range
-    const float st_scale = (iters >= 1) ? 1.f : ldexpf(1.f, -e_cur);
-    const float ru = out_unscale / st_scale;
-    if (doX) put_cols(sX[rb], accX, st_scale);
-    __syncthreads();
+    // ||W X_K - I||_F with the same split products: -(W X_K)^T through the segment-start path.
+    form_t();
     double ss = 0.0;
-    if (doT) {
-      mma_w(sX[rb], accT);
+    if (act) {
 #pragma unroll
-      for (int b = 0; b < CS; ++b)
+      for (int p = 0; p < NT; ++p)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (inside(b, r)) {
-            const double e2 = static_cast<double>(accT[0][b][r] * ru) - (row_i0() + r == col_j(b) ? 1.0 : 0.0);
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * p + 4 * gq + r;
+          if (i < m && col < m) {
+            const double e2 = -static_cast<double>(bt[p][r]) - (i == col ? 1.0 : 0.0);
             ss += e2 * e2;
           }
+        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    if (ln == 0) red_res[wv] = ss;
+    __syncthreads();  // every read of s_part by form_t is done
+    if (ln == 0) red[0][0][cs] = ss;
     __syncthreads();
-    if (tid == 0) {
-      double tot = 0.0;
-      for (int q = 0; q < 8; ++q) tot += red_res[q];
-      resid[g] = static_cast<float>(sqrt(tot));
-    }
+    if (tid == 0) resid[g] = static_cast<float>(sqrt(red[0][0][0] + red[0][0][1] + red[0][0][2] + red[0][0][3]));
   }
 }
 
-template <int ST, int KC>
-__global__ __launch_bounds__(512) void k_ns_small(const float* __restrict__ We, float* __restrict__ Xout,
-                                                  float* __restrict__ xs, float* __restrict__ alpha_out,
-                                                  float* __restrict__ resid, int m, int iters) {
-  ns_small_block<ST, KC>(static_cast<int>(blockIdx.x), We, Xout, xs, alpha_out, resid, m, iters);
+template <int ST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_ns_small(
+    const float* __restrict__ We, float* __restrict__ Xout, float* __restrict__ xs, float* __restrict__ alpha_out,
+    float* __restrict__ resid, int m, int iters) {
+  ns_small_block<ST>(static_cast<int>(blockIdx.x), We, Xout, xs, alpha_out, resid, m, iters);
 }
-
 // =====================================================================================================
 // Newton-Schulz with side work. The m <= 64 solver occupies one CU per slice for its whole chain of dependent
 // steps while the rest of the chip would idle, and a second stream costs more in cross-queue synchronisation than
@@ -489,15 +436,15 @@ __global__ __launch_bounds__(512) void k_ns_small(const float* __restrict__ We, 
 // S = C_K^T V, each one (slice, 16-landmark tile, 16-channel tile) of S over all N tokens. No block of this launch
 // waits for another: a cross-XCD hand-off of partial sums needs device-scope release and acquire fences, and
 // on this chip those write back and invalidate a whole L2, which costs more than the solver itself.
-// Each block holds the solver's LDS (one block per CU); the tiles fill the CUs the solver leaves free and finish
-// inside the solver's time.
+// Each block holds the solver's LDS (about 67 KB, so at most two blocks share a CU); the tiles fill the CUs the
+// solver leaves free and finish inside the solver's time.
 // =====================================================================================================
 
 // One S tile by one block of kSideWaves waves (the solver's block size). Wave w sums a contiguous range of 16-token
 // groups on fp32 MFMA (A = C_K, landmark-major, B = V): in group q, lane (i, k) feeds landmark i and channel i of
 // the tile with tokens 16q + 4k + u at k-step u, loaded from global memory straight into the MFMA operand layout.
 // The wave tiles are then summed in LDS in wave order, so the result does not depend on timing.
-constexpr int kSideWaves = 8;
+constexpr int kSideWaves = 4;
 
 template <typename T, int D>
 __device__ __forceinline__ void ckv_tile_block(int blk, const float* __restrict__ C, const T* __restrict__ V,
@@ -566,14 +513,14 @@ __device__ __forceinline__ void ckv_tile_block(int blk, const float* __restrict_
   }
 }
 
-template <typename T, int D, int ST, int KC>
-__global__ __launch_bounds__(512) void k_ns_side(const float* __restrict__ We, float* __restrict__ Xout,
+template <typename T, int D, int ST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_ns_side(const float* __restrict__ We, float* __restrict__ Xout,
                                                  float* __restrict__ xs, float* __restrict__ alpha_out, int m,
                                                  int iters, int N, int G, const float* __restrict__ CK,
                                                  const T* __restrict__ V, float* __restrict__ S) {
   const int b = static_cast<int>(blockIdx.x);
   if (b < G) {
-    ns_small_block<ST, KC>(b, We, Xout, xs, alpha_out, nullptr, m, iters);
+    ns_small_block<ST>(b, We, Xout, xs, alpha_out, nullptr, m, iters);
     return;
   }
   // The S tiles start at the first multiple of 8 after the solver blocks (the blocks in between exit at once), so
@@ -596,15 +543,15 @@ static void ns_side_st(const Shape& s, const float* We, float* X, float* xs, flo
                        const T* V, float* S, hipStream_t st) {
   const int blocks = ((s.G + 7) & ~7) + s.G * ((s.m + 15) / 16 * (D / 16));  // solver blocks, padding, S tiles
   const int nt = (s.m + 15) / 16;
-#define LF_NS_SIDE(ST_, KC_)                                                                                        \
-  hipLaunchKernelGGL((k_ns_side<T, D, ST_, KC_>), dim3(blocks), dim3(512), 0, st, We, X, xs, alpha, s.m, s.ns_iters, \
+#define LF_NS_SIDE(ST_)                                                                                        \
+  hipLaunchKernelGGL((k_ns_side<T, D, ST_>), dim3(blocks), dim3(256), 0, st, We, X, xs, alpha, s.m, s.ns_iters, \
                      s.N, s.G, CK, V, S)
   if (nt == 1)
-    LF_NS_SIDE(1, 1);
+    LF_NS_SIDE(1);
   else if (nt == 2)
-    LF_NS_SIDE(2, 1);
+    LF_NS_SIDE(2);
   else
-    LF_NS_SIDE(4, 2);
+    LF_NS_SIDE(4);
 #undef LF_NS_SIDE
 }
 
@@ -1053,13 +1000,13 @@ hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float
   const int m = s.m, K = s.ns_iters;
   if (m <= 64) {
     const int nt = (m + 15) / 16;
-    const dim3 grid(s.G), block(512);
+    const dim3 grid(s.G), block(256);
     if (nt == 1)
-      hipLaunchKernelGGL((k_ns_small<1, 1>), grid, block, 0, st, We, X, xs, alpha, resid, m, K);
+      hipLaunchKernelGGL((k_ns_small<1>), grid, block, 0, st, We, X, xs, alpha, resid, m, K);
     else if (nt == 2)
-      hipLaunchKernelGGL((k_ns_small<2, 1>), grid, block, 0, st, We, X, xs, alpha, resid, m, K);
+      hipLaunchKernelGGL((k_ns_small<2>), grid, block, 0, st, We, X, xs, alpha, resid, m, K);
     else
-      hipLaunchKernelGGL((k_ns_small<4, 2>), grid, block, 0, st, We, X, xs, alpha, resid, m, K);
+      hipLaunchKernelGGL((k_ns_small<4>), grid, block, 0, st, We, X, xs, alpha, resid, m, K);
     return hipGetLastError();
   }
   const int G = s.G, mp = ns_mp(m), nt = mp / kTile, nch = (m + kNsRows - 1) / kNsRows;
