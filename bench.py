@@ -1,8 +1,9 @@
 """Benchmark of the LaplacianFormer attention forward pass on one MI355X.
 
 A step is one lf_attn_fwd call over one batch of synthetic input that is already resident in HBM. The call is
-landmark pooling -> fused L1-distance+exp kernels -> Newton-Schulz pseudo-inverse -> C_K^T V -> landmark mix ->
-output GEMM with the depthwise-conv epilogue. The default workload is the PVT stage-1 shape: B=8, one head,
+landmark pooling -> fused L1-distance+exp kernel for C_K and W_eps -> Newton-Schulz pseudo-inverse, with
+S = C_K^T V and the C_Q distance pass in the same launch -> output GEMM (landmark mix P = X S inside it) with the
+depthwise-conv epilogue. The default workload is the PVT stage-1 shape: B=8, one head,
 56x56 tokens, d=64, r=8 (m=49), lambda=4, eps=1e-3, 12 Newton-Schulz steps, fp32.
 
 It prints one JSON line with the whole-job throughput (tokens/s = B*heads*N per step). It also prints the roofline
@@ -53,19 +54,22 @@ MFMA_F32_PEAK_TFLOPS = 157.3
 
 
 def laplace_source_hash():
-    """Hash of the distance kernel and its launcher as they stand in the source tree (None if not found)."""
+    """Hash of the distance kernel (its block, kernel wrapper and launcher) as it stands in the source tree (None if
+    not found)."""
     import hashlib
 
-    path = os.path.join(ROOT, "laplacian_nystr_vit_amd", "csrc", "lf_fwd.hip")
+    csrc = os.path.join(ROOT, "laplacian_nystr_vit_amd", "csrc")
     try:
-        src = open(path).read()
+        blk = open(os.path.join(csrc, "lf_laplace.h")).read()
+        src = open(os.path.join(csrc, "lf_fwd.hip")).read()
+        z = blk.index("template <int D>\nconstexpr int kLaplaceLds")
         a = src.index("__global__ __launch_bounds__(512) void k_laplace(")
-        b = src.index("// ====", a)
+        b = src.index("\n}\n", a)
         c = src.index("struct LaplacePlan {")
         e = src.index("static void laplace_d(", c)
     except (OSError, ValueError):
         return None
-    return hashlib.sha256((src[a:b] + src[c:e]).encode()).hexdigest()[:16]
+    return hashlib.sha256((blk[z:] + src[a:b] + src[c:e]).encode()).hexdigest()[:16]
 
 
 def load_traffic():

@@ -221,6 +221,13 @@ int fwd_launch(const lf_attn_params* p, const void* Q, const void* K, const void
   // (lf::out_fused_pays).
   const bool fuse_cq = !saved && !wh && p->kernel != LF_KERNEL_GAUSS && lf::out_fused_pays(s);
   LF_TRY(lf::launch_landmark_pool(s, Q, L, st));
+  if (!saved && !wh && p->kernel == LF_KERNEL_LAPLACE && lf::ns_laplace_supported(s) && lf::out_mix_supported(s)) {
+    // Inference: C_K and W_eps first, then the solver beside S = C_K^T V and the C_Q pass in one launch, then the
+    // output kernel (P = X S inside it).
+    LF_TRY(lf::launch_laplace(s, Q, K, L, CQ, CK, We, st, 6));
+    LF_TRY(lf::launch_ns_laplace(s, We, X, alpha, CK, V, S, Q, L, CQ, st));
+    return hip_status(lf::launch_out_mix(s, CQ, X, S, V, dwc_w, Y, st));
+  }
   if (p->kernel == LF_KERNEL_GAUSS)
     LF_TRY(lf::launch_gauss(s, Q, K, L, CQ, CK, We, st));
   else

@@ -9,6 +9,7 @@
 
 #include "lf_device.h"
 #include "lf_internal.h"
+#include "lf_laplace.h"
 #include "lf_split.h"
 
 namespace lf {
@@ -125,18 +126,22 @@ __device__ __forceinline__ double wave_max_nonneg_f64(double v) {
   return __longlong_as_double(static_cast<long long>(r));
 }
 
+// LDS of one solver block, in bytes: two split matrices, -B_k by step parity (at a segment start the idle one
+// carries -A_k), with W, W^T and the setup reductions inside them while the block starts up.
+constexpr int kNsSmallLds = 2 * static_cast<int>(sizeof(RegSplit));
+
 template <int ST>
-__device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ We, float* __restrict__ Xout,
-                                               float* __restrict__ xs, float* __restrict__ alpha_out,
-                                               float* __restrict__ resid, int m, int iters) {
+__device__ __forceinline__ void ns_small_block(char* __restrict__ lds, int g, const float* __restrict__ We,
+                                               float* __restrict__ Xout, float* __restrict__ xs,
+                                               float* __restrict__ alpha_out, float* __restrict__ resid, int m,
+                                               int iters) {
   constexpr int NT = ST;            // 16-row tiles per strip
   constexpr int KC = (ST + 1) / 2;  // 32-deep K chunks
   constexpr int NTH = 256;
-  // sU: -B_k split, by step parity; sX: -A_k split with one block-wide exponent at a segment start.
-  __shared__ RegSplit sU[2], sX;
-  __shared__ double red[3][4][64];
+  RegSplit* sU = reinterpret_cast<RegSplit*>(lds);
   __shared__ float s_alpha, s_wmax;
   __shared__ float s_part[4];
+  __shared__ double s_res[4];
   const int tid = threadIdx.x, ln = lane_id();
   const int cs = __builtin_amdgcn_readfirstlane(wave_id());  // the wave's column strip
   const bool act = cs < ST;
@@ -152,8 +157,10 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
   // W and W^T in fp32, zero-padded to 64 x 64, rows of kWp floats (four consecutive entries are one 16-byte
   // read), inside the U buffers, which no step uses yet. Every load of a thread is issued before any is used.
   constexpr int kWp = 68;
-  float* wrow = reinterpret_cast<float*>(&sU[0]);  // W[i][j] at i * kWp + j
-  float* wcol = wrow + 64 * kWp;                   // W[i][j] at j * kWp + i
+  float* wrow = reinterpret_cast<float*>(lds);  // W[i][j] at i * kWp + j
+  float* wcol = wrow + 64 * kWp;                // W[i][j] at j * kWp + i
+  double* red = reinterpret_cast<double*>(wcol + 64 * kWp);  // [3][4][64]: setup reductions
+  static_assert(2 * 64 * kWp * 4 + 3 * 4 * 64 * 8 <= kNsSmallLds, "setup area exceeds the solver's LDS");
   {
     const int mc = m - 1;
     float v[4096 / NTH];
@@ -188,16 +195,16 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
       rsum += (fabs(static_cast<double>(r.x)) + fabs(static_cast<double>(r.y))) +
               (fabs(static_cast<double>(r.z)) + fabs(static_cast<double>(r.w)));
     }
-    red[0][qtr][c] = csum;
-    red[1][qtr][c] = rsum;
-    red[2][qtr][c] = mx;
+    red[(0 * 4 + qtr) * 64 + c] = csum;
+    red[(1 * 4 + qtr) * 64 + c] = rsum;
+    red[(2 * 4 + qtr) * 64 + c] = mx;
   }
   __syncthreads();
   if (cs == 0) {
-    const double csum = wave_max_nonneg_f64(red[0][0][ln] + red[0][1][ln] + red[0][2][ln] + red[0][3][ln]);
-    const double rsum = wave_max_nonneg_f64(red[1][0][ln] + red[1][1][ln] + red[1][2][ln] + red[1][3][ln]);
+    const double csum = wave_max_nonneg_f64(red[(0 * 4 + 0) * 64 + ln] + red[(0 * 4 + 1) * 64 + ln] + red[(0 * 4 + 2) * 64 + ln] + red[(0 * 4 + 3) * 64 + ln]);
+    const double rsum = wave_max_nonneg_f64(red[(1 * 4 + 0) * 64 + ln] + red[(1 * 4 + 1) * 64 + ln] + red[(1 * 4 + 2) * 64 + ln] + red[(1 * 4 + 3) * 64 + ln]);
     const double mx =
-        wave_max_nonneg_f64(fmax(fmax(red[2][0][ln], red[2][1][ln]), fmax(red[2][2][ln], red[2][3][ln])));
+        wave_max_nonneg_f64(fmax(fmax(red[(2 * 4 + 0) * 64 + ln], red[(2 * 4 + 1) * 64 + ln]), fmax(red[(2 * 4 + 2) * 64 + ln], red[(2 * 4 + 3) * 64 + ln])));
     if (ln == 0) {
       s_alpha = static_cast<float>(1.0 / (csum * rsum));
       s_wmax = static_cast<float>(mx);
@@ -279,9 +286,9 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
     }
   };
 
-  // -B_k = (-A_k) W^T into bt: -A_k goes through sX with one block-wide exponent eb, the product comes back
-  // times 2^-eb.
-  auto form_t = [&]() {
+  // -B_k = (-A_k) W^T into bt: -A_k goes through tmp (a buffer that no wave reads once the first barrier is
+  // passed) with one block-wide exponent eb, and the product comes back times 2^-eb.
+  auto form_t = [&](RegSplit& tmp) {
     if (act) s_part[cs] = rescale() * ldexpf(1.f, ex);
     __syncthreads();
     float bm = s_part[0];
@@ -294,8 +301,8 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
       for (int p = 0; p < NT; ++p) {
         half8 h, l;
         split_chunk(ax[p] * s, ax[p] * s, one, h, l);
-        *reinterpret_cast<half4*>(&sX.hi[lane_w + 16 * p]) = half4{h[0], h[1], h[2], h[3]};
-        *reinterpret_cast<half4*>(&sX.lo[lane_w + 16 * p]) = half4{l[0], l[1], l[2], l[3]};
+        *reinterpret_cast<half4*>(&tmp.hi[lane_w + 16 * p]) = half4{h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<half4*>(&tmp.lo[lane_w + 16 * p]) = half4{l[0], l[1], l[2], l[3]};
       }
     }
     __syncthreads();
@@ -304,7 +311,7 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
 #pragma unroll
       for (int c = 0; c < KC; ++c)
 #pragma unroll
-        for (int p = 0; p < NT; ++p) load_rows<ST>(sX, lane_r, c, p, ah[p][c], al[p][c]);
+        for (int p = 0; p < NT; ++p) load_rows<ST>(tmp, lane_r, c, p, ah[p][c], al[p][c]);
       const float us = ldexpf(1.f, eb);
 #pragma unroll
       for (int p = 0; p < NT; ++p) {
@@ -334,7 +341,7 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
   //
   // Segment start at step k: -B_k = -(W X_k)^T, stored into the buffer of parity k & 1, which no wave reads now.
   auto resync = [&](int k) {
-    form_t();
+    form_t(sU[(k & 1) ^ 1]);  // the other buffer, last read by step k - 1, carries -A_k on the way
     if (act) put_b(sU[k & 1]);
     __syncthreads();
   };
@@ -400,7 +407,7 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
 
   if (resid) {
     // ||W X_K - I||_F with the same split products: -(W X_K)^T through the segment-start path.
-    form_t();
+    form_t(sU[0]);
     double ss = 0.0;
     if (act) {
 #pragma unroll
@@ -416,10 +423,10 @@ __device__ __forceinline__ void ns_small_block(int g, const float* __restrict__ 
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    __syncthreads();  // every read of s_part by form_t is done
-    if (ln == 0) red[0][0][cs] = ss;
     __syncthreads();
-    if (tid == 0) resid[g] = static_cast<float>(sqrt(red[0][0][0] + red[0][0][1] + red[0][0][2] + red[0][0][3]));
+    if (ln == 0) s_res[cs] = ss;
+    __syncthreads();
+    if (tid == 0) resid[g] = static_cast<float>(sqrt(s_res[0] + s_res[1] + s_res[2] + s_res[3]));
   }
 }
 
@@ -427,7 +434,8 @@ template <int ST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_ns_small(
     const float* __restrict__ We, float* __restrict__ Xout, float* __restrict__ xs, float* __restrict__ alpha_out,
     float* __restrict__ resid, int m, int iters) {
-  ns_small_block<ST>(static_cast<int>(blockIdx.x), We, Xout, xs, alpha_out, resid, m, iters);
+  __shared__ __attribute__((aligned(16))) char lds[kNsSmallLds];
+  ns_small_block<ST>(lds, static_cast<int>(blockIdx.x), We, Xout, xs, alpha_out, resid, m, iters);
 }
 // =====================================================================================================
 // Newton-Schulz with side work. The m <= 64 solver occupies one CU per slice for its whole chain of dependent
@@ -440,13 +448,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // solver leaves free and finish inside the solver's time.
 // =====================================================================================================
 
-// One S tile by one block of kSideWaves waves (the solver's block size). Wave w sums a contiguous range of 16-token
-// groups on fp32 MFMA (A = C_K, landmark-major, B = V): in group q, lane (i, k) feeds landmark i and channel i of
-// the tile with tokens 16q + 4k + u at k-step u, loaded from global memory straight into the MFMA operand layout.
-// The wave tiles are then summed in LDS in wave order, so the result does not depend on timing.
-constexpr int kSideWaves = 4;
+// One S tile by one block of NWV waves. Wave w sums a contiguous range of 16-token groups on fp32 MFMA (A = C_K,
+// landmark-major, B = V): in group q, lane (i, k) feeds landmark i and channel i of the tile with tokens
+// 16q + 4k + u at k-step u, loaded from global memory straight into the MFMA operand layout. The wave tiles are
+// then summed in LDS (sRed: NWV x 256 floats) in wave order, so the result does not depend on timing.
+constexpr int kSideWaves = 4;  // the solver's block size
 
-template <typename T, int D>
+template <typename T, int D, int NWV>
 __device__ __forceinline__ void ckv_tile_block(int blk, const float* __restrict__ C, const T* __restrict__ V,
                                                float* __restrict__ S, int N, int m, float* sRed) {
   constexpr int DT = D / 16;
@@ -459,7 +467,7 @@ __device__ __forceinline__ void ckv_tile_block(int blk, const float* __restrict_
   const bool lok = lt * 16 + i < m;
   const float* __restrict__ crow = C + (static_cast<size_t>(g) * m + (lok ? lt * 16 + i : 0)) * N;
   const T* __restrict__ vcol = V + static_cast<size_t>(g) * N * D + ct * 16 + i;
-  const int groups = (N + 15) / 16, gpw = (groups + kSideWaves - 1) / kSideWaves;
+  const int groups = (N + 15) / 16, gpw = (groups + NWV - 1) / NWV;
   const int q0 = min(groups, wv * gpw), q1 = min(groups, q0 + gpw);
   const int qf = max(q0, min(q1, N / 16));  // groups [q0, qf) have all 16 tokens in range
   const float amask = lok ? 1.f : 0.f;
@@ -508,9 +516,17 @@ __device__ __forceinline__ void ckv_tile_block(int blk, const float* __restrict_
     const int row = tid >> 4, col = tid & 15;
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < kSideWaves; ++w) sum += sRed[w * 256 + tid];
+    for (int w = 0; w < NWV; ++w) sum += sRed[w * 256 + tid];
     if (lt * 16 + row < m) S[(static_cast<size_t>(g) * m + lt * 16 + row) * D + ct * 16 + col] = sum;
   }
+}
+
+// Tile order of the S tiles of a launch (j < total): consecutive tiles are dealt to the 8 XCDs round-robin, so the
+// order is remapped to keep the tiles of one slice on one XCD: each slice's C_K rows and V columns are read by
+// several tiles, and one L2 then serves the repeats.
+__device__ __forceinline__ int ckv_tile_order(int j, int total) {
+  const int full = (total / 8) * 8;
+  return j < full ? (j % 8) * (full / 8) + j / 8 : j;
 }
 
 template <typename T, int D, int ST>
@@ -520,22 +536,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                                                  const T* __restrict__ V, float* __restrict__ S) {
   const int b = static_cast<int>(blockIdx.x);
   if (b < G) {
-    ns_small_block<ST>(b, We, Xout, xs, alpha_out, nullptr, m, iters);
+    __shared__ __attribute__((aligned(16))) char lds[kNsSmallLds];
+    ns_small_block<ST>(lds, b, We, Xout, xs, alpha_out, nullptr, m, iters);
     return;
   }
   // The S tiles start at the first multiple of 8 after the solver blocks (the blocks in between exit at once), so
-  // that tile j runs on XCD j % 8 (the hardware deals blocks to the 8 XCDs round-robin). Their order is remapped so
-  // that the tiles of one slice share an XCD: each slice's C_K rows and V columns are read by several tiles, and
-  // one L2 then serves the repeats.
+  // that tile j runs on XCD j % 8 (the hardware deals blocks to the 8 XCDs round-robin).
   const int s0 = (G + 7) & ~7;
   if (b < s0) return;
-  int j = b - s0;
-  {
-    const int total = static_cast<int>(gridDim.x) - s0, full = (total / 8) * 8;
-    if (j < full) j = (j % 8) * (full / 8) + j / 8;
-  }
+  const int j = ckv_tile_order(b - s0, static_cast<int>(gridDim.x) - s0);
   __shared__ float sRed[kSideWaves * 256];
-  ckv_tile_block<T, D>(j, CK, V, S, N, m, sRed);
+  ckv_tile_block<T, D, kSideWaves>(j, CK, V, S, N, m, sRed);
+}
+
+// =====================================================================================================
+// Newton-Schulz beside the S tiles and the C_Q distance pass (inference forward, Laplace kernel, m <= 64). C_Q is
+// needed only by the output kernel, so instead of running before the solver it runs in the solver's launch: after
+// the G solver blocks come the S = C_K^T V tiles (as in the launch above; C_K and W_eps come from the distance
+// launch before) and then the distance blocks for the rows of Q (four waves each, a quarter of the landmarks per
+// wave). All of them fill the CUs the solver leaves free and finish in its shadow. The three kinds of block share
+// one LDS allocation (the solver's 41 KB), so three blocks fit a CU.
+// =====================================================================================================
+template <typename T, int D, int ST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_ns_laplace(
+    const float* __restrict__ We, float* __restrict__ Xout, float* __restrict__ alpha_out, int m, int iters, int G,
+    const float* __restrict__ CK, const T* __restrict__ V, float* __restrict__ S, int nS, const T* __restrict__ Q,
+    const float* __restrict__ L, float* __restrict__ CQ, int N, int nlap, int tilesN, int lc, float scale) {
+  __shared__ __attribute__((aligned(16))) char lds[kNsSmallLds > kLaplaceLds<D> ? kNsSmallLds : kLaplaceLds<D>];
+  static_assert(kSideWaves * 256 * 4 <= kNsSmallLds, "S tile reduction exceeds the shared LDS");
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < G) {
+    ns_small_block<ST>(lds, b, We, Xout, nullptr, alpha_out, nullptr, m, iters);
+    return;
+  }
+  // each group of side blocks starts at a multiple of 8 (the blocks in between exit at once), so that side block j
+  // of a group runs on XCD j % 8
+  const int s0 = (G + 7) & ~7, s1 = s0 + ((nS + 7) & ~7);
+  if (b < s0) return;
+  if (b < s1) {
+    if (b - s0 < nS) ckv_tile_block<T, D, kSideWaves>(ckv_tile_order(b - s0, nS), CK, V, S, N, m, reinterpret_cast<float*>(lds));
+    return;
+  }
+  // (only rows of Q here: the W_eps and C_K outputs are never reached)
+  laplace_block<T, D>(reinterpret_cast<float*>(lds), b - s1, nlap, 4, Q, Q, L, CQ, CQ, const_cast<float*>(We), N, m,
+                      tilesN, 0, 0, 1, lc, scale, 0.f);
 }
 
 template <typename T, int D>
@@ -579,6 +623,51 @@ hipError_t launch_ns_side(const Shape& s, const float* We, float* X, float* xs, 
     ns_side_t<float>(s, We, X, xs, alpha, CK, V, S, st);
   return hipGetLastError();
 }
+
+bool ns_laplace_supported(const Shape& s) { return ns_side_supported(s); }
+
+template <typename T, int D>
+static void ns_laplace_st(const Shape& s, const float* We, float* X, float* alpha, const float* CK, const T* V,
+                          float* S, const T* Q, const float* L, float* CQ, hipStream_t st) {
+  const int tilesN = (s.N + 63) / 64, nlap = s.G * tilesN, lc = (s.m + 3) / 4;
+  const int nS = s.G * ((s.m + 15) / 16) * (D / 16);
+  const int blocks = ((s.G + 7) & ~7) + ((nS + 7) & ~7) + nlap;  // solver blocks, S tiles, C_Q distance blocks
+  const float scale = static_cast<float>(-1.4426950408889634 / static_cast<double>(s.lambda));
+  const int nt = (s.m + 15) / 16;
+#define LF_NS_LAP(ST_)                                                                                         \
+  hipLaunchKernelGGL((k_ns_laplace<T, D, ST_>), dim3(blocks), dim3(256), 0, st, We, X, alpha, s.m, s.ns_iters, \
+                     s.G, CK, V, S, nS, Q, L, CQ, s.N, nlap, tilesN, lc, scale)
+  if (nt == 1)
+    LF_NS_LAP(1);
+  else if (nt == 2)
+    LF_NS_LAP(2);
+  else
+    LF_NS_LAP(4);
+#undef LF_NS_LAP
+}
+
+template <typename T>
+static void ns_laplace_t(const Shape& s, const float* We, float* X, float* alpha, const float* CK, const void* V,
+                         float* S, const void* Q, const float* L, float* CQ, hipStream_t st) {
+  const T* v = static_cast<const T*>(V);
+  const T* q = static_cast<const T*>(Q);
+  switch (s.d) {
+    case 16: ns_laplace_st<T, 16>(s, We, X, alpha, CK, v, S, q, L, CQ, st); break;
+    case 32: ns_laplace_st<T, 32>(s, We, X, alpha, CK, v, S, q, L, CQ, st); break;
+    default: ns_laplace_st<T, 64>(s, We, X, alpha, CK, v, S, q, L, CQ, st); break;
+  }
+}
+
+hipError_t launch_ns_laplace(const Shape& s, const float* We, float* X, float* alpha, const float* CK, const void* V,
+                             float* S, const void* Q, const float* L, float* CQ, hipStream_t st) {
+  if (!ns_laplace_supported(s)) return hipErrorInvalidValue;
+  if (s.dtype == 1)
+    ns_laplace_t<bf16_t>(s, We, X, alpha, CK, V, S, Q, L, CQ, st);
+  else
+    ns_laplace_t<float>(s, We, X, alpha, CK, V, S, Q, L, CQ, st);
+  return hipGetLastError();
+}
+
 
 // =====================================================================================================
 // m > 64: the m x m matrices do not fit one CU's LDS, so every product is a batched launch over 32 x 32 output
