@@ -221,26 +221,26 @@ int fwd_launch(const lf_attn_params* p, const void* Q, const void* K, const void
   // (lf::out_fused_pays).
   const bool fuse_cq = !saved && !wh && p->kernel != LF_KERNEL_GAUSS && lf::out_fused_pays(s);
   LF_TRY(lf::launch_landmark_pool(s, Q, L, st));
-  if (!saved && !wh && p->kernel == LF_KERNEL_LAPLACE && lf::ns_laplace_supported(s) && lf::out_mix_supported(s)) {
-    // Inference: C_K and W_eps first, then the solver beside S = C_K^T V and the C_Q pass in one launch, then the
-    // output kernel (P = X S inside it).
+  if (p->kernel == LF_KERNEL_LAPLACE && !fuse_cq && lf::ns_laplace_supported(s)) {
+    // C_K and W_eps first, then the solver beside S = C_K^T V and the C_Q pass in one launch.
     LF_TRY(lf::launch_laplace(s, Q, K, L, CQ, CK, We, st, 6));
-    LF_TRY(lf::launch_ns_laplace(s, We, X, alpha, CK, V, S, Q, L, CQ, st));
-    return hip_status(lf::launch_out_mix(s, CQ, X, S, V, dwc_w, Y, st));
-  }
-  if (p->kernel == LF_KERNEL_GAUSS)
-    LF_TRY(lf::launch_gauss(s, Q, K, L, CQ, CK, We, st));
-  else
-    LF_TRY(lf::launch_laplace(s, Q, K, L, CQ, CK, We, st, fuse_cq ? 6 : 7));
-  if (wh) LF_TRY(lf::launch_whiten_stats(s, CQ, mu, rstd, st));
-  // The solver stays on the caller's stream: a fork of it to the side stream, concurrent with the C_Q / C_K launch
-  // and S = C_K^T V, measured slower on every shape (the event hand-off costs more than the ~21 us solver hides).
-  if (lf::ns_side_supported(s)) {
-    // One launch: Newton-Schulz on G CUs, S = C_K^T V on the others.
-    LF_TRY(lf::launch_ns_side(s, We, X, xs, alpha, CK, V, S, st));
+    LF_TRY(lf::launch_ns_laplace(s, We, X, xs, alpha, CK, V, S, Q, L, CQ, st));
+    if (wh) LF_TRY(lf::launch_whiten_stats(s, CQ, mu, rstd, st));
   } else {
-    LF_TRY(lf::launch_ns(s, We, X, xs, alpha, nullptr, nstmp, st));
-    LF_TRY(lf::launch_ckv(s, CK, V, part, S, st));
+    if (p->kernel == LF_KERNEL_GAUSS)
+      LF_TRY(lf::launch_gauss(s, Q, K, L, CQ, CK, We, st));
+    else
+      LF_TRY(lf::launch_laplace(s, Q, K, L, CQ, CK, We, st, fuse_cq ? 6 : 7));
+    if (wh) LF_TRY(lf::launch_whiten_stats(s, CQ, mu, rstd, st));
+    // The solver stays on the caller's stream: a fork of it to the side stream, concurrent with the C_Q / C_K
+    // launch and S = C_K^T V, measured slower on every shape (the event hand-off costs more than the solver hides).
+    if (lf::ns_side_supported(s)) {
+      // One launch: Newton-Schulz on G CUs, S = C_K^T V on the others.
+      LF_TRY(lf::launch_ns_side(s, We, X, xs, alpha, CK, V, S, st));
+    } else {
+      LF_TRY(lf::launch_ns(s, We, X, xs, alpha, nullptr, nstmp, st));
+      LF_TRY(lf::launch_ckv(s, CK, V, part, S, st));
+    }
   }
   if (fuse_cq) {
     LF_TRY(lf::launch_mix(s, X, S, nullptr, P, nullptr, st));

@@ -58,11 +58,11 @@ hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float
 // Newton-Schulz (m <= 64) in one launch with S = C_K^T V computed in the CUs the solver leaves idle.
 // ns_side_supported: m <= 64, d in {16, 32, 64} and fewer slices than CUs.
 bool ns_side_supported(const Shape& s);
-// Newton-Schulz beside S = C_K^T V and the C_Q distance pass in one launch (inference, Laplace kernel; C_K and
-// W_eps from a prior distance launch over the K and landmark rows).
+// Newton-Schulz beside S = C_K^T V and the C_Q distance pass in one launch (Laplace kernel; C_K and W_eps from a
+// prior distance launch over the K and landmark rows). xs: saved iterates or null.
 bool ns_laplace_supported(const Shape& s);
-hipError_t launch_ns_laplace(const Shape& s, const float* We, float* X, float* alpha, const float* CK, const void* V,
-                             float* S, const void* Q, const float* L, float* CQ, hipStream_t st);
+hipError_t launch_ns_laplace(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
+                             const void* V, float* S, const void* Q, const float* L, float* CQ, hipStream_t st);
 hipError_t launch_ns_side(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
                           const void* V, float* S, hipStream_t st);
 

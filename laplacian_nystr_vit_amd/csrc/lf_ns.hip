@@ -550,8 +550,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 // =====================================================================================================
-// Newton-Schulz beside the S tiles and the C_Q distance pass (inference forward, Laplace kernel, m <= 64). C_Q is
-// needed only by the output kernel, so instead of running before the solver it runs in the solver's launch: after
+// Newton-Schulz beside the S tiles and the C_Q distance pass (Laplace kernel, m <= 64). C_Q is needed only after
+// the solver (by the whitening statistics and the output kernel), so instead of running before the solver it runs in the solver's launch: after
 // the G solver blocks come the S = C_K^T V tiles (as in the launch above; C_K and W_eps come from the distance
 // launch before) and then the distance blocks for the rows of Q (four waves each, a quarter of the landmarks per
 // wave). All of them fill the CUs the solver leaves free and finish in its shadow. The three kinds of block share
@@ -559,14 +559,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // =====================================================================================================
 template <typename T, int D, int ST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_ns_laplace(
-    const float* __restrict__ We, float* __restrict__ Xout, float* __restrict__ alpha_out, int m, int iters, int G,
-    const float* __restrict__ CK, const T* __restrict__ V, float* __restrict__ S, int nS, const T* __restrict__ Q,
+    const float* __restrict__ We, float* __restrict__ Xout, float* __restrict__ xs, float* __restrict__ alpha_out,
+    int m, int iters, int G, const float* __restrict__ CK, const T* __restrict__ V, float* __restrict__ S, int nS,
+    const T* __restrict__ Q,
     const float* __restrict__ L, float* __restrict__ CQ, int N, int nlap, int tilesN, int lc, float scale) {
   __shared__ __attribute__((aligned(16))) char lds[kNsSmallLds > kLaplaceLds<D> ? kNsSmallLds : kLaplaceLds<D>];
   static_assert(kSideWaves * 256 * 4 <= kNsSmallLds, "S tile reduction exceeds the shared LDS");
   const int b = static_cast<int>(blockIdx.x);
   if (b < G) {
-    ns_small_block<ST>(lds, b, We, Xout, nullptr, alpha_out, nullptr, m, iters);
+    ns_small_block<ST>(lds, b, We, Xout, xs, alpha_out, nullptr, m, iters);
     return;
   }
   // each group of side blocks starts at a multiple of 8 (the blocks in between exit at once), so that side block j
@@ -627,16 +628,16 @@ hipError_t launch_ns_side(const Shape& s, const float* We, float* X, float* xs, 
 bool ns_laplace_supported(const Shape& s) { return ns_side_supported(s); }
 
 template <typename T, int D>
-static void ns_laplace_st(const Shape& s, const float* We, float* X, float* alpha, const float* CK, const T* V,
-                          float* S, const T* Q, const float* L, float* CQ, hipStream_t st) {
+static void ns_laplace_st(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
+                          const T* V, float* S, const T* Q, const float* L, float* CQ, hipStream_t st) {
   const int tilesN = (s.N + 63) / 64, nlap = s.G * tilesN, lc = (s.m + 3) / 4;
   const int nS = s.G * ((s.m + 15) / 16) * (D / 16);
   const int blocks = ((s.G + 7) & ~7) + ((nS + 7) & ~7) + nlap;  // solver blocks, S tiles, C_Q distance blocks
   const float scale = static_cast<float>(-1.4426950408889634 / static_cast<double>(s.lambda));
   const int nt = (s.m + 15) / 16;
 #define LF_NS_LAP(ST_)                                                                                         \
-  hipLaunchKernelGGL((k_ns_laplace<T, D, ST_>), dim3(blocks), dim3(256), 0, st, We, X, alpha, s.m, s.ns_iters, \
-                     s.G, CK, V, S, nS, Q, L, CQ, s.N, nlap, tilesN, lc, scale)
+  hipLaunchKernelGGL((k_ns_laplace<T, D, ST_>), dim3(blocks), dim3(256), 0, st, We, X, xs, alpha, s.m,          \
+                     s.ns_iters, s.G, CK, V, S, nS, Q, L, CQ, s.N, nlap, tilesN, lc, scale)
   if (nt == 1)
     LF_NS_LAP(1);
   else if (nt == 2)
@@ -647,24 +648,24 @@ static void ns_laplace_st(const Shape& s, const float* We, float* X, float* alph
 }
 
 template <typename T>
-static void ns_laplace_t(const Shape& s, const float* We, float* X, float* alpha, const float* CK, const void* V,
-                         float* S, const void* Q, const float* L, float* CQ, hipStream_t st) {
+static void ns_laplace_t(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
+                         const void* V, float* S, const void* Q, const float* L, float* CQ, hipStream_t st) {
   const T* v = static_cast<const T*>(V);
   const T* q = static_cast<const T*>(Q);
   switch (s.d) {
-    case 16: ns_laplace_st<T, 16>(s, We, X, alpha, CK, v, S, q, L, CQ, st); break;
-    case 32: ns_laplace_st<T, 32>(s, We, X, alpha, CK, v, S, q, L, CQ, st); break;
-    default: ns_laplace_st<T, 64>(s, We, X, alpha, CK, v, S, q, L, CQ, st); break;
+    case 16: ns_laplace_st<T, 16>(s, We, X, xs, alpha, CK, v, S, q, L, CQ, st); break;
+    case 32: ns_laplace_st<T, 32>(s, We, X, xs, alpha, CK, v, S, q, L, CQ, st); break;
+    default: ns_laplace_st<T, 64>(s, We, X, xs, alpha, CK, v, S, q, L, CQ, st); break;
   }
 }
 
-hipError_t launch_ns_laplace(const Shape& s, const float* We, float* X, float* alpha, const float* CK, const void* V,
-                             float* S, const void* Q, const float* L, float* CQ, hipStream_t st) {
+hipError_t launch_ns_laplace(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
+                             const void* V, float* S, const void* Q, const float* L, float* CQ, hipStream_t st) {
   if (!ns_laplace_supported(s)) return hipErrorInvalidValue;
   if (s.dtype == 1)
-    ns_laplace_t<bf16_t>(s, We, X, alpha, CK, V, S, Q, L, CQ, st);
+    ns_laplace_t<bf16_t>(s, We, X, xs, alpha, CK, V, S, Q, L, CQ, st);
   else
-    ns_laplace_t<float>(s, We, X, alpha, CK, V, S, Q, L, CQ, st);
+    ns_laplace_t<float>(s, We, X, xs, alpha, CK, V, S, Q, L, CQ, st);
   return hipGetLastError();
 }
 
