@@ -126,6 +126,14 @@ __device__ __forceinline__ double wave_max_nonneg_f64(double v) {
   return __longlong_as_double(static_cast<long long>(r));
 }
 
+// Barrier that orders LDS accesses only: global stores (the saved iterates) stay in flight across it, since no
+// other wave of the block reads them.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // LDS of one solver block, in bytes: two split matrices, -B_k by step parity (at a segment start the idle one
 // carries -A_k), with W, W^T and the setup reductions inside them while the block starts up.
 constexpr int kNsSmallLds = 2 * static_cast<int>(sizeof(RegSplit));
@@ -236,21 +244,27 @@ __device__ __forceinline__ void ns_small_block(char* __restrict__ lds, int g, co
       ax[p] = f32x4{w.x, w.y, w.z, w.w} * s0;
     }
   }
-  // X_k = -(the strip)^T to global memory: row col, columns 16p + 4g .. +3.
+  // X_k = -(the strip)^T to global memory: row col, columns 16p + 4g .. +3 (one base address per lane; only a
+  // tile that reaches past column m - 1 needs a per-entry check).
   auto store_x = [&](float* __restrict__ dst) {
     if (!act || col >= m) return;
     const float s = -ldexpf(1.f, ex);
+    float* __restrict__ row = dst + static_cast<size_t>(col) * m + 4 * gq;
 #pragma unroll
-    for (int p = 0; p < NT; ++p)
+    for (int p = 0; p < NT; ++p) {
+      if (16 * p + 16 <= m) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * p + 4 * gq + r;
-        if (j < m) dst[static_cast<size_t>(col) * m + j] = ax[p][r] * s;
+        for (int r = 0; r < 4; ++r) row[16 * p + r] = ax[p][r] * s;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * p + 4 * gq + r < m) row[16 * p + r] = ax[p][r] * s;
       }
+    }
   };
   auto xs_slot = [&](int k) { return xs + (static_cast<size_t>(g) * (iters + 1) + k) * mm; };
   if (xs) store_x(xs_slot(0));
-  __syncthreads();  // W and W^T (inside sU) are dead after this point
+  barrier_lds();  // W and W^T (inside sU) are dead after this point
 
   // Keep the strip's scale near 2^12: its largest entry (returned, wave-uniform, times 2^-ex), then, rarely, one
   // multiply per entry.
@@ -290,7 +304,7 @@ __device__ __forceinline__ void ns_small_block(char* __restrict__ lds, int g, co
   // passed) with one block-wide exponent eb, and the product comes back times 2^-eb.
   auto form_t = [&](RegSplit& tmp) {
     if (act) s_part[cs] = rescale() * ldexpf(1.f, ex);
-    __syncthreads();
+    barrier_lds();
     float bm = s_part[0];
 #pragma unroll
     for (int w = 1; w < ST; ++w) bm = fmaxf(bm, s_part[w]);
@@ -305,7 +319,7 @@ __device__ __forceinline__ void ns_small_block(char* __restrict__ lds, int g, co
         *reinterpret_cast<half4*>(&tmp.lo[lane_w + 16 * p]) = half4{l[0], l[1], l[2], l[3]};
       }
     }
-    __syncthreads();
+    barrier_lds();
     if (act) {
       half8 ah[NT][KC], al[NT][KC];
 #pragma unroll
@@ -343,7 +357,7 @@ __device__ __forceinline__ void ns_small_block(char* __restrict__ lds, int g, co
   auto resync = [&](int k) {
     form_t(sU[(k & 1) ^ 1]);  // the other buffer, last read by step k - 1, carries -A_k on the way
     if (act) put_b(sU[k & 1]);
-    __syncthreads();
+    barrier_lds();
   };
 
   // One pair step; the buffer parity is a template constant so that every LDS address is a fixed offset.
@@ -386,7 +400,7 @@ __device__ __forceinline__ void ns_small_block(char* __restrict__ lds, int g, co
       if constexpr (!kLast) put_b(sU[nxt]);
       if (xs) store_x(xs_slot(k + 1));
     }
-    __syncthreads();
+    barrier_lds();
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
