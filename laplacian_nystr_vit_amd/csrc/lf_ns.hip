@@ -100,32 +100,6 @@ __device__ __forceinline__ void load_rows(const RegSplit& M, int lane_r, int c, 
   l = half8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
 }
 
-// Maximum over the wave of a non-negative double, returned wave-uniform (non-negative doubles order like their
-// bit patterns): DPP steps inside each row of 16 lanes on both halves, then the four row results.
-__device__ __forceinline__ double wave_max_nonneg_f64(double v) {
-  unsigned long long x = static_cast<unsigned long long>(__double_as_longlong(v));
-  auto dpp_max = [&](auto ctrl) {
-    constexpr int c = decltype(ctrl)::value;
-    const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), c, 0xf, 0xf, false));
-    const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(x >> 32), c, 0xf, 0xf, false));
-    const unsigned long long y = (static_cast<unsigned long long>(hi) << 32) | lo;
-    x = x > y ? x : y;
-  };
-  dpp_max(std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
-  dpp_max(std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
-  dpp_max(std::integral_constant<int, 0x124>{});  // row_ror:4
-  dpp_max(std::integral_constant<int, 0x128>{});  // row_ror:8
-  unsigned long long r = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(x), 16 * q));
-    const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(x >> 32), 16 * q));
-    const unsigned long long y = (static_cast<unsigned long long>(hi) << 32) | lo;
-    r = r > y ? r : y;
-  }
-  return __longlong_as_double(static_cast<long long>(r));
-}
-
 // Barrier that orders LDS accesses only: global stores (the saved iterates) stay in flight across it, since no
 // other wave of the block reads them.
 __device__ __forceinline__ void barrier_lds() {
@@ -148,7 +122,7 @@ __device__ __forceinline__ void ns_small_block(char* __restrict__ lds, int g, co
   constexpr int NTH = 256;
   RegSplit* sU = reinterpret_cast<RegSplit*>(lds);
   __shared__ float s_alpha, s_wmax;
-  __shared__ float s_part[4];
+  __shared__ int s_ex[4];
   __shared__ double s_res[4];
   const int tid = threadIdx.x, ln = lane_id();
   const int cs = __builtin_amdgcn_readfirstlane(wave_id());  // the wave's column strip
@@ -209,13 +183,18 @@ __device__ __forceinline__ void ns_small_block(char* __restrict__ lds, int g, co
   }
   __syncthreads();
   if (cs == 0) {
-    const double csum = wave_max_nonneg_f64(red[(0 * 4 + 0) * 64 + ln] + red[(0 * 4 + 1) * 64 + ln] + red[(0 * 4 + 2) * 64 + ln] + red[(0 * 4 + 3) * 64 + ln]);
-    const double rsum = wave_max_nonneg_f64(red[(1 * 4 + 0) * 64 + ln] + red[(1 * 4 + 1) * 64 + ln] + red[(1 * 4 + 2) * 64 + ln] + red[(1 * 4 + 3) * 64 + ln]);
-    const double mx =
-        wave_max_nonneg_f64(fmax(fmax(red[(2 * 4 + 0) * 64 + ln], red[(2 * 4 + 1) * 64 + ln]), fmax(red[(2 * 4 + 2) * 64 + ln], red[(2 * 4 + 3) * 64 + ln])));
+    // the sums in float64, their maxima over the 64 columns (rows) in float32: alpha then differs from the
+    // all-float64 value by at most a few units of 2^-24
+    auto sum4 = [&](int a) {
+      return red[(a * 4 + 0) * 64 + ln] + red[(a * 4 + 1) * 64 + ln] + red[(a * 4 + 2) * 64 + ln] + red[(a * 4 + 3) * 64 + ln];
+    };
+    const float cmax = wave_max_nonneg(static_cast<float>(sum4(0)));
+    const float rmax = wave_max_nonneg(static_cast<float>(sum4(1)));
+    const float mx = wave_max_nonneg(static_cast<float>(
+        fmax(fmax(red[8 * 64 + ln], red[9 * 64 + ln]), fmax(red[10 * 64 + ln], red[11 * 64 + ln]))));
     if (ln == 0) {
-      s_alpha = static_cast<float>(1.0 / (csum * rsum));
-      s_wmax = static_cast<float>(mx);
+      s_alpha = static_cast<float>(1.0 / (static_cast<double>(cmax) * static_cast<double>(rmax)));
+      s_wmax = mx;
     }
   }
   __syncthreads();
@@ -266,23 +245,23 @@ __device__ __forceinline__ void ns_small_block(char* __restrict__ lds, int g, co
   if (xs) store_x(xs_slot(0));
   barrier_lds();  // W and W^T (inside sU) are dead after this point
 
-  // Keep the strip's scale near 2^12: its largest entry (returned, wave-uniform, times 2^-ex), then, rarely, one
-  // multiply per entry.
+  // Keep the strip's scale near 2^12: while its largest entry (times 2^-ex) stays in [2^8, 2^14), which the lanes
+  // test on their own maxima with no cross-lane reduction, nothing happens; otherwise the exact maximum sets a
+  // fresh exponent (one multiply per entry).
   auto rescale = [&]() {
     float lm = 0.f;
 #pragma unroll
     for (int p = 0; p < NT; ++p)
       lm = fmaxf(lm, fmaxf(fmaxf(fabsf(ax[p][0]), fabsf(ax[p][1])), fmaxf(fabsf(ax[p][2]), fabsf(ax[p][3]))));
-    lm = wave_max_nonneg(lm);
-    if (lm >= 16384.f || (lm < 256.f && lm > 0.f)) {
-      const int d = exp_of(lm) - 12;
+    const bool over = __ballot(lm >= 16384.f) != 0, some = __ballot(lm >= 256.f) != 0, any = __ballot(lm > 0.f) != 0;
+    if (over || (any && !some)) {
+      const float wm = wave_max_nonneg(lm);
+      const int d = exp_of(wm) - 12;
       const float s = ldexpf(1.f, -d);
 #pragma unroll
       for (int p = 0; p < NT; ++p) ax[p] *= s;
       ex += d;
-      lm *= s;
     }
-    return lm;
   };
 
   f32x4 bt[NT];            // -B_k
@@ -303,12 +282,17 @@ __device__ __forceinline__ void ns_small_block(char* __restrict__ lds, int g, co
   // -B_k = (-A_k) W^T into bt: -A_k goes through tmp (a buffer that no wave reads once the first barrier is
   // passed) with one block-wide exponent eb, and the product comes back times 2^-eb.
   auto form_t = [&](RegSplit& tmp) {
-    if (act) s_part[cs] = rescale() * ldexpf(1.f, ex);
+    // every strip's largest entry is below 2^14 times its exponent after the check, so 2^(2 + the largest
+    // exponent) puts every stored entry at or below 2^12
+    if (act) {
+      rescale();
+      if (ln == 0) s_ex[cs] = ex;
+    }
     barrier_lds();
-    float bm = s_part[0];
+    int eb = s_ex[0];
 #pragma unroll
-    for (int w = 1; w < ST; ++w) bm = fmaxf(bm, s_part[w]);
-    const int eb = store_exp(fminf(bm, 3.0e38f));
+    for (int w = 1; w < ST; ++w) eb = max(eb, s_ex[w]);
+    eb += 2;
     if (act) {
       const float s = ldexpf(1.f, ex - eb);
 #pragma unroll
