@@ -442,8 +442,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // S = C_K^T V, each one (slice, 16-landmark tile, 16-channel tile) of S over all N tokens. No block of this launch
 // waits for another: a cross-XCD hand-off of partial sums needs device-scope release and acquire fences, and
 // on this chip those write back and invalidate a whole L2, which costs more than the solver itself.
-// Each block holds the solver's LDS (about 67 KB, so at most two blocks share a CU); the tiles fill the CUs the
-// solver leaves free and finish inside the solver's time.
+// Each block holds the solver's LDS (41 KB, so three blocks share a CU); the tiles fill the CUs the solver leaves
+// free and finish inside the solver's time when C_K and V come from the last-level cache. Read from HBM they take
+// longer than the solver: their loads go out in batches of 12 token groups (5 memory round trips per wave at
+// N = 3136), which brought that case from 10.6 to about 6 us beyond the solver.
 // =====================================================================================================
 
 // One S tile by one block of NWV waves. Wave w sums a contiguous range of 16-token groups on fp32 MFMA (A = C_K,
@@ -451,6 +453,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // 16q + 4k + u at k-step u, loaded from global memory straight into the MFMA operand layout. The wave tiles are
 // then summed in LDS (sRed: NWV x 256 floats) in wave order, so the result does not depend on timing.
 constexpr int kSideWaves = 4;  // the solver's block size
+constexpr int kCkvBatch = 12;  // 16-token groups per batch of loads
 
 template <typename T, int D, int NWV>
 __device__ __forceinline__ void ckv_tile_block(int blk, const float* __restrict__ C, const T* __restrict__ V,
@@ -470,25 +473,34 @@ __device__ __forceinline__ void ckv_tile_block(int blk, const float* __restrict_
   const int qf = max(q0, min(q1, N / 16));  // groups [q0, qf) have all 16 tokens in range
   const float amask = lok ? 1.f : 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // Groups in batches of kCkvBatch, every load of a batch issued before its first MFMA: a wave walks about N / 64
+  // groups, so the batches (not the loads of one group) set how many memory round trips the tile waits for.
   auto full_groups = [&](auto vec) {
-#pragma unroll 4
-    for (int q = q0; q < qf; ++q) {
-      const int t = q * 16 + 4 * k;
-      float a[4], b[4];
-      if constexpr (decltype(vec)::value) {
-        const float4 c4 = load4(crow + t);
-        a[0] = c4.x;
-        a[1] = c4.y;
-        a[2] = c4.z;
-        a[3] = c4.w;
-      } else {
+    for (int q = q0; q < qf; q += kCkvBatch) {
+      float a[kCkvBatch][4], b[kCkvBatch][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) a[u] = crow[t + u];
+      for (int j = 0; j < kCkvBatch; ++j) {
+        // a group past the range repeats the last one with a zero weight (in bounds, adds nothing)
+        const int qj = min(q + j, qf - 1);
+        const int t = qj * 16 + 4 * k;
+        const float wj = q + j < qf ? amask : 0.f;
+        if constexpr (decltype(vec)::value) {
+          const float4 c4 = load4(crow + t);
+          a[j][0] = c4.x * wj;
+          a[j][1] = c4.y * wj;
+          a[j][2] = c4.z * wj;
+          a[j][3] = c4.w * wj;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) a[j][u] = crow[t + u] * wj;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) b[j][u] = to_f32(vcol[static_cast<size_t>(t + u) * D]);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) b[u] = to_f32(vcol[static_cast<size_t>(t + u) * D]);
+      for (int j = 0; j < kCkvBatch; ++j)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc = mfma16x16x4(a[u] * amask, b[u], acc);
+        for (int u = 0; u < 4; ++u) acc = mfma16x16x4(a[j][u], b[j][u], acc);
     }
   };
   if ((N & 3) == 0)
