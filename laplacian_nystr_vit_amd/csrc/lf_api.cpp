@@ -89,7 +89,7 @@ lf_saved_layout saved_layout(const lf::Shape& s) {
 // Forward workspace. Without a saved buffer every intermediate lives here; with one, only X, the scaled P,
 // the C_K^T V partials and the Newton-Schulz scratch do.
 struct FwdWs {
-  size_t L, CQ, CK, We, X, S, P, Pw, mu, rstd, alpha, part, nstmp, total;
+  size_t L, CQ, CK, We, X, S, P, Pw, mu, rstd, alpha, part, nstmp, wst, total;
 };
 
 FwdWs fwd_ws(const lf::Shape& s) {
@@ -111,6 +111,7 @@ FwdWs fwd_ws(const lf::Shape& s) {
   w.alpha = c.take(4 * G);
   w.part = c.take(nsplit > 1 ? 4 * G * static_cast<size_t>(nsplit) * m * d : 0);
   w.nstmp = c.take(4 * lf::ns_tmp_floats(s));
+  w.wst = c.take(4 * 2 * G * m * ((N + 63) / 64));
   w.total = c.off;
   return w;
 }
@@ -221,11 +222,14 @@ int fwd_launch(const lf_attn_params* p, const void* Q, const void* K, const void
   // (lf::out_fused_pays).
   const bool fuse_cq = !saved && !wh && p->kernel != LF_KERNEL_GAUSS && lf::out_fused_pays(s);
   LF_TRY(lf::launch_landmark_pool(s, Q, L, st));
+  // With whitening on this path the C_Q blocks leave per-tile partial statistics and the landmark mix finishes
+  // them (no separate statistics pass over C_Q).
+  float* wst = nullptr;
   if (p->kernel == LF_KERNEL_LAPLACE && !fuse_cq && lf::ns_laplace_supported(s)) {
     // C_K and W_eps first, then the solver beside S = C_K^T V and the C_Q pass in one launch.
+    if (wh) wst = at<float>(ws, w.wst);
     LF_TRY(lf::launch_laplace(s, Q, K, L, CQ, CK, We, st, 6));
-    LF_TRY(lf::launch_ns_laplace(s, We, X, xs, alpha, CK, V, S, Q, L, CQ, st));
-    if (wh) LF_TRY(lf::launch_whiten_stats(s, CQ, mu, rstd, st));
+    LF_TRY(lf::launch_ns_laplace(s, We, X, xs, alpha, CK, V, S, Q, L, CQ, st, wst));
   } else {
     if (p->kernel == LF_KERNEL_GAUSS)
       LF_TRY(lf::launch_gauss(s, Q, K, L, CQ, CK, We, st));
@@ -249,7 +253,10 @@ int fwd_launch(const lf_attn_params* p, const void* Q, const void* K, const void
     // Inference: P = X S is formed inside the output kernel (no landmark-mix launch, P never stored).
     LF_TRY(lf::launch_out_mix(s, CQ, X, S, V, dwc_w, Y, st));
   } else {
-    LF_TRY(lf::launch_mix(s, X, S, wh ? rstd : nullptr, P, Praw, st));
+    if (wst)
+      LF_TRY(lf::launch_mix_whiten(s, X, S, wst, mu, rstd, P, Praw, st));
+    else
+      LF_TRY(lf::launch_mix(s, X, S, wh ? rstd : nullptr, P, Praw, st));
     LF_TRY(lf::launch_out(s, CQ, P, wh ? mu : nullptr, V, dwc_w, Y, st));
   }
   return LF_OK;

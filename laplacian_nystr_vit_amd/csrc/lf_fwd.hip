@@ -257,15 +257,64 @@ __global__ __launch_bounds__(256) void k_ckv_finalize(const float* __restrict__ 
 //   [note] Designs 2 and 3; rstd from the diagonal whitening of Design 1). m x m times m x D per slice.
 // Block: 256 / D landmark rows x D channels of one slice, one output per thread; X rows and 64-row chunks of S are
 // staged in LDS, and each output sums its landmarks in order.
+// With wst the block first finishes the whitening statistics of its landmark rows from the per-tile partials of
+// C_Q (tile sum and sum of squared deviations from the tile mean, 64 rows per tile): wave w takes rows w, w + 4, ..;
+// lane t merges tiles t, t + 64, .. in order, then the lanes are merged in a fixed butterfly, each merge the
+// pairwise update of Chan, Golub and LeVeque in float64 (counts add, sums add, and the squared-deviation sums add
+// plus delta^2 n_a n_b / (n_a + n_b) for the difference delta of the two means). mu = sum / N and
+// rstd = 1 / sqrt(M2 / N + weps) (the population variance) are written for the output kernel and the backward.
 // =====================================================================================================
+__device__ __forceinline__ void chan_merge(double& na, double& sa, double& qa, double nb, double sb, double qb) {
+  if (nb == 0.0) return;
+  if (na == 0.0) {
+    na = nb;
+    sa = sb;
+    qa = qb;
+    return;
+  }
+  const double d = sb / nb - sa / na;
+  qa = (qa + qb) + d * d * (na * nb / (na + nb));
+  sa += sb;
+  na += nb;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void k_mix(const float* __restrict__ X, const float* __restrict__ S,
                                              const float* __restrict__ rstd, float* __restrict__ P,
-                                             float* __restrict__ Praw, int m) {
+                                             float* __restrict__ Praw, int m, const float* __restrict__ wst,
+                                             float* __restrict__ mu_out, float* __restrict__ rstd_out, int N,
+                                             float weps) {
   constexpr int RB = 256 / D;  // landmark rows per block: one output (row, channel) per thread
   __shared__ float sX[RB * 65];
   __shared__ float sS[64 * D];
+  __shared__ float s_rstd[RB];
   const int g = blockIdx.y, l0 = blockIdx.x * RB, tid = threadIdx.x;
+  if (wst) {
+    const int tiles = (N + 63) / 64, wv = tid >> 6, ln = tid & 63;
+    for (int r2 = wv; r2 < RB; r2 += 4) {
+      const int l = l0 + r2;
+      if (l >= m) break;
+      double n = 0.0, sum = 0.0, q = 0.0;
+      for (int t = ln; t < tiles; t += 64) {
+        const float* w = wst + 2 * ((static_cast<size_t>(g) * m + l) * tiles + t);
+        chan_merge(n, sum, q, static_cast<double>(min(64, N - 64 * t)), static_cast<double>(w[0]),
+                   static_cast<double>(w[1]));
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double n2 = __shfl_xor(n, off), s2 = __shfl_xor(sum, off), q2 = __shfl_xor(q, off);
+        chan_merge(n, sum, q, n2, s2, q2);
+      }
+      if (ln == 0) {
+        const double mean = sum / n, var = q / n;
+        const float r = static_cast<float>(1.0 / sqrt(var + static_cast<double>(weps)));
+        mu_out[static_cast<size_t>(g) * m + l] = static_cast<float>(mean);
+        rstd_out[static_cast<size_t>(g) * m + l] = r;
+        s_rstd[r2] = r;
+      }
+    }
+    __syncthreads();
+  }
   const int rr = tid / D, c = tid % D;
   float acc = 0.f;
   const float* xg = X + static_cast<size_t>(g) * m * m;
@@ -304,7 +353,7 @@ __global__ __launch_bounds__(256) void k_mix(const float* __restrict__ X, const 
   }
   const int l = l0 + rr;
   if (l < m) {
-    const float sc = rstd ? rstd[static_cast<size_t>(g) * m + l] : 1.f;
+    const float sc = wst ? s_rstd[rr] : (rstd ? rstd[static_cast<size_t>(g) * m + l] : 1.f);
     P[(static_cast<size_t>(g) * m + l) * D + c] = acc * sc;
     if (Praw) Praw[(static_cast<size_t>(g) * m + l) * D + c] = acc;
   }
@@ -1013,13 +1062,24 @@ hipError_t launch_ckv(const Shape& s, const float* CK, const void* V, float* par
 hipError_t launch_mix(const Shape& s, const float* X, const float* S, const float* rstd, float* P, float* Praw,
                       hipStream_t st) {
   // P = rstd * (X S) (rstd == nullptr means 1); Praw, when given, receives the unscaled X S.
+  return launch_mix_whiten(s, X, S, nullptr, nullptr, const_cast<float*>(rstd), P, Praw, st);
+}
+
+hipError_t launch_mix_whiten(const Shape& s, const float* X, const float* S, const float* wst, float* mu, float* rstd,
+                             float* P, float* Praw, hipStream_t st) {
+  // wst null: P = rstd * (X S) with the given rstd (null means 1). Otherwise mu and rstd are outputs.
   const dim3 grid(cdiv(s.m, 256 / s.d), s.G);  // 256 / d landmark rows per block (k_mix)
+  const float* rin = wst ? nullptr : rstd;
+  float* rout = wst ? rstd : nullptr;
+#define LF_MIX(D_)                                                                                                \
+  hipLaunchKernelGGL(k_mix<D_>, grid, dim3(256), 0, st, X, S, rin, P, Praw, s.m, wst, mu, rout, s.N, s.whiten_eps)
   switch (s.d) {
-    case 16: hipLaunchKernelGGL(k_mix<16>, grid, dim3(256), 0, st, X, S, rstd, P, Praw, s.m); break;
-    case 32: hipLaunchKernelGGL(k_mix<32>, grid, dim3(256), 0, st, X, S, rstd, P, Praw, s.m); break;
-    case 64: hipLaunchKernelGGL(k_mix<64>, grid, dim3(256), 0, st, X, S, rstd, P, Praw, s.m); break;
-    default: hipLaunchKernelGGL(k_mix<128>, grid, dim3(256), 0, st, X, S, rstd, P, Praw, s.m); break;
+    case 16: LF_MIX(16); break;
+    case 32: LF_MIX(32); break;
+    case 64: LF_MIX(64); break;
+    default: LF_MIX(128); break;
   }
+#undef LF_MIX
   return hipGetLastError();
 }
 

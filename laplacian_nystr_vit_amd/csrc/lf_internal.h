@@ -35,6 +35,10 @@ hipError_t launch_ckv_general(const Shape& s, const float* C, int ones, const vo
                               hipStream_t st);
 hipError_t launch_mix(const Shape& s, const float* X, const float* S, const float* rstd, float* P, float* Praw,
                       hipStream_t st);
+// launch_mix with the whitening statistics finished first from the per-tile partials wst (written by the C_Q
+// blocks of launch_ns_laplace): mu and rstd are written, and P = rstd (X S).
+hipError_t launch_mix_whiten(const Shape& s, const float* X, const float* S, const float* wst, float* mu, float* rstd,
+                             float* P, float* Praw, hipStream_t st);
 hipError_t launch_out(const Shape& s, const float* CQ, const float* P, const float* mu, const void* V,
                       const float* w, void* Y, hipStream_t st);
 // Y = C_Q (X S) + DWC(V) with P = X S formed in the output kernel (no whitening; out_mix_supported: m <= 64, d >= 32).
@@ -61,8 +65,11 @@ bool ns_side_supported(const Shape& s);
 // Newton-Schulz beside S = C_K^T V and the C_Q distance pass in one launch (Laplace kernel; C_K and W_eps from a
 // prior distance launch over the K and landmark rows). xs: saved iterates or null.
 bool ns_laplace_supported(const Shape& s);
+// wst: when not null, the C_Q blocks also write the per-tile whitening partials (2 G m ceil(N / 64) floats) that
+// launch_mix_whiten finishes.
 hipError_t launch_ns_laplace(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
-                             const void* V, float* S, const void* Q, const float* L, float* CQ, hipStream_t st);
+                             const void* V, float* S, const void* Q, const float* L, float* CQ, hipStream_t st,
+                             float* wst = nullptr);
 hipError_t launch_ns_side(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
                           const void* V, float* S, hipStream_t st);
 

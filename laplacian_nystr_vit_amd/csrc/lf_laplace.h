@@ -29,16 +29,31 @@ namespace lf {
 template <int D>
 constexpr int kLaplaceLds = 64 * (D + 4) * 4;
 
+// Sum over the wave, wave-uniform, in a fixed order: DPP steps inside each row of 16 lanes (quad swaps, then
+// rotations by 4 and 8), then the four row sums through scalar reads of lanes 0, 16, 32 and 48.
+__device__ __forceinline__ float wave_sum_fixed(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, false));  // row_ror:4
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));  // row_ror:8
+  const int b = __float_as_int(v);
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+}
+
 // One block of the distance kernel: b is the block's index among nblocks such blocks, which run nw waves each and
 // were dealt to the XCDs round-robin from a multiple of 8; sX is kLaplaceLds<D> bytes of LDS.
 // tilesQ / tilesK / tilesL: 64-row tiles of Q, K and L rows per slice (0 leaves that source out).
-template <typename T, int D>
+// STATS (Q rows only): per (slice, landmark, Q tile) the tile's sum of C and sum of squared deviations from the
+// tile's mean go to wst[2 ((g m + l) tilesQ + tile)] and + 1, for the whitening statistics of C_Q (Design 1 of
+// the note).
+template <typename T, int D, bool STATS = false>
 __device__ __forceinline__ void laplace_block(float* __restrict__ sX, int b, int nblocks, int nw,
                                               const T* __restrict__ Q, const T* __restrict__ K,
                                               const float* __restrict__ L, float* __restrict__ CQ,
                                               float* __restrict__ CK, float* __restrict__ We, int N, int m,
                                               int tilesQ, int tilesK, int tilesL, int nsc, int lc, float scale,
-                                              float eps) {
+                                              float eps, float* __restrict__ wst = nullptr) {
   constexpr int LDX = D + 4;
   {
     const int full = (nblocks / 8) * 8;
@@ -85,7 +100,11 @@ __device__ __forceinline__ void laplace_block(float* __restrict__ sX, int b, int
   }
   __syncthreads();
   const int row = tile * 64 + lane;
-  if (row >= rows || l0 >= l1) return;
+  // With the statistics every lane stays (rows past the end compute on zeros and store nothing); otherwise they
+  // leave here.
+  const bool stats = STATS && src == 0;
+  if ((row >= rows && !stats) || l0 >= l1) return;
+  const bool valid = row < rows;
 
   float x[D];
 #pragma unroll
@@ -119,7 +138,18 @@ __device__ __forceinline__ void laplace_block(float* __restrict__ sX, int b, int
     }
     float v = __builtin_amdgcn_exp2f(((a0 + a1) + (a2 + a3)) * scale);
     if (src == 2 && l == row) v += eps;
-    out[l * ostride] = v;
+    if (!STATS || valid) out[l * ostride] = v;
+    if (STATS && stats) {
+      const int n = min(64, rows - tile * 64);
+      const float sum = wave_sum_fixed(valid ? v : 0.f);
+      const float dv = valid ? v - sum / static_cast<float>(n) : 0.f;
+      const float ssd = wave_sum_fixed(dv * dv);
+      if (lane == 0) {
+        float* w = wst + 2 * ((static_cast<size_t>(g) * m + l) * tilesQ + tile);
+        w[0] = sum;
+        w[1] = ssd;
+      }
+    }
   };
   one(l0, lfirst);
   for (int l = l0 + 1; l < l1; ++l) one(l, Lg + static_cast<size_t>(l) * D);

@@ -572,7 +572,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const float* __restrict__ We, float* __restrict__ Xout, float* __restrict__ xs, float* __restrict__ alpha_out,
     int m, int iters, int G, const float* __restrict__ CK, const T* __restrict__ V, float* __restrict__ S, int nS,
     const T* __restrict__ Q,
-    const float* __restrict__ L, float* __restrict__ CQ, int N, int nlap, int tilesN, int lc, float scale) {
+    const float* __restrict__ L, float* __restrict__ CQ, int N, int nlap, int tilesN, int lc, float scale,
+    float* __restrict__ wst) {
   __shared__ __attribute__((aligned(16))) char lds[kNsSmallLds > kLaplaceLds<D> ? kNsSmallLds : kLaplaceLds<D>];
   static_assert(kSideWaves * 256 * 4 <= kNsSmallLds, "S tile reduction exceeds the shared LDS");
   const int b = static_cast<int>(blockIdx.x);
@@ -588,9 +589,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (b - s0 < nS) ckv_tile_block<T, D, kSideWaves>(ckv_tile_order(b - s0, nS), CK, V, S, N, m, reinterpret_cast<float*>(lds));
     return;
   }
-  // (only rows of Q here: the W_eps and C_K outputs are never reached)
-  laplace_block<T, D>(reinterpret_cast<float*>(lds), b - s1, nlap, 4, Q, Q, L, CQ, CQ, const_cast<float*>(We), N, m,
-                      tilesN, 0, 0, 1, lc, scale, 0.f);
+  // (only rows of Q here: the W_eps and C_K outputs are never reached); with wst, also the tiles' whitening
+  // partials
+  if (wst)
+    laplace_block<T, D, true>(reinterpret_cast<float*>(lds), b - s1, nlap, 4, Q, Q, L, CQ, CQ,
+                              const_cast<float*>(We), N, m, tilesN, 0, 0, 1, lc, scale, 0.f, wst);
+  else
+    laplace_block<T, D>(reinterpret_cast<float*>(lds), b - s1, nlap, 4, Q, Q, L, CQ, CQ, const_cast<float*>(We), N,
+                        m, tilesN, 0, 0, 1, lc, scale, 0.f);
 }
 
 template <typename T, int D>
@@ -639,7 +645,7 @@ bool ns_laplace_supported(const Shape& s) { return ns_side_supported(s); }
 
 template <typename T, int D>
 static void ns_laplace_st(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
-                          const T* V, float* S, const T* Q, const float* L, float* CQ, hipStream_t st) {
+                          const T* V, float* S, const T* Q, const float* L, float* CQ, float* wst, hipStream_t st) {
   const int tilesN = (s.N + 63) / 64, nlap = s.G * tilesN, lc = (s.m + 3) / 4;
   const int nS = s.G * ((s.m + 15) / 16) * (D / 16);
   const int blocks = ((s.G + 7) & ~7) + ((nS + 7) & ~7) + nlap;  // solver blocks, S tiles, C_Q distance blocks
@@ -647,7 +653,7 @@ static void ns_laplace_st(const Shape& s, const float* We, float* X, float* xs, 
   const int nt = (s.m + 15) / 16;
 #define LF_NS_LAP(ST_)                                                                                         \
   hipLaunchKernelGGL((k_ns_laplace<T, D, ST_>), dim3(blocks), dim3(256), 0, st, We, X, xs, alpha, s.m,          \
-                     s.ns_iters, s.G, CK, V, S, nS, Q, L, CQ, s.N, nlap, tilesN, lc, scale)
+                     s.ns_iters, s.G, CK, V, S, nS, Q, L, CQ, s.N, nlap, tilesN, lc, scale, wst)
   if (nt == 1)
     LF_NS_LAP(1);
   else if (nt == 2)
@@ -659,23 +665,25 @@ static void ns_laplace_st(const Shape& s, const float* We, float* X, float* xs, 
 
 template <typename T>
 static void ns_laplace_t(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
-                         const void* V, float* S, const void* Q, const float* L, float* CQ, hipStream_t st) {
+                         const void* V, float* S, const void* Q, const float* L, float* CQ, float* wst,
+                         hipStream_t st) {
   const T* v = static_cast<const T*>(V);
   const T* q = static_cast<const T*>(Q);
   switch (s.d) {
-    case 16: ns_laplace_st<T, 16>(s, We, X, xs, alpha, CK, v, S, q, L, CQ, st); break;
-    case 32: ns_laplace_st<T, 32>(s, We, X, xs, alpha, CK, v, S, q, L, CQ, st); break;
-    default: ns_laplace_st<T, 64>(s, We, X, xs, alpha, CK, v, S, q, L, CQ, st); break;
+    case 16: ns_laplace_st<T, 16>(s, We, X, xs, alpha, CK, v, S, q, L, CQ, wst, st); break;
+    case 32: ns_laplace_st<T, 32>(s, We, X, xs, alpha, CK, v, S, q, L, CQ, wst, st); break;
+    default: ns_laplace_st<T, 64>(s, We, X, xs, alpha, CK, v, S, q, L, CQ, wst, st); break;
   }
 }
 
 hipError_t launch_ns_laplace(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
-                             const void* V, float* S, const void* Q, const float* L, float* CQ, hipStream_t st) {
+                             const void* V, float* S, const void* Q, const float* L, float* CQ, hipStream_t st,
+                             float* wst) {
   if (!ns_laplace_supported(s)) return hipErrorInvalidValue;
   if (s.dtype == 1)
-    ns_laplace_t<bf16_t>(s, We, X, xs, alpha, CK, V, S, Q, L, CQ, st);
+    ns_laplace_t<bf16_t>(s, We, X, xs, alpha, CK, V, S, Q, L, CQ, wst, st);
   else
-    ns_laplace_t<float>(s, We, X, xs, alpha, CK, V, S, Q, L, CQ, st);
+    ns_laplace_t<float>(s, We, X, xs, alpha, CK, V, S, Q, L, CQ, wst, st);
   return hipGetLastError();
 }
 
