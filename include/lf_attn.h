@@ -126,7 +126,8 @@ int lf_attn_bwd(const lf_attn_params* p, const void* Q, const void* K, const voi
 
 /* A second stream lent by the caller to lf_attn_bwd_ex, with two events of the caller's (create them with
  * hipEventDisableTiming). Parts of the call's work that do not depend on each other run on `stream` after an
- * event recorded on the call's stream (`fork`); the call's stream then waits on `join`, recorded after those parts,
+ * event recorded on the call's stream (`fork`, recorded twice per call: at its start and after the first small
+ * products); the call's stream then waits on `join`, recorded after those parts,
  * so everything the call does is complete when work enqueued on the call's stream after it starts. The stream must
  * be another stream than the call's, on the same device (LF_EINVAL otherwise). The library keeps none of these
  * handles after the call returns; calls that lend the same lf_aux_stream must be ordered by the caller. */
@@ -145,7 +146,8 @@ typedef struct lf_aux_stream {
  *        without it alpha is held constant as in lf_attn_bwd. Other bits: LF_EINVAL.
  * aux:   NULL runs everything on `stream` (as lf_attn_bwd does), or a lent second stream (lf_aux_stream): the
  *        reverse Newton-Schulz chain, the landmark-matrix terms of dL and of the lambda gradient, and the DWC
- *        weight gradient then overlap the row gradients and the sign reductions (one fork, one join).
+ *        weight gradient then overlap the first small products, the row gradients and the sign reductions (two
+ *        forks, one join).
  * Same saved buffer, workspace (bwd_ws_bytes), alignment and errors as lf_attn_bwd; d_dwc_w is 16-byte aligned. */
 #define LF_BWD_EXACT_ALPHA 1
 int lf_attn_bwd_ex(const lf_attn_params* p, const void* Q, const void* K, const void* V, const float* dwc_w,

@@ -1189,10 +1189,15 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
   const float inv_lam = static_cast<float>(1.0 / static_cast<double>(s.lambda));
   const int wh = whiten ? 1 : 0;
 
-  // With a side stream, one fork and one join (an event wait costs the host about as much as two launches): after
-  // the first small products the side stream takes the reverse Newton-Schulz chain, dL's landmark-kernel term
-  // with the lambda gradient's W terms, and the DWC weight gradient, while the call's stream forms the row
-  // gradients, dV and the sign reductions; it then waits for the side stream before the last two kernels.
+  // With a side stream: two forks and one join (an event wait costs the host about as much as four launches).
+  // The side stream starts at once with the work that needs nothing from this call's other kernels (the split
+  // fragments of A1_k = W X_k and A2_k = X_k W, and the DWC weight gradient), beside T1 and the small products on
+  // the call's stream. After the small products it takes the reverse Newton-Schulz chain, D_k, dW and dL's
+  // landmark-kernel term, while the call's stream forms the row gradients, dV and the sign reductions; the call's
+  // stream then waits for it before the last two kernels. The side stream's kernels are enqueued ahead of the
+  // call's stream's long ones, so that the chain's few blocks reach the GPU before those fill it. (One fork after
+  // the small products, with the side stream's work enqueued after the call's stream's, left the chain waiting
+  // for the sign reductions to drain: the two streams' work ran one after the other.)
   hipError_t e = hipSuccess;
   hipStream_t ns_st = side ? side->s : st;
   bool forked = false;
@@ -1201,15 +1206,45 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
     if (forked && hipEventRecord(side->join, side->s) == hipSuccess) (void)hipStreamWaitEvent(st, side->join, 0);
     return err;
   };
+  auto fork = [&]() -> hipError_t {  // the side stream waits for everything enqueued on the call's stream so far
+    if (!side) return hipSuccess;
+    hipError_t f = hipEventRecord(side->fork, st);
+    if (f == hipSuccess) f = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (f == hipSuccess) forked = true;
+    return f;
+  };
+  float* lp = ex.d_lambda ? reinterpret_cast<float*>(b + p.lampart) : nullptr;
+  bh8* frag = reinterpret_cast<bh8*>(b + p.nsA1);
+  float* nsc = reinterpret_cast<float*>(b + p.nsA2);
+  const int Kn = s.ns_iters;
+  const int sliceblocks = 8 * cdiv(s.G, 8) * Kn;  // slice_step_of's grid
+  if ((e = fork()) != hipSuccess) return bail(e);
+  if (Kn > 0)
+    hipLaunchKernelGGL(k_bwd_ns_pre, dim3(sliceblocks), dim3(NSB_THREADS), 0, ns_st, sp.We, sp.xs, frag, nsc, s.m,
+                       Kn, s.G);
+  if (ex.d_dwc_w) {
+    float* dp = reinterpret_cast<float*>(b + p.dwcpart);
+    hipLaunchKernelGGL((k_dwc_wgrad_partial<T, D>), dim3(p.dwcblocks, s.G), dim3(kDwcThreads), 0, ns_st, dY, V, dp,
+                       s.H, s.W, p.dwcseg, p.dwcblocks);
+    hipLaunchKernelGGL(k_dwc_wgrad_final<D>, dim3(s.heads * 9, D / 16), dim3(256), 0, ns_st, dp, ex.d_dwc_w,
+                       s.G / s.heads, s.heads, p.dwcblocks);
+  }
   if ((e = launch_ckv_general(s, sp.CQ, 1, dY, part, T1, st)) != hipSuccess) return bail(e);
   hipLaunchKernelGGL(k_bwd_small1<D>, dim3(s.G, s.m < 32 ? s.m : 32), dim3(256), 0, st, T1, sp.S, sp.P, sp.xs, sp.mu,
                      sp.rstd, dX, dS, stats, s.m, s.ns_iters, s.N, wh);
-  if (side) {
-    if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
-    forked = true;
+  if ((e = fork()) != hipSuccess) return bail(e);
+  {
+    float* Gs = reinterpret_cast<float*>(b + p.nsG);
+    float* Dk = reinterpret_cast<float*>(b + p.nsD);
+    float* Gf = reinterpret_cast<float*>(b + p.nsGf);
+    hipLaunchKernelGGL(k_bwd_ns_chain, dim3(s.G), dim3(NSC_THREADS), 0, ns_st, frag, nsc, dX, Gs, Gf, s.m, Kn);
+    if (Kn > 0)
+      hipLaunchKernelGGL(k_bwd_ns_dk, dim3(sliceblocks), dim3(NSB_THREADS), 0, ns_st, sp.xs, Gs, Dk, s.m, Kn, s.G);
+    hipLaunchKernelGGL(k_bwd_ns_final, dim3(cdiv(static_cast<long>(s.m) * s.m, NSF_THREADS), s.G),
+                       dim3(NSF_THREADS), 0, ns_st, sp.We, sp.alpha, Dk, Gf, dWe, s.m, Kn, ex.exact_alpha ? 1 : 0);
   }
-  float* lp = ex.d_lambda ? reinterpret_cast<float*>(b + p.lampart) : nullptr;
+  hipLaunchKernelGGL(k_bwd_wpart, dim3(cdiv(static_cast<long>(s.m) * D, 256), s.G), dim3(256), 0, ns_st, sp.L, sp.We,
+                     dWe, dLW, lp, p.lamchunks, s.m, D, inv_lam);
   hipLaunchKernelGGL((k_bwd_rowgrad<T, D>), dim3(cdiv(s.N, 64), s.G, 2), dim3(256), 0, st, dY, V, sp.P, dS, sp.CQ,
                      sp.CK, sp.mu, sp.rstd, stats, Gq, Gk, lp, s.N, s.m, inv_lam, wh);
   if ((e = launch_out_adjoint(s, sp.CK, dS, dY, w, dVv, st)) != hipSuccess) return bail(e);
@@ -1239,33 +1274,6 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
       default: return bail(hipErrorInvalidValue);  // the backward takes m <= 64 (checked at the boundary)
     }
 #undef LF_SIGN
-  }
-  // the side stream's part, enqueued after the call's stream's (both are queued ahead of the GPU either way)
-  {
-    bh8* frag = reinterpret_cast<bh8*>(b + p.nsA1);
-    float* nsc = reinterpret_cast<float*>(b + p.nsA2);
-    float* Gs = reinterpret_cast<float*>(b + p.nsG);
-    float* Dk = reinterpret_cast<float*>(b + p.nsD);
-    float* Gf = reinterpret_cast<float*>(b + p.nsGf);
-    const int Kn = s.ns_iters;
-    const int sliceblocks = 8 * cdiv(s.G, 8) * Kn;  // slice_step_of's grid
-    if (Kn > 0)
-      hipLaunchKernelGGL(k_bwd_ns_pre, dim3(sliceblocks), dim3(NSB_THREADS), 0, ns_st, sp.We, sp.xs, frag, nsc, s.m,
-                         Kn, s.G);
-    hipLaunchKernelGGL(k_bwd_ns_chain, dim3(s.G), dim3(NSC_THREADS), 0, ns_st, frag, nsc, dX, Gs, Gf, s.m, Kn);
-    if (Kn > 0)
-      hipLaunchKernelGGL(k_bwd_ns_dk, dim3(sliceblocks), dim3(NSB_THREADS), 0, ns_st, sp.xs, Gs, Dk, s.m, Kn, s.G);
-    hipLaunchKernelGGL(k_bwd_ns_final, dim3(cdiv(static_cast<long>(s.m) * s.m, NSF_THREADS), s.G),
-                       dim3(NSF_THREADS), 0, ns_st, sp.We, sp.alpha, Dk, Gf, dWe, s.m, Kn, ex.exact_alpha ? 1 : 0);
-  }
-  hipLaunchKernelGGL(k_bwd_wpart, dim3(cdiv(static_cast<long>(s.m) * D, 256), s.G), dim3(256), 0, ns_st, sp.L, sp.We,
-                     dWe, dLW, lp, p.lamchunks, s.m, D, inv_lam);
-  if (ex.d_dwc_w) {
-    float* dp = reinterpret_cast<float*>(b + p.dwcpart);
-    hipLaunchKernelGGL((k_dwc_wgrad_partial<T, D>), dim3(p.dwcblocks, s.G), dim3(kDwcThreads), 0, ns_st, dY, V, dp,
-                       s.H, s.W, p.dwcseg, p.dwcblocks);
-    hipLaunchKernelGGL(k_dwc_wgrad_final<D>, dim3(s.heads * 9, D / 16), dim3(256), 0, ns_st, dp, ex.d_dwc_w,
-                       s.G / s.heads, s.heads, p.dwcblocks);
   }
   if (side && (e = hipEventRecord(side->join, side->s)) != hipSuccess) return bail(e);
   if (side && (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return bail(e);  // dLW, Gw's lambda terms
