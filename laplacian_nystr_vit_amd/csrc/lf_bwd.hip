@@ -976,19 +976,49 @@ __global__ __launch_bounds__(kSignSub * 64) void k_bwd_sign(const T* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// lambda gradient: every kernel entry k = exp(-D / lambda) moves by k D / lambda^2 = -k ln(k) / lambda, so
+// d/dlambda = -sum G ln(k) over G = dC C / lambda (Gq, Gk, and Gw = dW W / lambda off the diagonal, where W = W_eps
+// and the eps diagonal does not depend on lambda). The row-gradient kernel sums the Gq and Gk terms of each of
+// its blocks (it forms those G values), k_bwd_wpart the Gw terms of each landmark row; an entry whose k
+// underflowed to 0 has G = 0 and adds nothing. One extra block of k_bwd_dq_final adds the partials in a fixed
+// order (after the call's stream has joined the side stream, which writes the W terms).
+// ---------------------------------------------------------------------------------------------------------
+// One block of 256 threads: thread t sums the partials t, t + 256, ... in order, then a fixed tree in LDS (red:
+// 256 floats).
+__device__ __forceinline__ void dlam_sum_block(const float* __restrict__ part, float* __restrict__ out, int n,
+                                               float* red) {
+  const int tid = threadIdx.x;
+  float t = 0.f;
+  for (int i = tid; i < n; i += 256) t += part[i];
+  red[tid] = t;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) *out = red[0];
+}
+
 // dL = sum of the sign blocks' partials (in block order) + the landmark-kernel term dLW, then the pooling term of
 // dQ: every token i of landmark l's r x r block gets dQ_i = dQp_i + dL_l / r^2. Block = (landmark, slice); each
 // thread takes up to kDqPer of the block's r^2 D token entries, whose dQp loads are issued before the dL sum.
+// With dlam, block (m, 0) instead sums the nlam lambda-gradient partials into *dlam (blocks (m, g > 0) exit).
 constexpr int kDqPer = 16;
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_bwd_dq_final(const float* __restrict__ dLpart, const float* __restrict__ dLW,
                                                       const float* __restrict__ dQp, T* __restrict__ dQ, int N, int m,
-                                                      int W, int r, int nsplit) {
+                                                      int W, int r, int nsplit, const float* __restrict__ lampart,
+                                                      float* __restrict__ dlam, int nlam) {
   constexpr int P = 256 / D;
   __shared__ float part[256];
   __shared__ float add[D];
   const int l = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, c = tid % D, q = tid / D;
+  if (l >= m) {
+    if (g == 0 && dlam) dlam_sum_block(lampart, dlam, nlam, part);
+    return;
+  }
   const int wr = W / r, yb = l / wr, xb = l % wr, total = r * r * D;
   // entry e = e0 + tid + 256 u (u < kDqPer): token e / D of the block, channel e % D = c
   size_t o[kDqPer];
@@ -1032,29 +1062,6 @@ __global__ __launch_bounds__(256) void k_bwd_dq_final(const float* __restrict__ 
     if (e0 >= total) break;
     load_chunk(e0);  // r^2 D above kDqPer x 256
   }
-}
-
-// ---------------------------------------------------------------------------------------------------------
-// lambda gradient: every kernel entry k = exp(-D / lambda) moves by k D / lambda^2 = -k ln(k) / lambda, so
-// d/dlambda = -sum G ln(k) over G = dC C / lambda (Gq, Gk, and Gw = dW W / lambda off the diagonal, where W = W_eps
-// and the eps diagonal does not depend on lambda). The row-gradient kernel sums the Gq and Gk terms of each of
-// its blocks (it forms those G values), k_bwd_wpart the Gw terms of each landmark row; an entry whose k
-// underflowed to 0 has G = 0 and adds nothing. k_bwd_dlam_final adds the partials in a fixed order.
-// ---------------------------------------------------------------------------------------------------------
-// One block: thread t sums the partials t, t + 256, ... in order, then a fixed tree in LDS.
-__global__ __launch_bounds__(256) void k_bwd_dlam_final(const float* __restrict__ part, float* __restrict__ out,
-                                                        int n) {
-  const int tid = threadIdx.x;
-  float t = 0.f;
-  for (int i = tid; i < n; i += 256) t += part[i];
-  __shared__ float red[256];
-  red[tid] = t;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0) *out = red[0];
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -1277,10 +1284,8 @@ static hipError_t bwd_t(const Shape& s, bool whiten, const void* Qv, const void*
   }
   if (side && (e = hipEventRecord(side->join, side->s)) != hipSuccess) return bail(e);
   if (side && (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return bail(e);  // dLW, Gw's lambda terms
-  if (ex.d_lambda)
-    hipLaunchKernelGGL(k_bwd_dlam_final, dim3(1), dim3(256), 0, st, lp, ex.d_lambda, s.G * p.lamchunks);
-  hipLaunchKernelGGL((k_bwd_dq_final<T, D>), dim3(s.m, s.G), dim3(256), 0, st, dLpart, dLW, dQp, dQ, s.N, s.m, s.W,
-                     s.r, p.nsplitS);
+  hipLaunchKernelGGL((k_bwd_dq_final<T, D>), dim3(s.m + (ex.d_lambda ? 1 : 0), s.G), dim3(256), 0, st, dLpart, dLW,
+                     dQp, dQ, s.N, s.m, s.W, s.r, p.nsplitS, lp, ex.d_lambda, s.G * p.lamchunks);
   return hipGetLastError();
 }
 
