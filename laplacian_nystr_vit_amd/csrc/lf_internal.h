@@ -60,7 +60,7 @@ size_t ns_tmp_floats(const Shape& s);
 hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float* alpha, float* resid, float* tmp,
                      hipStream_t st);
 // Newton-Schulz (m <= 64) in one launch with S = C_K^T V computed in the CUs the solver leaves idle.
-// ns_side_supported: m <= 64, d in {16, 32, 64} and fewer slices than CUs.
+// ns_side_supported: m <= 64 and d in {16, 32, 64}. ns_laplace_supported also needs fewer slices than CUs.
 bool ns_side_supported(const Shape& s);
 // Newton-Schulz beside S = C_K^T V and the C_Q distance pass in one launch (Laplace kernel; C_K and W_eps from a
 // prior distance launch over the K and landmark rows). xs: saved iterates or null.

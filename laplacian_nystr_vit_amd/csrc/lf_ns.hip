@@ -531,6 +531,59 @@ __device__ __forceinline__ void ckv_tile_block(int blk, const float* __restrict_
   }
 }
 
+// All of slice g's S = C^T V by one block of 4 waves, for launches with more slices than CUs (few tokens per
+// slice): wave w takes tiles w, w + 4, .. of the slice and sums each over all N tokens by itself (the group loads
+// in batches as above), so the tiles need no reduction across waves.
+template <typename T, int D>
+__device__ __forceinline__ void ckv_slice_block(int g, const float* __restrict__ C, const T* __restrict__ V,
+                                                float* __restrict__ S, int N, int m) {
+  constexpr int DT = D / 16;
+  const int LT = (m + 15) / 16;
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
+  const int i = ln & 15, k = ln >> 4;
+  const int groups = (N + 15) / 16, qf = N / 16;  // groups [0, qf) have all 16 tokens in range
+  for (int tt = wv; tt < LT * DT; tt += 4) {
+    const int lt = tt / DT, ct = tt % DT;
+    const bool lok = lt * 16 + i < m;
+    const float* __restrict__ crow = C + (static_cast<size_t>(g) * m + (lok ? lt * 16 + i : 0)) * N;
+    const T* __restrict__ vcol = V + static_cast<size_t>(g) * N * D + ct * 16 + i;
+    const float amask = lok ? 1.f : 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < qf; q += kCkvBatch) {
+      float a[kCkvBatch][4], b[kCkvBatch][4];
+#pragma unroll
+      for (int j = 0; j < kCkvBatch; ++j) {
+        const int qj = min(q + j, qf - 1);  // past the range: the last group again with a zero weight
+        const int t = qj * 16 + 4 * k;
+        const float wj = q + j < qf ? amask : 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a[j][u] = crow[t + u] * wj;
+          b[j][u] = to_f32(vcol[static_cast<size_t>(t + u) * D]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kCkvBatch; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = mfma16x16x4(a[j][u], b[j][u], acc);
+    }
+    for (int q = qf; q < groups; ++q) {  // the ragged last group
+      const int t = q * 16 + 4 * k;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool in = t + u < N;
+        const float a = in ? crow[t + u] * amask : 0.f;
+        const float b = in ? to_f32(vcol[static_cast<size_t>(t + u) * D]) : 0.f;
+        acc = mfma16x16x4(a, b, acc);
+      }
+    }
+    // acc[r] is row 4k + r, column i of the tile
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (lt * 16 + 4 * k + r < m) S[(static_cast<size_t>(g) * m + lt * 16 + 4 * k + r) * D + ct * 16 + i] = acc[r];
+  }
+}
+
 // Tile order of the S tiles of a launch (j < total): consecutive tiles are dealt to the 8 XCDs round-robin, so the
 // order is remapped to keep the tiles of one slice on one XCD: each slice's C_K rows and V columns are read by
 // several tiles, and one L2 then serves the repeats.
@@ -543,11 +596,16 @@ template <typename T, int D, int ST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_ns_side(const float* __restrict__ We, float* __restrict__ Xout,
                                                  float* __restrict__ xs, float* __restrict__ alpha_out, int m,
                                                  int iters, int N, int G, const float* __restrict__ CK,
-                                                 const T* __restrict__ V, float* __restrict__ S) {
+                                                 const T* __restrict__ V, float* __restrict__ S, int per_slice) {
   const int b = static_cast<int>(blockIdx.x);
   if (b < G) {
     __shared__ __attribute__((aligned(16))) char lds[kNsSmallLds];
     ns_small_block<ST>(lds, b, We, Xout, xs, alpha_out, nullptr, m, iters);
+    return;
+  }
+  if (per_slice) {  // one block per slice (more slices than CUs): side block j is slice j
+    const int s0 = (G + 7) & ~7;
+    if (b >= s0) ckv_slice_block<T, D>(b - s0, CK, V, S, N, m);
     return;
   }
   // The S tiles start at the first multiple of 8 after the solver blocks (the blocks in between exit at once), so
@@ -602,11 +660,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 template <typename T, int D>
 static void ns_side_st(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
                        const T* V, float* S, hipStream_t st) {
-  const int blocks = ((s.G + 7) & ~7) + s.G * ((s.m + 15) / 16 * (D / 16));  // solver blocks, padding, S tiles
+  // With at least as many slices as CUs the solver blocks alone fill the chip, and S comes from one block per
+  // slice (fewer, longer side blocks) instead of one per 16 x 16 tile.
+  const int per_slice = s.G >= 256 ? 1 : 0;
+  const int side = per_slice ? s.G : s.G * ((s.m + 15) / 16 * (D / 16));
+  const int blocks = ((s.G + 7) & ~7) + side;  // solver blocks, padding, S blocks
   const int nt = (s.m + 15) / 16;
 #define LF_NS_SIDE(ST_)                                                                                        \
   hipLaunchKernelGGL((k_ns_side<T, D, ST_>), dim3(blocks), dim3(256), 0, st, We, X, xs, alpha, s.m, s.ns_iters, \
-                     s.N, s.G, CK, V, S)
+                     s.N, s.G, CK, V, S, per_slice)
   if (nt == 1)
     LF_NS_SIDE(1);
   else if (nt == 2)
@@ -616,9 +678,7 @@ static void ns_side_st(const Shape& s, const float* We, float* X, float* xs, flo
 #undef LF_NS_SIDE
 }
 
-bool ns_side_supported(const Shape& s) {
-  return s.m <= 64 && (s.d == 16 || s.d == 32 || s.d == 64) && s.G < 256;
-}
+bool ns_side_supported(const Shape& s) { return s.m <= 64 && (s.d == 16 || s.d == 32 || s.d == 64); }
 
 template <typename T>
 static void ns_side_t(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
@@ -641,7 +701,7 @@ hipError_t launch_ns_side(const Shape& s, const float* We, float* X, float* xs, 
   return hipGetLastError();
 }
 
-bool ns_laplace_supported(const Shape& s) { return ns_side_supported(s); }
+bool ns_laplace_supported(const Shape& s) { return ns_side_supported(s) && s.G < 256; }
 
 template <typename T, int D>
 static void ns_laplace_st(const Shape& s, const float* We, float* X, float* xs, float* alpha, const float* CK,
