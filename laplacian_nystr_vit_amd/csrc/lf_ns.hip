@@ -532,55 +532,83 @@ __device__ __forceinline__ void ckv_tile_block(int blk, const float* __restrict_
 }
 
 // All of slice g's S = C^T V by one block of 4 waves, for launches with more slices than CUs (few tokens per
-// slice): wave w takes tiles w, w + 4, .. of the slice and sums each over all N tokens by itself (the group loads
-// in batches as above), so the tiles need no reduction across waves.
+// slice): wave w takes tiles w, w + 4, .. (at most 4) of the slice and sums each over all N tokens by itself, so
+// the tiles need no reduction across waves. The loads go out in batches that cover all of the wave's tiles at
+// once (3 token groups of each), and the ragged last group of every tile in one more batch: a tile-by-tile walk
+// waited for twice as many memory round trips.
+constexpr int kSliceGpb = 3;  // 16-token groups of each tile per batch
+
 template <typename T, int D>
 __device__ __forceinline__ void ckv_slice_block(int g, const float* __restrict__ C, const T* __restrict__ V,
                                                 float* __restrict__ S, int N, int m) {
-  constexpr int DT = D / 16;
-  const int LT = (m + 15) / 16;
+  constexpr int DT = D / 16, TPW = 4;
+  const int LT = (m + 15) / 16, ntile = LT * DT;
   const int wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
   const int i = ln & 15, k = ln >> 4;
   const int groups = (N + 15) / 16, qf = N / 16;  // groups [0, qf) have all 16 tokens in range
-  for (int tt = wv; tt < LT * DT; tt += 4) {
-    const int lt = tt / DT, ct = tt % DT;
-    const bool lok = lt * 16 + i < m;
-    const float* __restrict__ crow = C + (static_cast<size_t>(g) * m + (lok ? lt * 16 + i : 0)) * N;
-    const T* __restrict__ vcol = V + static_cast<size_t>(g) * N * D + ct * 16 + i;
-    const float amask = lok ? 1.f : 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < qf; q += kCkvBatch) {
-      float a[kCkvBatch][4], b[kCkvBatch][4];
+  const float* crow[TPW];
+  const T* vcol[TPW];
+  float amask[TPW];
 #pragma unroll
-      for (int j = 0; j < kCkvBatch; ++j) {
-        const int qj = min(q + j, qf - 1);  // past the range: the last group again with a zero weight
-        const int t = qj * 16 + 4 * k;
-        const float wj = q + j < qf ? amask : 0.f;
+  for (int j = 0; j < TPW; ++j) {
+    const int tt = min(wv + 4 * j, ntile - 1), lt = tt / DT, ct = tt % DT;
+    const bool lok = lt * 16 + i < m && wv + 4 * j < ntile;
+    crow[j] = C + (static_cast<size_t>(g) * m + (lt * 16 + i < m ? lt * 16 + i : 0)) * N;
+    vcol[j] = V + static_cast<size_t>(g) * N * D + ct * 16 + i;
+    amask[j] = lok ? 1.f : 0.f;
+  }
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < qf; q += kSliceGpb) {
+    float a[TPW][kSliceGpb][4], b[TPW][kSliceGpb][4];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int h = 0; h < kSliceGpb; ++h) {
+        const int qh = min(q + h, qf - 1);  // past the range: the last group again with a zero weight
+        const int t = qh * 16 + 4 * k;
+        const float wh = q + h < qf ? amask[j] : 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          a[j][u] = crow[t + u] * wj;
-          b[j][u] = to_f32(vcol[static_cast<size_t>(t + u) * D]);
+          a[j][h][u] = crow[j][t + u] * wh;
+          b[j][h][u] = to_f32(vcol[j][static_cast<size_t>(t + u) * D]);
         }
       }
 #pragma unroll
-      for (int j = 0; j < kCkvBatch; ++j)
+    for (int j = 0; j < TPW; ++j)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc = mfma16x16x4(a[j][u], b[j][u], acc);
-    }
-    for (int q = qf; q < groups; ++q) {  // the ragged last group
-      const int t = q * 16 + 4 * k;
+      for (int h = 0; h < kSliceGpb; ++h)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[j] = mfma16x16x4(a[j][h][u], b[j][h][u], acc[j]);
+  }
+  if (qf < groups) {  // the ragged last group of every tile
+    const int t = qf * 16 + 4 * k;
+    float a[TPW][4], b[TPW][4];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const bool in = t + u < N;
-        const float a = in ? crow[t + u] * amask : 0.f;
-        const float b = in ? to_f32(vcol[static_cast<size_t>(t + u) * D]) : 0.f;
-        acc = mfma16x16x4(a, b, acc);
+        const size_t tc = static_cast<size_t>(in ? t + u : N - 1);
+        a[j][u] = in ? crow[j][tc] * amask[j] : 0.f;
+        b[j][u] = in ? to_f32(vcol[j][tc * D]) : 0.f;
       }
-    }
-    // acc[r] is row 4k + r, column i of the tile
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[j] = mfma16x16x4(a[j][u], b[j][u], acc[j]);
+  }
+  // acc[j][r] is row 4k + r, column i of the wave's tile j
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int tt = wv + 4 * j;
+    if (tt >= ntile) continue;
+    const int lt = tt / DT, ct = tt % DT;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (lt * 16 + 4 * k + r < m) S[(static_cast<size_t>(g) * m + lt * 16 + 4 * k + r) * D + ct * 16 + i] = acc[r];
+      if (lt * 16 + 4 * k + r < m)
+        S[(static_cast<size_t>(g) * m + lt * 16 + 4 * k + r) * D + ct * 16 + i] = acc[j][r];
   }
 }
 
