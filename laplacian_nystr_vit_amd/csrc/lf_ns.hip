@@ -933,17 +933,48 @@ struct NsTileLds {
 // One block's work on tile (ti, tj) of slice g for job J; NT = mp / 32 tiles per side.
 template <bool AW, bool BW, int NT>
 __device__ __forceinline__ void ns_tile_body(const NsJob& J, const NsInit& init, const float* __restrict__ We, int m,
-                                             int g, NsTileLds& L) {
+                                             int g, int ti, int tj, NsTileLds& L) {
   constexpr int mp = NT * kTile, nt = NT;
   _Float16* sA = L.a;
   _Float16* sB = L.b;
   float* s_red = L.red;
   double* s_cmax = L.cmax;
   double* s_rmax = L.rmax;
-  const int tj = blockIdx.x, ti = blockIdx.y;
   const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
   const size_t mpp = static_cast<size_t>(mp) * mp, mm = static_cast<size_t>(m) * m;
   const float* wg = We + g * mm;
+
+  // The exponents of A's row of tiles and B's column of tiles: one power of two per 32-wide K chunk, loaded with
+  // the strips so that their round trip overlaps the staging.
+  int ech[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    const int ea = J.a_exp ? J.a_exp[(static_cast<size_t>(g) * nt + ti) * nt + c] : 0;
+    const int eb = J.b_exp ? J.b_exp[(static_cast<size_t>(g) * nt + c) * nt + tj] : 0;
+    ech[c] = ea + eb;
+  }
+  // The wave's 16 x 16 sub-tile (wi, wj); the lane's output rows i0 .. i0+3 of column j.
+  const int wi = wv & 1, wj = wv >> 1, gq = ln >> 4, t = ln & 15;
+  const int i0 = ti * kTile + wi * 16 + 4 * gq, j = tj * kTile + wj * 16 + t;
+  // The first launch's own inputs, loaded with the strips: the alpha chunk partials of column tid (m <= 256
+  // columns, at most 32 chunks), chunk tid's largest row sum, and the lane's entries of W^T for X_0.
+  constexpr int kMaxCh = LF_NS_KMAX / kNsRows;
+  double pv[kMaxCh], rmx0 = 0.0;
+  float wt[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (AW && BW) {
+    if (init.part) {
+      const int jc = tid < m ? tid : 0;
+#pragma unroll
+      for (int c = 0; c < kMaxCh; ++c)
+        pv[c] = init.part[(static_cast<size_t>(g) * init.nch + (c < init.nch ? c : 0)) * m + jc];
+      rmx0 = tid < init.nch ? init.rmx[static_cast<size_t>(g) * init.nch + tid] : 0.0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = i0 + r < m && j < m;
+        wt[r] = wg[ok ? static_cast<size_t>(j) * m + i0 + r : 0];
+      }
+    }
+  }
 
   // 1. Stage both strips: every global load is issued before the first LDS store.
   // Each strip is 8 mp 16-byte pieces, NT per thread; a thread's loads are all issued before its first store.
@@ -986,21 +1017,14 @@ __device__ __forceinline__ void ns_tile_body(const NsJob& J, const NsInit& init,
   }
   // alpha = 1 / (max column sum * max row sum) of |W| from the chunk partials, in a fixed order.
   float scale = 1.f;
-  if (init.part) {
-    // thread j sums column j's chunk partials (m <= 256 columns, at most 32 chunks), every load in flight first
-    constexpr int kMaxCh = LF_NS_KMAX / kNsRows;
-    double pv[kMaxCh];
-    const int j = tid < m ? tid : 0;
-#pragma unroll
-    for (int c = 0; c < kMaxCh; ++c)
-      pv[c] = init.part[(static_cast<size_t>(g) * init.nch + (c < init.nch ? c : 0)) * m + j];
+  if (AW && BW && init.part) {
+    // thread j sums column j's chunk partials; chunk c's largest row sum comes from thread c
     double cs = 0.0;
 #pragma unroll
     for (int c = 0; c < kMaxCh; ++c)
       if (c < init.nch) cs += pv[c];
     double cmax = tid < m ? cs : 0.0;
-    // chunk c's largest row sum comes from thread c (at most 32 chunks)
-    double rmax = tid < init.nch ? init.rmx[static_cast<size_t>(g) * init.nch + tid] : 0.0;
+    double rmax = rmx0;
     for (int off = 32; off > 0; off >>= 1) {
       cmax = fmax(cmax, __shfl_xor(cmax, off));
       rmax = fmax(rmax, __shfl_xor(rmax, off));
@@ -1018,20 +1042,10 @@ __device__ __forceinline__ void ns_tile_body(const NsJob& J, const NsInit& init,
     }
   }
   __syncthreads();
-  if (init.part) scale = L.alpha;
+  if (AW && BW && init.part) scale = L.alpha;
 
   // 2. The wave's 16 x 16 sub-tile (wi, wj), chunk by chunk: three split-fp16 MFMAs per chunk into a fresh
-  //    accumulator, folded into the sum with the chunk's power of two (the exponents of A's row of tiles and B's
-  //    column of tiles, read before the first chunk).
-  const int wi = wv & 1, wj = wv >> 1;
-  int ech[NT];
-#pragma unroll
-  for (int c = 0; c < NT; ++c) {
-    const int ea = J.a_exp ? J.a_exp[(static_cast<size_t>(g) * nt + ti) * nt + c] : 0;
-    const int eb = J.b_exp ? J.b_exp[(static_cast<size_t>(g) * nt + c) * nt + tj] : 0;
-    ech[c] = ea + eb;
-  }
-  const int gq = ln >> 4, t = ln & 15;
+  //    accumulator, folded into the sum with the chunk's power of two.
   half8 ah[NT], al[NT], bh[NT], bl[NT];
 #pragma unroll
   for (int c = 0; c < NT; ++c) {
@@ -1070,7 +1084,6 @@ __device__ __forceinline__ void ns_tile_body(const NsJob& J, const NsInit& init,
   }
 
   // 3. Outputs. The lane holds rows i0 .. i0+3 of column j.
-  const int i0 = ti * kTile + wi * 16 + 4 * gq, j = tj * kTile + wj * 16 + t;
   f32x4 v;
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = acc[r] * scale;
@@ -1110,11 +1123,11 @@ __device__ __forceinline__ void ns_tile_body(const NsJob& J, const NsInit& init,
       if (O.f32b) O.f32b[g * O.f32b_stride + static_cast<size_t>(i) * m + j] = o;
     }
   }
-  if (init.part) {
+  if (AW && BW && init.part) {
     // X_0 = alpha W^T over this tile: X_0[i][j] = alpha W[j][i] (rows i0 .. i0+3 of column j, contiguous in W).
     f32x4 x;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = (i0 + r < m && j < m) ? scale * wg[static_cast<size_t>(j) * m + i0 + r] : 0.f;
+    for (int r = 0; r < 4; ++r) x[r] = (i0 + r < m && j < m) ? scale * wt[r] : 0.f;
     const float mx = block4_max_nonneg(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))),
                                        s_red);
     const int e = store_exp(mx);
@@ -1134,22 +1147,29 @@ __device__ __forceinline__ void ns_tile_body(const NsJob& J, const NsInit& init,
   }
 }
 
-// Block (tj, ti, z): tile (ti, tj) of slice z / njobs for job z % njobs (j0 or j1).
+// One block per output tile of nz products (z = slice * njobs + job; job z % njobs is j0 or j1). The 8 XCDs take
+// blocks round robin (block b on XCD b % 8), so when the tile count is a multiple of 8 block b takes tile
+// (b % 8) (count / 8) + b / 8: each XCD gets a contiguous run of whole rows of tiles of one product and reads few
+// distinct A strips, instead of every XCD reading every A strip. Any bijection is correct; this one is for L2.
 template <bool AW, bool BW, int NT>
 __global__ __launch_bounds__(256) void k_ns_tile(NsJob j0, NsJob j1, int njobs, NsInit init,
                                                  const float* __restrict__ We, int m) {
   __shared__ NsTileLds lds;
-  const int g = blockIdx.z / njobs;
-  if (blockIdx.z % njobs == 0)
-    ns_tile_body<AW, BW, NT>(j0, init, We, m, g, lds);
+  const int nb = gridDim.x, b = blockIdx.x;
+  const int t = (nb & 7) == 0 ? (b & 7) * (nb >> 3) + (b >> 3) : b;
+  const int z = t / (NT * NT), r = t % (NT * NT), ti = r / NT, tj = r % NT;
+  const int g = z / njobs;
+  if (z % njobs == 0)
+    ns_tile_body<AW, BW, NT>(j0, init, We, m, g, ti, tj, lds);
   else
-    ns_tile_body<AW, BW, NT>(j1, init, We, m, g, lds);
+    ns_tile_body<AW, BW, NT>(j1, init, We, m, g, ti, tj, lds);
 }
 
-// k_ns_tile for the tile count of m: 3 .. 8 (65 <= m <= 256).
+// k_ns_tile for the tile count of m: 3 .. 8 (65 <= m <= 256), over nz products.
 template <bool AW, bool BW>
-static void ns_tile_launch(int nt, dim3 grid, hipStream_t st, const NsJob& j0, const NsJob& j1, int njobs,
+static void ns_tile_launch(int nt, int nz, hipStream_t st, const NsJob& j0, const NsJob& j1, int njobs,
                            const NsInit& init, const float* We, int m) {
+  const dim3 grid(nt * nt * nz);
 #define LF_NS_TILE(NT_)                                                                                        \
   hipLaunchKernelGGL((k_ns_tile<AW, BW, NT_>), grid, dim3(256), 0, st, j0, j1, njobs, init, We, m)
   switch (nt) {
@@ -1232,7 +1252,7 @@ hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float
     j.out.t = Tb[0];
     j.out.u = Ub[0];
     NsInit in{part, rmx, nch, alpha, Xb[0], Xe[0], K == 0 ? X : nullptr, slot(0), xs_stride};
-    ns_tile_launch<true, true>(nt, dim3(nt, nt, G), st, j, none, 1, in, We, m);
+    ns_tile_launch<true, true>(nt, G, st, j, none, 1, in, We, m);
   }
   int tc = 0, xc = 0;  // buffers holding T_k, U_k and X_k
   for (int k = 0; k + 1 < K;) {
@@ -1243,7 +1263,7 @@ hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float
       j.b_exp = Xe[xc];
       j.out.t = Tb[tc];
       j.out.u = Ub[tc];
-      ns_tile_launch<true, false>(nt, dim3(nt, nt, G), st, j, none, 1, noinit, We, m);
+      ns_tile_launch<true, false>(nt, G, st, j, none, 1, noinit, We, m);
     }
     const int end = std::min(k + kPairRun, K - 1);
     for (; k < end; ++k) {
@@ -1263,7 +1283,7 @@ hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float
       jt.out.t = Tb[tc ^ 1];
       jt.out.u = Ub[tc ^ 1];
       const int nj = last ? 1 : 2;
-      ns_tile_launch<false, false>(nt, dim3(nt, nt, nj * G), st, jx, jt, nj, noinit, We, m);
+      ns_tile_launch<false, false>(nt, nj * G, st, jx, jt, nj, noinit, We, m);
       tc ^= 1;
       xc ^= 1;
     }
@@ -1275,7 +1295,7 @@ hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float
     ju.b = Xb[xc];
     ju.b_exp = Xe[xc];
     ju.out.u = Ub[tc];
-    ns_tile_launch<true, false>(nt, dim3(nt, nt, G), st, ju, none, 1, noinit, We, m);
+    ns_tile_launch<true, false>(nt, G, st, ju, none, 1, noinit, We, m);
     NsJob jx{};
     jx.a = Xb[xc];
     jx.a_exp = Xe[xc];
@@ -1288,7 +1308,7 @@ hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float
       jx.out.x = Xb[xc ^ 1];
       jx.out.x_exp = Xe[xc ^ 1];
     }
-    ns_tile_launch<false, false>(nt, dim3(nt, nt, G), st, jx, none, 1, noinit, We, m);
+    ns_tile_launch<false, false>(nt, G, st, jx, none, 1, noinit, We, m);
     xc ^= 1;
   }
   if (resid) {
@@ -1300,7 +1320,7 @@ hipError_t launch_ns(const Shape& s, const float* We, float* X, float* xs, float
     jr.out.f32 = E;
     jr.out.f32_stride = mm;
     jr.out.minus_eye = 1;
-    ns_tile_launch<true, false>(nt, dim3(nt, nt, G), st, jr, none, 1, noinit, We, m);
+    ns_tile_launch<true, false>(nt, G, st, jr, none, 1, noinit, We, m);
     hipLaunchKernelGGL(k_frob, dim3(G), dim3(256), 0, st, E, resid, m);
   }
   return hipGetLastError();
