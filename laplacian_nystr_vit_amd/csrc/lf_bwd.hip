@@ -109,23 +109,28 @@ BwdWs plan(const Shape& s) {
 // column means. m x m x d work per slice, on the VALU. The slice's output rows are spread over gridDim.y blocks
 // (rows l = blockIdx.y, blockIdx.y + gridDim.y, ...); each block forms the whole dP, which every dS row needs.
 // ---------------------------------------------------------------------------------------------------------
-// Copy of n <= MAXN floats from global memory to LDS by the NT threads of a block: every load is issued before the
-// first store, so the block waits for one memory round trip instead of one per strided pass.
+// Up to MAXN floats of a flat array, spread over the NT threads of a block (element it * NT + threadIdx.x in v[it]).
+// Loads go to clamped addresses (n >= 1), so a block can issue the loads of several arrays before the first LDS
+// store and wait for one memory round trip instead of one per array.
 template <int NT, int MAXN>
-__device__ __forceinline__ void stage_flat(float* __restrict__ dst, const float* __restrict__ src, int n) {
-  constexpr int IT = (MAXN + NT - 1) / NT;
+struct FlatRegs {
+  static constexpr int IT = (MAXN + NT - 1) / NT;
   float v[IT];
+  __device__ __forceinline__ void load(const float* __restrict__ src, int n) {
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int idx = static_cast<int>(threadIdx.x) + it * NT;
-    v[it] = idx < n ? src[idx] : 0.f;
+    for (int it = 0; it < IT; ++it) {
+      const int idx = static_cast<int>(threadIdx.x) + it * NT;
+      v[it] = src[idx < n ? idx : 0];
+    }
   }
+  __device__ __forceinline__ void store(float* __restrict__ dst, int n) const {
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int idx = static_cast<int>(threadIdx.x) + it * NT;
-    if (idx < n) dst[idx] = v[it];
+    for (int it = 0; it < IT; ++it) {
+      const int idx = static_cast<int>(threadIdx.x) + it * NT;
+      if (idx < n) dst[idx] = v[it];
+    }
   }
-}
+};
 
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_small1(const float* __restrict__ T1, const float* __restrict__ S,
@@ -138,18 +143,36 @@ __global__ __launch_bounds__(256) void k_bwd_small1(const float* __restrict__ T1
   __shared__ float sP[64 * D];
   __shared__ float sdP[64 * D];
   __shared__ float sX[64 * 64];
+  __shared__ float sMu[64], sRs[64];
   const int g = blockIdx.x, part = blockIdx.y, nparts = gridDim.y, tid = threadIdx.x;
   const size_t md = static_cast<size_t>(m) * D, mm = static_cast<size_t>(m) * m;
   const float* t1 = T1 + static_cast<size_t>(g) * (m + 1) * D;
-  stage_flat<256, 65 * D>(sT1, t1, (m + 1) * D);
-  stage_flat<256, 64 * D>(sS, S + g * md, m * D);
-  stage_flat<256, 64 * D>(sP, P + g * md, m * D);
-  stage_flat<256, 64 * 64>(sX, xs + (static_cast<size_t>(g) * (K + 1) + K) * mm, m * m);
+  // every load (T1, S, P, X_K and the whitening mean and scale) in flight before the first LDS store
+  FlatRegs<256, 65 * D> rT;
+  FlatRegs<256, 64 * D> rS, rP;
+  FlatRegs<256, 64 * 64> rX;
+  rT.load(t1, (m + 1) * D);
+  rS.load(S + g * md, m * D);
+  rP.load(P + g * md, m * D);
+  rX.load(xs + (static_cast<size_t>(g) * (K + 1) + K) * mm, m * m);
+  float mu_v = 0.f, rs_v = 1.f;
+  if (whiten && tid < m) {
+    mu_v = mu[g * m + tid];
+    rs_v = rstd[g * m + tid];
+  }
+  rT.store(sT1, (m + 1) * D);
+  rS.store(sS, m * D);
+  rP.store(sP, m * D);
+  rX.store(sX, m * m);
+  if (tid < m) {
+    sMu[tid] = mu_v;
+    sRs[tid] = rs_v;
+  }
   __syncthreads();
   for (int idx = tid; idx < m * D; idx += 256) {
     const int l = idx / D, c = idx % D;
     float v = sT1[idx];
-    if (whiten) v = rstd[g * m + l] * (v - mu[g * m + l] * sT1[m * D + c]);
+    if (whiten) v = sRs[l] * (v - sMu[l] * sT1[m * D + c]);
     sdP[idx] = v;
   }
   __syncthreads();
