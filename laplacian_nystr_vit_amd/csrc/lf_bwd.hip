@@ -734,6 +734,37 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
   const T* A = (side == 0 ? dY : V) + static_cast<size_t>(g) * N * D;
   const float* Bm = (side == 0 ? P : dS) + static_cast<size_t>(g) * m * D;
+  const float* cm = (side == 0 ? CQ : CK) + static_cast<size_t>(g) * m * N;  // landmark-major [m][N]
+  // The lane's 4 values of each landmark tile t are 4 consecutive tokens ib .. ib+3 of landmark t*16 + (ln & 15):
+  // one 16-byte load of C and store of G each when they are all in range and N keeps them aligned.
+  const int ib = i0 + wv * 16 + 4 * (ln >> 4);
+  const bool vec = (N & 3) == 0 && ib + 3 < N;
+  // The epilogue's inputs (C and, for whitened C_Q, the landmark's mean, scale and two column statistics) do
+  // not depend on the products: loaded here, their round trip overlaps the staging and the MFMAs.
+  f32x4 cv[4];
+  float wmu[4], wrs[4], wma[4], wmaa[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int l = t * 16 + (ln & 15), lc = l < m ? l : 0;
+    const float* crow = cm + static_cast<size_t>(lc) * N;
+    if (vec) {
+      const float4 c4 = *reinterpret_cast<const float4*>(crow + ib);
+      cv[t] = f32x4{c4.x, c4.y, c4.z, c4.w};
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cv[t][r] = crow[ib + r < N ? ib + r : N - 1];
+    }
+    wmu[t] = 0.f;
+    wrs[t] = 1.f;
+    wma[t] = 0.f;
+    wmaa[t] = 0.f;
+    if (side == 0 && whiten) {
+      wmu[t] = mu[static_cast<size_t>(g) * m + lc];
+      wrs[t] = rstd[static_cast<size_t>(g) * m + lc];
+      wma[t] = stats[static_cast<size_t>(g) * 2 * m + lc];
+      wmaa[t] = stats[static_cast<size_t>(g) * 2 * m + m + lc];
+    }
+  }
   {
     // both tiles' loads in flight before the first LDS store
     constexpr int IT = 64 * D / 256;
@@ -765,27 +796,16 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = mfma16x16x4(a, sB[k * LDB + t * 16 + (ln & 15)], acc[t]);
   }
-  const float* cm = (side == 0 ? CQ : CK) + static_cast<size_t>(g) * m * N;  // landmark-major [m][N]
   // Gq / Gk are written landmark-major too, [m][N]: the dL reduction then reads a landmark's weights for
   // consecutive tokens as one contiguous run, and the token-row kernel reads them coalesced across its lanes.
   float* out = (side == 0 ? Gq : Gk) + static_cast<size_t>(g) * m * N;
-  // the lane's 4 values are 4 consecutive tokens of one landmark: one 16-byte load of C and store of G each when
-  // they are all in range and N keeps them aligned
-  const int ib = i0 + wv * 16 + 4 * (ln >> 4);
-  const bool vec = (N & 3) == 0 && ib + 3 < N;
   float lam = 0.f;  // this lane's share of -sum G ln(C) (the lambda gradient)
   auto lam_term = [](float gv, float c) { return c > 0.f ? -gv * __logf(c) : 0.f; };
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int l = t * 16 + (ln & 15);
     if (l >= m) continue;
-    float mu_l = 0.f, rs_l = 1.f, mA = 0.f, mAA = 0.f;
-    if (side == 0 && whiten) {
-      mu_l = mu[static_cast<size_t>(g) * m + l];
-      rs_l = rstd[static_cast<size_t>(g) * m + l];
-      mA = stats[static_cast<size_t>(g) * 2 * m + l];
-      mAA = stats[static_cast<size_t>(g) * 2 * m + m + l];
-    }
+    const float mu_l = wmu[t], rs_l = wrs[t], mA = wma[t], mAA = wmaa[t];
     auto grad = [&](float v, float c) {
       if (side == 0 && whiten) {
         const float ahat = (c - mu_l) * rs_l;
@@ -794,17 +814,17 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
       return v * c * inv_lam;
     };
     if (vec) {
-      const float4 c4 = *reinterpret_cast<const float4*>(cm + static_cast<size_t>(l) * N + ib);
-      const float4 o = make_float4(grad(acc[t][0], c4.x), grad(acc[t][1], c4.y), grad(acc[t][2], c4.z),
-                                   grad(acc[t][3], c4.w));
+      const f32x4 c4 = cv[t];
+      const float4 o = make_float4(grad(acc[t][0], c4[0]), grad(acc[t][1], c4[1]), grad(acc[t][2], c4[2]),
+                                   grad(acc[t][3], c4[3]));
       *reinterpret_cast<float4*>(out + static_cast<size_t>(l) * N + ib) = o;
-      lam += lam_term(o.x, c4.x) + lam_term(o.y, c4.y) + lam_term(o.z, c4.z) + lam_term(o.w, c4.w);
+      lam += lam_term(o.x, c4[0]) + lam_term(o.y, c4[1]) + lam_term(o.z, c4[2]) + lam_term(o.w, c4[3]);
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = ib + r;
         if (i < N) {
-          const float c = cm[static_cast<size_t>(l) * N + i], o = grad(acc[t][r], c);
+          const float c = cv[t][r], o = grad(acc[t][r], c);
           out[static_cast<size_t>(l) * N + i] = o;
           lam += lam_term(o, c);
         }
