@@ -22,7 +22,9 @@
  *            or frees memory, never synchronises and holds no state between calls: no stream, event or buffer of
  *            its own. Work is enqueued on `stream` (a hipStream_t; NULL means the null stream) and the call returns
  *            as soon as it is enqueued. Only lf_attn_bwd_ex can spread its work over a second stream, and only one
- *            the caller lends it (lf_aux_stream).
+ *            the caller lends it (lf_aux_stream). A call enqueues kernels (and, for lf_attn_bwd_ex with a lent
+ *            stream, event records and waits) and nothing else: no copy, clear or synchronisation, so it can be
+ *            captured in a HIP graph (the lent stream joins the capture through its events) and replayed.
  *  Errors:   every entry point returns LF_OK (0) or a negative code. Parameters, pointers and workspace sizes are
  *            checked on the host before anything is launched; on an error nothing is launched. LF_EHIP reports a
  *            failed launch (hipGetLastError). Nothing throws across this ABI. Calls are reentrant; calls that
