@@ -24,6 +24,7 @@
 #include "../../include/lf_attn.h"
 #include "lf_bwd_internal.h"
 #include "lf_device.h"
+#include "lf_split.h"
 
 namespace lf {
 
@@ -714,9 +715,11 @@ __global__ __launch_bounds__(256) void k_bwd_wpart(const float* __restrict__ L, 
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// Row gradients of the kernel matrices on fp32 MFMA: dA_hat = dY P^T (side 0) and dC_K = V dS^T (side 1),
-// 64 tokens x m landmarks per block, K = d. The epilogue applies the whitening backward and the kernel
-// derivative factor: Gq = dC_Q C_Q / lambda, Gk = dC_K C_K / lambda.
+// Row gradients of the kernel matrices: dA_hat = dY P^T (side 0) and dC_K = V dS^T (side 1), 64 tokens x m
+// landmarks per block, K = d. The products run on the fp16 MFMA in split form (x = hi + lo, A B ~= A_hi B_hi +
+// A_hi B_lo + A_lo B_hi, fp32 accumulation): each operand tile is scaled by a power of two that puts its largest
+// entry in [2^12, 2^13) and the product is scaled back exactly. The epilogue applies the whitening backward and
+// the kernel derivative factor: Gq = dC_Q C_Q / lambda, Gk = dC_K C_K / lambda.
 // ---------------------------------------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, const T* __restrict__ V,
@@ -726,10 +729,14 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
                                                      const float* __restrict__ stats, float* __restrict__ Gq,
                                                      float* __restrict__ Gk, float* __restrict__ lam_part, int N,
                                                      int m, float inv_lam, int whiten) {
-  constexpr int LDA = D + 2;  // 2 mod 4 with LDA/2 odd: conflict-free A-style reads
-  constexpr int LDB = 80;     // 16 mod 32
-  __shared__ float sA[64 * LDA];
-  __shared__ float sB[D * LDB];
+  constexpr int KP = D < 32 ? 32 : D;  // K padded to the MFMA's 32
+  constexpr int LDH = KP + 8;           // fp16 row stride: 16 bytes mod 128, conflict-free 16-byte reads
+  // both operands as [row][k] fp16 halves: A rows are tokens, B rows are landmarks (rows past m are zeros)
+  __shared__ __align__(16) _Float16 sAh[64 * LDH];
+  __shared__ __align__(16) _Float16 sAl[64 * LDH];
+  __shared__ __align__(16) _Float16 sBh[64 * LDH];
+  __shared__ __align__(16) _Float16 sBl[64 * LDH];
+  __shared__ float sMax[8];
   const int side = blockIdx.z, g = blockIdx.y, i0 = blockIdx.x * 64;
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
   const T* A = (side == 0 ? dY : V) + static_cast<size_t>(g) * N * D;
@@ -765,37 +772,83 @@ __global__ __launch_bounds__(256) void k_bwd_rowgrad(const T* __restrict__ dY, c
       wmaa[t] = stats[static_cast<size_t>(g) * 2 * m + m + lc];
     }
   }
+  int esc;  // ea + eb: the two tiles' scale exponents, undone on the result
   {
-    // both tiles' loads in flight before the first LDS store
-    constexpr int IT = 64 * D / 256;
-    float va[IT], vb[IT];
+    // both tiles' loads (4 channels each) in flight before the first LDS store
+    constexpr int Q4 = 64 * D / 4 / 256;
+    float4 va[Q4], vb[Q4];
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int idx = tid + it * 256;
-      const int r = idx / D, c = idx % D;  // token row of A, landmark of B
-      va[it] = (i0 + r < N) ? to_f32(A[static_cast<size_t>(i0 + r) * D + c]) : 0.f;
-      vb[it] = (r < m) ? Bm[static_cast<size_t>(r) * D + c] : 0.f;
+    for (int q = 0; q < Q4; ++q) {
+      const int idx = tid + q * 256;
+      const int r = idx / (D / 4), c4 = 4 * (idx % (D / 4));  // token row of A, landmark row of B
+      va[q] = (i0 + r < N) ? load4(A + static_cast<size_t>(i0 + r) * D + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      vb[q] = (r < m) ? load4(Bm + static_cast<size_t>(r) * D + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float ma = 0.f, mb = 0.f;
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int idx = tid + it * 256;
-      const int r = idx / D, c = idx % D;
-      sA[r * LDA + c] = va[it];
-      sB[c * LDB + r] = vb[it];
+    for (int q = 0; q < Q4; ++q) {
+      ma = fmaxf(ma, fmaxf(fmaxf(fabsf(va[q].x), fabsf(va[q].y)), fmaxf(fabsf(va[q].z), fabsf(va[q].w))));
+      mb = fmaxf(mb, fmaxf(fmaxf(fabsf(vb[q].x), fabsf(vb[q].y)), fmaxf(fabsf(vb[q].z), fabsf(vb[q].w))));
+    }
+    ma = wave_max_nonneg(ma);
+    mb = wave_max_nonneg(mb);
+    if (ln == 0) {
+      sMax[wv] = ma;
+      sMax[4 + wv] = mb;
+    }
+    if constexpr (D < 32) {  // the K padding of every row is zero
+      const int r = tid >> 2, c4 = D + 4 * (tid & 3);
+      const half4 z = {0, 0, 0, 0};
+      *reinterpret_cast<half4*>(&sAh[r * LDH + c4]) = z;
+      *reinterpret_cast<half4*>(&sAl[r * LDH + c4]) = z;
+      *reinterpret_cast<half4*>(&sBh[r * LDH + c4]) = z;
+      *reinterpret_cast<half4*>(&sBl[r * LDH + c4]) = z;
+    }
+    __syncthreads();
+    ma = fmaxf(fmaxf(sMax[0], sMax[1]), fmaxf(sMax[2], sMax[3]));
+    mb = fmaxf(fmaxf(sMax[4], sMax[5]), fmaxf(sMax[6], sMax[7]));
+    // (clamped so that the scale factors stay finite for tiles of subnormal or zero entries)
+    const int ea = max(-100, min(100, store_exp(ma))), eb = max(-100, min(100, store_exp(mb)));
+    const float sa = ldexpf(1.f, -ea), sb = ldexpf(1.f, -eb);
+    esc = ea + eb;
+#pragma unroll
+    for (int q = 0; q < Q4; ++q) {
+      const int idx = tid + q * 256;
+      const int r = idx / (D / 4), c4 = 4 * (idx % (D / 4));
+      half4 h, l;
+      split_scaled4(f32x4{va[q].x, va[q].y, va[q].z, va[q].w}, sa, h, l);
+      *reinterpret_cast<half4*>(&sAh[r * LDH + c4]) = h;
+      *reinterpret_cast<half4*>(&sAl[r * LDH + c4]) = l;
+      split_scaled4(f32x4{vb[q].x, vb[q].y, vb[q].z, vb[q].w}, sb, h, l);
+      *reinterpret_cast<half4*>(&sBh[r * LDH + c4]) = h;
+      *reinterpret_cast<half4*>(&sBl[r * LDH + c4]) = l;
     }
   }
   __syncthreads();
-  // all 4 landmark tiles: the B columns past m are staged as zeros
+  // all 4 landmark tiles (B rows past m are zeros), K in chunks of 32: the lane supplies row (ln & 15) of its
+  // wave's 16 tokens and of the tile's 16 landmarks at k = 8 (ln >> 4) .. +7 of the chunk
   f32x4 acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < D / 4; ++ks) {
-    const int k = ks * 4 + (ln >> 4);
-    const float a = sA[(wv * 16 + (ln & 15)) * LDA + k];
+  for (int c = 0; c < KP / 32; ++c) {
+    const int oa = (wv * 16 + (ln & 15)) * LDH + c * 32 + 8 * (ln >> 4);
+    const half8 ah = *reinterpret_cast<const half8*>(&sAh[oa]);
+    const half8 al = *reinterpret_cast<const half8*>(&sAl[oa]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = mfma16x16x4(a, sB[k * LDB + t * 16 + (ln & 15)], acc[t]);
+    for (int t = 0; t < 4; ++t) {
+      const int ob = (t * 16 + (ln & 15)) * LDH + c * 32 + 8 * (ln >> 4);
+      const half8 bh = *reinterpret_cast<const half8*>(&sBh[ob]);
+      const half8 bl = *reinterpret_cast<const half8*>(&sBl[ob]);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[t], 0, 0, 0);
+    }
   }
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[t][r] = ldexpf(acc[t][r], esc);
   // Gq / Gk are written landmark-major too, [m][N]: the dL reduction then reads a landmark's weights for
   // consecutive tokens as one contiguous run, and the token-row kernel reads them coalesced across its lanes.
   float* out = (side == 0 ? Gq : Gk) + static_cast<size_t>(g) * m * N;
