@@ -119,8 +119,9 @@ __host__ __device__ inline int ld_b(int cols) { return ((cols + 31) / 32) * 32 +
 // =====================================================================================================
 // ckv_reduce: S[g][l][c] = sum_i C_K[g][i][l] V[g][i][c], deterministic split-N reduction
 //   ([note] motivation: linear attention forms K^T V first; Design 2).
-// Stage 1: each block reduces `rows_per_split` token rows of one slice into a partial [mout][D] on fp32 MFMA
-// (M = landmarks, N = channels, K = tokens), staging 64-row chunks of C and V through LDS. With more than 64
+// Stage 1: each block reduces `rows_per_split` token rows of one slice into a partial [mout][D] on the fp16 MFMA
+// in split form (M = landmarks, N = channels, K = tokens), staging 64-row chunks of C and V through LDS as fp16
+// halves, each chunk of each operand scaled by a power of two from its largest entry (undone exactly per chunk). With more than 64
 // landmarks the landmarks are split over blocks too (64 per block), so that each split covers more rows and the
 // partials stay small next to the C_K bytes they summarise.
 // Stage 2: the partials are summed in split order.
@@ -131,16 +132,20 @@ template <typename T, int D, int MT>
 __global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ C, const T* __restrict__ V,
                                                      float* __restrict__ part, int N, int mrow, int ones,
                                                      int nsplit, int rows_per_split, int lsplit) {
-  // LDS: the C chunk as [landmark][64 tokens] (row stride 68) and the V chunk as [64 tokens][D] (stride 16 mod 32).
-  // Landmark rows >= mrow are never written; they only feed output rows that are not stored.
-  constexpr int LDC = 68;
+  // LDS, as fp16 halves (hi, lo): the C chunk as [landmark][64 tokens] (A rows, K contiguous) and the V chunk as
+  // [64 tokens][D] (B, read by transposing reads); row strides of 16 bytes mod 128.
+  // Landmark rows >= mout are never written; they only feed output rows that are not stored.
+  constexpr int LDC = 64 + 8;
+  constexpr int LDV = D + 8;
   constexpr int DT = D / 16;
   constexpr int CTW = (DT + 3) / 4;  // column tiles per wave
-  constexpr int LDV = ((D + 31) / 32) * 32 + 16;
   constexpr int NQC = MT;            // float4 loads of C per thread: MT*16 landmarks x 16 float4
   constexpr int NQV = D / 16;        // 4-element loads of V per thread for a full chunk
-  __shared__ float sC[MT * 16 * LDC];
-  __shared__ float sV[64 * LDV];
+  __shared__ __align__(16) _Float16 sCh[MT * 16 * LDC];
+  __shared__ __align__(16) _Float16 sCl[MT * 16 * LDC];
+  __shared__ __align__(16) _Float16 sVh[64 * LDV];
+  __shared__ __align__(16) _Float16 sVl[64 * LDV];
+  __shared__ float sMax[8];
   const int mout = mrow + ones;
   // Block = (slice, token split, landmark block of MT*16 landmarks), landmark block fastest. Consecutive blocks run on
   // one XCD (blocks are dealt to the 8 XCDs round-robin), so the landmark blocks of one split read its V rows
@@ -156,6 +161,7 @@ __global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ C
   const int lbase = lsb * MT * 16;  // first landmark of this block
   const int tid = threadIdx.x, wv = wave_id(), ln = lane_id();
   const bool vec = (N & 3) == 0;  // landmark rows start 16-byte aligned
+  const int t16 = ln & 15, gq = ln >> 4;
 
   f32x4 acc[MT][CTW];
 #pragma unroll
@@ -186,42 +192,93 @@ __global__ __launch_bounds__(256) void k_ckv_partial(const float* __restrict__ C
           v.z = i + 2 < nr ? src[2] : 0.f;
           v.w = i + 3 < nr ? src[3] : 0.f;
         }
+      } else if (ones && l == mrow) {  // the appended column of ones (tokens of this chunk only)
+        v = make_float4(i + 0 < nr ? 1.f : 0.f, i + 1 < nr ? 1.f : 0.f, i + 2 < nr ? 1.f : 0.f,
+                        i + 3 < nr ? 1.f : 0.f);
       }
       cbuf[q] = v;
     }
+    float cmax = 0.f, vmax = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQC; ++q)
+      cmax = fmaxf(cmax, fmaxf(fmaxf(fabsf(cbuf[q].x), fabsf(cbuf[q].y)), fmaxf(fabsf(cbuf[q].z), fabsf(cbuf[q].w))));
 #pragma unroll
     for (int q = 0; q < NQV; ++q) {
       const int e = 4 * (tid + 256 * q);
       vbuf[q] = (e < nr * D) ? load4(vsrc + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      vmax = fmaxf(vmax, fmaxf(fmaxf(fabsf(vbuf[q].x), fabsf(vbuf[q].y)), fmaxf(fabsf(vbuf[q].z), fabsf(vbuf[q].w))));
     }
-    __syncthreads();  // the previous chunk's MFMA reads are done
+    cmax = wave_max_nonneg(cmax);
+    vmax = wave_max_nonneg(vmax);
+    if (ln == 0) {
+      sMax[wv] = cmax;
+      sMax[4 + wv] = vmax;
+    }
+    __syncthreads();  // the previous chunk's MFMA reads are done; the chunk's maxima are in
+    // each operand chunk's scale puts its largest entry in [2^12, 2^13) (clamped to keep the factors finite)
+    const int ec = max(-100, min(100, store_exp(fmaxf(fmaxf(sMax[0], sMax[1]), fmaxf(sMax[2], sMax[3])))));
+    const int ev = max(-100, min(100, store_exp(fmaxf(fmaxf(sMax[4], sMax[5]), fmaxf(sMax[6], sMax[7])))));
+    const float sc = ldexpf(1.f, -ec), sv = ldexpf(1.f, -ev);
 #pragma unroll
     for (int q = 0; q < NQC; ++q) {
       const int e = tid + 256 * q;
-      store4(sC + (e >> 4) * LDC + 4 * (e & 15), cbuf[q]);
+      half4 h, l;
+      split_scaled4(f32x4{cbuf[q].x, cbuf[q].y, cbuf[q].z, cbuf[q].w}, sc, h, l);
+      const int o = (e >> 4) * LDC + 4 * (e & 15);
+      *reinterpret_cast<half4*>(&sCh[o]) = h;
+      *reinterpret_cast<half4*>(&sCl[o]) = l;
     }
 #pragma unroll
     for (int q = 0; q < NQV; ++q) {
       const int e = 4 * (tid + 256 * q);
-      store4(sV + (e / D) * LDV + (e % D), vbuf[q]);
+      half4 h, l;
+      split_scaled4(f32x4{vbuf[q].x, vbuf[q].y, vbuf[q].z, vbuf[q].w}, sv, h, l);
+      const int o = (e / D) * LDV + (e % D);
+      *reinterpret_cast<half4*>(&sVh[o]) = h;
+      *reinterpret_cast<half4*>(&sVl[o]) = l;
     }
     __syncthreads();
     if (wv * CTW < DT) {
-#pragma unroll 4
-      for (int ks = 0; ks < 16; ++ks) {
-        const int kr = ks * 4 + (ln >> 4);
-        float b[CTW];
+      // K = the chunk's 64 tokens in two halves of 32; the lane supplies row t16 of A (landmark) and column t16 of
+      // B (channel) at tokens 8 gq .. 8 gq + 7 of the half. Each chunk sums into a fresh accumulator that is added
+      // to the block's sum with the chunk's scale undone.
+      f32x4 p[MT][CTW];
 #pragma unroll
-        for (int ct = 0; ct < CTW; ++ct) b[ct] = sV[kr * LDV + (wv * CTW + ct) * 16 + (ln & 15)];
+      for (int lt = 0; lt < MT; ++lt)
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) p[lt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        half8 bh[CTW], bl[CTW];
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+          const int k0 = kh * 32 + 8 * gq + (t16 >> 2), i = (wv * CTW + ct) * 16 + 4 * (t16 & 3);
+          const half4 h0 = __builtin_bit_cast(half4, lds_read_tr(&sVh[k0 * LDV + i]));
+          const half4 h1 = __builtin_bit_cast(half4, lds_read_tr(&sVh[(k0 + 4) * LDV + i]));
+          const half4 l0 = __builtin_bit_cast(half4, lds_read_tr(&sVl[k0 * LDV + i]));
+          const half4 l1 = __builtin_bit_cast(half4, lds_read_tr(&sVl[(k0 + 4) * LDV + i]));
+          bh[ct] = half8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+          bl[ct] = half8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+        }
 #pragma unroll
         for (int lt = 0; lt < MT; ++lt) {
-          const int l = lt * 16 + (ln & 15);
-          float a = sC[l * LDC + kr];
-          if (lbase + l == mrow) a = (ones && kr < nr) ? 1.f : 0.f;
+          const int oa = (lt * 16 + t16) * LDC + kh * 32 + 8 * gq;
+          const half8 ah = *reinterpret_cast<const half8*>(&sCh[oa]);
+          const half8 al = *reinterpret_cast<const half8*>(&sCl[oa]);
 #pragma unroll
-          for (int ct = 0; ct < CTW; ++ct) acc[lt][ct] = mfma16x16x4(a, b[ct], acc[lt][ct]);
+          for (int ct = 0; ct < CTW; ++ct) {
+            p[lt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh[ct], p[lt][ct], 0, 0, 0);
+            p[lt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl[ct], p[lt][ct], 0, 0, 0);
+            p[lt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh[ct], p[lt][ct], 0, 0, 0);
+          }
         }
       }
+#pragma unroll
+      for (int lt = 0; lt < MT; ++lt)
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) acc[lt][ct][rr] += ldexpf(p[lt][ct][rr], ec + ev);
     }
   }
   if (wv * CTW < DT) {
