@@ -346,6 +346,29 @@ __global__ __launch_bounds__(256) void k_mix(const float* __restrict__ X, const 
   __shared__ float sS[64 * D];
   __shared__ float s_rstd[RB];
   const int g = blockIdx.y, l0 = blockIdx.x * RB, tid = threadIdx.x;
+  const float* xg = X + static_cast<size_t>(g) * m * m;
+  const float* sg = S + static_cast<size_t>(g) * m * D;
+  // chunk k0 of S (64 landmark rows) and of the block's X rows into registers; the first chunk's loads go out
+  // before the whitening merge so that the two memory round trips overlap
+  constexpr int NQ = (64 * D / 4 + 255) / 256;
+  constexpr int NXV = (RB * 64 + 255) / 256;
+  float4 buf[NQ];
+  float xv[NXV];
+  auto load_chunk = [&](int k0) {
+    const int nk = min(64, m - k0);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = 4 * (tid + 256 * q);
+      buf[q] = (e < nk * D) ? load4(sg + static_cast<size_t>(k0) * D + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < NXV; ++q) {
+      const int e = tid + 256 * q;
+      const int xr = e >> 6, kk = e & 63;
+      xv[q] = (xr < RB && l0 + xr < m && kk < nk) ? xg[static_cast<size_t>(l0 + xr) * m + k0 + kk] : 0.f;
+    }
+  };
+  load_chunk(0);
   if (wst) {
     const int tiles = (N + 63) / 64, wv = tid >> 6, ln = tid & 63;
     for (int r2 = wv; r2 < RB; r2 += 4) {
@@ -374,25 +397,9 @@ __global__ __launch_bounds__(256) void k_mix(const float* __restrict__ X, const 
   }
   const int rr = tid / D, c = tid % D;
   float acc = 0.f;
-  const float* xg = X + static_cast<size_t>(g) * m * m;
-  const float* sg = S + static_cast<size_t>(g) * m * D;
   for (int k0 = 0; k0 < m; k0 += 64) {
     const int nk = min(64, m - k0);
-    constexpr int NQ = (64 * D / 4 + 255) / 256;
-    constexpr int NXV = (RB * 64 + 255) / 256;
-    float4 buf[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int e = 4 * (tid + 256 * q);
-      buf[q] = (e < nk * D) ? load4(sg + static_cast<size_t>(k0) * D + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    float xv[NXV];
-#pragma unroll
-    for (int q = 0; q < NXV; ++q) {
-      const int e = tid + 256 * q;
-      const int xr = e >> 6, kk = e & 63;
-      xv[q] = (xr < RB && l0 + xr < m && kk < nk) ? xg[static_cast<size_t>(l0 + xr) * m + k0 + kk] : 0.f;
-    }
+    if (k0 > 0) load_chunk(k0);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < NXV; ++q) {
