@@ -1128,16 +1128,18 @@ __global__ __launch_bounds__(256) void k_bwd_dq_final(const float* __restrict__ 
     }
   };
   load_chunk(0);
-  float v = 0.f;  // partials q, q + P, q + 2P, ... in that order, loaded 8 at a time
-  for (int s0 = q; s0 < nsplit; s0 += 8 * P) {
-    float pv[8];
+  // the landmark-kernel term of dL, loaded with everything else before the first sum
+  const float dlw = tid < D ? dLW[(static_cast<size_t>(g) * m + l) * D + tid] : 0.f;
+  float v = 0.f;  // partials q, q + P, q + 2P, ... in that order, loaded 16 at a time
+  for (int s0 = q; s0 < nsplit; s0 += 16 * P) {
+    float pv[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 16; ++u) {
       const int sidx = min(s0 + u * P, nsplit - 1);
       pv[u] = dLpart[((static_cast<size_t>(g) * nsplit + sidx) * m + l) * D + c];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 16; ++u)
       if (s0 + u * P < nsplit) v += pv[u];
   }
   part[tid] = v;
@@ -1146,7 +1148,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq_final(const float* __restrict__ 
     float a = 0.f;
 #pragma unroll
     for (int u = 0; u < P; ++u) a += part[u * D + tid];
-    add[tid] = (a + dLW[(static_cast<size_t>(g) * m + l) * D + tid]) * (1.f / static_cast<float>(r * r));
+    add[tid] = (a + dlw) * (1.f / static_cast<float>(r * r));
   }
   __syncthreads();
   const float ad = add[c];
