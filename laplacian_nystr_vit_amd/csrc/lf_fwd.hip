@@ -594,10 +594,17 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
     }
   }
 
-  // 1. V halo and filter taps
+  // 1. V halo and filter taps (both loaded here, stored to LDS after the prologue)
   constexpr int NQ = (100 * C4 + NT - 1) / NT;
+  constexpr int NWT = (9 * D + NT - 1) / NT;
   float4 vb[NQ];
+  float wt[NWT];
   if (has_w) {
+#pragma unroll
+    for (int q = 0; q < NWT; ++q) {
+      const int e = min(tid + NT * q, 9 * D - 1), tap = e / D, c = e % D;
+      wt[q] = w[(static_cast<size_t>(h) * D + c) * 9 + (flip ? 8 - tap : tap)];
+    }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int e = tid + NT * q;
@@ -719,10 +726,9 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
       const bool in = y >= 0 && y < H && x >= 0 && x < W;
       if (e < 100 * C4) store4(sVh + tok * Lay::LDV + 4 * (e % C4), in ? vb[q] : make_float4(0.f, 0.f, 0.f, 0.f));
     }
-    for (int e = tid; e < 9 * D; e += NT) {
-      const int q = e / D, c = e % D;
-      sWt[e] = w[(static_cast<size_t>(h) * D + c) * 9 + (flip ? 8 - q : q)];
-    }
+#pragma unroll
+    for (int q = 0; q < NWT; ++q)
+      if (tid + NT * q < 9 * D) sWt[tid + NT * q] = wt[q];
   }
   if constexpr (FUSED) {
     // chunk rows a wave does not write keep finite values: zero them once (their P^T columns are staged as zero)
