@@ -387,7 +387,7 @@ def main():
         ingest_counters(*args.ingest_counters)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the B*heads slices are "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the B*heads slices are "
               "independent, so a multi-GPU run would shard them with no communication.", file=sys.stderr)
         sys.exit(2)
 
