@@ -820,12 +820,13 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
     }
     const float muv = (mu && tid < 64 && tid < nl) ? mu[static_cast<size_t>(g) * m + lc0 + tid] : 0.f;
     // Scales of the chunk: every value of C this thread holds belongs to token ln (NT is a multiple of 64;
-    // FUSED: lane = token), and P's largest entry. The per-wave maxima go to LDS before the barrier below, which
-    // every thread passes only after the previous chunk's reads of them.
+    // FUSED: lane = token), and P's largest entry. P's per-wave maxima go to LDS before the barrier below (the
+    // previous chunk read them before its second barrier); C's per-token maxima only after it, because the
+    // previous chunk reads them until its MFMAs are done, and every thread passes the barrier below only after
+    // those reads.
     float cm = 0.f;
 #pragma unroll
     for (int q = 0; q < NCV; ++q) cm = fmaxf(cm, cv[q]);
-    sCmax[wv * 64 + ln] = cm;
     if constexpr (!MIX) {
       float pm = 0.f;
 #pragma unroll
@@ -835,6 +836,7 @@ __global__ __launch_bounds__(512) void k_out(const float* __restrict__ CQ, const
       if (ln == 0) sRed[wv] = pm;
     }
     __syncthreads();  // previous chunk's reads are done
+    sCmax[wv * 64 + ln] = cm;
     int eP = pexp;    // P of this chunk is stored times 2^-eP
     if constexpr (!MIX) {
       float bpm = sRed[0];
